@@ -1,0 +1,377 @@
+"""CPU oracle: top-k sparse decode attention over a bit-plane 4-bit key cache.
+
+TEST INFRASTRUCTURE ONLY.  This module is the slow, plain reference that the
+HIP library is checked against.  Only ``tests/``, ``__graft_entry__.smoke()``
+and the ``cpu_baseline`` leg of ``bench.py`` may import or run it; the product
+path never does.  It shares no code, header, table or helper with the HIP
+library and does not import it.
+
+Sources (cited by section; no sentence of them is reproduced):
+
+* [Fathom] the page "Fathom：针对卸载KV缓存的稀疏解码逐查询读取深度", a
+  translation of arXiv 2609.17652 -- §1 (observations 1 and 2), §2 ("Top-k
+  decoding", "SparQ"), §3.1 (cost model, Eq. 1), §3.2 (bit-plane K cache).
+  The extraction stops inside §3.2, so the plane word layout and the
+  prefix-decode formula follow the plainest reading listed in the design doc.
+* [ReadKV] the page "AI存储论文解读:ReadKV：KV 存得更细、每步少读..." --
+  §5.2 (key-channel importance summed over the query heads that share a KV
+  head), §5.4 (greedy allocation by largest predicted error drop),
+  §6.1 (append-only planes).
+
+Every floating-point decision that produces an integer (a code, a depth) is
+taken here in the precision the GPU takes it: codes from the exact real floor
+of k / s with s the stored fp16 scale, depths from fp32 gains compared
+exactly.  Everything else (scores, attention) is fp64.
+
+Parity pins: every function below is pinned by a ``-m "not gpu"`` test
+(tests/test_oracle_pins.py) against closed forms, brute force or a library
+routine; none is "parity unpinned".
+"""
+from __future__ import annotations
+
+import numpy as np
+
+D = 128          # channels per KV head (head dimension)
+BLOCK = 64       # tokens per quantisation block [Fathom §3.2]
+PLANES = 4       # bits per code [Fathom §3.2]
+FIRST_KEPT = 4   # always-kept leading tokens [Fathom §2, Top-k decoding]
+LAST_KEPT = 32   # always-kept trailing tokens [Fathom §2, Top-k decoding]
+FP16_MAX = 65504.0
+
+__all__ = [
+    "D", "BLOCK", "PLANES", "FIRST_KEPT", "LAST_KEPT",
+    "bf16_bits_to_f32", "block_scales", "quantize_codes", "encode_unit",
+    "codes_from_planes", "prefix_values", "channel_gains", "alloc_depth",
+    "alloc_depth_greedy", "scan_scores", "kept_tail", "select_topk",
+    "attend", "dense_attention", "rotate_basis", "decode_unit",
+    "scan_bits_per_token", "scan_bytes_unit",
+]
+
+
+# ----------------------------------------------------------------------------
+# storage format
+# ----------------------------------------------------------------------------
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) to the float32 values they denote."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def block_scales(k_block: np.ndarray) -> np.ndarray:
+    """fp16 scale of each channel of one 64-token block.
+
+    [Fathom §3.2] the block maximum a = max_i |k_ij| gives the cell width
+    s = a / 8, stored as one fp16 number per (block, channel).  a / 8 is exact
+    in fp32; the fp16 rounding is round-to-nearest-even and values beyond the
+    fp16 range saturate to 65504 (reading: a saturating store).
+    """
+    amax = np.max(np.abs(k_block.astype(np.float32)), axis=0)
+    with np.errstate(over="ignore"):
+        s = (amax / np.float32(8.0)).astype(np.float16)
+    s[np.isinf(s)] = np.float16(FP16_MAX)
+    return s
+
+
+def quantize_codes(k_block: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """4-bit codes c = clip(floor(k / s), -8, 7) + 8 of one block.
+
+    [Fathom §3.2] symmetric uniform code, code 8 is zero and the top bit is
+    the sign.  The floor is the exact real floor of k / s (s = the stored fp16
+    scale): the fp64 quotient is corrected with the exact products m*s.  A
+    zero scale gives code 8 for every token.
+    """
+    k = k_block.astype(np.float64)
+    sc = s.astype(np.float64)[None, :]
+    safe = np.where(sc == 0.0, 1.0, sc)
+    m = np.floor(k / safe)
+    m = m - (m * safe > k)
+    m = m + ((m + 1.0) * safe <= k)
+    c = np.clip(m, -8, 7) + 8
+    c = np.where(sc == 0.0, 8, c)
+    return c.astype(np.uint8)
+
+
+def encode_unit(keys: np.ndarray):
+    """Bit planes and scales of every complete 64-token block of one unit.
+
+    ``keys`` is (n, D) float32 (values of the stored key rows, or of the
+    rotated keys).  Returns ``planes`` uint64 [D][4][nb] and ``scales``
+    float16 [D][nb] with nb = n // 64: the open trailing block has no planes
+    yet (append-only planes, [ReadKV §6.1]).
+
+    [Fathom §3.2] for block b, channel j and bit p (p = 0 the most
+    significant bit), the 64 codes' bit p forms one 64-bit word; bit i of the
+    word belongs to token 64 b + i.  Words are stored channel-major.
+    """
+    n = keys.shape[0]
+    nb = n // BLOCK
+    blocks = keys[: nb * BLOCK].reshape(nb, BLOCK, keys.shape[1])
+    planes = np.zeros((keys.shape[1], PLANES, nb), dtype=np.uint64)
+    scales = np.zeros((keys.shape[1], nb), dtype=np.float16)
+    weights = np.uint64(1) << np.arange(BLOCK, dtype=np.uint64)
+    for b in range(nb):
+        s = block_scales(blocks[b])
+        c = quantize_codes(blocks[b], s)                 # (64, D)
+        scales[:, b] = s
+        for p in range(PLANES):
+            bit = ((c >> (PLANES - 1 - p)) & 1).astype(np.uint64)   # (64, D)
+            planes[:, p, b] = (bit * weights[:, None]).sum(axis=0, dtype=np.uint64)
+    return planes, scales
+
+
+def codes_from_planes(planes: np.ndarray, t: int, j: int, blocks: np.ndarray) -> np.ndarray:
+    """The t-bit prefix code of channel j for every token of ``blocks``.
+
+    Reads only planes p < t of channel j.  Returns an int64 array of shape
+    (len(blocks) * 64,) in token order.
+    """
+    out = np.zeros(len(blocks) * BLOCK, dtype=np.int64)
+    shifts = np.arange(BLOCK, dtype=np.uint64)
+    for p in range(t):
+        words = planes[j, p, blocks]
+        bits = ((words[:, None] >> shifts[None, :]) & np.uint64(1)).astype(np.int64)
+        out = out * 2 + bits.reshape(-1)
+    return out
+
+
+def prefix_values(prefix: np.ndarray, t: int) -> np.ndarray:
+    """Cell midpoint, in units of s, of a t-bit prefix code.
+
+    [Fathom §1 observation 2] the first t planes are the channel's t-bit
+    mid-rise quantizer with the same block scale: the prefix names a cell of
+    2^(4-t) consecutive codes whose midpoint is
+    (prefix + 1/2) * 2^(4-t) - 8.  Depth 0 reads nothing and reconstructs 0.
+    """
+    if t == 0:
+        return np.zeros(prefix.shape, dtype=np.float64)
+    return (prefix.astype(np.float64) + 0.5) * 2.0 ** (PLANES - t) - 8.0
+
+
+# ----------------------------------------------------------------------------
+# per-query depth allocation
+# ----------------------------------------------------------------------------
+
+def channel_gains(q_basis: np.ndarray, chan_var: np.ndarray) -> np.ndarray:
+    """g_j = var_j * sum_h q_hj^2 in fp32, h ascending, one rounding per op.
+
+    [Fathom §1 observation 1] g_j is channel j's share of this query's score
+    variance; [ReadKV §5.2] the importance of a key channel sums the squared
+    query components of every query head sharing the KV head.
+    """
+    q = np.asarray(q_basis, dtype=np.float32)
+    acc = np.zeros(q.shape[1], dtype=np.float32)
+    for h in range(q.shape[0]):
+        acc = (acc + q[h] * q[h]).astype(np.float32)
+    return (np.asarray(chan_var, dtype=np.float32) * acc).astype(np.float32)
+
+
+def alloc_depth(q_basis: np.ndarray, chan_var: np.ndarray, budget: int) -> np.ndarray:
+    """Depths t_j by reverse water-filling of ``budget`` planes (sort form).
+
+    [Fathom §1 observation 1, §3] the t-th plane of channel j is worth
+    g_j * 4^-t (each extra bit cuts the quantisation error by 4).  The budget
+    goes to the min(budget, 4 D) most valuable (channel, plane) candidates;
+    equal values go to the lower channel, then the lower plane.
+    """
+    g = channel_gains(q_basis, chan_var)
+    nd = g.shape[0]
+    take = min(max(int(budget), 0), PLANES * nd)
+    j = np.repeat(np.arange(nd), PLANES)
+    t = np.tile(np.arange(PLANES), nd)
+    v = (g[j] * np.float32(0.25) ** t.astype(np.float32)).astype(np.float32)
+    order = np.lexsort((t, j, -v.astype(np.float64)))
+    depth = np.zeros(nd, dtype=np.int64)
+    np.add.at(depth, j[order[:take]], 1)
+    return depth.astype(np.uint8)
+
+
+def alloc_depth_greedy(q_basis: np.ndarray, chan_var: np.ndarray, budget: int) -> np.ndarray:
+    """The same depths as the literal greedy loop.
+
+    [ReadKV §5.4] repeatedly give the next bit to the channel whose next
+    plane is worth the most (g_j * 4^-t_j), lower channel on ties, until the
+    budget is spent.
+    """
+    g = channel_gains(q_basis, chan_var)
+    nd = g.shape[0]
+    depth = np.zeros(nd, dtype=np.int64)
+    for _ in range(min(max(int(budget), 0), PLANES * nd)):
+        best, best_v = -1, -1.0
+        for jj in range(nd):
+            if depth[jj] < PLANES:
+                val = float(np.float32(g[jj] * np.float32(0.25) ** np.float32(depth[jj])))
+                if val > best_v:
+                    best, best_v = jj, val
+        depth[best] += 1
+    return depth.astype(np.uint8)
+
+
+# ----------------------------------------------------------------------------
+# key scan
+# ----------------------------------------------------------------------------
+
+def scan_scores(q_basis: np.ndarray, depth: np.ndarray, planes: np.ndarray,
+                scales: np.ndarray, n: int, chunk_blocks: int = 2048):
+    """Approximate scores of every key of the complete blocks, in fp64.
+
+    [Fathom §1, §3.2] each key is reconstructed from the first t_j planes of
+    every channel (the block's fp16 scale times the prefix cell midpoint) and
+    dotted with the query: s_hat[h, i] = sum_j q_hj * s_bj * m_ij.
+    Returns ``(scores, l1)`` of shape (G, nb * 64): ``l1`` is
+    sum_j |q_hj * s_bj * m_ij|, the scale of the rounding tolerance.
+    """
+    q = np.asarray(q_basis, dtype=np.float64)
+    nb = n // BLOCK
+    scores = np.zeros((q.shape[0], nb * BLOCK), dtype=np.float64)
+    l1 = np.zeros_like(scores)
+    for b0 in range(0, nb, chunk_blocks):
+        blocks = np.arange(b0, min(nb, b0 + chunk_blocks))
+        vals = np.zeros((len(blocks) * BLOCK, q.shape[1]), dtype=np.float64)
+        for j in range(q.shape[1]):
+            t = int(depth[j])
+            if t == 0:
+                continue
+            m = prefix_values(codes_from_planes(planes, t, j, blocks), t)
+            s = np.repeat(scales[j, blocks].astype(np.float64), BLOCK)
+            vals[:, j] = s * m
+        sl = slice(b0 * BLOCK, (b0 + len(blocks)) * BLOCK)
+        scores[:, sl] = q @ vals.T
+        l1[:, sl] = np.abs(q) @ np.abs(vals).T
+    return scores, l1
+
+
+# ----------------------------------------------------------------------------
+# top-k selection
+# ----------------------------------------------------------------------------
+
+def kept_tail(n: int) -> int:
+    """Number of always-kept trailing tokens.
+
+    [Fathom §2] the last 32 tokens are always kept.  Reading for an open
+    trailing block (n not a multiple of 64): its tokens have no planes yet,
+    so all of them are kept too -- W = max(32, n mod 64).
+    """
+    return max(LAST_KEPT, n % BLOCK)
+
+
+def select_topk(scores: np.ndarray, n: int, k: int) -> np.ndarray:
+    """Per query head: always-kept tokens plus the best remaining scores.
+
+    [Fathom §2, Top-k decoding] the first 4 and the last W tokens are always
+    kept; the other k - 4 - W are the highest-scoring keys, chosen for each
+    query head on its own (no group summing).  Equal scores go to the lower
+    token index.  If n <= k every token is kept.  Output: int64 array
+    (G, min(n, k)), ascending.
+    """
+    g = scores.shape[0]
+    if n <= k:
+        return np.tile(np.arange(n, dtype=np.int64), (g, 1))
+    w = kept_tail(n)
+    fixed = np.concatenate([np.arange(FIRST_KEPT), np.arange(n - w, n)])
+    rest = k - len(fixed)
+    if rest < 0 or n - w < FIRST_KEPT:
+        raise ValueError("k does not cover the always-kept tokens")
+    cand = np.arange(FIRST_KEPT, n - w)
+    out = np.zeros((g, k), dtype=np.int64)
+    for h in range(g):
+        order = np.lexsort((cand, -scores[h, cand]))
+        out[h] = np.sort(np.concatenate([fixed, cand[order[:rest]]]))
+    return out
+
+
+# ----------------------------------------------------------------------------
+# exact attention over the selected keys
+# ----------------------------------------------------------------------------
+
+def attend(q: np.ndarray, k_rows: np.ndarray, v_rows: np.ndarray, idx: np.ndarray,
+           scale: float) -> np.ndarray:
+    """Softmax attention of each query head over its own selected rows, fp64.
+
+    [Fathom §2] methods are judged by exact attention restricted to their
+    selected set: softmax(q K^T * scale) over S_h, then the weighted sum of
+    the V rows.  ``idx`` entries < 0 are padding and ignored.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    out = np.zeros((q.shape[0], v_rows.shape[1]), dtype=np.float64)
+    for h in range(q.shape[0]):
+        sel = idx[h][idx[h] >= 0]
+        logits = (k_rows[sel].astype(np.float64) @ q[h]) * scale
+        p = np.exp(logits - logits.max())
+        p /= p.sum()
+        out[h] = p @ v_rows[sel].astype(np.float64)
+    return out
+
+
+def dense_attention(q, k_rows, v_rows, scale):
+    """Full softmax attention over every row (the k = n special case)."""
+    n = k_rows.shape[0]
+    idx = np.tile(np.arange(n), (np.asarray(q).shape[0], 1))
+    return attend(q, k_rows, v_rows, idx, scale)
+
+
+# ----------------------------------------------------------------------------
+# rotated (KLT) basis
+# ----------------------------------------------------------------------------
+
+def rotate_basis(rot: np.ndarray, x: np.ndarray) -> np.ndarray:
+    """z = R^T x for every row of x, fp64 running sum in d order, then fp32.
+
+    [Fathom §1 contributions] models without QK normalisation are scanned in
+    a KLT basis.  Reading: the encoder and the query both use z = R^T x with
+    the per-(layer, head) orthogonal R; each product of two fp32/bf16 values
+    is exact in fp64 and is added in channel order d = 0 .. D-1.
+    """
+    r = np.asarray(rot, dtype=np.float64)
+    xx = np.asarray(x, dtype=np.float64)
+    acc = np.zeros((xx.shape[0], r.shape[1]), dtype=np.float64)
+    for d in range(r.shape[0]):
+        acc = acc + xx[:, d:d + 1] * r[d:d + 1, :]
+    return acc.astype(np.float32)
+
+
+# ----------------------------------------------------------------------------
+# one decode step of one (sequence, layer, KV head) unit
+# ----------------------------------------------------------------------------
+
+def decode_unit(q: np.ndarray, chan_var: np.ndarray, k_rows: np.ndarray,
+                v_rows: np.ndarray, n: int, budget: int, k: int, scale: float,
+                rot: np.ndarray | None = None, planes=None, scales=None):
+    """encode -> allocate -> scan -> select -> attend for one unit.
+
+    ``q`` (G, D) float32 (bf16 values), ``k_rows`` / ``v_rows`` (n, D)
+    float32 values of the stored rows.  Returns a dict of every stage.
+    """
+    enc_in = k_rows[:n] if rot is None else rotate_basis(rot, k_rows[:n])
+    if planes is None:
+        planes, scales = encode_unit(enc_in)
+    qb = np.asarray(q, dtype=np.float32) if rot is None else rotate_basis(rot, q)
+    depth = alloc_depth(qb, chan_var, budget)
+    scores, l1 = scan_scores(qb, depth, planes, scales, n)
+    full = np.zeros((qb.shape[0], n), dtype=np.float64)
+    full[:, : scores.shape[1]] = scores
+    idx = select_topk(full, n, k)
+    out = attend(q, k_rows, v_rows, idx, scale)
+    return dict(planes=planes, scales=scales, q_basis=qb, depth=depth,
+                scores=scores, l1=l1, idx=idx, out=out)
+
+
+# ----------------------------------------------------------------------------
+# byte accounting
+# ----------------------------------------------------------------------------
+
+def scan_bits_per_token(depth: np.ndarray) -> float:
+    """Bits one key costs the scan at depths t.
+
+    [Fathom §1, §2] counts are per token, per KV head, per layer; a fp16
+    scale per 64-token block costs 16 / 64 = 0.25 bit for every channel that
+    is read at all.
+    """
+    t = np.asarray(depth, dtype=np.int64)
+    return float(t.sum()) + 0.25 * float((t > 0).sum())
+
+
+def scan_bytes_unit(depth: np.ndarray, n: int) -> float:
+    """Algorithmic bytes of one unit's scan over n tokens: planes + scales."""
+    t = np.asarray(depth, dtype=np.int64)
+    nb = n // BLOCK
+    return float(t.sum()) * nb * 8.0 + float((t > 0).sum()) * nb * 2.0

@@ -1,0 +1,397 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+None of these re-types an oracle formula: each checks the oracle against an
+independent route (exact rationals, brute force, a library routine, a bound,
+or a number the Fathom page prints).
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _blocks(rng, nb, d, sigma=None):
+    sigma = np.ones(d) if sigma is None else sigma
+    return (rng.standard_normal((nb * 64, d)) * sigma).astype(np.float32)
+
+
+# --------------------------------------------------------------------------
+# quantizer and scales (Fathom §3.2)
+# --------------------------------------------------------------------------
+
+def test_scale_is_nearest_fp16_of_blockmax_over_8(rng):
+    k = _blocks(rng, 4, 16, sigma=np.exp(rng.uniform(-6, 6, 16)))
+    for b in range(4):
+        blk = k[b * 64:(b + 1) * 64]
+        s = O.block_scales(blk)
+        for j in range(16):
+            target = Fraction(float(np.max(np.abs(blk[:, j])))) / 8
+            got = Fraction(float(s[j]))
+            for nb_ in (np.nextafter(s[j], np.float16(np.inf)), np.nextafter(s[j], np.float16(0))):
+                assert abs(got - target) <= abs(Fraction(float(nb_)) - target)
+
+
+def test_scale_zero_block_and_saturation():
+    blk = np.zeros((64, 3), dtype=np.float32)
+    blk[5, 1] = 1e9           # beyond fp16 range after /8
+    blk[7, 2] = -3.0
+    s = O.block_scales(blk)
+    assert s[0] == 0 and s[1] == np.float16(65504) and s[2] == np.float16(0.375)
+    c = O.quantize_codes(blk, s)
+    assert np.all(c[:, 0] == 8)          # zero scale -> code 8 (zero)
+    assert c[5, 1] == 15                 # clipped at the top code
+    assert c[7, 2] == 0                  # -3 / 0.375 = -8 exactly
+
+
+def test_codes_match_exact_rational_floor(rng):
+    k = _blocks(rng, 2, 8, sigma=np.exp(rng.uniform(-3, 3, 8)))
+    # plant exact multiples of the scale and their neighbours
+    s = O.block_scales(k[:64])
+    for j in range(8):
+        k[63, j] = np.float32(8 * float(s[j]))      # keeps the block scale at s
+        for i, m in enumerate(range(-8, 8)):
+            v = np.float32(m * float(s[j]))
+            k[i, j] = v
+            k[16 + i, j] = np.nextafter(v, np.float32(-np.inf))
+    s2 = O.block_scales(k[:64])
+    assert np.array_equal(s2, s)
+    c = O.quantize_codes(k[:64], s)
+    for i in range(64):
+        for j in range(8):
+            q = Fraction(float(k[i, j])) / Fraction(float(s[j]))
+            m = math.floor(q)
+            assert c[i, j] == min(max(m, -8), 7) + 8
+
+
+def test_top_plane_is_sign_and_token_i_is_bit_i(rng):
+    """Fathom §3.2: code 8 is zero and the most significant bit is the sign."""
+    k = _blocks(rng, 3, 8)
+    planes, scales = O.encode_unit(k)
+    for b in range(3):
+        for j in range(8):
+            w = int(planes[j, 0, b])
+            for i in range(64):
+                assert ((w >> i) & 1) == int(k[64 * b + i, j] >= 0)
+
+
+def test_open_block_has_no_planes(rng):
+    k = _blocks(rng, 3, 4)[: 64 * 2 + 17]
+    planes, scales = O.encode_unit(k)
+    assert planes.shape == (4, 4, 2) and scales.shape == (4, 2)
+
+
+# --------------------------------------------------------------------------
+# prefix identity (Fathom §1 observation 2)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("t", [0, 1, 2, 3, 4])
+def test_plane_prefix_is_the_t_bit_quantizer(rng, t):
+    """Reading t planes equals quantizing k directly with t bits and cell s*2^(4-t)."""
+    k = _blocks(rng, 4, 6, sigma=np.exp(rng.uniform(-2, 2, 6)))
+    planes, scales = O.encode_unit(k)
+    for j in range(6):
+        pre = O.codes_from_planes(planes, t, j, np.arange(4))
+        vals = O.prefix_values(pre, t)
+        for i in range(0, 256, 3):
+            s = Fraction(float(scales[j, i // 64]))
+            if t == 0:
+                expect = Fraction(0)
+            else:
+                w = s * 2 ** (4 - t)
+                half = 2 ** (t - 1)
+                cell = min(max(math.floor(Fraction(float(k[i, j])) / w), -half), half - 1)
+                expect = (cell + Fraction(1, 2)) * w
+            assert Fraction(vals[i]) * s == expect
+
+
+def test_prefix_all_codes_all_depths():
+    """Exhaustive over the 16 codes: a t-bit prefix reconstructs the midpoint of
+    the 2^(4-t)-code cell that contains the code."""
+    k = np.zeros((64, 1), dtype=np.float32)
+    for i in range(64):
+        k[i, 0] = (i % 16 - 8 + 0.25)          # code i % 16 under s = 1
+    k[63, 0] = 7.25
+    k[0, 0] = -8.0
+    planes, scales = O.encode_unit(k * 1.0)
+    assert float(scales[0, 0]) == 1.0
+    for t in range(5):
+        vals = O.prefix_values(O.codes_from_planes(planes, t, 0, np.arange(1)), t)
+        for i in range(64):
+            c = int(math.floor(k[i, 0])) + 8
+            if t == 0:
+                assert vals[i] == 0
+                continue
+            width = 2 ** (4 - t)
+            lo = (c // width) * width - 8
+            assert vals[i] == lo + width / 2
+
+
+def test_error_quarters_per_bit(rng):
+    """Fathom §1 observation 1: each further bit cuts the squared error ~4x."""
+    k = _blocks(rng, 64, 32)
+    planes, scales = O.encode_unit(k)
+    mse = []
+    for t in range(1, 5):
+        err = 0.0
+        for j in range(32):
+            v = O.prefix_values(O.codes_from_planes(planes, t, j, np.arange(64)), t)
+            v = v * np.repeat(scales[j].astype(np.float64), 64)
+            err += np.mean((v - k[:, j]) ** 2)
+        mse.append(err / 32)
+    ratios = [mse[i] / mse[i + 1] for i in range(3)]
+    assert all(3.3 < r < 4.8 for r in ratios), ratios
+
+
+def test_reconstruction_error_bound(rng):
+    """|k - k_hat| <= s * 2^(3-t) (+ fp16 rounding slack of the scale)."""
+    k = _blocks(rng, 8, 16, sigma=np.exp(rng.uniform(-4, 4, 16)))
+    planes, scales = O.encode_unit(k)
+    for t in range(5):
+        for j in range(16):
+            v = O.prefix_values(O.codes_from_planes(planes, t, j, np.arange(8)), t)
+            s = np.repeat(scales[j].astype(np.float64), 64)
+            bound = s * 2.0 ** (3 - t) + s * 8 * 2.0 ** -10
+            assert np.all(np.abs(v * s - k[:, j]) <= bound)
+
+
+# --------------------------------------------------------------------------
+# depth allocation (Fathom §1 observation 1, ReadKV §5.2 / §5.4)
+# --------------------------------------------------------------------------
+
+def _objective(g, t):
+    return sum(Fraction(float(gj)) / 4 ** int(tj) for gj, tj in zip(g, t))
+
+
+@pytest.mark.parametrize("d", [1, 2, 3, 5])
+def test_alloc_brute_force_optimal(rng, d):
+    for trial in range(12):
+        q = rng.standard_normal((4, d)).astype(np.float32)
+        var = np.exp(rng.uniform(-3, 3, d)).astype(np.float32)
+        if trial == 0:
+            var[:] = 1.0
+            q[:] = 1.0        # all gains equal: ties everywhere
+        g = O.channel_gains(q, var)
+        import itertools
+        allt = list(itertools.product(range(5), repeat=d))
+        for p in range(0, 4 * d + 2):
+            t = O.alloc_depth(q, var, p)
+            assert int(t.sum()) == min(p, 4 * d)
+            best = min(_objective(g, tt) for tt in allt if sum(tt) == min(p, 4 * d))
+            assert _objective(g, t) == best
+
+
+def test_alloc_gain_sums_group_heads():
+    """ReadKV §5.2: channel importance sums the squared components of all heads."""
+    var = np.ones(4, dtype=np.float32)
+    q = np.zeros((4, 4), dtype=np.float32)
+    q[0, 0] = 1.0           # channel 0: one head at 1
+    q[:, 1] = 0.6           # channel 1: four heads at 0.6 -> 1.44 > 1
+    t = O.alloc_depth(q, var, 1)
+    assert list(t) == [0, 1, 0, 0]
+
+
+def test_alloc_sort_form_equals_greedy_loop(rng):
+    for trial in range(6):
+        q = rng.standard_normal((4, 128)).astype(np.float32)
+        var = np.exp(rng.uniform(-4.6, 2.8, 128)).astype(np.float32)
+        for p in (0, 1, 64, 88, 128, 511, 512, 600):
+            assert np.array_equal(O.alloc_depth(q, var, p), O.alloc_depth_greedy(q, var, p))
+
+
+def test_alloc_water_filling_threshold(rng):
+    """Closed form: some level lam splits planes worth more / less than lam."""
+    q = rng.standard_normal((4, 128)).astype(np.float32)
+    var = np.exp(rng.uniform(-4.6, 2.8, 128)).astype(np.float32)
+    g = O.channel_gains(q, var).astype(np.float64)
+    for p in (17, 64, 88, 128, 300):
+        t = O.alloc_depth(q, var, p)
+        vals = np.sort((g[:, None] * 0.25 ** np.arange(4)[None, :]).ravel())[::-1]
+        lam = vals[p - 1]
+        above = (g[:, None] * 0.25 ** np.arange(4)[None, :] > lam).sum(1)
+        atleast = (g[:, None] * 0.25 ** np.arange(4)[None, :] >= lam).sum(1)
+        assert np.all(t >= above) and np.all(t <= atleast)
+        with np.errstate(divide="ignore"):
+            closed = np.clip(np.floor(np.log(g / lam) / np.log(4.0)) + 1, 0, 4)
+        clean = (above == atleast)
+        assert np.array_equal(t[clean], closed[clean].astype(np.uint8))
+
+
+def test_alloc_zero_gains_fill_low_channels_first():
+    q = np.zeros((4, 8), dtype=np.float32)
+    var = np.ones(8, dtype=np.float32)
+    assert list(O.alloc_depth(q, var, 9)) == [4, 4, 1, 0, 0, 0, 0, 0]
+    assert list(O.alloc_depth(q, var, 0)) == [0] * 8
+    assert list(O.alloc_depth(q, var, 99)) == [4] * 8
+
+
+# --------------------------------------------------------------------------
+# scan (Fathom §1, §3.2)
+# --------------------------------------------------------------------------
+
+def test_scan_full_depth_equals_dequantized_codes(rng):
+    k = _blocks(rng, 5, 128, sigma=np.exp(rng.uniform(-2.3, 1.4, 128)))
+    q = rng.standard_normal((4, 128)).astype(np.float32)
+    planes, scales = O.encode_unit(k)
+    sc, _ = O.scan_scores(q, np.full(128, 4), planes, scales, k.shape[0])
+    # independent route: codes straight from the quantizer, no planes
+    ref = np.zeros_like(sc)
+    for b in range(5):
+        blk = k[b * 64:(b + 1) * 64]
+        s = O.block_scales(blk).astype(np.float64)
+        c = O.quantize_codes(blk, O.block_scales(blk)).astype(np.float64)
+        khat = (c - 8 + 0.5) * s[None, :]
+        ref[:, b * 64:(b + 1) * 64] = q.astype(np.float64) @ khat.T
+    assert np.allclose(sc, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_scan_depth_zero_is_zero(rng):
+    k = _blocks(rng, 2, 128)
+    planes, scales = O.encode_unit(k)
+    sc, l1 = O.scan_scores(rng.standard_normal((4, 128)), np.zeros(128), planes, scales, 128)
+    assert np.all(sc == 0) and np.all(l1 == 0)
+
+
+def test_scan_within_quantizer_bound_of_exact_dot(rng):
+    sig = np.exp(rng.uniform(-2.3, 1.4, 128))
+    k = _blocks(rng, 6, 128, sigma=sig)
+    q = rng.standard_normal((4, 128)).astype(np.float32)
+    planes, scales = O.encode_unit(k)
+    depth = O.alloc_depth(q, (sig ** 2).astype(np.float32), 88)
+    sc, _ = O.scan_scores(q, depth, planes, scales, k.shape[0])
+    exact = q.astype(np.float64) @ k.astype(np.float64).T
+    s = np.repeat(scales.astype(np.float64), 64, axis=1)          # (D, n)
+    half = s * (2.0 ** (3 - depth.astype(np.float64)))[:, None] + s * 8 * 2.0 ** -10
+    bound = np.abs(q.astype(np.float64)) @ half
+    assert np.all(np.abs(sc - exact) <= bound + 1e-9)
+
+
+def test_more_planes_never_hurt_on_average(rng):
+    sig = np.exp(rng.uniform(-2.3, 1.4, 128))
+    k = _blocks(rng, 32, 128, sigma=sig)
+    q = rng.standard_normal((4, 128)).astype(np.float32)
+    planes, scales = O.encode_unit(k)
+    exact = q.astype(np.float64) @ k.astype(np.float64).T
+    errs = []
+    for p in (32, 64, 88, 128, 256, 512):
+        depth = O.alloc_depth(q, (sig ** 2).astype(np.float32), p)
+        sc, _ = O.scan_scores(q, depth, planes, scales, k.shape[0])
+        errs.append(np.mean((sc - exact) ** 2))
+    assert all(errs[i] > errs[i + 1] for i in range(len(errs) - 1)), errs
+
+
+# --------------------------------------------------------------------------
+# selection (Fathom §2 Top-k decoding)
+# --------------------------------------------------------------------------
+
+def _check_topk_property(scores, n, k, idx):
+    w = O.kept_tail(n)
+    fixed = set(range(4)) | set(range(n - w, n))
+    for h in range(scores.shape[0]):
+        sel = set(idx[h].tolist())
+        assert len(sel) == k and fixed <= sel
+        assert list(idx[h]) == sorted(idx[h])
+        chosen = sel - fixed
+        rest = set(range(4, n - w)) - chosen
+        for a in chosen:
+            for b in rest:
+                assert scores[h, a] > scores[h, b] or (scores[h, a] == scores[h, b] and a < b)
+
+
+@pytest.mark.parametrize("n", [100, 128, 150, 191])
+def test_select_is_a_top_k(rng, n):
+    scores = np.round(rng.standard_normal((4, n)) * 3) / 2     # many exact ties
+    for k in (70, 80, n - 1):
+        if k < 4 + O.kept_tail(n):
+            continue
+        idx = O.select_topk(scores, n, k)
+        _check_topk_property(scores, n, k, idx)
+
+
+def test_select_keeps_open_block():
+    n = 64 * 3 + 40
+    scores = np.zeros((1, n))
+    idx = O.select_topk(scores, n, 60)
+    assert set(range(n - 40, n)) <= set(idx[0].tolist())
+    assert O.kept_tail(n) == 40 and O.kept_tail(64 * 3) == 32 and O.kept_tail(64 * 3 + 5) == 32
+
+
+def test_select_all_when_k_covers_n():
+    idx = O.select_topk(np.zeros((2, 50)), 50, 64)
+    assert idx.shape == (2, 50) and np.array_equal(idx[1], np.arange(50))
+
+
+# --------------------------------------------------------------------------
+# attention (Fathom §2)
+# --------------------------------------------------------------------------
+
+def test_k_equals_n_is_dense_attention(rng):
+    n = 300
+    q = rng.standard_normal((4, 128)).astype(np.float32)
+    kr = rng.standard_normal((n, 128)).astype(np.float32)
+    vr = rng.standard_normal((n, 128)).astype(np.float32)
+    sig = np.ones(128, dtype=np.float32)
+    r = O.decode_unit(q, sig, kr, vr, n, 88, n, 1 / math.sqrt(128))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q.astype(np.float64))[:, None, :],
+        torch.from_numpy(kr.astype(np.float64))[None].expand(4, n, 128),
+        torch.from_numpy(vr.astype(np.float64))[None].expand(4, n, 128),
+        scale=1 / math.sqrt(128))[:, 0, :].numpy()
+    assert np.allclose(r["out"], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_attention_two_keys_closed_form():
+    q = np.zeros((1, 2))
+    q[0, 0] = 1.0
+    kr = np.array([[0.0, 0.0], [math.log(3.0), 0.0]])
+    vr = np.array([[1.0, 0.0], [0.0, 1.0]])
+    out = O.attend(q, kr, vr, np.array([[0, 1]]), 1.0)
+    assert np.allclose(out[0], [0.25, 0.75], rtol=0, atol=1e-15)
+
+
+# --------------------------------------------------------------------------
+# rotated basis
+# --------------------------------------------------------------------------
+
+def test_rotation_matches_matmul_and_inverts(rng):
+    a = rng.standard_normal((128, 128))
+    r, _ = np.linalg.qr(a)
+    r = r.astype(np.float32)
+    x = rng.standard_normal((50, 128)).astype(np.float32)
+    z = O.rotate_basis(r, x)
+    assert np.allclose(z, x.astype(np.float64) @ r.astype(np.float64), rtol=0, atol=1e-5)
+    assert np.array_equal(O.rotate_basis(np.eye(128, dtype=np.float32), x), x)
+    back = z.astype(np.float64) @ r.astype(np.float64).T
+    assert np.allclose(back, x, atol=1e-4)
+
+
+# --------------------------------------------------------------------------
+# byte accounting (Fathom §1, §2; numbers the page prints)
+# --------------------------------------------------------------------------
+
+def test_bit_accounting_matches_page():
+    g = json.load(open(os.path.join(GOLDEN, "fathom_bit_accounting.json")))
+    m = g["model"]
+    t = np.zeros(128, dtype=np.int64)
+    t[: g["scan_136"]["channels"]] = g["scan_136"]["depth"]
+    assert O.scan_bits_per_token(t) == g["scan_136"]["bits_per_token"]
+    t2 = np.full(128, g["thumbnail_288"]["depth"])
+    assert O.scan_bits_per_token(t2) == g["thumbnail_288"]["bits_per_token"]
+    assert O.scan_bits_per_token(t) / 8 == g["label_cache_bytes_per_token"]["bytes"]
+    n32 = g["scan_bytes_per_pair_32k"]["tokens"]
+    per_pair = O.scan_bytes_unit(t, n32)
+    assert round(per_pair / 1000) == g["scan_bytes_per_pair_32k"]["kilobytes"]
+    pairs = m["layers"] * m["kv_heads"]
+    assert round(per_pair * pairs / 1e6) == g["scan_bytes_per_step_32k"]["megabytes"]
+    n1m = g["scan_bytes_per_step_1m"]["tokens"]
+    assert round(O.scan_bytes_unit(t, n1m) * pairs / 1e9, 1) == g["scan_bytes_per_step_1m"]["gigabytes"]
+    dense = 2 * n32 * m["head_dim"] * 2 * pairs
+    assert round(dense / 1e9, 1) == g["dense_kv_bytes_per_step_32k"]["gigabytes"]
+    assert m["q_per_kv"] * g["union_rows_per_kv_head_max"]["k"] == g["union_rows_per_kv_head_max"]["rows"]
