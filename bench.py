@@ -1,0 +1,201 @@
+#!/usr/bin/env python3
+"""Benchmark of the bit-plane top-k decode path on one MI355X.
+
+A step is one decode step over every (sequence, layer, KV head) unit of the
+workload: depth allocation -> prefix-plane key scan -> per-head top-k ->
+union-gather attention, on a cache resident in HBM (rows, planes, scales).
+Default workload: 36 layers x 8 KV heads x 1 sequence of n = 1,048,576 tokens,
+G = 4 query heads per KV head, plane budget P = 88 (the "92-bit" point),
+k = 512; KV heads 4-7 have Pareto channel variances.
+
+The headline value is the key scan's bandwidth: algorithmic bytes of one scan
+launch (the selected planes, P*n/8 bytes per unit, plus the fp16 scales of the
+channels read, 2*C_read*n/64 bytes per unit) over its average duration,
+measured with HIP events on the stream the kernels run on.  Prints one JSON
+line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def scan_bytes(depth_np, n: int) -> float:
+    """Algorithmic bytes of one scan over the units whose depths are given."""
+    t = depth_np.reshape(-1, depth_np.shape[-1]).astype("int64")
+    nb = n // 64
+    return float(t.sum()) * nb * 8.0 + float((t > 0).sum()) * nb * 2.0
+
+
+def time_launches(fn, steps: int):
+    import torch
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(steps):
+        fn()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps  # ms
+
+
+def cpu_baseline(cfg, budget: int, tokens: int, units):
+    """The oracle's scan on a bounded sample: host-regenerated keys of `units`,
+    first `tokens` tokens each, encoded, allocated and scanned by the oracle."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle as O
+    from synth import workload as W
+    total_bytes, total_s, step_s = 0.0, 0.0, 0.0
+    with threadpool_limits(limits=1):
+        for (s, l, h) in units:
+            _, k = W.key_rows(cfg, s, l, h, np.arange(tokens))
+            _, q = W.query(cfg, s, l, h)
+            var = cfg.chan_var(s, l, h)
+            planes, scales = O.encode_unit(k)
+            t0 = time.perf_counter()
+            depth = O.alloc_depth(q, var, budget)
+            O.scan_scores(q, depth, planes, scales, tokens)
+            total_s += time.perf_counter() - t0
+            total_bytes += O.scan_bytes_unit(depth, tokens)
+    return {"value": round(total_bytes / total_s / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": (f"oracle alloc+scan of {len(units)} units {list(units)} of the same "
+                       f"workload, first {tokens} tokens each, P={budget}; "
+                       f"{total_s:.1f} s of CPU time")}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="c4")
+    ap.add_argument("--budget", type=int, default=88)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=65536)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards over sequences and (layer, KV head) units with no exchange; "
+              "see DESIGN.md)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import bit_plane_key_amd as bpk
+    from bit_plane_key_amd import workloads
+    from synth import config_by_name
+
+    cfg = config_by_name(args.config)
+    budget, k, n = args.budget, cfg.k, cfg.n
+    torch.cuda.set_device(0)
+    t0 = time.perf_counter()
+    log(f"building {cfg.name}: {cfg.description}")
+    cache = workloads.build_cache(cfg)
+    log(f"cache built in {time.perf_counter() - t0:.1f} s")
+    q = workloads.queries(cfg)
+    scale = workloads.softmax_scale(cfg)
+    L = cfg.layers
+    ws = torch.empty(bpk.workspace_bytes(cache, bpk.BPK_OP_DECODE, 0, L, k), dtype=torch.uint8,
+                     device="cuda")
+    out = torch.empty((cfg.seqs, L, cfg.heads, cfg.group, 128), dtype=torch.float32,
+                      device="cuda")
+
+    def step():
+        bpk.decode_step(cache, q, 0, L, budget, k, scale, out=out, ws=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log("warmup done")
+    ms_step = time_launches(step, args.steps)
+    log(f"decode step: {ms_step * 1e3:.1f} us")
+
+    # per-stage timing with the standalone entry points (same kernels, same stream)
+    del ws
+    depth, qb = bpk.alloc_depth(cache, q, 0, L, budget)
+    scores = torch.empty((cfg.seqs, L, cfg.heads, cfg.group, cfg.capacity), dtype=torch.float32,
+                         device="cuda")
+    bpk.scan_scores(cache, qb, depth, 0, L, scores=scores)
+    idx = bpk.select_topk(cache, scores, 0, L, k)
+    torch.cuda.synchronize()
+    ms_alloc = time_launches(lambda: bpk.alloc_depth(cache, q, 0, L, budget, depth, qb), args.steps)
+    ms_scan = time_launches(lambda: bpk.scan_scores(cache, qb, depth, 0, L, scores=scores),
+                            args.steps)
+    ms_select = time_launches(lambda: bpk.select_topk(cache, scores, 0, L, k, idx=idx), args.steps)
+    att_ws = torch.empty(bpk.workspace_bytes(cache, bpk.BPK_OP_ATTEND, 0, L, k),
+                         dtype=torch.uint8, device="cuda")
+    ms_attend = time_launches(lambda: bpk.sparse_attend(cache, q, idx, 0, L, k, scale, out=out,
+                                                        ws=att_ws), args.steps)
+    log(f"stages (us): alloc {ms_alloc*1e3:.1f} scan {ms_scan*1e3:.1f} "
+        f"select {ms_select*1e3:.1f} attend {ms_attend*1e3:.1f}")
+
+    d = depth.cpu().numpy()
+    sbytes = scan_bytes(d, n)
+    bits = [float(t.sum()) + 0.25 * float((t > 0).sum()) for t in d.reshape(-1, 128)]
+    scan_gbs = sbytes / (ms_scan * 1e-3) / 1e9
+    units = cfg.units
+    keys_per_s = units * n / (ms_scan * 1e-3)
+
+    result = {
+        "metric": "K-scan GB/s (% of HBM peak) + decode-step us at n=1M tokens, 92-bit budget",
+        "value": round(scan_gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"{cfg.name}: {cfg.seqs} seq x {cfg.layers} layers x {cfg.heads} KV "
+                         f"heads, G={cfg.group}, D=128, n={n}, P={budget}, k={k}"),
+            "units": units, "n": n, "budget_planes": budget, "k": k,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(scan_gbs, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(scan_gbs / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "kernel": "scan_kernel",
+            "bytes_per_launch": sbytes,
+            "avg_launch_us": round(ms_scan * 1e3, 2),
+        },
+        "decode_step_us": round(ms_step * 1e3, 1),
+        "stage_us": {"alloc": round(ms_alloc * 1e3, 1), "scan": round(ms_scan * 1e3, 1),
+                     "select": round(ms_select * 1e3, 1), "attend": round(ms_attend * 1e3, 1)},
+        "keys_per_s": round(keys_per_s, 0),
+        "scan_bits_per_token_mean": round(float(np.mean(bits)), 2),
+    }
+    if not args.no_cpu_baseline:
+        log("timing the oracle on a CPU sample")
+        sample_units = [(0, 0, 0), (0, 0, cfg.heads - 1)]
+        result["cpu_baseline"] = cpu_baseline(cfg, budget, min(args.cpu_tokens, n), sample_units)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

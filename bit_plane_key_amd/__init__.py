@@ -1,0 +1,26 @@
+"""MI355X (gfx950) top-k sparse decode attention over a bit-plane 4-bit key cache.
+
+The computation lives in ``libbpk.so`` (hand-written HIP, C ABI declared in
+``include/bpk.h``); this package is its Python binding.  Importing it without
+the built library raises ImportError: there is no fallback path.
+"""
+from ._lib import (  # noqa: F401
+    BLOCK,
+    BPK_OP_ATTEND,
+    BPK_OP_DECODE,
+    BPK_OP_SELECT,
+    EXPORTS,
+    HEAD_DIM,
+    LIB_PATH,
+    PLANES,
+    BpkError,
+    Cache,
+    alloc_depth,
+    decode_step,
+    encode_append,
+    last_error,
+    scan_scores,
+    select_topk,
+    sparse_attend,
+    workspace_bytes,
+)

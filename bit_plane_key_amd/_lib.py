@@ -1,0 +1,256 @@
+"""ctypes binding of libbpk.so: argument marshalling only.
+
+Every entry point of ``include/bpk.h`` has a function of the same name here
+(without the ``bpk_`` prefix).  Tensors are torch tensors on the GPU; the
+functions check dtypes, shapes and devices, pass raw pointers and the current
+torch stream, and raise ``BpkError`` on a nonzero return.  No step of the
+computation runs in Python, and there is no fallback: importing this module
+without the built library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbpk.so")
+
+BPK_OK, BPK_EINVAL, BPK_EUNSUPPORTED, BPK_EWORKSPACE, BPK_ECAPACITY, BPK_EHIP = 0, -1, -2, -3, -4, -5
+BPK_F32, BPK_BF16 = 0, 1
+BPK_OP_SELECT, BPK_OP_ATTEND, BPK_OP_DECODE = 3, 4, 5
+HEAD_DIM, BLOCK, PLANES = 128, 64, 4
+
+EXPORTS = ("bpk_encode_append", "bpk_alloc_depth", "bpk_scan_scores", "bpk_select_topk",
+           "bpk_sparse_attend", "bpk_decode_step", "bpk_workspace_bytes", "bpk_last_error")
+
+
+class BpkError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"bpk error {code}: {message}")
+        self.code = code
+
+
+class BpkCacheStruct(ctypes.Structure):
+    _fields_ = [
+        ("num_seqs", ctypes.c_int32),
+        ("num_layers", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("group", ctypes.c_int32),
+        ("k_dtype", ctypes.c_int32),
+        ("capacity", ctypes.c_int64),
+        ("n_tokens", ctypes.POINTER(ctypes.c_int64)),
+        ("k_rows", ctypes.c_void_p),
+        ("v_rows", ctypes.c_void_p),
+        ("planes", ctypes.c_void_p),
+        ("scales", ctypes.c_void_p),
+        ("chan_var", ctypes.c_void_p),
+        ("rot", ctypes.c_void_p),
+    ]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                          "(python bit_plane_key_amd/build.py)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, SZ, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+    C = ctypes.POINTER(BpkCacheStruct)
+    sig = {
+        "bpk_encode_append": (ctypes.c_int, [C, I32, P, P, I64, P]),
+        "bpk_alloc_depth": (ctypes.c_int, [C, P, I32, I32, I32, P, P, P]),
+        "bpk_scan_scores": (ctypes.c_int, [C, P, P, I32, I32, P, P]),
+        "bpk_select_topk": (ctypes.c_int, [C, P, I32, I32, I32, P, P, SZ, P]),
+        "bpk_sparse_attend": (ctypes.c_int, [C, P, P, I32, I32, I32, F, P, P, SZ, P]),
+        "bpk_decode_step": (ctypes.c_int, [C, P, I32, I32, I32, I32, F, P, P, P, P, SZ, P]),
+        "bpk_workspace_bytes": (ctypes.c_size_t, [C, I32, I32, I32, I32]),
+        "bpk_last_error": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype, fn.argtypes = res, args
+    return lib
+
+
+LIB = _load()
+
+
+def last_error() -> str:
+    return LIB.bpk_last_error().decode()
+
+
+def _check(rc: int) -> None:
+    if rc != BPK_OK:
+        raise BpkError(rc, last_error())
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, dtype, shape) -> None:
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: must be a GPU tensor")
+
+
+class Cache:
+    """Caller-owned storage of a bit-plane key cache (see include/bpk.h).
+
+    Device arrays are torch tensors; ``n_tokens`` is a host int64 array the
+    caller advances after appends.
+    """
+
+    def __init__(self, num_seqs: int, num_layers: int, num_kv_heads: int, capacity: int,
+                 group: int = 4, k_dtype: str = "bf16", rotated: bool = False,
+                 device: str = "cuda"):
+        if capacity % BLOCK:
+            raise ValueError("capacity must be a multiple of 64")
+        S, L, H, D = num_seqs, num_layers, num_kv_heads, HEAD_DIM
+        self.S, self.L, self.H, self.G, self.capacity = S, L, H, group, capacity
+        self.k_dtype = k_dtype
+        kt = torch.float32 if k_dtype == "f32" else torch.bfloat16
+        self.k_rows = torch.empty((S, L, H, capacity, D), dtype=kt, device=device)
+        self.v_rows = torch.empty((S, L, H, capacity, D), dtype=torch.bfloat16, device=device)
+        nb = capacity // BLOCK
+        self.planes = torch.zeros((S, L, H, D, PLANES, nb), dtype=torch.int64, device=device)
+        self.scales = torch.zeros((S, L, H, D, nb), dtype=torch.float16, device=device)
+        self.chan_var = torch.ones((S, L, H, D), dtype=torch.float32, device=device)
+        self.rot = (torch.empty((L, H, D, D), dtype=torch.float32, device=device)
+                    if rotated else None)
+        self.n_tokens = np.zeros(S, dtype=np.int64)
+        self._struct = BpkCacheStruct()
+
+    def struct(self) -> ctypes.POINTER(BpkCacheStruct):
+        s = self._struct
+        s.num_seqs, s.num_layers, s.num_kv_heads = self.S, self.L, self.H
+        s.head_dim, s.group = HEAD_DIM, self.G
+        s.k_dtype = BPK_F32 if self.k_dtype == "f32" else BPK_BF16
+        s.capacity = self.capacity
+        s.n_tokens = self.n_tokens.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+        s.k_rows, s.v_rows = self.k_rows.data_ptr(), self.v_rows.data_ptr()
+        s.planes, s.scales = self.planes.data_ptr(), self.scales.data_ptr()
+        s.chan_var = self.chan_var.data_ptr()
+        s.rot = None if self.rot is None else self.rot.data_ptr()
+        return ctypes.pointer(s)
+
+    def units(self, l0: int, l1: int) -> int:
+        return self.S * (l1 - l0) * self.H
+
+
+# ---------------------------------------------------------------------------
+# entry points (same names as the C ABI)
+# ---------------------------------------------------------------------------
+
+def workspace_bytes(cache: Cache, op: int, l0: int, l1: int, k: int) -> int:
+    return int(LIB.bpk_workspace_bytes(cache.struct(), op, l0, l1, k))
+
+
+def encode_append(cache: Cache, seq: int, k_new=None, v_new=None, n_new: int | None = None,
+                  stream=None) -> None:
+    """Append tokens to sequence ``seq`` and encode the blocks they complete.
+
+    With ``k_new``/``v_new`` None the rows are already in place and ``n_new``
+    must be given.  Advances ``cache.n_tokens[seq]``.
+    """
+    if k_new is not None:
+        n_new = k_new.shape[2]
+        kt = torch.float32 if cache.k_dtype == "f32" else torch.bfloat16
+        _need(k_new, "k_new", kt, (cache.L, cache.H, n_new, HEAD_DIM))
+        _need(v_new, "v_new", torch.bfloat16, (cache.L, cache.H, n_new, HEAD_DIM))
+    _check(LIB.bpk_encode_append(cache.struct(), seq, _ptr(k_new), _ptr(v_new), int(n_new),
+                                 _stream(stream)))
+    cache.n_tokens[seq] += int(n_new)
+
+
+def alloc_depth(cache: Cache, q: torch.Tensor, l0: int, l1: int, budget: int, depth=None,
+                q_basis=None, stream=None):
+    u = (cache.S, l1 - l0, cache.H)
+    _need(q, "q", torch.bfloat16, (*u, cache.G, HEAD_DIM))
+    if depth is None:
+        depth = torch.empty((*u, HEAD_DIM), dtype=torch.uint8, device=q.device)
+    if q_basis is None:
+        q_basis = torch.empty((*u, cache.G, HEAD_DIM), dtype=torch.float32, device=q.device)
+    _need(depth, "depth", torch.uint8, (*u, HEAD_DIM))
+    _need(q_basis, "q_basis", torch.float32, (*u, cache.G, HEAD_DIM))
+    _check(LIB.bpk_alloc_depth(cache.struct(), q.data_ptr(), l0, l1, int(budget),
+                               depth.data_ptr(), q_basis.data_ptr(), _stream(stream)))
+    return depth, q_basis
+
+
+def scan_scores(cache: Cache, q_basis: torch.Tensor, depth: torch.Tensor, l0: int, l1: int,
+                scores=None, stream=None):
+    u = (cache.S, l1 - l0, cache.H)
+    _need(q_basis, "q_basis", torch.float32, (*u, cache.G, HEAD_DIM))
+    _need(depth, "depth", torch.uint8, (*u, HEAD_DIM))
+    if scores is None:
+        scores = torch.zeros((*u, cache.G, cache.capacity), dtype=torch.float32,
+                             device=q_basis.device)
+    _need(scores, "scores", torch.float32, (*u, cache.G, cache.capacity))
+    _check(LIB.bpk_scan_scores(cache.struct(), q_basis.data_ptr(), depth.data_ptr(), l0, l1,
+                               scores.data_ptr(), _stream(stream)))
+    return scores
+
+
+def select_topk(cache: Cache, scores: torch.Tensor, l0: int, l1: int, k: int, idx=None,
+                stream=None):
+    u = (cache.S, l1 - l0, cache.H)
+    _need(scores, "scores", torch.float32, (*u, cache.G, cache.capacity))
+    if idx is None:
+        idx = torch.empty((*u, cache.G, k), dtype=torch.int32, device=scores.device)
+    _need(idx, "idx", torch.int32, (*u, cache.G, k))
+    _check(LIB.bpk_select_topk(cache.struct(), scores.data_ptr(), l0, l1, int(k),
+                               idx.data_ptr(), None, 0, _stream(stream)))
+    return idx
+
+
+def sparse_attend(cache: Cache, q: torch.Tensor, idx: torch.Tensor, l0: int, l1: int, k: int,
+                  softmax_scale: float, out=None, ws=None, stream=None):
+    u = (cache.S, l1 - l0, cache.H)
+    _need(q, "q", torch.bfloat16, (*u, cache.G, HEAD_DIM))
+    _need(idx, "idx", torch.int32, (*u, cache.G, k))
+    if out is None:
+        out = torch.empty((*u, cache.G, HEAD_DIM), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.float32, (*u, cache.G, HEAD_DIM))
+    need = workspace_bytes(cache, BPK_OP_ATTEND, l0, l1, k)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(LIB.bpk_sparse_attend(cache.struct(), q.data_ptr(), idx.data_ptr(), l0, l1, int(k),
+                                 float(softmax_scale), out.data_ptr(), ws.data_ptr(),
+                                 ws.numel(), _stream(stream)))
+    return out
+
+
+def decode_step(cache: Cache, q: torch.Tensor, l0: int, l1: int, budget: int, k: int,
+                softmax_scale: float, out=None, depth_out=None, idx_out=None, ws=None,
+                stream=None):
+    u = (cache.S, l1 - l0, cache.H)
+    _need(q, "q", torch.bfloat16, (*u, cache.G, HEAD_DIM))
+    if out is None:
+        out = torch.empty((*u, cache.G, HEAD_DIM), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.float32, (*u, cache.G, HEAD_DIM))
+    if depth_out is not None:
+        _need(depth_out, "depth_out", torch.uint8, (*u, HEAD_DIM))
+    if idx_out is not None:
+        _need(idx_out, "idx_out", torch.int32, (*u, cache.G, k))
+    need = workspace_bytes(cache, BPK_OP_DECODE, l0, l1, k)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(LIB.bpk_decode_step(cache.struct(), q.data_ptr(), l0, l1, int(budget), int(k),
+                               float(softmax_scale), out.data_ptr(), _ptr(depth_out),
+                               _ptr(idx_out), ws.data_ptr(), ws.numel(), _stream(stream)))
+    return out

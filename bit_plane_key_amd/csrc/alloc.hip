@@ -1,0 +1,132 @@
+// Per-query depth allocation by reverse water-filling (Fathom §1 observation 1
+// and §3; ReadKV §5.2 and §5.4).  One wavefront per unit: lane l owns channels
+// 2l and 2l+1 and their 8 (channel, plane) candidates.  The budget of P planes
+// goes to the P candidates of largest value g_j * 4^-t; the P-th largest
+// candidate is found by a 41-step bitwise search over the totally ordered keys
+// (value bits << 9 | 511 - (4 j + t)), counting with wave ballots, and a
+// channel's depth is the number of its candidates at or above that key.
+#include "bpk_internal.h"
+
+namespace bpk {
+namespace {
+
+struct AllocArgs {
+  Geom g;
+  const uint16_t* q;
+  const float* chan_var;
+  const float* rot;
+  int budget;
+  uint8_t* depth;
+  float* q_basis;
+};
+
+template <int G, bool ROT>
+__global__ __launch_bounds__(64) void alloc_kernel(AllocArgs a) {
+  __shared__ float sq[ROT ? G : 1][ROT ? D : 1];
+  const int u = blockIdx.x;
+  const long long gu = a.g.global_unit(u);
+  const int lane = threadIdx.x;
+  const uint16_t* qu = a.q + (long long)u * G * D;
+
+  float qb[G][2];
+  if constexpr (!ROT) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) qb[h][c] = bf16_to_f32(qu[h * D + 2 * lane + c]);
+  } else {
+    for (int e = lane; e < G * D; e += 64) sq[e / D][e % D] = bf16_to_f32(qu[e]);
+    __syncthreads();
+    const int l = a.g.l0 + (u / a.g.H) % a.g.nl;
+    const int hh = u % a.g.H;
+    const float* r = a.rot + (long long)(l * a.g.H + hh) * D * D;
+    // q'_j = sum_d R[d][j] q_d, exact fp64 products added in ascending d
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int j = 2 * lane + c;
+      for (int h = 0; h < G; ++h) {
+        double acc = 0.0;
+        for (int d = 0; d < D; ++d) acc = __dadd_rn(acc, (double)r[d * D + j] * (double)sq[h][d]);
+        qb[h][c] = (float)acc;
+      }
+    }
+  }
+  float* qbo = a.q_basis + (long long)u * G * D;
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) qbo[h * D + 2 * lane + c] = qb[h][c];
+
+  // g_j = var_j * (((q_0j^2 + q_1j^2) + ...) + q_(G-1)j^2), one rounding per op
+  float gain[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    float acc = 0.f;
+#pragma unroll
+    for (int h = 0; h < G; ++h) acc = __fadd_rn(acc, __fmul_rn(qb[h][c], qb[h][c]));
+    gain[c] = __fmul_rn(a.chan_var[gu * D + 2 * lane + c], acc);
+  }
+
+  uint8_t* dep = a.depth + (long long)u * D;
+  const int take = a.budget < NP * D ? a.budget : NP * D;
+  if (take <= 0 || take >= NP * D) {
+    const uint8_t v = take <= 0 ? 0 : NP;
+    dep[2 * lane] = v;
+    dep[2 * lane + 1] = v;
+    return;
+  }
+
+  const float quarter_pow[NP] = {1.0f, 0.25f, 0.0625f, 0.015625f};
+  uint64_t key[2][NP];
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int t = 0; t < NP; ++t) {
+      const float v = __fmul_rn(gain[c], quarter_pow[t]);
+      const uint32_t j = 2 * lane + c;
+      key[c][t] = ((uint64_t)__float_as_uint(v) << 9) | (uint64_t)(511u - (NP * j + t));
+    }
+
+  uint64_t prefix = 0;
+  for (int b = 40; b >= 0; --b) {
+    const uint64_t cand = prefix | (1ull << b);
+    int cnt = 0;
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int t = 0; t < NP; ++t) cnt += __popcll(__ballot(key[c][t] >= cand));
+    if (cnt >= take) prefix = cand;
+  }
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    int t_j = 0;
+#pragma unroll
+    for (int t = 0; t < NP; ++t) t_j += key[c][t] >= prefix ? 1 : 0;
+    dep[2 * lane + c] = (uint8_t)t_j;
+  }
+}
+
+template <int G>
+void launch_g(const AllocArgs& a, hipStream_t st) {
+  if (a.rot)
+    alloc_kernel<G, true><<<a.g.units(), 64, 0, st>>>(a);
+  else
+    alloc_kernel<G, false><<<a.g.units(), 64, 0, st>>>(a);
+}
+
+}  // namespace
+
+hipError_t launch_alloc(const Geom& g, const uint16_t* q, const float* chan_var, const float* rot,
+                        int budget, uint8_t* depth, float* q_basis, hipStream_t st) {
+  AllocArgs a{g, q, chan_var, rot, budget, depth, q_basis};
+  switch (g.G) {
+    case 1: launch_g<1>(a, st); break;
+    case 2: launch_g<2>(a, st); break;
+    case 4: launch_g<4>(a, st); break;
+    case 8: launch_g<8>(a, st); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace bpk

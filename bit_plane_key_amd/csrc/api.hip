@@ -1,0 +1,236 @@
+// C ABI of the library: argument validation, workspace carving and launch
+// sequencing.  Every check runs before the first launch, so a call that
+// returns a validation error has enqueued nothing.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "bpk_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return BPK_OK;
+  return fail(BPK_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Checks shared by every entry point; fills the geometry of layers [l0, l1).
+int check_cache(const bpk_cache_t* c, int l0, int l1, bpk::Geom* g) {
+  if (!c) return fail(BPK_EINVAL, "cache is NULL");
+  if (c->head_dim != BPK_HEAD_DIM)
+    return fail(BPK_EUNSUPPORTED, "head_dim %d unsupported (only %d)", c->head_dim, BPK_HEAD_DIM);
+  if (c->group != 1 && c->group != 2 && c->group != 4 && c->group != 8)
+    return fail(BPK_EUNSUPPORTED, "group %d unsupported (1, 2, 4 or 8)", c->group);
+  if (c->num_seqs < 1 || c->num_seqs > BPK_MAX_SEQS)
+    return fail(BPK_EUNSUPPORTED, "num_seqs %d outside [1, %d]", c->num_seqs, BPK_MAX_SEQS);
+  if (c->num_layers < 1 || c->num_kv_heads < 1)
+    return fail(BPK_EINVAL, "num_layers and num_kv_heads must be >= 1");
+  if ((long long)c->num_layers * c->num_kv_heads > 65535)
+    return fail(BPK_EUNSUPPORTED, "num_layers * num_kv_heads > 65535");
+  if (c->capacity <= 0 || c->capacity % BPK_BLOCK != 0 || c->capacity > (1ll << 28))
+    return fail(BPK_EUNSUPPORTED, "capacity %lld must be a positive multiple of 64, <= 2^28",
+                (long long)c->capacity);
+  if (c->k_dtype != BPK_F32 && c->k_dtype != BPK_BF16)
+    return fail(BPK_EINVAL, "k_dtype %d invalid", c->k_dtype);
+  if (!c->n_tokens) return fail(BPK_EINVAL, "n_tokens is NULL");
+  if (!c->k_rows || !c->v_rows || !c->planes || !c->scales || !c->chan_var)
+    return fail(BPK_EINVAL, "cache array pointer is NULL");
+  for (int s = 0; s < c->num_seqs; ++s)
+    if (c->n_tokens[s] < 0 || c->n_tokens[s] > c->capacity)
+      return fail(BPK_EINVAL, "n_tokens[%d] = %lld outside [0, capacity]", s,
+                  (long long)c->n_tokens[s]);
+  if (l0 < 0 || l1 > c->num_layers || l0 >= l1)
+    return fail(BPK_EINVAL, "layer range [%d, %d) invalid for %d layers", l0, l1, c->num_layers);
+  const long long units = (long long)c->num_seqs * (l1 - l0) * c->num_kv_heads;
+  if (units > 65535) return fail(BPK_EUNSUPPORTED, "more than 65535 units in one call");
+  g->S = c->num_seqs;
+  g->L = c->num_layers;
+  g->H = c->num_kv_heads;
+  g->G = c->group;
+  g->l0 = l0;
+  g->nl = l1 - l0;
+  g->cap = c->capacity;
+  for (int s = 0; s < BPK_MAX_SEQS; ++s) g->n[s] = s < c->num_seqs ? c->n_tokens[s] : 0;
+  return BPK_OK;
+}
+
+int check_k(const bpk_cache_t* c, int k) {
+  if (k < 1 || k > BPK_MAX_K) return fail(BPK_EINVAL, "k = %d outside [1, %d]", k, BPK_MAX_K);
+  if ((long long)k * c->group > BPK_MAX_SELECTED)
+    return fail(BPK_EUNSUPPORTED, "group * k = %lld > %d", (long long)k * c->group,
+                BPK_MAX_SELECTED);
+  for (int s = 0; s < c->num_seqs; ++s) {
+    const long long n = c->n_tokens[s];
+    const long long w = (n % BPK_BLOCK) > 32 ? (n % BPK_BLOCK) : 32;
+    if (n > k && k < 4 + w)
+      return fail(BPK_EINVAL, "k = %d does not cover the %lld always-kept tokens of sequence %d",
+                  k, 4 + w, s);
+  }
+  return BPK_OK;
+}
+
+struct DecodeWs {
+  size_t q_basis, depth, scores, idx, attend, total;
+};
+
+DecodeWs decode_ws(const bpk::Geom& g, int k) {
+  DecodeWs w;
+  const size_t units = (size_t)g.units();
+  size_t off = 0;
+  w.q_basis = off; off += align256(units * g.G * bpk::D * sizeof(float));
+  w.depth = off;   off += align256(units * bpk::D);
+  w.scores = off;  off += align256(units * g.G * (size_t)g.cap * sizeof(float));
+  w.idx = off;     off += align256(units * g.G * (size_t)k * sizeof(int32_t));
+  w.attend = off;  off += align256(bpk::attend_ws_bytes(g, k));
+  w.total = off;
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* bpk_last_error(void) { return g_err.c_str(); }
+
+size_t bpk_workspace_bytes(const bpk_cache_t* c, int32_t op, int32_t l0, int32_t l1, int32_t k) {
+  bpk::Geom g;
+  if (check_cache(c, l0, l1, &g) != BPK_OK) return 0;
+  if (k < 1 || k > BPK_MAX_K) return 0;
+  switch (op) {
+    case BPK_OP_SELECT: return 0;
+    case BPK_OP_ATTEND: return bpk::attend_ws_bytes(g, k);
+    case BPK_OP_DECODE: return decode_ws(g, k).total;
+    default: return 0;
+  }
+}
+
+int bpk_encode_append(const bpk_cache_t* c, int32_t seq, const void* k_new, const uint16_t* v_new,
+                      int64_t n_new, void* stream) {
+  bpk::Geom g;
+  int rc = check_cache(c, 0, c ? c->num_layers : 1, &g);
+  if (rc) return rc;
+  if (seq < 0 || seq >= c->num_seqs) return fail(BPK_EINVAL, "seq %d out of range", seq);
+  if (n_new < 0) return fail(BPK_EINVAL, "n_new < 0");
+  if ((k_new == nullptr) != (v_new == nullptr))
+    return fail(BPK_EINVAL, "k_new and v_new must both be given or both be NULL");
+  const long long n0 = c->n_tokens[seq];
+  if (n0 + n_new > c->capacity)
+    return fail(BPK_ECAPACITY, "append of %lld tokens to %lld passes capacity %lld",
+                (long long)n_new, n0, (long long)c->capacity);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (k_new) {
+    rc = hip_status(bpk::launch_append_rows(g, seq, c->k_dtype, k_new, v_new, n0, n_new, c->k_rows,
+                                            c->v_rows, st),
+                    "append rows");
+    if (rc) return rc;
+  }
+  const long long b0 = n0 / BPK_BLOCK, b1 = (n0 + n_new) / BPK_BLOCK;
+  return hip_status(bpk::launch_encode(g, seq, c->k_dtype, c->k_rows, c->rot, c->planes,
+                                       c->scales, b0, b1 - b0, st),
+                    "encode");
+}
+
+int bpk_alloc_depth(const bpk_cache_t* c, const uint16_t* q, int32_t l0, int32_t l1,
+                    int32_t budget_planes, uint8_t* depth, float* q_basis, void* stream) {
+  bpk::Geom g;
+  int rc = check_cache(c, l0, l1, &g);
+  if (rc) return rc;
+  if (!q || !depth || !q_basis) return fail(BPK_EINVAL, "q, depth and q_basis must be non-NULL");
+  if (budget_planes < 0) return fail(BPK_EINVAL, "budget_planes < 0");
+  return hip_status(bpk::launch_alloc(g, q, c->chan_var, c->rot, budget_planes, depth, q_basis,
+                                      static_cast<hipStream_t>(stream)),
+                    "alloc_depth");
+}
+
+int bpk_scan_scores(const bpk_cache_t* c, const float* q_basis, const uint8_t* depth, int32_t l0,
+                    int32_t l1, float* scores, void* stream) {
+  bpk::Geom g;
+  int rc = check_cache(c, l0, l1, &g);
+  if (rc) return rc;
+  if (!q_basis || !depth || !scores)
+    return fail(BPK_EINVAL, "q_basis, depth and scores must be non-NULL");
+  return hip_status(bpk::launch_scan(g, q_basis, depth, c->planes, c->scales, scores,
+                                     static_cast<hipStream_t>(stream)),
+                    "scan_scores");
+}
+
+int bpk_select_topk(const bpk_cache_t* c, const float* scores, int32_t l0, int32_t l1, int32_t k,
+                    int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  bpk::Geom g;
+  int rc = check_cache(c, l0, l1, &g);
+  if (rc) return rc;
+  if (!scores || !idx) return fail(BPK_EINVAL, "scores and idx must be non-NULL");
+  rc = check_k(c, k);
+  if (rc) return rc;
+  return hip_status(bpk::launch_topk(g, scores, k, idx, static_cast<hipStream_t>(stream)),
+                    "select_topk");
+}
+
+int bpk_sparse_attend(const bpk_cache_t* c, const uint16_t* q, const int32_t* idx, int32_t l0,
+                      int32_t l1, int32_t k, float softmax_scale, float* out, void* ws,
+                      size_t ws_bytes, void* stream) {
+  bpk::Geom g;
+  int rc = check_cache(c, l0, l1, &g);
+  if (rc) return rc;
+  if (!q || !idx || !out) return fail(BPK_EINVAL, "q, idx and out must be non-NULL");
+  rc = check_k(c, k);
+  if (rc) return rc;
+  const size_t need = bpk::attend_ws_bytes(g, k);
+  if (!ws || ws_bytes < need)
+    return fail(BPK_EWORKSPACE, "workspace of %zu bytes < %zu needed", ws_bytes, need);
+  return hip_status(bpk::launch_attend(g, c->k_dtype, c->k_rows, c->v_rows, q, idx, k,
+                                       softmax_scale, out, ws, static_cast<hipStream_t>(stream)),
+                    "sparse_attend");
+}
+
+int bpk_decode_step(const bpk_cache_t* c, const uint16_t* q, int32_t l0, int32_t l1,
+                    int32_t budget_planes, int32_t k, float softmax_scale, float* out,
+                    uint8_t* depth_out, int32_t* idx_out, void* ws, size_t ws_bytes,
+                    void* stream) {
+  bpk::Geom g;
+  int rc = check_cache(c, l0, l1, &g);
+  if (rc) return rc;
+  if (!q || !out) return fail(BPK_EINVAL, "q and out must be non-NULL");
+  if (budget_planes < 0) return fail(BPK_EINVAL, "budget_planes < 0");
+  rc = check_k(c, k);
+  if (rc) return rc;
+  const DecodeWs w = decode_ws(g, k);
+  if (!ws || ws_bytes < w.total)
+    return fail(BPK_EWORKSPACE, "workspace of %zu bytes < %zu needed", ws_bytes, w.total);
+  char* base = static_cast<char*>(ws);
+  float* q_basis = reinterpret_cast<float*>(base + w.q_basis);
+  uint8_t* depth = depth_out ? depth_out : reinterpret_cast<uint8_t*>(base + w.depth);
+  float* scores = reinterpret_cast<float*>(base + w.scores);
+  int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(base + w.idx);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  rc = hip_status(bpk::launch_alloc(g, q, c->chan_var, c->rot, budget_planes, depth, q_basis, st),
+                  "decode_step/alloc");
+  if (rc) return rc;
+  rc = hip_status(bpk::launch_scan(g, q_basis, depth, c->planes, c->scales, scores, st),
+                  "decode_step/scan");
+  if (rc) return rc;
+  rc = hip_status(bpk::launch_topk(g, scores, k, idx, st), "decode_step/select");
+  if (rc) return rc;
+  return hip_status(bpk::launch_attend(g, c->k_dtype, c->k_rows, c->v_rows, q, idx, k,
+                                       softmax_scale, out, base + w.attend, st),
+                    "decode_step/attend");
+}
+
+}  // extern "C"

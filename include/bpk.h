@@ -1,0 +1,208 @@
+/*
+ * bpk.h -- C ABI of the MI355X (gfx950) bit-plane key-cache decode library.
+ *
+ * Top-k sparse decode attention over a 4-bit key cache stored as bit planes:
+ * a query chooses how many planes of each key channel to read (reverse
+ * water-filling of a plane budget), scans every key at those depths to rank
+ * it, and runs exact softmax attention only over each query head's winners.
+ *
+ * Sources (the Fathom page, a translation of arXiv 2609.17652, and the
+ * ReadKV explainer page), cited per entry point below by section.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every pointer is a DEVICE pointer owned by the caller, except where marked
+ *   HOST.  The library allocates nothing, keeps no state between calls and
+ *   never synchronises the host; every call is enqueued on `stream`
+ *   (a hipStream_t passed as void*, NULL = the null stream).  Outputs are valid
+ *   once the stream has reached the call.
+ * - A *unit* is one (sequence s, layer l, KV head h).  Cache arrays (rows,
+ *   planes, scales, chan_var) cover every unit: [S][L][H]..., unit index
+ *   (s * L + l) * H + h.  Entry points that take a layer range [l0, l1) work
+ *   on the units of every sequence and of those layers, and their per-call
+ *   arrays (q, q_basis, depth, scores, idx, out) cover only those:
+ *   [S][l1 - l0][H]..., unit index (s * (l1 - l0) + (l - l0)) * H + h.
+ * - Return value: BPK_OK (0) or a negative BPK_E* code.  All arguments are
+ *   validated before anything is enqueued, so a call that fails with
+ *   BPK_EINVAL / BPK_EUNSUPPORTED / BPK_EWORKSPACE / BPK_ECAPACITY has no
+ *   effect.  bpk_last_error() returns a thread-local message for the last
+ *   failing call of the calling thread.  No C++ exception crosses the ABI.
+ * - Supported shapes: head_dim == 128, group (query heads per KV head) in
+ *   {1, 2, 4, 8}, 1 <= num_seqs <= 64, capacity a positive multiple of 64.
+ */
+#ifndef BPK_H
+#define BPK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BPK_HEAD_DIM 128 /* channels per KV head */
+#define BPK_BLOCK 64     /* tokens per quantisation block (Fathom §3.2) */
+#define BPK_PLANES 4     /* bits per key code (Fathom §3.2) */
+#define BPK_MAX_SEQS 64
+#define BPK_MAX_K 4096   /* largest top-k per query head */
+#define BPK_MAX_SELECTED 8192 /* largest group * k */
+
+enum bpk_status {
+  BPK_OK = 0,
+  BPK_EINVAL = -1,       /* null pointer, bad range, k or budget out of range */
+  BPK_EUNSUPPORTED = -2, /* shape outside the supported set */
+  BPK_EWORKSPACE = -3,   /* workspace missing or smaller than bpk_workspace_bytes */
+  BPK_ECAPACITY = -4,    /* an append would pass the cache capacity */
+  BPK_EHIP = -5          /* a HIP launch failed; the message names the error */
+};
+
+enum bpk_dtype { BPK_F32 = 0, BPK_BF16 = 1 };
+
+enum bpk_op { BPK_OP_SELECT = 3, BPK_OP_ATTEND = 4, BPK_OP_DECODE = 5 };
+
+/*
+ * The cache: storage shared by every entry point.  All arrays are
+ * caller-allocated device memory except n_tokens (HOST).
+ *
+ * k_rows   [S][L][H][capacity][128]  key rows, fp32 or bf16 (k_dtype).
+ * v_rows   [S][L][H][capacity][128]  value rows, bf16 bit patterns.
+ * planes   [S][L][H][128][4][capacity/64] uint64.  Word (j, p, b) holds bit p
+ *          (p = 0 is the most significant bit, i.e. the sign) of the 4-bit
+ *          codes of channel j over the 64 tokens of block b; bit i of the word
+ *          belongs to token 64 b + i.  Channel-major, so the first t planes of
+ *          a channel are contiguous (Fathom §3.2).
+ * scales   [S][L][H][128][capacity/64] fp16 bit patterns, one per (channel,
+ *          block): the block's max |k| divided by 8 (Fathom §3.2).
+ * chan_var [S][L][H][128] fp32: the variance of each key channel in the scan
+ *          basis, used by the depth rule (Fathom §1, observation 1).
+ * rot      NULL for the raw channel basis, or [L][H][128][128] fp32 row-major
+ *          orthogonal R per (layer, head): keys and queries are scanned in the
+ *          basis z = R^T x (the KLT basis of Fathom §1, contributions).
+ * n_tokens HOST [S]: tokens present in each sequence, including the tokens of
+ *          an open (incomplete) trailing block, which have rows but no planes.
+ */
+typedef struct bpk_cache {
+  int32_t num_seqs;
+  int32_t num_layers;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t group;
+  int32_t k_dtype;
+  int64_t capacity;
+  const int64_t* n_tokens; /* HOST */
+  void* k_rows;
+  uint16_t* v_rows;
+  uint64_t* planes;
+  uint16_t* scales;
+  const float* chan_var;
+  const float* rot;
+} bpk_cache_t;
+
+/*
+ * Append n_new tokens to sequence `seq` of every (layer, KV head) and encode
+ * the 64-token blocks the append completes (Fathom §3.2; planes are
+ * append-only and never re-encoded, ReadKV §6.1).
+ *
+ * k_new [L][H][n_new][128] in the cache's k_dtype, v_new [L][H][n_new][128]
+ * bf16: copied to rows n_tokens[seq] .. n_tokens[seq] + n_new - 1.  If both
+ * are NULL the rows are taken to be in place already.  Each completed block
+ * gets, per channel j, the scale s = fp16_rne(max|k| / 8) (saturated at
+ * 65504) and the codes c = clip(floor(k / s), -8, 7) + 8 with the exact real
+ * floor (c = 8 when s = 0), packed into the four plane words.  With rot set,
+ * k is first mapped to z = R^T k (fp64 sum over d ascending, rounded to fp32).
+ * The caller advances n_tokens[seq] by n_new afterwards.
+ * Errors: BPK_EINVAL (seq out of range, n_new < 0, only one of k_new / v_new
+ * given), BPK_ECAPACITY (n_tokens[seq] + n_new > capacity).
+ */
+int bpk_encode_append(const bpk_cache_t* cache, int32_t seq, const void* k_new,
+                      const uint16_t* v_new, int64_t n_new, void* stream);
+
+/*
+ * Per-query depth allocation (Fathom §1 observation 1 and §3; ReadKV §5.2,
+ * §5.4): one wavefront per unit.
+ *
+ * q [S][nl][H][G][128] bf16 (nl = l1 - l0).  Writes q_basis [S][nl][H][G][128]
+ * fp32 (the query in the scan basis: q itself, or R^T q with rot set) and
+ * depth [S][nl][H][128] uint8.  g_j = chan_var_j * sum_h q_hj^2 (fp32, h ascending);
+ * the budget of min(budget_planes, 512) planes goes to the (channel, plane)
+ * candidates of largest value g_j * 4^-t, ties to the lower channel then the
+ * lower plane; depth_j = number of channel j's candidates taken.
+ * Errors: BPK_EINVAL (bad layer range, budget_planes < 0, null pointer).
+ */
+int bpk_alloc_depth(const bpk_cache_t* cache, const uint16_t* q, int32_t l0, int32_t l1,
+                    int32_t budget_planes, uint8_t* depth, float* q_basis, void* stream);
+
+/*
+ * Key scan (Fathom §1, §3.2): approximate scores of every token of every
+ * complete block, reading only planes p < depth_j of each channel and the
+ * scales of channels with depth_j >= 1:
+ *   score[h][i] = sum_j q_basis_hj * s_bj * m_ij,
+ *   m_ij = (prefix_ij + 1/2) * 2^(4 - t_j) - 8   (t_j >= 1), 0 (t_j = 0),
+ * where prefix_ij is the t_j-bit prefix of the token's code.
+ * q_basis and depth as written by bpk_alloc_depth.
+ * scores [S][nl][H][G][capacity] fp32; entries at or past 64 * floor(n/64) are
+ * not written.  Errors: BPK_EINVAL.
+ */
+int bpk_scan_scores(const bpk_cache_t* cache, const float* q_basis, const uint8_t* depth,
+                    int32_t l0, int32_t l1, float* scores, void* stream);
+
+/*
+ * Per-query-head top-k (Fathom §2, "Top-k decoding"): the first 4 and the
+ * last W tokens are always kept, W = max(32, n mod 64) (the open trailing
+ * block has no planes, so it is kept whole); the other k - 4 - W are the
+ * highest scores among tokens [4, n - W), equal scores to the lower index.
+ * If n <= k all n tokens are kept.  scores as written by bpk_scan_scores.
+ * idx [S][nl][H][G][k] int32: the min(n, k)
+ * selected token indices in ascending order, then -1 padding.
+ * ws may be NULL (needs 0 bytes).
+ * Errors: BPK_EINVAL (k < 1, k > BPK_MAX_K, or n > k with k < 4 + W).
+ */
+int bpk_select_topk(const bpk_cache_t* cache, const float* scores, int32_t l0, int32_t l1,
+                    int32_t k, int32_t* idx, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Exact attention over each query head's selected rows (Fathom §1, §2): the
+ * union of the G heads' index sets is fetched once per unit, then for each
+ * head h, out_h = sum_i softmax_i(softmax_scale * q_h . K_i) V_i over its own
+ * set, accumulated in fp32 from the bf16 (or fp32) rows.  q is bf16 in the
+ * model basis, [S][nl][H][G][128]; idx as written by
+ * bpk_select_topk (entries outside [0, n) are skipped, so -1 padding is
+ * harmless); out [S][nl][H][G][128] fp32 (zero for a head with no rows).
+ * ws: at least bpk_workspace_bytes(cache, BPK_OP_ATTEND, l0, l1, k) bytes.
+ * Errors: BPK_EINVAL, BPK_EWORKSPACE.
+ */
+int bpk_sparse_attend(const bpk_cache_t* cache, const uint16_t* q, const int32_t* idx,
+                      int32_t l0, int32_t l1, int32_t k, float softmax_scale, float* out,
+                      void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * One decode step over layers [l0, l1) of every sequence: alloc_depth ->
+ * scan_scores -> select_topk -> sparse_attend, all enqueued on `stream`,
+ * the cost model of Fathom §3.1 (Eq. 1) without the weight term.
+ * q [S][nl][H][G][128] bf16, out [S][nl][H][G][128] fp32.
+ * depth_out ([S][nl][H][128]) and idx_out ([S][nl][H][G][k]) are optional
+ * (NULL: kept in the workspace).  ws: at least
+ * bpk_workspace_bytes(cache, BPK_OP_DECODE, l0, l1, k) bytes.
+ * Errors: those of the four stages, BPK_EWORKSPACE.
+ */
+int bpk_decode_step(const bpk_cache_t* cache, const uint16_t* q, int32_t l0, int32_t l1,
+                    int32_t budget_planes, int32_t k, float softmax_scale, float* out,
+                    uint8_t* depth_out, int32_t* idx_out, void* ws, size_t ws_bytes,
+                    void* stream);
+
+/*
+ * Workspace bytes an entry point needs for layers [l0, l1) and top-k k
+ * (op = BPK_OP_SELECT, BPK_OP_ATTEND or BPK_OP_DECODE).  Returns 0 for an
+ * invalid cache or op.
+ */
+size_t bpk_workspace_bytes(const bpk_cache_t* cache, int32_t op, int32_t l0, int32_t l1,
+                           int32_t k);
+
+/* Message of the calling thread's last failing call ("" if none). */
+const char* bpk_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BPK_H */

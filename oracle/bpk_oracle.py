@@ -289,12 +289,15 @@ def attend(q: np.ndarray, k_rows: np.ndarray, v_rows: np.ndarray, idx: np.ndarra
 
     [Fathom §2] methods are judged by exact attention restricted to their
     selected set: softmax(q K^T * scale) over S_h, then the weighted sum of
-    the V rows.  ``idx`` entries < 0 are padding and ignored.
+    the V rows.  ``idx`` entries < 0 are padding and ignored; a head with no
+    selected row (an empty sequence) outputs zeros.
     """
     q = np.asarray(q, dtype=np.float64)
     out = np.zeros((q.shape[0], v_rows.shape[1]), dtype=np.float64)
     for h in range(q.shape[0]):
         sel = idx[h][idx[h] >= 0]
+        if len(sel) == 0:
+            continue
         logits = (k_rows[sel].astype(np.float64) @ q[h]) * scale
         p = np.exp(logits - logits.max())
         p /= p.sum()
