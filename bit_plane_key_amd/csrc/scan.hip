@@ -1,162 +1,431 @@
 // Prefix-plane key scan (Fathom §1, §3.2): approximate scores of every key of
-// every complete block, reading only planes p < t_j of each channel and the
-// block scales of the channels that are read at all.
+// every complete block, reading only planes p < t_j of each read channel and
+// the fp16 block scales of those channels.
 //
-// Work split: one workgroup (4 wavefronts) per (unit, chunk of CB blocks).
-// The workgroup stages, in LDS, the compacted list of read channels, the
-// chunk's plane words (each (channel, plane) row of CB words is one contiguous
-// CB*8-byte read) and, per (block, channel, head), the coefficient
-// q_hj * s_bj * 2^(4-t_j) plus a per-(block, head) constant.  Then each
-// wavefront scores whole 64-token blocks, lane i <-> token i: the prefix code
-// of a channel is assembled from bit i of its plane words (Horner), converted
-// to fp32 and accumulated into G per-head scores:
-//   score_h = sum_j coef_bjh * prefix_ij + const_bh,
-//   const_bh = sum_j q_hj s_bj (2^(3-t_j) - 8) = sum_j coef_bjh (1/2 - 2^(t_j-1)),
-// which is sum_j q_hj s_bj ((prefix_ij + 1/2) 2^(4-t_j) - 8) regrouped.
+// Per unit the score of token i for query head h is
+//   s_hat = sum_j q_hj s_bj m_ij,  m = (c' + 1/2) 2^(4-t) - 8 = z 2^(4-t) + 2^(3-t)
+// with c' the t-bit prefix code and z = c' - 2^(t-1) in [-8, 7].  Writing
+// A_hj = q_hj s_bj 2^(4-t_j) gives s_hat = sum_j A_hj z_ij + sum_j A_hj / 2.
+//
+// Mapping onto gfx950:
+// * A workgroup (4 wavefronts) owns a range of blocks of one unit and walks it
+//   in steps of 16 blocks.  The read channels are cut into segments of whole
+//   8-channel chunks holding at most 128 plane rows, so the LDS footprint is
+//   fixed (~36 KB) whatever the depth vector.  Per (step, segment) the
+//   workgroup stages into LDS, with coalesced reads, the segment's plane words
+//   (rows of 16 consecutive blocks, split into 32-bit halves, the sign plane
+//   complemented) and, per (block, channel, head), A_hj split into bf16 hi + lo
+//   parts plus per-wavefront partial sums of the per-(block, head) constant.
+//   Every global load of a (step, segment) is issued before the first is
+//   used, and several resident workgroups per CU overlap one step's loads
+//   with another's arithmetic.
+// * Wavefront w scores blocks 4w .. 4w+3 of the step, lane i <-> token i.  For
+//   a read channel a lane reads its half-word of each plane for the four
+//   blocks with one 16-byte LDS read per plane and assembles z by a Horner
+//   chain of bit-field extracts (a signed extract of the complemented sign
+//   bit gives b0 - 1).
+// * The G-head contraction runs on the matrix cores: v_mfma_f32_16x16x32_bf16
+//   with B = 8 channels' z values of the lane's token (exact in bf16) and A
+//   block-diagonal over the four 16-lane token groups (row 4g + h of A is
+//   nonzero only in token group g's k-range), so D row 4g + h, column n is
+//   head h's partial score of token 16g + n and each lane ends with the G
+//   scores of its own token.  The hi + lo split of A keeps each term within
+//   ~2^-17 of its exact value.
 #include "bpk_internal.h"
 
 namespace bpk {
 namespace {
 
-struct ScanArgs {
-  Geom g;
-  const float* q_basis;
-  const uint8_t* depth;
-  const uint64_t* planes;
-  const uint16_t* scales;
-  float* scores;
-};
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float floatx4;
 
 constexpr int SCAN_THREADS = 256;
 constexpr int SCAN_WAVES = SCAN_THREADS / 64;
+constexpr int NB = 4;                 // blocks per wavefront per step
+constexpr int GB = NB * SCAN_WAVES;   // blocks per workgroup step
+constexpr int SEG_ROWS = 128;         // plane rows staged per segment
+constexpr int SEG_CHUNKS = 8;         // 8-channel chunks per segment
+constexpr int MAX_SEGS = D / 8;       // one chunk per segment at worst
 
-template <int G, int CB>
-struct ScanSmem {
-  uint64_t words[NP * D][CB];   // staged plane words, row r = (channel c, plane p)
-  float coef[CB][D][G];         // q_hj * s_bj * 2^(4 - t_j) of read channel c
-  float cst[CB][G];
-  int scan_buf[D];
-  uint8_t sel_j[D];
-  uint8_t sel_t[D];
-  uint16_t sel_pb[D];           // first staged row of read channel c
-  uint8_t row_c[NP * D];        // staged row -> read channel
-  uint8_t row_p[NP * D];        // staged row -> plane
-  int n_read, n_rows;
+enum ScanMode { SCAN_FULL = 0 };
+
+struct ScanArgs {
+  Geom g;
+  const float* __restrict__ q_basis;
+  const uint8_t* __restrict__ depth;
+  const uint64_t* __restrict__ planes;
+  const uint16_t* __restrict__ scales;
+  float* __restrict__ scores;
+  int wg_blocks;  // blocks per workgroup (multiple of GB)
 };
 
-template <int G, int CB>
+__device__ __forceinline__ uint16_t bf16_rne_bits(float x) {
+  const uint32_t b = __float_as_uint(x);
+  return (uint16_t)((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16);
+}
+
+// 128-bit LDS accesses must be 16-byte aligned (misaligned ones stall)
+template <int G>
+struct ScanSmem {
+  static constexpr int HG = (G + 3) / 4;  // head groups of 4 (MFMA rows)
+  int scan_buf[D];
+  uint8_t sel_j[D];
+  uint8_t sel_t[D];                // depth of read channel c (0 past the last)
+  uint16_t sel_pb[D];              // first plane row of read channel c
+  int counts[4];                   // read channels, planes, segments
+  int seg_c[MAX_SEGS + 1];         // first read channel of each segment
+  uint64_t chan_sc[D];             // offset of the scales of read channel c; its plane 0
+                                   // starts at word 4 * chan_sc[c] (planes [D][4][nbcap])
+  uint8_t row_c[NP * D];           // plane row -> read channel
+  uint8_t row_p[NP * D];           // plane row -> plane
+  alignas(16) float qc[D * G];     // q_hj * 2^(4 - t_j) of read channel c
+  alignas(16) uint32_t words[SEG_ROWS + 6][2][GB];  // [row][half][block] (+6 rows of slack)
+  // A hi/lo per block: [chunk][hg][part][h][ch] bf16, rows padded by 16 bytes so
+  // that the 16 blocks of a staging write land in different LDS banks
+  static constexpr int ASTRIDE = SEG_CHUNKS * HG * 2 * 4 * 8 + 8;
+  alignas(16) uint16_t atab[GB][ASTRIDE];
+  alignas(16) float cpart[SCAN_WAVES][GB][G];  // per-wavefront partial sums of A / 2
+};
+
+template <int G, int MODE>
 __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(ScanArgs a) {
-  __shared__ ScanSmem<G, CB> sm;
+  using SM = ScanSmem<G>;
+  constexpr int HG = SM::HG;
+  // offset of the 8 channels of (chunk k, head group hg, part, head h) in a block's A row
+  auto a_index = [](int k, int hg, int part, int h) { return (((k * HG + hg) * 2 + part) * 4 + h) * 8; };
+  __shared__ __attribute__((aligned(16))) SM sm;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int u = blockIdx.y;
   const long long gu = a.g.global_unit(u);
   const long long n = a.g.n[a.g.seq_of(u)];
   const long long nb = n / BLK;
-  const long long blk0 = (long long)blockIdx.x * CB;
-  if (blk0 >= nb) return;
-  const int nblk = (int)((nb - blk0) < CB ? (nb - blk0) : CB);
+  const long long wb0 = (long long)blockIdx.x * a.wg_blocks;
+  if (wb0 >= nb) return;
+  const long long wb1 = (wb0 + a.wg_blocks) < nb ? (wb0 + a.wg_blocks) : nb;
   const long long nbcap = a.g.nbcap();
-  const int tid = threadIdx.x;
 
-  // 1. compact the read channels (t_j >= 1) and number their plane rows
-  int tj = 0, flag = 0;
+  // ---- plan: compact the read channels (t_j >= 1) in order of j ----
+  int tj = 0;
+  if (tid < D) sm.sel_t[tid] = 0;
   if (tid < D) {
     tj = a.depth[(long long)u * D + tid];
     tj = tj > NP ? NP : tj;
-    flag = tj > 0;
-    sm.scan_buf[tid] = (flag << 16) | tj;  // two counters in one int
+    sm.scan_buf[tid] = (1 << 16) * (tj > 0) + tj;  // (channels, planes) counters
   }
   __syncthreads();
-  for (int off = 1; off < D; off <<= 1) {  // inclusive Hillis-Steele scan
+  for (int off = 1; off < D; off <<= 1) {
     int v = 0;
     if (tid < D && tid >= off) v = sm.scan_buf[tid - off];
     __syncthreads();
     if (tid < D) sm.scan_buf[tid] += v;
     __syncthreads();
   }
-  if (tid < D && flag) {
-    const int incl = sm.scan_buf[tid];
-    const int c = (incl >> 16) - 1;
-    const int pb = (incl & 0xffff) - tj;
+  __syncthreads();  // sel_t cleared before it is filled
+  if (tid < D && tj > 0) {
+    const int c = (sm.scan_buf[tid] >> 16) - 1;
     sm.sel_j[c] = (uint8_t)tid;
     sm.sel_t[c] = (uint8_t)tj;
+    const int pb = (sm.scan_buf[tid] & 0xFFFF) - tj;
     sm.sel_pb[c] = (uint16_t)pb;
+    sm.chan_sc[c] = (uint64_t)(gu * D + tid) * (uint64_t)nbcap;
     for (int p = 0; p < tj; ++p) {
       sm.row_c[pb + p] = (uint8_t)c;
       sm.row_p[pb + p] = (uint8_t)p;
     }
-  }
-  if (tid == D - 1) {
-    sm.n_read = sm.scan_buf[tid] >> 16;
-    sm.n_rows = sm.scan_buf[tid] & 0xffff;
-  }
-  __syncthreads();
-  const int n_read = sm.n_read;
-  const int n_rows = sm.n_rows;
-
-  // 2. stage plane words: row r of channel sel_j[c], plane p, blocks blk0..
-  for (int e = tid; e < n_rows * CB; e += SCAN_THREADS) {
-    const int r = e / CB, b = e % CB;
-    uint64_t w = 0;
-    if (b < nblk) {
-      const int j = sm.sel_j[sm.row_c[r]];
-      w = a.planes[((gu * D + j) * NP + sm.row_p[r]) * nbcap + blk0 + b];
-    }
-    sm.words[r][b] = w;
-  }
-  // 3. per-(block, read channel, head) coefficients
-  const float* qb = a.q_basis + (long long)u * G * D;
-  for (int e = tid; e < n_read * CB; e += SCAN_THREADS) {
-    const int c = e / CB, b = e % CB;
-    const int j = sm.sel_j[c], t = sm.sel_t[c];
-    float s = 0.f;
-    if (b < nblk) s = (float)__builtin_bit_cast(_Float16, a.scales[(gu * D + j) * nbcap + blk0 + b]);
-    const float w = s * (float)(1 << (NP - t));
+    const float w = (float)(1 << (NP - tj));
 #pragma unroll
-    for (int h = 0; h < G; ++h) sm.coef[b][c][h] = qb[h * D + j] * w;
+    for (int h = 0; h < G; ++h)
+      sm.qc[c * G + h] = a.q_basis[((long long)u * G + h) * D + tid] * w;
   }
   __syncthreads();
-  if (tid < CB * G) {
-    // q_hj s_bj (2^(3-t) - 8) = coef_bjh * (1/2 - 2^(t-1))
-    const int b = tid / G, h = tid % G;
-    float acc = 0.f;
-    for (int c = 0; c < n_read; ++c)
-      acc = fmaf(sm.coef[b][c][h], 0.5f - (float)(1 << (sm.sel_t[c] - 1)), acc);
-    sm.cst[b][h] = acc;
-  }
-  __syncthreads();
-
-  // 4. score: wavefront w takes blocks w, w + 4, ...; lane <-> token
-  const int wave = tid >> 6, lane = tid & 63;
-  const int half = lane >> 5, bitpos = lane & 31;
-  float* out = a.scores + (long long)u * G * a.g.cap;
-  for (int b = wave; b < nblk; b += SCAN_WAVES) {
-    float acc[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) acc[h] = sm.cst[b][h];
-    for (int c = 0; c < n_read; ++c) {
-      const int t = sm.sel_t[c], pb = sm.sel_pb[c];
-      uint32_t code = 0;
-      for (int p = 0; p < t; ++p) {
-        const uint32_t wh = reinterpret_cast<const uint32_t*>(&sm.words[pb + p][b])[half];
-        code = (code << 1) | ((wh >> bitpos) & 1u);
+  if (tid == 0) {
+    // segments: whole chunks, at most SEG_CHUNKS chunks and SEG_ROWS rows
+    const int C = sm.scan_buf[D - 1] >> 16;
+    const int P = sm.scan_buf[D - 1] & 0xFFFF;
+    int ns = 0, c = 0;
+    while (c < C) {
+      sm.seg_c[ns++] = c;
+      int rows = 0, chunks = 0;
+      while (c < C && chunks < SEG_CHUNKS) {
+        const int ce = (c + 8) < C ? (c + 8) : C;
+        const int r = (int)sm.sel_pb[ce - 1] + sm.sel_t[ce - 1] - sm.sel_pb[c];
+        if (chunks > 0 && rows + r > SEG_ROWS) break;
+        rows += r;
+        c = ce;
+        ++chunks;
       }
-      const float fc = (float)code;
-#pragma unroll
-      for (int h = 0; h < G; ++h) acc[h] = fmaf(sm.coef[b][c][h], fc, acc[h]);
     }
-    const long long tok = (blk0 + b) * BLK + lane;
+    sm.seg_c[ns] = C;
+    sm.counts[0] = C;
+    sm.counts[1] = P;
+    sm.counts[2] = ns;
+  }
+  __syncthreads();
+  const int C = sm.counts[0];
+  const int nseg = sm.counts[2];
+
+  // rows SEG_ROWS+2 .. +5 stay zero: a padding slot reads them and gets z = 0
+  if (tid < 8 * GB) (&sm.words[SEG_ROWS + 2][0][0])[tid] = 0u;
+  // A-operand ownership: lane l holds row 4*(l/16) + (l%4) of a head group,
+  // in k-group l/16, only when (l%16)/4 == l/16 (block-diagonal).
+  const bool a_active = ((lane & 15) >> 2) == (lane >> 4) && (lane & 3) < (G < 4 ? G : 4);
+  const int a_hh = lane & 3;
+  const int half = lane >> 5, bitpos = lane & 31;
+  const int wb = NB * wave;
+
+  // ---- tasks = (16-block step, segment); the loads of task i+1 are in flight
+  // while task i is scored ----
+  const int nsteps = (int)((wb1 - wb0 + GB - 1) / GB);
+  const int ntask = nsteps * nseg;
+  constexpr int PER = SEG_ROWS * (GB / 2) / SCAN_THREADS;   // word pairs per thread
+  constexpr int PERS = SEG_CHUNKS * 8 * GB / SCAN_THREADS;  // scales per thread
+  const int sb = tid % GB;  // block of this thread's scales (same for every i)
+  uint64_t w[PER][2];
+  float sv[PERS];
+  auto issue_loads = [&](int task) {
+    const long long g0 = wb0 + (long long)(task / nseg) * GB;
+    const int sg = task % nseg;
+    const int gblk = (wb1 - g0) < GB ? (int)(wb1 - g0) : GB;
+    const int cs0 = sm.seg_c[sg], cs1 = sm.seg_c[sg + 1];
+    const int rbase = sm.sel_pb[cs0];
+    const int nrows = (int)sm.sel_pb[cs1 - 1] + sm.sel_t[cs1 - 1] - rbase;
 #pragma unroll
-    for (int h = 0; h < G; ++h) out[h * a.g.cap + tok] = acc[h];
+    for (int i = 0; i < PER; ++i) {
+      const int e = tid + i * SCAN_THREADS;
+      const int rr = e / (GB / 2), b2 = 2 * (e % (GB / 2));
+      w[i][0] = 0;
+      w[i][1] = 0;
+      if (rr < nrows) {
+        const int r = rbase + rr;
+        const int c = sm.row_c[r], p = sm.row_p[r];
+        const uint64_t* src = a.planes + NP * sm.chan_sc[c] + (uint64_t)p * nbcap + g0 + b2;
+        if (b2 + 1 < gblk) {  // rows are 8-byte aligned only
+          w[i][0] = src[0];
+          w[i][1] = src[1];
+        } else if (b2 < gblk) {
+          w[i][0] = src[0];
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < PERS; ++i) {
+      const int c = cs0 + (tid + i * SCAN_THREADS) / GB;
+      sv[i] = 0.f;
+      if (c < cs1 && sb < gblk)
+        sv[i] = (float)__builtin_bit_cast(_Float16, a.scales[sm.chan_sc[c] + g0 + sb]);
+    }
+  };
+
+  if (nseg == 0) {  // nothing is read: every score is 0
+    for (long long e = tid; e < (wb1 - wb0) * BLK; e += SCAN_THREADS)
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+        if constexpr (MODE == SCAN_FULL)
+          a.scores[((long long)u * G + h) * a.g.cap + wb0 * BLK + e] = 0.f;
+    return;
+  }
+  floatx4 acc[NB][HG];
+  issue_loads(0);
+  for (int task = 0; task < ntask; ++task) {
+    const long long g0 = wb0 + (long long)(task / nseg) * GB;
+    const int sg = task % nseg;
+    const int gblk = (wb1 - g0) < GB ? (int)(wb1 - g0) : GB;
+    if (sg == 0) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int hg = 0; hg < HG; ++hg) acc[b][hg] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+    {
+      const int cs0 = sm.seg_c[sg], cs1 = sm.seg_c[sg + 1];
+      const int rbase = sm.sel_pb[cs0];
+      const int nrows = (int)sm.sel_pb[cs1 - 1] + sm.sel_t[cs1 - 1] - rbase;
+      const int nck = (cs1 - cs0 + 7) >> 3;
+      __syncthreads();  // the previous task's tables are no longer read
+
+      // ---- words -> LDS (the sign plane complemented) ----
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int e = tid + i * SCAN_THREADS;
+        const int rr = e / (GB / 2), b2 = 2 * (e % (GB / 2));
+        if (rr < nrows) {
+          if (sm.row_p[rbase + rr] == 0) {
+            w[i][0] = ~w[i][0];
+            w[i][1] = ~w[i][1];
+          }
+          *reinterpret_cast<uint2*>(&sm.words[rr][0][b2]) =
+              make_uint2((uint32_t)w[i][0], (uint32_t)w[i][1]);
+          *reinterpret_cast<uint2*>(&sm.words[rr][1][b2]) =
+              make_uint2((uint32_t)(w[i][0] >> 32), (uint32_t)(w[i][1] >> 32));
+        }
+      }
+      // ---- A = q_hj s_bj 2^(4-t_j) as bf16 hi + lo, partial sums of A / 2 ----
+      float part[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) part[h] = 0.f;
+#pragma unroll
+      for (int i = 0; i < PERS; ++i) {
+        const int cl = (tid + i * SCAN_THREADS) / GB;
+        if (cl < nck * 8) {
+          const int c = cs0 + cl;
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            const float x = c < cs1 ? sm.qc[c * G + h] * sv[i] : 0.f;
+            part[h] += 0.5f * x;
+            const uint16_t hi = bf16_rne_bits(x);
+            const uint16_t lo = bf16_rne_bits(x - __uint_as_float((uint32_t)hi << 16));
+            sm.atab[sb][a_index(cl >> 3, h >> 2, 0, h & 3) + (cl & 7)] = hi;
+            sm.atab[sb][a_index(cl >> 3, h >> 2, 1, h & 3) + (cl & 7)] = lo;
+          }
+        }
+      }
+      // lanes l, l+16, l+32, l+48 share a block: fixed-order reduction
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        part[h] += __shfl_xor(part[h], 16);
+        part[h] += __shfl_xor(part[h], 32);
+      }
+      if (lane < GB) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) sm.cpart[wave][lane][h] = part[h];
+      }
+      __syncthreads();
+      if (task + 1 < ntask) issue_loads(task + 1);  // in flight during the scoring below
+
+      // ---- score the segment: wavefront takes blocks wb .. wb+3 of the step ----
+      if (wb < gblk) {
+        // the constant sum_j A_hj / 2 enters the accumulator of (token, head 4hg + r)
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+          for (int hg = 0; hg < HG; ++hg)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int h = 4 * hg + r;
+              if (h < G) {
+                float cs = 0.f;
+#pragma unroll
+                for (int ww = 0; ww < SCAN_WAVES; ++ww) cs += sm.cpart[ww][wb + b][h];
+                acc[b][hg][r] += cs;
+              }
+            }
+
+        for (int kl = 0; kl < nck; ++kl) {
+          const int cb = cs0 + 8 * kl;
+          // the chunk's depths and first rows, wave-uniform
+          const uint32_t t03 = __builtin_amdgcn_readfirstlane(*reinterpret_cast<const uint32_t*>(&sm.sel_t[cb]));
+          const uint32_t t47 = __builtin_amdgcn_readfirstlane(*reinterpret_cast<const uint32_t*>(&sm.sel_t[cb + 4]));
+          uint32_t pbw[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            pbw[i] = __builtin_amdgcn_readfirstlane(*reinterpret_cast<const uint32_t*>(&sm.sel_pb[cb + 2 * i]));
+          uint32_t bw[NB][4];
+#pragma unroll
+          for (int cc = 0; cc < 8; ++cc) {
+            const int t = (int)(((cc < 4 ? t03 : t47) >> (8 * (cc & 3))) & 0xFFu);
+            // channels past the segment read the zero rows (A = 0 there)
+            const int rr = t > 0 ? (int)((pbw[cc >> 1] >> (16 * (cc & 1))) & 0xFFFFu) - rbase
+                                 : SEG_ROWS + 2;
+            const uint32_t* rowp = &sm.words[rr][half][wb];
+            // all four rows at once (rows past t are not used)
+            const uint4 w0 = *reinterpret_cast<const uint4*>(rowp);
+            const uint4 w1 = *reinterpret_cast<const uint4*>(rowp + 2 * GB);
+            const uint4 w2 = *reinterpret_cast<const uint4*>(rowp + 4 * GB);
+            const uint4 w3 = *reinterpret_cast<const uint4*>(rowp + 6 * GB);
+            // plane 0 (complemented sign): z = b0 - 1, then z = 2 z + b_p
+            int z[NB];
+            z[0] = __builtin_amdgcn_sbfe(w0.x, bitpos, 1);
+            z[1] = __builtin_amdgcn_sbfe(w0.y, bitpos, 1);
+            z[2] = __builtin_amdgcn_sbfe(w0.z, bitpos, 1);
+            z[3] = __builtin_amdgcn_sbfe(w0.w, bitpos, 1);
+            if (t >= 2) {
+              z[0] = (z[0] << 1) | __builtin_amdgcn_ubfe(w1.x, bitpos, 1);
+              z[1] = (z[1] << 1) | __builtin_amdgcn_ubfe(w1.y, bitpos, 1);
+              z[2] = (z[2] << 1) | __builtin_amdgcn_ubfe(w1.z, bitpos, 1);
+              z[3] = (z[3] << 1) | __builtin_amdgcn_ubfe(w1.w, bitpos, 1);
+            }
+            if (t >= 3) {
+              z[0] = (z[0] << 1) | __builtin_amdgcn_ubfe(w2.x, bitpos, 1);
+              z[1] = (z[1] << 1) | __builtin_amdgcn_ubfe(w2.y, bitpos, 1);
+              z[2] = (z[2] << 1) | __builtin_amdgcn_ubfe(w2.z, bitpos, 1);
+              z[3] = (z[3] << 1) | __builtin_amdgcn_ubfe(w2.w, bitpos, 1);
+            }
+            if (t >= 4) {
+              z[0] = (z[0] << 1) | __builtin_amdgcn_ubfe(w3.x, bitpos, 1);
+              z[1] = (z[1] << 1) | __builtin_amdgcn_ubfe(w3.y, bitpos, 1);
+              z[2] = (z[2] << 1) | __builtin_amdgcn_ubfe(w3.z, bitpos, 1);
+              z[3] = (z[3] << 1) | __builtin_amdgcn_ubfe(w3.w, bitpos, 1);
+            }
+            // bf16 of z (exact): the high half of its fp32 value
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+              const uint32_t zb = __float_as_uint((float)z[b]) >> 16;
+              if (cc & 1)
+                bw[b][cc >> 1] |= zb << 16;
+              else
+                bw[b][cc >> 1] = zb;
+            }
+          }
+#pragma unroll
+          for (int b = 0; b < NB; ++b) {
+            bf16x8 bv;
+            __builtin_memcpy(&bv, bw[b], 16);
+#pragma unroll
+            for (int hg = 0; hg < HG; ++hg) {
+              bf16x8 ahi, alo;
+              uint32_t z4[4] = {0u, 0u, 0u, 0u};
+              __builtin_memcpy(&ahi, z4, 16);
+              __builtin_memcpy(&alo, z4, 16);
+              if (a_active) {
+                ahi = *reinterpret_cast<const bf16x8*>(&sm.atab[wb + b][a_index(kl, hg, 0, a_hh)]);
+                alo = *reinterpret_cast<const bf16x8*>(&sm.atab[wb + b][a_index(kl, hg, 1, a_hh)]);
+              }
+              acc[b][hg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, bv, acc[b][hg], 0, 0, 0);
+              acc[b][hg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, bv, acc[b][hg], 0, 0, 0);
+            }
+          }
+        }
+      }
+    }
+
+    // ---- epilogue after the last segment: lane <-> token, acc row r <-> head 4*hg + r ----
+    if (sg == nseg - 1 && wb < gblk) {
+      const int nblk = (gblk - wb) < NB ? (gblk - wb) : NB;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        if (b >= nblk) break;
+        const long long tok = (g0 + wb + b) * BLK + lane;
+#pragma unroll
+        for (int hg = 0; hg < HG; ++hg)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int h = 4 * hg + r;
+            if (h < G) {
+              const float s = acc[b][hg][r];
+              if constexpr (MODE == SCAN_FULL)
+                a.scores[((long long)u * G + h) * a.g.cap + tok] = s;
+            }
+          }
+      }
+    }
   }
 }
 
-template <int G, int CB>
-void launch_gc(const ScanArgs& a, hipStream_t st) {
+template <int G, int MODE>
+hipError_t launch_gm(const ScanArgs& a0, hipStream_t st) {
+  ScanArgs a = a0;
   long long maxnb = 0;
   for (int s = 0; s < a.g.S; ++s) maxnb = a.g.n[s] / BLK > maxnb ? a.g.n[s] / BLK : maxnb;
-  if (maxnb == 0) return;
-  dim3 grid((unsigned)((maxnb + CB - 1) / CB), (unsigned)a.g.units());
-  scan_kernel<G, CB><<<grid, SCAN_THREADS, 0, st>>>(a);
+  if (maxnb == 0) return hipSuccess;
+  const long long total = maxnb * a.g.units();
+  int wb = GB;
+  while (wb < 256 && total / (2 * wb) >= 4096) wb *= 2;
+  a.wg_blocks = wb;
+  dim3 grid((unsigned)((maxnb + wb - 1) / wb), (unsigned)a.g.units());
+  scan_kernel<G, MODE><<<grid, SCAN_THREADS, 0, st>>>(a);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -164,15 +433,14 @@ void launch_gc(const ScanArgs& a, hipStream_t st) {
 hipError_t launch_scan(const Geom& g, const float* q_basis, const uint8_t* depth,
                        const uint64_t* planes, const uint16_t* scales, float* scores,
                        hipStream_t st) {
-  ScanArgs a{g, q_basis, depth, planes, scales, scores};
+  ScanArgs a{g, q_basis, depth, planes, scales, scores, 0};
   switch (g.G) {
-    case 1: launch_gc<1, 8>(a, st); break;
-    case 2: launch_gc<2, 8>(a, st); break;
-    case 4: launch_gc<4, 8>(a, st); break;
-    case 8: launch_gc<8, 4>(a, st); break;
+    case 1: return launch_gm<1, SCAN_FULL>(a, st);
+    case 2: return launch_gm<2, SCAN_FULL>(a, st);
+    case 4: return launch_gm<4, SCAN_FULL>(a, st);
+    case 8: return launch_gm<8, SCAN_FULL>(a, st);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 }  // namespace bpk
