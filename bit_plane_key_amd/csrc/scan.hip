@@ -19,6 +19,9 @@
 //   Every global load of a (step, segment) is issued before the first is
 //   used, and several resident workgroups per CU overlap one step's loads
 //   with another's arithmetic.
+// * Read channels are ordered deepest first, so an 8-channel chunk nearly
+//   always has one depth and its Horner loop runs without per-channel
+//   branches (a bit-field width of 0 idles a shallower channel).
 // * Wavefront w scores blocks 4w .. 4w+3 of the step, lane i <-> token i.  For
 //   a read channel a lane reads its half-word of each plane for the four
 //   blocks with one 16-byte LDS read per plane and assembles z by a Horner
@@ -64,6 +67,36 @@ __device__ __forceinline__ uint16_t bf16_rne_bits(float x) {
   return (uint16_t)((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16);
 }
 
+// z = c' - 2^(t-1) of the 8 channels of a chunk for the wavefront's 4 blocks.
+// `base` is the lane's half-word of block 0 in plane row 0; row r is 2*GB
+// dwords further.  All reads of a plane level are issued before they are
+// used; a channel shallower than the level gets bit-field width 0 (no shift,
+// no bit), a padding slot (t = 0) width 0 throughout (z = 0).
+template <int TMAX>
+__device__ __forceinline__ void chunk_codes(const uint32_t* base, const int rr[8], const int tc[8],
+                                            int bitpos, int z[8][NB]) {
+#pragma unroll
+  for (int cc = 0; cc < 8; ++cc) {
+    const uint32_t* row = base + rr[cc] * (2 * GB);
+    const uint4 w0 = *reinterpret_cast<const uint4*>(row);
+    const int wd0 = (int)((0u - (uint32_t)tc[cc]) >> 31);  // 1 if t > 0
+    // plane 0 is stored complemented: a signed extract gives b0 - 1
+    z[cc][0] = __builtin_amdgcn_sbfe(w0.x, bitpos, wd0);
+    z[cc][1] = __builtin_amdgcn_sbfe(w0.y, bitpos, wd0);
+    z[cc][2] = __builtin_amdgcn_sbfe(w0.z, bitpos, wd0);
+    z[cc][3] = __builtin_amdgcn_sbfe(w0.w, bitpos, wd0);
+#pragma unroll
+    for (int p = 1; p < TMAX; ++p) {
+      const uint4 w = *reinterpret_cast<const uint4*>(row + p * (2 * GB));
+      const int wd = (int)(((uint32_t)p - (uint32_t)tc[cc]) >> 31);  // 1 if t > p
+      z[cc][0] = (z[cc][0] << wd) | __builtin_amdgcn_ubfe(w.x, bitpos, wd);
+      z[cc][1] = (z[cc][1] << wd) | __builtin_amdgcn_ubfe(w.y, bitpos, wd);
+      z[cc][2] = (z[cc][2] << wd) | __builtin_amdgcn_ubfe(w.z, bitpos, wd);
+      z[cc][3] = (z[cc][3] << wd) | __builtin_amdgcn_ubfe(w.w, bitpos, wd);
+    }
+  }
+}
+
 // 128-bit LDS accesses must be 16-byte aligned (misaligned ones stall)
 template <int G>
 struct ScanSmem {
@@ -79,7 +112,7 @@ struct ScanSmem {
   uint8_t row_c[NP * D];           // plane row -> read channel
   uint8_t row_p[NP * D];           // plane row -> plane
   alignas(16) float qc[D * G];     // q_hj * 2^(4 - t_j) of read channel c
-  alignas(16) uint32_t words[SEG_ROWS + 6][2][GB];  // [row][half][block] (+6 rows of slack)
+  alignas(16) uint32_t words[SEG_ROWS + 4][2][GB];  // [row][half][block] (+4 rows of slack)
   // A hi/lo per block: [chunk][hg][part][h][ch] bf16, rows padded by 16 bytes so
   // that the 16 blocks of a staging write land in different LDS banks
   static constexpr int ASTRIDE = SEG_CHUNKS * HG * 2 * 4 * 8 + 8;
@@ -88,7 +121,8 @@ struct ScanSmem {
 };
 
 template <int G, int MODE>
-__global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(ScanArgs a) {
+__global__ __launch_bounds__(SCAN_THREADS) __attribute__((amdgpu_waves_per_eu(4, 8)))
+void scan_kernel(ScanArgs a) {
   using SM = ScanSmem<G>;
   constexpr int HG = SM::HG;
   // offset of the 8 channels of (chunk k, head group hg, part, head h) in a block's A row
@@ -106,13 +140,15 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(ScanArgs a) {
   const long long wb1 = (wb0 + a.wg_blocks) < nb ? (wb0 + a.wg_blocks) : nb;
   const long long nbcap = a.g.nbcap();
 
-  // ---- plan: compact the read channels (t_j >= 1) in order of j ----
+  // ---- plan: the read channels (t_j >= 1) sorted by depth, deepest first (j
+  // ascending within a depth), so an 8-channel chunk is almost always of one
+  // depth.  scan_buf packs four 8-bit counters, one per depth.
   int tj = 0;
-  if (tid < D) sm.sel_t[tid] = 0;
   if (tid < D) {
+    sm.sel_t[tid] = 0;
     tj = a.depth[(long long)u * D + tid];
     tj = tj > NP ? NP : tj;
-    sm.scan_buf[tid] = (1 << 16) * (tj > 0) + tj;  // (channels, planes) counters
+    sm.scan_buf[tid] = tj > 0 ? 1 << (8 * (tj - 1)) : 0;
   }
   __syncthreads();
   for (int off = 1; off < D; off <<= 1) {
@@ -122,12 +158,18 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(ScanArgs a) {
     if (tid < D) sm.scan_buf[tid] += v;
     __syncthreads();
   }
-  __syncthreads();  // sel_t cleared before it is filled
+  const int tot = sm.scan_buf[D - 1];
+  const int n4 = (tot >> 24) & 0xFF, n3 = (tot >> 16) & 0xFF, n2 = (tot >> 8) & 0xFF,
+            n1 = tot & 0xFF;
   if (tid < D && tj > 0) {
-    const int c = (sm.scan_buf[tid] >> 16) - 1;
+    const int k = ((sm.scan_buf[tid] >> (8 * (tj - 1))) & 0xFF) - 1;  // rank within its depth
+    const int cbase = tj == 4 ? 0 : tj == 3 ? n4 : tj == 2 ? n4 + n3 : n4 + n3 + n2;
+    const int rbase0 = tj == 4 ? 0 : tj == 3 ? 4 * n4 : tj == 2 ? 4 * n4 + 3 * n3
+                                                               : 4 * n4 + 3 * n3 + 2 * n2;
+    const int c = cbase + k;
+    const int pb = rbase0 + k * tj;
     sm.sel_j[c] = (uint8_t)tid;
     sm.sel_t[c] = (uint8_t)tj;
-    const int pb = (sm.scan_buf[tid] & 0xFFFF) - tj;
     sm.sel_pb[c] = (uint16_t)pb;
     sm.chan_sc[c] = (uint64_t)(gu * D + tid) * (uint64_t)nbcap;
     for (int p = 0; p < tj; ++p) {
@@ -142,8 +184,8 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(ScanArgs a) {
   __syncthreads();
   if (tid == 0) {
     // segments: whole chunks, at most SEG_CHUNKS chunks and SEG_ROWS rows
-    const int C = sm.scan_buf[D - 1] >> 16;
-    const int P = sm.scan_buf[D - 1] & 0xFFFF;
+    const int C = n4 + n3 + n2 + n1;
+    const int P = 4 * n4 + 3 * n3 + 2 * n2 + n1;
     int ns = 0, c = 0;
     while (c < C) {
       sm.seg_c[ns++] = c;
@@ -166,8 +208,6 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(ScanArgs a) {
   const int C = sm.counts[0];
   const int nseg = sm.counts[2];
 
-  // rows SEG_ROWS+2 .. +5 stay zero: a padding slot reads them and gets z = 0
-  if (tid < 8 * GB) (&sm.words[SEG_ROWS + 2][0][0])[tid] = 0u;
   // A-operand ownership: lane l holds row 4*(l/16) + (l%4) of a head group,
   // in k-group l/16, only when (l%16)/4 == l/16 (block-diagonal).
   const bool a_active = ((lane & 15) >> 2) == (lane >> 4) && (lane & 3) < (G < 4 ? G : 4);
@@ -227,6 +267,12 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(ScanArgs a) {
     return;
   }
   floatx4 acc[NB][HG];
+  bf16x8 ahi, alo;  // A operand (hi, lo parts); zero on the block-diagonal's idle lanes
+  {
+    const uint32_t z4[4] = {0u, 0u, 0u, 0u};
+    __builtin_memcpy(&ahi, z4, 16);
+    __builtin_memcpy(&alo, z4, 16);
+  }
   issue_loads(0);
   for (int task = 0; task < ntask; ++task) {
     const long long g0 = wb0 + (long long)(task / nseg) * GB;
@@ -321,63 +367,36 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(ScanArgs a) {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
             pbw[i] = __builtin_amdgcn_readfirstlane(*reinterpret_cast<const uint32_t*>(&sm.sel_pb[cb + 2 * i]));
-          uint32_t bw[NB][4];
+          // chunk channels are sorted by depth: channel 0 is the deepest
+          const int tmax = (int)(t03 & 0xFFu);
+          int tc[8], rr[8], z[8][NB];
 #pragma unroll
           for (int cc = 0; cc < 8; ++cc) {
-            const int t = (int)(((cc < 4 ? t03 : t47) >> (8 * (cc & 3))) & 0xFFu);
-            // channels past the segment read the zero rows (A = 0 there)
-            const int rr = t > 0 ? (int)((pbw[cc >> 1] >> (16 * (cc & 1))) & 0xFFFFu) - rbase
-                                 : SEG_ROWS + 2;
-            const uint32_t* rowp = &sm.words[rr][half][wb];
-            // all four rows at once (rows past t are not used)
-            const uint4 w0 = *reinterpret_cast<const uint4*>(rowp);
-            const uint4 w1 = *reinterpret_cast<const uint4*>(rowp + 2 * GB);
-            const uint4 w2 = *reinterpret_cast<const uint4*>(rowp + 4 * GB);
-            const uint4 w3 = *reinterpret_cast<const uint4*>(rowp + 6 * GB);
-            // plane 0 (complemented sign): z = b0 - 1, then z = 2 z + b_p
-            int z[NB];
-            z[0] = __builtin_amdgcn_sbfe(w0.x, bitpos, 1);
-            z[1] = __builtin_amdgcn_sbfe(w0.y, bitpos, 1);
-            z[2] = __builtin_amdgcn_sbfe(w0.z, bitpos, 1);
-            z[3] = __builtin_amdgcn_sbfe(w0.w, bitpos, 1);
-            if (t >= 2) {
-              z[0] = (z[0] << 1) | __builtin_amdgcn_ubfe(w1.x, bitpos, 1);
-              z[1] = (z[1] << 1) | __builtin_amdgcn_ubfe(w1.y, bitpos, 1);
-              z[2] = (z[2] << 1) | __builtin_amdgcn_ubfe(w1.z, bitpos, 1);
-              z[3] = (z[3] << 1) | __builtin_amdgcn_ubfe(w1.w, bitpos, 1);
-            }
-            if (t >= 3) {
-              z[0] = (z[0] << 1) | __builtin_amdgcn_ubfe(w2.x, bitpos, 1);
-              z[1] = (z[1] << 1) | __builtin_amdgcn_ubfe(w2.y, bitpos, 1);
-              z[2] = (z[2] << 1) | __builtin_amdgcn_ubfe(w2.z, bitpos, 1);
-              z[3] = (z[3] << 1) | __builtin_amdgcn_ubfe(w2.w, bitpos, 1);
-            }
-            if (t >= 4) {
-              z[0] = (z[0] << 1) | __builtin_amdgcn_ubfe(w3.x, bitpos, 1);
-              z[1] = (z[1] << 1) | __builtin_amdgcn_ubfe(w3.y, bitpos, 1);
-              z[2] = (z[2] << 1) | __builtin_amdgcn_ubfe(w3.z, bitpos, 1);
-              z[3] = (z[3] << 1) | __builtin_amdgcn_ubfe(w3.w, bitpos, 1);
-            }
-            // bf16 of z (exact): the high half of its fp32 value
-#pragma unroll
-            for (int b = 0; b < NB; ++b) {
-              const uint32_t zb = __float_as_uint((float)z[b]) >> 16;
-              if (cc & 1)
-                bw[b][cc >> 1] |= zb << 16;
-              else
-                bw[b][cc >> 1] = zb;
-            }
+            tc[cc] = (int)(((cc < 4 ? t03 : t47) >> (8 * (cc & 3))) & 0xFFu);
+            // a padding slot (t = 0) reads row 0 of the segment with width 0: z = 0
+            rr[cc] = tc[cc] > 0 ? (int)((pbw[cc >> 1] >> (16 * (cc & 1))) & 0xFFFFu) - rbase : 0;
           }
+          switch (tmax) {
+            case 1: chunk_codes<1>(&sm.words[0][half][wb], rr, tc, bitpos, z); break;
+            case 2: chunk_codes<2>(&sm.words[0][half][wb], rr, tc, bitpos, z); break;
+            case 3: chunk_codes<3>(&sm.words[0][half][wb], rr, tc, bitpos, z); break;
+            default: chunk_codes<4>(&sm.words[0][half][wb], rr, tc, bitpos, z); break;
+          }
+          // bf16 pairs of z (exact): the high halves of their fp32 values
+          uint32_t bw[NB][4];
+#pragma unroll
+          for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int cp = 0; cp < 4; ++cp)
+              bw[b][cp] = __builtin_amdgcn_perm(__float_as_uint((float)z[2 * cp + 1][b]),
+                                                __float_as_uint((float)z[2 * cp][b]), 0x07060302u);
 #pragma unroll
           for (int b = 0; b < NB; ++b) {
             bf16x8 bv;
             __builtin_memcpy(&bv, bw[b], 16);
 #pragma unroll
             for (int hg = 0; hg < HG; ++hg) {
-              bf16x8 ahi, alo;
-              uint32_t z4[4] = {0u, 0u, 0u, 0u};
-              __builtin_memcpy(&ahi, z4, 16);
-              __builtin_memcpy(&alo, z4, 16);
+              // inactive lanes keep the zeros they were given once
               if (a_active) {
                 ahi = *reinterpret_cast<const bf16x8*>(&sm.atab[wb + b][a_index(kl, hg, 0, a_hh)]);
                 alo = *reinterpret_cast<const bf16x8*>(&sm.atab[wb + b][a_index(kl, hg, 1, a_hh)]);
