@@ -84,19 +84,36 @@ int check_k(const bpk_cache_t* c, int k) {
   return BPK_OK;
 }
 
+// decode_step's workspace.  Sizes follow the capacity, not the current token
+// counts, so one workspace serves every step of a growing cache.
 struct DecodeWs {
-  size_t q_basis, depth, scores, idx, attend, total;
+  size_t q_basis, depth, scores, idx, attend;
+  size_t sample, thresh, count, cval, cidx, flag;  // fused selection
+  long long sample_ld, regions;
+  size_t total;
 };
 
 DecodeWs decode_ws(const bpk::Geom& g, int k) {
   DecodeWs w;
   const size_t units = (size_t)g.units();
+  const size_t uh = units * g.G;
+  const long long groups = (g.nbcap() + bpk::SAMPLE_STRIDE - 1) / bpk::SAMPLE_STRIDE;
+  w.sample_ld = groups * bpk::SAMPLE_GROUP * bpk::BLK;
+  // candidate regions: one per scan workgroup, at most nbcap / 16 per unit
+  w.regions = (g.nbcap() + bpk::SCAN_MIN_WG_BLOCKS - 1) / bpk::SCAN_MIN_WG_BLOCKS;
+  const size_t slots = uh * (size_t)w.regions * bpk::CAND_SLOTS;
   size_t off = 0;
-  w.q_basis = off; off += align256(units * g.G * bpk::D * sizeof(float));
+  w.q_basis = off; off += align256(uh * bpk::D * sizeof(float));
   w.depth = off;   off += align256(units * bpk::D);
-  w.scores = off;  off += align256(units * g.G * (size_t)g.cap * sizeof(float));
-  w.idx = off;     off += align256(units * g.G * (size_t)k * sizeof(int32_t));
+  w.scores = off;  off += align256(uh * (size_t)g.cap * sizeof(float));
+  w.idx = off;     off += align256(uh * (size_t)k * sizeof(int32_t));
   w.attend = off;  off += align256(bpk::attend_ws_bytes(g, k));
+  w.sample = off;  off += align256(uh * (size_t)w.sample_ld * sizeof(float));
+  w.thresh = off;  off += align256(uh * sizeof(uint32_t));
+  w.count = off;   off += align256(uh * (size_t)w.regions * sizeof(int32_t));
+  w.cval = off;    off += align256(slots * sizeof(float));
+  w.cidx = off;    off += align256(slots * sizeof(int32_t));
+  w.flag = off;    off += align256(units * sizeof(int32_t));
   w.total = off;
   return w;
 }
@@ -223,11 +240,43 @@ int bpk_decode_step(const bpk_cache_t* c, const uint16_t* q, int32_t l0, int32_t
   rc = hip_status(bpk::launch_alloc(g, q, c->chan_var, c->rot, budget_planes, depth, q_basis, st),
                   "decode_step/alloc");
   if (rc) return rc;
-  rc = hip_status(bpk::launch_scan(g, q_basis, depth, c->planes, c->scales, scores, st),
-                  "decode_step/scan");
-  if (rc) return rc;
-  rc = hip_status(bpk::launch_topk(g, scores, k, idx, st), "decode_step/select");
-  if (rc) return rc;
+  if (k <= bpk::FUSED_MAX_K) {
+    // sampled threshold -> scan keeping candidates -> exact top-k among them;
+    // flagged units (too few candidates, or too many) are redone unfused
+    bpk::CandBufs cb;
+    cb.sample = reinterpret_cast<float*>(base + w.sample);
+    cb.sample_ld = w.sample_ld;
+    cb.thresh = reinterpret_cast<uint32_t*>(base + w.thresh);
+    cb.wg_blocks = bpk::scan_wg_blocks(g);
+    cb.regions = w.regions;
+    cb.count = reinterpret_cast<int32_t*>(base + w.count);
+    cb.val = reinterpret_cast<float*>(base + w.cval);
+    cb.idx = reinterpret_cast<int32_t*>(base + w.cidx);
+    cb.flag = reinterpret_cast<int32_t*>(base + w.flag);
+    rc = hip_status(bpk::launch_scan_sample(g, q_basis, depth, c->planes, c->scales, cb, st),
+                    "decode_step/sample scan");
+    if (rc) return rc;
+    rc = hip_status(bpk::launch_threshold(g, k, cb, st), "decode_step/threshold");
+    if (rc) return rc;
+    rc = hip_status(bpk::launch_scan_cand(g, q_basis, depth, c->planes, c->scales, k, cb, st),
+                    "decode_step/scan");
+    if (rc) return rc;
+    rc = hip_status(bpk::launch_cand_select(g, k, cb, idx, st), "decode_step/select");
+    if (rc) return rc;
+    rc = hip_status(bpk::launch_scan_flagged(g, q_basis, depth, c->planes, c->scales, scores,
+                                             cb.flag, st),
+                    "decode_step/fallback scan");
+    if (rc) return rc;
+    rc = hip_status(bpk::launch_topk_flagged(g, scores, k, idx, cb.flag, st),
+                    "decode_step/fallback select");
+    if (rc) return rc;
+  } else {
+    rc = hip_status(bpk::launch_scan(g, q_basis, depth, c->planes, c->scales, scores, st),
+                    "decode_step/scan");
+    if (rc) return rc;
+    rc = hip_status(bpk::launch_topk(g, scores, k, idx, st), "decode_step/select");
+    if (rc) return rc;
+  }
   return hip_status(bpk::launch_attend(g, c->k_dtype, c->k_rows, c->v_rows, q, idx, k,
                                        softmax_scale, out, base + w.attend, st),
                     "decode_step/attend");

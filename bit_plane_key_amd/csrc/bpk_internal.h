@@ -50,6 +50,70 @@ hipError_t launch_scan(const Geom& g, const float* q_basis, const uint8_t* depth
 
 hipError_t launch_topk(const Geom& g, const float* scores, int k, int32_t* idx, hipStream_t st);
 
+// ---- decode_step's fused selection ----
+// A sampled scan (the first 64 blocks of every 4096) sets per (unit, query
+// head) a score threshold expected to pass about 3 (k - 4 - W) tokens; the full
+// scan then keeps only the tokens at or above it, and the exact top-k is taken
+// among those.  Each scan workgroup owns a region of CAND_SLOTS slots per head
+// (no global atomics); a unit whose candidates are too few, overflow a region
+// or exceed CAND_CAP in all is flagged and redone by a full scan and radix
+// select.
+constexpr int SAMPLE_STRIDE = 4096;  // blocks from one sampled group to the next
+constexpr int SAMPLE_GROUP = 64;     // blocks per sampled group
+constexpr int CAND_SLOTS = 128;      // candidate slots per (scan workgroup, head)
+constexpr int CAND_CAP = 4096;       // candidates the exact selection takes per head
+constexpr int FUSED_MAX_K = 1024;    // larger k take the unfused path
+constexpr int SCAN_MIN_WG_BLOCKS = 16;
+
+struct CandBufs {
+  float* sample;        // [units][G][sample_ld] scores of the sampled blocks
+  long long sample_ld;  // sample_groups * SAMPLE_GROUP * 64
+  uint32_t* thresh;     // [units][G] order key of the threshold
+  int wg_blocks;        // blocks per workgroup of the candidate scan
+  long long regions;    // region stride: workgroups per unit the buffers hold
+  int32_t* count;       // [units][G][regions] candidates found by each workgroup
+  float* val;           // [units][G][regions][CAND_SLOTS]
+  int32_t* idx;         // [units][G][regions][CAND_SLOTS]
+  int32_t* flag;        // [units] 1 = redo this unit unfused
+};
+
+// blocks per workgroup of a scan over g: 16, doubled up to 256 while the
+// launch keeps at least 4096 workgroups
+inline int scan_wg_blocks(const Geom& g) {
+  long long maxnb = 0;
+  for (int s = 0; s < g.S; ++s) maxnb = g.n[s] / BPK_BLOCK > maxnb ? g.n[s] / BPK_BLOCK : maxnb;
+  const long long total = maxnb * g.units();
+  int wb = SCAN_MIN_WG_BLOCKS;
+  while (wb < 256 && total / (2 * wb) >= 4096) wb *= 2;
+  return wb;
+}
+
+// largest number of sampled groups over the sequences of g
+__host__ __device__ inline long long sample_groups(const Geom& g) {
+  long long m = 0;
+  for (int s = 0; s < g.S; ++s) {
+    const long long ns = (g.n[s] / BPK_BLOCK + SAMPLE_STRIDE - 1) / SAMPLE_STRIDE;
+    m = ns > m ? ns : m;
+  }
+  return m;
+}
+
+hipError_t launch_scan_sample(const Geom& g, const float* q_basis, const uint8_t* depth,
+                              const uint64_t* planes, const uint16_t* scales, const CandBufs& cb,
+                              hipStream_t st);
+hipError_t launch_threshold(const Geom& g, int k, const CandBufs& cb, hipStream_t st);
+hipError_t launch_scan_cand(const Geom& g, const float* q_basis, const uint8_t* depth,
+                            const uint64_t* planes, const uint16_t* scales, int k,
+                            const CandBufs& cb, hipStream_t st);
+hipError_t launch_cand_select(const Geom& g, int k, const CandBufs& cb, int32_t* idx,
+                              hipStream_t st);
+// full scan and radix select of the flagged units only
+hipError_t launch_scan_flagged(const Geom& g, const float* q_basis, const uint8_t* depth,
+                               const uint64_t* planes, const uint16_t* scales, float* scores,
+                               const int32_t* flag, hipStream_t st);
+hipError_t launch_topk_flagged(const Geom& g, const float* scores, int k, int32_t* idx,
+                               const int32_t* flag, hipStream_t st);
+
 size_t attend_ws_bytes(const Geom& g, int k);
 hipError_t launch_attend(const Geom& g, int k_dtype, const void* k_rows, const uint16_t* v_rows,
                          const uint16_t* q, const int32_t* idx, int k, float scale, float* out,
@@ -58,6 +122,19 @@ hipError_t launch_attend(const Geom& g, int k_dtype, const void* k_rows, const u
 // ---- small device helpers ----
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(((uint32_t)b) << 16);
+}
+
+// monotone map float -> uint32 (larger float, larger key); -0 is mapped to +0
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u << 1) == 0) u = 0;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// always-kept tail of a sequence of n tokens: the last 32, or the whole open
+// block when it holds more
+__host__ __device__ inline long long kept_tail(long long n) {
+  return (n % BPK_BLOCK) > 32 ? (n % BPK_BLOCK) : 32;
 }
 
 }  // namespace bpk

@@ -49,8 +49,20 @@ constexpr int GB = NB * SCAN_WAVES;   // blocks per workgroup step
 constexpr int SEG_ROWS = 128;         // plane rows staged per segment
 constexpr int SEG_CHUNKS = 8;         // 8-channel chunks per segment
 constexpr int MAX_SEGS = D / 8;       // one chunk per segment at worst
+static_assert(SCAN_MIN_WG_BLOCKS == GB, "a workgroup takes whole steps");
+static_assert(SAMPLE_GROUP % GB == 0 && SAMPLE_STRIDE % SAMPLE_GROUP == 0, "sample plan");
 
-enum ScanMode { SCAN_FULL = 0 };
+// What a launch does with the scores it computes:
+// * SCAN_FULL writes every score ([unit][G][cap]);
+// * SCAN_SAMPLE scores only the first SAMPLE_GROUP blocks of every
+//   SAMPLE_STRIDE (one workgroup per sampled group) into [unit][G][sample_ld];
+// * SCAN_CAND appends (score, token) of the tokens of [4, n - W) whose score
+//   is at or above the head's threshold to the workgroup's candidate region
+//   of that head (slots handed out by an LDS counter; the count, which may
+//   pass the region's size, is stored at the end).
+// A block's scores are computed by the same instructions in every mode, so
+// they are bit-identical across modes and workgroup sizes.
+enum ScanMode { SCAN_FULL = 0, SCAN_SAMPLE = 1, SCAN_CAND = 2 };
 
 struct ScanArgs {
   Geom g;
@@ -58,9 +70,37 @@ struct ScanArgs {
   const uint8_t* __restrict__ depth;
   const uint64_t* __restrict__ planes;
   const uint16_t* __restrict__ scales;
-  float* __restrict__ scores;
-  int wg_blocks;  // blocks per workgroup (multiple of GB)
+  float* __restrict__ out;          // scores (FULL) or sampled scores (SAMPLE)
+  long long out_ld;                 // per (unit, head) row length of out
+  int wg_blocks;                    // blocks per workgroup (multiple of GB)
+  int k;                            // top-k (CAND: units with n <= k are skipped)
+  const int32_t* __restrict__ unit_flag;  // FULL: if set, only units with flag != 0
+  const uint32_t* __restrict__ thresh;    // CAND: [unit][G] order keys
+  long long regions;                      // CAND: region stride per (unit, head)
+  int32_t* __restrict__ cand_count;       // CAND: [unit][G][regions]
+  float* __restrict__ cand_val;           // CAND: [unit][G][regions][CAND_SLOTS]
+  int32_t* __restrict__ cand_idx;         // CAND: [unit][G][regions][CAND_SLOTS]
 };
+
+// Appends (s, tok) of the lanes with pred to a candidate region; all 64 lanes
+// of the wavefront take part.  One LDS atomic per wavefront reserves the
+// slots; the count keeps growing past the region's size so that overflow is
+// seen.
+__device__ __forceinline__ void cand_append(bool pred, float s, long long tok, int* count,
+                                            float* val, int32_t* idx, int lane) {
+  const unsigned long long m = __ballot(pred);
+  if (m == 0ull) return;
+  const int leader = __ffsll(m) - 1;
+  int base = 0;
+  if (lane == leader) base = atomicAdd(count, __popcll(m));
+  base = __shfl(base, leader);
+  const int off = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                        __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+  if (pred && off < CAND_SLOTS) {
+    val[off] = s;
+    idx[off] = (int32_t)tok;
+  }
+}
 
 __device__ __forceinline__ uint16_t bf16_rne_bits(float x) {
   const uint32_t b = __float_as_uint(x);
@@ -118,6 +158,7 @@ struct ScanSmem {
   static constexpr int ASTRIDE = SEG_CHUNKS * HG * 2 * 4 * 8 + 8;
   alignas(16) uint16_t atab[GB][ASTRIDE];
   alignas(16) float cpart[SCAN_WAVES][GB][G];  // per-wavefront partial sums of A / 2
+  int ccount[G];                               // candidates of this workgroup per head
 };
 
 template <int G, int MODE>
@@ -135,15 +176,51 @@ void scan_kernel(ScanArgs a) {
   const long long gu = a.g.global_unit(u);
   const long long n = a.g.n[a.g.seq_of(u)];
   const long long nb = n / BLK;
-  const long long wb0 = (long long)blockIdx.x * a.wg_blocks;
+  if constexpr (MODE == SCAN_FULL) {
+    if (a.unit_flag && a.unit_flag[u] == 0) return;
+  }
+  if constexpr (MODE == SCAN_CAND) {
+    if (n <= a.k) return;  // everything is selected
+  }
+  const long long span = MODE == SCAN_SAMPLE ? SAMPLE_GROUP : a.wg_blocks;
+  const long long wb0 = (long long)blockIdx.x * (MODE == SCAN_SAMPLE ? SAMPLE_STRIDE : a.wg_blocks);
   if (wb0 >= nb) return;
-  const long long wb1 = (wb0 + a.wg_blocks) < nb ? (wb0 + a.wg_blocks) : nb;
+  const long long wb1 = (wb0 + span) < nb ? (wb0 + span) : nb;
   const long long nbcap = a.g.nbcap();
+
+  // where the score of (token, head) goes
+  const long long cand_hi = n - kept_tail(n);  // candidates are tokens [4, cand_hi)
+  uint32_t tkey[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) tkey[h] = MODE == SCAN_CAND ? a.thresh[(long long)u * G + h] : 0u;
+  auto emit = [&](long long tok, int h, float s) {  // every lane of the wavefront calls it
+    const long long uh = (long long)u * G + h;
+    if constexpr (MODE == SCAN_FULL) {
+      a.out[uh * a.out_ld + tok] = s;
+    } else if constexpr (MODE == SCAN_SAMPLE) {
+      a.out[uh * a.out_ld + (long long)blockIdx.x * (SAMPLE_GROUP * BLK) + (tok - wb0 * BLK)] = s;
+    } else {
+      const bool pred = tok >= 4 && tok < cand_hi && order_key(s) >= tkey[h];
+      const long long reg = (uh * a.regions + blockIdx.x) * CAND_SLOTS;
+      cand_append(pred, s, tok, &sm.ccount[h], a.cand_val + reg, a.cand_idx + reg,
+                  threadIdx.x & 63);
+    }
+  };
+  // the region's count, once every wavefront has appended
+  auto store_counts = [&]() {
+    if constexpr (MODE == SCAN_CAND) {
+      __syncthreads();
+      if (threadIdx.x < G)
+        a.cand_count[((long long)u * G + threadIdx.x) * a.regions + blockIdx.x] =
+            sm.ccount[threadIdx.x];
+    }
+  };
 
   // ---- plan: the read channels (t_j >= 1) sorted by depth, deepest first (j
   // ascending within a depth), so an 8-channel chunk is almost always of one
   // depth.  scan_buf packs four 8-bit counters, one per depth.
   int tj = 0;
+  if (MODE == SCAN_CAND && tid < G) sm.ccount[tid] = 0;
   if (tid < D) {
     sm.sel_t[tid] = 0;
     tj = a.depth[(long long)u * D + tid];
@@ -259,11 +336,11 @@ void scan_kernel(ScanArgs a) {
   };
 
   if (nseg == 0) {  // nothing is read: every score is 0
+    // (wb1 - wb0) * 64 is a multiple of 64: each wavefront's lanes run the same trips
     for (long long e = tid; e < (wb1 - wb0) * BLK; e += SCAN_THREADS)
 #pragma unroll
-      for (int h = 0; h < G; ++h)
-        if constexpr (MODE == SCAN_FULL)
-          a.scores[((long long)u * G + h) * a.g.cap + wb0 * BLK + e] = 0.f;
+      for (int h = 0; h < G; ++h) emit(wb0 * BLK + e, h, 0.f);
+    store_counts();
     return;
   }
   floatx4 acc[NB][HG];
@@ -421,15 +498,12 @@ void scan_kernel(ScanArgs a) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int h = 4 * hg + r;
-            if (h < G) {
-              const float s = acc[b][hg][r];
-              if constexpr (MODE == SCAN_FULL)
-                a.scores[((long long)u * G + h) * a.g.cap + tok] = s;
-            }
+            if (h < G) emit(tok, h, acc[b][hg][r]);
           }
       }
     }
   }
+  store_counts();
 }
 
 template <int G, int MODE>
@@ -437,14 +511,40 @@ hipError_t launch_gm(const ScanArgs& a0, hipStream_t st) {
   ScanArgs a = a0;
   long long maxnb = 0;
   for (int s = 0; s < a.g.S; ++s) maxnb = a.g.n[s] / BLK > maxnb ? a.g.n[s] / BLK : maxnb;
-  if (maxnb == 0) return hipSuccess;
-  const long long total = maxnb * a.g.units();
-  int wb = GB;
-  while (wb < 256 && total / (2 * wb) >= 4096) wb *= 2;
-  a.wg_blocks = wb;
-  dim3 grid((unsigned)((maxnb + wb - 1) / wb), (unsigned)a.g.units());
+  if (maxnb == 0 || a.g.units() == 0) return hipSuccess;
+  dim3 grid;
+  if (MODE == SCAN_SAMPLE) {
+    a.wg_blocks = SAMPLE_GROUP;
+    grid = dim3((unsigned)sample_groups(a.g), (unsigned)a.g.units());
+  } else {
+    const int wb = scan_wg_blocks(a.g);
+    a.wg_blocks = wb;
+    grid = dim3((unsigned)((maxnb + wb - 1) / wb), (unsigned)a.g.units());
+  }
   scan_kernel<G, MODE><<<grid, SCAN_THREADS, 0, st>>>(a);
   return hipGetLastError();
+}
+
+template <int MODE>
+hipError_t dispatch(const ScanArgs& a, hipStream_t st) {
+  switch (a.g.G) {
+    case 1: return launch_gm<1, MODE>(a, st);
+    case 2: return launch_gm<2, MODE>(a, st);
+    case 4: return launch_gm<4, MODE>(a, st);
+    case 8: return launch_gm<8, MODE>(a, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+ScanArgs base_args(const Geom& g, const float* q_basis, const uint8_t* depth,
+                   const uint64_t* planes, const uint16_t* scales) {
+  ScanArgs a{};
+  a.g = g;
+  a.q_basis = q_basis;
+  a.depth = depth;
+  a.planes = planes;
+  a.scales = scales;
+  return a;
 }
 
 }  // namespace
@@ -452,14 +552,42 @@ hipError_t launch_gm(const ScanArgs& a0, hipStream_t st) {
 hipError_t launch_scan(const Geom& g, const float* q_basis, const uint8_t* depth,
                        const uint64_t* planes, const uint16_t* scales, float* scores,
                        hipStream_t st) {
-  ScanArgs a{g, q_basis, depth, planes, scales, scores, 0};
-  switch (g.G) {
-    case 1: return launch_gm<1, SCAN_FULL>(a, st);
-    case 2: return launch_gm<2, SCAN_FULL>(a, st);
-    case 4: return launch_gm<4, SCAN_FULL>(a, st);
-    case 8: return launch_gm<8, SCAN_FULL>(a, st);
-    default: return hipErrorInvalidValue;
-  }
+  ScanArgs a = base_args(g, q_basis, depth, planes, scales);
+  a.out = scores;
+  a.out_ld = g.cap;
+  return dispatch<SCAN_FULL>(a, st);
+}
+
+hipError_t launch_scan_flagged(const Geom& g, const float* q_basis, const uint8_t* depth,
+                               const uint64_t* planes, const uint16_t* scales, float* scores,
+                               const int32_t* flag, hipStream_t st) {
+  ScanArgs a = base_args(g, q_basis, depth, planes, scales);
+  a.out = scores;
+  a.out_ld = g.cap;
+  a.unit_flag = flag;
+  return dispatch<SCAN_FULL>(a, st);
+}
+
+hipError_t launch_scan_sample(const Geom& g, const float* q_basis, const uint8_t* depth,
+                              const uint64_t* planes, const uint16_t* scales, const CandBufs& cb,
+                              hipStream_t st) {
+  ScanArgs a = base_args(g, q_basis, depth, planes, scales);
+  a.out = cb.sample;
+  a.out_ld = cb.sample_ld;
+  return dispatch<SCAN_SAMPLE>(a, st);
+}
+
+hipError_t launch_scan_cand(const Geom& g, const float* q_basis, const uint8_t* depth,
+                            const uint64_t* planes, const uint16_t* scales, int k,
+                            const CandBufs& cb, hipStream_t st) {
+  ScanArgs a = base_args(g, q_basis, depth, planes, scales);
+  a.k = k;
+  a.thresh = cb.thresh;
+  a.regions = cb.regions;
+  a.cand_count = cb.count;
+  a.cand_val = cb.val;
+  a.cand_idx = cb.idx;
+  return dispatch<SCAN_CAND>(a, st);
 }
 
 }  // namespace bpk

@@ -9,6 +9,18 @@
 // select over the complemented token index picks the lowest indices among the
 // ties.  The winners are collected into LDS, sorted ascending with a bitonic
 // network and written out.
+//
+// decode_step's fused selection adds two kernels on the same machinery:
+// * threshold_kernel: per (unit, head), the r-th largest of the sampled
+//   scores of candidate tokens, with r chosen so that about 3 (k - 4 - W)
+//   tokens of the whole range are expected at or above it (plus 8 for the
+//   sampling noise of small r);
+// * cand_select_kernel: per (unit, head), the exact top (k - 4 - W) of the
+//   candidates (every token at or above the threshold, so the k - 4 - W
+//   largest of the whole range are among them whenever there are at least
+//   that many), by a bitonic sort of (score key, complemented index) pairs.
+//   A head with too few candidates, or more than the buffer holds, flags its
+//   unit for the full scan and radix select.
 #include <limits.h>
 
 #include "bpk_internal.h"
@@ -24,14 +36,8 @@ struct TopkArgs {
   const float* scores;
   int k;
   int32_t* idx;
+  const int32_t* unit_flag;  // if set, only units with flag != 0
 };
-
-// monotone map float -> uint32 (larger float, larger key); -0 is mapped to +0
-__device__ __forceinline__ uint32_t order_key(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u << 1) == 0) u = 0;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
 
 struct TkSmem {
   uint32_t hist[TK_BINS];
@@ -110,10 +116,37 @@ __device__ uint32_t radix_select(TkSmem& sm, long long lo, long long hi, int wan
   return prefix;
 }
 
+// Sorts buf[0..k) ascending (a bitonic network, INT_MAX padding up to a power
+// of two; buf holds at least that many entries) and writes it to out.
+__device__ void sort_and_write(int32_t* buf, int k, int32_t* out) {
+  const int tid = threadIdx.x;
+  int m = 1;
+  while (m < k) m <<= 1;
+  for (int i = k + tid; i < m; i += TK_THREADS) buf[i] = INT_MAX;
+  __syncthreads();
+  for (int size = 2; size <= m; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = tid; i < m / 2; i += TK_THREADS) {
+        const int lo_i = 2 * i - (i & (stride - 1));
+        const int hi_i = lo_i + stride;
+        const bool up = ((lo_i & size) == 0);
+        const int32_t x = buf[lo_i], y = buf[hi_i];
+        if ((x > y) == up) {
+          buf[lo_i] = y;
+          buf[hi_i] = x;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int i = tid; i < k; i += TK_THREADS) out[i] = buf[i];
+}
+
 __global__ __launch_bounds__(TK_THREADS) void topk_kernel(TopkArgs a) {
   __shared__ TkSmem sm;
   const int G = a.g.G;
   const int u = blockIdx.x / G, h = blockIdx.x % G;
+  if (a.unit_flag && a.unit_flag[u] == 0) return;
   const long long n = a.g.n[a.g.seq_of(u)];
   const int k = a.k;
   const int tid = threadIdx.x;
@@ -122,7 +155,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(TopkArgs a) {
     for (int i = tid; i < k; i += TK_THREADS) out[i] = i < n ? i : -1;
     return;
   }
-  const long long w = (n % BLK) > 32 ? (n % BLK) : 32;
+  const long long w = kept_tail(n);
   const long long lo = 4, hi = n - w;
   const int want = k - 4 - (int)w;
   const float* sc = a.scores + ((long long)u * G + h) * a.g.cap;
@@ -157,36 +190,186 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(TopkArgs a) {
     }
   }
   __syncthreads();
-  // bitonic sort of buf[0..k) ascending (padding INT_MAX up to a power of two)
-  int m = 1;
-  while (m < k) m <<= 1;
-  for (int i = k + tid; i < m; i += TK_THREADS) sm.buf[i] = INT_MAX;
-  __syncthreads();
-  for (int size = 2; size <= m; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = tid; i < m / 2; i += TK_THREADS) {
-        const int lo_i = 2 * i - (i & (stride - 1));
-        const int hi_i = lo_i + stride;
-        const bool up = ((lo_i & size) == 0);
-        const int32_t x = sm.buf[lo_i], y = sm.buf[hi_i];
-        if ((x > y) == up) {
-          sm.buf[lo_i] = y;
-          sm.buf[hi_i] = x;
-        }
-      }
-      __syncthreads();
+  sort_and_write(sm.buf, k, out);
+}
+
+struct ThreshArgs {
+  Geom g;
+  int k;
+  CandBufs cb;
+};
+
+__global__ __launch_bounds__(TK_THREADS) void threshold_kernel(ThreshArgs a) {
+  __shared__ TkSmem sm;
+  const int G = a.g.G;
+  const int u = blockIdx.x / G, h = blockIdx.x % G;
+  const long long uh = (long long)u * G + h;
+  const int tid = threadIdx.x;
+  const long long n = a.g.n[a.g.seq_of(u)];
+  const long long w = kept_tail(n);
+  const long long hi = n - w;
+  const long long want = (long long)a.k - 4 - w;
+  uint32_t tkey = 0xFFFFFFFFu;  // nothing is a candidate
+  if (n > a.k && want > 0) {
+    // sample position i = (group gi, offset j) holds token gi * SAMPLE_STRIDE * 64 + j
+    const long long nb = n / BLK;
+    const long long ngr = (nb + SAMPLE_STRIDE - 1) / SAMPLE_STRIDE;
+    const long long gtok = (long long)SAMPLE_STRIDE * BLK, glen = (long long)SAMPLE_GROUP * BLK;
+    auto tok_of = [&](long long i) { return (i / glen) * gtok + i % glen; };
+    auto valid = [&](long long i) {
+      const long long t = tok_of(i);
+      return t >= 4 && t < hi;
+    };
+    // candidate tokens that were sampled
+    long long m = 0;
+    for (long long gi = 0; gi < ngr; ++gi) {
+      const long long t0 = gi * gtok, t1 = t0 + glen;
+      const long long x0 = t0 > 4 ? t0 : 4, x1 = t1 < hi ? t1 : hi;
+      m += x1 > x0 ? x1 - x0 : 0;
+    }
+    const long long nc = hi - 4;
+    const long long r = (3 * want * m + nc - 1) / nc + 8;
+    if (r > m) {
+      tkey = 0;  // the sample is too small to cut anything: all are candidates
+    } else {
+      const float* sc = a.cb.sample + uh * a.cb.sample_ld;
+      auto keyf = [&](long long i) { return order_key(sc[i]); };
+      int t_eq, c_eq;
+      tkey = radix_select(sm, 0, ngr * glen, (int)r, keyf, valid, &t_eq, &c_eq);
     }
   }
-  for (int i = tid; i < k; i += TK_THREADS) out[i] = sm.buf[i];
+  if (tid == 0) {
+    a.cb.thresh[uh] = tkey;
+    if (h == 0) a.cb.flag[u] = 0;
+  }
+}
+
+struct CandSmem {
+  uint64_t key[CAND_CAP];
+  int32_t buf[BPK_MAX_K];
+  int total, over, fill;
+};
+
+struct CandArgs {
+  Geom g;
+  int k;
+  CandBufs cb;
+  int32_t* idx;
+};
+
+__global__ __launch_bounds__(TK_THREADS) void cand_select_kernel(CandArgs a) {
+  __shared__ CandSmem sm;
+  const int G = a.g.G;
+  const int u = blockIdx.x / G, h = blockIdx.x % G;
+  const long long uh = (long long)u * G + h;
+  const int tid = threadIdx.x;
+  const int k = a.k;
+  const long long n = a.g.n[a.g.seq_of(u)];
+  int32_t* out = a.idx + uh * k;
+  if (n <= k) {
+    for (int i = tid; i < k; i += TK_THREADS) out[i] = i < n ? i : -1;
+    return;
+  }
+  const long long w = kept_tail(n);
+  const long long hi = n - w;
+  const int want = k - 4 - (int)w;
+  int nk = 0;
+  if (want > 0) {
+    // the candidate regions of this unit's scan workgroups
+    const long long R = (n / BLK + a.cb.wg_blocks - 1) / a.cb.wg_blocks;
+    const int32_t* cnt = a.cb.count + uh * a.cb.regions;
+    if (tid == 0) {
+      sm.total = 0;
+      sm.over = 0;
+      sm.fill = 0;
+    }
+    __syncthreads();
+    int tot = 0, over = 0;
+    for (long long x = tid; x < R; x += TK_THREADS) {
+      const int c = cnt[x];
+      tot += c;
+      over |= c > CAND_SLOTS;
+    }
+    if (tot) atomicAdd(&sm.total, tot);
+    if (over) atomicOr(&sm.over, 1);
+    __syncthreads();
+    const int total = sm.total;
+    if (sm.over || total < want || total > CAND_CAP) {
+      if (tid == 0) a.cb.flag[u] = 1;
+      return;
+    }
+    // (score key, complemented index) in descending order = score down, index up
+    const float* v = a.cb.val + uh * a.cb.regions * CAND_SLOTS;
+    const int32_t* ix = a.cb.idx + uh * a.cb.regions * CAND_SLOTS;
+    for (long long e = tid; e < R * CAND_SLOTS; e += TK_THREADS) {
+      const long long x = e / CAND_SLOTS;
+      if ((int)(e % CAND_SLOTS) < cnt[x]) {
+        const int pos = atomicAdd(&sm.fill, 1);
+        sm.key[pos] = ((uint64_t)order_key(v[e]) << 32) | (uint32_t)(~(uint32_t)ix[e]);
+      }
+    }
+    int m = 1;
+    while (m < total) m <<= 1;
+    for (int i = total + tid; i < m; i += TK_THREADS) sm.key[i] = 0ull;
+    __syncthreads();
+    for (int size = 2; size <= m; size <<= 1) {
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        for (int i = tid; i < m / 2; i += TK_THREADS) {
+          const int lo_i = 2 * i - (i & (stride - 1));
+          const int hi_i = lo_i + stride;
+          const bool down = ((lo_i & size) == 0);
+          const uint64_t x = sm.key[lo_i], y = sm.key[hi_i];
+          if ((x < y) == down) {
+            sm.key[lo_i] = y;
+            sm.key[hi_i] = x;
+          }
+        }
+        __syncthreads();
+      }
+    }
+    for (int i = tid; i < want; i += TK_THREADS)
+      sm.buf[i] = (int32_t)(~(uint32_t)(sm.key[i] & 0xFFFFFFFFull));
+    nk = want;
+  }
+  for (int i = tid; i < 4; i += TK_THREADS) sm.buf[nk + i] = i;
+  for (long long i = tid; i < w; i += TK_THREADS) sm.buf[nk + 4 + i] = (int32_t)(hi + i);
+  __syncthreads();
+  sort_and_write(sm.buf, k, out);
 }
 
 }  // namespace
 
 hipError_t launch_topk(const Geom& g, const float* scores, int k, int32_t* idx, hipStream_t st) {
-  TopkArgs a{g, scores, k, idx};
+  TopkArgs a{g, scores, k, idx, nullptr};
   const long long blocks = (long long)g.units() * g.G;
   if (blocks == 0) return hipSuccess;
   topk_kernel<<<(unsigned)blocks, TK_THREADS, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_flagged(const Geom& g, const float* scores, int k, int32_t* idx,
+                               const int32_t* flag, hipStream_t st) {
+  TopkArgs a{g, scores, k, idx, flag};
+  const long long blocks = (long long)g.units() * g.G;
+  if (blocks == 0) return hipSuccess;
+  topk_kernel<<<(unsigned)blocks, TK_THREADS, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_threshold(const Geom& g, int k, const CandBufs& cb, hipStream_t st) {
+  ThreshArgs a{g, k, cb};
+  const long long blocks = (long long)g.units() * g.G;
+  if (blocks == 0) return hipSuccess;
+  threshold_kernel<<<(unsigned)blocks, TK_THREADS, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_cand_select(const Geom& g, int k, const CandBufs& cb, int32_t* idx,
+                              hipStream_t st) {
+  CandArgs a{g, k, cb, idx};
+  const long long blocks = (long long)g.units() * g.G;
+  if (blocks == 0) return hipSuccess;
+  cand_select_kernel<<<(unsigned)blocks, TK_THREADS, 0, st>>>(a);
   return hipGetLastError();
 }
 

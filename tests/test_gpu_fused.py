@@ -1,0 +1,193 @@
+"""GPU: decode_step's fused selection (sampled threshold -> candidate scan ->
+exact top-k among the candidates, with a full scan + radix select for the
+units it cannot settle) selects exactly what select_topk(scan_scores(...))
+selects, and matches the oracle.
+
+Bars as in test_gpu_parity: top-k sets equal to the oracle's up to near-tie
+swaps; fused and unfused index arrays identical; attention within 2e-3.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from synth import config_by_name
+from synth.workload import bf16_bits_to_f32, f32_to_bf16_bits
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+# the plan of the fused path: the first 64 blocks of every 4096 are sampled;
+# each scan workgroup keeps at most 128 candidates per head
+SAMPLE_STRIDE, SAMPLE_GROUP, SLOTS = 4096, 64, 128
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+@pytest.fixture(scope="module")
+def bpk():
+    import bit_plane_key_amd as b
+    from bit_plane_key_amd import workloads
+    return b, workloads
+
+
+def _to_dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def _unit_cache(b, kb, vb, var, group):
+    n = kb.shape[0]
+    cache = b.Cache(1, 1, 1, max(64, (n + 63) // 64 * 64), group=group)
+    cache.chan_var.copy_(torch.from_numpy(var)[None, None, None])
+    b.encode_append(cache, 0, _to_dev(kb)[None, None], _to_dev(vb)[None, None])
+    return cache
+
+
+def _unfused(b, cache, q, budget, k, scale):
+    depth, qb = b.alloc_depth(cache, q, 0, 1, budget)
+    scores = b.scan_scores(cache, qb, depth, 0, 1)
+    idx = b.select_topk(cache, scores, 0, 1, k)
+    return scores, idx
+
+
+def _fused(b, cache, q, budget, k, scale, group):
+    idx = torch.empty((1, 1, 1, group, k), dtype=torch.int32, device="cuda")
+    out = b.decode_step(cache, q, 0, 1, budget, k, scale, idx_out=idx)
+    return idx, out
+
+
+def _wg_blocks(nb, units=1):
+    wb = 16
+    while wb < 256 and nb * units // (2 * wb) >= 4096:
+        wb *= 2
+    return wb
+
+
+def _fused_needs_fallback(scores_h, n, k):
+    """Whether the fused plan cannot settle this head (one unit): fewer than
+    k - 4 - W tokens at or above the sampled threshold, more than 4096, or
+    more than 128 in one scan workgroup's range."""
+    w = O.kept_tail(n)
+    hi, want = n - w, k - 4 - w
+    nb = n // 64
+    toks = np.concatenate([np.arange(g * SAMPLE_STRIDE * 64,
+                                     min(g * SAMPLE_STRIDE + SAMPLE_GROUP, nb) * 64)
+                           for g in range((nb + SAMPLE_STRIDE - 1) // SAMPLE_STRIDE)])
+    toks = toks[(toks >= 4) & (toks < hi)]
+    m, nc = len(toks), hi - 4
+    r = (3 * want * m + nc - 1) // nc + 8
+    tau = -np.inf if r > m else np.sort(scores_h[toks])[::-1][r - 1]
+    passed = np.zeros(n, dtype=bool)
+    passed[4:hi] = scores_h[4:hi] >= tau
+    count = int(passed.sum())
+    wb = _wg_blocks(nb) * 64
+    per_wg = np.add.reduceat(passed[: nb * 64], np.arange(0, nb * 64, wb))
+    return count < want or count > 4096 or int(per_wg.max()) > SLOTS
+
+
+@pytest.mark.parametrize("budget", [64, 88, 128])
+def test_fused_equals_unfused_c2(bpk, budget):
+    b, wl = bpk
+    cfg = config_by_name("c2")
+    cache = wl.build_cache(cfg)
+    q = wl.queries(cfg)
+    scale = wl.softmax_scale(cfg)
+    idx = torch.empty((1, 1, 8, 4, cfg.k), dtype=torch.int32, device="cuda")
+    out = b.decode_step(cache, q, 0, 1, budget, cfg.k, scale, idx_out=idx)
+    depth, qb = b.alloc_depth(cache, q, 0, 1, budget)
+    idx2 = b.select_topk(cache, b.scan_scores(cache, qb, depth, 0, 1), 0, 1, cfg.k)
+    out2 = b.sparse_attend(cache, q, idx2, 0, 1, cfg.k, scale)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx2)
+    assert torch.equal(out, out2)
+
+
+@pytest.mark.parametrize("n,group", [(4096 * 64 * 3 + 1000, 4), (4096 * 64 + 77, 1),
+                                     (4096 * 64 * 2 + 64 * 7, 8)])
+def test_fused_many_sample_groups_against_oracle(bpk, n, group):
+    """Several sampled groups, a ragged tail, G = 1, 4, 8."""
+    b, wl = bpk
+    _say(f"fused n={n} G={group}")
+    rng = np.random.default_rng(n + group)
+    sig = np.exp(rng.uniform(math.log(0.1), math.log(4.0), 128))
+    kb = f32_to_bf16_bits((rng.standard_normal((n, 128)) * sig).astype(np.float32))
+    vb = f32_to_bf16_bits(rng.standard_normal((n, 128)).astype(np.float32))
+    qb = f32_to_bf16_bits(rng.standard_normal((group, 128)).astype(np.float32))
+    var = (sig ** 2).astype(np.float32)
+    cache = _unit_cache(b, kb, vb, var, group)
+    q = _to_dev(qb)[None, None, None]
+    k, budget, scale = 512 if group < 8 else 256, 88, 1 / math.sqrt(128)
+    idx, out = _fused(b, cache, q, budget, k, scale, group)
+    scores, idx2 = _unfused(b, cache, q, budget, k, scale)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx2)
+    kv, vv, qv = bf16_bits_to_f32(kb), bf16_bits_to_f32(vb), bf16_bits_to_f32(qb)
+    ref = O.decode_unit(qv, var, kv, vv, n, budget, k, scale)
+    ix = idx[0, 0, 0].cpu().numpy()
+    P.check_selection(ix, ref["idx"], ref["scores"], ref["l1"], n, k, f"n={n}")
+    P.check_attention(out[0, 0, 0].cpu().numpy(), O.attend(qv, kv, vv, ix, scale), f"n={n}")
+    sc = scores[0, 0, 0].cpu().numpy()
+    assert not any(_fused_needs_fallback(sc[h], n, k) for h in range(group))
+
+
+def test_fused_too_few_candidates_falls_back(bpk):
+    """Keys of the sampled blocks score far above the rest, so the sampled
+    threshold passes fewer than k - 4 - W tokens: the unit is redone by the
+    full scan and radix select, and the result is still exact."""
+    b, wl = bpk
+    n, group, k, budget = 4096 * 64 * 2 + 64 * 100, 4, 512, 88
+    rng = np.random.default_rng(11)
+    k_f = rng.standard_normal((n, 128)).astype(np.float32) * 0.5
+    for g in range(3):
+        t0 = g * SAMPLE_STRIDE * 64
+        k_f[t0:t0 + SAMPLE_GROUP * 64] = np.abs(k_f[t0:t0 + SAMPLE_GROUP * 64]) + 2.0
+    kb = f32_to_bf16_bits(k_f)
+    vb = f32_to_bf16_bits(rng.standard_normal((n, 128)).astype(np.float32))
+    qb = f32_to_bf16_bits(np.ones((group, 128), dtype=np.float32))
+    var = np.ones(128, dtype=np.float32)
+    cache = _unit_cache(b, kb, vb, var, group)
+    q = _to_dev(qb)[None, None, None]
+    scale = 1 / math.sqrt(128)
+    idx, out = _fused(b, cache, q, budget, k, scale, group)
+    scores, idx2 = _unfused(b, cache, q, budget, k, scale)
+    torch.cuda.synchronize()
+    sc = scores[0, 0, 0].cpu().numpy()
+    assert all(_fused_needs_fallback(sc[h], n, k) for h in range(group))
+    assert torch.equal(idx, idx2)
+    P.check_topk_valid(sc[:, :n].astype(np.float64), idx[0, 0, 0].cpu().numpy(), n, k, "few")
+
+
+def test_fused_overflow_falls_back(bpk):
+    """Budget 0 makes every score 0: all candidates tie at the threshold and
+    overflow the buffer; the fallback takes the lowest indices."""
+    b, wl = bpk
+    n, k = 64 * 100, 100
+    rng = np.random.default_rng(5)
+    kb = f32_to_bf16_bits(rng.standard_normal((n, 128)).astype(np.float32))
+    cache = _unit_cache(b, kb, kb, np.ones(128, dtype=np.float32), 4)
+    q = _to_dev(f32_to_bf16_bits(rng.standard_normal((4, 128)).astype(np.float32)))[None, None, None]
+    idx, out = _fused(b, cache, q, 0, k, 1 / math.sqrt(128), 4)
+    torch.cuda.synchronize()
+    want = np.concatenate([np.arange(4), np.arange(4, 4 + k - 36), np.arange(n - 32, n)])
+    for h in range(4):
+        assert np.array_equal(idx[0, 0, 0, h].cpu().numpy(), want)
+
+
+def test_large_k_takes_unfused_path(bpk):
+    """k above the fused limit (1024) runs the unfused scan + radix select."""
+    b, wl = bpk
+    n, k = 64 * 600 + 9, 2000
+    rng = np.random.default_rng(9)
+    kb = f32_to_bf16_bits(rng.standard_normal((n, 128)).astype(np.float32))
+    vb = f32_to_bf16_bits(rng.standard_normal((n, 128)).astype(np.float32))
+    cache = _unit_cache(b, kb, vb, np.ones(128, dtype=np.float32), 2)
+    q = _to_dev(f32_to_bf16_bits(rng.standard_normal((2, 128)).astype(np.float32)))[None, None, None]
+    scale = 1 / math.sqrt(128)
+    idx, out = _fused(b, cache, q, 88, k, scale, 2)
+    scores, idx2 = _unfused(b, cache, q, 88, k, scale)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx2)
