@@ -2,55 +2,60 @@
 // every complete block, reading only planes p < t_j of each read channel and
 // the fp16 block scales of those channels.
 //
-// Per unit the score of token i for query head h is
-//   s_hat = sum_j q_hj s_bj m_ij,  m = (c' + 1/2) 2^(4-t) - 8 = z 2^(4-t) + 2^(3-t)
-// with c' the t-bit prefix code and z = c' - 2^(t-1) in [-8, 7].  Writing
-// A_hj = q_hj s_bj 2^(4-t_j) gives s_hat = sum_j A_hj z_ij + sum_j A_hj / 2.
+// The t-bit prefix value of a 4-bit code is m = (c' + 1/2) 2^(4-t) - 8, with
+// c' = sum_{p<t} b_p 2^(t-1-p) read from planes 0 .. t-1 (plane 0 = most
+// significant bit).  Since sum_{p<t} 2^(2-p) = 8 - 2^(3-t), the same value is
+// a signed binary expansion:
+//   m = sum_{p<t} 2^(2-p) B_p,   B_p = 2 b_p - 1 in {-1, +1},
+// so with one "row" per read plane (j, p) and A_{h,(j,p)} = q_hj s_bj 2^(2-p):
+//   s_hat = sum_j q_hj s_bj m_ij = sum_rows A_{h,r} B_{r,i},
+// a contraction over rows of +-1 bits with no constant term.
 //
 // Mapping onto gfx950:
 // * A workgroup (4 wavefronts) owns a range of blocks of one unit and walks it
-//   in steps of 16 blocks.  The read channels are cut into segments of whole
-//   8-channel chunks holding at most 128 plane rows, so the LDS footprint is
-//   fixed (~36 KB) whatever the depth vector.  Per (step, segment) the
-//   workgroup stages into LDS, with coalesced reads, the segment's plane words
-//   (rows of 16 consecutive blocks, split into 32-bit halves, the sign plane
-//   complemented) and, per (block, channel, head), A_hj split into bf16 hi + lo
-//   parts plus per-wavefront partial sums of the per-(block, head) constant.
-//   Every global load of a (step, segment) is issued before the first is
-//   used, and several resident workgroups per CU overlap one step's loads
-//   with another's arithmetic.
-// * Read channels are ordered deepest first, so an 8-channel chunk nearly
-//   always has one depth and its Horner loop runs without per-channel
-//   branches (a bit-field width of 0 idles a shallower channel).
-// * Wavefront w scores blocks 4w .. 4w+3 of the step, lane i <-> token i.  For
-//   a read channel a lane reads its half-word of each plane for the four
-//   blocks with one 16-byte LDS read per plane and assembles z by a Horner
-//   chain of bit-field extracts (a signed extract of the complemented sign
-//   bit gives b0 - 1).
+//   in steps of 16 blocks.  The read planes are listed channel by channel,
+//   padded to whole 8-row chunks (padding rows have A = 0) and cut into
+//   segments of 64 rows, so the LDS footprint is fixed whatever the depths.
+//   Per (step, segment) the workgroup stages into LDS, with coalesced global
+//   reads: the plane words, complemented and interleaved in pairs of rows at a
+//   16-bit stride (dword (pair, g, block) = 16 tokens of row 2q in its low half
+//   and of row 2q+1 in its high half), and A split into bf16 hi + lo parts per
+//   (block, chunk, head).  The block scales are loaded once per step and kept
+//   in registers by the thread that applies them.  The global loads of the next
+//   (step, segment) are in flight while the current one is scored.
+// * Wavefront w scores blocks 4w .. 4w+3 of the step, lane i <-> token i.  One
+//   16-byte LDS read gives a row pair's dword for the four blocks; a funnel
+//   rotation by a per-lane constant moves the lane's two bits to the bf16 sign
+//   positions, and one and-or makes the pair (+-1.0, +-1.0): two VALU
+//   operations per two planes of a token.
 // * The G-head contraction runs on the matrix cores: v_mfma_f32_16x16x32_bf16
-//   with B = 8 channels' z values of the lane's token (exact in bf16) and A
-//   block-diagonal over the four 16-lane token groups (row 4g + h of A is
-//   nonzero only in token group g's k-range), so D row 4g + h, column n is
-//   head h's partial score of token 16g + n and each lane ends with the G
-//   scores of its own token.  The hi + lo split of A keeps each term within
-//   ~2^-17 of its exact value.
+//   with B = the lane's 8 rows of the chunk and A block-diagonal over the four
+//   16-lane token groups (row 4g + h of A is nonzero only in token group g's
+//   k-range), so D row 4g + h, column n is head h's partial score of token
+//   16g + n and each lane ends with the G scores of its own token.  The hi + lo
+//   split keeps each term within ~2^-17 of its exact value.
 #include "bpk_internal.h"
 
 namespace bpk {
 namespace {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float floatx2;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float floatx4;
 
 constexpr int SCAN_THREADS = 256;
 constexpr int SCAN_WAVES = SCAN_THREADS / 64;
-constexpr int NB = 4;                 // blocks per wavefront per step
-constexpr int GB = NB * SCAN_WAVES;   // blocks per workgroup step
-constexpr int SEG_ROWS = 128;         // plane rows staged per segment
-constexpr int SEG_CHUNKS = 8;         // 8-channel chunks per segment
-constexpr int MAX_SEGS = D / 8;       // one chunk per segment at worst
+constexpr int NB = 4;                       // blocks per wavefront per step
+constexpr int GB = NB * SCAN_WAVES;         // blocks per workgroup step
+constexpr int SEG_ROWS = 64;                // plane rows staged per segment
+constexpr int SEG_PAIRS = SEG_ROWS / 2;
+constexpr int SEG_CHUNKS = SEG_ROWS / 8;    // 8-row chunks (one MFMA k-range each)
+constexpr int MAX_ROWS = NP * D;
+constexpr int SC_PER = D * GB / SCAN_THREADS;  // block scales a thread keeps per step
 static_assert(SCAN_MIN_WG_BLOCKS == GB, "a workgroup takes whole steps");
 static_assert(SAMPLE_GROUP % GB == 0 && SAMPLE_STRIDE % SAMPLE_GROUP == 0, "sample plan");
+static_assert(SEG_PAIRS * (GB / 2) == SCAN_THREADS, "one (row pair, block pair) per thread");
 
 // What a launch does with the scores it computes:
 // * SCAN_FULL writes every score ([unit][G][cap]);
@@ -102,71 +107,42 @@ __device__ __forceinline__ void cand_append(bool pred, float s, long long tok, i
   }
 }
 
-__device__ __forceinline__ uint16_t bf16_rne_bits(float x) {
-  const uint32_t b = __float_as_uint(x);
-  return (uint16_t)((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16);
-}
-
-// z = c' - 2^(t-1) of the 8 channels of a chunk for the wavefront's 4 blocks.
-// `base` is the lane's half-word of block 0 in plane row 0; row r is 2*GB
-// dwords further.  All reads of a plane level are issued before they are
-// used; a channel shallower than the level gets bit-field width 0 (no shift,
-// no bit), a padding slot (t = 0) width 0 throughout (z = 0).
-template <int TMAX>
-__device__ __forceinline__ void chunk_codes(const uint32_t* base, const int rr[8], const int tc[8],
-                                            int bitpos, int z[8][NB]) {
-#pragma unroll
-  for (int cc = 0; cc < 8; ++cc) {
-    const uint32_t* row = base + rr[cc] * (2 * GB);
-    const uint4 w0 = *reinterpret_cast<const uint4*>(row);
-    const int wd0 = (int)((0u - (uint32_t)tc[cc]) >> 31);  // 1 if t > 0
-    // plane 0 is stored complemented: a signed extract gives b0 - 1
-    z[cc][0] = __builtin_amdgcn_sbfe(w0.x, bitpos, wd0);
-    z[cc][1] = __builtin_amdgcn_sbfe(w0.y, bitpos, wd0);
-    z[cc][2] = __builtin_amdgcn_sbfe(w0.z, bitpos, wd0);
-    z[cc][3] = __builtin_amdgcn_sbfe(w0.w, bitpos, wd0);
-#pragma unroll
-    for (int p = 1; p < TMAX; ++p) {
-      const uint4 w = *reinterpret_cast<const uint4*>(row + p * (2 * GB));
-      const int wd = (int)(((uint32_t)p - (uint32_t)tc[cc]) >> 31);  // 1 if t > p
-      z[cc][0] = (z[cc][0] << wd) | __builtin_amdgcn_ubfe(w.x, bitpos, wd);
-      z[cc][1] = (z[cc][1] << wd) | __builtin_amdgcn_ubfe(w.y, bitpos, wd);
-      z[cc][2] = (z[cc][2] << wd) | __builtin_amdgcn_ubfe(w.z, bitpos, wd);
-      z[cc][3] = (z[cc][3] << wd) | __builtin_amdgcn_ubfe(w.w, bitpos, wd);
-    }
-  }
+// (x0, x1) -> bf16 hi parts (round to nearest even) and bf16 lo parts of the
+// exact fp32 residuals, each packed low = x0, high = x1
+__device__ __forceinline__ void split2(float x0, float x1, uint32_t* hi, uint32_t* lo) {
+  const floatx2 x = {x0, x1};
+  const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
+  const floatx2 r = {x0 - __uint_as_float(h << 16), x1 - __uint_as_float(h & 0xFFFF0000u)};
+  *hi = h;
+  *lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2));
 }
 
 // 128-bit LDS accesses must be 16-byte aligned (misaligned ones stall)
 template <int G>
 struct ScanSmem {
   static constexpr int HG = (G + 3) / 4;  // head groups of 4 (MFMA rows)
-  int scan_buf[D];
-  uint8_t sel_j[D];
-  uint8_t sel_t[D];                // depth of read channel c (0 past the last)
-  uint16_t sel_pb[D];              // first plane row of read channel c
-  int counts[4];                   // read channels, planes, segments
-  int seg_c[MAX_SEGS + 1];         // first read channel of each segment
-  uint64_t chan_sc[D];             // offset of the scales of read channel c; its plane 0
-                                   // starts at word 4 * chan_sc[c] (planes [D][4][nbcap])
-  uint8_t row_c[NP * D];           // plane row -> read channel
-  uint8_t row_p[NP * D];           // plane row -> plane
-  alignas(16) float qc[D * G];     // q_hj * 2^(4 - t_j) of read channel c
-  alignas(16) uint32_t words[SEG_ROWS + 4][2][GB];  // [row][half][block] (+4 rows of slack)
-  // A hi/lo per block: [chunk][hg][part][h][ch] bf16, rows padded by 16 bytes so
-  // that the 16 blocks of a staging write land in different LDS banks
+  int scan_buf[D];                 // plan: prefix sums of (rows, read channels)
+  uint8_t row_j[MAX_ROWS];         // channel of each plane row
+  uint8_t row_p[MAX_ROWS];         // plane of each plane row
+  uint8_t slot_j[D];               // read channel slot -> channel
+  uint8_t slot_t[D];               // its depth
+  uint16_t slot_r0[D];             // its first plane row
+  alignas(16) float qc[D * G];     // q_hj (scan basis)
+  alignas(16) uint32_t words[SEG_PAIRS][4][GB];  // [row pair][token group][block]
+  // A hi/lo per block: [chunk][hg][part][h][row] bf16, each block's table
+  // padded by 16 bytes so that the 16 blocks of a staging write land in
+  // different LDS banks
   static constexpr int ASTRIDE = SEG_CHUNKS * HG * 2 * 4 * 8 + 8;
   alignas(16) uint16_t atab[GB][ASTRIDE];
-  alignas(16) float cpart[SCAN_WAVES][GB][G];  // per-wavefront partial sums of A / 2
-  int ccount[G];                               // candidates of this workgroup per head
+  alignas(16) uint32_t zero4[4];   // the A operand of lanes off the block diagonal
+  int ccount[G];                   // candidates of this workgroup per head
 };
 
 template <int G, int MODE>
-__global__ __launch_bounds__(SCAN_THREADS) __attribute__((amdgpu_waves_per_eu(4, 8)))
-void scan_kernel(ScanArgs a) {
+__global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(ScanArgs a) {
   using SM = ScanSmem<G>;
   constexpr int HG = SM::HG;
-  // offset of the 8 channels of (chunk k, head group hg, part, head h) in a block's A row
+  // offset of the 8 rows of (chunk k, head group hg, part, head h) in a block's A table
   auto a_index = [](int k, int hg, int part, int h) { return (((k * HG + hg) * 2 + part) * 4 + h) * 8; };
   __shared__ __attribute__((aligned(16))) SM sm;
 
@@ -216,16 +192,17 @@ void scan_kernel(ScanArgs a) {
     }
   };
 
-  // ---- plan: the read channels (t_j >= 1) sorted by depth, deepest first (j
-  // ascending within a depth), so an 8-channel chunk is almost always of one
-  // depth.  scan_buf packs four 8-bit counters, one per depth.
+  // ---- plan: plane rows channel by channel (j ascending, p ascending), and
+  // the read channels in slots.  scan_buf packs (rows << 8 | read channels).
   int tj = 0;
   if (MODE == SCAN_CAND && tid < G) sm.ccount[tid] = 0;
+  if (tid < 4) sm.zero4[tid] = 0u;
   if (tid < D) {
-    sm.sel_t[tid] = 0;
     tj = a.depth[(long long)u * D + tid];
     tj = tj > NP ? NP : tj;
-    sm.scan_buf[tid] = tj > 0 ? 1 << (8 * (tj - 1)) : 0;
+    sm.scan_buf[tid] = (tj << 8) | (tj > 0 ? 1 : 0);
+#pragma unroll
+    for (int h = 0; h < G; ++h) sm.qc[tid * G + h] = a.q_basis[((long long)u * G + h) * D + tid];
   }
   __syncthreads();
   for (int off = 1; off < D; off <<= 1) {
@@ -236,102 +213,67 @@ void scan_kernel(ScanArgs a) {
     __syncthreads();
   }
   const int tot = sm.scan_buf[D - 1];
-  const int n4 = (tot >> 24) & 0xFF, n3 = (tot >> 16) & 0xFF, n2 = (tot >> 8) & 0xFF,
-            n1 = tot & 0xFF;
+  const int R = tot >> 8, C = tot & 0xFF;
+  const int Rp = (R + 7) & ~7;                      // whole 8-row chunks
+  const int nseg = (Rp + SEG_ROWS - 1) / SEG_ROWS;
   if (tid < D && tj > 0) {
-    const int k = ((sm.scan_buf[tid] >> (8 * (tj - 1))) & 0xFF) - 1;  // rank within its depth
-    const int cbase = tj == 4 ? 0 : tj == 3 ? n4 : tj == 2 ? n4 + n3 : n4 + n3 + n2;
-    const int rbase0 = tj == 4 ? 0 : tj == 3 ? 4 * n4 : tj == 2 ? 4 * n4 + 3 * n3
-                                                               : 4 * n4 + 3 * n3 + 2 * n2;
-    const int c = cbase + k;
-    const int pb = rbase0 + k * tj;
-    sm.sel_j[c] = (uint8_t)tid;
-    sm.sel_t[c] = (uint8_t)tj;
-    sm.sel_pb[c] = (uint16_t)pb;
-    sm.chan_sc[c] = (uint64_t)(gu * D + tid) * (uint64_t)nbcap;
+    const int incl = sm.scan_buf[tid];
+    const int r0 = (incl >> 8) - tj, c = (incl & 0xFF) - 1;
+    sm.slot_j[c] = (uint8_t)tid;
+    sm.slot_t[c] = (uint8_t)tj;
+    sm.slot_r0[c] = (uint16_t)r0;
     for (int p = 0; p < tj; ++p) {
-      sm.row_c[pb + p] = (uint8_t)c;
-      sm.row_p[pb + p] = (uint8_t)p;
+      sm.row_j[r0 + p] = (uint8_t)tid;
+      sm.row_p[r0 + p] = (uint8_t)p;
     }
-    const float w = (float)(1 << (NP - tj));
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-      sm.qc[c * G + h] = a.q_basis[((long long)u * G + h) * D + tid] * w;
   }
   __syncthreads();
-  if (tid == 0) {
-    // segments: whole chunks, at most SEG_CHUNKS chunks and SEG_ROWS rows
-    const int C = n4 + n3 + n2 + n1;
-    const int P = 4 * n4 + 3 * n3 + 2 * n2 + n1;
-    int ns = 0, c = 0;
-    while (c < C) {
-      sm.seg_c[ns++] = c;
-      int rows = 0, chunks = 0;
-      while (c < C && chunks < SEG_CHUNKS) {
-        const int ce = (c + 8) < C ? (c + 8) : C;
-        const int r = (int)sm.sel_pb[ce - 1] + sm.sel_t[ce - 1] - sm.sel_pb[c];
-        if (chunks > 0 && rows + r > SEG_ROWS) break;
-        rows += r;
-        c = ce;
-        ++chunks;
-      }
-    }
-    sm.seg_c[ns] = C;
-    sm.counts[0] = C;
-    sm.counts[1] = P;
-    sm.counts[2] = ns;
-  }
-  __syncthreads();
-  const int C = sm.counts[0];
-  const int nseg = sm.counts[2];
 
   // A-operand ownership: lane l holds row 4*(l/16) + (l%4) of a head group,
   // in k-group l/16, only when (l%16)/4 == l/16 (block-diagonal).
   const bool a_active = ((lane & 15) >> 2) == (lane >> 4) && (lane & 3) < (G < 4 ? G : 4);
   const int a_hh = lane & 3;
-  const int half = lane >> 5, bitpos = lane & 31;
+  const int grp = lane >> 4;                        // token group of the lane
+  const uint32_t rot = (uint32_t)(((lane & 15) + 17) & 31);  // bit (lane%16) -> bit 15
   const int wb = NB * wave;
 
   // ---- tasks = (16-block step, segment); the loads of task i+1 are in flight
   // while task i is scored ----
   const int nsteps = (int)((wb1 - wb0 + GB - 1) / GB);
   const int ntask = nsteps * nseg;
-  constexpr int PER = SEG_ROWS * (GB / 2) / SCAN_THREADS;   // word pairs per thread
-  constexpr int PERS = SEG_CHUNKS * 8 * GB / SCAN_THREADS;  // scales per thread
-  const int sb = tid % GB;  // block of this thread's scales (same for every i)
-  uint64_t w[PER][2];
-  float sv[PERS];
+  const int sb = tid % GB;                 // block of this thread's scales
+  const int pr = tid / (GB / 2), bp = 2 * (tid % (GB / 2));  // row pair, first block
+  uint64_t w[2][2];                        // [row of the pair][block]
+  float sv[SC_PER];                        // scales of slots tid/16 + 16 i, block sb
   auto issue_loads = [&](int task) {
     const long long g0 = wb0 + (long long)(task / nseg) * GB;
     const int sg = task % nseg;
     const int gblk = (wb1 - g0) < GB ? (int)(wb1 - g0) : GB;
-    const int cs0 = sm.seg_c[sg], cs1 = sm.seg_c[sg + 1];
-    const int rbase = sm.sel_pb[cs0];
-    const int nrows = (int)sm.sel_pb[cs1 - 1] + sm.sel_t[cs1 - 1] - rbase;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int e = tid + i * SCAN_THREADS;
-      const int rr = e / (GB / 2), b2 = 2 * (e % (GB / 2));
-      w[i][0] = 0;
-      w[i][1] = 0;
-      if (rr < nrows) {
-        const int r = rbase + rr;
-        const int c = sm.row_c[r], p = sm.row_p[r];
-        const uint64_t* src = a.planes + NP * sm.chan_sc[c] + (uint64_t)p * nbcap + g0 + b2;
-        if (b2 + 1 < gblk) {  // rows are 8-byte aligned only
-          w[i][0] = src[0];
-          w[i][1] = src[1];
-        } else if (b2 < gblk) {
-          w[i][0] = src[0];
+    for (int q = 0; q < 2; ++q) {
+      const int r = sg * SEG_ROWS + 2 * pr + q;
+      w[q][0] = 0;
+      w[q][1] = 0;
+      if (r < R) {
+        const uint64_t* src = a.planes +
+                              ((uint64_t)(gu * D + sm.row_j[r]) * NP + sm.row_p[r]) * nbcap + g0 + bp;
+        if (bp + 1 < gblk) {  // rows are 8-byte aligned only
+          w[q][0] = src[0];
+          w[q][1] = src[1];
+        } else if (bp < gblk) {
+          w[q][0] = src[0];
         }
       }
     }
+    if (sg == 0) {
 #pragma unroll
-    for (int i = 0; i < PERS; ++i) {
-      const int c = cs0 + (tid + i * SCAN_THREADS) / GB;
-      sv[i] = 0.f;
-      if (c < cs1 && sb < gblk)
-        sv[i] = (float)__builtin_bit_cast(_Float16, a.scales[sm.chan_sc[c] + g0 + sb]);
+      for (int i = 0; i < SC_PER; ++i) {
+        const int c = tid / GB + i * (SCAN_THREADS / GB);
+        sv[i] = 0.f;
+        if (c < C && sb < gblk)
+          sv[i] = (float)__builtin_bit_cast(
+              _Float16, a.scales[(uint64_t)(gu * D + sm.slot_j[c]) * nbcap + g0 + sb]);
+      }
     }
   };
 
@@ -344,143 +286,102 @@ void scan_kernel(ScanArgs a) {
     return;
   }
   floatx4 acc[NB][HG];
-  bf16x8 ahi, alo;  // A operand (hi, lo parts); zero on the block-diagonal's idle lanes
-  {
-    const uint32_t z4[4] = {0u, 0u, 0u, 0u};
-    __builtin_memcpy(&ahi, z4, 16);
-    __builtin_memcpy(&alo, z4, 16);
-  }
   issue_loads(0);
   for (int task = 0; task < ntask; ++task) {
     const long long g0 = wb0 + (long long)(task / nseg) * GB;
     const int sg = task % nseg;
     const int gblk = (wb1 - g0) < GB ? (int)(wb1 - g0) : GB;
+    const int seg_r0 = sg * SEG_ROWS;
+    const int nck = ((Rp - seg_r0) < SEG_ROWS ? (Rp - seg_r0) : SEG_ROWS) >> 3;
     if (sg == 0) {
 #pragma unroll
       for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int hg = 0; hg < HG; ++hg) acc[b][hg] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
-    {
-      const int cs0 = sm.seg_c[sg], cs1 = sm.seg_c[sg + 1];
-      const int rbase = sm.sel_pb[cs0];
-      const int nrows = (int)sm.sel_pb[cs1 - 1] + sm.sel_t[cs1 - 1] - rbase;
-      const int nck = (cs1 - cs0 + 7) >> 3;
-      __syncthreads();  // the previous task's tables are no longer read
+    __syncthreads();  // the previous task's tables are no longer read
 
-      // ---- words -> LDS (the sign plane complemented) ----
+    // ---- plane words -> LDS: complemented, row pairs interleaved at 16 bits ----
+    if (2 * pr < nck * 8) {
 #pragma unroll
-      for (int i = 0; i < PER; ++i) {
-        const int e = tid + i * SCAN_THREADS;
-        const int rr = e / (GB / 2), b2 = 2 * (e % (GB / 2));
-        if (rr < nrows) {
-          if (sm.row_p[rbase + rr] == 0) {
-            w[i][0] = ~w[i][0];
-            w[i][1] = ~w[i][1];
+      for (int gq = 0; gq < 4; ++gq) {
+        const uint32_t sel = (gq & 1) ? 0x07060302u : 0x05040100u;
+        uint32_t d[2];
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb) {
+          const uint32_t x0 = (uint32_t)(w[0][bb] >> (32 * (gq >> 1)));
+          const uint32_t x1 = (uint32_t)(w[1][bb] >> (32 * (gq >> 1)));
+          d[bb] = ~__builtin_amdgcn_perm(x1, x0, sel);
+        }
+        *reinterpret_cast<uint2*>(&sm.words[pr][gq][bp]) = make_uint2(d[0], d[1]);
+      }
+    }
+    // ---- A = q_hj s_bj 2^(2-p), bf16 hi + lo, by the thread holding s_bj ----
+#pragma unroll
+    for (int i = 0; i < SC_PER; ++i) {
+      const int c = tid / GB + i * (SCAN_THREADS / GB);
+      if (c < C) {
+        const int r0 = sm.slot_r0[c], t = sm.slot_t[c], j = sm.slot_j[c];
+        float f = 4.f * sv[i];
+        for (int p = 0; p < t; ++p, f *= 0.5f) {
+          const int lr = r0 + p - seg_r0;
+          if (lr < 0 || lr >= SEG_ROWS) continue;
+          const int k = lr >> 3, i8 = lr & 7;
+#pragma unroll
+          for (int h0 = 0; h0 < G; h0 += 2) {
+            const float x0 = sm.qc[j * G + h0] * f;
+            const float x1 = h0 + 1 < G ? sm.qc[j * G + h0 + 1] * f : 0.f;
+            uint32_t hi, lo;
+            split2(x0, x1, &hi, &lo);
+            sm.atab[sb][a_index(k, h0 >> 2, 0, h0 & 3) + i8] = (uint16_t)hi;
+            sm.atab[sb][a_index(k, h0 >> 2, 1, h0 & 3) + i8] = (uint16_t)lo;
+            if (h0 + 1 < G) {
+              sm.atab[sb][a_index(k, (h0 + 1) >> 2, 0, (h0 + 1) & 3) + i8] = (uint16_t)(hi >> 16);
+              sm.atab[sb][a_index(k, (h0 + 1) >> 2, 1, (h0 + 1) & 3) + i8] = (uint16_t)(lo >> 16);
+            }
           }
-          *reinterpret_cast<uint2*>(&sm.words[rr][0][b2]) =
-              make_uint2((uint32_t)w[i][0], (uint32_t)w[i][1]);
-          *reinterpret_cast<uint2*>(&sm.words[rr][1][b2]) =
-              make_uint2((uint32_t)(w[i][0] >> 32), (uint32_t)(w[i][1] >> 32));
         }
       }
-      // ---- A = q_hj s_bj 2^(4-t_j) as bf16 hi + lo, partial sums of A / 2 ----
-      float part[G];
-#pragma unroll
-      for (int h = 0; h < G; ++h) part[h] = 0.f;
-#pragma unroll
-      for (int i = 0; i < PERS; ++i) {
-        const int cl = (tid + i * SCAN_THREADS) / GB;
-        if (cl < nck * 8) {
-          const int c = cs0 + cl;
-#pragma unroll
-          for (int h = 0; h < G; ++h) {
-            const float x = c < cs1 ? sm.qc[c * G + h] * sv[i] : 0.f;
-            part[h] += 0.5f * x;
-            const uint16_t hi = bf16_rne_bits(x);
-            const uint16_t lo = bf16_rne_bits(x - __uint_as_float((uint32_t)hi << 16));
-            sm.atab[sb][a_index(cl >> 3, h >> 2, 0, h & 3) + (cl & 7)] = hi;
-            sm.atab[sb][a_index(cl >> 3, h >> 2, 1, h & 3) + (cl & 7)] = lo;
-          }
-        }
+    }
+    // padding rows of the last chunk: A = 0
+    if (seg_r0 + nck * 8 > R) {
+      const int lr0 = R - seg_r0, npad = seg_r0 + nck * 8 - R;
+      for (int e = tid; e < npad * GB * G * 2; e += SCAN_THREADS) {
+        const int b = e % GB, x = e / GB;
+        const int part = x & 1, h = (x >> 1) % G, lr = lr0 + (x >> 1) / G;
+        sm.atab[b][a_index(lr >> 3, h >> 2, part, h & 3) + (lr & 7)] = 0;
       }
-      // lanes l, l+16, l+32, l+48 share a block: fixed-order reduction
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        part[h] += __shfl_xor(part[h], 16);
-        part[h] += __shfl_xor(part[h], 32);
-      }
-      if (lane < GB) {
-#pragma unroll
-        for (int h = 0; h < G; ++h) sm.cpart[wave][lane][h] = part[h];
-      }
-      __syncthreads();
-      if (task + 1 < ntask) issue_loads(task + 1);  // in flight during the scoring below
+    }
+    __syncthreads();
+    if (task + 1 < ntask) issue_loads(task + 1);  // in flight during the scoring below
 
-      // ---- score the segment: wavefront takes blocks wb .. wb+3 of the step ----
-      if (wb < gblk) {
-        // the constant sum_j A_hj / 2 enters the accumulator of (token, head 4hg + r)
+    // ---- score the segment: wavefront takes blocks wb .. wb+3 of the step ----
+    if (wb < gblk) {
+      for (int k = 0; k < nck; ++k) {
+        uint4 v[4];
 #pragma unroll
-        for (int b = 0; b < NB; ++b)
+        for (int q = 0; q < 4; ++q)
+          v[q] = *reinterpret_cast<const uint4*>(&sm.words[4 * k + q][grp][wb]);
 #pragma unroll
-          for (int hg = 0; hg < HG; ++hg)
+        for (int b = 0; b < NB; ++b) {
+          uint32_t bw[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int h = 4 * hg + r;
-              if (h < G) {
-                float cs = 0.f;
-#pragma unroll
-                for (int ww = 0; ww < SCAN_WAVES; ++ww) cs += sm.cpart[ww][wb + b][h];
-                acc[b][hg][r] += cs;
-              }
-            }
-
-        for (int kl = 0; kl < nck; ++kl) {
-          const int cb = cs0 + 8 * kl;
-          // the chunk's depths and first rows, wave-uniform
-          const uint32_t t03 = __builtin_amdgcn_readfirstlane(*reinterpret_cast<const uint32_t*>(&sm.sel_t[cb]));
-          const uint32_t t47 = __builtin_amdgcn_readfirstlane(*reinterpret_cast<const uint32_t*>(&sm.sel_t[cb + 4]));
-          uint32_t pbw[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            pbw[i] = __builtin_amdgcn_readfirstlane(*reinterpret_cast<const uint32_t*>(&sm.sel_pb[cb + 2 * i]));
-          // chunk channels are sorted by depth: channel 0 is the deepest
-          const int tmax = (int)(t03 & 0xFFu);
-          int tc[8], rr[8], z[8][NB];
-#pragma unroll
-          for (int cc = 0; cc < 8; ++cc) {
-            tc[cc] = (int)(((cc < 4 ? t03 : t47) >> (8 * (cc & 3))) & 0xFFu);
-            // a padding slot (t = 0) reads row 0 of the segment with width 0: z = 0
-            rr[cc] = tc[cc] > 0 ? (int)((pbw[cc >> 1] >> (16 * (cc & 1))) & 0xFFFFu) - rbase : 0;
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t x = b == 0 ? v[q].x : b == 1 ? v[q].y : b == 2 ? v[q].z : v[q].w;
+            // the lane's bits of rows 2q and 2q+1 at the sign bits of a bf16 pair
+            bw[q] = (__builtin_amdgcn_alignbit(x, x, rot) & 0x80008000u) | 0x3F803F80u;
           }
-          switch (tmax) {
-            case 1: chunk_codes<1>(&sm.words[0][half][wb], rr, tc, bitpos, z); break;
-            case 2: chunk_codes<2>(&sm.words[0][half][wb], rr, tc, bitpos, z); break;
-            case 3: chunk_codes<3>(&sm.words[0][half][wb], rr, tc, bitpos, z); break;
-            default: chunk_codes<4>(&sm.words[0][half][wb], rr, tc, bitpos, z); break;
-          }
-          // bf16 pairs of z (exact): the high halves of their fp32 values
-          uint32_t bw[NB][4];
+          bf16x8 bv;
+          __builtin_memcpy(&bv, bw, 16);
 #pragma unroll
-          for (int b = 0; b < NB; ++b)
-#pragma unroll
-            for (int cp = 0; cp < 4; ++cp)
-              bw[b][cp] = __builtin_amdgcn_perm(__float_as_uint((float)z[2 * cp + 1][b]),
-                                                __float_as_uint((float)z[2 * cp][b]), 0x07060302u);
-#pragma unroll
-          for (int b = 0; b < NB; ++b) {
-            bf16x8 bv;
-            __builtin_memcpy(&bv, bw[b], 16);
-#pragma unroll
-            for (int hg = 0; hg < HG; ++hg) {
-              // inactive lanes keep the zeros they were given once
-              if (a_active) {
-                ahi = *reinterpret_cast<const bf16x8*>(&sm.atab[wb + b][a_index(kl, hg, 0, a_hh)]);
-                alo = *reinterpret_cast<const bf16x8*>(&sm.atab[wb + b][a_index(kl, hg, 1, a_hh)]);
-              }
-              acc[b][hg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, bv, acc[b][hg], 0, 0, 0);
-              acc[b][hg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, bv, acc[b][hg], 0, 0, 0);
-            }
+          for (int hg = 0; hg < HG; ++hg) {
+            const uint16_t* ap = a_active ? &sm.atab[wb + b][a_index(k, hg, 0, a_hh)]
+                                          : reinterpret_cast<const uint16_t*>(sm.zero4);
+            const uint16_t* aq = a_active ? ap + 4 * 8 : ap;
+            const bf16x8 ahi = *reinterpret_cast<const bf16x8*>(ap);
+            const bf16x8 alo = *reinterpret_cast<const bf16x8*>(aq);
+            acc[b][hg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, bv, acc[b][hg], 0, 0, 0);
+            acc[b][hg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, bv, acc[b][hg], 0, 0, 0);
           }
         }
       }
