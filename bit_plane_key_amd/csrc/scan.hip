@@ -17,17 +17,18 @@
 //   padded to whole 8-row chunks (padding rows have A = 0) and cut into
 //   segments of 64 rows, so the LDS footprint is fixed whatever the depths.
 //   Per (step, segment) the workgroup stages into LDS, with coalesced global
-//   reads: the plane words, complemented and interleaved in pairs of rows at a
-//   16-bit stride (dword (pair, g, block) = 16 tokens of row 2q in its low half
-//   and of row 2q+1 in its high half), and A split into bf16 hi + lo parts per
-//   (block, chunk, head).  The block scales are loaded once per step and kept
-//   in registers by the thread that applies them.  The global loads of the next
-//   (step, segment) are in flight while the current one is scored.
+//   reads: the plane words, interleaved in pairs of rows at a 16-bit stride
+//   (dword (pair, g, block) = 16 tokens of row 2q in its low half and of row
+//   2q+1 in its high half), and A split into bf16 hi + lo parts per (block,
+//   chunk, head): each thread takes (row, block) items, multiplying the row's
+//   -q_hj 2^(2-p) (tabled once per workgroup) by the block scale it loaded.
+//   The global loads of the next (step, segment) are in flight while the
+//   current one is scored.
 // * Wavefront w scores blocks 4w .. 4w+3 of the step, lane i <-> token i.  One
 //   16-byte LDS read gives a row pair's dword for the four blocks; a funnel
 //   rotation by a per-lane constant moves the lane's two bits to the bf16 sign
-//   positions, and one and-or makes the pair (+-1.0, +-1.0): two VALU
-//   operations per two planes of a token.
+//   positions, and one and-or makes the pair (-B, -B) = (+-1.0, +-1.0) (A is
+//   negated to match): two VALU operations per two planes of a token.
 // * The G-head contraction runs on the matrix cores: v_mfma_f32_16x16x32_bf16
 //   with B = the lane's 8 rows of the chunk and A block-diagonal over the four
 //   16-lane token groups (row 4g + h of A is nonzero only in token group g's
@@ -52,10 +53,20 @@ constexpr int SEG_ROWS = 64;                // plane rows staged per segment
 constexpr int SEG_PAIRS = SEG_ROWS / 2;
 constexpr int SEG_CHUNKS = SEG_ROWS / 8;    // 8-row chunks (one MFMA k-range each)
 constexpr int MAX_ROWS = NP * D;
-constexpr int SC_PER = D * GB / SCAN_THREADS;  // block scales a thread keeps per step
+constexpr int SC_PER = SEG_ROWS * GB / SCAN_THREADS;  // (row, block) items per thread
 static_assert(SCAN_MIN_WG_BLOCKS == GB, "a workgroup takes whole steps");
 static_assert(SAMPLE_GROUP % GB == 0 && SAMPLE_STRIDE % SAMPLE_GROUP == 0, "sample plan");
 static_assert(SEG_PAIRS * (GB / 2) == SCAN_THREADS, "one (row pair, block pair) per thread");
+static_assert(SCAN_THREADS % GB == 0 && SEG_ROWS % (SCAN_THREADS / GB) == 0, "row items");
+
+// bf16 pair (-1)^(bit 15 of x) * 1.0, (-1)^(bit 31 of x) * 1.0.  Written out
+// because the and-or form needs its two constants in registers (a VOP3
+// instruction takes no literal here); mask is wave-uniform, one a register.
+__device__ __forceinline__ uint32_t sign_pair(uint32_t x, uint32_t mask, uint32_t one) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(mask), "v"(one));
+  return r;
+}
 
 // What a launch does with the scores it computes:
 // * SCAN_FULL writes every score ([unit][G][cap]);
@@ -121,13 +132,10 @@ __device__ __forceinline__ void split2(float x0, float x1, uint32_t* hi, uint32_
 template <int G>
 struct ScanSmem {
   static constexpr int HG = (G + 3) / 4;  // head groups of 4 (MFMA rows)
-  int scan_buf[D];                 // plan: prefix sums of (rows, read channels)
+  int scan_buf[D];                 // plan: prefix sums of the depths
   uint8_t row_j[MAX_ROWS];         // channel of each plane row
   uint8_t row_p[MAX_ROWS];         // plane of each plane row
-  uint8_t slot_j[D];               // read channel slot -> channel
-  uint8_t slot_t[D];               // its depth
-  uint16_t slot_r0[D];             // its first plane row
-  alignas(16) float qc[D * G];     // q_hj (scan basis)
+  alignas(16) float fq[MAX_ROWS][G];  // -q_hj 2^(2-p) of each row (0 for padding rows)
   alignas(16) uint32_t words[SEG_PAIRS][4][GB];  // [row pair][token group][block]
   // A hi/lo per block: [chunk][hg][part][h][row] bf16, each block's table
   // padded by 16 bytes so that the 16 blocks of a staging write land in
@@ -192,17 +200,14 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(ScanArgs a) {
     }
   };
 
-  // ---- plan: plane rows channel by channel (j ascending, p ascending), and
-  // the read channels in slots.  scan_buf packs (rows << 8 | read channels).
+  // ---- plan: plane rows channel by channel (j ascending, p ascending) ----
   int tj = 0;
   if (MODE == SCAN_CAND && tid < G) sm.ccount[tid] = 0;
   if (tid < 4) sm.zero4[tid] = 0u;
   if (tid < D) {
     tj = a.depth[(long long)u * D + tid];
     tj = tj > NP ? NP : tj;
-    sm.scan_buf[tid] = (tj << 8) | (tj > 0 ? 1 : 0);
-#pragma unroll
-    for (int h = 0; h < G; ++h) sm.qc[tid * G + h] = a.q_basis[((long long)u * G + h) * D + tid];
+    sm.scan_buf[tid] = tj;
   }
   __syncthreads();
   for (int off = 1; off < D; off <<= 1) {
@@ -212,20 +217,25 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(ScanArgs a) {
     if (tid < D) sm.scan_buf[tid] += v;
     __syncthreads();
   }
-  const int tot = sm.scan_buf[D - 1];
-  const int R = tot >> 8, C = tot & 0xFF;
+  const int R = sm.scan_buf[D - 1];
   const int Rp = (R + 7) & ~7;                      // whole 8-row chunks
   const int nseg = (Rp + SEG_ROWS - 1) / SEG_ROWS;
   if (tid < D && tj > 0) {
-    const int incl = sm.scan_buf[tid];
-    const int r0 = (incl >> 8) - tj, c = (incl & 0xFF) - 1;
-    sm.slot_j[c] = (uint8_t)tid;
-    sm.slot_t[c] = (uint8_t)tj;
-    sm.slot_r0[c] = (uint16_t)r0;
-    for (int p = 0; p < tj; ++p) {
+    const int r0 = sm.scan_buf[tid] - tj;
+    float qv[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) qv[h] = a.q_basis[((long long)u * G + h) * D + tid];
+    float f = -4.f;
+    for (int p = 0; p < tj; ++p, f *= 0.5f) {
       sm.row_j[r0 + p] = (uint8_t)tid;
       sm.row_p[r0 + p] = (uint8_t)p;
+#pragma unroll
+      for (int h = 0; h < G; ++h) sm.fq[r0 + p][h] = qv[h] * f;
     }
+  }
+  if (tid < Rp - R) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) sm.fq[R + tid][h] = 0.f;
   }
   __syncthreads();
 
@@ -235,16 +245,18 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(ScanArgs a) {
   const int a_hh = lane & 3;
   const int grp = lane >> 4;                        // token group of the lane
   const uint32_t rot = (uint32_t)(((lane & 15) + 17) & 31);  // bit (lane%16) -> bit 15
+  const uint32_t smask = __builtin_amdgcn_readfirstlane(0x80008000u);
+  const uint32_t vone = 0x3F803F80u;
   const int wb = NB * wave;
 
   // ---- tasks = (16-block step, segment); the loads of task i+1 are in flight
   // while task i is scored ----
   const int nsteps = (int)((wb1 - wb0 + GB - 1) / GB);
   const int ntask = nsteps * nseg;
-  const int sb = tid % GB;                 // block of this thread's scales
+  const int sb = tid % GB;                 // block of this thread's (row, block) items
   const int pr = tid / (GB / 2), bp = 2 * (tid % (GB / 2));  // row pair, first block
   uint64_t w[2][2];                        // [row of the pair][block]
-  float sv[SC_PER];                        // scales of slots tid/16 + 16 i, block sb
+  float sv[SC_PER];                        // scales of rows tid/16 + 16 i, block sb
   auto issue_loads = [&](int task) {
     const long long g0 = wb0 + (long long)(task / nseg) * GB;
     const int sg = task % nseg;
@@ -265,15 +277,13 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(ScanArgs a) {
         }
       }
     }
-    if (sg == 0) {
 #pragma unroll
-      for (int i = 0; i < SC_PER; ++i) {
-        const int c = tid / GB + i * (SCAN_THREADS / GB);
-        sv[i] = 0.f;
-        if (c < C && sb < gblk)
-          sv[i] = (float)__builtin_bit_cast(
-              _Float16, a.scales[(uint64_t)(gu * D + sm.slot_j[c]) * nbcap + g0 + sb]);
-      }
+    for (int i = 0; i < SC_PER; ++i) {
+      const int r = sg * SEG_ROWS + tid / GB + i * (SCAN_THREADS / GB);
+      sv[i] = 0.f;
+      if (r < R && sb < gblk)
+        sv[i] = (float)__builtin_bit_cast(
+            _Float16, a.scales[(uint64_t)(gu * D + sm.row_j[r]) * nbcap + g0 + sb]);
     }
   };
 
@@ -301,7 +311,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(ScanArgs a) {
     }
     __syncthreads();  // the previous task's tables are no longer read
 
-    // ---- plane words -> LDS: complemented, row pairs interleaved at 16 bits ----
+    // ---- plane words -> LDS: row pairs interleaved at 16 bits ----
     if (2 * pr < nck * 8) {
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
@@ -311,45 +321,31 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(ScanArgs a) {
         for (int bb = 0; bb < 2; ++bb) {
           const uint32_t x0 = (uint32_t)(w[0][bb] >> (32 * (gq >> 1)));
           const uint32_t x1 = (uint32_t)(w[1][bb] >> (32 * (gq >> 1)));
-          d[bb] = ~__builtin_amdgcn_perm(x1, x0, sel);
+          d[bb] = __builtin_amdgcn_perm(x1, x0, sel);
         }
         *reinterpret_cast<uint2*>(&sm.words[pr][gq][bp]) = make_uint2(d[0], d[1]);
       }
     }
-    // ---- A = q_hj s_bj 2^(2-p), bf16 hi + lo, by the thread holding s_bj ----
+    // ---- A = -q_hj 2^(2-p) s_bj, bf16 hi + lo, per (row, block); padding rows 0 ----
 #pragma unroll
     for (int i = 0; i < SC_PER; ++i) {
-      const int c = tid / GB + i * (SCAN_THREADS / GB);
-      if (c < C) {
-        const int r0 = sm.slot_r0[c], t = sm.slot_t[c], j = sm.slot_j[c];
-        float f = 4.f * sv[i];
-        for (int p = 0; p < t; ++p, f *= 0.5f) {
-          const int lr = r0 + p - seg_r0;
-          if (lr < 0 || lr >= SEG_ROWS) continue;
-          const int k = lr >> 3, i8 = lr & 7;
+      const int lr = tid / GB + i * (SCAN_THREADS / GB);
+      if (lr < nck * 8) {
+        const int k = lr >> 3, i8 = lr & 7;
+        const float* fr = sm.fq[seg_r0 + lr];
 #pragma unroll
-          for (int h0 = 0; h0 < G; h0 += 2) {
-            const float x0 = sm.qc[j * G + h0] * f;
-            const float x1 = h0 + 1 < G ? sm.qc[j * G + h0 + 1] * f : 0.f;
-            uint32_t hi, lo;
-            split2(x0, x1, &hi, &lo);
-            sm.atab[sb][a_index(k, h0 >> 2, 0, h0 & 3) + i8] = (uint16_t)hi;
-            sm.atab[sb][a_index(k, h0 >> 2, 1, h0 & 3) + i8] = (uint16_t)lo;
-            if (h0 + 1 < G) {
-              sm.atab[sb][a_index(k, (h0 + 1) >> 2, 0, (h0 + 1) & 3) + i8] = (uint16_t)(hi >> 16);
-              sm.atab[sb][a_index(k, (h0 + 1) >> 2, 1, (h0 + 1) & 3) + i8] = (uint16_t)(lo >> 16);
-            }
+        for (int h0 = 0; h0 < G; h0 += 2) {
+          const float x0 = fr[h0] * sv[i];
+          const float x1 = h0 + 1 < G ? fr[h0 + 1] * sv[i] : 0.f;
+          uint32_t hi, lo;
+          split2(x0, x1, &hi, &lo);
+          sm.atab[sb][a_index(k, h0 >> 2, 0, h0 & 3) + i8] = (uint16_t)hi;
+          sm.atab[sb][a_index(k, h0 >> 2, 1, h0 & 3) + i8] = (uint16_t)lo;
+          if (h0 + 1 < G) {
+            sm.atab[sb][a_index(k, (h0 + 1) >> 2, 0, (h0 + 1) & 3) + i8] = (uint16_t)(hi >> 16);
+            sm.atab[sb][a_index(k, (h0 + 1) >> 2, 1, (h0 + 1) & 3) + i8] = (uint16_t)(lo >> 16);
           }
         }
-      }
-    }
-    // padding rows of the last chunk: A = 0
-    if (seg_r0 + nck * 8 > R) {
-      const int lr0 = R - seg_r0, npad = seg_r0 + nck * 8 - R;
-      for (int e = tid; e < npad * GB * G * 2; e += SCAN_THREADS) {
-        const int b = e % GB, x = e / GB;
-        const int part = x & 1, h = (x >> 1) % G, lr = lr0 + (x >> 1) / G;
-        sm.atab[b][a_index(lr >> 3, h >> 2, part, h & 3) + (lr & 7)] = 0;
       }
     }
     __syncthreads();
@@ -369,7 +365,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(ScanArgs a) {
           for (int q = 0; q < 4; ++q) {
             const uint32_t x = b == 0 ? v[q].x : b == 1 ? v[q].y : b == 2 ? v[q].z : v[q].w;
             // the lane's bits of rows 2q and 2q+1 at the sign bits of a bf16 pair
-            bw[q] = (__builtin_amdgcn_alignbit(x, x, rot) & 0x80008000u) | 0x3F803F80u;
+            bw[q] = sign_pair(__builtin_amdgcn_alignbit(x, x, rot), smask, vone);
           }
           bf16x8 bv;
           __builtin_memcpy(&bv, bw, 16);
