@@ -181,7 +181,7 @@ int bpk_scan_scores(const bpk_cache_t* c, const float* q_basis, const uint8_t* d
   if (rc) return rc;
   if (!q_basis || !depth || !scores)
     return fail(BPK_EINVAL, "q_basis, depth and scores must be non-NULL");
-  return hip_status(bpk::launch_scan(g, q_basis, depth, c->planes, c->scales, scores,
+  return hip_status(bpk::launch_scan(g, q_basis, depth, c->planes, c->scales, scores, -1,
                                      static_cast<hipStream_t>(stream)),
                     "scan_scores");
 }
@@ -237,6 +237,8 @@ int bpk_decode_step(const bpk_cache_t* c, const uint16_t* q, int32_t l0, int32_t
   float* scores = reinterpret_cast<float*>(base + w.scores);
   int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(base + w.idx);
   hipStream_t st = static_cast<hipStream_t>(stream);
+  // alloc_depth hands out exactly min(P, 4D) planes per unit
+  const int rows = budget_planes < 4 * bpk::D ? budget_planes : 4 * bpk::D;
   rc = hip_status(bpk::launch_alloc(g, q, c->chan_var, c->rot, budget_planes, depth, q_basis, st),
                   "decode_step/alloc");
   if (rc) return rc;
@@ -253,25 +255,25 @@ int bpk_decode_step(const bpk_cache_t* c, const uint16_t* q, int32_t l0, int32_t
     cb.val = reinterpret_cast<float*>(base + w.cval);
     cb.idx = reinterpret_cast<int32_t*>(base + w.cidx);
     cb.flag = reinterpret_cast<int32_t*>(base + w.flag);
-    rc = hip_status(bpk::launch_scan_sample(g, q_basis, depth, c->planes, c->scales, cb, st),
+    rc = hip_status(bpk::launch_scan_sample(g, q_basis, depth, c->planes, c->scales, cb, rows, st),
                     "decode_step/sample scan");
     if (rc) return rc;
     rc = hip_status(bpk::launch_threshold(g, k, cb, st), "decode_step/threshold");
     if (rc) return rc;
-    rc = hip_status(bpk::launch_scan_cand(g, q_basis, depth, c->planes, c->scales, k, cb, st),
+    rc = hip_status(bpk::launch_scan_cand(g, q_basis, depth, c->planes, c->scales, k, cb, rows, st),
                     "decode_step/scan");
     if (rc) return rc;
     rc = hip_status(bpk::launch_cand_select(g, k, cb, idx, st), "decode_step/select");
     if (rc) return rc;
     rc = hip_status(bpk::launch_scan_flagged(g, q_basis, depth, c->planes, c->scales, scores,
-                                             cb.flag, st),
+                                             cb.flag, rows, st),
                     "decode_step/fallback scan");
     if (rc) return rc;
     rc = hip_status(bpk::launch_topk_flagged(g, scores, k, idx, cb.flag, st),
                     "decode_step/fallback select");
     if (rc) return rc;
   } else {
-    rc = hip_status(bpk::launch_scan(g, q_basis, depth, c->planes, c->scales, scores, st),
+    rc = hip_status(bpk::launch_scan(g, q_basis, depth, c->planes, c->scales, scores, rows, st),
                     "decode_step/scan");
     if (rc) return rc;
     rc = hip_status(bpk::launch_topk(g, scores, k, idx, st), "decode_step/select");

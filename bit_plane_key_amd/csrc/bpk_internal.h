@@ -44,8 +44,14 @@ hipError_t launch_append_rows(const Geom& g, int seq, int k_dtype, const void* k
 hipError_t launch_alloc(const Geom& g, const uint16_t* q, const float* chan_var, const float* rot,
                         int budget, uint8_t* depth, float* q_basis, hipStream_t st);
 
+// Every scan launcher takes `rows`, the number of plane rows every unit of
+// the call reads (min(P, 4D) after alloc_depth), or -1 when it is not known:
+// units reading at most SCAN_FAST_ROWS rows go to the fast kernel, the others
+// to the wide one, and with -1 both are launched and each skips the other's
+// units.
+constexpr int SCAN_FAST_ROWS = 128;
 hipError_t launch_scan(const Geom& g, const float* q_basis, const uint8_t* depth,
-                       const uint64_t* planes, const uint16_t* scales, float* scores,
+                       const uint64_t* planes, const uint16_t* scales, float* scores, int rows,
                        hipStream_t st);
 
 hipError_t launch_topk(const Geom& g, const float* scores, int k, int32_t* idx, hipStream_t st);
@@ -100,17 +106,17 @@ __host__ __device__ inline long long sample_groups(const Geom& g) {
 
 hipError_t launch_scan_sample(const Geom& g, const float* q_basis, const uint8_t* depth,
                               const uint64_t* planes, const uint16_t* scales, const CandBufs& cb,
-                              hipStream_t st);
+                              int rows, hipStream_t st);
 hipError_t launch_threshold(const Geom& g, int k, const CandBufs& cb, hipStream_t st);
 hipError_t launch_scan_cand(const Geom& g, const float* q_basis, const uint8_t* depth,
                             const uint64_t* planes, const uint16_t* scales, int k,
-                            const CandBufs& cb, hipStream_t st);
+                            const CandBufs& cb, int rows, hipStream_t st);
 hipError_t launch_cand_select(const Geom& g, int k, const CandBufs& cb, int32_t* idx,
                               hipStream_t st);
 // full scan and radix select of the flagged units only
 hipError_t launch_scan_flagged(const Geom& g, const float* q_basis, const uint8_t* depth,
                                const uint64_t* planes, const uint16_t* scales, float* scores,
-                               const int32_t* flag, hipStream_t st);
+                               const int32_t* flag, int rows, hipStream_t st);
 hipError_t launch_topk_flagged(const Geom& g, const float* scores, int k, int32_t* idx,
                                const int32_t* flag, hipStream_t st);
 

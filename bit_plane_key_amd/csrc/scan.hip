@@ -1,6 +1,8 @@
 // Prefix-plane key scan (Fathom §1, §3.2): approximate scores of every key of
 // every complete block, reading only planes p < t_j of each read channel and
-// the fp16 block scales of those channels.
+// the fp16 block scales of those channels.  This file holds the kernel for
+// units that read at most SCAN_FAST_ROWS plane rows (budgets up to 128
+// planes) and the launchers; scan_wide.hip holds the kernel for the others.
 //
 // Arithmetic.  The t-bit prefix value of a 4-bit code is
 //   m = sum_{p<t} 2^(3-p) b_p + 2^(3-t) - 8 = sum_{p<t} 2^(3-p) (b_p - 1/2)
@@ -21,160 +23,78 @@
 // its own.  Frames depend only on the step's blocks, so scores are
 // bit-identical in every launch mode.
 //
-// Mapping onto gfx950:
-// * A workgroup (4 wavefronts) owns a range of blocks of one unit and walks
-//   it in steps of 16 blocks; the plane rows (channel by channel) are cut into
-//   segments of 128 rows (64 when G = 8) so the LDS footprint is fixed.  Per
-//   (step, segment) task the workgroup stages the 16 words of each row in LDS
-//   (coalesced 128-byte reads, issued one task ahead) and builds, per (block,
-//   row), the 16-byte record of the digits of the G heads' X.
-// * Wavefront w contracts blocks 4w .. 4w+3 on the matrix cores with
-//   v_mfma_i32_16x16x64_i8 (and _16x16x32_i8 for a 32-row remainder).  The
-//   A operand (row m = 4h + digit, K = plane rows) and the B operand (K =
-//   plane rows, column = token) both come from LDS through the transposing
-//   read ds_read_b64_tr_b8: the B bytes are the raw plane words, each byte
-//   holding 8 tokens of one row, and one AND per 4 bytes keeps bit
-//   2c + (n / 8) of column n, so the four matrices c = 0..3 give the 64
-//   tokens of the block, token 8 (n % 8) + 2c + n / 8 in column n, each
-//   scaled by 2^(2c + n / 8) (by -2^7 for bit 7: the int8 byte 0x80 is
-//   -128).  A fifth product with all-one bytes gives C.
-// * Lane l ends with the four digit sums of head 4 hg + l / 16 for its token,
-//   and recombines them with shifts into the int32 S.  In the candidate mode
-//   the test score >= threshold is the exact integer test 2 S - C >= I on
-//   the same value the score would be written as.
-#include "bpk_internal.h"
+// Mapping onto gfx950 (fast kernel):
+// * A workgroup (4 wavefronts, two per CU) owns a range of blocks of one unit
+//   and walks it in steps of 16 blocks, with one barrier per step.  Each
+//   thread prefetches its share of the step's plane words (coalesced 128-byte
+//   reads of every read row) two steps ahead and the fp16 scales three steps
+//   ahead, in registers; at the top of a step they go to LDS (planes double-,
+//   scales triple-buffered), and after the barrier wavefront w computes the
+//   frames of head w for the next step.
+// * Wavefront w then takes blocks 4w .. 4w+3 one at a time: it writes the
+//   block's X digits (4 bytes per (row, head)) into its own LDS records and
+//   contracts them with the plane bits on the matrix cores,
+//   v_mfma_i32_16x16x64_i8 (and _16x16x32_i8 for a 32-row remainder).  Both
+//   operands come from LDS through the transposing read ds_read_b64_tr_b8:
+//   the B bytes are the raw plane words, each byte holding 8 tokens of one
+//   row, and one AND per 4 bytes keeps bit 2c + (n / 8) of column n, so the
+//   four matrices c = 0..3 give the 64 tokens of the block, token
+//   8 (n % 8) + 2c + n / 8 in column n, scaled by 2^(2c + n / 8) (by -2^7 for
+//   bit 7: the int8 byte 0x80 is -128).  A fifth product with all-one bytes
+//   gives C.
+// * Lane l ends with the digit sums of head 4 hg + l / 16 for its token and
+//   recombines them with shifts into the int32 S; the candidate test compares
+//   (float)(2 S - C) with threshold 2^(E+1), the same value the score is
+//   written from.
+#include "scan_common.h"
 
 namespace bpk {
 namespace {
 
-typedef int i32x2 __attribute__((ext_vector_type(2)));
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-// 16-byte global words of rows that are only 8-byte aligned (odd capacity / 64)
-typedef uint32_t u32x4_a8 __attribute__((ext_vector_type(4), aligned(8)));
-typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+constexpr int NB = 4;                 // blocks per wavefront per step
+constexpr int GB = SCAN_GB;           // blocks per step
+constexpr int RMAX = SCAN_FAST_ROWS;  // plane rows at most
+constexpr int CMAX = D;               // read channels at most
+constexpr int PSTRIDE = 144;          // LDS bytes per plane row: 16 words + 16 bytes of padding
+constexpr int PL = RMAX * 8 / SCAN_THREADS;  // 16-byte plane loads per thread and step
 
-constexpr int SCAN_THREADS = 256;
-constexpr int NB = 4;                    // blocks per wavefront per step
-constexpr int GB = 16;                   // blocks per step
-constexpr int CMAX = D;                  // read channels at most
-constexpr int PSTRIDE = 144;             // LDS bytes per plane row: 16 words + 16 bytes of padding
-constexpr float DIGIT_BIAS = 8421504.f;  // 0x808080: X + bias has three bytes of balanced digits + 128
-static_assert(SCAN_MIN_WG_BLOCKS == GB, "a workgroup takes whole steps");
-static_assert(SAMPLE_GROUP % GB == 0 && SAMPLE_STRIDE % SAMPLE_GROUP == 0, "sample plan");
-
-// What a launch does with the scores it computes:
-// * SCAN_FULL writes every score ([unit][G][cap]);
-// * SCAN_SAMPLE scores only the first SAMPLE_GROUP blocks of every
-//   SAMPLE_STRIDE (one workgroup per sampled group) into [unit][G][sample_ld];
-// * SCAN_CAND appends (score, token) of the tokens of [4, n - W) whose score
-//   is at or above the head's threshold to the workgroup's candidate region
-//   of that head (slots handed out by an LDS counter; the count, which may
-//   pass the region's size, is stored at the end).
-enum ScanMode { SCAN_FULL = 0, SCAN_SAMPLE = 1, SCAN_CAND = 2 };
-
-struct ScanArgs {
-  Geom g;
-  const float* __restrict__ q_basis;
-  const uint8_t* __restrict__ depth;
-  const uint64_t* __restrict__ planes;
-  const uint16_t* __restrict__ scales;
-  float* __restrict__ out;          // scores (FULL) or sampled scores (SAMPLE)
-  long long out_ld;                 // per (unit, head) row length of out
-  int wg_blocks;                    // blocks per workgroup (multiple of GB)
-  int k;                            // top-k (CAND: units with n <= k are skipped)
-  const int32_t* __restrict__ unit_flag;  // FULL: if set, only units with flag != 0
-  const uint32_t* __restrict__ thresh;    // CAND: [unit][G] order keys
-  long long regions;                      // CAND: region stride per (unit, head)
-  int32_t* __restrict__ cand_count;       // CAND: [unit][G][regions]
-  float* __restrict__ cand_val;           // CAND: [unit][G][regions][CAND_SLOTS]
-  int32_t* __restrict__ cand_idx;         // CAND: [unit][G][regions][CAND_SLOTS]
-};
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 template <int HG>
-struct ScanSmem {
-  static constexpr int SEG = HG == 1 ? 128 : 64;  // plane rows per segment
+struct FastSmem {
   static constexpr int GP = 4 * HG;               // heads, padded to whole MFMA row groups
-  alignas(16) uint8_t planes[SEG * PSTRIDE];      // [row][block] words of one task
-  alignas(16) uint8_t atab[GB][SEG][16 * HG];     // [block][row] X digits: 4 bytes per head
-  alignas(16) float fqe[2][SEG][GP];              // per task parity: q_hj 2^(3-p+E_h) of each row
-  alignas(16) uint16_t sc[2][CMAX][GB];           // per step parity: fp16 scales [read channel][block]
-  float smax[2][CMAX];                            // per step parity: largest scale of a read channel
+  alignas(16) uint8_t planes[2][RMAX * PSTRIDE];  // per step parity: [row][block] words
+  alignas(16) uint8_t atab[4][2][RMAX][16 * HG];  // per wavefront, two blocks: [row] X digits, 4 bytes a head
+  alignas(16) uint16_t sc[3][CMAX][GB];           // per step mod 3: fp16 scales [read channel][block]
+  float smax[3][CMAX];                            // per step mod 3: largest scale of a read channel
   float q[GP][D];                                 // the unit's query heads (0 beyond G)
+  float thp[2][GP][GB];                           // per step parity: threshold 2^(E+1) of (head, block)
   int ex[2][GP][GB];                              // per step parity: frame exponent of (head, block)
-  int ith[2][GP][GB];                             // per step parity: integer threshold of (head, block)
   int exh[2][GP];                                 // per step parity: frame exponent of the step
-  int own[2][GP];                                 // per step parity: some block has a frame of its own
+  int own[2][GP];                                 // per step parity: a block of the head has its own frame
   int scan_buf[D];                                // plan: prefix sums of (depth, read flag)
-  uint8_t rowc[NP * D];                           // read channel of each plane row
-  uint8_t rowp[NP * D];                           // plane of each plane row
+  uint8_t rowc[RMAX];                             // read channel of each plane row
+  uint8_t rowp[RMAX];                             // plane of each plane row
   uint8_t chj[CMAX];                              // channel of each read channel
   int ccount[GP];                                 // candidates of this workgroup per head
 };
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
-  return v;
-}
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    const uint32_t o = (uint32_t)__shfl_xor((int)v, off);
-    v = o > v ? o : v;
-  }
-  return v;
-}
-
-__device__ __forceinline__ float half_bits_to_f32(uint16_t b) {
-  return (float)__builtin_bit_cast(_Float16, b);
-}
-
-// Largest E with m 2^E < 2^lx (0 for m == 0), clamped to a range where every
-// later scaling stays normal.
-__device__ __forceinline__ int frame_exp(float m, int lx) {
-  if (!(m > 0.f)) return 0;
-  int e;
-  frexpf(m, &e);  // m < 2^e
-  int E = lx - e;
-  return E < -100 ? -100 : (E > 100 ? 100 : E);
-}
-
-// Inverse of order_key; 0 and ~0 (everything / nothing is a candidate) map to
-// -inf / +inf.
-__device__ __forceinline__ float key_to_float(uint32_t k) {
-  if (k == 0u) return -__builtin_inff();
-  if (k == 0xFFFFFFFFu) return __builtin_inff();
-  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
-}
-
-// Smallest integer T with ldexp((float)T, -(E+1)) >= theta, clamped to
-// [-2^30, 2^30] (every |T| here is below 2^29).
-__device__ int int_threshold(float theta, int E) {
-  if (theta == -__builtin_inff()) return -(1 << 30);
-  if (!(theta < __builtin_inff())) return 1 << 30;
-  const double tp = ldexp((double)theta, E + 1);
-  if (tp <= -1073741824.0) return -(1 << 30);
-  if (tp >= 1073741824.0) return 1 << 30;
-  int t = (int)ceil(tp);
-  // (float) rounds to nearest, so a few integers below ceil(tp) may still
-  // convert to a value >= tp; the predicate is monotone in t
-  for (int d = 64; d >= 1; d >>= 1)
-    if ((double)(float)(t - d) >= tp) t -= d;
+// theta 2^(E+1) for the test (float)T >= it, T an integer: values of
+// magnitude below 1 (including an underflow to 0) are replaced by +-1/2, which
+// decides every integer the same way
+__device__ __forceinline__ float scaled_threshold(float theta, int e) {
+  float t = ldexpf(theta, e + 1);
+  if (theta != 0.f && fabsf(t) < 1.f) t = theta > 0.f ? 0.5f : -0.5f;
   return t;
 }
 
-__device__ __forceinline__ i32x2 tr8(const uint8_t* p) {
-  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(p));
-}
-
-template <int G, int MODE>
-__global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : 2) void scan_kernel(ScanArgs a) {
+template <int G, int MODE, bool VEC>
+__global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : 2) void scan_fast_kernel(ScanArgs a) {
   constexpr int HG = (G + 3) / 4;
-  using SM = ScanSmem<HG>;
-  constexpr int SEG = SM::SEG;
+  using SM = FastSmem<HG>;
   constexpr int GP = SM::GP;
-  constexpr int PL = SEG * 8 / SCAN_THREADS;  // 16-byte plane loads per thread and task
+  constexpr int NPAIR = GP / 2;           // head pairs of a row (8-byte record halves)
+  constexpr int RPP = 64 / NPAIR;         // rows per builder pass
   __shared__ __attribute__((aligned(16))) SM sm;
 
   const int tid = threadIdx.x;
@@ -196,13 +116,10 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : 2) void scan_kernel(Scan
   const long long nbcap = a.g.nbcap();
   const long long cand_hi = n - kept_tail(n);  // candidates are tokens [4, cand_hi)
 
-  // ---- where a score goes (every lane of the wavefront calls emit) ----
-  float theta[GP];
-#pragma unroll
-  for (int h = 0; h < GP; ++h)
-    theta[h] = (MODE == SCAN_CAND && h < G) ? key_to_float(a.thresh[(long long)u * G + h])
-                                            : -__builtin_inff();
-  auto region = [&](int h) { return (((long long)u * G + h) * a.regions + blockIdx.x) * CAND_SLOTS; };
+  // ---- where a score goes ----
+  auto region = [&](int h) {
+    return (((long long)u * G + h) * a.regions + blockIdx.x) * CAND_SLOTS;
+  };
   auto store = [&](long long tok, int h, float s) {  // FULL / SAMPLE
     const long long uh = (long long)u * G + h;
     if constexpr (MODE == SCAN_FULL) {
@@ -211,7 +128,7 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : 2) void scan_kernel(Scan
       a.out[uh * a.out_ld + (long long)blockIdx.x * (SAMPLE_GROUP * BLK) + (tok - wb0 * BLK)] = s;
     }
   };
-  auto append = [&](long long tok, int h, float s) {  // CAND, lanes whose test passed
+  auto append = [&](long long tok, int h, float s) {  // CAND, a lane whose test passed
     if (tok < 4 || tok >= cand_hi) return;
     const int off = atomicAdd(&sm.ccount[h], 1);
     if (off < CAND_SLOTS) {
@@ -248,6 +165,7 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : 2) void scan_kernel(Scan
   }
   const int R = sm.scan_buf[D - 1] & 0xFFFF;
   const int CR = sm.scan_buf[D - 1] >> 16;  // read channels
+  if (R > RMAX) return;                      // the wide kernel's unit (uniform)
   if (tid < D && tj > 0) {
     const int r0 = (sm.scan_buf[tid] & 0xFFFF) - tj;
     const int c = (sm.scan_buf[tid] >> 16) - 1;
@@ -260,6 +178,10 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : 2) void scan_kernel(Scan
   __syncthreads();
 
   if (R == 0) {  // nothing is read: every score is 0
+    float theta[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+      theta[h] = MODE == SCAN_CAND ? key_to_float(a.thresh[(long long)u * G + h]) : 0.f;
     // (wb1 - wb0) * 64 is a multiple of 64: each wavefront's lanes run the same trips
     for (long long e = tid; e < (wb1 - wb0) * BLK; e += SCAN_THREADS) {
       const long long tok = wb0 * BLK + e;
@@ -280,119 +202,158 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : 2) void scan_kernel(Scan
   int lx = 29;
   for (int r = R - 1; r > 0; r >>= 1) --lx;  // 29 - ceil(log2 R)
   lx = lx > 22 ? 22 : lx;
-  const int nseg = (R + SEG - 1) / SEG;
   const int nsteps = (int)((wb1 - wb0 + GB - 1) / GB);
-  const int ntask = nsteps * nseg;
+  const int rpt = (R + 31) / 32;  // 32-row pieces of the K passes (A is zero beyond R)
   auto step_g0 = [&](int i) { return wb0 + (long long)i * GB; };
   auto step_blocks = [&](int i) {
     const long long r = wb1 - step_g0(i);
     return r < GB ? (int)r : GB;
   };
-  auto seg_rows = [&](int s) { return (R - s * SEG) < SEG ? (R - s * SEG) : SEG; };
 
-  // ---- loads (global -> registers; written to LDS at the top of a task) ----
-  u32x4 pw[PL];        // plane words: row e / 8 of the segment, words 2 (e % 8), +1
-  u32x4 sw;            // scales: read channel tid / 2, blocks 8 (tid % 2) .. +7
-  const bool vec_scales = (nbcap % 8) == 0;
-  auto issue_planes = [&](int task) {
-    const int i = task / nseg, s = task % nseg;
-    const long long g0 = step_g0(i);
-    const int gblk = step_blocks(i);
-    const int rs = seg_rows(s);
+  // ---- per-thread load slots ----
+  // planes: slot k covers row (tid + 256 k) / 8, words 2 ((tid + 256 k) % 8), +1
+  // of the step; scales: read channel tid / 2, blocks 8 (tid % 2) .. +7.  With
+  // VEC (capacity / 64 a multiple of 8: every plane row 16-byte aligned, every
+  // scale row too) each thread issues the same loads at every step, with no
+  // branch: rows >= R read row 0, words past the capacity re-read the last
+  // ones, steps past the range re-read the last step (duplicates the caches
+  // serve, never used).  The compiler can then wait for the oldest step's loads
+  // alone, and two steps stay in flight.
+  const uint64_t* prow[PL];  // the slot's plane row (row 0 for rows >= R)
+  int ppart[PL];
+  bool pvalid[PL];
 #pragma unroll
-    for (int k = 0; k < PL; ++k) {
-      const int e = tid + k * SCAN_THREADS;
-      const int rr = e >> 3, part = e & 7;
-      pw[k] = u32x4{0u, 0u, 0u, 0u};
-      if (rr < rs) {
-        const int r = s * SEG + rr;
-        const uint64_t* src =
-            a.planes + ((uint64_t)(gu * D + sm.chj[sm.rowc[r]]) * NP + sm.rowp[r]) * nbcap + g0 + 2 * part;
-        if (2 * part + 1 < gblk) {
-          pw[k] = *reinterpret_cast<const u32x4_a8*>(src);
-        } else if (2 * part < gblk) {
-          const uint64_t w0 = src[0];
-          pw[k] = u32x4{(uint32_t)w0, (uint32_t)(w0 >> 32), 0u, 0u};
+  for (int k = 0; k < PL; ++k) {
+    const int e = tid + k * SCAN_THREADS, r = e >> 3, rr = r < R ? r : 0;
+    prow[k] = a.planes + ((uint64_t)(gu * D + sm.chj[sm.rowc[rr]]) * NP + sm.rowp[rr]) * nbcap;
+    ppart[k] = 2 * (e & 7);
+    pvalid[k] = r < R;
+  }
+  const int sc_c = tid >> 1, sc_h = tid & 1;
+  const uint16_t* srow = a.scales + (uint64_t)(gu * D + sm.chj[sc_c < CR ? sc_c : 0]) * nbcap;
+  const bool svalid = sc_c < CR;
+  const long long g0_last = step_g0(nsteps - 1);
+
+  u32x4 pw[2][PL];  // plane words of the steps of parity 0 / 1
+  u32x4 sw[2];      // scales of the steps of parity 0 / 1
+  auto issue_planes = [&](int i, auto P) {
+    constexpr int p = decltype(P)::value;
+    if constexpr (VEC) {
+      const long long g0 = step_g0(i) < g0_last ? step_g0(i) : g0_last;
+#pragma unroll
+      for (int k = 0; k < PL; ++k) {
+        const long long w = (g0 + ppart[k]) < nbcap - 2 ? (g0 + ppart[k]) : nbcap - 2;
+        pw[p][k] = *reinterpret_cast<const u32x4_a8*>(prow[k] + w);
+      }
+    } else {
+      if (i >= nsteps) return;
+      const long long g0 = step_g0(i);
+      const int gblk = step_blocks(i);
+#pragma unroll
+      for (int k = 0; k < PL; ++k) {
+        pw[p][k] = u32x4{0u, 0u, 0u, 0u};
+        if (pvalid[k]) {
+          const uint64_t* src = prow[k] + g0 + ppart[k];
+          if (ppart[k] + 1 < gblk) {
+            pw[p][k] = *reinterpret_cast<const u32x4_a8*>(src);
+          } else if (ppart[k] < gblk) {
+            const uint64_t w0 = src[0];
+            pw[p][k] = u32x4{(uint32_t)w0, (uint32_t)(w0 >> 32), 0u, 0u};
+          }
         }
       }
     }
   };
-  auto issue_scales = [&](int i) {
-    sw = u32x4{0u, 0u, 0u, 0u};
-    const int c = tid >> 1, hf = tid & 1;
-    if (i >= nsteps || c >= CR) return;
-    const long long g0 = step_g0(i) + 8 * hf;
-    const int gblk = step_blocks(i) - 8 * hf;
-    const uint16_t* src = a.scales + (uint64_t)(gu * D + sm.chj[c]) * nbcap + g0;
-    if (vec_scales && gblk >= 8) {
-      sw = *reinterpret_cast<const u32x4*>(src);
+  auto issue_scales = [&](int i, auto P) {
+    constexpr int p = decltype(P)::value;
+    if constexpr (VEC) {
+      const long long g0 = step_g0(i) < g0_last ? step_g0(i) : g0_last;
+      const long long w = (g0 + 8 * sc_h) < nbcap - 8 ? (g0 + 8 * sc_h) : nbcap - 8;
+      sw[p] = *reinterpret_cast<const u32x4*>(srow + w);
     } else {
+      if (i >= nsteps) return;
+      sw[p] = u32x4{0u, 0u, 0u, 0u};
+      if (!svalid) return;
+      const uint16_t* src = srow + step_g0(i) + 8 * sc_h;
+      const int gblk = step_blocks(i) - 8 * sc_h;
       uint32_t v[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
       for (int b = 0; b < 8; ++b)
         if (b < gblk) v[b >> 1] |= (uint32_t)src[b] << (16 * (b & 1));
-      sw = u32x4{v[0], v[1], v[2], v[3]};
+      sw[p] = u32x4{v[0], v[1], v[2], v[3]};
     }
   };
-  auto write_planes = [&](int task) {
-    (void)task;
+  auto write_planes = [&](int i, auto P) {  // rows >= R: row 0's words, never used (A is zero there)
+    constexpr int p = decltype(P)::value;
 #pragma unroll
     for (int k = 0; k < PL; ++k) {
       const int e = tid + k * SCAN_THREADS;
-      *reinterpret_cast<u32x4*>(&sm.planes[(e >> 3) * PSTRIDE + 16 * (e & 7)]) = pw[k];
+      *reinterpret_cast<u32x4*>(&sm.planes[i & 1][(e >> 3) * PSTRIDE + 16 * (e & 7)]) = pw[p][k];
     }
   };
-  auto write_scales = [&](int i) {  // scales of step i (loaded by issue_scales(i))
-    const int c = tid >> 1, hf = tid & 1, par = i & 1;
-    float m = 0.f;
+  auto write_scales = [&](int i, auto P) {  // scales of step i and their per-channel max
+    constexpr int p = decltype(P)::value;
+    const int b3 = i % 3;
+    // the blocks of the step only; fp16 bits of non-negative values order like the values
+    const int nv = step_blocks(i) - 8 * sc_h;
+    u16x2 mv = {0, 0};
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      m = fmaxf(m, half_bits_to_f32((uint16_t)(sw[b] & 0xFFFF)));
-      m = fmaxf(m, half_bits_to_f32((uint16_t)(sw[b] >> 16)));
+    for (int x = 0; x < 4; ++x) {
+      const uint32_t keep = (2 * x < nv ? 0xFFFFu : 0u) | (2 * x + 1 < nv ? 0xFFFF0000u : 0u);
+      mv = __builtin_elementwise_max(mv, __builtin_bit_cast(u16x2, sw[p][x] & keep));
     }
-    m = fmaxf(m, __shfl_xor(m, 1));
-    if (c < CR) {
-      *reinterpret_cast<u32x4*>(&sm.sc[par][c][8 * hf]) = sw;
-      if (hf == 0) sm.smax[par][c] = m;
+    uint32_t m = mv.x > mv.y ? mv.x : mv.y;
+    const uint32_t mo = (uint32_t)__shfl_xor((int)m, 1);
+    m = mo > m ? mo : m;
+    if (svalid) {
+      *reinterpret_cast<u32x4*>(&sm.sc[b3][sc_c][8 * sc_h]) = sw[p];
+      if (sc_h == 0) sm.smax[b3][sc_c] = half_bits_to_f32((uint16_t)m);
     }
   };
 
-  // ---- frames of step i (wavefront w handles heads w, w + 4) ----
+  // the thresholds of this wavefront's heads (w, w + 4), read once
+  float theta_k[HG];
+#pragma unroll
+  for (int k = 0; k < HG; ++k) {
+    const int h = wave + 4 * k;
+    theta_k[k] = (MODE == SCAN_CAND && h < G) ? key_to_float(a.thresh[(long long)u * G + h]) : 0.f;
+  }
+
+  // ---- frames of step i: wavefront w handles heads w, w + 4 ----
   auto compute_frame = [&](int i) {
-    const int par = i & 1, gblk = step_blocks(i);
+    const int par = i & 1, b3 = i % 3, gblk = step_blocks(i);
 #pragma unroll
     for (int k = 0; k < HG; ++k) {
       const int h = wave + 4 * k;
       if (h >= G) continue;  // wavefront-uniform
-      float best = 0.f;
-      uint32_t bkey = 0;
+      uint32_t key = 0;
       for (int c = lane; c < CR; c += 64) {
-        const float v = fabsf(sm.q[h][sm.chj[c]]) * 8.f * sm.smax[par][c];
-        best = fmaxf(best, v);
-        const uint32_t key = (__float_as_uint(v) & 0xFFFFFF00u) | (uint32_t)c;
-        bkey = key > bkey ? key : bkey;
+        const float v = fabsf(sm.q[h][sm.chj[c]]) * 8.f * sm.smax[b3][c];
+        const uint32_t kk = (__float_as_uint(v) & 0xFFFFFF00u) | (uint32_t)c;
+        key = kk > key ? kk : key;
       }
-      best = wave_max(best);
-      bkey = wave_max_u32(bkey);
-      const int cs = (int)(bkey & 0xFFu);
+      key = wave_max_u32(key);
+      // an upper bound of the largest |q| 8 smax, and the channel that reaches it
+      const float best = key ? __uint_as_float((key & 0xFFFFFF00u) + 0x100u) : 0.f;
+      const int cs = (int)(key & 0xFFu);
       const int E = frame_exp(best, lx);
       int eb = E;
       bool own = false;
-      if (lane < GB && lane < gblk && best > 0.f) {
+      if (lane < gblk && best > 0.f) {
         // the block's own largest weight is at least a quarter of the frame's
         // if the channel that sets the frame keeps a quarter of its step max
-        if (4.f * half_bits_to_f32(sm.sc[par][cs][lane]) < sm.smax[par][cs]) {
+        if (4.f * half_bits_to_f32(sm.sc[b3][cs][lane]) < sm.smax[b3][cs]) {
           float mb = 0.f;
           for (int c = 0; c < CR; ++c)
-            mb = fmaxf(mb, fabsf(sm.q[h][sm.chj[c]]) * 8.f * half_bits_to_f32(sm.sc[par][c][lane]));
+            mb = fmaxf(mb, fabsf(sm.q[h][sm.chj[c]]) * 8.f * half_bits_to_f32(sm.sc[b3][c][lane]));
           eb = frame_exp(mb, lx);
           own = eb != E;
         }
       }
       if (lane < GB) {
         sm.ex[par][h][lane] = eb;
-        sm.ith[par][h][lane] =
-            MODE == SCAN_CAND ? int_threshold(key_to_float(a.thresh[(long long)u * G + h]), eb) : 0;
+        if constexpr (MODE == SCAN_CAND)
+          sm.thp[par][h][lane] = scaled_threshold(theta_k[k], eb);
       }
       const bool any_own = __ballot(own) != 0ull;
       if (lane == 0) {
@@ -401,212 +362,218 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : 2) void scan_kernel(Scan
       }
     }
   };
-  // q_hj 2^(3-p+E_h) of the rows of task (i, s), into fqe[tp] (0 beyond the
-  // segment's rows and for heads >= G); wavefront w handles heads w, w + 4
-  auto fill_fqe = [&](int task, int tp) {
-    const int i = task / nseg, s = task % nseg;
-    const int rs = seg_rows(s);
+
+  // ---- the main loop, specialised on the K passes: RPT 32-row pieces, that
+  // is RPT / 2 passes of 64 rows and, for odd RPT, one of 32 ----
+  auto main_loop = [&](auto RPTC) {
+    constexpr int RPT = decltype(RPTC)::value;
+    constexpr int N64 = RPT / 2;
+    constexpr bool HAS32 = (RPT & 1) != 0;
+    constexpr int NPASS = 32 * RPT / RPP;  // builder passes
+
+    // builder items: pass m covers row RPP m + lane / NPAIR and heads
+    // 2 (lane % NPAIR), +1; rows >= R have zero weights, hence zero digits
+    const int prow = lane / NPAIR, ppair = lane % NPAIR;
+    float fq0[NPASS][2];  // q_hj 2^(3-p) of the item's row and heads
+    int soff[NPASS];      // the item's row's scales in sc[.]: read channel * GB
 #pragma unroll
-    for (int k = 0; k < HG; ++k) {
-      const int h = wave + 4 * k;
-      const int E = h < G ? sm.exh[i & 1][h] : 0;
-      for (int rr = lane; rr < SEG; rr += 64) {
-        float v = 0.f;
-        if (h < G && rr < rs) {
-          const int r = s * SEG + rr;
-          v = ldexpf(sm.q[h][sm.chj[sm.rowc[r]]], 3 - sm.rowp[r] + E);
-        }
-        sm.fqe[tp][rr][h] = v;
+    for (int m = 0; m < NPASS; ++m) {
+      const int r = m * RPP + prow;
+      soff[m] = (r < R ? sm.rowc[r] : 0) * GB;
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const int h = 2 * ppair + x;
+        fq0[m][x] = (r < R && h < G) ? ldexpf(sm.q[h][sm.chj[sm.rowc[r]]], 3 - sm.rowp[r]) : 0.f;
       }
+    }
+
+    // MFMA operand addressing: lane l is column / A-row l % 16 of K-group l / 16;
+    // a transposing read takes, in each 16-lane group, row r0 + (l % 16) / 2
+    const int kg = lane >> 4, s16 = lane & 15;
+    const int rsub = s16 >> 1, ahalf = 8 * (s16 & 1);
+    uint32_t bmask[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) bmask[c] = 0x01010101u << (2 * c + (s16 >> 3));
+    const uint32_t neg7 = (s16 >> 3) ? 0xFFFFFFFFu : 0u;  // lanes whose c = 3 column keeps bit 7
+    const i32x4 ones4 = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
+    const long ones2 = 0x0101010101010101l;
+    const i32x4 zero4 = {0, 0, 0, 0};
+
+    // A records of block blk into buffer buf
+    auto build = [&](int b3, int blk, int buf, const float (&fqe)[NPASS][2]) {
+      const uint16_t* scb = &sm.sc[b3][0][0] + blk;
+      uint8_t* rec = &sm.atab[wave][buf][prow][8 * ppair];
+#pragma unroll
+      for (int m = 0; m < NPASS; ++m) {
+        const float sv = half_bits_to_f32(scb[soff[m]]);
+        const uint32_t x0 = (uint32_t)__builtin_fmaf(fqe[m][0], sv, DIGIT_BIAS) ^ 0x808080u;
+        const uint32_t x1 = (uint32_t)__builtin_fmaf(fqe[m][1], sv, DIGIT_BIAS) ^ 0x808080u;
+        *reinterpret_cast<uint2*>(rec + m * RPP * (16 * HG)) = make_uint2(x0, x1);
+      }
+    };
+    // the same for a step where some (head, block) has a frame of its own
+    auto build_own = [&](int par, int b3, int blk, int buf, const float (&fqe)[NPASS][2],
+                         const int (&exh2)[2]) {
+      float g[2];
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const int h = 2 * ppair + x;
+        g[x] = h < G ? ldexpf(1.f, sm.ex[par][h][blk] - exh2[x]) : 0.f;
+      }
+      const uint16_t* scb = &sm.sc[b3][0][0] + blk;
+      uint8_t* rec = &sm.atab[wave][buf][prow][8 * ppair];
+#pragma unroll
+      for (int m = 0; m < NPASS; ++m) {
+        const float sv = half_bits_to_f32(scb[soff[m]]);
+        const uint32_t x0 = (uint32_t)__builtin_fmaf(fqe[m][0] * g[0], sv, DIGIT_BIAS) ^ 0x808080u;
+        const uint32_t x1 = (uint32_t)__builtin_fmaf(fqe[m][1] * g[1], sv, DIGIT_BIAS) ^ 0x808080u;
+        *reinterpret_cast<uint2*>(rec + m * RPP * (16 * HG)) = make_uint2(x0, x1);
+      }
+    };
+    // digit sums of block blk (planes pl, A records of buffer buf)
+    auto contract = [&](const uint8_t* pl, int blk, int buf, i32x4 (&acc)[HG][4], i32x4 (&accc)[HG]) {
+      const uint8_t* at = &sm.atab[wave][buf][0][0];
+#pragma unroll
+      for (int kp = 0; kp < N64; ++kp) {
+        const int r0 = 64 * kp + 16 * kg + rsub;
+        const i32x2 b0 = tr8(pl + r0 * PSTRIDE + 8 * blk);
+        const i32x2 b1 = tr8(pl + (r0 + 8) * PSTRIDE + 8 * blk);
+        const i32x4 bv = {b0.x, b0.y, b1.x, b1.y};
+#pragma unroll
+        for (int hg = 0; hg < HG; ++hg) {
+          const i32x2 a0 = tr8(at + r0 * (16 * HG) + 16 * hg + ahalf);
+          const i32x2 a1 = tr8(at + (r0 + 8) * (16 * HG) + 16 * hg + ahalf);
+          const i32x4 av = {a0.x, a0.y, a1.x, a1.y};
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            acc[hg][c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bv & (int)bmask[c],
+                                                               kp ? acc[hg][c] : zero4, 0, 0, 0);
+          accc[hg] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, ones4, kp ? accc[hg] : zero4, 0, 0, 0);
+        }
+      }
+      if constexpr (HAS32) {
+        const int r0 = 64 * N64 + 8 * kg + rsub;
+        const i32x2 b0 = tr8(pl + r0 * PSTRIDE + 8 * blk);
+#pragma unroll
+        for (int hg = 0; hg < HG; ++hg) {
+          const long av = __builtin_bit_cast(long, tr8(at + r0 * (16 * HG) + 16 * hg + ahalf));
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            acc[hg][c] = __builtin_amdgcn_mfma_i32_16x16x32_i8(
+                av, __builtin_bit_cast(long, b0 & (int)bmask[c]), N64 ? acc[hg][c] : zero4, 0, 0, 0);
+          accc[hg] = __builtin_amdgcn_mfma_i32_16x16x32_i8(av, ones2, N64 ? accc[hg] : zero4, 0, 0, 0);
+        }
+      }
+    };
+    // scores of block blk: lane <-> (head 4 hg + l / 16, column l % 16)
+    auto scores = [&](int par, long long g0, int blk, const i32x4 (&acc)[HG][4], const i32x4 (&accc)[HG]) {
+      const long long tok0 = (g0 + blk) * BLK + 8 * (s16 & 7) + (s16 >> 3);
+#pragma unroll
+      for (int hg = 0; hg < HG; ++hg) {
+        const int h = 4 * hg + kg;
+        const int hh = h < G ? h : 0;
+        const i32x4 dc = accc[hg];
+        const uint32_t cc = ((uint32_t)dc.z << 16) + ((uint32_t)dc.y << 8) + (uint32_t)dc.x;  // C
+        const int eb = sm.ex[par][hh][blk];
+        float thr = 0.f;
+        if constexpr (MODE == SCAN_CAND) thr = sm.thp[par][hh][blk];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int bp = 2 * c + (s16 >> 3);
+          const i32x4 d = acc[hg][c];
+          // S = sum_r X_r b_r (the digit sums are multiples of 2^bp); T = 2 S - C
+          const uint32_t sS = ((uint32_t)d.z << (16 - bp)) + ((uint32_t)d.y << (8 - bp)) +
+                              (uint32_t)(d.x >> bp);
+          uint32_t s2 = 2u * sS;
+          if (c == 3) s2 = (s2 ^ neg7) - neg7;  // bit 7 kept as the int8 byte 0x80 = -128
+          const float tf = (float)(int)(s2 - cc);
+          const long long tok = tok0 + 2 * c;
+          if constexpr (MODE == SCAN_CAND) {
+            const bool pass = h < G && tf >= thr;
+            if (__ballot(pass) != 0ull && pass) append(tok, h, ldexpf(tf, -(eb + 1)));
+          } else {
+            if (h < G) store(tok, h, ldexpf(tf, -(eb + 1)));
+          }
+        }
+      }
+    };
+
+    // ---- one step: the wavefront's blocks, building block b + 1 while the
+    // matrix cores work on block b ----
+    auto blocks = [&](int i) {
+      const int par = i & 1, b3 = i % 3;
+      const long long g0 = step_g0(i);
+      const int wb = NB * wave;
+      const int nblk = step_blocks(i) - wb;  // blocks of this wavefront (uniform)
+      if (nblk <= 0) return;
+      // the rows' weights in this step's frames
+      float fqe[NPASS][2];
+      int exh2[2];
+#pragma unroll
+      for (int x = 0; x < 2; ++x) exh2[x] = 2 * ppair + x < G ? sm.exh[par][2 * ppair + x] : 0;
+#pragma unroll
+      for (int m = 0; m < NPASS; ++m)
+#pragma unroll
+        for (int x = 0; x < 2; ++x) fqe[m][x] = ldexpf(fq0[m][x], exh2[x]);
+      bool own_any = false;
+#pragma unroll
+      for (int h = 0; h < G; ++h) own_any |= sm.own[par][h] != 0;
+      const uint8_t* pl = &sm.planes[par][0];
+
+      if (own_any) build_own(par, b3, wb, 0, fqe, exh2);
+      else build(b3, wb, 0, fqe);
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        if (b >= nblk) break;
+        i32x4 acc[HG][4];
+        i32x4 accc[HG];
+        contract(pl, wb + b, b & 1, acc, accc);
+        if (b + 1 < nblk) {
+          if (own_any) build_own(par, b3, wb + b + 1, (b + 1) & 1, fqe, exh2);
+          else build(b3, wb + b + 1, (b + 1) & 1, fqe);
+        }
+        scores(par, g0, wb + b, acc, accc);
+      }
+    };
+
+    // ---- prologue: loads of steps 0 and 1, scales and frames of step 0 ----
+    constexpr std::integral_constant<int, 0> P0{};
+    constexpr std::integral_constant<int, 1> P1{};
+    issue_planes(0, P0);
+    issue_planes(1, P1);
+    issue_scales(0, P0);
+    issue_scales(1, P1);
+    write_scales(0, P0);
+    issue_scales(2, P0);
+    __syncthreads();
+    compute_frame(0);
+
+    // ---- steps (two per trip, so that the prefetch registers are static) ----
+    auto step = [&](int i, auto P, auto Q) {  // P = i % 2, Q = (i + 1) % 2
+      write_planes(i, P);
+      if (i + 1 < nsteps) write_scales(i + 1, Q);
+      __syncthreads();  // planes of i, scales of i + 1 and frames of i are in LDS
+      issue_planes(i + 2, P);
+      issue_scales(i + 3, Q);
+      if (i + 1 < nsteps) compute_frame(i + 1);
+      blocks(i);
+    };
+    for (int i = 0; i < nsteps; i += 2) {
+      step(i, P0, P1);
+      if (i + 1 < nsteps) step(i + 1, P1, P0);
     }
   };
-
-  // ---- prologue: scales and frames of step 0, fqe of task 0 (the loop's
-  // first barrier publishes them) ----
-  issue_scales(0);
-  write_scales(0);
-  __syncthreads();
-  issue_planes(0);
-  issue_scales(1);
-  compute_frame(0);
-  fill_fqe(0, 0);
-
-  // MFMA operand addressing: lane l is column / A-row l % 16 of K-group l / 16;
-  // a transposing read takes, in each 16-lane group, row r0 + (l % 16) / 2
-  const int kg = lane >> 4, s16 = lane & 15;
-  const int rsub = s16 >> 1, ahalf = 8 * (s16 & 1);
-  uint32_t bmask[4];
-#pragma unroll
-  for (int c = 0; c < 4; ++c) bmask[c] = 0x01010101u << (2 * c + (s16 >> 3));
-  const uint32_t neg7 = (s16 >> 3) ? 0xFFFFFFFFu : 0u;  // lanes whose c = 3 column keeps bit 7
-  const i32x4 ones4 = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
-  const long ones2 = 0x0101010101010101l;
-
-  i32x4 acc[NB][HG][4];
-  i32x4 accc[NB][HG];
-
-  for (int task = 0; task < ntask; ++task) {
-    const int i = task / nseg, s = task % nseg;
-    const int par = i & 1, tp = task & 1;
-    const long long g0 = step_g0(i);
-    const int gblk = step_blocks(i);
-    const int rs = seg_rows(s);
-    int n64 = rs >> 6, rem = rs & 63;
-    if (rem > 32) {
-      ++n64;
-      rem = 0;
-    }
-    const bool has32 = rem > 0;
-    const int rp = 64 * n64 + (has32 ? 32 : 0);  // rows with A records (zero beyond rs)
-
-    // ---- the previous task's planes and A records are no longer read: this
-    // task's plane words, and the next step's scales, into LDS ----
-    __syncthreads();
-    write_planes(task);
-    if (s == 0 && i + 1 < nsteps) write_scales(i + 1);
-
-    // ---- A records: X digits of (block, row) for every head ----
-    const bool own_any = [&]() {
-      bool o = false;
-#pragma unroll
-      for (int h = 0; h < G; ++h) o |= sm.own[par][h] != 0;
-      return o;
-    }();
-    // thread -> block tid / 16, rows tid % 16 + 16 k (rp is a multiple of 32)
-    for (int rr = tid & 15, b = tid >> 4; rr < rp; rr += 16) {
-      u32x4 rec[HG];
-#pragma unroll
-      for (int hg = 0; hg < HG; ++hg) rec[hg] = u32x4{0u, 0u, 0u, 0u};
-      if (b < gblk && rr < rs) {
-        const float sv = half_bits_to_f32(sm.sc[par][sm.rowc[s * SEG + rr]][b]);
-#pragma unroll
-        for (int hg = 0; hg < HG; ++hg) {
-          const float4 f = *reinterpret_cast<const float4*>(&sm.fqe[tp][rr][4 * hg]);
-          float fv[4] = {f.x, f.y, f.z, f.w};
-          if (own_any) {
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-              const int h = 4 * hg + x;
-              if (h < G) fv[x] = ldexpf(fv[x], sm.ex[par][h][b] - sm.exh[par][h]);
-            }
-          }
-#pragma unroll
-          for (int x = 0; x < 4; ++x)
-            rec[hg][x] = (uint32_t)__builtin_fmaf(fv[x], sv, DIGIT_BIAS) ^ 0x808080u;
-        }
-      }
-#pragma unroll
-      for (int hg = 0; hg < HG; ++hg)
-        *reinterpret_cast<u32x4*>(&sm.atab[b][rr][16 * hg]) = rec[hg];
-    }
-    __syncthreads();  // planes, A records and the next step's scales are in LDS
-    if (task + 1 < ntask) {
-      issue_planes(task + 1);
-      const int i1 = (task + 1) / nseg;
-      if (i1 != i) issue_scales(i1 + 1);
-      // what the next task needs: the next step's frames (from its scales,
-      // written above) and its rows' q 2^(3-p+E); each wavefront fills the
-      // heads whose frames it computed
-      if (i1 != i) compute_frame(i1);
-      fill_fqe(task + 1, tp ^ 1);
-    }
-
-    // ---- contraction: wavefront takes blocks 4 wave .. 4 wave + 3 of the step ----
-    const int wb = NB * wave;
-    if (s == 0) {
-#pragma unroll
-      for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int hg = 0; hg < HG; ++hg) {
-          accc[b][hg] = i32x4{0, 0, 0, 0};
-#pragma unroll
-          for (int c = 0; c < 4; ++c) acc[b][hg][c] = i32x4{0, 0, 0, 0};
-        }
-    }
-    if (wb < gblk) {
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const int blk = wb + b;
-        if (blk >= gblk) break;
-        for (int kp = 0; kp < n64; ++kp) {
-          const int r0 = 64 * kp + 16 * kg + rsub;
-          const i32x2 b0 = tr8(&sm.planes[r0 * PSTRIDE + 8 * blk]);
-          const i32x2 b1 = tr8(&sm.planes[(r0 + 8) * PSTRIDE + 8 * blk]);
-          const i32x4 bv = {b0.x, b0.y, b1.x, b1.y};
-#pragma unroll
-          for (int hg = 0; hg < HG; ++hg) {
-            const i32x2 a0 = tr8(&sm.atab[blk][r0][16 * hg + ahalf]);
-            const i32x2 a1 = tr8(&sm.atab[blk][r0 + 8][16 * hg + ahalf]);
-            const i32x4 av = {a0.x, a0.y, a1.x, a1.y};
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-              const i32x4 m = bv & (int)bmask[c];
-              acc[b][hg][c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, m, acc[b][hg][c], 0, 0, 0);
-            }
-            accc[b][hg] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, ones4, accc[b][hg], 0, 0, 0);
-          }
-        }
-        if (has32) {
-          const int r0 = 64 * n64 + 8 * kg + rsub;
-          const i32x2 b0 = tr8(&sm.planes[r0 * PSTRIDE + 8 * blk]);
-#pragma unroll
-          for (int hg = 0; hg < HG; ++hg) {
-            const i32x2 a0 = tr8(&sm.atab[blk][r0][16 * hg + ahalf]);
-            const long av = __builtin_bit_cast(long, a0);
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-              const i32x2 m = b0 & (int)bmask[c];
-              acc[b][hg][c] = __builtin_amdgcn_mfma_i32_16x16x32_i8(av, __builtin_bit_cast(long, m),
-                                                                     acc[b][hg][c], 0, 0, 0);
-            }
-            accc[b][hg] = __builtin_amdgcn_mfma_i32_16x16x32_i8(av, ones2, accc[b][hg], 0, 0, 0);
-          }
-        }
-      }
-    }
-
-    // ---- epilogue after the last segment: lane <-> (head 4 hg + l / 16, column l % 16) ----
-    if (s == nseg - 1 && wb < gblk) {
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const int blk = wb + b;
-        if (blk >= gblk) break;
-        const long long tok0 = (g0 + blk) * BLK + 8 * (s16 & 7) + (s16 >> 3);
-#pragma unroll
-        for (int hg = 0; hg < HG; ++hg) {
-          const int h = 4 * hg + kg;
-          const i32x4 dc = accc[b][hg];
-          const uint32_t cc = ((uint32_t)dc.z << 16) + ((uint32_t)dc.y << 8) + (uint32_t)dc.x;  // C
-          const int eb = sm.ex[par][h < G ? h : 0][blk];
-          const int ith = sm.ith[par][h < G ? h : 0][blk];
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const int bp = 2 * c + (s16 >> 3);
-            const i32x4 d = acc[b][hg][c];
-            // S = sum_r X_r b_r (the digit sums are multiples of 2^bp); T = 2 S - C
-            const uint32_t sS = ((uint32_t)d.z << (16 - bp)) + ((uint32_t)d.y << (8 - bp)) +
-                                (uint32_t)(d.x >> bp);
-            uint32_t s2 = 2u * sS;
-            if (c == 3) s2 = (s2 ^ neg7) - neg7;  // bit 7 kept as the int8 byte 0x80 = -128
-            const int t = (int)(s2 - cc);
-            const long long tok = tok0 + 2 * c;
-            if constexpr (MODE == SCAN_CAND) {
-              const bool pass = h < G && t >= ith;
-              if (__ballot(pass) != 0ull && pass)
-                append(tok, h, ldexpf((float)t, -(eb + 1)));
-            } else {
-              if (h < G) store(tok, h, ldexpf((float)t, -(eb + 1)));
-            }
-          }
-        }
-      }
-    }
+  switch (rpt) {
+    case 1: main_loop(std::integral_constant<int, 1>{}); break;
+    case 2: main_loop(std::integral_constant<int, 2>{}); break;
+    case 3: main_loop(std::integral_constant<int, 3>{}); break;
+    default: main_loop(std::integral_constant<int, 4>{}); break;
   }
   store_counts();
 }
 
 template <int G, int MODE>
-hipError_t launch_gm(const ScanArgs& a0, hipStream_t st) {
+hipError_t launch_fast(const ScanArgs& a0, hipStream_t st) {
   ScanArgs a = a0;
   long long maxnb = 0;
   for (int s = 0; s < a.g.S; ++s) maxnb = a.g.n[s] / BLK > maxnb ? a.g.n[s] / BLK : maxnb;
@@ -620,19 +587,34 @@ hipError_t launch_gm(const ScanArgs& a0, hipStream_t st) {
     a.wg_blocks = wb;
     grid = dim3((unsigned)((maxnb + wb - 1) / wb), (unsigned)a.g.units());
   }
-  scan_kernel<G, MODE><<<grid, SCAN_THREADS, 0, st>>>(a);
+  if (a.g.nbcap() % 8 == 0)
+    scan_fast_kernel<G, MODE, true><<<grid, SCAN_THREADS, 0, st>>>(a);
+  else
+    scan_fast_kernel<G, MODE, false><<<grid, SCAN_THREADS, 0, st>>>(a);
   return hipGetLastError();
 }
 
 template <int MODE>
-hipError_t dispatch(const ScanArgs& a, hipStream_t st) {
+hipError_t dispatch_fast(const ScanArgs& a, hipStream_t st) {
   switch (a.g.G) {
-    case 1: return launch_gm<1, MODE>(a, st);
-    case 2: return launch_gm<2, MODE>(a, st);
-    case 4: return launch_gm<4, MODE>(a, st);
-    case 8: return launch_gm<8, MODE>(a, st);
+    case 1: return launch_fast<1, MODE>(a, st);
+    case 2: return launch_fast<2, MODE>(a, st);
+    case 4: return launch_fast<4, MODE>(a, st);
+    case 8: return launch_fast<8, MODE>(a, st);
     default: return hipErrorInvalidValue;
   }
+}
+
+// rows >= 0: every unit reads that many rows, one kernel; rows < 0: both,
+// the wide one with fewer, larger workgroups (its workgroups of fast units
+// only read the depths and leave)
+template <int MODE>
+hipError_t dispatch(const ScanArgs& a, int rows, hipStream_t st) {
+  if (rows >= 0 && rows <= SCAN_FAST_ROWS) return dispatch_fast<MODE>(a, st);
+  if (rows > SCAN_FAST_ROWS) return launch_scan_wide(a, MODE, 0, st);
+  const hipError_t e = dispatch_fast<MODE>(a, st);
+  if (e != hipSuccess) return e;
+  return launch_scan_wide(a, MODE, MODE == SCAN_FULL ? SCAN_WIDE_SPAN : 0, st);
 }
 
 ScanArgs base_args(const Geom& g, const float* q_basis, const uint8_t* depth,
@@ -649,36 +631,36 @@ ScanArgs base_args(const Geom& g, const float* q_basis, const uint8_t* depth,
 }  // namespace
 
 hipError_t launch_scan(const Geom& g, const float* q_basis, const uint8_t* depth,
-                       const uint64_t* planes, const uint16_t* scales, float* scores,
+                       const uint64_t* planes, const uint16_t* scales, float* scores, int rows,
                        hipStream_t st) {
   ScanArgs a = base_args(g, q_basis, depth, planes, scales);
   a.out = scores;
   a.out_ld = g.cap;
-  return dispatch<SCAN_FULL>(a, st);
+  return dispatch<SCAN_FULL>(a, rows, st);
 }
 
 hipError_t launch_scan_flagged(const Geom& g, const float* q_basis, const uint8_t* depth,
                                const uint64_t* planes, const uint16_t* scales, float* scores,
-                               const int32_t* flag, hipStream_t st) {
+                               const int32_t* flag, int rows, hipStream_t st) {
   ScanArgs a = base_args(g, q_basis, depth, planes, scales);
   a.out = scores;
   a.out_ld = g.cap;
   a.unit_flag = flag;
-  return dispatch<SCAN_FULL>(a, st);
+  return dispatch<SCAN_FULL>(a, rows, st);
 }
 
 hipError_t launch_scan_sample(const Geom& g, const float* q_basis, const uint8_t* depth,
                               const uint64_t* planes, const uint16_t* scales, const CandBufs& cb,
-                              hipStream_t st) {
+                              int rows, hipStream_t st) {
   ScanArgs a = base_args(g, q_basis, depth, planes, scales);
   a.out = cb.sample;
   a.out_ld = cb.sample_ld;
-  return dispatch<SCAN_SAMPLE>(a, st);
+  return dispatch<SCAN_SAMPLE>(a, rows, st);
 }
 
 hipError_t launch_scan_cand(const Geom& g, const float* q_basis, const uint8_t* depth,
                             const uint64_t* planes, const uint16_t* scales, int k,
-                            const CandBufs& cb, hipStream_t st) {
+                            const CandBufs& cb, int rows, hipStream_t st) {
   ScanArgs a = base_args(g, q_basis, depth, planes, scales);
   a.k = k;
   a.thresh = cb.thresh;
@@ -686,7 +668,7 @@ hipError_t launch_scan_cand(const Geom& g, const float* q_basis, const uint8_t* 
   a.cand_count = cb.count;
   a.cand_val = cb.val;
   a.cand_idx = cb.idx;
-  return dispatch<SCAN_CAND>(a, st);
+  return dispatch<SCAN_CAND>(a, rows, st);
 }
 
 }  // namespace bpk

@@ -1,0 +1,573 @@
+// Prefix-plane key scan (Fathom §1, §3.2), wide kernel: the units that read
+// more than SCAN_FAST_ROWS plane rows (budgets above 128 planes).  Same
+// arithmetic as the fast kernel in scan.hip, but the rows are cut into
+// segments that are staged one after the other, with the accumulators of a
+// wavefront's four blocks kept across segments.
+//
+// Arithmetic.  The t-bit prefix value of a 4-bit code is
+//   m = sum_{p<t} 2^(3-p) b_p + 2^(3-t) - 8 = sum_{p<t} 2^(3-p) (b_p - 1/2)
+// (plane 0 = most significant bit), so with one row r = (j, p) per read plane
+// and the weight w_r = q_hj s_bj 2^(3-p):
+//   s_hat = sum_j q_hj s_bj m_ij = sum_r w_r (b_r - 1/2) = S - C/2,
+//   S = sum_r w_r b_r,  C = sum_r w_r.
+// The weights of one 16-block step and head are put in a common fixed-point
+// frame, X_r = round(w_r 2^E), with E chosen so that sum_r |X_r| < 2^29, and
+// each X_r (|X_r| < 2^23) is split into three balanced signed bytes.  S and C
+// are then exact integer contractions of int8 digits with 0/1 bits, and the
+// score is s_hat = (2 S - C) 2^-(E+1).  The only rounding is that of X_r (half
+// a unit), far below the 1e-4 tolerance relative to the score's own L1 mass
+// as long as the frame is within a few bits of each block's largest weight.
+// E comes from max_j |q_hj| 8 smax_j over the step (smax_j = the largest scale
+// of channel j in the step); a block whose own largest weight may be more
+// than 4x smaller (tested on the channel that sets the frame) gets a frame of
+// its own.  Frames depend only on the step's blocks, so scores are
+// bit-identical in every launch mode.
+//
+// Mapping onto gfx950:
+// * A workgroup (4 wavefronts) owns a range of blocks of one unit and walks
+//   it in steps of 16 blocks; the plane rows (channel by channel) are cut into
+//   segments of 128 rows (64 when G = 8) so the LDS footprint is fixed.  Per
+//   (step, segment) task the workgroup stages the 16 words of each row in LDS
+//   (coalesced 128-byte reads, issued one task ahead) and builds, per (block,
+//   row), the 16-byte record of the digits of the G heads' X.
+// * Wavefront w contracts blocks 4w .. 4w+3 on the matrix cores with
+//   v_mfma_i32_16x16x64_i8 (and _16x16x32_i8 for a 32-row remainder).  The
+//   A operand (row m = 4h + digit, K = plane rows) and the B operand (K =
+//   plane rows, column = token) both come from LDS through the transposing
+//   read ds_read_b64_tr_b8: the B bytes are the raw plane words, each byte
+//   holding 8 tokens of one row, and one AND per 4 bytes keeps bit
+//   2c + (n / 8) of column n, so the four matrices c = 0..3 give the 64
+//   tokens of the block, token 8 (n % 8) + 2c + n / 8 in column n, each
+//   scaled by 2^(2c + n / 8) (by -2^7 for bit 7: the int8 byte 0x80 is
+//   -128).  A fifth product with all-one bytes gives C.
+// * Lane l ends with the four digit sums of head 4 hg + l / 16 for its token,
+//   and recombines them with shifts into the int32 S.  In the candidate mode
+//   the test score >= threshold is the exact integer test 2 S - C >= I on
+//   the same value the score would be written as.
+#include "scan_common.h"
+
+namespace bpk {
+namespace {
+
+constexpr int NB = 4;        // blocks per wavefront per step
+constexpr int GB = SCAN_GB;  // blocks per step
+constexpr int CMAX = D;      // read channels at most
+constexpr int PSTRIDE = 144; // LDS bytes per plane row: 16 words + 16 bytes of padding
+
+template <int HG>
+struct ScanSmem {
+  static constexpr int SEG = HG == 1 ? 128 : 64;  // plane rows per segment
+  static constexpr int GP = 4 * HG;               // heads, padded to whole MFMA row groups
+  alignas(16) uint8_t planes[SEG * PSTRIDE];      // [row][block] words of one task
+  alignas(16) uint8_t atab[GB][SEG][16 * HG];     // [block][row] X digits: 4 bytes per head
+  alignas(16) float fqe[2][SEG][GP];              // per task parity: q_hj 2^(3-p+E_h) of each row
+  alignas(16) uint16_t sc[2][CMAX][GB];           // per step parity: fp16 scales [read channel][block]
+  float smax[2][CMAX];                            // per step parity: largest scale of a read channel
+  float q[GP][D];                                 // the unit's query heads (0 beyond G)
+  int ex[2][GP][GB];                              // per step parity: frame exponent of (head, block)
+  int ith[2][GP][GB];                             // per step parity: integer threshold of (head, block)
+  int exh[2][GP];                                 // per step parity: frame exponent of the step
+  int own[2][GP];                                 // per step parity: some block has a frame of its own
+  int scan_buf[D];                                // plan: prefix sums of (depth, read flag)
+  uint8_t rowc[NP * D];                           // read channel of each plane row
+  uint8_t rowp[NP * D];                           // plane of each plane row
+  uint8_t chj[CMAX];                              // channel of each read channel
+  int ccount[GP];                                 // candidates of this workgroup per head
+};
+
+// Smallest integer T with ldexp((float)T, -(E+1)) >= theta, clamped to
+// [-2^30, 2^30] (every |T| here is below 2^29).
+__device__ int int_threshold(float theta, int E) {
+  if (theta == -__builtin_inff()) return -(1 << 30);
+  if (!(theta < __builtin_inff())) return 1 << 30;
+  const double tp = ldexp((double)theta, E + 1);
+  if (tp <= -1073741824.0) return -(1 << 30);
+  if (tp >= 1073741824.0) return 1 << 30;
+  int t = (int)ceil(tp);
+  // (float) rounds to nearest, so a few integers below ceil(tp) may still
+  // convert to a value >= tp; the predicate is monotone in t
+  for (int d = 64; d >= 1; d >>= 1)
+    if ((double)(float)(t - d) >= tp) t -= d;
+  return t;
+}
+
+template <int G, int MODE>
+__global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : 2) void scan_wide_kernel(ScanArgs a) {
+  constexpr int HG = (G + 3) / 4;
+  using SM = ScanSmem<HG>;
+  constexpr int SEG = SM::SEG;
+  constexpr int GP = SM::GP;
+  constexpr int PL = SEG * 8 / SCAN_THREADS;  // 16-byte plane loads per thread and task
+  __shared__ __attribute__((aligned(16))) SM sm;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int u = blockIdx.y;
+  const long long gu = a.g.global_unit(u);
+  const long long n = a.g.n[a.g.seq_of(u)];
+  const long long nb = n / BLK;
+  if constexpr (MODE == SCAN_FULL) {
+    if (a.unit_flag && a.unit_flag[u] == 0) return;
+  }
+  if constexpr (MODE == SCAN_CAND) {
+    if (n <= a.k) return;  // everything is selected
+  }
+  const long long span = MODE == SCAN_SAMPLE ? SAMPLE_GROUP : a.wg_blocks;
+  const long long wb0 = (long long)blockIdx.x * (MODE == SCAN_SAMPLE ? SAMPLE_STRIDE : a.wg_blocks);
+  if (wb0 >= nb) return;
+  const long long wb1 = (wb0 + span) < nb ? (wb0 + span) : nb;
+  const long long nbcap = a.g.nbcap();
+  const long long cand_hi = n - kept_tail(n);  // candidates are tokens [4, cand_hi)
+
+  // ---- where a score goes (every lane of the wavefront calls emit) ----
+  float theta[GP];
+#pragma unroll
+  for (int h = 0; h < GP; ++h)
+    theta[h] = (MODE == SCAN_CAND && h < G) ? key_to_float(a.thresh[(long long)u * G + h])
+                                            : -__builtin_inff();
+  auto region = [&](int h) { return (((long long)u * G + h) * a.regions + blockIdx.x) * CAND_SLOTS; };
+  auto store = [&](long long tok, int h, float s) {  // FULL / SAMPLE
+    const long long uh = (long long)u * G + h;
+    if constexpr (MODE == SCAN_FULL) {
+      a.out[uh * a.out_ld + tok] = s;
+    } else {
+      a.out[uh * a.out_ld + (long long)blockIdx.x * (SAMPLE_GROUP * BLK) + (tok - wb0 * BLK)] = s;
+    }
+  };
+  auto append = [&](long long tok, int h, float s) {  // CAND, lanes whose test passed
+    if (tok < 4 || tok >= cand_hi) return;
+    const int off = atomicAdd(&sm.ccount[h], 1);
+    if (off < CAND_SLOTS) {
+      a.cand_val[region(h) + off] = s;
+      a.cand_idx[region(h) + off] = (int32_t)tok;
+    }
+  };
+  auto store_counts = [&]() {
+    if constexpr (MODE == SCAN_CAND) {
+      __syncthreads();
+      if (tid < G) a.cand_count[((long long)u * G + tid) * a.regions + blockIdx.x] = sm.ccount[tid];
+    }
+  };
+
+  // ---- plan: plane rows channel by channel (j ascending, p ascending) ----
+  int tj = 0;
+  if (MODE == SCAN_CAND && tid < GP) sm.ccount[tid] = 0;
+  if (tid < D) {
+    tj = a.depth[(long long)u * D + tid];
+    tj = tj > NP ? NP : tj;
+    sm.scan_buf[tid] = tj | ((tj > 0) << 16);
+  }
+  for (int i = tid; i < GP * D; i += SCAN_THREADS) {
+    const int h = i / D;
+    sm.q[h][i % D] = h < G ? a.q_basis[((long long)u * G + h) * D + i % D] : 0.f;
+  }
+  __syncthreads();
+  for (int off = 1; off < D; off <<= 1) {
+    int v = 0;
+    if (tid < D && tid >= off) v = sm.scan_buf[tid - off];
+    __syncthreads();
+    if (tid < D) sm.scan_buf[tid] += v;
+    __syncthreads();
+  }
+  const int R = sm.scan_buf[D - 1] & 0xFFFF;
+  const int CR = sm.scan_buf[D - 1] >> 16;  // read channels
+  if (R <= SCAN_FAST_ROWS) return;           // the fast kernel's unit (uniform)
+  if (tid < D && tj > 0) {
+    const int r0 = (sm.scan_buf[tid] & 0xFFFF) - tj;
+    const int c = (sm.scan_buf[tid] >> 16) - 1;
+    sm.chj[c] = (uint8_t)tid;
+    for (int p = 0; p < tj; ++p) {
+      sm.rowc[r0 + p] = (uint8_t)c;
+      sm.rowp[r0 + p] = (uint8_t)p;
+    }
+  }
+  __syncthreads();
+
+  if (R == 0) {  // nothing is read: every score is 0
+    // (wb1 - wb0) * 64 is a multiple of 64: each wavefront's lanes run the same trips
+    for (long long e = tid; e < (wb1 - wb0) * BLK; e += SCAN_THREADS) {
+      const long long tok = wb0 * BLK + e;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        if constexpr (MODE == SCAN_CAND) {
+          if (0.f >= theta[h]) append(tok, h, 0.f);
+        } else {
+          store(tok, h, 0.f);
+        }
+      }
+    }
+    store_counts();
+    return;
+  }
+
+  // frame size: |X| < 2^lx and R 2^lx <= 2^29
+  int lx = 29;
+  for (int r = R - 1; r > 0; r >>= 1) --lx;  // 29 - ceil(log2 R)
+  lx = lx > 22 ? 22 : lx;
+  const int nseg = (R + SEG - 1) / SEG;
+  const int nsteps = (int)((wb1 - wb0 + GB - 1) / GB);
+  const int ntask = nsteps * nseg;
+  auto step_g0 = [&](int i) { return wb0 + (long long)i * GB; };
+  auto step_blocks = [&](int i) {
+    const long long r = wb1 - step_g0(i);
+    return r < GB ? (int)r : GB;
+  };
+  auto seg_rows = [&](int s) { return (R - s * SEG) < SEG ? (R - s * SEG) : SEG; };
+
+  // ---- loads (global -> registers; written to LDS at the top of a task) ----
+  u32x4 pw[PL];        // plane words: row e / 8 of the segment, words 2 (e % 8), +1
+  u32x4 sw;            // scales: read channel tid / 2, blocks 8 (tid % 2) .. +7
+  const bool vec_scales = (nbcap % 8) == 0;
+  auto issue_planes = [&](int task) {
+    const int i = task / nseg, s = task % nseg;
+    const long long g0 = step_g0(i);
+    const int gblk = step_blocks(i);
+    const int rs = seg_rows(s);
+#pragma unroll
+    for (int k = 0; k < PL; ++k) {
+      const int e = tid + k * SCAN_THREADS;
+      const int rr = e >> 3, part = e & 7;
+      pw[k] = u32x4{0u, 0u, 0u, 0u};
+      if (rr < rs) {
+        const int r = s * SEG + rr;
+        const uint64_t* src =
+            a.planes + ((uint64_t)(gu * D + sm.chj[sm.rowc[r]]) * NP + sm.rowp[r]) * nbcap + g0 + 2 * part;
+        if (2 * part + 1 < gblk) {
+          pw[k] = *reinterpret_cast<const u32x4_a8*>(src);
+        } else if (2 * part < gblk) {
+          const uint64_t w0 = src[0];
+          pw[k] = u32x4{(uint32_t)w0, (uint32_t)(w0 >> 32), 0u, 0u};
+        }
+      }
+    }
+  };
+  auto issue_scales = [&](int i) {
+    sw = u32x4{0u, 0u, 0u, 0u};
+    const int c = tid >> 1, hf = tid & 1;
+    if (i >= nsteps || c >= CR) return;
+    const long long g0 = step_g0(i) + 8 * hf;
+    const int gblk = step_blocks(i) - 8 * hf;
+    const uint16_t* src = a.scales + (uint64_t)(gu * D + sm.chj[c]) * nbcap + g0;
+    if (vec_scales && gblk >= 8) {
+      sw = *reinterpret_cast<const u32x4*>(src);
+    } else {
+      uint32_t v[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int b = 0; b < 8; ++b)
+        if (b < gblk) v[b >> 1] |= (uint32_t)src[b] << (16 * (b & 1));
+      sw = u32x4{v[0], v[1], v[2], v[3]};
+    }
+  };
+  auto write_planes = [&](int task) {
+    (void)task;
+#pragma unroll
+    for (int k = 0; k < PL; ++k) {
+      const int e = tid + k * SCAN_THREADS;
+      *reinterpret_cast<u32x4*>(&sm.planes[(e >> 3) * PSTRIDE + 16 * (e & 7)]) = pw[k];
+    }
+  };
+  auto write_scales = [&](int i) {  // scales of step i (loaded by issue_scales(i))
+    const int c = tid >> 1, hf = tid & 1, par = i & 1;
+    float m = 0.f;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      m = fmaxf(m, half_bits_to_f32((uint16_t)(sw[b] & 0xFFFF)));
+      m = fmaxf(m, half_bits_to_f32((uint16_t)(sw[b] >> 16)));
+    }
+    m = fmaxf(m, __shfl_xor(m, 1));
+    if (c < CR) {
+      *reinterpret_cast<u32x4*>(&sm.sc[par][c][8 * hf]) = sw;
+      if (hf == 0) sm.smax[par][c] = m;
+    }
+  };
+
+  // ---- frames of step i (wavefront w handles heads w, w + 4) ----
+  auto compute_frame = [&](int i) {
+    const int par = i & 1, gblk = step_blocks(i);
+#pragma unroll
+    for (int k = 0; k < HG; ++k) {
+      const int h = wave + 4 * k;
+      if (h >= G) continue;  // wavefront-uniform
+      float best = 0.f;
+      uint32_t bkey = 0;
+      for (int c = lane; c < CR; c += 64) {
+        const float v = fabsf(sm.q[h][sm.chj[c]]) * 8.f * sm.smax[par][c];
+        best = fmaxf(best, v);
+        const uint32_t key = (__float_as_uint(v) & 0xFFFFFF00u) | (uint32_t)c;
+        bkey = key > bkey ? key : bkey;
+      }
+      best = wave_max(best);
+      bkey = wave_max_u32(bkey);
+      const int cs = (int)(bkey & 0xFFu);
+      const int E = frame_exp(best, lx);
+      int eb = E;
+      bool own = false;
+      if (lane < GB && lane < gblk && best > 0.f) {
+        // the block's own largest weight is at least a quarter of the frame's
+        // if the channel that sets the frame keeps a quarter of its step max
+        if (4.f * half_bits_to_f32(sm.sc[par][cs][lane]) < sm.smax[par][cs]) {
+          float mb = 0.f;
+          for (int c = 0; c < CR; ++c)
+            mb = fmaxf(mb, fabsf(sm.q[h][sm.chj[c]]) * 8.f * half_bits_to_f32(sm.sc[par][c][lane]));
+          eb = frame_exp(mb, lx);
+          own = eb != E;
+        }
+      }
+      if (lane < GB) {
+        sm.ex[par][h][lane] = eb;
+        sm.ith[par][h][lane] =
+            MODE == SCAN_CAND ? int_threshold(key_to_float(a.thresh[(long long)u * G + h]), eb) : 0;
+      }
+      const bool any_own = __ballot(own) != 0ull;
+      if (lane == 0) {
+        sm.exh[par][h] = E;
+        sm.own[par][h] = any_own;
+      }
+    }
+  };
+  // q_hj 2^(3-p+E_h) of the rows of task (i, s), into fqe[tp] (0 beyond the
+  // segment's rows and for heads >= G); wavefront w handles heads w, w + 4
+  auto fill_fqe = [&](int task, int tp) {
+    const int i = task / nseg, s = task % nseg;
+    const int rs = seg_rows(s);
+#pragma unroll
+    for (int k = 0; k < HG; ++k) {
+      const int h = wave + 4 * k;
+      const int E = h < G ? sm.exh[i & 1][h] : 0;
+      for (int rr = lane; rr < SEG; rr += 64) {
+        float v = 0.f;
+        if (h < G && rr < rs) {
+          const int r = s * SEG + rr;
+          v = ldexpf(sm.q[h][sm.chj[sm.rowc[r]]], 3 - sm.rowp[r] + E);
+        }
+        sm.fqe[tp][rr][h] = v;
+      }
+    }
+  };
+
+  // ---- prologue: scales and frames of step 0, fqe of task 0 (the loop's
+  // first barrier publishes them) ----
+  issue_scales(0);
+  write_scales(0);
+  __syncthreads();
+  issue_planes(0);
+  issue_scales(1);
+  compute_frame(0);
+  fill_fqe(0, 0);
+
+  // MFMA operand addressing: lane l is column / A-row l % 16 of K-group l / 16;
+  // a transposing read takes, in each 16-lane group, row r0 + (l % 16) / 2
+  const int kg = lane >> 4, s16 = lane & 15;
+  const int rsub = s16 >> 1, ahalf = 8 * (s16 & 1);
+  uint32_t bmask[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) bmask[c] = 0x01010101u << (2 * c + (s16 >> 3));
+  const uint32_t neg7 = (s16 >> 3) ? 0xFFFFFFFFu : 0u;  // lanes whose c = 3 column keeps bit 7
+  const i32x4 ones4 = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
+  const long ones2 = 0x0101010101010101l;
+
+  i32x4 acc[NB][HG][4];
+  i32x4 accc[NB][HG];
+
+  for (int task = 0; task < ntask; ++task) {
+    const int i = task / nseg, s = task % nseg;
+    const int par = i & 1, tp = task & 1;
+    const long long g0 = step_g0(i);
+    const int gblk = step_blocks(i);
+    const int rs = seg_rows(s);
+    int n64 = rs >> 6, rem = rs & 63;
+    if (rem > 32) {
+      ++n64;
+      rem = 0;
+    }
+    const bool has32 = rem > 0;
+    const int rp = 64 * n64 + (has32 ? 32 : 0);  // rows with A records (zero beyond rs)
+
+    // ---- the previous task's planes and A records are no longer read: this
+    // task's plane words, and the next step's scales, into LDS ----
+    __syncthreads();
+    write_planes(task);
+    if (s == 0 && i + 1 < nsteps) write_scales(i + 1);
+
+    // ---- A records: X digits of (block, row) for every head ----
+    const bool own_any = [&]() {
+      bool o = false;
+#pragma unroll
+      for (int h = 0; h < G; ++h) o |= sm.own[par][h] != 0;
+      return o;
+    }();
+    // thread -> block tid / 16, rows tid % 16 + 16 k (rp is a multiple of 32)
+    for (int rr = tid & 15, b = tid >> 4; rr < rp; rr += 16) {
+      u32x4 rec[HG];
+#pragma unroll
+      for (int hg = 0; hg < HG; ++hg) rec[hg] = u32x4{0u, 0u, 0u, 0u};
+      if (b < gblk && rr < rs) {
+        const float sv = half_bits_to_f32(sm.sc[par][sm.rowc[s * SEG + rr]][b]);
+#pragma unroll
+        for (int hg = 0; hg < HG; ++hg) {
+          const float4 f = *reinterpret_cast<const float4*>(&sm.fqe[tp][rr][4 * hg]);
+          float fv[4] = {f.x, f.y, f.z, f.w};
+          if (own_any) {
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+              const int h = 4 * hg + x;
+              if (h < G) fv[x] = ldexpf(fv[x], sm.ex[par][h][b] - sm.exh[par][h]);
+            }
+          }
+#pragma unroll
+          for (int x = 0; x < 4; ++x)
+            rec[hg][x] = (uint32_t)__builtin_fmaf(fv[x], sv, DIGIT_BIAS) ^ 0x808080u;
+        }
+      }
+#pragma unroll
+      for (int hg = 0; hg < HG; ++hg)
+        *reinterpret_cast<u32x4*>(&sm.atab[b][rr][16 * hg]) = rec[hg];
+    }
+    __syncthreads();  // planes, A records and the next step's scales are in LDS
+    if (task + 1 < ntask) {
+      issue_planes(task + 1);
+      const int i1 = (task + 1) / nseg;
+      if (i1 != i) issue_scales(i1 + 1);
+      // what the next task needs: the next step's frames (from its scales,
+      // written above) and its rows' q 2^(3-p+E); each wavefront fills the
+      // heads whose frames it computed
+      if (i1 != i) compute_frame(i1);
+      fill_fqe(task + 1, tp ^ 1);
+    }
+
+    // ---- contraction: wavefront takes blocks 4 wave .. 4 wave + 3 of the step ----
+    const int wb = NB * wave;
+    if (s == 0) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int hg = 0; hg < HG; ++hg) {
+          accc[b][hg] = i32x4{0, 0, 0, 0};
+#pragma unroll
+          for (int c = 0; c < 4; ++c) acc[b][hg][c] = i32x4{0, 0, 0, 0};
+        }
+    }
+    if (wb < gblk) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const int blk = wb + b;
+        if (blk >= gblk) break;
+        for (int kp = 0; kp < n64; ++kp) {
+          const int r0 = 64 * kp + 16 * kg + rsub;
+          const i32x2 b0 = tr8(&sm.planes[r0 * PSTRIDE + 8 * blk]);
+          const i32x2 b1 = tr8(&sm.planes[(r0 + 8) * PSTRIDE + 8 * blk]);
+          const i32x4 bv = {b0.x, b0.y, b1.x, b1.y};
+#pragma unroll
+          for (int hg = 0; hg < HG; ++hg) {
+            const i32x2 a0 = tr8(&sm.atab[blk][r0][16 * hg + ahalf]);
+            const i32x2 a1 = tr8(&sm.atab[blk][r0 + 8][16 * hg + ahalf]);
+            const i32x4 av = {a0.x, a0.y, a1.x, a1.y};
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              const i32x4 m = bv & (int)bmask[c];
+              acc[b][hg][c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, m, acc[b][hg][c], 0, 0, 0);
+            }
+            accc[b][hg] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, ones4, accc[b][hg], 0, 0, 0);
+          }
+        }
+        if (has32) {
+          const int r0 = 64 * n64 + 8 * kg + rsub;
+          const i32x2 b0 = tr8(&sm.planes[r0 * PSTRIDE + 8 * blk]);
+#pragma unroll
+          for (int hg = 0; hg < HG; ++hg) {
+            const i32x2 a0 = tr8(&sm.atab[blk][r0][16 * hg + ahalf]);
+            const long av = __builtin_bit_cast(long, a0);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              const i32x2 m = b0 & (int)bmask[c];
+              acc[b][hg][c] = __builtin_amdgcn_mfma_i32_16x16x32_i8(av, __builtin_bit_cast(long, m),
+                                                                     acc[b][hg][c], 0, 0, 0);
+            }
+            accc[b][hg] = __builtin_amdgcn_mfma_i32_16x16x32_i8(av, ones2, accc[b][hg], 0, 0, 0);
+          }
+        }
+      }
+    }
+
+    // ---- epilogue after the last segment: lane <-> (head 4 hg + l / 16, column l % 16) ----
+    if (s == nseg - 1 && wb < gblk) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const int blk = wb + b;
+        if (blk >= gblk) break;
+        const long long tok0 = (g0 + blk) * BLK + 8 * (s16 & 7) + (s16 >> 3);
+#pragma unroll
+        for (int hg = 0; hg < HG; ++hg) {
+          const int h = 4 * hg + kg;
+          const i32x4 dc = accc[b][hg];
+          const uint32_t cc = ((uint32_t)dc.z << 16) + ((uint32_t)dc.y << 8) + (uint32_t)dc.x;  // C
+          const int eb = sm.ex[par][h < G ? h : 0][blk];
+          const int ith = sm.ith[par][h < G ? h : 0][blk];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const int bp = 2 * c + (s16 >> 3);
+            const i32x4 d = acc[b][hg][c];
+            // S = sum_r X_r b_r (the digit sums are multiples of 2^bp); T = 2 S - C
+            const uint32_t sS = ((uint32_t)d.z << (16 - bp)) + ((uint32_t)d.y << (8 - bp)) +
+                                (uint32_t)(d.x >> bp);
+            uint32_t s2 = 2u * sS;
+            if (c == 3) s2 = (s2 ^ neg7) - neg7;  // bit 7 kept as the int8 byte 0x80 = -128
+            const int t = (int)(s2 - cc);
+            const long long tok = tok0 + 2 * c;
+            if constexpr (MODE == SCAN_CAND) {
+              const bool pass = h < G && t >= ith;
+              if (__ballot(pass) != 0ull && pass)
+                append(tok, h, ldexpf((float)t, -(eb + 1)));
+            } else {
+              if (h < G) store(tok, h, ldexpf((float)t, -(eb + 1)));
+            }
+          }
+        }
+      }
+    }
+  }
+  store_counts();
+}
+
+template <int G, int MODE>
+hipError_t launch_gm(const ScanArgs& a0, int span, hipStream_t st) {
+  ScanArgs a = a0;
+  long long maxnb = 0;
+  for (int s = 0; s < a.g.S; ++s) maxnb = a.g.n[s] / BLK > maxnb ? a.g.n[s] / BLK : maxnb;
+  if (maxnb == 0 || a.g.units() == 0) return hipSuccess;
+  dim3 grid;
+  if (MODE == SCAN_SAMPLE) {
+    a.wg_blocks = SAMPLE_GROUP;
+    grid = dim3((unsigned)sample_groups(a.g), (unsigned)a.g.units());
+  } else {
+    const int wb = span > 0 ? span : scan_wg_blocks(a.g);
+    a.wg_blocks = wb;
+    grid = dim3((unsigned)((maxnb + wb - 1) / wb), (unsigned)a.g.units());
+  }
+  scan_wide_kernel<G, MODE><<<grid, SCAN_THREADS, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+template <int MODE>
+hipError_t dispatch(const ScanArgs& a, int span, hipStream_t st) {
+  switch (a.g.G) {
+    case 1: return launch_gm<1, MODE>(a, span, st);
+    case 2: return launch_gm<2, MODE>(a, span, st);
+    case 4: return launch_gm<4, MODE>(a, span, st);
+    case 8: return launch_gm<8, MODE>(a, span, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_scan_wide(const ScanArgs& a, int mode, int span, hipStream_t st) {
+  switch (mode) {
+    case SCAN_FULL: return dispatch<SCAN_FULL>(a, span, st);
+    case SCAN_SAMPLE: return dispatch<SCAN_SAMPLE>(a, span, st);
+    case SCAN_CAND: return dispatch<SCAN_CAND>(a, span, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace bpk

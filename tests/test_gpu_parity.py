@@ -171,7 +171,7 @@ def _oracle_unit(inp, n, budget, k, scale):
                          rot=inp["rot"])
 
 
-@pytest.mark.parametrize("budget", [64, 88, 128])
+@pytest.mark.parametrize("budget", [64, 88, 128, 200, 512])
 def test_calls_c2(bpk, c2, budget):
     b, wl = bpk
     cfg, cache, q, inps = c2
@@ -226,6 +226,38 @@ def test_decode_step_matches_single_calls(bpk, c2):
     torch.cuda.synchronize()
     assert torch.equal(idx, idx2)
     assert torch.equal(out, out2)
+
+
+def test_scan_mixed_row_counts(bpk, c2):
+    """One scan over units that read up to 128 plane rows and units that read
+    more: each unit's scores equal those of a call over that unit's budget."""
+    b, wl = bpk
+    cfg, cache, q, inps = c2
+    n = cfg.n
+    d_small, qb = b.alloc_depth(cache, q, 0, 1, 88)
+    d_big, _ = b.alloc_depth(cache, q, 0, 1, 200)
+    depth = d_small.clone()
+    depth[0, 0, 1::2] = d_big[0, 0, 1::2]  # odd KV heads read 200 rows
+    scores = b.scan_scores(cache, qb, depth, 0, 1)
+    torch.cuda.synchronize()
+    sc = scores.cpu().numpy()
+    for h in range(cfg.heads):
+        budget = 200 if h % 2 else 88
+        ref = _oracle_unit(inps[h], n, budget, cfg.k, wl.softmax_scale(cfg))
+        P.check_scores(sc[0, 0, h, :, :n], ref["scores"], ref["l1"], f"mixed head {h} P={budget}")
+
+
+@pytest.mark.parametrize("budget", [88, 200])
+def test_decode_step_matches_single_calls_budgets(bpk, c2, budget):
+    b, wl = bpk
+    cfg, cache, q, inps = c2
+    scale = wl.softmax_scale(cfg)
+    idx = torch.empty((1, 1, 8, 4, cfg.k), dtype=torch.int32, device="cuda")
+    out = b.decode_step(cache, q, 0, 1, budget, cfg.k, scale, idx_out=idx)
+    depth, qb = b.alloc_depth(cache, q, 0, 1, budget)
+    idx2 = b.select_topk(cache, b.scan_scores(cache, qb, depth, 0, 1), 0, 1, cfg.k)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx2)
 
 
 # ---------------------------------------------------------------------------
