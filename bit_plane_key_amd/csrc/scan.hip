@@ -11,26 +11,42 @@
 //   s_hat = sum_j q_hj s_bj m_ij = sum_r w_r (b_r - 1/2) = S - C/2,
 //   S = sum_r w_r b_r,  C = sum_r w_r.
 // The weights of one 16-block step and head are put in a common fixed-point
-// frame, X_r = round(w_r 2^E), with E chosen so that sum_r |X_r| < 2^29, and
-// each X_r (|X_r| < 2^23) is split into three balanced signed bytes.  S and C
-// are then exact integer contractions of int8 digits with 0/1 bits, and the
-// score is s_hat = (2 S - C) 2^-(E+1).  The only rounding is that of X_r (half
-// a unit), far below the 1e-4 tolerance relative to the score's own L1 mass
-// as long as the frame is within a few bits of each block's largest weight.
-// E comes from max_j |q_hj| 8 smax_j over the step (smax_j = the largest scale
-// of channel j in the step); a block whose own largest weight may be more
-// than 4x smaller (tested on the channel that sets the frame) gets a frame of
-// its own.  Frames depend only on the step's blocks, so scores are
-// bit-identical in every launch mode.
+// frame, X_r = round(w_r 2^E) (to nearest, ties to even), with E chosen so
+// that |X_r| < 2^21 and sum_r |X_r| <= 2^29, and each X_r is split into three
+// balanced signed bytes.  S and C are then exact integer contractions of int8
+// digits with 0/1 bits, and the score is s_hat = (2 S - C) 2^-(E+1).  The only
+// rounding is that of X_r (half a unit), far below the 1e-4 tolerance relative
+// to the score's own L1 mass as long as the frame is within a few bits of each
+// block's largest weight.  E comes from max_j |q_hj| 8 smax_j over the step
+// (smax_j = the largest scale of channel j in the step); a block whose own
+// largest weight may be more than 4x smaller (tested on the channel that sets
+// the frame) gets a frame of its own.  Frames depend only on the step's blocks,
+// so scores are bit-identical in every launch mode.
+//
+// The digits come from one fma and one xor-add: for |X| < 2^21,
+// f = X + 2^23 + 0x408080 lies in [2^23, 2^24), where a float's low 23 bits
+// are the integer f - 2^23 = X + 0x408080; flipping bit 7 of the two low bytes
+// and subtracting 0x40 from the third (0x4B40 from the upper half, which also
+// clears the exponent byte up to a borrow) leaves bytes d0, d1 in [-128, 127]
+// and d2 in [-64, 63] with d0 + 2^8 d1 + 2^16 d2 = X.  The fourth byte (0 or
+// -1) only feeds an MFMA output row that is never read.
+//
+// The candidate test (decode_step's fused selection) is a cheap superset of
+// "score >= theta": with t = floor(theta 2^(E+1)) - 32 (the float rounding of
+// 2 S - C moves it by at most 32 units), a token passes if
+// S' >= floor((t + C) / 2) - 2^14, where S' is S without its lowest digit row
+// (which is at most 128 R <= 2^14 in magnitude).  Passing tokens are appended
+// with their exact scores; the selection keeps only those at or above theta.
 //
 // Mapping onto gfx950 (fast kernel):
 // * A workgroup (4 wavefronts, two per CU) owns a range of blocks of one unit
 //   and walks it in steps of 16 blocks, with one barrier per step.  Each
 //   thread prefetches its share of the step's plane words (coalesced 128-byte
-//   reads of every read row) two steps ahead and the fp16 scales three steps
-//   ahead, in registers; at the top of a step they go to LDS (planes double-,
-//   scales triple-buffered), and after the barrier wavefront w computes the
-//   frames of head w for the next step.
+//   reads of every read row; buffer loads at offsets fixed per thread, rows
+//   past the last read one out of range so that they read zeros) two steps
+//   ahead and the fp16 scales three steps ahead, in registers; at the top of a
+//   step they go to LDS (planes double-, scales triple-buffered), and after the
+//   barrier wavefront w computes the frames of head w for the next step.
 // * Wavefront w then takes blocks 4w .. 4w+3 one at a time: it writes the
 //   block's X digits (4 bytes per (row, head)) into its own LDS records and
 //   contracts them with the plane bits on the matrix cores,
@@ -43,9 +59,8 @@
 //   bit 7: the int8 byte 0x80 is -128).  A fifth product with all-one bytes
 //   gives C.
 // * Lane l ends with the digit sums of head 4 hg + l / 16 for its token and
-//   recombines them with shifts into the int32 S; the candidate test compares
-//   (float)(2 S - C) with threshold 2^(E+1), the same value the score is
-//   written from.
+//   recombines them with shifts; one branch per block skips the appends when
+//   no lane passes.
 #include "scan_common.h"
 
 namespace bpk {
@@ -56,19 +71,24 @@ constexpr int GB = SCAN_GB;           // blocks per step
 constexpr int RMAX = SCAN_FAST_ROWS;  // plane rows at most
 constexpr int CMAX = D;               // read channels at most
 constexpr int PSTRIDE = 144;          // LDS bytes per plane row: 16 words + 16 bytes of padding
-constexpr int PL = RMAX * 8 / SCAN_THREADS;  // 16-byte plane loads per thread and step
+constexpr int SCS = 24;               // LDS fp16 slots per read channel: 16 blocks + 8 of padding
+constexpr long long FAST_MAX_CAP = 1ll << 25;   // one unit's planes fit a 32-bit buffer offset
+constexpr float DIGIT_MAGIC = 12615808.f;       // 2^23 + 0x408080
+constexpr uint32_t OUT_OF_RANGE = 0x80000000u;  // a buffer offset past every unit's planes
+constexpr int RSRC_WORD3 = 0x00020000;          // raw (untyped) buffer, 32-bit data format
 
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 template <int HG>
 struct FastSmem {
   static constexpr int GP = 4 * HG;               // heads, padded to whole MFMA row groups
   alignas(16) uint8_t planes[2][RMAX * PSTRIDE];  // per step parity: [row][block] words
   alignas(16) uint8_t atab[4][2][RMAX][16 * HG];  // per wavefront, two blocks: [row] X digits, 4 bytes a head
-  alignas(16) uint16_t sc[3][CMAX][GB];           // per step mod 3: fp16 scales [read channel][block]
+  alignas(16) uint16_t sc[3][CMAX][SCS];          // per step mod 3: fp16 scales [read channel][block]
   float smax[3][CMAX];                            // per step mod 3: largest scale of a read channel
   float q[GP][D];                                 // the unit's query heads (0 beyond G)
-  float thp[2][GP][GB];                           // per step parity: threshold 2^(E+1) of (head, block)
+  int tlo[2][GP][GB];                             // per step parity: candidate test threshold of (head, block)
   int ex[2][GP][GB];                              // per step parity: frame exponent of (head, block)
   int exh[2][GP];                                 // per step parity: frame exponent of the step
   int own[2][GP];                                 // per step parity: a block of the head has its own frame
@@ -79,13 +99,28 @@ struct FastSmem {
   int ccount[GP];                                 // candidates of this workgroup per head
 };
 
-// theta 2^(E+1) for the test (float)T >= it, T an integer: values of
-// magnitude below 1 (including an underflow to 0) are replaced by +-1/2, which
-// decides every integer the same way
-__device__ __forceinline__ float scaled_threshold(float theta, int e) {
-  float t = ldexpf(theta, e + 1);
-  if (theta != 0.f && fabsf(t) < 1.f) t = theta > 0.f ? 0.5f : -0.5f;
-  return t;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           RSRC_WORD3);
+}
+
+// the three balanced digits of X = round(f s) (|X| < 2^21) in bytes 0..2
+__device__ __forceinline__ uint32_t x_digits(float f, _Float16 s) {
+  const uint32_t b = __float_as_uint(__builtin_fmaf(f, (float)s, DIGIT_MAGIC));
+  uint32_t x;
+  asm("v_xad_u32 %0, %1, %2, %3" : "=v"(x) : "v"(b), "s"(0x8080u), "v"(0xB4C00000u));
+  return x;
+}
+
+// t - 2^15 of the candidate test, with t clamped to just outside the range of
+// 2 S - C (|2 S - C| <= 2^29)
+__device__ __forceinline__ int cand_threshold(float theta, int e) {
+  const float t = ldexpf(theta, e + 1);
+  int t1;
+  if (!(t < 536870912.f)) t1 = (1 << 29) + 1;  // above every score (or NaN)
+  else if (t <= -536870912.f) t1 = -(1 << 29) - 1;
+  else t1 = (int)floorf(t) - 32;
+  return t1 - (1 << 15);
 }
 
 template <int G, int MODE, bool VEC>
@@ -155,6 +190,10 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : 2) void scan_fast_kernel
     const int h = i / D;
     sm.q[h][i % D] = h < G ? a.q_basis[((long long)u * G + h) * D + i % D] : 0.f;
   }
+  if (tid < 2 * GP * GB) {  // padding heads never pass
+    const int h = (tid / GB) % GP;
+    if (h >= G) sm.tlo[tid / (GP * GB)][h][tid % GB] = 1 << 30;
+  }
   __syncthreads();
   for (int off = 1; off < D; off <<= 1) {
     int v = 0;
@@ -201,7 +240,7 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : 2) void scan_fast_kernel
   // frame size: |X| < 2^lx and R 2^lx <= 2^29
   int lx = 29;
   for (int r = R - 1; r > 0; r >>= 1) --lx;  // 29 - ceil(log2 R)
-  lx = lx > 22 ? 22 : lx;
+  lx = lx > 21 ? 21 : lx;
   const int nsteps = (int)((wb1 - wb0 + GB - 1) / GB);
   const int rpt = (R + 31) / 32;  // 32-row pieces of the K passes (A is zero beyond R)
   auto step_g0 = [&](int i) { return wb0 + (long long)i * GB; };
@@ -209,98 +248,67 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : 2) void scan_fast_kernel
     const long long r = wb1 - step_g0(i);
     return r < GB ? (int)r : GB;
   };
-
-  // ---- per-thread load slots ----
-  // planes: slot k covers row (tid + 256 k) / 8, words 2 ((tid + 256 k) % 8), +1
-  // of the step; scales: read channel tid / 2, blocks 8 (tid % 2) .. +7.  With
-  // VEC (capacity / 64 a multiple of 8: every plane row 16-byte aligned, every
-  // scale row too) each thread issues the same loads at every step, with no
-  // branch: rows >= R read row 0, words past the capacity re-read the last
-  // ones, steps past the range re-read the last step (duplicates the caches
-  // serve, never used).  The compiler can then wait for the oldest step's loads
-  // alone, and two steps stay in flight.
-  const uint64_t* prow[PL];  // the slot's plane row (row 0 for rows >= R)
-  int ppart[PL];
-  bool pvalid[PL];
-#pragma unroll
-  for (int k = 0; k < PL; ++k) {
-    const int e = tid + k * SCAN_THREADS, r = e >> 3, rr = r < R ? r : 0;
-    prow[k] = a.planes + ((uint64_t)(gu * D + sm.chj[sm.rowc[rr]]) * NP + sm.rowp[rr]) * nbcap;
-    ppart[k] = 2 * (e & 7);
-    pvalid[k] = r < R;
-  }
-  const int sc_c = tid >> 1, sc_h = tid & 1;
-  const uint16_t* srow = a.scales + (uint64_t)(gu * D + sm.chj[sc_c < CR ? sc_c : 0]) * nbcap;
-  const bool svalid = sc_c < CR;
   const long long g0_last = step_g0(nsteps - 1);
-
-  u32x4 pw[2][PL];  // plane words of the steps of parity 0 / 1
-  u32x4 sw[2];      // scales of the steps of parity 0 / 1
-  auto issue_planes = [&](int i, auto P) {
-    constexpr int p = decltype(P)::value;
-    if constexpr (VEC) {
-      const long long g0 = step_g0(i) < g0_last ? step_g0(i) : g0_last;
-#pragma unroll
-      for (int k = 0; k < PL; ++k) {
-        const long long w = (g0 + ppart[k]) < nbcap - 2 ? (g0 + ppart[k]) : nbcap - 2;
-        pw[p][k] = *reinterpret_cast<const u32x4_a8*>(prow[k] + w);
-      }
-    } else {
-      if (i >= nsteps) return;
-      const long long g0 = step_g0(i);
-      const int gblk = step_blocks(i);
-#pragma unroll
-      for (int k = 0; k < PL; ++k) {
-        pw[p][k] = u32x4{0u, 0u, 0u, 0u};
-        if (pvalid[k]) {
-          const uint64_t* src = prow[k] + g0 + ppart[k];
-          if (ppart[k] + 1 < gblk) {
-            pw[p][k] = *reinterpret_cast<const u32x4_a8*>(src);
-          } else if (ppart[k] < gblk) {
-            const uint64_t w0 = src[0];
-            pw[p][k] = u32x4{(uint32_t)w0, (uint32_t)(w0 >> 32), 0u, 0u};
-          }
-        }
-      }
-    }
+  // the unit's planes and scales; a step's loads use a buffer based at its
+  // first block (steps past the range re-read the last one, never used)
+  const long long unit_words = (long long)D * NP * nbcap;
+  const uint64_t* ubase = a.planes + gu * unit_words;
+  const uint16_t* sbase = a.scales + gu * (long long)D * nbcap;
+  auto step_first = [&](int i) { return step_g0(i) < g0_last ? step_g0(i) : g0_last; };
+  auto plane_rsrc = [&](int i) {
+    const long long f = step_first(i);
+    return make_rsrc(ubase + f, (uint32_t)((unit_words - f) * 8));
   };
+  auto scale_rsrc = [&](int i) {
+    const long long f = step_first(i);
+    return make_rsrc(sbase + f, (uint32_t)(((long long)D * nbcap - f) * 2));
+  };
+
+  // ---- scales: thread t loads read channel t / 2, blocks 8 (t % 2) .. +7 ----
+  const int sc_c = tid >> 1, sc_h = tid & 1;
+  const bool svalid = sc_c < CR;
+  const long long srow = svalid ? (long long)sm.chj[sc_c] * nbcap : 0;
+  // VEC: byte offsets; in the last step clamped to the capacity (the words past
+  // it are never used)
+  uint32_t soff = OUT_OF_RANGE, soff_last = OUT_OF_RANGE;
+  if (svalid) {
+    soff = (uint32_t)((srow + 8 * sc_h) * 2);
+    const long long w = (g0_last + 8 * sc_h) < nbcap - 8 ? (g0_last + 8 * sc_h) : nbcap - 8;
+    soff_last = (uint32_t)((srow + w - g0_last) * 2);
+  }
+  u32x4 sw[2];  // scales of the steps of parity 0 / 1
   auto issue_scales = [&](int i, auto P) {
     constexpr int p = decltype(P)::value;
+    const auto rs = scale_rsrc(i);
     if constexpr (VEC) {
-      const long long g0 = step_g0(i) < g0_last ? step_g0(i) : g0_last;
-      const long long w = (g0 + 8 * sc_h) < nbcap - 8 ? (g0 + 8 * sc_h) : nbcap - 8;
-      sw[p] = *reinterpret_cast<const u32x4*>(srow + w);
+      sw[p] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(i >= nsteps - 1 ? soff_last : soff), 0, 0);
     } else {
-      if (i >= nsteps) return;
-      sw[p] = u32x4{0u, 0u, 0u, 0u};
-      if (!svalid) return;
-      const uint16_t* src = srow + step_g0(i) + 8 * sc_h;
-      const int gblk = step_blocks(i) - 8 * sc_h;
+      const long long f = step_first(i);
       uint32_t v[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int b = 0; b < 8; ++b)
-        if (b < gblk) v[b >> 1] |= (uint32_t)src[b] << (16 * (b & 1));
+      for (int b = 0; b < 8; ++b) {
+        const long long w = (f + 8 * sc_h + b) < nbcap ? (f + 8 * sc_h + b) : nbcap - 1;
+        const uint32_t o = svalid ? (uint32_t)((srow + w - f) * 2) : OUT_OF_RANGE;
+        v[b >> 1] |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, (int)o, 0, 0) << (16 * (b & 1));
+      }
       sw[p] = u32x4{v[0], v[1], v[2], v[3]};
-    }
-  };
-  auto write_planes = [&](int i, auto P) {  // rows >= R: row 0's words, never used (A is zero there)
-    constexpr int p = decltype(P)::value;
-#pragma unroll
-    for (int k = 0; k < PL; ++k) {
-      const int e = tid + k * SCAN_THREADS;
-      *reinterpret_cast<u32x4*>(&sm.planes[i & 1][(e >> 3) * PSTRIDE + 16 * (e & 7)]) = pw[p][k];
     }
   };
   auto write_scales = [&](int i, auto P) {  // scales of step i and their per-channel max
     constexpr int p = decltype(P)::value;
     const int b3 = i % 3;
-    // the blocks of the step only; fp16 bits of non-negative values order like the values
-    const int nv = step_blocks(i) - 8 * sc_h;
+    // fp16 bits of non-negative values order like the values; only the step's blocks count
     u16x2 mv = {0, 0};
+    if (step_blocks(i) == GB) {
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      const uint32_t keep = (2 * x < nv ? 0xFFFFu : 0u) | (2 * x + 1 < nv ? 0xFFFF0000u : 0u);
-      mv = __builtin_elementwise_max(mv, __builtin_bit_cast(u16x2, sw[p][x] & keep));
+      for (int x = 0; x < 4; ++x) mv = __builtin_elementwise_max(mv, __builtin_bit_cast(u16x2, sw[p][x]));
+    } else {
+      const int nv = step_blocks(i) - 8 * sc_h;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const uint32_t keep = (2 * x < nv ? 0xFFFFu : 0u) | (2 * x + 1 < nv ? 0xFFFF0000u : 0u);
+        mv = __builtin_elementwise_max(mv, __builtin_bit_cast(u16x2, sw[p][x] & keep));
+      }
     }
     uint32_t m = mv.x > mv.y ? mv.x : mv.y;
     const uint32_t mo = (uint32_t)__shfl_xor((int)m, 1);
@@ -311,12 +319,19 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : 2) void scan_fast_kernel
     }
   };
 
-  // the thresholds of this wavefront's heads (w, w + 4), read once
+  // the thresholds of this wavefront's heads (w, w + 4), read once, and
+  // |q_hj| 8 of the read channels lane, lane + 64
   float theta_k[HG];
+  float qa8[HG][2];
 #pragma unroll
   for (int k = 0; k < HG; ++k) {
     const int h = wave + 4 * k;
     theta_k[k] = (MODE == SCAN_CAND && h < G) ? key_to_float(a.thresh[(long long)u * G + h]) : 0.f;
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+      const int c = lane + 64 * cc;
+      qa8[k][cc] = (h < G && c < CR) ? fabsf(sm.q[h][sm.chj[c]]) * 8.f : 0.f;
+    }
   }
 
   // ---- frames of step i: wavefront w handles heads w, w + 4 ----
@@ -327,9 +342,12 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : 2) void scan_fast_kernel
       const int h = wave + 4 * k;
       if (h >= G) continue;  // wavefront-uniform
       uint32_t key = 0;
-      for (int c = lane; c < CR; c += 64) {
-        const float v = fabsf(sm.q[h][sm.chj[c]]) * 8.f * sm.smax[b3][c];
-        const uint32_t kk = (__float_as_uint(v) & 0xFFFFFF00u) | (uint32_t)c;
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+        const int c = lane + 64 * cc;
+        if (cc == 1 && CR <= 64) break;  // uniform
+        const float v = qa8[k][cc] * (c < CR ? sm.smax[b3][c] : 0.f);
+        const uint32_t kk = v > 0.f ? (__float_as_uint(v) & 0xFFFFFF00u) | (uint32_t)c : 0u;
         key = kk > key ? kk : key;
       }
       key = wave_max_u32(key);
@@ -352,8 +370,7 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : 2) void scan_fast_kernel
       }
       if (lane < GB) {
         sm.ex[par][h][lane] = eb;
-        if constexpr (MODE == SCAN_CAND)
-          sm.thp[par][h][lane] = scaled_threshold(theta_k[k], eb);
+        if constexpr (MODE == SCAN_CAND) sm.tlo[par][h][lane] = cand_threshold(theta_k[k], eb);
       }
       const bool any_own = __ballot(own) != 0ull;
       if (lane == 0) {
@@ -370,16 +387,67 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : 2) void scan_fast_kernel
     constexpr int N64 = RPT / 2;
     constexpr bool HAS32 = (RPT & 1) != 0;
     constexpr int NPASS = 32 * RPT / RPP;  // builder passes
+    constexpr int PL = RPT;                // 16-byte plane loads per thread and step
+
+    // ---- plane loads: slot k covers row (tid + 256 k) / 8, words
+    // 2 ((tid + 256 k) % 8), +1 of the step; rows >= R read zeros ----
+    uint32_t poff[PL], poff_last[PL];  // byte offsets; in the last step clamped to the capacity
+#pragma unroll
+    for (int k = 0; k < PL; ++k) {
+      const int e = tid + k * SCAN_THREADS, r = e >> 3, part = 2 * (e & 7);
+      poff[k] = poff_last[k] = OUT_OF_RANGE;
+      if (r < R) {
+        const long long row = ((long long)sm.chj[sm.rowc[r]] * NP + sm.rowp[r]) * nbcap;
+        poff[k] = (uint32_t)((row + part) * 8);
+        const long long w = (g0_last + part) < nbcap - 2 ? (g0_last + part) : nbcap - 2;
+        poff_last[k] = (uint32_t)((row + w - g0_last) * 8);
+      }
+    }
+    u32x4 pw[2][PL];  // plane words of the steps of parity 0 / 1
+    auto issue_planes = [&](int i, auto P) {
+      constexpr int p = decltype(P)::value;
+      const auto rs = plane_rsrc(i);
+      const bool last = i >= nsteps - 1;
+#pragma unroll
+      for (int k = 0; k < PL; ++k) {
+        if constexpr (VEC) {
+          pw[p][k] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(last ? poff_last[k] : poff[k]), 0, 0);
+        } else {
+          // 8-byte aligned rows: two 8-byte loads, each word clamped to the capacity
+          const long long f = step_first(i);
+          const int e = tid + k * SCAN_THREADS, r = e >> 3, part = 2 * (e & 7);
+          u32x2 wv[2];
+#pragma unroll
+          for (int x = 0; x < 2; ++x) {
+            uint32_t o = OUT_OF_RANGE;
+            if (r < R) {
+              const long long w = (f + part + x) < nbcap ? (f + part + x) : nbcap - 1;
+              o = (uint32_t)((long long)poff[k] + (w - f - part) * 8);
+            }
+            wv[x] = __builtin_amdgcn_raw_buffer_load_b64(rs, (int)o, 0, 0);
+          }
+          pw[p][k] = u32x4{wv[0].x, wv[0].y, wv[1].x, wv[1].y};
+        }
+      }
+    };
+    auto write_planes = [&](int i, auto P) {
+      constexpr int p = decltype(P)::value;
+#pragma unroll
+      for (int k = 0; k < PL; ++k) {
+        const int e = tid + k * SCAN_THREADS;
+        *reinterpret_cast<u32x4*>(&sm.planes[i & 1][(e >> 3) * PSTRIDE + 16 * (e & 7)]) = pw[p][k];
+      }
+    };
 
     // builder items: pass m covers row RPP m + lane / NPAIR and heads
     // 2 (lane % NPAIR), +1; rows >= R have zero weights, hence zero digits
     const int prow = lane / NPAIR, ppair = lane % NPAIR;
     float fq0[NPASS][2];  // q_hj 2^(3-p) of the item's row and heads
-    int soff[NPASS];      // the item's row's scales in sc[.]: read channel * GB
+    int soffm[NPASS];     // the item's row's scales in sc[.]: read channel * SCS
 #pragma unroll
     for (int m = 0; m < NPASS; ++m) {
       const int r = m * RPP + prow;
-      soff[m] = (r < R ? sm.rowc[r] : 0) * GB;
+      soffm[m] = (r < R ? sm.rowc[r] : 0) * SCS;
 #pragma unroll
       for (int x = 0; x < 2; ++x) {
         const int h = 2 * ppair + x;
@@ -390,165 +458,232 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : 2) void scan_fast_kernel
     // MFMA operand addressing: lane l is column / A-row l % 16 of K-group l / 16;
     // a transposing read takes, in each 16-lane group, row r0 + (l % 16) / 2
     const int kg = lane >> 4, s16 = lane & 15;
-    const int rsub = s16 >> 1, ahalf = 8 * (s16 & 1);
+    const int rsub = s16 >> 1, ahalf = 8 * (s16 & 1), hb = s16 >> 3;
     uint32_t bmask[4];
+    int shy[4], shz[4];  // 8 - bp and 16 - bp, bp = 2c + hb the bit that column n keeps
 #pragma unroll
-    for (int c = 0; c < 4; ++c) bmask[c] = 0x01010101u << (2 * c + (s16 >> 3));
-    const uint32_t neg7 = (s16 >> 3) ? 0xFFFFFFFFu : 0u;  // lanes whose c = 3 column keeps bit 7
+    for (int c = 0; c < 4; ++c) {
+      bmask[c] = 0x01010101u << (2 * c + hb);
+      shy[c] = 8 - 2 * c - hb;
+      shz[c] = 16 - 2 * c - hb;
+    }
+    const uint32_t neg7 = hb ? 0xFFFFFFFFu : 0u;  // lanes whose c = 3 column keeps bit 7
     const i32x4 ones4 = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
     const long ones2 = 0x0101010101010101l;
     const i32x4 zero4 = {0, 0, 0, 0};
 
-    // A records of block blk into buffer buf
-    auto build = [&](int b3, int blk, int buf, const float (&fqe)[NPASS][2]) {
-      const uint16_t* scb = &sm.sc[b3][0][0] + blk;
+    // fp16 scale of block b (0..3) of the wavefront's four, from a pass's 8 bytes
+    auto scale_of = [](const u32x2& v, int b) {
+      const uint32_t w = b < 2 ? v.x : v.y;
+      return __builtin_bit_cast(_Float16, (uint16_t)((b & 1) ? (w >> 16) : w));
+    };
+    // A records of the wavefront's block b into buffer buf
+    auto build = [&](int b, int buf, const float (&fqe)[NPASS][2], const u32x2 (&scl)[NPASS]) {
       uint8_t* rec = &sm.atab[wave][buf][prow][8 * ppair];
 #pragma unroll
       for (int m = 0; m < NPASS; ++m) {
-        const float sv = half_bits_to_f32(scb[soff[m]]);
-        const uint32_t x0 = (uint32_t)__builtin_fmaf(fqe[m][0], sv, DIGIT_BIAS) ^ 0x808080u;
-        const uint32_t x1 = (uint32_t)__builtin_fmaf(fqe[m][1], sv, DIGIT_BIAS) ^ 0x808080u;
-        *reinterpret_cast<uint2*>(rec + m * RPP * (16 * HG)) = make_uint2(x0, x1);
+        const _Float16 sv = scale_of(scl[m], b);
+        *reinterpret_cast<uint2*>(rec + m * RPP * (16 * HG)) =
+            make_uint2(x_digits(fqe[m][0], sv), x_digits(fqe[m][1], sv));
       }
     };
     // the same for a step where some (head, block) has a frame of its own
-    auto build_own = [&](int par, int b3, int blk, int buf, const float (&fqe)[NPASS][2],
-                         const int (&exh2)[2]) {
+    auto build_own = [&](int par, int wb, int b, int buf, const float (&fqe)[NPASS][2],
+                         const u32x2 (&scl)[NPASS], const int (&exh2)[2]) {
       float g[2];
 #pragma unroll
       for (int x = 0; x < 2; ++x) {
         const int h = 2 * ppair + x;
-        g[x] = h < G ? ldexpf(1.f, sm.ex[par][h][blk] - exh2[x]) : 0.f;
+        g[x] = h < G ? ldexpf(1.f, sm.ex[par][h][wb + b] - exh2[x]) : 0.f;
       }
-      const uint16_t* scb = &sm.sc[b3][0][0] + blk;
       uint8_t* rec = &sm.atab[wave][buf][prow][8 * ppair];
 #pragma unroll
       for (int m = 0; m < NPASS; ++m) {
-        const float sv = half_bits_to_f32(scb[soff[m]]);
-        const uint32_t x0 = (uint32_t)__builtin_fmaf(fqe[m][0] * g[0], sv, DIGIT_BIAS) ^ 0x808080u;
-        const uint32_t x1 = (uint32_t)__builtin_fmaf(fqe[m][1] * g[1], sv, DIGIT_BIAS) ^ 0x808080u;
-        *reinterpret_cast<uint2*>(rec + m * RPP * (16 * HG)) = make_uint2(x0, x1);
+        const _Float16 sv = scale_of(scl[m], b);
+        *reinterpret_cast<uint2*>(rec + m * RPP * (16 * HG)) =
+            make_uint2(x_digits(fqe[m][0] * g[0], sv), x_digits(fqe[m][1] * g[1], sv));
       }
     };
-    // digit sums of block blk (planes pl, A records of buffer buf)
-    auto contract = [&](const uint8_t* pl, int blk, int buf, i32x4 (&acc)[HG][4], i32x4 (&accc)[HG]) {
+    // operands of block blk (planes pl, A records of buffer buf), read from LDS
+    // ahead of their products
+    struct Ops {
+      i32x4 b[N64 ? N64 : 1];
+      i32x4 a[N64 ? N64 : 1][HG];
+      i32x2 b32;
+      i32x2 a32[HG];
+    };
+    auto fetch = [&](const uint8_t* pl, int blk, int buf, Ops& o) {
       const uint8_t* at = &sm.atab[wave][buf][0][0];
 #pragma unroll
       for (int kp = 0; kp < N64; ++kp) {
         const int r0 = 64 * kp + 16 * kg + rsub;
         const i32x2 b0 = tr8(pl + r0 * PSTRIDE + 8 * blk);
         const i32x2 b1 = tr8(pl + (r0 + 8) * PSTRIDE + 8 * blk);
-        const i32x4 bv = {b0.x, b0.y, b1.x, b1.y};
+        o.b[kp] = i32x4{b0.x, b0.y, b1.x, b1.y};
 #pragma unroll
         for (int hg = 0; hg < HG; ++hg) {
           const i32x2 a0 = tr8(at + r0 * (16 * HG) + 16 * hg + ahalf);
           const i32x2 a1 = tr8(at + (r0 + 8) * (16 * HG) + 16 * hg + ahalf);
-          const i32x4 av = {a0.x, a0.y, a1.x, a1.y};
-#pragma unroll
-          for (int c = 0; c < 4; ++c)
-            acc[hg][c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bv & (int)bmask[c],
-                                                               kp ? acc[hg][c] : zero4, 0, 0, 0);
-          accc[hg] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, ones4, kp ? accc[hg] : zero4, 0, 0, 0);
+          o.a[kp][hg] = i32x4{a0.x, a0.y, a1.x, a1.y};
         }
       }
       if constexpr (HAS32) {
         const int r0 = 64 * N64 + 8 * kg + rsub;
-        const i32x2 b0 = tr8(pl + r0 * PSTRIDE + 8 * blk);
+        o.b32 = tr8(pl + r0 * PSTRIDE + 8 * blk);
+#pragma unroll
+        for (int hg = 0; hg < HG; ++hg) o.a32[hg] = tr8(at + r0 * (16 * HG) + 16 * hg + ahalf);
+      }
+    };
+    // digit sums of a block from its operands
+    auto contract = [&](const Ops& o, i32x4 (&acc)[HG][4], i32x4 (&accc)[HG]) {
+#pragma unroll
+      for (int kp = 0; kp < N64; ++kp) {
 #pragma unroll
         for (int hg = 0; hg < HG; ++hg) {
-          const long av = __builtin_bit_cast(long, tr8(at + r0 * (16 * HG) + 16 * hg + ahalf));
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            acc[hg][c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(o.a[kp][hg], o.b[kp] & (int)bmask[c],
+                                                               kp ? acc[hg][c] : zero4, 0, 0, 0);
+          accc[hg] = __builtin_amdgcn_mfma_i32_16x16x64_i8(o.a[kp][hg], ones4, kp ? accc[hg] : zero4, 0, 0, 0);
+        }
+      }
+      if constexpr (HAS32) {
+#pragma unroll
+        for (int hg = 0; hg < HG; ++hg) {
+          const long av = __builtin_bit_cast(long, o.a32[hg]);
 #pragma unroll
           for (int c = 0; c < 4; ++c)
             acc[hg][c] = __builtin_amdgcn_mfma_i32_16x16x32_i8(
-                av, __builtin_bit_cast(long, b0 & (int)bmask[c]), N64 ? acc[hg][c] : zero4, 0, 0, 0);
+                av, __builtin_bit_cast(long, o.b32 & (int)bmask[c]), N64 ? acc[hg][c] : zero4, 0, 0, 0);
           accc[hg] = __builtin_amdgcn_mfma_i32_16x16x32_i8(av, ones2, N64 ? accc[hg] : zero4, 0, 0, 0);
         }
       }
     };
+    // exact score of column c: S = sum_r X_r b_r, T = 2 S - C, s_hat = T 2^-(e+1)
+    auto exact_score = [&](const i32x4& d, int c, uint32_t cc, int eb) {
+      const uint32_t sS = ((uint32_t)d.z << shz[c]) + ((uint32_t)d.y << shy[c]) +
+                          (uint32_t)(d.x >> (2 * c + hb));
+      uint32_t s2 = 2u * sS;
+      if (c == 3) s2 = (s2 ^ neg7) - neg7;  // bit 7 kept as the int8 byte 0x80 = -128
+      return ldexpf((float)(int)(s2 - cc), -(eb + 1));
+    };
     // scores of block blk: lane <-> (head 4 hg + l / 16, column l % 16)
-    auto scores = [&](int par, long long g0, int blk, const i32x4 (&acc)[HG][4], const i32x4 (&accc)[HG]) {
-      const long long tok0 = (g0 + blk) * BLK + 8 * (s16 & 7) + (s16 >> 3);
+    auto scores = [&](int par, long long g0, int blk, const i32x4 (&acc)[HG][4], const i32x4 (&accc)[HG],
+                      const int (&tl)[HG]) {
+      const long long tok0 = (g0 + blk) * BLK + 8 * (s16 & 7) + hb;
 #pragma unroll
       for (int hg = 0; hg < HG; ++hg) {
         const int h = 4 * hg + kg;
-        const int hh = h < G ? h : 0;
         const i32x4 dc = accc[hg];
         const uint32_t cc = ((uint32_t)dc.z << 16) + ((uint32_t)dc.y << 8) + (uint32_t)dc.x;  // C
-        const int eb = sm.ex[par][hh][blk];
-        float thr = 0.f;
-        if constexpr (MODE == SCAN_CAND) thr = sm.thp[par][hh][blk];
+        if constexpr (MODE == SCAN_CAND) {
+          const int tA = (tl[hg] + (int)cc) >> 1;
+          const int tA3 = tA + (int)neg7;  // for c = 3 the high lanes hold -S: ~(-S) = S - 1
+          bool pass[4];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int bp = 2 * c + (s16 >> 3);
-          const i32x4 d = acc[hg][c];
-          // S = sum_r X_r b_r (the digit sums are multiples of 2^bp); T = 2 S - C
-          const uint32_t sS = ((uint32_t)d.z << (16 - bp)) + ((uint32_t)d.y << (8 - bp)) +
-                              (uint32_t)(d.x >> bp);
-          uint32_t s2 = 2u * sS;
-          if (c == 3) s2 = (s2 ^ neg7) - neg7;  // bit 7 kept as the int8 byte 0x80 = -128
-          const float tf = (float)(int)(s2 - cc);
-          const long long tok = tok0 + 2 * c;
-          if constexpr (MODE == SCAN_CAND) {
-            const bool pass = h < G && tf >= thr;
-            if (__ballot(pass) != 0ull && pass) append(tok, h, ldexpf(tf, -(eb + 1)));
-          } else {
-            if (h < G) store(tok, h, ldexpf(tf, -(eb + 1)));
+          for (int c = 0; c < 4; ++c) {
+            const i32x4 d = acc[hg][c];
+            const uint32_t sa = ((uint32_t)d.z << shz[c]) + ((uint32_t)d.y << shy[c]);
+            pass[c] = c == 3 ? (int)(sa ^ neg7) >= tA3 : (int)sa >= tA;
           }
+          if (__ballot(pass[0] || pass[1] || pass[2] || pass[3]) != 0ull) {
+            const int eb = sm.ex[par][h][blk];
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+              if (pass[c]) append(tok0 + 2 * c, h, exact_score(acc[hg][c], c, cc, eb));
+          }
+        } else {
+          const int eb = sm.ex[par][h < G ? h : 0][blk];
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            if (h < G) store(tok0 + 2 * c, h, exact_score(acc[hg][c], c, cc, eb));
         }
       }
     };
 
-    // ---- one step: the wavefront's blocks, building block b + 1 while the
-    // matrix cores work on block b ----
+    // ---- one step: the wavefront's blocks ----
     auto blocks = [&](int i) {
       const int par = i & 1, b3 = i % 3;
       const long long g0 = step_g0(i);
       const int wb = NB * wave;
       const int nblk = step_blocks(i) - wb;  // blocks of this wavefront (uniform)
       if (nblk <= 0) return;
-      // the rows' weights in this step's frames
+      // the rows' weights in this step's frames, and the rows' scales of the
+      // wavefront's four blocks
       float fqe[NPASS][2];
+      u32x2 scl[NPASS];
       int exh2[2];
 #pragma unroll
       for (int x = 0; x < 2; ++x) exh2[x] = 2 * ppair + x < G ? sm.exh[par][2 * ppair + x] : 0;
 #pragma unroll
-      for (int m = 0; m < NPASS; ++m)
+      for (int m = 0; m < NPASS; ++m) {
 #pragma unroll
         for (int x = 0; x < 2; ++x) fqe[m][x] = ldexpf(fq0[m][x], exh2[x]);
+        scl[m] = *reinterpret_cast<const u32x2*>(&sm.sc[b3][0][0] + soffm[m] + wb);
+      }
       bool own_any = false;
 #pragma unroll
       for (int h = 0; h < G; ++h) own_any |= sm.own[par][h] != 0;
       const uint8_t* pl = &sm.planes[par][0];
 
-      if (own_any) build_own(par, b3, wb, 0, fqe, exh2);
-      else build(b3, wb, 0, fqe);
+      auto bld = [&](int b, int buf) {
+        if (own_any) build_own(par, wb, b, buf, fqe, scl, exh2);
+        else build(b, buf, fqe, scl);
+      };
+      // the candidate thresholds of the four blocks for the lane's heads
+      int4 tl4[HG];
+#pragma unroll
+      for (int hg = 0; hg < HG; ++hg) {
+        if constexpr (MODE == SCAN_CAND) tl4[hg] = *reinterpret_cast<const int4*>(&sm.tlo[par][4 * hg + kg][wb]);
+        else tl4[hg] = int4{0, 0, 0, 0};
+      }
+      auto tl_of = [&](int b, int (&tl)[HG]) {
+#pragma unroll
+        for (int hg = 0; hg < HG; ++hg) tl[hg] = b == 0 ? tl4[hg].x : b == 1 ? tl4[hg].y : b == 2 ? tl4[hg].z : tl4[hg].w;
+      };
+      // per block b: score b, then read the operands of b + 1 and issue its
+      // products, then write the digits of b + 2.  A transposing read returns
+      // into its registers asynchronously, so the operands are only replaced
+      // once the products that read them have completed (the scores of b
+      // waited for them).
+      i32x4 acc[HG][4];
+      i32x4 accc[HG];
+      Ops ops;
+      bld(0, 0);
+      fetch(pl, wb, 0, ops);
+      contract(ops, acc, accc);
+      if (nblk > 1) bld(1, 1);
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
         if (b >= nblk) break;
-        i32x4 acc[HG][4];
-        i32x4 accc[HG];
-        contract(pl, wb + b, b & 1, acc, accc);
+        int tl[HG];
+        tl_of(b, tl);
+        scores(par, g0, wb + b, acc, accc, tl);
         if (b + 1 < nblk) {
-          if (own_any) build_own(par, b3, wb + b + 1, (b + 1) & 1, fqe, exh2);
-          else build(b3, wb + b + 1, (b + 1) & 1, fqe);
+          fetch(pl, wb + b + 1, (b + 1) & 1, ops);
+          contract(ops, acc, accc);
         }
-        scores(par, g0, wb + b, acc, accc);
+        if (b + 2 < nblk) bld(b + 2, b & 1);
       }
     };
 
-    // ---- prologue: loads of steps 0 and 1, scales and frames of step 0 ----
+    // ---- prologue: loads of steps 0 and 1, scales and frames of step 0; the
+    // loads are issued in the loop's order (planes of i, scales of i + 1) ----
     constexpr std::integral_constant<int, 0> P0{};
     constexpr std::integral_constant<int, 1> P1{};
-    issue_planes(0, P0);
-    issue_planes(1, P1);
     issue_scales(0, P0);
+    issue_planes(0, P0);
     issue_scales(1, P1);
+    issue_planes(1, P1);
     write_scales(0, P0);
     issue_scales(2, P0);
     __syncthreads();
     compute_frame(0);
 
-    // ---- steps (two per trip, so that the prefetch registers are static) ----
+    // ---- steps, two per trip so that the prefetch registers are static; an
+    // odd count ends with an empty step (its blocks() returns at once), so that
+    // every trip issues the same loads and the compiler waits for the oldest
+    // step's loads alone ----
     auto step = [&](int i, auto P, auto Q) {  // P = i % 2, Q = (i + 1) % 2
       write_planes(i, P);
       if (i + 1 < nsteps) write_scales(i + 1, Q);
@@ -560,7 +695,7 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : 2) void scan_fast_kernel
     };
     for (int i = 0; i < nsteps; i += 2) {
       step(i, P0, P1);
-      if (i + 1 < nsteps) step(i + 1, P1, P0);
+      step(i + 1, P1, P0);
     }
   };
   switch (rpt) {
@@ -607,9 +742,15 @@ hipError_t dispatch_fast(const ScanArgs& a, hipStream_t st) {
 
 // rows >= 0: every unit reads that many rows, one kernel; rows < 0: both,
 // the wide one with fewer, larger workgroups (its workgroups of fast units
-// only read the depths and leave)
+// only read the depths and leave).  Capacities past FAST_MAX_CAP take the wide
+// kernel for every unit.
 template <int MODE>
 hipError_t dispatch(const ScanArgs& a, int rows, hipStream_t st) {
+  if (a.g.cap > FAST_MAX_CAP) {
+    ScanArgs w = a;
+    w.all_rows = 1;
+    return launch_scan_wide(w, MODE, 0, st);
+  }
   if (rows >= 0 && rows <= SCAN_FAST_ROWS) return dispatch_fast<MODE>(a, st);
   if (rows > SCAN_FAST_ROWS) return launch_scan_wide(a, MODE, 0, st);
   const hipError_t e = dispatch_fast<MODE>(a, st);

@@ -48,10 +48,12 @@ struct ScanArgs {
   int32_t* __restrict__ cand_count;       // CAND: [unit][G][regions]
   float* __restrict__ cand_val;           // CAND: [unit][G][regions][CAND_SLOTS]
   int32_t* __restrict__ cand_idx;         // CAND: [unit][G][regions][CAND_SLOTS]
+  int all_rows;                           // wide kernel: take every unit, whatever it reads
 };
 
-// the wide kernel (units reading more than SCAN_FAST_ROWS rows); span = blocks
-// per workgroup (0: the standard scan_wg_blocks / SAMPLE_GROUP)
+// the wide kernel (units reading more than SCAN_FAST_ROWS rows, or every unit
+// with all_rows); span = blocks per workgroup (0: the standard scan_wg_blocks /
+// SAMPLE_GROUP)
 hipError_t launch_scan_wide(const ScanArgs& a, int mode, int span, hipStream_t st);
 
 __device__ __forceinline__ float wave_max(float v) {

@@ -171,7 +171,7 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : 2) void scan_wide_kernel
   }
   const int R = sm.scan_buf[D - 1] & 0xFFFF;
   const int CR = sm.scan_buf[D - 1] >> 16;  // read channels
-  if (R <= SCAN_FAST_ROWS) return;           // the fast kernel's unit (uniform)
+  if (!a.all_rows && R <= SCAN_FAST_ROWS) return;  // the fast kernel's unit (uniform)
   if (tid < D && tj > 0) {
     const int r0 = (sm.scan_buf[tid] & 0xFFFF) - tj;
     const int c = (sm.scan_buf[tid] >> 16) - 1;

@@ -16,11 +16,12 @@
 //   tokens of the whole range are expected at or above it (plus 8 for the
 //   sampling noise of small r);
 // * cand_select_kernel: per (unit, head), the exact top (k - 4 - W) of the
-//   candidates (every token at or above the threshold, so the k - 4 - W
-//   largest of the whole range are among them whenever there are at least
-//   that many), by a bitonic sort of (score key, complemented index) pairs.
-//   A head with too few candidates, or more than the buffer holds, flags its
-//   unit for the full scan and radix select.
+//   candidates (every token at or above the threshold, and possibly a few just
+//   below it, so the k - 4 - W largest of the whole range are among them
+//   whenever at least that many are at or above it), by a bitonic sort of
+//   (score key, complemented index) pairs.  A head with too few candidates at
+//   or above the threshold, or more than the buffer holds, flags its unit for
+//   the full scan and radix select.
 #include <limits.h>
 
 #include "bpk_internal.h"
@@ -247,7 +248,7 @@ __global__ __launch_bounds__(TK_THREADS) void threshold_kernel(ThreshArgs a) {
 struct CandSmem {
   uint64_t key[CAND_CAP];
   int32_t buf[BPK_MAX_K];
-  int total, over, fill;
+  int total, over, fill, ge;
 };
 
 struct CandArgs {
@@ -282,6 +283,7 @@ __global__ __launch_bounds__(TK_THREADS) void cand_select_kernel(CandArgs a) {
       sm.total = 0;
       sm.over = 0;
       sm.fill = 0;
+      sm.ge = 0;
     }
     __syncthreads();
     int tot = 0, over = 0;
@@ -298,15 +300,27 @@ __global__ __launch_bounds__(TK_THREADS) void cand_select_kernel(CandArgs a) {
       if (tid == 0) a.cb.flag[u] = 1;
       return;
     }
-    // (score key, complemented index) in descending order = score down, index up
+    // (score key, complemented index) in descending order = score down, index
+    // up; the scan's test may also pass tokens a little below the threshold,
+    // so only those at or above it count towards want
+    const uint32_t tkey = a.cb.thresh[uh];
     const float* v = a.cb.val + uh * a.cb.regions * CAND_SLOTS;
     const int32_t* ix = a.cb.idx + uh * a.cb.regions * CAND_SLOTS;
+    int ge = 0;
     for (long long e = tid; e < R * CAND_SLOTS; e += TK_THREADS) {
       const long long x = e / CAND_SLOTS;
       if ((int)(e % CAND_SLOTS) < cnt[x]) {
         const int pos = atomicAdd(&sm.fill, 1);
-        sm.key[pos] = ((uint64_t)order_key(v[e]) << 32) | (uint32_t)(~(uint32_t)ix[e]);
+        const uint32_t key = order_key(v[e]);
+        ge += key >= tkey;
+        sm.key[pos] = ((uint64_t)key << 32) | (uint32_t)(~(uint32_t)ix[e]);
       }
+    }
+    if (ge) atomicAdd(&sm.ge, ge);
+    __syncthreads();
+    if (sm.ge < want) {
+      if (tid == 0) a.cb.flag[u] = 1;
+      return;
     }
     int m = 1;
     while (m < total) m <<= 1;
