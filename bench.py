@@ -2,17 +2,19 @@
 """Benchmark of the bit-plane top-k decode path on one MI355X.
 
 A step is one decode step over every (sequence, layer, KV head) unit of the
-workload: depth allocation -> prefix-plane key scan -> per-head top-k ->
-union-gather attention, on a cache resident in HBM (rows, planes, scales).
-Default workload: 36 layers x 8 KV heads x 1 sequence of n = 1,048,576 tokens,
-G = 4 query heads per KV head, plane budget P = 88 (the "92-bit" point),
-k = 512; KV heads 4-7 have Pareto channel variances.
+workload: depth allocation -> prefix-plane key scan (with the fused candidate
+selection: sampled threshold, candidate scan, exact top-k among the
+candidates) -> union-gather attention, on a cache resident in HBM (rows,
+planes, scales).  Default workload: 36 layers x 8 KV heads x 1 sequence of
+n = 1,048,576 tokens, G = 4 query heads per KV head, plane budget P = 88 (the
+"92-bit" point), k = 512; KV heads 4-7 have Pareto channel variances.
 
-The headline value is the key scan's bandwidth: algorithmic bytes of one scan
-launch (the selected planes, P*n/8 bytes per unit, plus the fp16 scales of the
-channels read, 2*C_read*n/64 bytes per unit) over its average duration,
-measured with HIP events on the stream the kernels run on.  Prints one JSON
-line on stdout; progress goes to stderr.
+The headline value is the bandwidth of the decode step's key scan: the
+algorithmic bytes of one scan (the selected planes, P*n/8 bytes per unit, plus
+the fp16 scales of the channels read, 2*C_read*n/64 bytes per unit) over the
+scan kernel's average duration, measured with the library's stage tracing
+(HIP events recorded on the stream the kernels run on, around the scan
+launch).  Prints one JSON line on stdout; progress goes to stderr.
 """
 from __future__ import annotations
 
@@ -41,7 +43,8 @@ def scan_bytes(depth_np, n: int) -> float:
     return float(t.sum()) * nb * 8.0 + float((t > 0).sum()) * nb * 2.0
 
 
-TRAFFIC_SOURCES = ("bit_plane_key_amd/csrc/scan.hip", "bit_plane_key_amd/csrc/bpk_internal.h")
+TRAFFIC_SOURCES = ("bit_plane_key_amd/csrc/scan.hip", "bit_plane_key_amd/csrc/scan_common.h",
+                   "bit_plane_key_amd/csrc/bpk_internal.h")
 
 
 def counted_traffic(config: str, budget: int):
@@ -49,7 +52,7 @@ def counted_traffic(config: str, budget: int):
     workload, or None when there is none or the scan's source has changed
     since the counters were taken."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", f"scan_kernel_{config}_P{budget}_hbm_bytes.md")
+    path = os.path.join(ROOT, "profiles", f"scan_cand_kernel_{config}_P{budget}_hbm_bytes.md")
     if not os.path.exists(path):
         return None
     fields = {}
@@ -160,24 +163,31 @@ def main() -> int:
     ms_step = time_launches(step, args.steps)
     log(f"decode step: {ms_step * 1e3:.1f} us")
 
-    # per-stage timing with the standalone entry points (same kernels, same stream)
+    # the same steps again with stage tracing: HIP events around each stage on
+    # the decode step's stream
+    bpk.trace_enable(True)
+    try:
+        for _ in range(args.steps):
+            step()
+        stage_ms, calls = bpk.trace_read()
+    finally:
+        bpk.trace_enable(False)
+    stage_ms = {name: v / calls for name, v in stage_ms.items()}
+    ms_scan = stage_ms["scan"]
+    log("stages (us): " + " ".join(f"{n} {v * 1e3:.1f}" for n, v in stage_ms.items()))
+
+    # the standalone full scan (scan_scores writes every score: same reads,
+    # plus 16 bytes of scores per token)
     del ws
     depth, qb = bpk.alloc_depth(cache, q, 0, L, budget)
     scores = torch.empty((cfg.seqs, L, cfg.heads, cfg.group, cfg.capacity), dtype=torch.float32,
                          device="cuda")
     bpk.scan_scores(cache, qb, depth, 0, L, scores=scores)
-    idx = bpk.select_topk(cache, scores, 0, L, k)
     torch.cuda.synchronize()
-    ms_alloc = time_launches(lambda: bpk.alloc_depth(cache, q, 0, L, budget, depth, qb), args.steps)
-    ms_scan = time_launches(lambda: bpk.scan_scores(cache, qb, depth, 0, L, scores=scores),
+    ms_full = time_launches(lambda: bpk.scan_scores(cache, qb, depth, 0, L, scores=scores),
                             args.steps)
-    ms_select = time_launches(lambda: bpk.select_topk(cache, scores, 0, L, k, idx=idx), args.steps)
-    att_ws = torch.empty(bpk.workspace_bytes(cache, bpk.BPK_OP_ATTEND, 0, L, k),
-                         dtype=torch.uint8, device="cuda")
-    ms_attend = time_launches(lambda: bpk.sparse_attend(cache, q, idx, 0, L, k, scale, out=out,
-                                                        ws=att_ws), args.steps)
-    log(f"stages (us): alloc {ms_alloc*1e3:.1f} scan {ms_scan*1e3:.1f} "
-        f"select {ms_select*1e3:.1f} attend {ms_attend*1e3:.1f}")
+    del scores
+    log(f"standalone full scan: {ms_full * 1e3:.1f} us")
 
     # the practical streaming ceiling: a plain device copy of 2 GiB (read + write),
     # also the known-size kernel the HBM byte counters are scaled by
@@ -207,7 +217,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "i8",
         "data": "synthetic",
         "config": {
             "workload": (f"{cfg.name}: {cfg.seqs} seq x {cfg.layers} layers x {cfg.heads} KV "
@@ -221,13 +231,14 @@ def main() -> int:
             "unit": "GB/s",
             "frac": round(scan_gbs / HBM_PEAK_GBS, 4),
             "traffic": counted_traffic(cfg.name, budget),
-            "kernel": "scan_kernel",
+            "kernel": "scan_fast_kernel<4, 2, true> (the decode step's candidate scan)",
             "bytes_per_launch": sbytes,
             "avg_launch_us": round(ms_scan * 1e3, 2),
         },
         "decode_step_us": round(ms_step * 1e3, 1),
-        "stage_us": {"alloc": round(ms_alloc * 1e3, 1), "scan": round(ms_scan * 1e3, 1),
-                     "select": round(ms_select * 1e3, 1), "attend": round(ms_attend * 1e3, 1)},
+        "stage_us": {name: round(v * 1e3, 1) for name, v in stage_ms.items()},
+        "full_scan_us": round(ms_full * 1e3, 1),
+        "full_scan_gbs": round(sbytes / (ms_full * 1e-3) / 1e9, 2),
         "keys_per_s": round(keys_per_s, 0),
         "copy_gbs": round(copy_gbs, 1),
         "scan_bits_per_token_mean": round(float(np.mean(bits)), 2),

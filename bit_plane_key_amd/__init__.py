@@ -13,6 +13,7 @@ from ._lib import (  # noqa: F401
     HEAD_DIM,
     LIB_PATH,
     PLANES,
+    STAGES,
     BpkError,
     Cache,
     alloc_depth,
@@ -22,5 +23,7 @@ from ._lib import (  # noqa: F401
     scan_scores,
     select_topk,
     sparse_attend,
+    trace_enable,
+    trace_read,
     workspace_bytes,
 )

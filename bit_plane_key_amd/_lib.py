@@ -24,7 +24,9 @@ BPK_OP_SELECT, BPK_OP_ATTEND, BPK_OP_DECODE = 3, 4, 5
 HEAD_DIM, BLOCK, PLANES = 128, 64, 4
 
 EXPORTS = ("bpk_encode_append", "bpk_alloc_depth", "bpk_scan_scores", "bpk_select_topk",
-           "bpk_sparse_attend", "bpk_decode_step", "bpk_workspace_bytes", "bpk_last_error")
+           "bpk_sparse_attend", "bpk_decode_step", "bpk_workspace_bytes", "bpk_last_error",
+           "bpk_trace_enable", "bpk_trace_read")
+STAGES = ("alloc", "sample", "threshold", "scan", "select", "fallback", "attend")
 
 
 class BpkError(RuntimeError):
@@ -68,6 +70,8 @@ def _load() -> ctypes.CDLL:
         "bpk_decode_step": (ctypes.c_int, [C, P, I32, I32, I32, I32, F, P, P, P, P, SZ, P]),
         "bpk_workspace_bytes": (ctypes.c_size_t, [C, I32, I32, I32, I32]),
         "bpk_last_error": (ctypes.c_char_p, []),
+        "bpk_trace_enable": (ctypes.c_int, [I32]),
+        "bpk_trace_read": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I64), I32]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -254,3 +258,17 @@ def decode_step(cache: Cache, q: torch.Tensor, l0: int, l1: int, budget: int, k:
                                float(softmax_scale), out.data_ptr(), _ptr(depth_out),
                                _ptr(idx_out), ws.data_ptr(), ws.numel(), _stream(stream)))
     return out
+
+
+def trace_enable(on: bool = True) -> None:
+    """Turn stage tracing of decode_step on or off for the calling thread."""
+    _check(LIB.bpk_trace_enable(1 if on else 0))
+
+
+def trace_read(reset: bool = True) -> tuple[dict, int]:
+    """Summed milliseconds per decode_step stage over the traced calls, and
+    the number of calls (waits for the recorded events)."""
+    ms = (ctypes.c_double * len(STAGES))()
+    calls = ctypes.c_int64(0)
+    _check(LIB.bpk_trace_read(ms, ctypes.byref(calls), 1 if reset else 0))
+    return {name: ms[i] for i, name in enumerate(STAGES)}, int(calls.value)

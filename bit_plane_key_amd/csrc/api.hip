@@ -5,6 +5,7 @@
 #include <stdio.h>
 
 #include <string>
+#include <vector>
 
 #include "bpk_internal.h"
 
@@ -28,6 +29,54 @@ int hip_status(hipError_t e, const char* what) {
 }
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// ---- stage tracing: per thread, event pairs around the stages of
+// decode_step, read back and summed by bpk_trace_read ----
+struct TraceRecord {
+  int stage;
+  hipEvent_t start, stop;
+};
+struct TraceState {
+  bool on = false;
+  std::vector<hipEvent_t> pool;  // events created so far, reused after a reset
+  size_t used = 0;
+  std::vector<TraceRecord> records;
+  long long calls = 0;
+  ~TraceState() {
+    for (hipEvent_t e : pool) (void)hipEventDestroy(e);
+  }
+};
+thread_local TraceState g_trace;
+
+hipEvent_t trace_event() {
+  if (g_trace.used == g_trace.pool.size()) {
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    g_trace.pool.push_back(e);
+  }
+  return g_trace.pool[g_trace.used++];
+}
+
+// Records the events around one stage when tracing is on; a failing event
+// call turns tracing off for the rest of the call (results are unaffected).
+class StageTimer {
+ public:
+  StageTimer(int stage, hipStream_t st) : st_(st) {
+    if (!g_trace.on) return;
+    rec_.stage = stage;
+    rec_.start = trace_event();
+    rec_.stop = trace_event();
+    if (rec_.start && rec_.stop && hipEventRecord(rec_.start, st_) == hipSuccess) active_ = true;
+  }
+  ~StageTimer() {
+    if (active_ && hipEventRecord(rec_.stop, st_) == hipSuccess) g_trace.records.push_back(rec_);
+  }
+
+ private:
+  hipStream_t st_;
+  TraceRecord rec_{};
+  bool active_ = false;
+};
 
 // Checks shared by every entry point; fills the geometry of layers [l0, l1).
 int check_cache(const bpk_cache_t* c, int l0, int l1, bpk::Geom* g) {
@@ -239,8 +288,12 @@ int bpk_decode_step(const bpk_cache_t* c, const uint16_t* q, int32_t l0, int32_t
   hipStream_t st = static_cast<hipStream_t>(stream);
   // alloc_depth hands out exactly min(P, 4D) planes per unit
   const int rows = budget_planes < 4 * bpk::D ? budget_planes : 4 * bpk::D;
-  rc = hip_status(bpk::launch_alloc(g, q, c->chan_var, c->rot, budget_planes, depth, q_basis, st),
-                  "decode_step/alloc");
+  if (g_trace.on) ++g_trace.calls;
+  {
+    StageTimer t(BPK_STAGE_ALLOC, st);
+    rc = hip_status(bpk::launch_alloc(g, q, c->chan_var, c->rot, budget_planes, depth, q_basis, st),
+                    "decode_step/alloc");
+  }
   if (rc) return rc;
   if (k <= bpk::FUSED_MAX_K) {
     // sampled threshold -> scan keeping candidates -> exact top-k among them;
@@ -255,33 +308,86 @@ int bpk_decode_step(const bpk_cache_t* c, const uint16_t* q, int32_t l0, int32_t
     cb.val = reinterpret_cast<float*>(base + w.cval);
     cb.idx = reinterpret_cast<int32_t*>(base + w.cidx);
     cb.flag = reinterpret_cast<int32_t*>(base + w.flag);
-    rc = hip_status(bpk::launch_scan_sample(g, q_basis, depth, c->planes, c->scales, cb, rows, st),
-                    "decode_step/sample scan");
+    {
+      StageTimer t(BPK_STAGE_SAMPLE, st);
+      rc = hip_status(
+          bpk::launch_scan_sample(g, q_basis, depth, c->planes, c->scales, cb, rows, st),
+          "decode_step/sample scan");
+    }
     if (rc) return rc;
-    rc = hip_status(bpk::launch_threshold(g, k, cb, st), "decode_step/threshold");
+    {
+      StageTimer t(BPK_STAGE_THRESHOLD, st);
+      rc = hip_status(bpk::launch_threshold(g, k, cb, st), "decode_step/threshold");
+    }
     if (rc) return rc;
-    rc = hip_status(bpk::launch_scan_cand(g, q_basis, depth, c->planes, c->scales, k, cb, rows, st),
-                    "decode_step/scan");
+    {
+      StageTimer t(BPK_STAGE_SCAN, st);
+      rc = hip_status(
+          bpk::launch_scan_cand(g, q_basis, depth, c->planes, c->scales, k, cb, rows, st),
+          "decode_step/scan");
+    }
     if (rc) return rc;
-    rc = hip_status(bpk::launch_cand_select(g, k, cb, idx, st), "decode_step/select");
+    {
+      StageTimer t(BPK_STAGE_SELECT, st);
+      rc = hip_status(bpk::launch_cand_select(g, k, cb, idx, st), "decode_step/select");
+    }
     if (rc) return rc;
-    rc = hip_status(bpk::launch_scan_flagged(g, q_basis, depth, c->planes, c->scales, scores,
-                                             cb.flag, rows, st),
-                    "decode_step/fallback scan");
-    if (rc) return rc;
-    rc = hip_status(bpk::launch_topk_flagged(g, scores, k, idx, cb.flag, st),
-                    "decode_step/fallback select");
+    {
+      StageTimer t(BPK_STAGE_FALLBACK, st);
+      rc = hip_status(bpk::launch_scan_flagged(g, q_basis, depth, c->planes, c->scales, scores,
+                                               cb.flag, rows, st),
+                      "decode_step/fallback scan");
+      if (!rc)
+        rc = hip_status(bpk::launch_topk_flagged(g, scores, k, idx, cb.flag, st),
+                        "decode_step/fallback select");
+    }
     if (rc) return rc;
   } else {
-    rc = hip_status(bpk::launch_scan(g, q_basis, depth, c->planes, c->scales, scores, rows, st),
-                    "decode_step/scan");
+    {
+      StageTimer t(BPK_STAGE_SCAN, st);
+      rc = hip_status(bpk::launch_scan(g, q_basis, depth, c->planes, c->scales, scores, rows, st),
+                      "decode_step/scan");
+    }
     if (rc) return rc;
-    rc = hip_status(bpk::launch_topk(g, scores, k, idx, st), "decode_step/select");
+    {
+      StageTimer t(BPK_STAGE_SELECT, st);
+      rc = hip_status(bpk::launch_topk(g, scores, k, idx, st), "decode_step/select");
+    }
     if (rc) return rc;
   }
+  StageTimer t(BPK_STAGE_ATTEND, st);
   return hip_status(bpk::launch_attend(g, c->k_dtype, c->k_rows, c->v_rows, q, idx, k,
                                        softmax_scale, out, base + w.attend, st),
                     "decode_step/attend");
+}
+
+int bpk_trace_enable(int32_t on) {
+  g_trace.on = on != 0;
+  if (!g_trace.on) {
+    g_trace.records.clear();
+    g_trace.used = 0;
+    g_trace.calls = 0;
+  }
+  return BPK_OK;
+}
+
+int bpk_trace_read(double* ms, int64_t* calls, int32_t reset) {
+  if (!ms || !calls) return fail(BPK_EINVAL, "ms and calls must be non-NULL");
+  for (int i = 0; i < BPK_STAGE_COUNT; ++i) ms[i] = 0.0;
+  for (const TraceRecord& r : g_trace.records) {
+    float t = 0.f;
+    int rc = hip_status(hipEventSynchronize(r.stop), "trace_read");
+    if (!rc) rc = hip_status(hipEventElapsedTime(&t, r.start, r.stop), "trace_read");
+    if (rc) return rc;
+    ms[r.stage] += t;
+  }
+  *calls = g_trace.calls;
+  if (reset) {
+    g_trace.records.clear();
+    g_trace.used = 0;
+    g_trace.calls = 0;
+  }
+  return BPK_OK;
 }
 
 }  // extern "C"

@@ -201,6 +201,32 @@ size_t bpk_workspace_bytes(const bpk_cache_t* cache, int32_t op, int32_t l0, int
 /* Message of the calling thread's last failing call ("" if none). */
 const char* bpk_last_error(void);
 
+/* The stages of bpk_decode_step that stage tracing times. */
+enum bpk_stage {
+  BPK_STAGE_ALLOC = 0,     /* depth allocation */
+  BPK_STAGE_SAMPLE = 1,    /* sampled scan (fused selection) */
+  BPK_STAGE_THRESHOLD = 2, /* per-head candidate thresholds (fused selection) */
+  BPK_STAGE_SCAN = 3,      /* the key scan over every complete block */
+  BPK_STAGE_SELECT = 4,    /* top-k (exact, among the candidates when fused) */
+  BPK_STAGE_FALLBACK = 5,  /* full scan and select of flagged units (fused selection) */
+  BPK_STAGE_ATTEND = 6,    /* union-gather attention */
+  BPK_STAGE_COUNT = 7
+};
+
+/*
+ * Stage tracing, a profiling aid that changes no result.  While it is on for
+ * the calling thread, each bpk_decode_step call of that thread records a HIP
+ * event before and after every stage on the call's stream (the stages a call
+ * skips get none).  bpk_trace_read waits for the recorded events, writes
+ * to ms[BPK_STAGE_COUNT] the milliseconds of each stage summed over the
+ * recorded calls and to *calls their number, and with reset != 0 forgets them.
+ * bpk_trace_enable(0) also forgets them.  The events are created by the
+ * library and kept for reuse until the thread ends.
+ * Errors: BPK_EINVAL (NULL ms or calls), BPK_EHIP (an event call failed).
+ */
+int bpk_trace_enable(int32_t on);
+int bpk_trace_read(double* ms, int64_t* calls, int32_t reset);
+
 #ifdef __cplusplus
 }
 #endif

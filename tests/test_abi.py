@@ -129,3 +129,13 @@ def test_product_has_no_cpu_path():
         if f.endswith(".py"):
             src = open(os.path.join(pkg, f)).read()
             assert "oracle" not in src.replace("no CPU", ""), f
+
+
+def test_trace_calls_validate_and_start_empty(lib):
+    """Stage tracing: NULL outputs are rejected, and with nothing recorded a
+    read returns zeros without touching the GPU."""
+    assert lib.LIB.bpk_trace_read(None, None, 0) == -1
+    assert lib.LIB.bpk_trace_enable(1) == 0
+    ms, calls = lib.trace_read()
+    assert calls == 0 and set(ms) == set(lib.STAGES) and all(v == 0.0 for v in ms.values())
+    assert lib.LIB.bpk_trace_enable(0) == 0

@@ -228,6 +228,30 @@ def test_decode_step_matches_single_calls(bpk, c2):
     assert torch.equal(out, out2)
 
 
+def test_stage_trace_times_decode_step(bpk, c2):
+    """Stage tracing records every stage a fused decode step runs and leaves
+    its results unchanged."""
+    b, wl = bpk
+    cfg, cache, q, inps = c2
+    scale = wl.softmax_scale(cfg)
+    idx = torch.empty((1, 1, 8, 4, cfg.k), dtype=torch.int32, device="cuda")
+    out = b.decode_step(cache, q, 0, 1, 88, cfg.k, scale, idx_out=idx)
+    b.trace_enable(True)
+    try:
+        idx2 = torch.empty_like(idx)
+        out2 = b.decode_step(cache, q, 0, 1, 88, cfg.k, scale, idx_out=idx2)
+        out3 = b.decode_step(cache, q, 0, 1, 88, cfg.k, scale)
+        ms, calls = b.trace_read()
+    finally:
+        b.trace_enable(False)
+    torch.cuda.synchronize()
+    assert calls == 2
+    for stage in b.STAGES:
+        assert ms[stage] > 0.0, stage
+    assert torch.equal(idx, idx2) and torch.equal(out, out2) and torch.equal(out, out3)
+    assert b.trace_read() == ({s: 0.0 for s in b.STAGES}, 0)
+
+
 def test_scan_mixed_row_counts(bpk, c2):
     """One scan over units that read up to 128 plane rows and units that read
     more: each unit's scores equal those of a call over that unit's budget."""
