@@ -50,7 +50,7 @@
 // * Wavefront w then takes blocks 4w .. 4w+3 one at a time: it writes the
 //   block's X digits (4 bytes per (row, head)) into its own LDS records and
 //   contracts them with the plane bits on the matrix cores,
-//   v_mfma_i32_16x16x64_i8 (and _16x16x32_i8 for a 32-row remainder).  Both
+//   v_mfma_i32_16x16x64_i8 (a 32-row remainder with zero upper bytes).  Both
 //   operands come from LDS through the transposing read ds_read_b64_tr_b8:
 //   the B bytes are the raw plane words, each byte holding 8 tokens of one
 //   row, and one AND per 4 bytes keeps bit 2c + (n / 8) of column n, so the
@@ -311,7 +311,7 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : 2) void scan_fast_kernel
       }
     }
     uint32_t m = mv.x > mv.y ? mv.x : mv.y;
-    const uint32_t mo = (uint32_t)__shfl_xor((int)m, 1);
+    const uint32_t mo = lane_xor1(m);
     m = mo > m ? mo : m;
     if (svalid) {
       *reinterpret_cast<u32x4*>(&sm.sc[b3][sc_c][8 * sc_h]) = sw[p];
@@ -350,7 +350,7 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : 2) void scan_fast_kernel
         const uint32_t kk = v > 0.f ? (__float_as_uint(v) & 0xFFFFFF00u) | (uint32_t)c : 0u;
         key = kk > key ? kk : key;
       }
-      key = wave_max_u32(key);
+      key = wave_max_u32_dpp(key);
       // an upper bound of the largest |q| 8 smax, and the channel that reaches it
       const float best = key ? __uint_as_float((key & 0xFFFFFF00u) + 0x100u) : 0.f;
       const int cs = (int)(key & 0xFFu);
@@ -469,7 +469,7 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : 2) void scan_fast_kernel
     }
     const uint32_t neg7 = hb ? 0xFFFFFFFFu : 0u;  // lanes whose c = 3 column keeps bit 7
     const i32x4 ones4 = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
-    const long ones2 = 0x0101010101010101l;
+    const i32x4 ones2x = {0x01010101, 0x01010101, 0, 0};
     const i32x4 zero4 = {0, 0, 0, 0};
 
     // fp16 scale of block b (0..3) of the wavefront's four, from a pass's 8 bytes
@@ -548,14 +548,18 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : 2) void scan_fast_kernel
         }
       }
       if constexpr (HAS32) {
+        // the 32-row remainder as a K = 64 product whose upper 8 bytes per lane
+        // are zero (the K = 32 form's result latency is not reliably waited for)
 #pragma unroll
         for (int hg = 0; hg < HG; ++hg) {
-          const long av = __builtin_bit_cast(long, o.a32[hg]);
+          const i32x4 av = {o.a32[hg].x, o.a32[hg].y, 0, 0};
 #pragma unroll
-          for (int c = 0; c < 4; ++c)
-            acc[hg][c] = __builtin_amdgcn_mfma_i32_16x16x32_i8(
-                av, __builtin_bit_cast(long, o.b32 & (int)bmask[c]), N64 ? acc[hg][c] : zero4, 0, 0, 0);
-          accc[hg] = __builtin_amdgcn_mfma_i32_16x16x32_i8(av, ones2, N64 ? accc[hg] : zero4, 0, 0, 0);
+          for (int c = 0; c < 4; ++c) {
+            const i32x2 bm = o.b32 & (int)bmask[c];
+            acc[hg][c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, i32x4{bm.x, bm.y, 0, 0},
+                                                               N64 ? acc[hg][c] : zero4, 0, 0, 0);
+          }
+          accc[hg] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, ones2x, N64 ? accc[hg] : zero4, 0, 0, 0);
         }
       }
     };
@@ -626,10 +630,6 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : 2) void scan_fast_kernel
       for (int h = 0; h < G; ++h) own_any |= sm.own[par][h] != 0;
       const uint8_t* pl = &sm.planes[par][0];
 
-      auto bld = [&](int b, int buf) {
-        if (own_any) build_own(par, wb, b, buf, fqe, scl, exh2);
-        else build(b, buf, fqe, scl);
-      };
       // the candidate thresholds of the four blocks for the lane's heads
       int4 tl4[HG];
 #pragma unroll
@@ -645,26 +645,37 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : 2) void scan_fast_kernel
       // products, then write the digits of b + 2.  A transposing read returns
       // into its registers asynchronously, so the operands are only replaced
       // once the products that read them have completed (the scores of b
-      // waited for them).
-      i32x4 acc[HG][4];
-      i32x4 accc[HG];
-      Ops ops;
-      bld(0, 0);
-      fetch(pl, wb, 0, ops);
-      contract(ops, acc, accc);
-      if (nblk > 1) bld(1, 1);
+      // waited for them).  COMMON: all four blocks present and no block with
+      // a frame of its own (the loop then has no run-time test).
+      auto run = [&](auto COMMON) {
+        constexpr bool common = decltype(COMMON)::value;
+        auto bld = [&](int b, int buf) {
+          if (!common && own_any) build_own(par, wb, b, buf, fqe, scl, exh2);
+          else build(b, buf, fqe, scl);
+        };
+        auto has = [&](int b) { return common ? b < NB : b < nblk; };
+        i32x4 acc[HG][4];
+        i32x4 accc[HG];
+        Ops ops;
+        bld(0, 0);
+        fetch(pl, wb, 0, ops);
+        contract(ops, acc, accc);
+        if (has(1)) bld(1, 1);
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        if (b >= nblk) break;
-        int tl[HG];
-        tl_of(b, tl);
-        scores(par, g0, wb + b, acc, accc, tl);
-        if (b + 1 < nblk) {
-          fetch(pl, wb + b + 1, (b + 1) & 1, ops);
-          contract(ops, acc, accc);
+        for (int b = 0; b < NB; ++b) {
+          if (!has(b)) break;
+          int tl[HG];
+          tl_of(b, tl);
+          scores(par, g0, wb + b, acc, accc, tl);
+          if (has(b + 1)) {
+            fetch(pl, wb + b + 1, (b + 1) & 1, ops);
+            contract(ops, acc, accc);
+          }
+          if (has(b + 2)) bld(b + 2, b & 1);
         }
-        if (b + 2 < nblk) bld(b + 2, b & 1);
-      }
+      };
+      if (nblk >= NB && !own_any) run(std::true_type{});
+      else run(std::false_type{});
     };
 
     // ---- prologue: loads of steps 0 and 1, scales and frames of step 0; the

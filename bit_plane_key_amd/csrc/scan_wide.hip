@@ -31,7 +31,7 @@
 //   (coalesced 128-byte reads, issued one task ahead) and builds, per (block,
 //   row), the 16-byte record of the digits of the G heads' X.
 // * Wavefront w contracts blocks 4w .. 4w+3 on the matrix cores with
-//   v_mfma_i32_16x16x64_i8 (and _16x16x32_i8 for a 32-row remainder).  The
+//   v_mfma_i32_16x16x64_i8 (a 32-row remainder with zero upper bytes).  The
 //   A operand (row m = 4h + digit, K = plane rows) and the B operand (K =
 //   plane rows, column = token) both come from LDS through the transposing
 //   read ds_read_b64_tr_b8: the B bytes are the raw plane words, each byte
@@ -364,7 +364,7 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : 2) void scan_wide_kernel
   for (int c = 0; c < 4; ++c) bmask[c] = 0x01010101u << (2 * c + (s16 >> 3));
   const uint32_t neg7 = (s16 >> 3) ? 0xFFFFFFFFu : 0u;  // lanes whose c = 3 column keeps bit 7
   const i32x4 ones4 = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
-  const long ones2 = 0x0101010101010101l;
+  const i32x4 ones2x = {0x01010101, 0x01010101, 0, 0};
 
   i32x4 acc[NB][HG][4];
   i32x4 accc[NB][HG];
@@ -473,17 +473,19 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : 2) void scan_wide_kernel
         if (has32) {
           const int r0 = 64 * n64 + 8 * kg + rsub;
           const i32x2 b0 = tr8(&sm.planes[r0 * PSTRIDE + 8 * blk]);
+          // as a K = 64 product with zero upper bytes (the K = 32 form's result
+          // latency is not reliably waited for)
 #pragma unroll
           for (int hg = 0; hg < HG; ++hg) {
             const i32x2 a0 = tr8(&sm.atab[blk][r0][16 * hg + ahalf]);
-            const long av = __builtin_bit_cast(long, a0);
+            const i32x4 av = {a0.x, a0.y, 0, 0};
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
               const i32x2 m = b0 & (int)bmask[c];
-              acc[b][hg][c] = __builtin_amdgcn_mfma_i32_16x16x32_i8(av, __builtin_bit_cast(long, m),
+              acc[b][hg][c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, i32x4{m.x, m.y, 0, 0},
                                                                      acc[b][hg][c], 0, 0, 0);
             }
-            accc[b][hg] = __builtin_amdgcn_mfma_i32_16x16x32_i8(av, ones2, accc[b][hg], 0, 0, 0);
+            accc[b][hg] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, ones2x, accc[b][hg], 0, 0, 0);
           }
         }
       }
