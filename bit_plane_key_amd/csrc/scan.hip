@@ -68,10 +68,9 @@ namespace {
 
 constexpr int NB = 4;                 // blocks per wavefront per step
 constexpr int GB = SCAN_GB;           // blocks per step
-constexpr int RMAX = SCAN_FAST_ROWS;  // plane rows at most
-constexpr int CMAX = D;               // read channels at most
-constexpr int PSTRIDE = 144;          // LDS bytes per plane row: 16 words + 16 bytes of padding
-constexpr int SCS = 24;               // LDS fp16 slots per read channel: 16 blocks + 8 of padding
+constexpr int PSTRIDE = 136;          // LDS bytes per plane row: 16 words + 8 bytes of padding
+constexpr int SCS = 20;               // LDS fp16 slots per read channel: 16 blocks + 4 of padding
+constexpr int RM_SMALL = 96;          // row capacity of the three-workgroups-per-CU variant
 constexpr long long FAST_MAX_CAP = 1ll << 25;   // one unit's planes fit a 32-bit buffer offset
 constexpr float DIGIT_MAGIC = 12615808.f;       // 2^23 + 0x408080
 constexpr uint32_t OUT_OF_RANGE = 0x80000000u;  // a buffer offset past every unit's planes
@@ -80,22 +79,24 @@ constexpr int RSRC_WORD3 = 0x00020000;          // raw (untyped) buffer, 32-bit 
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-template <int HG>
+// LDS of a workgroup whose unit reads at most RM plane rows (and so at most
+// RM channels)
+template <int HG, int RM>
 struct FastSmem {
   static constexpr int GP = 4 * HG;               // heads, padded to whole MFMA row groups
-  alignas(16) uint8_t planes[2][RMAX * PSTRIDE];  // per step parity: [row][block] words
-  alignas(16) uint8_t atab[4][2][RMAX][16 * HG];  // per wavefront, two blocks: [row] X digits, 4 bytes a head
-  alignas(16) uint16_t sc[3][CMAX][SCS];          // per step mod 3: fp16 scales [read channel][block]
-  float smax[3][CMAX];                            // per step mod 3: largest scale of a read channel
+  alignas(16) uint8_t planes[2][RM * PSTRIDE];    // per step parity: [row][block] words
+  alignas(16) uint8_t atab[4][RM][16 * HG];       // per wavefront: [row] X digits, 4 bytes a head
+  alignas(16) uint16_t sc[3][RM][SCS];            // per step mod 3: fp16 scales [read channel][block]
+  float smax[3][RM];                              // per step mod 3: largest scale of a read channel
   float q[GP][D];                                 // the unit's query heads (0 beyond G)
   int tlo[2][GP][GB];                             // per step parity: candidate test threshold of (head, block)
   int ex[2][GP][GB];                              // per step parity: frame exponent of (head, block)
   int exh[2][GP];                                 // per step parity: frame exponent of the step
   int own[2][GP];                                 // per step parity: a block of the head has its own frame
   int scan_buf[D];                                // plan: prefix sums of (depth, read flag)
-  uint8_t rowc[RMAX];                             // read channel of each plane row
-  uint8_t rowp[RMAX];                             // plane of each plane row
-  uint8_t chj[CMAX];                              // channel of each read channel
+  uint8_t rowc[RM];                               // read channel of each plane row
+  uint8_t rowp[RM];                               // plane of each plane row
+  uint8_t chj[RM];                                // channel of each read channel
   int ccount[GP];                                 // candidates of this workgroup per head
 };
 
@@ -123,10 +124,11 @@ __device__ __forceinline__ int cand_threshold(float theta, int e) {
   return t1 - (1 << 15);
 }
 
-template <int G, int MODE, bool VEC>
-__global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : 2) void scan_fast_kernel(ScanArgs a) {
+template <int G, int MODE, bool VEC, int RM>
+__global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : (RM <= RM_SMALL ? 3 : 2)) void scan_fast_kernel(
+    ScanArgs a) {
   constexpr int HG = (G + 3) / 4;
-  using SM = FastSmem<HG>;
+  using SM = FastSmem<HG, RM>;
   constexpr int GP = SM::GP;
   constexpr int NPAIR = GP / 2;           // head pairs of a row (8-byte record halves)
   constexpr int RPP = 64 / NPAIR;         // rows per builder pass
@@ -204,7 +206,7 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : 2) void scan_fast_kernel
   }
   const int R = sm.scan_buf[D - 1] & 0xFFFF;
   const int CR = sm.scan_buf[D - 1] >> 16;  // read channels
-  if (R > RMAX) return;                      // the wide kernel's unit (uniform)
+  if (R > RM) return;                        // another launch's unit (uniform)
   if (tid < D && tj > 0) {
     const int r0 = (sm.scan_buf[tid] & 0xFFFF) - tj;
     const int c = (sm.scan_buf[tid] >> 16) - 1;
@@ -276,12 +278,11 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : 2) void scan_fast_kernel
     const long long w = (g0_last + 8 * sc_h) < nbcap - 8 ? (g0_last + 8 * sc_h) : nbcap - 8;
     soff_last = (uint32_t)((srow + w - g0_last) * 2);
   }
-  u32x4 sw[2];  // scales of the steps of parity 0 / 1
-  auto issue_scales = [&](int i, auto P) {
-    constexpr int p = decltype(P)::value;
+  u32x4 sw;  // scales of the next step to write
+  auto issue_scales = [&](int i) {
     const auto rs = scale_rsrc(i);
     if constexpr (VEC) {
-      sw[p] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(i >= nsteps - 1 ? soff_last : soff), 0, 0);
+      sw = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(i >= nsteps - 1 ? soff_last : soff), 0, 0);
     } else {
       const long long f = step_first(i);
       uint32_t v[4] = {0u, 0u, 0u, 0u};
@@ -291,30 +292,31 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : 2) void scan_fast_kernel
         const uint32_t o = svalid ? (uint32_t)((srow + w - f) * 2) : OUT_OF_RANGE;
         v[b >> 1] |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, (int)o, 0, 0) << (16 * (b & 1));
       }
-      sw[p] = u32x4{v[0], v[1], v[2], v[3]};
+      sw = u32x4{v[0], v[1], v[2], v[3]};
     }
   };
-  auto write_scales = [&](int i, auto P) {  // scales of step i and their per-channel max
-    constexpr int p = decltype(P)::value;
+  auto write_scales = [&](int i) {  // scales of step i and their per-channel max
     const int b3 = i % 3;
     // fp16 bits of non-negative values order like the values; only the step's blocks count
     u16x2 mv = {0, 0};
     if (step_blocks(i) == GB) {
 #pragma unroll
-      for (int x = 0; x < 4; ++x) mv = __builtin_elementwise_max(mv, __builtin_bit_cast(u16x2, sw[p][x]));
+      for (int x = 0; x < 4; ++x) mv = __builtin_elementwise_max(mv, __builtin_bit_cast(u16x2, sw[x]));
     } else {
       const int nv = step_blocks(i) - 8 * sc_h;
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
         const uint32_t keep = (2 * x < nv ? 0xFFFFu : 0u) | (2 * x + 1 < nv ? 0xFFFF0000u : 0u);
-        mv = __builtin_elementwise_max(mv, __builtin_bit_cast(u16x2, sw[p][x] & keep));
+        mv = __builtin_elementwise_max(mv, __builtin_bit_cast(u16x2, sw[x] & keep));
       }
     }
     uint32_t m = mv.x > mv.y ? mv.x : mv.y;
     const uint32_t mo = lane_xor1(m);
     m = mo > m ? mo : m;
     if (svalid) {
-      *reinterpret_cast<u32x4*>(&sm.sc[b3][sc_c][8 * sc_h]) = sw[p];
+      uint32_t* dst = reinterpret_cast<uint32_t*>(&sm.sc[b3][sc_c][8 * sc_h]);  // 8-byte aligned
+      *reinterpret_cast<uint2*>(dst) = make_uint2(sw.x, sw.y);
+      *reinterpret_cast<uint2*>(dst + 2) = make_uint2(sw.z, sw.w);
       if (sc_h == 0) sm.smax[b3][sc_c] = half_bits_to_f32((uint16_t)m);
     }
   };
@@ -403,15 +405,14 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : 2) void scan_fast_kernel
         poff_last[k] = (uint32_t)((row + w - g0_last) * 8);
       }
     }
-    u32x4 pw[2][PL];  // plane words of the steps of parity 0 / 1
-    auto issue_planes = [&](int i, auto P) {
-      constexpr int p = decltype(P)::value;
+    u32x4 pw[PL];  // plane words of the next step to write
+    auto issue_planes = [&](int i) {
       const auto rs = plane_rsrc(i);
       const bool last = i >= nsteps - 1;
 #pragma unroll
       for (int k = 0; k < PL; ++k) {
         if constexpr (VEC) {
-          pw[p][k] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(last ? poff_last[k] : poff[k]), 0, 0);
+          pw[k] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(last ? poff_last[k] : poff[k]), 0, 0);
         } else {
           // 8-byte aligned rows: two 8-byte loads, each word clamped to the capacity
           const long long f = step_first(i);
@@ -426,16 +427,17 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : 2) void scan_fast_kernel
             }
             wv[x] = __builtin_amdgcn_raw_buffer_load_b64(rs, (int)o, 0, 0);
           }
-          pw[p][k] = u32x4{wv[0].x, wv[0].y, wv[1].x, wv[1].y};
+          pw[k] = u32x4{wv[0].x, wv[0].y, wv[1].x, wv[1].y};
         }
       }
     };
-    auto write_planes = [&](int i, auto P) {
-      constexpr int p = decltype(P)::value;
+    auto write_planes = [&](int i) {  // rows are 8-byte aligned
 #pragma unroll
       for (int k = 0; k < PL; ++k) {
         const int e = tid + k * SCAN_THREADS;
-        *reinterpret_cast<u32x4*>(&sm.planes[i & 1][(e >> 3) * PSTRIDE + 16 * (e & 7)]) = pw[p][k];
+        uint8_t* dst = &sm.planes[i & 1][(e >> 3) * PSTRIDE + 16 * (e & 7)];
+        *reinterpret_cast<uint2*>(dst) = make_uint2(pw[k].x, pw[k].y);
+        *reinterpret_cast<uint2*>(dst + 8) = make_uint2(pw[k].z, pw[k].w);
       }
     };
 
@@ -460,12 +462,11 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : 2) void scan_fast_kernel
     const int kg = lane >> 4, s16 = lane & 15;
     const int rsub = s16 >> 1, ahalf = 8 * (s16 & 1), hb = s16 >> 3;
     uint32_t bmask[4];
-    int shy[4], shz[4];  // 8 - bp and 16 - bp, bp = 2c + hb the bit that column n keeps
+    int shy[4];  // 8 - bp, bp = 2c + hb the bit that column n keeps
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       bmask[c] = 0x01010101u << (2 * c + hb);
       shy[c] = 8 - 2 * c - hb;
-      shz[c] = 16 - 2 * c - hb;
     }
     const uint32_t neg7 = hb ? 0xFFFFFFFFu : 0u;  // lanes whose c = 3 column keeps bit 7
     const i32x4 ones4 = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
@@ -477,9 +478,9 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : 2) void scan_fast_kernel
       const uint32_t w = b < 2 ? v.x : v.y;
       return __builtin_bit_cast(_Float16, (uint16_t)((b & 1) ? (w >> 16) : w));
     };
-    // A records of the wavefront's block b into buffer buf
-    auto build = [&](int b, int buf, const float (&fqe)[NPASS][2], const u32x2 (&scl)[NPASS]) {
-      uint8_t* rec = &sm.atab[wave][buf][prow][8 * ppair];
+    // A records of the wavefront's block b
+    auto build = [&](int b, const float (&fqe)[NPASS][2], const u32x2 (&scl)[NPASS]) {
+      uint8_t* rec = &sm.atab[wave][prow][8 * ppair];
 #pragma unroll
       for (int m = 0; m < NPASS; ++m) {
         const _Float16 sv = scale_of(scl[m], b);
@@ -488,7 +489,7 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : 2) void scan_fast_kernel
       }
     };
     // the same for a step where some (head, block) has a frame of its own
-    auto build_own = [&](int par, int wb, int b, int buf, const float (&fqe)[NPASS][2],
+    auto build_own = [&](int par, int wb, int b, const float (&fqe)[NPASS][2],
                          const u32x2 (&scl)[NPASS], const int (&exh2)[2]) {
       float g[2];
 #pragma unroll
@@ -496,7 +497,7 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : 2) void scan_fast_kernel
         const int h = 2 * ppair + x;
         g[x] = h < G ? ldexpf(1.f, sm.ex[par][h][wb + b] - exh2[x]) : 0.f;
       }
-      uint8_t* rec = &sm.atab[wave][buf][prow][8 * ppair];
+      uint8_t* rec = &sm.atab[wave][prow][8 * ppair];
 #pragma unroll
       for (int m = 0; m < NPASS; ++m) {
         const _Float16 sv = scale_of(scl[m], b);
@@ -504,7 +505,7 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : 2) void scan_fast_kernel
             make_uint2(x_digits(fqe[m][0] * g[0], sv), x_digits(fqe[m][1] * g[1], sv));
       }
     };
-    // operands of block blk (planes pl, A records of buffer buf), read from LDS
+    // operands of block blk (planes pl, the wavefront's A records), read from LDS
     // ahead of their products
     struct Ops {
       i32x4 b[N64 ? N64 : 1];
@@ -512,8 +513,8 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : 2) void scan_fast_kernel
       i32x2 b32;
       i32x2 a32[HG];
     };
-    auto fetch = [&](const uint8_t* pl, int blk, int buf, Ops& o) {
-      const uint8_t* at = &sm.atab[wave][buf][0][0];
+    auto fetch = [&](const uint8_t* pl, int blk, Ops& o) {
+      const uint8_t* at = &sm.atab[wave][0][0];
 #pragma unroll
       for (int kp = 0; kp < N64; ++kp) {
         const int r0 = 64 * kp + 16 * kg + rsub;
@@ -534,6 +535,10 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : 2) void scan_fast_kernel
         for (int hg = 0; hg < HG; ++hg) o.a32[hg] = tr8(at + r0 * (16 * HG) + 16 * hg + ahalf);
       }
     };
+    auto mask4 = [](const i32x4& v, uint32_t m) {
+      const int mi = (int)m;
+      return i32x4{v.x & mi, v.y & mi, v.z & mi, v.w & mi};
+    };
     // digit sums of a block from its operands
     auto contract = [&](const Ops& o, i32x4 (&acc)[HG][4], i32x4 (&accc)[HG]) {
 #pragma unroll
@@ -542,7 +547,7 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : 2) void scan_fast_kernel
         for (int hg = 0; hg < HG; ++hg) {
 #pragma unroll
           for (int c = 0; c < 4; ++c)
-            acc[hg][c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(o.a[kp][hg], o.b[kp] & (int)bmask[c],
+            acc[hg][c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(o.a[kp][hg], mask4(o.b[kp], bmask[c]),
                                                                kp ? acc[hg][c] : zero4, 0, 0, 0);
           accc[hg] = __builtin_amdgcn_mfma_i32_16x16x64_i8(o.a[kp][hg], ones4, kp ? accc[hg] : zero4, 0, 0, 0);
         }
@@ -555,8 +560,8 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : 2) void scan_fast_kernel
           const i32x4 av = {o.a32[hg].x, o.a32[hg].y, 0, 0};
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
-            const i32x2 bm = o.b32 & (int)bmask[c];
-            acc[hg][c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, i32x4{bm.x, bm.y, 0, 0},
+            const int m = (int)bmask[c];
+            acc[hg][c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, i32x4{o.b32.x & m, o.b32.y & m, 0, 0},
                                                                N64 ? acc[hg][c] : zero4, 0, 0, 0);
           }
           accc[hg] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, ones2x, N64 ? accc[hg] : zero4, 0, 0, 0);
@@ -565,8 +570,8 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : 2) void scan_fast_kernel
     };
     // exact score of column c: S = sum_r X_r b_r, T = 2 S - C, s_hat = T 2^-(e+1)
     auto exact_score = [&](const i32x4& d, int c, uint32_t cc, int eb) {
-      const uint32_t sS = ((uint32_t)d.z << shz[c]) + ((uint32_t)d.y << shy[c]) +
-                          (uint32_t)(d.x >> (2 * c + hb));
+      const uint32_t sS = ((((uint32_t)d.z << 8) + (uint32_t)d.y) << shy[c]) +
+                          (uint32_t)(d.x >> (8 - shy[c]));
       uint32_t s2 = 2u * sS;
       if (c == 3) s2 = (s2 ^ neg7) - neg7;  // bit 7 kept as the int8 byte 0x80 = -128
       return ldexpf((float)(int)(s2 - cc), -(eb + 1));
@@ -587,7 +592,7 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : 2) void scan_fast_kernel
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
             const i32x4 d = acc[hg][c];
-            const uint32_t sa = ((uint32_t)d.z << shz[c]) + ((uint32_t)d.y << shy[c]);
+            const uint32_t sa = (((uint32_t)d.z << 8) + (uint32_t)d.y) << shy[c];
             pass[c] = c == 3 ? (int)(sa ^ neg7) >= tA3 : (int)sa >= tA;
           }
           if (__ballot(pass[0] || pass[1] || pass[2] || pass[3]) != 0ull) {
@@ -641,26 +646,28 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : 2) void scan_fast_kernel
 #pragma unroll
         for (int hg = 0; hg < HG; ++hg) tl[hg] = b == 0 ? tl4[hg].x : b == 1 ? tl4[hg].y : b == 2 ? tl4[hg].z : tl4[hg].w;
       };
-      // per block b: score b, then read the operands of b + 1 and issue its
-      // products, then write the digits of b + 2.  A transposing read returns
-      // into its registers asynchronously, so the operands are only replaced
-      // once the products that read them have completed (the scores of b
-      // waited for them).  COMMON: all four blocks present and no block with
-      // a frame of its own (the loop then has no run-time test).
+      // per block b: score b, then read the operands of b + 1 (its digits
+      // were written one block earlier) and issue its products, then write
+      // the digits of b + 2 over those of b + 1 (the reads come first: LDS
+      // operations of a wavefront complete in order).  A transposing read
+      // returns into its registers asynchronously, so the operands are only
+      // replaced once the products that read them have completed (the scores
+      // of b waited for them).  COMMON: all four blocks present and no block
+      // with a frame of its own (the loop then has no run-time test).
       auto run = [&](auto COMMON) {
         constexpr bool common = decltype(COMMON)::value;
-        auto bld = [&](int b, int buf) {
-          if (!common && own_any) build_own(par, wb, b, buf, fqe, scl, exh2);
-          else build(b, buf, fqe, scl);
+        auto bld = [&](int b) {
+          if (!common && own_any) build_own(par, wb, b, fqe, scl, exh2);
+          else build(b, fqe, scl);
         };
         auto has = [&](int b) { return common ? b < NB : b < nblk; };
         i32x4 acc[HG][4];
         i32x4 accc[HG];
         Ops ops;
-        bld(0, 0);
-        fetch(pl, wb, 0, ops);
+        bld(0);
+        fetch(pl, wb, ops);
         contract(ops, acc, accc);
-        if (has(1)) bld(1, 1);
+        if (has(1)) bld(1);
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
           if (!has(b)) break;
@@ -668,58 +675,54 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : 2) void scan_fast_kernel
           tl_of(b, tl);
           scores(par, g0, wb + b, acc, accc, tl);
           if (has(b + 1)) {
-            fetch(pl, wb + b + 1, (b + 1) & 1, ops);
+            fetch(pl, wb + b + 1, ops);
             contract(ops, acc, accc);
           }
-          if (has(b + 2)) bld(b + 2, b & 1);
+          if (has(b + 2)) bld(b + 2);
         }
       };
       if (nblk >= NB && !own_any) run(std::true_type{});
       else run(std::false_type{});
     };
 
-    // ---- prologue: loads of steps 0 and 1, scales and frames of step 0; the
-    // loads are issued in the loop's order (planes of i, scales of i + 1) ----
-    constexpr std::integral_constant<int, 0> P0{};
-    constexpr std::integral_constant<int, 1> P1{};
-    issue_scales(0, P0);
-    issue_planes(0, P0);
-    issue_scales(1, P1);
-    issue_planes(1, P1);
-    write_scales(0, P0);
-    issue_scales(2, P0);
+    // ---- prologue: scales of steps 0 and 1, planes of step 0, frames of
+    // step 0; the loads are issued in the loop's order (planes of i, then
+    // scales of i + 1) ----
+    issue_scales(0);
+    issue_planes(0);
+    write_scales(0);
+    issue_scales(1);
     __syncthreads();
     compute_frame(0);
 
-    // ---- steps, two per trip so that the prefetch registers are static; an
-    // odd count ends with an empty step (its blocks() returns at once), so that
-    // every trip issues the same loads and the compiler waits for the oldest
-    // step's loads alone ----
-    auto step = [&](int i, auto P, auto Q) {  // P = i % 2, Q = (i + 1) % 2
-      write_planes(i, P);
-      if (i + 1 < nsteps) write_scales(i + 1, Q);
+    // ---- steps: the loads of step i + 1 (planes) and i + 2 (scales) are in
+    // flight while step i is computed ----
+    for (int i = 0; i < nsteps; ++i) {
+      write_planes(i);
+      if (i + 1 < nsteps) write_scales(i + 1);
       __syncthreads();  // planes of i, scales of i + 1 and frames of i are in LDS
-      issue_planes(i + 2, P);
-      issue_scales(i + 3, Q);
+      issue_planes(i + 1);
+      issue_scales(i + 2);
       if (i + 1 < nsteps) compute_frame(i + 1);
       blocks(i);
-    };
-    for (int i = 0; i < nsteps; i += 2) {
-      step(i, P0, P1);
-      step(i + 1, P1, P0);
     }
   };
-  switch (rpt) {
+  switch (rpt) {  // rpt <= RM / 32
     case 1: main_loop(std::integral_constant<int, 1>{}); break;
     case 2: main_loop(std::integral_constant<int, 2>{}); break;
     case 3: main_loop(std::integral_constant<int, 3>{}); break;
-    default: main_loop(std::integral_constant<int, 4>{}); break;
+    default:
+      if constexpr (RM > RM_SMALL) main_loop(std::integral_constant<int, 4>{});
+      break;
   }
   store_counts();
 }
 
+// rows: the plane rows every unit reads (-1: not known, any up to
+// SCAN_FAST_ROWS); up to RM_SMALL rows take the variant with the smaller LDS
+// footprint (three workgroups per CU)
 template <int G, int MODE>
-hipError_t launch_fast(const ScanArgs& a0, hipStream_t st) {
+hipError_t launch_fast(const ScanArgs& a0, int rows, hipStream_t st) {
   ScanArgs a = a0;
   long long maxnb = 0;
   for (int s = 0; s < a.g.S; ++s) maxnb = a.g.n[s] / BLK > maxnb ? a.g.n[s] / BLK : maxnb;
@@ -733,20 +736,24 @@ hipError_t launch_fast(const ScanArgs& a0, hipStream_t st) {
     a.wg_blocks = wb;
     grid = dim3((unsigned)((maxnb + wb - 1) / wb), (unsigned)a.g.units());
   }
-  if (a.g.nbcap() % 8 == 0)
-    scan_fast_kernel<G, MODE, true><<<grid, SCAN_THREADS, 0, st>>>(a);
-  else
-    scan_fast_kernel<G, MODE, false><<<grid, SCAN_THREADS, 0, st>>>(a);
+  const bool vec = a.g.nbcap() % 8 == 0;
+  if (rows >= 0 && rows <= RM_SMALL) {
+    if (vec) scan_fast_kernel<G, MODE, true, RM_SMALL><<<grid, SCAN_THREADS, 0, st>>>(a);
+    else scan_fast_kernel<G, MODE, false, RM_SMALL><<<grid, SCAN_THREADS, 0, st>>>(a);
+  } else {
+    if (vec) scan_fast_kernel<G, MODE, true, SCAN_FAST_ROWS><<<grid, SCAN_THREADS, 0, st>>>(a);
+    else scan_fast_kernel<G, MODE, false, SCAN_FAST_ROWS><<<grid, SCAN_THREADS, 0, st>>>(a);
+  }
   return hipGetLastError();
 }
 
 template <int MODE>
-hipError_t dispatch_fast(const ScanArgs& a, hipStream_t st) {
+hipError_t dispatch_fast(const ScanArgs& a, int rows, hipStream_t st) {
   switch (a.g.G) {
-    case 1: return launch_fast<1, MODE>(a, st);
-    case 2: return launch_fast<2, MODE>(a, st);
-    case 4: return launch_fast<4, MODE>(a, st);
-    case 8: return launch_fast<8, MODE>(a, st);
+    case 1: return launch_fast<1, MODE>(a, rows, st);
+    case 2: return launch_fast<2, MODE>(a, rows, st);
+    case 4: return launch_fast<4, MODE>(a, rows, st);
+    case 8: return launch_fast<8, MODE>(a, rows, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -762,9 +769,9 @@ hipError_t dispatch(const ScanArgs& a, int rows, hipStream_t st) {
     w.all_rows = 1;
     return launch_scan_wide(w, MODE, 0, st);
   }
-  if (rows >= 0 && rows <= SCAN_FAST_ROWS) return dispatch_fast<MODE>(a, st);
+  if (rows >= 0 && rows <= SCAN_FAST_ROWS) return dispatch_fast<MODE>(a, rows, st);
   if (rows > SCAN_FAST_ROWS) return launch_scan_wide(a, MODE, 0, st);
-  const hipError_t e = dispatch_fast<MODE>(a, st);
+  const hipError_t e = dispatch_fast<MODE>(a, -1, st);
   if (e != hipSuccess) return e;
   return launch_scan_wide(a, MODE, MODE == SCAN_FULL ? SCAN_WIDE_SPAN : 0, st);
 }
