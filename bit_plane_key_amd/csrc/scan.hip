@@ -93,7 +93,7 @@ struct FastSmem {
   int ex[2][GP][GB];                              // per step parity: frame exponent of (head, block)
   int exh[2][GP];                                 // per step parity: frame exponent of the step
   int own[2][GP];                                 // per step parity: a block of the head has its own frame
-  int scan_buf[D];                                // plan: prefix sums of (depth, read flag)
+  int wsum[2];                                    // plan: (rows, read channels) of channels 0-63, 64-127
   uint8_t rowc[RM];                               // read channel of each plane row
   uint8_t rowp[RM];                               // plane of each plane row
   uint8_t chj[RM];                                // channel of each read channel
@@ -181,13 +181,28 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : (RM <= RM_SMALL ? 3 : 2)
   };
 
   // ---- plan: plane rows channel by channel (j ascending, p ascending) ----
+  // inclusive prefix sums of (depth, read flag) over the channels, held by
+  // wavefronts 0 and 1; the unit's row count comes first so that a unit of
+  // another launch leaves at once
   int tj = 0;
-  if (MODE == SCAN_CAND && tid < GP) sm.ccount[tid] = 0;
   if (tid < D) {
     tj = a.depth[(long long)u * D + tid];
     tj = tj > NP ? NP : tj;
-    sm.scan_buf[tid] = tj | ((tj > 0) << 16);
   }
+  int pre = tid < D ? (tj | ((tj > 0) << 16)) : 0;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(pre, off);
+    if (lane >= off) pre += o;
+  }
+  if (lane == 63 && wave < 2) sm.wsum[wave] = pre;
+  __syncthreads();
+  const int tot = sm.wsum[0] + sm.wsum[1];
+  const int R = tot & 0xFFFF;
+  const int CR = tot >> 16;                  // read channels
+  if (R > RM || R <= a.rows_above) return;   // another launch's unit (uniform)
+  if (wave == 1) pre += sm.wsum[0];
+  if (MODE == SCAN_CAND && tid < GP) sm.ccount[tid] = 0;
   for (int i = tid; i < GP * D; i += SCAN_THREADS) {
     const int h = i / D;
     sm.q[h][i % D] = h < G ? a.q_basis[((long long)u * G + h) * D + i % D] : 0.f;
@@ -196,20 +211,9 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : (RM <= RM_SMALL ? 3 : 2)
     const int h = (tid / GB) % GP;
     if (h >= G) sm.tlo[tid / (GP * GB)][h][tid % GB] = 1 << 30;
   }
-  __syncthreads();
-  for (int off = 1; off < D; off <<= 1) {
-    int v = 0;
-    if (tid < D && tid >= off) v = sm.scan_buf[tid - off];
-    __syncthreads();
-    if (tid < D) sm.scan_buf[tid] += v;
-    __syncthreads();
-  }
-  const int R = sm.scan_buf[D - 1] & 0xFFFF;
-  const int CR = sm.scan_buf[D - 1] >> 16;  // read channels
-  if (R > RM) return;                        // another launch's unit (uniform)
   if (tid < D && tj > 0) {
-    const int r0 = (sm.scan_buf[tid] & 0xFFFF) - tj;
-    const int c = (sm.scan_buf[tid] >> 16) - 1;
+    const int r0 = (pre & 0xFFFF) - tj;
+    const int c = (pre >> 16) - 1;
     sm.chj[c] = (uint8_t)tid;
     for (int p = 0; p < tj; ++p) {
       sm.rowc[r0 + p] = (uint8_t)c;
@@ -720,10 +724,12 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : (RM <= RM_SMALL ? 3 : 2)
 
 // rows: the plane rows every unit reads (-1: not known, any up to
 // SCAN_FAST_ROWS); up to RM_SMALL rows take the variant with the smaller LDS
-// footprint (three workgroups per CU)
+// footprint (three workgroups per CU).  Not known: both variants are launched
+// and each takes its own units.
 template <int G, int MODE>
 hipError_t launch_fast(const ScanArgs& a0, int rows, hipStream_t st) {
   ScanArgs a = a0;
+  a.rows_above = -1;
   long long maxnb = 0;
   for (int s = 0; s < a.g.S; ++s) maxnb = a.g.n[s] / BLK > maxnb ? a.g.n[s] / BLK : maxnb;
   if (maxnb == 0 || a.g.units() == 0) return hipSuccess;
@@ -737,13 +743,14 @@ hipError_t launch_fast(const ScanArgs& a0, int rows, hipStream_t st) {
     grid = dim3((unsigned)((maxnb + wb - 1) / wb), (unsigned)a.g.units());
   }
   const bool vec = a.g.nbcap() % 8 == 0;
-  if (rows >= 0 && rows <= RM_SMALL) {
+  if (rows <= RM_SMALL) {  // known and small, or not known: the small variant first
     if (vec) scan_fast_kernel<G, MODE, true, RM_SMALL><<<grid, SCAN_THREADS, 0, st>>>(a);
     else scan_fast_kernel<G, MODE, false, RM_SMALL><<<grid, SCAN_THREADS, 0, st>>>(a);
-  } else {
-    if (vec) scan_fast_kernel<G, MODE, true, SCAN_FAST_ROWS><<<grid, SCAN_THREADS, 0, st>>>(a);
-    else scan_fast_kernel<G, MODE, false, SCAN_FAST_ROWS><<<grid, SCAN_THREADS, 0, st>>>(a);
+    if (rows >= 0) return hipGetLastError();
+    a.rows_above = RM_SMALL;  // not known: the large variant takes the rest
   }
+  if (vec) scan_fast_kernel<G, MODE, true, SCAN_FAST_ROWS><<<grid, SCAN_THREADS, 0, st>>>(a);
+  else scan_fast_kernel<G, MODE, false, SCAN_FAST_ROWS><<<grid, SCAN_THREADS, 0, st>>>(a);
   return hipGetLastError();
 }
 

@@ -49,6 +49,7 @@ struct ScanArgs {
   float* __restrict__ cand_val;           // CAND: [unit][G][regions][CAND_SLOTS]
   int32_t* __restrict__ cand_idx;         // CAND: [unit][G][regions][CAND_SLOTS]
   int all_rows;                           // wide kernel: take every unit, whatever it reads
+  int rows_above;                         // fast kernel: skip units reading at most this many rows
 };
 
 // the wide kernel (units reading more than SCAN_FAST_ROWS rows, or every unit
