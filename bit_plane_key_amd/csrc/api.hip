@@ -159,7 +159,7 @@ DecodeWs decode_ws(const bpk::Geom& g, int k) {
   w.attend = off;  off += align256(bpk::attend_ws_bytes(g, k));
   w.sample = off;  off += align256(uh * (size_t)w.sample_ld * sizeof(float));
   w.thresh = off;  off += align256(uh * sizeof(uint32_t));
-  w.count = off;   off += align256(uh * (size_t)w.regions * sizeof(int32_t));
+  w.count = off;   off += align256(uh * (size_t)w.regions * bpk::CAND_PARTS * sizeof(int32_t));
   w.cval = off;    off += align256(slots * sizeof(float));
   w.cidx = off;    off += align256(slots * sizeof(int32_t));
   w.flag = off;    off += align256(units * sizeof(int32_t));

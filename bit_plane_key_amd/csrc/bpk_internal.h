@@ -58,7 +58,7 @@ hipError_t launch_topk(const Geom& g, const float* scores, int k, int32_t* idx, 
 
 // ---- decode_step's fused selection ----
 // A sampled scan (the first 64 blocks of every 4096) sets per (unit, query
-// head) a score threshold expected to pass about 3 (k - 4 - W) tokens; the full
+// head) a score threshold expected to pass about 2 (k - 4 - W) tokens; the full
 // scan then keeps only the tokens at or above it, and the exact top-k is taken
 // among those.  Each scan workgroup owns a region of CAND_SLOTS slots per head
 // (no global atomics); a unit whose candidates are too few, overflow a region
@@ -67,6 +67,8 @@ hipError_t launch_topk(const Geom& g, const float* scores, int k, int32_t* idx, 
 constexpr int SAMPLE_STRIDE = 4096;  // blocks from one sampled group to the next
 constexpr int SAMPLE_GROUP = 64;     // blocks per sampled group
 constexpr int CAND_SLOTS = 128;      // candidate slots per (scan workgroup, head)
+constexpr int CAND_PARTS = 4;        // parts of a region, one per scan wavefront, counted apart
+constexpr int CAND_PART_SLOTS = CAND_SLOTS / CAND_PARTS;
 constexpr int CAND_CAP = 4096;       // candidates the exact selection takes per head
 constexpr int FUSED_MAX_K = 1024;    // larger k take the unfused path
 constexpr int SCAN_MIN_WG_BLOCKS = 16;
@@ -77,7 +79,7 @@ struct CandBufs {
   uint32_t* thresh;     // [units][G] order key of the threshold
   int wg_blocks;        // blocks per workgroup of the candidate scan
   long long regions;    // region stride: workgroups per unit the buffers hold
-  int32_t* count;       // [units][G][regions] candidates found by each workgroup
+  int32_t* count;       // [units][G][regions][CAND_PARTS] candidates found per region part
   float* val;           // [units][G][regions][CAND_SLOTS]
   int32_t* idx;         // [units][G][regions][CAND_SLOTS]
   int32_t* flag;        // [units] 1 = redo this unit unfused

@@ -67,6 +67,7 @@ namespace bpk {
 namespace {
 
 constexpr int NB = 4;                 // blocks per wavefront per step
+static_assert(SCAN_THREADS / 64 == CAND_PARTS, "one candidate part per wavefront");
 constexpr int GB = SCAN_GB;           // blocks per step
 constexpr int PSTRIDE = 136;          // LDS bytes per plane row: 16 words + 8 bytes of padding
 constexpr int SCS = 20;               // LDS fp16 slots per read channel: 16 blocks + 4 of padding
@@ -165,7 +166,9 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : (RM <= RM_SMALL ? 3 : 2)
       a.out[uh * a.out_ld + (long long)blockIdx.x * (SAMPLE_GROUP * BLK) + (tok - wb0 * BLK)] = s;
     }
   };
-  auto append = [&](long long tok, int h, float s) {  // CAND, a lane whose test passed
+  // (only where nothing is read) the workgroup's candidates fill each head's
+  // region front to back through an LDS counter
+  auto append = [&](long long tok, int h, float s) {
     if (tok < 4 || tok >= cand_hi) return;
     const int off = atomicAdd(&sm.ccount[h], 1);
     if (off < CAND_SLOTS) {
@@ -176,7 +179,10 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : (RM <= RM_SMALL ? 3 : 2)
   auto store_counts = [&]() {
     if constexpr (MODE == SCAN_CAND) {
       __syncthreads();
-      if (tid < G) a.cand_count[((long long)u * G + tid) * a.regions + blockIdx.x] = sm.ccount[tid];
+      if (tid < G)
+        contiguous_part_counts(
+            a.cand_count + (((long long)u * G + tid) * a.regions + blockIdx.x) * CAND_PARTS,
+            sm.ccount[tid]);
     }
   };
 
@@ -581,8 +587,13 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : (RM <= RM_SMALL ? 3 : 2)
       return ldexpf((float)(int)(s2 - cc), -(eb + 1));
     };
     // scores of block blk: lane <-> (head 4 hg + l / 16, column l % 16)
+    // candidates: wavefront w fills part w of each head's region; wcnt[hg]
+    // counts those of head 4 hg + kg (the same in the 16 lanes of the head)
+    int wcnt[HG];
+#pragma unroll
+    for (int hg = 0; hg < HG; ++hg) wcnt[hg] = 0;
     auto scores = [&](int par, long long g0, int blk, const i32x4 (&acc)[HG][4], const i32x4 (&accc)[HG],
-                      const int (&tl)[HG]) {
+                      const int (&tl)[HG], const int (&exb)[HG]) {
       const long long tok0 = (g0 + blk) * BLK + 8 * (s16 & 7) + hb;
 #pragma unroll
       for (int hg = 0; hg < HG; ++hg) {
@@ -600,16 +611,40 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : (RM <= RM_SMALL ? 3 : 2)
             pass[c] = c == 3 ? (int)(sa ^ neg7) >= tA3 : (int)sa >= tA;
           }
           if (__ballot(pass[0] || pass[1] || pass[2] || pass[3]) != 0ull) {
-            const int eb = sm.ex[par][h][blk];
+            // tokens outside [4, cand_hi) are never candidates: only the unit's
+            // first block and its last ones hold such tokens
+            if ((g0 + blk) == 0 || (g0 + blk + 1) * BLK > cand_hi) {
 #pragma unroll
-            for (int c = 0; c < 4; ++c)
-              if (pass[c]) append(tok0 + 2 * c, h, exact_score(acc[hg][c], c, cc, eb));
+              for (int c = 0; c < 4; ++c) {
+                const long long tok = tok0 + 2 * c;
+                pass[c] = pass[c] && tok >= 4 && tok < cand_hi;
+              }
+            }
+            // slot of a passing (lane, c): the head's passing pairs before it,
+            // c-major, after the wavefront's earlier ones
+            const uint64_t gm = 0xFFFFull << (16 * kg);
+            int before = 0;
+            const long long base = region(h) + wave * CAND_PART_SLOTS;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              const uint64_t mc = __ballot(pass[c]) & gm;
+              if (pass[c]) {
+                const int slot = wcnt[hg] + before +
+                                 (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mc >> 32),
+                                                                __builtin_amdgcn_mbcnt_lo((uint32_t)mc, 0u));
+                if (slot < CAND_PART_SLOTS) {
+                  a.cand_val[base + slot] = exact_score(acc[hg][c], c, cc, exb[hg]);
+                  a.cand_idx[base + slot] = (int32_t)(tok0 + 2 * c);
+                }
+              }
+              before += __popcll(mc);
+            }
+            wcnt[hg] += before;
           }
         } else {
-          const int eb = sm.ex[par][h < G ? h : 0][blk];
 #pragma unroll
           for (int c = 0; c < 4; ++c)
-            if (h < G) store(tok0 + 2 * c, h, exact_score(acc[hg][c], c, cc, eb));
+            if (h < G) store(tok0 + 2 * c, h, exact_score(acc[hg][c], c, cc, exb[hg]));
         }
       }
     };
@@ -646,9 +681,17 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : (RM <= RM_SMALL ? 3 : 2)
         if constexpr (MODE == SCAN_CAND) tl4[hg] = *reinterpret_cast<const int4*>(&sm.tlo[par][4 * hg + kg][wb]);
         else tl4[hg] = int4{0, 0, 0, 0};
       }
-      auto tl_of = [&](int b, int (&tl)[HG]) {
+      // and their frame exponents (heads past G: never used)
+      int4 ex4[HG];
 #pragma unroll
-        for (int hg = 0; hg < HG; ++hg) tl[hg] = b == 0 ? tl4[hg].x : b == 1 ? tl4[hg].y : b == 2 ? tl4[hg].z : tl4[hg].w;
+      for (int hg = 0; hg < HG; ++hg) ex4[hg] = *reinterpret_cast<const int4*>(&sm.ex[par][4 * hg + kg][wb]);
+      auto pick = [](const int4& v, int b) { return b == 0 ? v.x : b == 1 ? v.y : b == 2 ? v.z : v.w; };
+      auto tl_of = [&](int b, int (&tl)[HG], int (&exb)[HG]) {
+#pragma unroll
+        for (int hg = 0; hg < HG; ++hg) {
+          tl[hg] = pick(tl4[hg], b);
+          exb[hg] = pick(ex4[hg], b);
+        }
       };
       // per block b: score b, then read the operands of b + 1 (its digits
       // were written one block earlier) and issue its products, then write
@@ -675,9 +718,9 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : (RM <= RM_SMALL ? 3 : 2)
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
           if (!has(b)) break;
-          int tl[HG];
-          tl_of(b, tl);
-          scores(par, g0, wb + b, acc, accc, tl);
+          int tl[HG], exb[HG];
+          tl_of(b, tl, exb);
+          scores(par, g0, wb + b, acc, accc, tl, exb);
           if (has(b + 1)) {
             fetch(pl, wb + b + 1, ops);
             contract(ops, acc, accc);
@@ -710,6 +753,14 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : (RM <= RM_SMALL ? 3 : 2)
       if (i + 1 < nsteps) compute_frame(i + 1);
       blocks(i);
     }
+    if constexpr (MODE == SCAN_CAND) {
+#pragma unroll
+      for (int hg = 0; hg < HG; ++hg) {
+        const int h = 4 * hg + kg;
+        if (s16 == 0 && h < G)
+          a.cand_count[(((long long)u * G + h) * a.regions + blockIdx.x) * CAND_PARTS + wave] = wcnt[hg];
+      }
+    }
   };
   switch (rpt) {  // rpt <= RM / 32
     case 1: main_loop(std::integral_constant<int, 1>{}); break;
@@ -719,7 +770,6 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : (RM <= RM_SMALL ? 3 : 2)
       if constexpr (RM > RM_SMALL) main_loop(std::integral_constant<int, 4>{});
       break;
   }
-  store_counts();
 }
 
 // rows: the plane rows every unit reads (-1: not known, any up to

@@ -115,6 +115,18 @@ __device__ __forceinline__ float key_to_float(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
+// the per-part counts of a candidate region filled front to back with total
+// candidates (the last part takes any overflow, which the selection flags)
+__device__ __forceinline__ void contiguous_part_counts(int32_t* cnt, int total) {
+#pragma unroll
+  for (int p = 0; p < CAND_PARTS; ++p) {
+    int c = total - p * CAND_PART_SLOTS;
+    c = c < 0 ? 0 : c;
+    if (p + 1 < CAND_PARTS && c > CAND_PART_SLOTS) c = CAND_PART_SLOTS;
+    cnt[p] = c;
+  }
+}
+
 // ds_read_b64_tr_b8: in each 16-lane group, lane i < 8 gets byte i of the 8
 // bytes at the addresses of lanes 0, 2, .., 14, and lane i >= 8 gets byte
 // i - 8 of those of lanes 1, 3, .., 15 (byte j of the result from the j-th

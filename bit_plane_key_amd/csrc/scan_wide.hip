@@ -145,7 +145,10 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : 2) void scan_wide_kernel
   auto store_counts = [&]() {
     if constexpr (MODE == SCAN_CAND) {
       __syncthreads();
-      if (tid < G) a.cand_count[((long long)u * G + tid) * a.regions + blockIdx.x] = sm.ccount[tid];
+      if (tid < G)
+        contiguous_part_counts(
+            a.cand_count + (((long long)u * G + tid) * a.regions + blockIdx.x) * CAND_PARTS,
+            sm.ccount[tid]);
     }
   };
 

@@ -12,7 +12,7 @@
 //
 // decode_step's fused selection adds two kernels on the same machinery:
 // * threshold_kernel: per (unit, head), the r-th largest of the sampled
-//   scores of candidate tokens, with r chosen so that about 3 (k - 4 - W)
+//   scores of candidate tokens, with r chosen so that about 2 (k - 4 - W)
 //   tokens of the whole range are expected at or above it (plus 8 for the
 //   sampling noise of small r);
 // * cand_select_kernel: per (unit, head), the exact top (k - 4 - W) of the
@@ -229,7 +229,7 @@ __global__ __launch_bounds__(TK_THREADS) void threshold_kernel(ThreshArgs a) {
       m += x1 > x0 ? x1 - x0 : 0;
     }
     const long long nc = hi - 4;
-    const long long r = (3 * want * m + nc - 1) / nc + 8;
+    const long long r = (2 * want * m + nc - 1) / nc + 8;
     if (r > m) {
       tkey = 0;  // the sample is too small to cut anything: all are candidates
     } else {
@@ -278,7 +278,7 @@ __global__ __launch_bounds__(TK_THREADS) void cand_select_kernel(CandArgs a) {
   if (want > 0) {
     // the candidate regions of this unit's scan workgroups
     const long long R = (n / BLK + a.cb.wg_blocks - 1) / a.cb.wg_blocks;
-    const int32_t* cnt = a.cb.count + uh * a.cb.regions;
+    const int32_t* cnt = a.cb.count + uh * a.cb.regions * CAND_PARTS;  // [region][part]
     if (tid == 0) {
       sm.total = 0;
       sm.over = 0;
@@ -287,10 +287,10 @@ __global__ __launch_bounds__(TK_THREADS) void cand_select_kernel(CandArgs a) {
     }
     __syncthreads();
     int tot = 0, over = 0;
-    for (long long x = tid; x < R; x += TK_THREADS) {
+    for (long long x = tid; x < R * CAND_PARTS; x += TK_THREADS) {
       const int c = cnt[x];
       tot += c;
-      over |= c > CAND_SLOTS;
+      over |= c > CAND_PART_SLOTS;
     }
     if (tot) atomicAdd(&sm.total, tot);
     if (over) atomicOr(&sm.over, 1);
@@ -308,8 +308,8 @@ __global__ __launch_bounds__(TK_THREADS) void cand_select_kernel(CandArgs a) {
     const int32_t* ix = a.cb.idx + uh * a.cb.regions * CAND_SLOTS;
     int ge = 0;
     for (long long e = tid; e < R * CAND_SLOTS; e += TK_THREADS) {
-      const long long x = e / CAND_SLOTS;
-      if ((int)(e % CAND_SLOTS) < cnt[x]) {
+      const long long x = e / CAND_PART_SLOTS;  // region part
+      if ((int)(e % CAND_PART_SLOTS) < cnt[x]) {
         const int pos = atomicAdd(&sm.fill, 1);
         const uint32_t key = order_key(v[e]);
         ge += key >= tkey;
