@@ -153,8 +153,32 @@ def main() -> int:
     out = torch.empty((cfg.seqs, L, cfg.heads, cfg.group, 128), dtype=torch.float32,
                       device="cuda")
 
-    def step():
-        bpk.decode_step(cache, q, 0, L, budget, k, scale, out=out, ws=ws)
+    appends = cfg.append_steps > 0
+    if appends:
+        # the workload appends one token per sequence before each decode step:
+        # the rows of those tokens are written once here, outside any timing
+        workloads.fill_tokens(cfg, cache, n, cfg.append_steps)
+        if args.warmup + 2 * args.steps > cfg.append_steps:
+            log(f"{cfg.name} holds {cfg.append_steps} appended tokens: use warmup + 2 * steps <= that")
+            return 2
+
+    def step(p=budget):
+        if appends:
+            for s in range(cfg.seqs):
+                bpk.encode_append(cache, s, None, None, 1)
+        bpk.decode_step(cache, q, 0, L, p, k, scale, out=out, ws=ws)
+
+    def traced(p, steps):
+        """Per-stage milliseconds of `steps` decode steps at budget p (stage
+        tracing: HIP events around each stage on the step's stream)."""
+        bpk.trace_enable(True)
+        try:
+            for _ in range(steps):
+                step(p)
+            ms, calls = bpk.trace_read()
+        finally:
+            bpk.trace_enable(False)
+        return {name: v / calls for name, v in ms.items()}
 
     for _ in range(args.warmup):
         step()
@@ -162,19 +186,27 @@ def main() -> int:
     log("warmup done")
     ms_step = time_launches(step, args.steps)
     log(f"decode step: {ms_step * 1e3:.1f} us")
-
-    # the same steps again with stage tracing: HIP events around each stage on
-    # the decode step's stream
-    bpk.trace_enable(True)
-    try:
-        for _ in range(args.steps):
-            step()
-        stage_ms, calls = bpk.trace_read()
-    finally:
-        bpk.trace_enable(False)
-    stage_ms = {name: v / calls for name, v in stage_ms.items()}
+    stage_ms = traced(budget, args.steps)
     ms_scan = stage_ms["scan"]
     log("stages (us): " + " ".join(f"{n} {v * 1e3:.1f}" for n, v in stage_ms.items()))
+
+    # the workload's other plane budgets: does the step scale with the bits read?
+    sweep = {}
+    if not appends:
+        for p in cfg.budgets:
+            d_p, _ = bpk.alloc_depth(cache, q, 0, L, p)
+            d_np = d_p.cpu().numpy()
+            bits_p = float(np.mean([float(t.sum()) + 0.25 * float((t > 0).sum())
+                                    for t in d_np.reshape(-1, 128)]))
+            for _ in range(2):
+                step(p)
+            ms_p = time_launches(lambda: step(p), args.steps)
+            st_p = traced(p, args.steps)
+            sweep[str(p)] = {"bits_per_token": round(bits_p, 2),
+                             "decode_step_us": round(ms_p * 1e3, 1),
+                             "scan_us": round(st_p["scan"] * 1e3, 1),
+                             "scan_gbs": round(scan_bytes(d_np, n) / (st_p["scan"] * 1e-3) / 1e9, 2)}
+            log(f"P={p}: {sweep[str(p)]}")
 
     # the standalone full scan (scan_scores writes every score: same reads,
     # plus 16 bytes of scores per token)
@@ -242,6 +274,7 @@ def main() -> int:
         "keys_per_s": round(keys_per_s, 0),
         "copy_gbs": round(copy_gbs, 1),
         "scan_bits_per_token_mean": round(float(np.mean(bits)), 2),
+        "budget_sweep": sweep,
     }
     if not args.no_cpu_baseline:
         log("timing the oracle on a CPU sample")

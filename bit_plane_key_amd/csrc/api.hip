@@ -148,8 +148,9 @@ DecodeWs decode_ws(const bpk::Geom& g, int k) {
   const size_t uh = units * g.G;
   const long long groups = (g.nbcap() + bpk::SAMPLE_STRIDE - 1) / bpk::SAMPLE_STRIDE;
   w.sample_ld = groups * bpk::SAMPLE_GROUP * bpk::BLK;
-  // candidate regions: one per scan workgroup, at most nbcap / 16 per unit
-  w.regions = (g.nbcap() + bpk::SCAN_MIN_WG_BLOCKS - 1) / bpk::SCAN_MIN_WG_BLOCKS;
+  // candidate regions of 16 blocks (a scan workgroup of wb blocks takes wb / 16
+  // of them); the capacity rounded up to 256 blocks fits every workgroup size
+  w.regions = (g.nbcap() + 255) / 256 * (256 / bpk::SCAN_MIN_WG_BLOCKS);
   const size_t slots = uh * (size_t)w.regions * bpk::CAND_SLOTS;
   size_t off = 0;
   w.q_basis = off; off += align256(uh * bpk::D * sizeof(float));
@@ -303,6 +304,7 @@ int bpk_decode_step(const bpk_cache_t* c, const uint16_t* q, int32_t l0, int32_t
     cb.sample_ld = w.sample_ld;
     cb.thresh = reinterpret_cast<uint32_t*>(base + w.thresh);
     cb.wg_blocks = bpk::scan_wg_blocks(g);
+    cb.part_slots = bpk::CAND_PART_SLOTS * cb.wg_blocks / bpk::SCAN_MIN_WG_BLOCKS;
     cb.regions = w.regions;
     cb.count = reinterpret_cast<int32_t*>(base + w.count);
     cb.val = reinterpret_cast<float*>(base + w.cval);

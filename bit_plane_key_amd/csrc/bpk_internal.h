@@ -60,13 +60,15 @@ hipError_t launch_topk(const Geom& g, const float* scores, int k, int32_t* idx, 
 // A sampled scan (the first 64 blocks of every 4096) sets per (unit, query
 // head) a score threshold expected to pass about 2 (k - 4 - W) tokens; the full
 // scan then keeps only the tokens at or above it, and the exact top-k is taken
-// among those.  Each scan workgroup owns a region of CAND_SLOTS slots per head
-// (no global atomics); a unit whose candidates are too few, overflow a region
-// or exceed CAND_CAP in all is flagged and redone by a full scan and radix
+// among those.  Each scan workgroup of wg_blocks blocks owns a region of
+// CAND_SLOTS * wg_blocks / SCAN_MIN_WG_BLOCKS slots per head (a unit's regions
+// together always hold about 8 slots per block; no global atomics), in one
+// part per wavefront; a unit whose candidates are too few, overflow a part or
+// exceed CAND_CAP in all is flagged and redone by a full scan and radix
 // select.
 constexpr int SAMPLE_STRIDE = 4096;  // blocks from one sampled group to the next
 constexpr int SAMPLE_GROUP = 64;     // blocks per sampled group
-constexpr int CAND_SLOTS = 128;      // candidate slots per (scan workgroup, head)
+constexpr int CAND_SLOTS = 128;      // candidate slots per (16 scanned blocks, head)
 constexpr int CAND_PARTS = 4;        // parts of a region, one per scan wavefront, counted apart
 constexpr int CAND_PART_SLOTS = CAND_SLOTS / CAND_PARTS;
 constexpr int CAND_CAP = 4096;       // candidates the exact selection takes per head
@@ -78,10 +80,11 @@ struct CandBufs {
   long long sample_ld;  // sample_groups * SAMPLE_GROUP * 64
   uint32_t* thresh;     // [units][G] order key of the threshold
   int wg_blocks;        // blocks per workgroup of the candidate scan
-  long long regions;    // region stride: workgroups per unit the buffers hold
-  int32_t* count;       // [units][G][regions][CAND_PARTS] candidates found per region part
-  float* val;           // [units][G][regions][CAND_SLOTS]
-  int32_t* idx;         // [units][G][regions][CAND_SLOTS]
+  int part_slots;       // CAND_PART_SLOTS * wg_blocks / SCAN_MIN_WG_BLOCKS
+  long long regions;    // per (unit, head): regions of 16 blocks the buffers hold
+  int32_t* count;       // [units][G][regions][CAND_PARTS]: workgroup x, part p at x * CAND_PARTS + p
+  float* val;           // [units][G][regions * CAND_SLOTS]: workgroup x, part p from (x * CAND_PARTS + p) * part_slots
+  int32_t* idx;         // the same
   int32_t* flag;        // [units] 1 = redo this unit unfused
 };
 

@@ -156,7 +156,8 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : (RM <= RM_SMALL ? 3 : 2)
 
   // ---- where a score goes ----
   auto region = [&](int h) {
-    return (((long long)u * G + h) * a.regions + blockIdx.x) * CAND_SLOTS;
+    return ((long long)u * G + h) * a.regions * CAND_SLOTS +
+           (long long)blockIdx.x * CAND_PARTS * a.part_slots;
   };
   auto store = [&](long long tok, int h, float s) {  // FULL / SAMPLE
     const long long uh = (long long)u * G + h;
@@ -171,7 +172,7 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : (RM <= RM_SMALL ? 3 : 2)
   auto append = [&](long long tok, int h, float s) {
     if (tok < 4 || tok >= cand_hi) return;
     const int off = atomicAdd(&sm.ccount[h], 1);
-    if (off < CAND_SLOTS) {
+    if (off < CAND_PARTS * a.part_slots) {
       a.cand_val[region(h) + off] = s;
       a.cand_idx[region(h) + off] = (int32_t)tok;
     }
@@ -182,7 +183,7 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : (RM <= RM_SMALL ? 3 : 2)
       if (tid < G)
         contiguous_part_counts(
             a.cand_count + (((long long)u * G + tid) * a.regions + blockIdx.x) * CAND_PARTS,
-            sm.ccount[tid]);
+            sm.ccount[tid], a.part_slots);
     }
   };
 
@@ -624,7 +625,7 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : (RM <= RM_SMALL ? 3 : 2)
             // c-major, after the wavefront's earlier ones
             const uint64_t gm = 0xFFFFull << (16 * kg);
             int before = 0;
-            const long long base = region(h) + wave * CAND_PART_SLOTS;
+            const long long base = region(h) + (long long)wave * a.part_slots;
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
               const uint64_t mc = __ballot(pass[c]) & gm;
@@ -632,7 +633,7 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : (RM <= RM_SMALL ? 3 : 2)
                 const int slot = wcnt[hg] + before +
                                  (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mc >> 32),
                                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)mc, 0u));
-                if (slot < CAND_PART_SLOTS) {
+                if (slot < a.part_slots) {
                   a.cand_val[base + slot] = exact_score(acc[hg][c], c, cc, exb[hg]);
                   a.cand_idx[base + slot] = (int32_t)(tok0 + 2 * c);
                 }
@@ -881,6 +882,7 @@ hipError_t launch_scan_cand(const Geom& g, const float* q_basis, const uint8_t* 
   a.k = k;
   a.thresh = cb.thresh;
   a.regions = cb.regions;
+  a.part_slots = cb.part_slots;
   a.cand_count = cb.count;
   a.cand_val = cb.val;
   a.cand_idx = cb.idx;

@@ -48,6 +48,7 @@ struct ScanArgs {
   int32_t* __restrict__ cand_count;       // CAND: [unit][G][regions]
   float* __restrict__ cand_val;           // CAND: [unit][G][regions][CAND_SLOTS]
   int32_t* __restrict__ cand_idx;         // CAND: [unit][G][regions][CAND_SLOTS]
+  int part_slots;                         // CAND: candidate slots per (workgroup, head, wavefront)
   int all_rows;                           // wide kernel: take every unit, whatever it reads
   int rows_above;                         // fast kernel: skip units reading at most this many rows
 };
@@ -117,12 +118,12 @@ __device__ __forceinline__ float key_to_float(uint32_t k) {
 
 // the per-part counts of a candidate region filled front to back with total
 // candidates (the last part takes any overflow, which the selection flags)
-__device__ __forceinline__ void contiguous_part_counts(int32_t* cnt, int total) {
+__device__ __forceinline__ void contiguous_part_counts(int32_t* cnt, int total, int part_slots) {
 #pragma unroll
   for (int p = 0; p < CAND_PARTS; ++p) {
-    int c = total - p * CAND_PART_SLOTS;
+    int c = total - p * part_slots;
     c = c < 0 ? 0 : c;
-    if (p + 1 < CAND_PARTS && c > CAND_PART_SLOTS) c = CAND_PART_SLOTS;
+    if (p + 1 < CAND_PARTS && c > part_slots) c = part_slots;
     cnt[p] = c;
   }
 }

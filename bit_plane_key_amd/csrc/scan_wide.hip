@@ -125,7 +125,10 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : 2) void scan_wide_kernel
   for (int h = 0; h < GP; ++h)
     theta[h] = (MODE == SCAN_CAND && h < G) ? key_to_float(a.thresh[(long long)u * G + h])
                                             : -__builtin_inff();
-  auto region = [&](int h) { return (((long long)u * G + h) * a.regions + blockIdx.x) * CAND_SLOTS; };
+  auto region = [&](int h) {
+    return ((long long)u * G + h) * a.regions * CAND_SLOTS +
+           (long long)blockIdx.x * CAND_PARTS * a.part_slots;
+  };
   auto store = [&](long long tok, int h, float s) {  // FULL / SAMPLE
     const long long uh = (long long)u * G + h;
     if constexpr (MODE == SCAN_FULL) {
@@ -137,7 +140,7 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : 2) void scan_wide_kernel
   auto append = [&](long long tok, int h, float s) {  // CAND, lanes whose test passed
     if (tok < 4 || tok >= cand_hi) return;
     const int off = atomicAdd(&sm.ccount[h], 1);
-    if (off < CAND_SLOTS) {
+    if (off < CAND_PARTS * a.part_slots) {
       a.cand_val[region(h) + off] = s;
       a.cand_idx[region(h) + off] = (int32_t)tok;
     }
@@ -148,7 +151,7 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : 2) void scan_wide_kernel
       if (tid < G)
         contiguous_part_counts(
             a.cand_count + (((long long)u * G + tid) * a.regions + blockIdx.x) * CAND_PARTS,
-            sm.ccount[tid]);
+            sm.ccount[tid], a.part_slots);
     }
   };
 

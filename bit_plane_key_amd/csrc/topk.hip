@@ -287,10 +287,11 @@ __global__ __launch_bounds__(TK_THREADS) void cand_select_kernel(CandArgs a) {
     }
     __syncthreads();
     int tot = 0, over = 0;
+    const int ps = a.cb.part_slots;
     for (long long x = tid; x < R * CAND_PARTS; x += TK_THREADS) {
       const int c = cnt[x];
       tot += c;
-      over |= c > CAND_PART_SLOTS;
+      over |= c > ps;
     }
     if (tot) atomicAdd(&sm.total, tot);
     if (over) atomicOr(&sm.over, 1);
@@ -304,16 +305,17 @@ __global__ __launch_bounds__(TK_THREADS) void cand_select_kernel(CandArgs a) {
     // up; the scan's test may also pass tokens a little below the threshold,
     // so only those at or above it count towards want
     const uint32_t tkey = a.cb.thresh[uh];
-    const float* v = a.cb.val + uh * a.cb.regions * CAND_SLOTS;
+    const float* v = a.cb.val + uh * a.cb.regions * CAND_SLOTS;  // part x at x * ps
     const int32_t* ix = a.cb.idx + uh * a.cb.regions * CAND_SLOTS;
     int ge = 0;
-    for (long long e = tid; e < R * CAND_SLOTS; e += TK_THREADS) {
-      const long long x = e / CAND_PART_SLOTS;  // region part
-      if ((int)(e % CAND_PART_SLOTS) < cnt[x]) {
-        const int pos = atomicAdd(&sm.fill, 1);
+    for (long long x = tid; x < R * CAND_PARTS; x += TK_THREADS) {  // one region part a thread
+      const int c = cnt[x];
+      const int pos0 = c ? atomicAdd(&sm.fill, c) : 0;
+      for (int i = 0; i < c; ++i) {
+        const long long e = x * ps + i;
         const uint32_t key = order_key(v[e]);
         ge += key >= tkey;
-        sm.key[pos] = ((uint64_t)key << 32) | (uint32_t)(~(uint32_t)ix[e]);
+        sm.key[pos0 + i] = ((uint64_t)key << 32) | (uint32_t)(~(uint32_t)ix[e]);
       }
     }
     if (ge) atomicAdd(&sm.ge, ge);
