@@ -589,7 +589,12 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : (RM <= RM_SMALL ? 3 : 2)
     };
     // scores of block blk: lane <-> (head 4 hg + l / 16, column l % 16)
     // candidates: wavefront w fills part w of each head's region; wcnt[hg]
-    // counts those of head 4 hg + kg (the same in the 16 lanes of the head)
+    // counts those of head 4 hg + kg (the same in the 16 lanes of the head).
+    // Offsets within the unit's buffers fit 32 bits (capacity <= FAST_MAX_CAP).
+    float* cand_val_u = MODE == SCAN_CAND ? a.cand_val + (long long)u * G * a.regions * CAND_SLOTS : nullptr;
+    int32_t* cand_idx_u = MODE == SCAN_CAND ? a.cand_idx + (long long)u * G * a.regions * CAND_SLOTS : nullptr;
+    const int cand_head_ld = (int)(a.regions * CAND_SLOTS);
+    const int part_off = (int)(blockIdx.x * CAND_PARTS + wave) * a.part_slots;
     int wcnt[HG];
 #pragma unroll
     for (int hg = 0; hg < HG; ++hg) wcnt[hg] = 0;
@@ -622,20 +627,23 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : (RM <= RM_SMALL ? 3 : 2)
               }
             }
             // slot of a passing (lane, c): the head's passing pairs before it,
-            // c-major, after the wavefront's earlier ones
+            // c-major, after the wavefront's earlier ones; a column with no
+            // passing lane is skipped as a whole
             const uint64_t gm = 0xFFFFull << (16 * kg);
             int before = 0;
-            const long long base = region(h) + (long long)wave * a.part_slots;
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-              const uint64_t mc = __ballot(pass[c]) & gm;
+              const uint64_t mw = __ballot(pass[c]);
+              if (mw == 0ull) continue;  // uniform
+              const uint64_t mc = mw & gm;
               if (pass[c]) {
                 const int slot = wcnt[hg] + before +
                                  (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mc >> 32),
                                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)mc, 0u));
                 if (slot < a.part_slots) {
-                  a.cand_val[base + slot] = exact_score(acc[hg][c], c, cc, exb[hg]);
-                  a.cand_idx[base + slot] = (int32_t)(tok0 + 2 * c);
+                  const int off = h * cand_head_ld + part_off + slot;
+                  cand_val_u[off] = exact_score(acc[hg][c], c, cc, exb[hg]);
+                  cand_idx_u[off] = (int32_t)(tok0 + 2 * c);
                 }
               }
               before += __popcll(mc);
