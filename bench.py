@@ -122,6 +122,8 @@ def main() -> int:
     ap.add_argument("--config", default="c4")
     ap.add_argument("--budget", type=int, default=88)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the sweep over the workload's plane budgets (profiling runs)")
     ap.add_argument("--cpu-tokens", type=int, default=1 << 20)
     ap.add_argument("--cpu-layers", type=int, default=2)
     args = ap.parse_args()
@@ -192,7 +194,7 @@ def main() -> int:
 
     # the workload's other plane budgets: does the step scale with the bits read?
     sweep = {}
-    if not appends:
+    if not appends and not args.no_sweep:
         for p in cfg.budgets:
             d_p, _ = bpk.alloc_depth(cache, q, 0, L, p)
             d_np = d_p.cpu().numpy()
@@ -263,7 +265,7 @@ def main() -> int:
             "unit": "GB/s",
             "frac": round(scan_gbs / HBM_PEAK_GBS, 4),
             "traffic": counted_traffic(cfg.name, budget),
-            "kernel": "scan_fast_kernel<4, 2, true> (the decode step's candidate scan)",
+            "kernel": "scan_fast_kernel<4, 2, true, 96> (the decode step's candidate scan)",
             "bytes_per_launch": sbytes,
             "avg_launch_us": round(ms_scan * 1e3, 2),
         },
