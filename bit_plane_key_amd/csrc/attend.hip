@@ -6,10 +6,11 @@
 //    merged with a bitonic sort of (token << 3 | head) keys in LDS, runs of
 //    equal tokens collapse to one union row carrying a G-bit head mask.
 // 2. attend_kernel (one workgroup per (split of ATT_ROWS union rows, unit)):
-//    thread r loads union row r of K once and forms the logits of the heads in
-//    its mask; per-head max and exp-sum over the split; then the split's V rows
-//    are read once (a wavefront reads one 256-byte row per step, lane <-> two
-//    channels) and accumulated for every head with its weights.  The split
+//    every K row of the split is read once, whole and coalesced (16 lanes of a
+//    wavefront per row, 16 bytes a lane, all of a wavefront's loads in flight
+//    together), the logits of the heads in its mask reduced across the 16
+//    lanes; per-head max and exp-sum over the split; then the V rows are read
+//    the same way and accumulated for every head with its weights.  The split
 //    writes (max, sum, unnormalised output) per head.
 // 3. combine_kernel: log-sum-exp merge of the splits per (unit, head).
 #include <limits.h>
@@ -138,14 +139,32 @@ struct AttArgs {
   int nsplit;
 };
 
+// sum over the 16 lanes of a DPP row (every lane of the row gets it; the
+// butterfly and mirrors add the same pairs in every lane, so the result is
+// the same in all 16)
+__device__ __forceinline__ float row16_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
+  return v;
+}
+
+// One workgroup per (split of ATT_ROWS union rows, unit).  Rows are read whole
+// and coalesced: in each wavefront, lane l takes 16-byte chunk l % 16 (8
+// channels) of row 4 it + l / 16 of the wavefront's 64, for it = 0..15, with
+// all 16 loads in flight before the arithmetic.
 template <int G, bool F32>
 __global__ __launch_bounds__(ATT_THREADS) void attend_kernel(AttArgs a) {
-  __shared__ float sq[G][D];
-  __shared__ float p[G][ATT_ROWS];
+  constexpr int RPW = ATT_ROWS / (ATT_THREADS / 64);  // rows per wavefront (64)
+  constexpr int IT = RPW / 4;                          // 4 rows per wavefront load
   __shared__ int32_t rows[ATT_ROWS];
+  __shared__ int masks[ATT_ROWS];
+  __shared__ float p[ATT_ROWS][G];                     // logits, then weights
   __shared__ float red[ATT_THREADS / 64][G];
-  __shared__ float oacc[4][G][D];
+  __shared__ float oacc[ATT_THREADS / 16][G][D];       // per 16-lane row group
   const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, rs = lane >> 4, ch = lane & 15;
   const int split = blockIdx.x, u = blockIdx.y;
   const long long gu = a.g.global_unit(u);
   const long long sel = (long long)G * a.k;
@@ -153,59 +172,86 @@ __global__ __launch_bounds__(ATT_THREADS) void attend_kernel(AttArgs a) {
   const int r0 = split * ATT_ROWS;
   const int nr = count - r0 < ATT_ROWS ? (count - r0 > 0 ? count - r0 : 0) : ATT_ROWS;
   float* part = a.part + (((long long)u * a.nsplit + split) * G) * (D + 2);
-
-  for (int e = tid; e < G * D; e += ATT_THREADS) sq[e / D][e % D] = bf16_to_f32(a.q[(long long)u * G * D + e]);
-  // logits of union row tid for the heads in its mask
-  int mask = 0;
-  long long row = 0;
-  if (tid < nr) {
-    row = a.uidx[(long long)u * sel + r0 + tid];
-    mask = a.umask[(long long)u * sel + r0 + tid];
+  if (nr == 0) {  // an empty split contributes nothing
+    if (tid < G) part[tid * (D + 2)] = -INFINITY;
+    return;
   }
-  rows[tid] = (int32_t)row;
+  {
+    int row = 0, mask = 0;  // rows past nr: token 0 of the unit (read, weight 0)
+    if (tid < nr) {
+      row = a.uidx[(long long)u * sel + r0 + tid];
+      mask = a.umask[(long long)u * sel + r0 + tid];
+    }
+    rows[tid] = row;
+    masks[tid] = mask;
+  }
+  // the lane's 8 channels of each query head
+  float qf[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const uint4 qv = *reinterpret_cast<const uint4*>(a.q + ((long long)u * G + h) * D + 8 * ch);
+    const uint32_t w[4] = {qv.x, qv.y, qv.z, qv.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      qf[h][2 * e] = __uint_as_float(w[e] << 16);
+      qf[h][2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+    }
+  }
   __syncthreads();
-  float lg[G];
+
+  // ---- logits ----
+  auto krow = [&](int r) { return (gu * a.g.cap + rows[r]) * D + 8 * ch; };
+  float kf[IT][8];
+  if constexpr (F32) {
+    float4 kv[IT][2];
 #pragma unroll
-  for (int h = 0; h < G; ++h) lg[h] = 0.f;
-  if (mask) {
-    const long long base = (gu * a.g.cap + row) * D;
-    if constexpr (F32) {
-      const float4* kr = reinterpret_cast<const float4*>(static_cast<const float*>(a.k_rows) + base);
-      for (int c = 0; c < D / 4; ++c) {
-        const float4 v = kr[c];
+    for (int it = 0; it < IT; ++it) {
+      const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(a.k_rows) +
+                                                          krow(RPW * wave + 4 * it + rs));
+      kv[it][0] = src[0];
+      kv[it][1] = src[1];
+    }
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-          lg[h] = fmaf(sq[h][4 * c], v.x, lg[h]);
-          lg[h] = fmaf(sq[h][4 * c + 1], v.y, lg[h]);
-          lg[h] = fmaf(sq[h][4 * c + 2], v.z, lg[h]);
-          lg[h] = fmaf(sq[h][4 * c + 3], v.w, lg[h]);
-        }
-      }
-    } else {
-      const uint4* kr = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.k_rows) + base);
-      for (int c = 0; c < D / 8; ++c) {
-        const uint4 v = kr[c];
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    for (int it = 0; it < IT; ++it) {
+      kf[it][0] = kv[it][0].x; kf[it][1] = kv[it][0].y; kf[it][2] = kv[it][0].z; kf[it][3] = kv[it][0].w;
+      kf[it][4] = kv[it][1].x; kf[it][5] = kv[it][1].y; kf[it][6] = kv[it][1].z; kf[it][7] = kv[it][1].w;
+    }
+  } else {
+    uint4 kv[IT];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float lo = __uint_as_float(w[e] << 16);
-          const float hi = __uint_as_float(w[e] & 0xFFFF0000u);
+    for (int it = 0; it < IT; ++it)
+      kv[it] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.k_rows) +
+                                               krow(RPW * wave + 4 * it + rs));
 #pragma unroll
-          for (int h = 0; h < G; ++h) {
-            lg[h] = fmaf(sq[h][8 * c + 2 * e], lo, lg[h]);
-            lg[h] = fmaf(sq[h][8 * c + 2 * e + 1], hi, lg[h]);
-          }
-        }
+    for (int it = 0; it < IT; ++it) {
+      const uint32_t w[4] = {kv[it].x, kv[it].y, kv[it].z, kv[it].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        kf[it][2 * e] = __uint_as_float(w[e] << 16);
+        kf[it][2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
       }
     }
   }
-  // per-head max over the split
-  const int wave = tid >> 6, lane = tid & 63;
-  float mx[G];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int r = RPW * wave + 4 * it + rs;
+    const int mask = masks[r];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float d = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) d = fmaf(qf[h][e], kf[it][e], d);
+      d = row16_sum(d);
+      if (ch == 0) p[r][h] = ((mask >> h) & 1) ? d * a.scale : -INFINITY;
+    }
+  }
+  __syncthreads();
+
+  // ---- per-head max and exp-sum over the split (thread tid <-> row tid) ----
+  float mx[G], sum[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    float v = ((mask >> h) & 1) ? lg[h] * a.scale : -INFINITY;
-    lg[h] = v;
+    float v = p[tid][h];
     for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
     if (lane == 0) red[wave][h] = v;
   }
@@ -217,11 +263,11 @@ __global__ __launch_bounds__(ATT_THREADS) void attend_kernel(AttArgs a) {
     mx[h] = v;
   }
   __syncthreads();
-  float sum[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    const float e = (lg[h] == -INFINITY) ? 0.f : expf(lg[h] - mx[h]);
-    p[h][tid] = e;
+    const float lg = p[tid][h];
+    const float e = (lg == -INFINITY) ? 0.f : expf(lg - mx[h]);
+    p[tid][h] = e;
     float v = e;
     for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
     if (lane == 0) red[wave][h] = v;
@@ -233,31 +279,44 @@ __global__ __launch_bounds__(ATT_THREADS) void attend_kernel(AttArgs a) {
     for (int w = 0; w < ATT_THREADS / 64; ++w) v += red[w][h];
     sum[h] = v;
   }
-  // V: wavefront `wave` takes rows wave, wave + 4, ...; lane owns channels 2*lane, 2*lane+1
-  float o[G][2];
+
+  // ---- V: the same row mapping; lane accumulates its 8 channels per head ----
+  uint4 vv[IT];
 #pragma unroll
-  for (int h = 0; h < G; ++h) o[h][0] = o[h][1] = 0.f;
-  for (int r = wave; r < nr; r += ATT_THREADS / 64) {
-    const uint32_t v2 =
-        reinterpret_cast<const uint32_t*>(a.v_rows + (gu * a.g.cap + rows[r]) * D)[lane];
-    const float v0 = __uint_as_float(v2 << 16), v1 = __uint_as_float(v2 & 0xFFFF0000u);
+  for (int it = 0; it < IT; ++it)
+    vv[it] = *reinterpret_cast<const uint4*>(
+        a.v_rows + (gu * a.g.cap + rows[RPW * wave + 4 * it + rs]) * D + 8 * ch);
+  float o[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[h][e] = 0.f;
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int r = RPW * wave + 4 * it + rs;
+    const uint32_t w[4] = {vv[it].x, vv[it].y, vv[it].z, vv[it].w};
+    float vf[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      vf[2 * e] = __uint_as_float(w[e] << 16);
+      vf[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+    }
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const float w = p[h][r];
-      o[h][0] = fmaf(w, v0, o[h][0]);
-      o[h][1] = fmaf(w, v1, o[h][1]);
+      const float wt = p[r][h];  // 0 for rows past nr and heads without the row
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[h][e] = fmaf(wt, vf[e], o[h][e]);
     }
   }
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    oacc[wave][h][2 * lane] = o[h][0];
-    oacc[wave][h][2 * lane + 1] = o[h][1];
-  }
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) oacc[4 * wave + rs][h][8 * ch + e] = o[h][e];
   __syncthreads();
   for (int e = tid; e < G * D; e += ATT_THREADS) {
     const int h = e / D, d = e % D;
     float v = 0.f;
-    for (int w = 0; w < ATT_THREADS / 64; ++w) v += oacc[w][h][d];
+    for (int gidx = 0; gidx < ATT_THREADS / 16; ++gidx) v += oacc[gidx][h][d];
     part[h * (D + 2) + 2 + d] = v;
   }
   if (tid < G) {
