@@ -77,6 +77,56 @@ __global__ __launch_bounds__(UNION_THREADS) void union_kernel(UnionArgs a) {
   }
   for (int e = tid; e < BPK_MAX_SELECTED / 4; e += UNION_THREADS) masks[e] = 0;
   __syncthreads();
+  // select_topk's lists are strictly ascending with padding at the end: then
+  // the merged position of an entry is its index in its list plus the number
+  // of smaller keys in each other list (a binary search).  Any other input is
+  // sorted whole.
+  bool bad = false;
+  for (int e = tid; e < sel; e += UNION_THREADS) {
+    if ((e + 1) % a.k == 0) continue;
+    const uint32_t x = keys[e], y = keys[e + 1];
+    bad |= !(x < y || (x == 0xFFFFFFFFu && y == 0xFFFFFFFFu));
+  }
+  if (!__syncthreads_or(bad)) {
+    uint32_t mk[BPK_MAX_SELECTED / UNION_THREADS];
+    int pos[BPK_MAX_SELECTED / UNION_THREADS];
+    int nv = 0;  // valid entries over all lists
+    for (int h = 0; h < G; ++h) {
+      int lo = 0, hi = a.k;  // first padding entry of list h
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (keys[h * a.k + mid] != 0xFFFFFFFFu) lo = mid + 1;
+        else hi = mid;
+      }
+      nv += lo;
+    }
+    int c = 0;
+    for (int e = tid; e < sel; e += UNION_THREADS, ++c) {
+      const uint32_t x = keys[e];
+      mk[c] = x;
+      pos[c] = -1;
+      if (x == 0xFFFFFFFFu) continue;
+      const int h = e / a.k;
+      int p = e - h * a.k;
+      for (int b = 0; b < G; ++b) {
+        if (b == h) continue;
+        int lo = 0, hi = a.k;  // keys of list b below x
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          if (keys[b * a.k + mid] < x) lo = mid + 1;
+          else hi = mid;
+        }
+        p += lo;
+      }
+      pos[c] = p;
+    }
+    __syncthreads();
+    c = 0;
+    for (int e = tid; e < sel; e += UNION_THREADS, ++c)
+      if (pos[c] >= 0) keys[pos[c]] = mk[c];
+    for (int e = nv + tid; e < m; e += UNION_THREADS) keys[e] = 0xFFFFFFFFu;
+    __syncthreads();
+  } else {
   for (int size = 2; size <= m; size <<= 1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
       for (int i = tid; i < m / 2; i += UNION_THREADS) {
@@ -91,6 +141,7 @@ __global__ __launch_bounds__(UNION_THREADS) void union_kernel(UnionArgs a) {
       }
       __syncthreads();
     }
+  }
   }
   // thread t owns a contiguous run of `per` sorted positions
   const int per = (m + UNION_THREADS - 1) / UNION_THREADS;

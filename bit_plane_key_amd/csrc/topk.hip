@@ -194,6 +194,28 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(TopkArgs a) {
   sort_and_write(sm.buf, k, out);
 }
 
+// sum over the wavefront (DPP inside each 16-lane row, then the four rows'
+// results read out); every lane must be active
+__device__ __forceinline__ int wave_sum_dpp(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);   // quad_perm xor 1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);   // quad_perm xor 2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);  // row_half_mirror
+  v += __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false);  // row_mirror
+  return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) +
+         __builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48);
+}
+
+// maximum over the wavefront, the same way
+__device__ __forceinline__ uint32_t wave_max_dpp(uint32_t v) {
+  auto mx = [](uint32_t x, uint32_t y) { return x > y ? x : y; };
+  v = mx(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
+  v = mx(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
+  v = mx(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));
+  v = mx(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));
+  return mx(mx((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16)),
+            mx((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48)));
+}
+
 struct ThreshArgs {
   Geom g;
   int k;
@@ -245,112 +267,403 @@ __global__ __launch_bounds__(TK_THREADS) void threshold_kernel(ThreshArgs a) {
   }
 }
 
-struct CandSmem {
-  uint64_t key[CAND_CAP];
-  int32_t buf[BPK_MAX_K];
-  int total, over, fill, ge;
-};
+// The same threshold with the sample in registers (NPT keys a thread, the
+// sample of every head of the launch at most 256 * NPT): the largest key T
+// with at least r valid keys >= T, found bit by bit from the top.  The top 16
+// bits are probed over every key (each count reduced over the wavefronts
+// through LDS, two slots, so one barrier a probe); the keys sharing those 16
+// bits are then compacted into LDS and the low 16 bits probed over them alone
+// (over every key again if more than TH_CAP share them).
+constexpr int TH_THREADS = 256;
+constexpr int TH_CAP = 1024;
+
+template <int NPT>
+__global__ __launch_bounds__(TH_THREADS) void threshold_reg_kernel(ThreshArgs a) {
+  __shared__ int part[2][TH_THREADS / 64];
+  __shared__ uint32_t near[TH_CAP];
+  __shared__ int nnear;
+  const int G = a.g.G;
+  const int u = blockIdx.x / G, h = blockIdx.x % G;
+  const long long uh = (long long)u * G + h;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const long long n = a.g.n[a.g.seq_of(u)];
+  const long long w = kept_tail(n);
+  const long long hi = n - w;
+  const long long want = (long long)a.k - 4 - w;
+  uint32_t tkey = 0xFFFFFFFFu;  // nothing is a candidate
+  if (n > a.k && want > 0) {
+    const long long nb = n / BLK;
+    const long long ngr = (nb + SAMPLE_STRIDE - 1) / SAMPLE_STRIDE;
+    const long long gtok = (long long)SAMPLE_STRIDE * BLK, glen = (long long)SAMPLE_GROUP * BLK;
+    long long m = 0;
+    for (long long gi = 0; gi < ngr; ++gi) {
+      const long long t0 = gi * gtok, t1 = t0 + glen;
+      const long long x0 = t0 > 4 ? t0 : 4, x1 = t1 < hi ? t1 : hi;
+      m += x1 > x0 ? x1 - x0 : 0;
+    }
+    const long long nc = hi - 4;
+    const long long r = (2 * want * m + nc - 1) / nc + 8;
+    if (r > m) {
+      tkey = 0;  // the sample is too small to cut anything: all are candidates
+    } else {
+      // sample position i = (group gi, offset j) holds token gi * SAMPLE_STRIDE * 64 + j;
+      // invalid positions hold key 0, below every probe
+      const float* sc = a.cb.sample + uh * a.cb.sample_ld;
+      const long long len = ngr * glen;
+      float f[NPT];
+#pragma unroll
+      for (int q = 0; q < NPT; ++q) {
+        const long long i = (long long)q * TH_THREADS + tid;
+        f[q] = sc[i < len ? i : 0];
+      }
+      uint32_t key[NPT];
+#pragma unroll
+      for (int q = 0; q < NPT; ++q) {
+        const long long i = (long long)q * TH_THREADS + tid;
+        const long long t = (i / glen) * gtok + i % glen;
+        key[q] = (i < len && t >= 4 && t < hi) ? order_key(f[q]) : 0u;
+      }
+      if (tid == 0) nnear = 0;
+      int slot = 0;
+      // keys >= t over the workgroup
+      auto block_count = [&](uint32_t t) {
+        int c = 0;
+#pragma unroll
+        for (int q = 0; q < NPT; ++q) {
+          c += __popcll(__ballot(key[q] >= t));
+          // a few masks live at a time (the compiler would otherwise hold
+          // them all in scalar registers)
+          if (q % 8 == 7) __builtin_amdgcn_sched_barrier(0);
+        }
+        if (lane == 0) part[slot][wave] = c;
+        __syncthreads();
+        int tot = 0;
+#pragma unroll
+        for (int x = 0; x < TH_THREADS / 64; ++x) tot += part[slot][x];
+        slot ^= 1;
+        return tot;
+      };
+      uint32_t T = 0u;
+      for (int b = 31; b >= 16; --b) {
+        const uint32_t t = T | (1u << b);
+        if (block_count(t) >= r) T = t;
+      }
+      const long long above = T >= 0xFFFF0000u ? 0 : block_count(T + 0x10000u);
+      // the keys with T's top 16 bits
+#pragma unroll
+      for (int q = 0; q < NPT; ++q) {
+        const bool nr = (key[q] & 0xFFFF0000u) == T && key[q] != 0u;
+        const uint64_t mk = __ballot(nr);
+        if (mk != 0ull) {
+          int base = 0;
+          if (lane == 0) base = atomicAdd(&nnear, __popcll(mk));
+          base = __shfl(base, 0);
+          const int pos = base + (int)__builtin_amdgcn_mbcnt_hi(
+                                     (uint32_t)(mk >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mk, 0u));
+          if (nr && pos < TH_CAP) near[pos] = key[q];
+        }
+      }
+      __syncthreads();
+      const int nn = nnear;
+      if (nn <= TH_CAP) {
+        // every wavefront finishes the same search over the compacted keys
+        const long long rr = r - above;
+        for (int b = 15; b >= 0; --b) {
+          const uint32_t t = T | (1u << b);
+          int c = 0;
+          for (int i = lane; i < nn; i += 64) c += near[i] >= t ? 1 : 0;
+          if (wave_sum_dpp(c) >= rr) T = t;
+        }
+      } else {
+        for (int b = 15; b >= 0; --b) {
+          const uint32_t t = T | (1u << b);
+          if (block_count(t) >= r) T = t;
+        }
+      }
+      tkey = T;
+    }
+  }
+  if (tid == 0) {
+    a.cb.thresh[uh] = tkey;
+    if (h == 0) a.cb.flag[u] = 0;
+  }
+}
+
+constexpr int CAND_MAX_PARTS = 4096;  // region parts per head the selection indexes (more: flagged)
+constexpr int CS_WAVES = 4;            // heads per workgroup, one wavefront each
+constexpr int CS_NPL = CAND_CAP / 64;  // candidates per lane
+constexpr int CS_WPL = FUSED_MAX_K / 64;  // winners per lane in the index sort
+static_assert(CAND_CAP % 64 == 0 && FUSED_MAX_K % 64 == 0, "whole wavefront rows");
 
 struct CandArgs {
   Geom g;
   int k;
   CandBufs cb;
   int32_t* idx;
+  int lds_ints;  // LDS ints per wavefront: the part prefix, then the winners
 };
 
-__global__ __launch_bounds__(TK_THREADS) void cand_select_kernel(CandArgs a) {
-  __shared__ CandSmem sm;
+// number of lanes of candidate rows r < NPL with pred(r); rows are taken in
+// groups of CS_GROUP, a group wholly at or past total skipped
+constexpr int CS_GROUP = 16;
+template <int NPL, typename Pred>
+__device__ __forceinline__ int wave_count(int total, Pred pred) {
+  int c = 0;
+#pragma unroll
+  for (int g = 0; g < NPL; g += CS_GROUP) {
+    if (g * 64 >= total) break;
+#pragma unroll
+    for (int r = g; r < g + CS_GROUP; ++r) c += __popcll(__ballot(pred(r)));
+  }
+  return c;
+}
+
+// Sorts the wavefront's 64 * NE values ascending (lane-major: element
+// lane * NE + r in x[r]) with a bitonic network: exchanges inside a lane for
+// strides below NE, across lanes by shuffles above.
+template <int NE>
+__device__ __forceinline__ void wave_bitonic_sort(int32_t (&x)[NE], int lane) {
+#pragma unroll
+  for (int k = 2; k <= 64 * NE; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      if (j < NE) {
+#pragma unroll
+        for (int r = 0; r < NE; ++r) {
+          if (r & j) continue;
+          const bool asc = k < NE ? ((r & k) == 0) : (((lane * NE) & k) == 0);
+          const int32_t a = x[r], b = x[r | j];
+          const int32_t lo = a < b ? a : b, hi = a < b ? b : a;
+          x[r] = asc ? lo : hi;
+          x[r | j] = asc ? hi : lo;
+        }
+      } else {
+        const int d = j / NE;
+        const bool keep_min = ((lane & d) == 0) == (((lane * NE) & k) == 0);
+#pragma unroll
+        for (int r = 0; r < NE; ++r) {
+          const int32_t y = __shfl_xor(x[r], d);
+          x[r] = keep_min ? (x[r] < y ? x[r] : y) : (x[r] < y ? y : x[r]);
+        }
+      }
+    }
+  }
+}
+
+// the want winners in lds sorted ascending and written to out (NE a lane)
+template <int NE>
+__device__ __forceinline__ void sort_winners(const int* lds, int want, int lane, int32_t* out) {
+  int32_t x[NE];
+#pragma unroll
+  for (int r = 0; r < NE; ++r) {
+    const int e = lane * NE + r;
+    x[r] = e < want ? lds[e] : INT_MAX;
+  }
+  wave_bitonic_sort<NE>(x, lane);
+#pragma unroll
+  for (int r = 0; r < NE; ++r) {
+    const int e = lane * NE + r;
+    if (e < want) out[e] = x[r];
+  }
+}
+
+// One wavefront per (unit, query head).  The candidates (at most CAND_CAP,
+// CS_NPL a lane in registers) are gathered through the prefix of the region
+// part counts; the key K* of the (k - 4 - W)-th largest is found bit by bit
+// from the top (the largest T with at least want keys >= T), the lowest token
+// indices among keys equal to K* likewise when not all of them are taken; the
+// winners are compacted in LDS, sorted by token index and written between
+// the first 4 and the last W tokens.
+__global__ __launch_bounds__(CS_WAVES * 64) void cand_select_kernel(CandArgs a) {
+  extern __shared__ int cs_lds[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int G = a.g.G;
-  const int u = blockIdx.x / G, h = blockIdx.x % G;
-  const long long uh = (long long)u * G + h;
-  const int tid = threadIdx.x;
+  const long long uh = (long long)blockIdx.x * CS_WAVES + wave;
+  if (uh >= (long long)a.g.units() * G) return;
+  const int u = (int)(uh / G);
+  int* lds = cs_lds + wave * a.lds_ints;
   const int k = a.k;
   const long long n = a.g.n[a.g.seq_of(u)];
   int32_t* out = a.idx + uh * k;
   if (n <= k) {
-    for (int i = tid; i < k; i += TK_THREADS) out[i] = i < n ? i : -1;
+    for (int i = lane; i < k; i += 64) out[i] = i < n ? i : -1;
     return;
   }
   const long long w = kept_tail(n);
   const long long hi = n - w;
   const int want = k - 4 - (int)w;
-  int nk = 0;
   if (want > 0) {
-    // the candidate regions of this unit's scan workgroups
     const long long R = (n / BLK + a.cb.wg_blocks - 1) / a.cb.wg_blocks;
-    const int32_t* cnt = a.cb.count + uh * a.cb.regions * CAND_PARTS;  // [region][part]
-    if (tid == 0) {
-      sm.total = 0;
-      sm.over = 0;
-      sm.fill = 0;
-      sm.ge = 0;
-    }
-    __syncthreads();
-    int tot = 0, over = 0;
-    const int ps = a.cb.part_slots;
-    for (long long x = tid; x < R * CAND_PARTS; x += TK_THREADS) {
-      const int c = cnt[x];
-      tot += c;
-      over |= c > ps;
-    }
-    if (tot) atomicAdd(&sm.total, tot);
-    if (over) atomicOr(&sm.over, 1);
-    __syncthreads();
-    const int total = sm.total;
-    if (sm.over || total < want || total > CAND_CAP) {
-      if (tid == 0) a.cb.flag[u] = 1;
+    const int nparts = (int)(R * CAND_PARTS);
+    if (nparts > CAND_MAX_PARTS || nparts > a.lds_ints) {
+      if (lane == 0) a.cb.flag[u] = 1;
       return;
     }
-    // (score key, complemented index) in descending order = score down, index
-    // up; the scan's test may also pass tokens a little below the threshold,
-    // so only those at or above it count towards want
-    const uint32_t tkey = a.cb.thresh[uh];
+    // exclusive prefix of the part counts ([region][part], in order): lane l
+    // takes parts [l * cpl, (l + 1) * cpl), loads them all, then writes
+    // their prefix after a scan of the lane sums
+    const int32_t* cnt = a.cb.count + uh * a.cb.regions * CAND_PARTS;
+    const int ps = a.cb.part_slots;
+    const int cpl = (nparts + 63) / 64;
+    const int x0 = lane * cpl;
+    int sum = 0;
+    bool over = false;
+#pragma unroll 8
+    for (int i = 0; i < cpl; ++i) {
+      const int x = x0 + i;
+      if (x < nparts) {
+        const int c = cnt[x];
+        lds[x] = c;
+        sum += c;
+        over |= c > ps;
+      }
+    }
+    int incl = sum;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off);
+      if (lane >= off) incl += y;
+    }
+    const int carry = __shfl(incl, 63);
+    int run = incl - sum;
+    for (int i = 0; i < cpl; ++i) {
+      const int x = x0 + i;
+      if (x < nparts) {
+        const int c = lds[x];
+        lds[x] = run;
+        run += c;
+      }
+    }
+    const int total = carry;
+    if (__ballot(over) != 0ull || total < want || total > CAND_CAP) {
+      if (lane == 0) a.cb.flag[u] = 1;
+      return;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // candidate j = r * 64 + lane: its part is the last with prefix <= j
+    int top = 1;
+    while (2 * top < nparts) top <<= 1;
+    int part[CS_NPL];
+#pragma unroll
+    for (int r = 0; r < CS_NPL; ++r) part[r] = 0;
+    for (int s = top; s > 0; s >>= 1) {
+#pragma unroll
+      for (int g = 0; g < CS_NPL; g += CS_GROUP) {
+        if (g * 64 >= total) break;
+#pragma unroll
+        for (int r = g; r < g + CS_GROUP; ++r) {
+          const int q = part[r] + s;
+          if (q < nparts && lds[q] <= r * 64 + lane) part[r] = q;
+        }
+      }
+    }
+    // (order key, token index); padding (past total) is (0, INT_MAX), and no
+    // token index is INT_MAX
     const float* v = a.cb.val + uh * a.cb.regions * CAND_SLOTS;  // part x at x * ps
     const int32_t* ix = a.cb.idx + uh * a.cb.regions * CAND_SLOTS;
-    int ge = 0;
-    for (long long x = tid; x < R * CAND_PARTS; x += TK_THREADS) {  // one region part a thread
-      const int c = cnt[x];
-      const int pos0 = c ? atomicAdd(&sm.fill, c) : 0;
-      for (int i = 0; i < c; ++i) {
-        const long long e = x * ps + i;
-        const uint32_t key = order_key(v[e]);
-        ge += key >= tkey;
-        sm.key[pos0 + i] = ((uint64_t)key << 32) | (uint32_t)(~(uint32_t)ix[e]);
+    uint32_t key[CS_NPL];
+    int32_t id[CS_NPL];
+#pragma unroll
+    for (int r = 0; r < CS_NPL; ++r) {
+      key[r] = 0u;
+      id[r] = INT_MAX;
+    }
+#pragma unroll
+    for (int g = 0; g < CS_NPL; g += CS_GROUP) {
+      if (g * 64 >= total) break;
+      // every load of the group issued before any is used (invalid lanes
+      // read slot 0)
+      float sv[CS_GROUP];
+      int32_t si[CS_GROUP];
+#pragma unroll
+      for (int r = g; r < g + CS_GROUP; ++r) {
+        const int j = r * 64 + lane;
+        const long long e = j < total ? (long long)part[r] * ps + (j - lds[part[r]]) : 0;
+        sv[r - g] = v[e];
+        si[r - g] = ix[e];
+      }
+#pragma unroll
+      for (int r = g; r < g + CS_GROUP; ++r) {
+        const bool ok = r * 64 + lane < total;
+        key[r] = ok ? order_key(sv[r - g]) : 0u;
+        id[r] = ok ? si[r - g] : INT_MAX;
       }
     }
-    if (ge) atomicAdd(&sm.ge, ge);
-    __syncthreads();
-    if (sm.ge < want) {
-      if (tid == 0) a.cb.flag[u] = 1;
+    // the scan's test may also pass tokens a little below the threshold: only
+    // those at or above it count towards want
+    const uint32_t tkey = a.cb.thresh[uh];
+    const int ge =
+        wave_count<CS_NPL>(total, [&](int r) { return id[r] != INT_MAX && key[r] >= tkey; });
+    if (ge < want) {
+      if (lane == 0) a.cb.flag[u] = 1;
       return;
     }
-    int m = 1;
-    while (m < total) m <<= 1;
-    for (int i = total + tid; i < m; i += TK_THREADS) sm.key[i] = 0ull;
-    __syncthreads();
-    for (int size = 2; size <= m; size <<= 1) {
-      for (int stride = size >> 1; stride > 0; stride >>= 1) {
-        for (int i = tid; i < m / 2; i += TK_THREADS) {
-          const int lo_i = 2 * i - (i & (stride - 1));
-          const int hi_i = lo_i + stride;
-          const bool down = ((lo_i & size) == 0);
-          const uint64_t x = sm.key[lo_i], y = sm.key[hi_i];
-          if ((x < y) == down) {
-            sm.key[lo_i] = y;
-            sm.key[hi_i] = x;
-          }
-        }
-        __syncthreads();
-      }
+    // K*: the largest T with at least want keys >= T.  tkey <= K* <= the
+    // largest key, so K* has their common top bits and the probes start below
+    // them (padding keys are 0 and every probed T is at least 1).
+    uint32_t mx = 0u;
+#pragma unroll
+    for (int r = 0; r < CS_NPL; ++r) mx = key[r] > mx ? key[r] : mx;
+    mx = wave_max_dpp(mx);
+    const uint32_t diff = tkey ^ mx;
+    const int b0 = diff == 0u ? -1 : 31 - __builtin_clz(diff);
+    uint32_t T = b0 < 0 ? tkey : (b0 == 31 ? 0u : tkey & ~((2u << b0) - 1u));
+    for (int b = b0; b >= 0; --b) {
+      const uint32_t t = T | (1u << b);
+      if (wave_count<CS_NPL>(total, [&](int r) { return key[r] >= t; }) >= want) T = t;
     }
-    for (int i = tid; i < want; i += TK_THREADS)
-      sm.buf[i] = (int32_t)(~(uint32_t)(sm.key[i] & 0xFFFFFFFFull));
-    nk = want;
+    // the winners, compacted into LDS over the spent part prefix: first the
+    // keys above K*, then the lowest-index keys equal to it
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    int base = 0;
+    auto emit = [&](auto win) {
+#pragma unroll
+      for (int g = 0; g < CS_NPL; g += CS_GROUP) {
+        if (g * 64 >= total) break;
+#pragma unroll
+        for (int r = g; r < g + CS_GROUP; ++r) {
+          const bool w_ = win(r);
+          const uint64_t m = __ballot(w_);
+          const int pos = base + (int)__builtin_amdgcn_mbcnt_hi(
+                                     (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+          if (w_) lds[pos] = id[r];
+          base += __popcll(m);
+        }
+      }
+    };
+    emit([&](int r) { return key[r] > T; });
+    const int rem = want - base;  // >= 1 keys equal to K* are taken
+    // the ties' indices (INT_MAX for every other slot)
+#pragma unroll
+    for (int r = 0; r < CS_NPL; ++r) id[r] = key[r] == T ? id[r] : INT_MAX;
+    const int eq = wave_count<CS_NPL>(total, [&](int r) { return id[r] != INT_MAX; });
+    int32_t imax = INT_MAX - 1;  // ties taken: index <= imax
+    if (eq > rem) {
+      // the rem-th lowest tie index: the largest I with fewer than rem tie
+      // indices below it
+      int32_t I = 0;
+      for (int b = 30; b >= 0; --b) {
+        const int32_t t = I | (1 << b);
+        if (wave_count<CS_NPL>(total, [&](int r) { return id[r] < t; }) < rem) I = t;
+      }
+      imax = I;
+    }
+    emit([&](int r) { return id[r] <= imax; });
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (want <= 64 * (CS_WPL / 2))
+      sort_winners<CS_WPL / 2>(lds, want, lane, out + 4);
+    else
+      sort_winners<CS_WPL>(lds, want, lane, out + 4);
   }
-  for (int i = tid; i < 4; i += TK_THREADS) sm.buf[nk + i] = i;
-  for (long long i = tid; i < w; i += TK_THREADS) sm.buf[nk + 4 + i] = (int32_t)(hi + i);
-  __syncthreads();
-  sort_and_write(sm.buf, k, out);
+  const int nk = want > 0 ? want : 0;
+  if (lane < 4 && lane < k) out[lane] = lane;
+  for (long long i = lane; 4 + nk + i < k; i += 64) out[4 + nk + i] = (int32_t)(hi + i);
 }
 
 }  // namespace
@@ -376,16 +689,28 @@ hipError_t launch_threshold(const Geom& g, int k, const CandBufs& cb, hipStream_
   ThreshArgs a{g, k, cb};
   const long long blocks = (long long)g.units() * g.G;
   if (blocks == 0) return hipSuccess;
-  threshold_kernel<<<(unsigned)blocks, TK_THREADS, 0, st>>>(a);
+  const long long len = sample_groups(g) * SAMPLE_GROUP * BLK;
+  if (len <= 16 * TH_THREADS)
+    threshold_reg_kernel<16><<<(unsigned)blocks, TH_THREADS, 0, st>>>(a);
+  else if (len <= 64 * TH_THREADS)
+    threshold_reg_kernel<64><<<(unsigned)blocks, TH_THREADS, 0, st>>>(a);
+  else
+    threshold_kernel<<<(unsigned)blocks, TK_THREADS, 0, st>>>(a);
   return hipGetLastError();
 }
 
 hipError_t launch_cand_select(const Geom& g, int k, const CandBufs& cb, int32_t* idx,
                               hipStream_t st) {
-  CandArgs a{g, k, cb, idx};
-  const long long blocks = (long long)g.units() * g.G;
-  if (blocks == 0) return hipSuccess;
-  cand_select_kernel<<<(unsigned)blocks, TK_THREADS, 0, st>>>(a);
+  const long long heads = (long long)g.units() * g.G;
+  if (heads == 0) return hipSuccess;
+  long long maxnb = 0;
+  for (int s = 0; s < g.S; ++s) maxnb = g.n[s] / BLK > maxnb ? g.n[s] / BLK : maxnb;
+  const long long parts = (maxnb + cb.wg_blocks - 1) / cb.wg_blocks * CAND_PARTS;
+  int lds_ints = (int)(parts < CAND_MAX_PARTS ? parts : CAND_MAX_PARTS);
+  lds_ints = lds_ints > FUSED_MAX_K ? lds_ints : FUSED_MAX_K;
+  CandArgs a{g, k, cb, idx, lds_ints};
+  const size_t lds = (size_t)lds_ints * sizeof(int) * CS_WAVES;
+  cand_select_kernel<<<(unsigned)((heads + CS_WAVES - 1) / CS_WAVES), CS_WAVES * 64, lds, st>>>(a);
   return hipGetLastError();
 }
 
