@@ -216,6 +216,18 @@ __device__ __forceinline__ uint32_t wave_max_dpp(uint32_t v) {
             mx((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48)));
 }
 
+// bits at and below the highest set bit of x (0 for x == 0), by smearing
+// (no leading-zero count and no select on x == 0, both of which have
+// compiled to scalar code testing the wrong condition)
+__device__ __forceinline__ uint32_t low_mask(uint32_t x) {
+  x |= x >> 1;
+  x |= x >> 2;
+  x |= x >> 4;
+  x |= x >> 8;
+  x |= x >> 16;
+  return x;
+}
+
 struct ThreshArgs {
   Geom g;
   int k;
@@ -268,18 +280,21 @@ __global__ __launch_bounds__(TK_THREADS) void threshold_kernel(ThreshArgs a) {
 }
 
 // The same threshold with the sample in registers (NPT keys a thread, the
-// sample of every head of the launch at most 256 * NPT): the largest key T
-// with at least r valid keys >= T, found bit by bit from the top.  The top 16
-// bits are probed over every key (each count reduced over the wavefronts
-// through LDS, two slots, so one barrier a probe); the keys sharing those 16
-// bits are then compacted into LDS and the low 16 bits probed over them alone
-// (over every key again if more than TH_CAP share them).
+// sample of every head of the launch at most 256 * NPT): T, the largest key
+// with at least r valid keys >= T.  When r <= 64, each wavefront first takes
+// the r-th largest of its lanes' largest keys: r keys of that wavefront alone
+// are at or above it, so it is at most T, and so is the largest of the four.
+// The keys at or above that bound (a few r) are compacted into LDS and T is
+// found bit by bit from the top over them alone.  Otherwise (or when more than
+// TH_CAP keys pass the bound) every bit is probed over all keys, each count
+// reduced over the wavefronts through LDS (two slots, so one barrier a probe).
 constexpr int TH_THREADS = 256;
 constexpr int TH_CAP = 1024;
 
 template <int NPT>
 __global__ __launch_bounds__(TH_THREADS) void threshold_reg_kernel(ThreshArgs a) {
   __shared__ int part[2][TH_THREADS / 64];
+  __shared__ uint32_t bound[TH_THREADS / 64];
   __shared__ uint32_t near[TH_CAP];
   __shared__ int nnear;
   const int G = a.g.G;
@@ -317,11 +332,13 @@ __global__ __launch_bounds__(TH_THREADS) void threshold_reg_kernel(ThreshArgs a)
         f[q] = sc[i < len ? i : 0];
       }
       uint32_t key[NPT];
+      uint32_t mx = 0u;
 #pragma unroll
       for (int q = 0; q < NPT; ++q) {
         const long long i = (long long)q * TH_THREADS + tid;
         const long long t = (i / glen) * gtok + i % glen;
         key[q] = (i < len && t >= 4 && t < hi) ? order_key(f[q]) : 0u;
+        mx = key[q] > mx ? key[q] : mx;
       }
       if (tid == 0) nnear = 0;
       int slot = 0;
@@ -343,39 +360,76 @@ __global__ __launch_bounds__(TH_THREADS) void threshold_reg_kernel(ThreshArgs a)
         slot ^= 1;
         return tot;
       };
-      uint32_t T = 0u;
-      for (int b = 31; b >= 16; --b) {
-        const uint32_t t = T | (1u << b);
-        if (block_count(t) >= r) T = t;
-      }
-      const long long above = T >= 0xFFFF0000u ? 0 : block_count(T + 0x10000u);
-      // the keys with T's top 16 bits
-#pragma unroll
-      for (int q = 0; q < NPT; ++q) {
-        const bool nr = (key[q] & 0xFFFF0000u) == T && key[q] != 0u;
-        const uint64_t mk = __ballot(nr);
-        if (mk != 0ull) {
-          int base = 0;
-          if (lane == 0) base = atomicAdd(&nnear, __popcll(mk));
-          base = __shfl(base, 0);
-          const int pos = base + (int)__builtin_amdgcn_mbcnt_hi(
-                                     (uint32_t)(mk >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mk, 0u));
-          if (nr && pos < TH_CAP) near[pos] = key[q];
+      // the lower bound (0 when r > 64: no cut)
+      uint32_t lw = 0u;
+      if (r <= 64) {
+        for (int b = 31; b >= 0; --b) {
+          const uint32_t t = lw | (1u << b);
+          if (__popcll(__ballot(mx >= t)) >= r) lw = t;
         }
       }
+      if (lane == 0) bound[wave] = lw;
       __syncthreads();
+      uint32_t L = 0u;
+#pragma unroll
+      for (int x = 0; x < TH_THREADS / 64; ++x) L = bound[x] > L ? bound[x] : L;
+      uint32_t T = 0u;
+      if (L != 0u) {
+        // the keys at or above the bound
+#pragma unroll
+        for (int q = 0; q < NPT; ++q) {
+          const bool nr = key[q] >= L;
+          const uint64_t mk = __ballot(nr);
+          if (mk != 0ull) {
+            int base = 0;
+            if (lane == 0) base = atomicAdd(&nnear, __popcll(mk));
+            base = __shfl(base, 0);
+            const int pos = base + (int)__builtin_amdgcn_mbcnt_hi(
+                                       (uint32_t)(mk >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mk, 0u));
+            if (nr && pos < TH_CAP) near[pos] = key[q];
+          }
+        }
+        __syncthreads();
+      }
       const int nn = nnear;
-      if (nn <= TH_CAP) {
-        // every wavefront finishes the same search over the compacted keys
-        const long long rr = r - above;
-        for (int b = 15; b >= 0; --b) {
+      if (L != 0u && nn <= 256) {
+        // every wavefront finishes the same search over the compacted keys,
+        // four a lane in registers (0 past nn, below every probe); T >= L,
+        // so the bits above the highest one where L and the largest compacted
+        // key differ are L's
+        uint32_t nk[4];
+        uint32_t hk = 0u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int i = lane + 64 * j;
+          nk[j] = i < nn ? near[i] : 0u;
+          hk = nk[j] > hk ? nk[j] : hk;
+        }
+        hk = wave_max_dpp(hk);
+        const uint32_t low = low_mask(L ^ hk);
+        T = L & ~low;
+        for (int b = __popc(low) - 1; b >= 0; --b) {
+          const uint32_t t = T | (1u << b);
+          int c = 0;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) c += __popcll(__ballot(nk[j] >= t));
+          if (c >= r) T = t;
+        }
+      } else if (L != 0u && nn <= TH_CAP) {
+        // the same with the keys read from LDS at every probe
+        uint32_t hk = 0u;
+        for (int i = lane; i < nn; i += 64) hk = near[i] > hk ? near[i] : hk;
+        hk = wave_max_dpp(hk);
+        const uint32_t low = low_mask(L ^ hk);
+        T = L & ~low;
+        for (int b = __popc(low) - 1; b >= 0; --b) {
           const uint32_t t = T | (1u << b);
           int c = 0;
           for (int i = lane; i < nn; i += 64) c += near[i] >= t ? 1 : 0;
-          if (wave_sum_dpp(c) >= rr) T = t;
+          if (wave_sum_dpp(c) >= r) T = t;
         }
       } else {
-        for (int b = 15; b >= 0; --b) {
+        for (int b = 31; b >= 0; --b) {
           const uint32_t t = T | (1u << b);
           if (block_count(t) >= r) T = t;
         }
@@ -607,10 +661,9 @@ __global__ __launch_bounds__(CS_WAVES * 64) void cand_select_kernel(CandArgs a) 
 #pragma unroll
     for (int r = 0; r < CS_NPL; ++r) mx = key[r] > mx ? key[r] : mx;
     mx = wave_max_dpp(mx);
-    const uint32_t diff = tkey ^ mx;
-    const int b0 = diff == 0u ? -1 : 31 - __builtin_clz(diff);
-    uint32_t T = b0 < 0 ? tkey : (b0 == 31 ? 0u : tkey & ~((2u << b0) - 1u));
-    for (int b = b0; b >= 0; --b) {
+    const uint32_t low = low_mask(tkey ^ mx);
+    uint32_t T = tkey & ~low;
+    for (int b = __popc(low) - 1; b >= 0; --b) {
       const uint32_t t = T | (1u << b);
       if (wave_count<CS_NPL>(total, [&](int r) { return key[r] >= t; }) >= want) T = t;
     }
