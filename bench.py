@@ -118,7 +118,7 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=20)  # clocks ramp over the first steps
     ap.add_argument("--config", default="c4")
     ap.add_argument("--budget", type=int, default=88)
     ap.add_argument("--no-cpu-baseline", action="store_true")
