@@ -2,9 +2,11 @@
 // of its query heads' winners (Fathom §1: at most G*k rows per KV head;
 // Fathom §2: each head's output is softmax attention over its own set).
 //
-// 1. union_kernel (one workgroup per unit): the G sorted index lists are
-//    merged with a bitonic sort of (token << 3 | head) keys in LDS, runs of
-//    equal tokens collapse to one union row carrying a G-bit head mask.
+// 1. union_kernel (one workgroup per unit): the G index lists, as
+//    (token << 3 | head) keys in LDS, are merged by rank when each is strictly
+//    ascending (as select_topk writes them) and sorted with a bitonic network
+//    otherwise; runs of equal tokens collapse to one union row carrying a
+//    G-bit head mask.
 // 2. attend_kernel (one workgroup per (split of ATT_ROWS union rows, unit)):
 //    every K row of the split is read once, whole and coalesced (16 lanes of a
 //    wavefront per row, 16 bytes a lane, all of a wavefront's loads in flight
@@ -151,15 +153,24 @@ __global__ __launch_bounds__(UNION_THREADS) void union_kernel(UnionArgs a) {
     const uint32_t key = keys[e];
     if (key != 0xFFFFFFFFu && (e == 0 || (keys[e - 1] >> 3) != (key >> 3))) ++own;
   }
-  scan[tid] = own;
-  __syncthreads();
-  for (int off = 1; off < UNION_THREADS; off <<= 1) {
-    const int x = tid >= off ? scan[tid - off] : 0;
-    __syncthreads();
-    scan[tid] += x;
-    __syncthreads();
+  // exclusive prefix of `own` over the workgroup: a scan inside each
+  // wavefront, then the wavefronts' totals
+  const int lane = tid & 63, wv = tid >> 6;
+  int incl = own;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
   }
-  int pos = scan[tid] - own - 1;  // union position of the current run
+  if (lane == 63) scan[wv] = incl;
+  __syncthreads();
+  int before = 0, total = 0;
+  for (int x = 0; x < UNION_THREADS / 64; ++x) {
+    const int t = scan[x];
+    before += x < wv ? t : 0;
+    total += t;
+  }
+  int pos = before + incl - own - 1;  // union position of the current run
   for (int e = e0; e < e0 + per && e < m; ++e) {
     const uint32_t key = keys[e];
     if (key == 0xFFFFFFFFu) break;
@@ -170,7 +181,6 @@ __global__ __launch_bounds__(UNION_THREADS) void union_kernel(UnionArgs a) {
     atomicOr(&masks[pos >> 2], (1u << (key & 7u)) << (8 * (pos & 3)));
   }
   __syncthreads();
-  const int total = scan[UNION_THREADS - 1];
   for (int e = tid; e < total; e += UNION_THREADS)
     a.umask[(long long)u * sel + e] = (uint8_t)(masks[e >> 2] >> (8 * (e & 3)));
   if (tid == 0) a.ucount[u] = total;
@@ -296,6 +306,12 @@ __global__ __launch_bounds__(ATT_THREADS) void attend_kernel(AttArgs a) {
       if (ch == 0) p[r][h] = ((mask >> h) & 1) ? d * a.scale : -INFINITY;
     }
   }
+  // the V rows (same mapping), in flight during the softmax reductions
+  uint4 vv[IT];
+#pragma unroll
+  for (int it = 0; it < IT; ++it)
+    vv[it] = *reinterpret_cast<const uint4*>(
+        a.v_rows + (gu * a.g.cap + rows[RPW * wave + 4 * it + rs]) * D + 8 * ch);
   __syncthreads();
 
   // ---- per-head max and exp-sum over the split (thread tid <-> row tid) ----
@@ -331,12 +347,8 @@ __global__ __launch_bounds__(ATT_THREADS) void attend_kernel(AttArgs a) {
     sum[h] = v;
   }
 
-  // ---- V: the same row mapping; lane accumulates its 8 channels per head ----
-  uint4 vv[IT];
-#pragma unroll
-  for (int it = 0; it < IT; ++it)
-    vv[it] = *reinterpret_cast<const uint4*>(
-        a.v_rows + (gu * a.g.cap + rows[RPW * wave + 4 * it + rs]) * D + 8 * ch);
+  // ---- V (loaded above): the same row mapping; lane accumulates its 8
+  // channels per head ----
   float o[G][8];
 #pragma unroll
   for (int h = 0; h < G; ++h)
