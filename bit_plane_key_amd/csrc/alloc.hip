@@ -40,16 +40,25 @@ __global__ __launch_bounds__(64) void alloc_kernel(AllocArgs a) {
     const int l = a.g.l0 + (u / a.g.H) % a.g.nl;
     const int hh = u % a.g.H;
     const float* r = a.rot + (long long)(l * a.g.H + hh) * D * D;
-    // q'_j = sum_d R[d][j] q_d, exact fp64 products added in ascending d
+    // q'_j = sum_d R[d][j] q_d, exact fp64 products added in ascending d;
+    // each row of R is read once for every head (lane: columns 2 lane, +1)
+    double acc[G][2];
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int j = 2 * lane + c;
+    for (int h = 0; h < G; ++h) acc[h][0] = acc[h][1] = 0.0;
+#pragma unroll 8
+    for (int d = 0; d < D; ++d) {
+      const float2 rv = *reinterpret_cast<const float2*>(r + d * D + 2 * lane);
+#pragma unroll
       for (int h = 0; h < G; ++h) {
-        double acc = 0.0;
-        for (int d = 0; d < D; ++d) acc = __dadd_rn(acc, (double)r[d * D + j] * (double)sq[h][d]);
-        qb[h][c] = (float)acc;
+        const double qd = (double)sq[h][d];
+        acc[h][0] = __dadd_rn(acc[h][0], (double)rv.x * qd);
+        acc[h][1] = __dadd_rn(acc[h][1], (double)rv.y * qd);
       }
     }
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) qb[h][c] = (float)acc[h][c];
   }
   float* qbo = a.q_basis + (long long)u * G * D;
 #pragma unroll
