@@ -285,11 +285,12 @@ __global__ __launch_bounds__(TK_THREADS) void threshold_kernel(ThreshArgs a) {
 // the r-th largest of its lanes' largest keys: r keys of that wavefront alone
 // are at or above it, so it is at most T, and so is the largest of the four.
 // The keys at or above that bound (a few r) are compacted into LDS and T is
-// found bit by bit from the top over them alone.  Otherwise (or when more than
-// TH_CAP keys pass the bound) every bit is probed over all keys, each count
-// reduced over the wavefronts through LDS (two slots, so one barrier a probe).
+// found bit by bit from the top over them alone, four a lane in registers.
+// Otherwise (r > 64, or more than TH_CAP keys pass the bound, as when r is
+// close to 64) every bit is probed over all keys, each count reduced over the
+// wavefronts through LDS (two slots, so one barrier a probe).
 constexpr int TH_THREADS = 256;
-constexpr int TH_CAP = 1024;
+constexpr int TH_CAP = 256;  // compacted keys searched in registers (4 a lane)
 
 template <int NPT>
 __global__ __launch_bounds__(TH_THREADS) void threshold_reg_kernel(ThreshArgs a) {
@@ -392,7 +393,7 @@ __global__ __launch_bounds__(TH_THREADS) void threshold_reg_kernel(ThreshArgs a)
         __syncthreads();
       }
       const int nn = nnear;
-      if (L != 0u && nn <= 256) {
+      if (L != 0u && nn <= TH_CAP) {
         // every wavefront finishes the same search over the compacted keys,
         // four a lane in registers (0 past nn, below every probe); T >= L,
         // so the bits above the highest one where L and the largest compacted
@@ -414,19 +415,6 @@ __global__ __launch_bounds__(TH_THREADS) void threshold_reg_kernel(ThreshArgs a)
 #pragma unroll
           for (int j = 0; j < 4; ++j) c += __popcll(__ballot(nk[j] >= t));
           if (c >= r) T = t;
-        }
-      } else if (L != 0u && nn <= TH_CAP) {
-        // the same with the keys read from LDS at every probe
-        uint32_t hk = 0u;
-        for (int i = lane; i < nn; i += 64) hk = near[i] > hk ? near[i] : hk;
-        hk = wave_max_dpp(hk);
-        const uint32_t low = low_mask(L ^ hk);
-        T = L & ~low;
-        for (int b = __popc(low) - 1; b >= 0; --b) {
-          const uint32_t t = T | (1u << b);
-          int c = 0;
-          for (int i = lane; i < nn; i += 64) c += near[i] >= t ? 1 : 0;
-          if (wave_sum_dpp(c) >= r) T = t;
         }
       } else {
         for (int b = 31; b >= 0; --b) {
