@@ -47,26 +47,39 @@ TRAFFIC_SOURCES = ("bit_plane_key_amd/csrc/scan.hip", "bit_plane_key_amd/csrc/sc
                    "bit_plane_key_amd/csrc/bpk_internal.h")
 
 
-def counted_traffic(config: str, budget: int):
-    """HBM bytes per scan launch from the committed counter summary of this
-    workload, or None when there is none or the scan's source has changed
-    since the counters were taken."""
+def profile_field(name: str, key: str):
+    """A value from a committed counter summary under profiles/, or None when
+    there is none or the scan's source has changed since it was taken."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", f"scan_cand_kernel_{config}_P{budget}_hbm_bytes.md")
+    path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None
     fields = {}
     for line in open(path):
-        if ":" in line and not line.startswith(("|", "#", " ")):
-            key, _, val = line.partition(":")
-            fields[key.strip()] = val.strip()
+        if ":" in line and not line.startswith(("|", "#", " ", "*")):
+            k, _, val = line.partition(":")
+            fields[k.strip()] = val.strip()
     h = hashlib.sha256()
     for f in TRAFFIC_SOURCES:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
-    if fields.get("kernel_source_sha256") != h.hexdigest():
+    if fields.get("kernel_source_sha256") != h.hexdigest() or key not in fields:
         return None
-    return int(fields["traffic_bytes_per_launch"])
+    return fields[key]
+
+
+def counted_traffic(config: str, budget: int):
+    """HBM bytes per scan launch (FETCH_SIZE + WRITE_SIZE, scaled)."""
+    v = profile_field(f"scan_cand_kernel_{config}_P{budget}_hbm_bytes.md", "traffic_bytes_per_launch")
+    return None if v is None else int(v)
+
+
+def counted_valu(config: str, budget: int):
+    """(VALU busy %, VALU instructions per 64-token block) of the scan launch."""
+    name = f"scan_cand_kernel_{config}_P{budget}_sq_counters.md"
+    busy = profile_field(name, "valu_busy_percent")
+    per = profile_field(name, "valu_insts_per_block")
+    return (None if busy is None else float(busy)), (None if per is None else float(per))
 
 
 def time_launches(fn, steps: int):
@@ -265,6 +278,8 @@ def main() -> int:
             "unit": "GB/s",
             "frac": round(scan_gbs / HBM_PEAK_GBS, 4),
             "traffic": counted_traffic(cfg.name, budget),
+            "valu_busy_percent": counted_valu(cfg.name, budget)[0],
+            "valu_insts_per_block": counted_valu(cfg.name, budget)[1],
             "kernel": "scan_fast_kernel<4, 2, true, 96> (the decode step's candidate scan)",
             "bytes_per_launch": sbytes,
             "avg_launch_us": round(ms_scan * 1e3, 2),
