@@ -10,18 +10,20 @@
 // ties.  The winners are collected into LDS, sorted ascending with a bitonic
 // network and written out.
 //
-// decode_step's fused selection adds two kernels on the same machinery:
-// * threshold_kernel: per (unit, head), the r-th largest of the sampled
-//   scores of candidate tokens, with r chosen so that about 2 (k - 4 - W)
-//   tokens of the whole range are expected at or above it (plus 8 for the
-//   sampling noise of small r);
-// * cand_select_kernel: per (unit, head), the exact top (k - 4 - W) of the
-//   candidates (every token at or above the threshold, and possibly a few just
-//   below it, so the k - 4 - W largest of the whole range are among them
-//   whenever at least that many are at or above it), by a bitonic sort of
-//   (score key, complemented index) pairs.  A head with too few candidates at
-//   or above the threshold, or more than the buffer holds, flags its unit for
-//   the full scan and radix select.
+// decode_step's fused selection adds two kernels:
+// * threshold_reg_kernel (threshold_kernel, on the radix machinery, for
+//   samples over 16384 scores): per (unit, head), the r-th largest of the
+//   sampled scores of candidate tokens, with r chosen so that about
+//   2 (k - 4 - W) tokens of the whole range are expected at or above it (plus
+//   8 for the sampling noise of small r);
+// * cand_select_kernel: per (unit, head), one wavefront takes the exact top
+//   (k - 4 - W) of the candidates (every token at or above the threshold, and
+//   possibly a few just below it, so the k - 4 - W largest of the whole range
+//   are among them whenever at least that many are at or above it) by a
+//   bit-by-bit counting search over its register-resident keys, and sorts the
+//   winners by index.  A head with too few candidates at or above the
+//   threshold, or more than the buffers hold, flags its unit for the full scan
+//   and radix select.
 #include <limits.h>
 
 #include "bpk_internal.h"
