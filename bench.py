@@ -94,7 +94,7 @@ def time_launches(fn, steps: int):
     return start.elapsed_time(end) / steps  # ms
 
 
-def cpu_baseline(cfg, cache, budget: int, tokens: int, units):
+def cpu_baseline(cfg, cache, budget: int, tokens: int, units, n: int, step_units: int):
     """The oracle's scan (depth allocation + prefix-plane scores) timed on one
     host core over a bounded sample of the workload: the first ``tokens``
     tokens of each of ``units``.  The sample's key rows are the generator's
@@ -119,8 +119,14 @@ def cpu_baseline(cfg, cache, budget: int, tokens: int, units):
             O.scan_scores(q, depth, planes, scales, tokens)
             total_s += time.perf_counter() - t0
             total_bytes += O.scan_bytes_unit(depth, tokens)
+    per_unit_s = total_s / len(units)
     return {"value": round(total_bytes / total_s / 1e9, 4), "unit": "GB/s", "cores": 1,
             "kind": "oracle",
+            "keys_per_s": round(tokens * len(units) / total_s, 1),
+            "per_unit_ms": round(per_unit_s * 1e3, 2),
+            # the sample's per-unit time scaled to every unit of the step and
+            # all n tokens: an extrapolation, not a measurement
+            "step_s_extrapolated": round(per_unit_s * (n / tokens) * step_units, 2),
             "sample": (f"oracle depth allocation + scan of {len(units)} units (sequence 0, "
                        f"layers {sorted({u[1] for u in units})}, all KV heads) of the same "
                        f"workload, first {tokens} tokens each, P={budget}, one thread; "
@@ -297,7 +303,7 @@ def main() -> int:
         log("timing the oracle on a CPU sample")
         sample_units = [(0, l, h) for l in range(min(args.cpu_layers, L)) for h in range(cfg.heads)]
         result["cpu_baseline"] = cpu_baseline(cfg, cache, budget, min(args.cpu_tokens, n),
-                                              sample_units)
+                                              sample_units, n, cfg.units)
     print(json.dumps(result), flush=True)
     return 0
 
