@@ -100,6 +100,8 @@ struct FastSmem {
   uint8_t rowp[RM];                               // plane of each plane row
   uint8_t chj[RM];                                // channel of each read channel
   int ccount[GP];                                 // candidates of this workgroup per head
+  float qa8[GP][128];                             // |q_hj| 8 of read channel c (0 past the read ones)
+  float theta[GP];                                // candidate threshold of each head
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -333,63 +335,114 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : (RM <= RM_SMALL ? 3 : 2)
     }
   };
 
-  // the thresholds of this wavefront's heads (w, w + 4), read once, and
-  // |q_hj| 8 of the read channels lane, lane + 64
-  float theta_k[HG];
-  float qa8[HG][2];
-#pragma unroll
-  for (int k = 0; k < HG; ++k) {
-    const int h = wave + 4 * k;
-    theta_k[k] = (MODE == SCAN_CAND && h < G) ? key_to_float(a.thresh[(long long)u * G + h]) : 0.f;
-#pragma unroll
-    for (int cc = 0; cc < 2; ++cc) {
-      const int c = lane + 64 * cc;
-      qa8[k][cc] = (h < G && c < CR) ? fabsf(sm.q[h][sm.chj[c]]) * 8.f : 0.f;
+  // Frames of a step.  With 16-byte plane loads (VEC) one wavefront computes
+  // them for every head: 16-lane row r takes head 4 k + r, and lane b of the
+  // row takes block b of the step and the read channels 8 b .. 8 b + 7; the
+  // thresholds of the heads and |q_hj| 8 of every head and read channel go to
+  // LDS once (seen by the frames after the prologue's barrier).  Otherwise
+  // (more registers live) wavefront w computes those of its heads w, w + 4
+  // from registers: the threshold, and |q_hj| 8 of read channels lane,
+  // lane + 64.
+  if constexpr (VEC) {
+    if (tid < FastSmem<HG, RM>::GP)
+      sm.theta[tid] = (MODE == SCAN_CAND && tid < G) ? key_to_float(a.thresh[(long long)u * G + tid]) : 0.f;
+    for (int e = tid; e < FastSmem<HG, RM>::GP * 128; e += SCAN_THREADS) {
+      const int h = e >> 7, c = e & 127;
+      sm.qa8[h][c] = (h < G && c < CR) ? fabsf(sm.q[h][sm.chj[c]]) * 8.f : 0.f;
     }
   }
-
-  // ---- frames of step i: wavefront w handles heads w, w + 4 ----
-  auto compute_frame = [&](int i) {
-    const int par = i & 1, b3 = i % 3, gblk = step_blocks(i);
+  float theta_k[VEC ? 1 : HG];
+  float qa8[VEC ? 1 : HG][2];
+  if constexpr (!VEC) {
 #pragma unroll
     for (int k = 0; k < HG; ++k) {
       const int h = wave + 4 * k;
-      if (h >= G) continue;  // wavefront-uniform
-      uint32_t key = 0;
+      theta_k[k] = (MODE == SCAN_CAND && h < G) ? key_to_float(a.thresh[(long long)u * G + h]) : 0.f;
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {
         const int c = lane + 64 * cc;
-        if (cc == 1 && CR <= 64) break;  // uniform
-        const float v = qa8[k][cc] * (c < CR ? sm.smax[b3][c] : 0.f);
-        const uint32_t kk = v > 0.f ? (__float_as_uint(v) & 0xFFFFFF00u) | (uint32_t)c : 0u;
-        key = kk > key ? kk : key;
+        qa8[k][cc] = (h < G && c < CR) ? fabsf(sm.q[h][sm.chj[c]]) * 8.f : 0.f;
       }
-      key = wave_max_u32_dpp(key);
-      // an upper bound of the largest |q| 8 smax, and the channel that reaches it
-      const float best = key ? __uint_as_float((key & 0xFFFFFF00u) + 0x100u) : 0.f;
-      const int cs = (int)(key & 0xFFu);
-      const int E = frame_exp(best, lx);
-      int eb = E;
-      bool own = false;
-      if (lane < gblk && best > 0.f) {
-        // the block's own largest weight is at least a quarter of the frame's
-        // if the channel that sets the frame keeps a quarter of its step max
-        if (4.f * half_bits_to_f32(sm.sc[b3][cs][lane]) < sm.smax[b3][cs]) {
-          float mb = 0.f;
-          for (int c = 0; c < CR; ++c)
-            mb = fmaxf(mb, fabsf(sm.q[h][sm.chj[c]]) * 8.f * half_bits_to_f32(sm.sc[b3][c][lane]));
-          eb = frame_exp(mb, lx);
-          own = eb != E;
+    }
+  }
+
+  // the frame of (head h, block blk): E of the step (from the largest key,
+  // value bits and read channel, over the head's read channels), the block's
+  // own exponent, and the candidate test threshold
+  auto frame_write = [&](int par, int b3, int gblk, int h, int blk, uint32_t key, float theta,
+                         bool& own) {
+    // an upper bound of the largest |q| 8 smax, and the channel that reaches it
+    const float best = key ? __uint_as_float((key & 0xFFFFFF00u) + 0x100u) : 0.f;
+    const int cs = (int)(key & 0xFFu);
+    const int E = frame_exp(best, lx);
+    int eb = E;
+    own = false;
+    if (blk < gblk && best > 0.f) {
+      // the block's own largest weight is at least a quarter of the frame's
+      // if the channel that sets the frame keeps a quarter of its step max
+      if (4.f * half_bits_to_f32(sm.sc[b3][cs][blk]) < sm.smax[b3][cs]) {
+        float mb = 0.f;
+        for (int c = 0; c < CR; ++c)
+          mb = fmaxf(mb, fabsf(sm.q[h][sm.chj[c]]) * 8.f * half_bits_to_f32(sm.sc[b3][c][blk]));
+        eb = frame_exp(mb, lx);
+        own = eb != E;
+      }
+    }
+    if (h < G && blk < GB) {
+      sm.ex[par][h][blk] = eb;
+      if constexpr (MODE == SCAN_CAND) sm.tlo[par][h][blk] = cand_threshold(theta, eb);
+    }
+    return E;
+  };
+
+  // ---- frames of step i (VEC: by the calling wavefront for every head;
+  // otherwise its own heads); every lane of the wavefront must be active ----
+  auto compute_frame = [&](int i) {
+    const int par = i & 1, b3 = i % 3, gblk = step_blocks(i);
+    if constexpr (VEC) {
+      const int frow = lane >> 4, fblk = lane & 15;
+#pragma unroll
+      for (int k = 0; k < HG; ++k) {
+        const int h = 4 * k + frow;  // heads past G compute zeros and write nothing
+        uint32_t key = 0;
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          const int c = 8 * fblk + m;
+          const float v = sm.qa8[h][c] * (c < CR ? sm.smax[b3][c] : 0.f);
+          const uint32_t kk = v > 0.f ? (__float_as_uint(v) & 0xFFFFFF00u) | (uint32_t)c : 0u;
+          key = kk > key ? kk : key;
+        }
+        key = row_max_u32_dpp(key);
+        bool own;
+        const int E = frame_write(par, b3, gblk, h, fblk, key, sm.theta[h], own);
+        const uint64_t ob = __ballot(own);
+        if (h < G && fblk == 0) {
+          sm.exh[par][h] = E;
+          sm.own[par][h] = ((ob >> (16 * frow)) & 0xFFFFull) != 0ull;
         }
       }
-      if (lane < GB) {
-        sm.ex[par][h][lane] = eb;
-        if constexpr (MODE == SCAN_CAND) sm.tlo[par][h][lane] = cand_threshold(theta_k[k], eb);
-      }
-      const bool any_own = __ballot(own) != 0ull;
-      if (lane == 0) {
-        sm.exh[par][h] = E;
-        sm.own[par][h] = any_own;
+    } else {
+#pragma unroll
+      for (int k = 0; k < HG; ++k) {
+        const int h = wave + 4 * k;
+        if (h >= G) continue;  // wavefront-uniform
+        uint32_t key = 0;
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+          const int c = lane + 64 * cc;
+          if (cc == 1 && CR <= 64) break;  // uniform
+          const float v = qa8[k][cc] * (c < CR ? sm.smax[b3][c] : 0.f);
+          const uint32_t kk = v > 0.f ? (__float_as_uint(v) & 0xFFFFFF00u) | (uint32_t)c : 0u;
+          key = kk > key ? kk : key;
+        }
+        key = wave_max_u32_dpp(key);
+        bool own;
+        const int E = frame_write(par, b3, gblk, h, lane, key, theta_k[k], own);
+        const bool any_own = __ballot(own) != 0ull;
+        if (lane == 0) {
+          sm.exh[par][h] = E;
+          sm.own[par][h] = any_own;
+        }
       }
     }
   };
@@ -750,7 +803,7 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : (RM <= RM_SMALL ? 3 : 2)
     write_scales(0);
     issue_scales(1);
     __syncthreads();
-    compute_frame(0);
+    if (!VEC || wave == 0) compute_frame(0);
 
     // ---- steps: the loads of step i + 1 (planes) and i + 2 (scales) are in
     // flight while step i is computed ----
@@ -760,7 +813,7 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : (RM <= RM_SMALL ? 3 : 2)
       __syncthreads();  // planes of i, scales of i + 1 and frames of i are in LDS
       issue_planes(i + 1);
       issue_scales(i + 2);
-      if (i + 1 < nsteps) compute_frame(i + 1);
+      if (i + 1 < nsteps && (!VEC || wave == ((i + 1) & 3))) compute_frame(i + 1);  // VEC: by turns
       blocks(i);
     }
     if constexpr (MODE == SCAN_CAND) {

@@ -89,6 +89,17 @@ __device__ __forceinline__ uint32_t wave_max_u32_dpp(uint32_t v) {
   return mx(mx(r0, r1), mx(r2, r3));
 }
 
+// the same maximum within each 16-lane row, in every lane of the row (every
+// lane of the row must be active)
+__device__ __forceinline__ uint32_t row_max_u32_dpp(uint32_t v) {
+  auto mx = [](uint32_t a, uint32_t b) { return a > b ? a : b; };
+  v = mx(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
+  v = mx(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
+  v = mx(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));
+  v = mx(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));
+  return v;
+}
+
 // value of the neighbouring lane (lane ^ 1)
 __device__ __forceinline__ uint32_t lane_xor1(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);
