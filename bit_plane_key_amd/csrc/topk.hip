@@ -196,18 +196,9 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(TopkArgs a) {
   sort_and_write(sm.buf, k, out);
 }
 
-// sum over the wavefront (DPP inside each 16-lane row, then the four rows'
-// results read out); every lane must be active
-__device__ __forceinline__ int wave_sum_dpp(int v) {
-  v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);   // quad_perm xor 1
-  v += __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);   // quad_perm xor 2
-  v += __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);  // row_half_mirror
-  v += __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false);  // row_mirror
-  return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) +
-         __builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48);
-}
-
-// maximum over the wavefront, the same way
+// maximum over the wavefront: DPP inside each 16-lane row (quad_perm xor 1,
+// xor 2, row_half_mirror, row_mirror), then the four rows' results read out;
+// every lane must be active
 __device__ __forceinline__ uint32_t wave_max_dpp(uint32_t v) {
   auto mx = [](uint32_t x, uint32_t y) { return x > y ? x : y; };
   v = mx(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
