@@ -198,6 +198,75 @@ def test_alloc_gain_sums_group_heads():
     assert list(t) == [0, 1, 0, 0]
 
 
+def test_gain_is_channel_share_of_score_variance(rng):
+    """Fathom §1 observation 1: g_j is channel j's contribution to the score
+    variance, here summed over the heads that share the KV head [ReadKV §5.2].
+
+    Monte Carlo with independent channels k_j ~ N(0, sigma_j^2), sigma_j far
+    from 1: the empirical sum over heads of Var_i(q_hj k_ij) must match g_j,
+    and the shares must add up to the summed variance of the real scores."""
+    sigma = np.array([0.3, 0.55, 1.0, 1.7, 2.6, 4.0], dtype=np.float64)
+    q = np.array([[0.9, -1.6, 0.2, 0.05, -0.7, 0.3],
+                  [-0.4, 0.1, 1.3, -0.2, 0.0, -0.35],
+                  [1.8, 0.6, -0.5, 0.9, 0.25, 0.1],
+                  [0.0, -0.3, 0.8, 1.1, -0.15, 0.2]], dtype=np.float32)
+    var = (sigma ** 2).astype(np.float32)
+    g = O.channel_gains(q, var).astype(np.float64)
+    n = 400_000
+    k = rng.standard_normal((n, 6)) * sigma
+    qd = q.astype(np.float64)
+    share = np.array([sum(np.var(qd[h, j] * k[:, j]) for h in range(4)) for j in range(6)])
+    np.testing.assert_allclose(g, share, rtol=0.02)
+    total = sum(np.var(k @ qd[h]) for h in range(4))
+    assert abs(g.sum() - total) <= 0.02 * total
+
+
+def test_gain_predicts_next_plane_error_drop(rng):
+    """Fathom §1 observation 1: one more plane of channel j cuts the summed
+    squared score error by an amount proportional to g_j 4^-t_j.  Measured on
+    the oracle's own encoder: at each depth the drop divided by g_j must be the
+    same for every channel (the quantizer is scale-free), so a gain that weighs
+    sigma instead of sigma^2, or |q| instead of q^2, fails."""
+    sigma = np.array([0.25, 1.0, 3.0, 0.6], dtype=np.float64)
+    q = np.array([[1.5, -0.2, 0.4, 0.0],
+                  [0.3, 0.9, -0.1, 2.0],
+                  [-0.6, 0.4, 0.05, 0.7],
+                  [0.2, -1.2, 0.3, 0.1]], dtype=np.float32)
+    g = O.channel_gains(q, (sigma ** 2).astype(np.float32)).astype(np.float64)
+    n = 64 * 2048
+    keys = (rng.standard_normal((n, 4)) * sigma).astype(np.float32)
+    planes, scales = O.encode_unit(keys)
+    blocks = np.arange(n // 64)
+    qd = q.astype(np.float64)
+    err = np.zeros((4, 5))
+    for j in range(4):
+        s = np.repeat(scales[j].astype(np.float64), 64)
+        for t in range(5):
+            rec = s * O.prefix_values(O.codes_from_planes(planes, t, j, blocks), t)
+            e2 = np.mean((keys[:, j].astype(np.float64) - rec) ** 2)
+            err[j, t] = e2 * float(np.sum(qd[:, j] ** 2))   # summed over heads
+    for t in range(1, 4):
+        ratio = (err[:, t] - err[:, t + 1]) / (g * 0.25 ** t)
+        assert ratio.max() <= 1.03 * ratio.min(), (t, ratio)
+
+
+def test_gain_two_channel_hand_worked():
+    """Hand-worked: heads (3, 2) and (0, 2) on channels 0, 1 with variances 4
+    and 1.  Gains: 4 (9 + 0) = 36 and 1 (4 + 4) = 8, so the planes are worth
+    36, 9, 2.25, 0.5625 (channel 0) and 8, 2, 0.5, 0.125 (channel 1).  Taking
+    them in value order gives the depths below.  (With sigma in place of
+    sigma^2, sum |q| in place of sum q^2, or no variance at all, the second
+    plane would go to channel 1.)"""
+    q = np.array([[3.0, 2.0], [0.0, 2.0]], dtype=np.float32)
+    var = np.array([4.0, 1.0], dtype=np.float32)
+    assert list(O.channel_gains(q, var)) == [36.0, 8.0]
+    expect = {0: [0, 0], 1: [1, 0], 2: [2, 0], 3: [2, 1], 4: [3, 1], 5: [3, 2],
+              6: [4, 2], 7: [4, 3], 8: [4, 4], 9: [4, 4]}
+    for p, t in expect.items():
+        assert list(O.alloc_depth(q, var, p)) == t, p
+        assert list(O.alloc_depth_greedy(q, var, p)) == t, p
+
+
 def test_alloc_sort_form_equals_greedy_loop(rng):
     for trial in range(6):
         q = rng.standard_normal((4, 128)).astype(np.float32)
