@@ -18,6 +18,8 @@ from ._lib import (  # noqa: F401
     Cache,
     alloc_depth,
     decode_step,
+    decode_step_noalloc,
+    NOALLOC_SCRATCH_BYTES,
     encode_append,
     last_error,
     scan_scores,

@@ -24,7 +24,7 @@ BPK_OP_SELECT, BPK_OP_ATTEND, BPK_OP_DECODE = 3, 4, 5
 HEAD_DIM, BLOCK, PLANES = 128, 64, 4
 
 EXPORTS = ("bpk_encode_append", "bpk_alloc_depth", "bpk_scan_scores", "bpk_select_topk",
-           "bpk_sparse_attend", "bpk_decode_step", "bpk_workspace_bytes", "bpk_last_error",
+           "bpk_sparse_attend", "bpk_decode_step", "bpk_decode_step_noalloc", "bpk_workspace_bytes", "bpk_last_error",
            "bpk_trace_enable", "bpk_trace_read")
 STAGES = ("alloc", "sample", "threshold", "scan", "select", "fallback", "attend")
 
@@ -68,6 +68,7 @@ def _load() -> ctypes.CDLL:
         "bpk_select_topk": (ctypes.c_int, [C, P, I32, I32, I32, P, P, SZ, P]),
         "bpk_sparse_attend": (ctypes.c_int, [C, P, P, I32, I32, I32, F, P, P, SZ, P]),
         "bpk_decode_step": (ctypes.c_int, [C, P, I32, I32, I32, I32, F, P, P, P, P, SZ, P]),
+        "bpk_decode_step_noalloc": (ctypes.c_int, [C, P, I32, I32, I32, I32, F, P, P, P, P]),
         "bpk_workspace_bytes": (ctypes.c_size_t, [C, I32, I32, I32, I32]),
         "bpk_last_error": (ctypes.c_char_p, []),
         "bpk_trace_enable": (ctypes.c_int, [I32]),
@@ -257,6 +258,27 @@ def decode_step(cache: Cache, q: torch.Tensor, l0: int, l1: int, budget: int, k:
     _check(LIB.bpk_decode_step(cache.struct(), q.data_ptr(), l0, l1, int(budget), int(k),
                                float(softmax_scale), out.data_ptr(), _ptr(depth_out),
                                _ptr(idx_out), ws.data_ptr(), ws.numel(), _stream(stream)))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def decode_step_noalloc(cache: Cache, q: torch.Tensor, l0: int, l1: int, budget: int, k: int,
+                        softmax_scale: float, out: torch.Tensor, depth_out=None, idx_out=None,
+                        stream=None):
+    """decode_step on the library's own scratch array: nothing is allocated,
+    so ``out`` (and the optional outputs) must be given."""
+    u = (cache.S, l1 - l0, cache.H)
+    _need(q, "q", torch.bfloat16, (*u, cache.G, HEAD_DIM))
+    _need(out, "out", torch.float32, (*u, cache.G, HEAD_DIM))
+    if depth_out is not None:
+        _need(depth_out, "depth_out", torch.uint8, (*u, HEAD_DIM))
+    if idx_out is not None:
+        _need(idx_out, "idx_out", torch.int32, (*u, cache.G, k))
+    _check(LIB.bpk_decode_step_noalloc(cache.struct(), q.data_ptr(), l0, l1, int(budget), int(k),
+                                       float(softmax_scale), out.data_ptr(), _ptr(depth_out),
+                                       _ptr(idx_out), _stream(stream)))
     return out
 
 

@@ -4,10 +4,17 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
 #include <string>
 #include <vector>
 
 #include "bpk_internal.h"
+
+// Scratch memory of bpk_decode_step_noalloc: one copy per GPU, held until the
+// process ends.  Host code never uses the array's name as an address (on the
+// host it is only a stand-in): the device address comes from
+// hipGetSymbolAddress, once per device.
+static __device__ __align__(256) char scratch[BPK_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -61,8 +68,8 @@ hipEvent_t trace_event() {
 // call turns tracing off for the rest of the call (results are unaffected).
 class StageTimer {
  public:
-  StageTimer(int stage, hipStream_t st) : st_(st) {
-    if (!g_trace.on) return;
+  StageTimer(int stage, hipStream_t st, bool traced) : st_(st) {
+    if (!traced || !g_trace.on) return;
     rec_.stage = stage;
     rec_.start = trace_event();
     rec_.stop = trace_event();
@@ -267,31 +274,28 @@ int bpk_sparse_attend(const bpk_cache_t* c, const uint16_t* q, const int32_t* id
                     "sparse_attend");
 }
 
-int bpk_decode_step(const bpk_cache_t* c, const uint16_t* q, int32_t l0, int32_t l1,
-                    int32_t budget_planes, int32_t k, float softmax_scale, float* out,
-                    uint8_t* depth_out, int32_t* idx_out, void* ws, size_t ws_bytes,
-                    void* stream) {
-  bpk::Geom g;
-  int rc = check_cache(c, l0, l1, &g);
-  if (rc) return rc;
-  if (!q || !out) return fail(BPK_EINVAL, "q and out must be non-NULL");
-  if (budget_planes < 0) return fail(BPK_EINVAL, "budget_planes < 0");
-  rc = check_k(c, k);
-  if (rc) return rc;
+}  // extern "C"
+
+namespace {
+
+// The decode step on a workspace the caller has checked (ws holds at least
+// decode_ws(g, k).total bytes); `traced` lets stage tracing record events.
+int decode_step_impl(const bpk_cache_t* c, const bpk::Geom& g, const uint16_t* q,
+                     int32_t budget_planes, int32_t k, float softmax_scale, float* out,
+                     uint8_t* depth_out, int32_t* idx_out, char* base, bool traced,
+                     hipStream_t st) {
   const DecodeWs w = decode_ws(g, k);
-  if (!ws || ws_bytes < w.total)
-    return fail(BPK_EWORKSPACE, "workspace of %zu bytes < %zu needed", ws_bytes, w.total);
-  char* base = static_cast<char*>(ws);
   float* q_basis = reinterpret_cast<float*>(base + w.q_basis);
   uint8_t* depth = depth_out ? depth_out : reinterpret_cast<uint8_t*>(base + w.depth);
   float* scores = reinterpret_cast<float*>(base + w.scores);
   int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(base + w.idx);
-  hipStream_t st = static_cast<hipStream_t>(stream);
+  int rc = BPK_OK;
   // alloc_depth hands out exactly min(P, 4D) planes per unit
   const int rows = budget_planes < 4 * bpk::D ? budget_planes : 4 * bpk::D;
-  if (g_trace.on) ++g_trace.calls;
+  if (traced && g_trace.on) ++g_trace.calls;
+  auto timer = [&](int stage) { return StageTimer(stage, st, traced); };
   {
-    StageTimer t(BPK_STAGE_ALLOC, st);
+    auto t = timer(BPK_STAGE_ALLOC);
     rc = hip_status(bpk::launch_alloc(g, q, c->chan_var, c->rot, budget_planes, depth, q_basis, st),
                     "decode_step/alloc");
   }
@@ -311,31 +315,31 @@ int bpk_decode_step(const bpk_cache_t* c, const uint16_t* q, int32_t l0, int32_t
     cb.idx = reinterpret_cast<int32_t*>(base + w.cidx);
     cb.flag = reinterpret_cast<int32_t*>(base + w.flag);
     {
-      StageTimer t(BPK_STAGE_SAMPLE, st);
+      auto t = timer(BPK_STAGE_SAMPLE);
       rc = hip_status(
           bpk::launch_scan_sample(g, q_basis, depth, c->planes, c->scales, cb, rows, st),
           "decode_step/sample scan");
     }
     if (rc) return rc;
     {
-      StageTimer t(BPK_STAGE_THRESHOLD, st);
+      auto t = timer(BPK_STAGE_THRESHOLD);
       rc = hip_status(bpk::launch_threshold(g, k, cb, st), "decode_step/threshold");
     }
     if (rc) return rc;
     {
-      StageTimer t(BPK_STAGE_SCAN, st);
+      auto t = timer(BPK_STAGE_SCAN);
       rc = hip_status(
           bpk::launch_scan_cand(g, q_basis, depth, c->planes, c->scales, k, cb, rows, st),
           "decode_step/scan");
     }
     if (rc) return rc;
     {
-      StageTimer t(BPK_STAGE_SELECT, st);
+      auto t = timer(BPK_STAGE_SELECT);
       rc = hip_status(bpk::launch_cand_select(g, k, cb, idx, st), "decode_step/select");
     }
     if (rc) return rc;
     {
-      StageTimer t(BPK_STAGE_FALLBACK, st);
+      auto t = timer(BPK_STAGE_FALLBACK);
       rc = hip_status(bpk::launch_scan_flagged(g, q_basis, depth, c->planes, c->scales, scores,
                                                cb.flag, rows, st),
                       "decode_step/fallback scan");
@@ -346,21 +350,88 @@ int bpk_decode_step(const bpk_cache_t* c, const uint16_t* q, int32_t l0, int32_t
     if (rc) return rc;
   } else {
     {
-      StageTimer t(BPK_STAGE_SCAN, st);
+      auto t = timer(BPK_STAGE_SCAN);
       rc = hip_status(bpk::launch_scan(g, q_basis, depth, c->planes, c->scales, scores, rows, st),
                       "decode_step/scan");
     }
     if (rc) return rc;
     {
-      StageTimer t(BPK_STAGE_SELECT, st);
+      auto t = timer(BPK_STAGE_SELECT);
       rc = hip_status(bpk::launch_topk(g, scores, k, idx, st), "decode_step/select");
     }
     if (rc) return rc;
   }
-  StageTimer t(BPK_STAGE_ATTEND, st);
+  auto t = timer(BPK_STAGE_ATTEND);
   return hip_status(bpk::launch_attend(g, c->k_dtype, c->k_rows, c->v_rows, q, idx, k,
                                        softmax_scale, out, base + w.attend, st),
                     "decode_step/attend");
+}
+
+// Checks shared by the two decode entry points.
+int check_decode(const bpk_cache_t* c, int32_t l0, int32_t l1, const uint16_t* q,
+                 int32_t budget_planes, int32_t k, const float* out, bpk::Geom* g) {
+  int rc = check_cache(c, l0, l1, g);
+  if (rc) return rc;
+  if (!q || !out) return fail(BPK_EINVAL, "q and out must be non-NULL");
+  if (budget_planes < 0) return fail(BPK_EINVAL, "budget_planes < 0");
+  return check_k(c, k);
+}
+
+// Device address of this device's scratch array (looked up once per device).
+int scratch_address(char** out) {
+  static std::mutex mu;
+  static void* addr[256] = {};
+  int dev = -1;
+  int rc = hip_status(hipGetDevice(&dev), "decode_step_noalloc/hipGetDevice");
+  if (rc) return rc;
+  if (dev < 0 || dev >= 256) return fail(BPK_EUNSUPPORTED, "device %d out of range", dev);
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    rc = hip_status(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)),
+                    "decode_step_noalloc/hipGetSymbolAddress");
+    if (rc) return rc;
+    addr[dev] = p;
+  }
+  *out = static_cast<char*>(addr[dev]);
+  return BPK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int bpk_decode_step(const bpk_cache_t* c, const uint16_t* q, int32_t l0, int32_t l1,
+                    int32_t budget_planes, int32_t k, float softmax_scale, float* out,
+                    uint8_t* depth_out, int32_t* idx_out, void* ws, size_t ws_bytes,
+                    void* stream) {
+  bpk::Geom g;
+  int rc = check_decode(c, l0, l1, q, budget_planes, k, out, &g);
+  if (rc) return rc;
+  const size_t need = decode_ws(g, k).total;
+  if (!ws || ws_bytes < need)
+    return fail(BPK_EWORKSPACE, "workspace of %zu bytes < %zu needed", ws_bytes, need);
+  return decode_step_impl(c, g, q, budget_planes, k, softmax_scale, out, depth_out, idx_out,
+                          static_cast<char*>(ws), true, static_cast<hipStream_t>(stream));
+}
+
+int bpk_decode_step_noalloc(const bpk_cache_t* c, const uint16_t* q, int32_t l0, int32_t l1,
+                            int32_t budget_planes, int32_t k, float softmax_scale, float* out,
+                            uint8_t* depth_out, int32_t* idx_out, void* stream) {
+  bpk::Geom g;
+  int rc = check_decode(c, l0, l1, q, budget_planes, k, out, &g);
+  if (rc) return rc;
+  const size_t need = decode_ws(g, k).total;
+  if (need > (size_t)BPK_NOALLOC_SCRATCH_BYTES)
+    return fail(BPK_EWORKSPACE,
+                "this call needs %zu bytes of scratch; the allocation-free decode step holds "
+                "%zu (use bpk_decode_step with a workspace)",
+                need, (size_t)BPK_NOALLOC_SCRATCH_BYTES);
+  char* base = nullptr;
+  rc = scratch_address(&base);
+  if (rc) return rc;
+  return decode_step_impl(c, g, q, budget_planes, k, softmax_scale, out, depth_out, idx_out, base,
+                          false, static_cast<hipStream_t>(stream));
 }
 
 int bpk_trace_enable(int32_t on) {

@@ -191,6 +191,28 @@ int bpk_decode_step(const bpk_cache_t* cache, const uint16_t* q, int32_t l0, int
                     void* stream);
 
 /*
+ * bpk_decode_step without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, results and errors as
+ * bpk_decode_step; the workspace is instead a scratch array inside the
+ * library, BPK_NOALLOC_SCRATCH_BYTES on each GPU, held until the process ends
+ * (its address is looked up once per device, on the first call with that
+ * device current).  The call allocates nothing.
+ * - It runs on the current device, which must be the device of `stream` and
+ *   of the cache.
+ * - Every call on one GPU shares that GPU's array, which keeps the last call's
+ *   contents: calls that overlap on one GPU (other streams, other threads)
+ *   race and must be serialised by the caller.
+ * Errors: those of bpk_decode_step; BPK_EWORKSPACE when
+ * bpk_workspace_bytes(cache, BPK_OP_DECODE, l0, l1, k) exceeds
+ * BPK_NOALLOC_SCRATCH_BYTES (use bpk_decode_step with a workspace instead).
+ */
+#define BPK_NOALLOC_SCRATCH_BYTES (32u << 20)
+int bpk_decode_step_noalloc(const bpk_cache_t* cache, const uint16_t* q, int32_t l0, int32_t l1,
+                            int32_t budget_planes, int32_t k, float softmax_scale, float* out,
+                            uint8_t* depth_out, int32_t* idx_out, void* stream);
+
+/*
  * Workspace bytes an entry point needs for layers [l0, l1) and top-k k
  * (op = BPK_OP_SELECT, BPK_OP_ATTEND or BPK_OP_DECODE).  Returns 0 for an
  * invalid cache or op.

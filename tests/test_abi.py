@@ -122,6 +122,21 @@ def test_workspace_checked(lib):
     assert lib.LIB.bpk_workspace_bytes(ctypes.pointer(s), lib.BPK_OP_SELECT, 0, 1, 512) == 0
 
 
+def test_noalloc_refuses_more_than_its_scratch(lib):
+    """The allocation-free decode step rejects, before any launch, a call whose
+    workspace would not fit its scratch array; a small call passes the size
+    check (here it then fails on the null q, still before any launch)."""
+    s, n = _cache(lib, n=1 << 20, capacity=1 << 20)
+    need = lib.LIB.bpk_workspace_bytes(ctypes.pointer(s), lib.BPK_OP_DECODE, 0, 2, 512)
+    assert need > lib.NOALLOC_SCRATCH_BYTES
+    rc = lib.LIB.bpk_decode_step_noalloc(ctypes.pointer(s), FAKE, 0, 2, 88, 512, 0.088, FAKE,
+                                         None, None, None)
+    assert rc == -3 and "scratch" in lib.last_error()
+    rc = lib.LIB.bpk_decode_step_noalloc(ctypes.pointer(s), None, 0, 1, 88, 512, 0.088, FAKE,
+                                         None, None, None)
+    assert rc == -1
+
+
 def test_product_has_no_cpu_path():
     """The package never imports the oracle or any CPU implementation."""
     pkg = os.path.join(ROOT, "bit_plane_key_amd")
