@@ -29,6 +29,11 @@ EXPORTS = ("bpk_encode_append", "bpk_alloc_depth", "bpk_scan_scores", "bpk_selec
 STAGES = ("alloc", "sample", "threshold", "scan", "select", "fallback", "attend")
 
 
+def block_stride(capacity: int) -> int:
+    """Words per plane row (and scales per scale row): BPK_BLOCK_STRIDE."""
+    return (capacity // BLOCK + 7) // 8 * 8
+
+
 class BpkError(RuntimeError):
     def __init__(self, code: int, message: str):
         super().__init__(f"bpk error {code}: {message}")
@@ -131,7 +136,7 @@ class Cache:
         kt = torch.float32 if k_dtype == "f32" else torch.bfloat16
         self.k_rows = torch.empty((S, L, H, capacity, D), dtype=kt, device=device)
         self.v_rows = torch.empty((S, L, H, capacity, D), dtype=torch.bfloat16, device=device)
-        nb = capacity // BLOCK
+        nb = block_stride(capacity)
         self.planes = torch.zeros((S, L, H, D, PLANES, nb), dtype=torch.int64, device=device)
         self.scales = torch.zeros((S, L, H, D, nb), dtype=torch.float16, device=device)
         self.chan_var = torch.ones((S, L, H, D), dtype=torch.float32, device=device)

@@ -29,7 +29,9 @@ struct Geom {
     int s = u / (H * nl);
     return ((long long)s * L + l) * H + h;
   }
-  __host__ __device__ long long nbcap() const { return cap / BLK; }
+  // words per plane row (and fp16 scales per scale row): the capacity in
+  // blocks rounded up to a multiple of 8, so every row starts 64-byte aligned
+  __host__ __device__ long long nbcap() const { return BPK_BLOCK_STRIDE(cap); }
 };
 
 // ---- launchers (each returns hipGetLastError() of its launches) ----

@@ -12,30 +12,27 @@
 //   S = sum_r w_r b_r,  C = sum_r w_r.
 // The weights of one 16-block step and head are put in a common fixed-point
 // frame, X_r = round(w_r 2^E) (to nearest, ties to even), with E chosen so
-// that |X_r| < 2^21 and sum_r |X_r| <= 2^29, and each X_r is split into three
-// balanced signed bytes.  S and C are then exact integer contractions of int8
-// digits with 0/1 bits, and the score is s_hat = (2 S - C) 2^-(E+1).  The only
-// rounding is that of X_r (half a unit), far below the 1e-4 tolerance relative
-// to the score's own L1 mass as long as the frame is within a few bits of each
-// block's largest weight.  E comes from max_j |q_hj| 8 smax_j over the step
-// (smax_j = the largest scale of channel j in the step); a block whose own
+// that |X_r| < 2^29, and each X_r is split into four balanced signed bytes
+// (one fp64 fma: w_r 2^E is exact in fp64).  S and C are then exact integer
+// contractions of int8 digits with 0/1 bits, and the score is
+// s_hat = (2 S - C) 2^-(E+1).  E comes from max_j |q_hj| 8 smax_j over the
+// step (smax_j = the largest scale of channel j in the step); a block whose own
 // largest weight may be more than 4x smaller (tested on the channel that sets
-// the frame) gets a frame of its own.  Frames depend only on the step's blocks,
-// so scores are bit-identical in every launch mode.
+// the frame) gets a frame of its own, so every block's largest weight is at
+// least 2^26 units.  Frames depend only on the step's blocks, so scores are
+// bit-identical in every launch mode.
 //
-// The digits come from one fma and one xor-add: for |X| < 2^21,
-// f = X + 2^23 + 0x408080 lies in [2^23, 2^24), where a float's low 23 bits
-// are the integer f - 2^23 = X + 0x408080; flipping bit 7 of the two low bytes
-// and subtracting 0x40 from the third (0x4B40 from the upper half, which also
-// clears the exponent byte up to a borrow) leaves bytes d0, d1 in [-128, 127]
-// and d2 in [-64, 63] with d0 + 2^8 d1 + 2^16 d2 = X.  The fourth byte (0 or
-// -1) only feeds an MFMA output row that is never read.
+// Error bound.  Rounding X_r moves the score by at most sum_r |X_r - w_r 2^E|
+// |b_r - 1/2| <= R/4 units of 2^-E, the fp32 assembly of 2 S - C by at most
+// 4 units plus 2^-23 of the score.  A token's L1 mass sum_j |q_hj s_bj m_ij|
+// is at least the largest weight / 16 (|m| >= 2^(3-t) >= 1/2), so at least
+// 2^22 units, and the error is below (R/4 + 4) 2^-22 + 2^-23 <= 1e-5 of the L1
+// mass for every R <= 128 (the 1e-4 tolerance holds with a factor of 10).
 //
 // The candidate test (decode_step's fused selection) is a cheap superset of
-// "score >= theta": with t = floor(theta 2^(E+1)) - 32 (the float rounding of
-// 2 S - C moves it by at most 32 units), a token passes if
-// S' >= floor((t + C) / 2) - 2^14, where S' is S without its lowest digit row
-// (which is at most 128 R <= 2^14 in magnitude).  Passing tokens are appended
+// "written score >= theta": it drops the two low digit rows of S and C (at
+// most 3 R (2^15 + 2^7) units of 2 S - C) and compares the high halves with a
+// per-(head, block) integer threshold (cand_tau).  Passing tokens are appended
 // with their exact scores; the selection keeps only those at or above theta.
 //
 // Mapping onto gfx950 (fast kernel):
@@ -50,7 +47,8 @@
 // * Wavefront w then takes blocks 4w .. 4w+3 one at a time: it writes the
 //   block's X digits (4 bytes per (row, head)) into its own LDS records and
 //   contracts them with the plane bits on the matrix cores,
-//   v_mfma_i32_16x16x64_i8 (a 32-row remainder with zero upper bytes).  Both
+//   v_mfma_i32_16x16x64_i8 (a 32-row remainder as the same product with
+//   zero A bytes in the upper half of each K group).  Both
 //   operands come from LDS through the transposing read ds_read_b64_tr_b8:
 //   the B bytes are the raw plane words, each byte holding 8 tokens of one
 //   row, and one AND per 4 bytes keeps bit 2c + (n / 8) of column n, so the
@@ -58,9 +56,9 @@
 //   8 (n % 8) + 2c + n / 8 in column n, scaled by 2^(2c + n / 8) (by -2^7 for
 //   bit 7: the int8 byte 0x80 is -128).  A fifth product with all-one bytes
 //   gives C.
-// * Lane l ends with the digit sums of head 4 hg + l / 16 for its token and
-//   recombines them with shifts; one branch per block skips the appends when
-//   no lane passes.
+// * Lane l ends with the four digit sums of head 4 hg + l / 16 for its
+//   token; the candidate test combines the two high ones, and one branch per
+//   block skips the appends when no lane passes.
 #include "scan_common.h"
 
 namespace bpk {
@@ -74,7 +72,6 @@ constexpr int SCS = 20;               // LDS fp16 slots per read channel: 16 blo
 constexpr int RM_SMALL = 96;          // row capacity of the three-workgroups-per-CU variant
 constexpr long long FAST_MAX_CAP = 1ll << 25;   // one unit's planes fit a 32-bit buffer offset
 constexpr int FLAGGED_SPAN = 1024;              // blocks per workgroup of a flagged-units scan
-constexpr float DIGIT_MAGIC = 12615808.f;       // 2^23 + 0x408080
 constexpr uint32_t OUT_OF_RANGE = 0x80000000u;  // a buffer offset past every unit's planes
 constexpr int RSRC_WORD3 = 0x00020000;          // raw (untyped) buffer, 32-bit data format
 
@@ -88,10 +85,11 @@ struct FastSmem {
   static constexpr int GP = 4 * HG;               // heads, padded to whole MFMA row groups
   alignas(16) uint8_t planes[2][RM * PSTRIDE];    // per step parity: [row][block] words
   alignas(16) uint8_t atab[4][RM][16 * HG];       // per wavefront: [row] X digits, 4 bytes a head
+  alignas(16) uint8_t azero[16][16 * HG];         // zero A rows (upper K groups of a 32-row pass)
   alignas(16) uint16_t sc[3][RM][SCS];            // per step mod 3: fp16 scales [read channel][block]
   float smax[3][RM];                              // per step mod 3: largest scale of a read channel
   float q[GP][D];                                 // the unit's query heads (0 beyond G)
-  int tlo[2][GP][GB];                             // per step parity: candidate test threshold of (head, block)
+  int tlo[2][GP][GB];                             // per step parity: cand_tau + 1 of (head, block)
   int ex[2][GP][GB];                              // per step parity: frame exponent of (head, block)
   int exh[2][GP];                                 // per step parity: frame exponent of the step
   int own[2][GP];                                 // per step parity: a block of the head has its own frame
@@ -100,6 +98,7 @@ struct FastSmem {
   uint8_t rowp[RM];                               // plane of each plane row
   uint8_t chj[RM];                                // channel of each read channel
   int ccount[GP];                                 // candidates of this workgroup per head
+  int wcount[4][GP];                              // candidates of each wavefront's part, per head
   float qa8[GP][128];                             // |q_hj| 8 of read channel c (0 past the read ones)
   float theta[GP];                                // candidate threshold of each head
 };
@@ -109,26 +108,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
                                            RSRC_WORD3);
 }
 
-// the three balanced digits of X = round(f s) (|X| < 2^21) in bytes 0..2
-__device__ __forceinline__ uint32_t x_digits(float f, _Float16 s) {
-  const uint32_t b = __float_as_uint(__builtin_fmaf(f, (float)s, DIGIT_MAGIC));
-  uint32_t x;
-  asm("v_xad_u32 %0, %1, %2, %3" : "=v"(x) : "v"(b), "s"(0x8080u), "v"(0xB4C00000u));
-  return x;
-}
-
-// t - 2^15 of the candidate test, with t clamped to just outside the range of
-// 2 S - C (|2 S - C| <= 2^29)
-__device__ __forceinline__ int cand_threshold(float theta, int e) {
-  const float t = ldexpf(theta, e + 1);
-  int t1;
-  if (!(t < 536870912.f)) t1 = (1 << 29) + 1;  // above every score (or NaN)
-  else if (t <= -536870912.f) t1 = -(1 << 29) - 1;
-  else t1 = (int)floorf(t) - 32;
-  return t1 - (1 << 15);
-}
-
-template <int G, int MODE, bool VEC, int RM>
+template <int G, int MODE, int RM>
 __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : (RM <= RM_SMALL ? 3 : 2)) void scan_fast_kernel(
     ScanArgs a) {
   constexpr int HG = (G + 3) / 4;
@@ -213,13 +193,15 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : (RM <= RM_SMALL ? 3 : 2)
   if (R > RM || R <= a.rows_above) return;   // another launch's unit (uniform)
   if (wave == 1) pre += sm.wsum[0];
   if (MODE == SCAN_CAND && tid < GP) sm.ccount[tid] = 0;
+  if (MODE == SCAN_CAND && tid < 4 * GP) (&sm.wcount[0][0])[tid] = 0;
+  if (tid < 4 * 16 * HG) reinterpret_cast<uint32_t*>(&sm.azero[0][0])[tid] = 0u;
   for (int i = tid; i < GP * D; i += SCAN_THREADS) {
     const int h = i / D;
     sm.q[h][i % D] = h < G ? a.q_basis[((long long)u * G + h) * D + i % D] : 0.f;
   }
   if (tid < 2 * GP * GB) {  // padding heads never pass
     const int h = (tid / GB) % GP;
-    if (h >= G) sm.tlo[tid / (GP * GB)][h][tid % GB] = 1 << 30;
+    if (h >= G) sm.tlo[tid / (GP * GB)][h][tid % GB] = (1 << 24) + 1;
   }
   if (tid < D && tj > 0) {
     const int r0 = (pre & 0xFFFF) - tj;
@@ -253,10 +235,6 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : (RM <= RM_SMALL ? 3 : 2)
     return;
   }
 
-  // frame size: |X| < 2^lx and R 2^lx <= 2^29
-  int lx = 29;
-  for (int r = R - 1; r > 0; r >>= 1) --lx;  // 29 - ceil(log2 R)
-  lx = lx > 21 ? 21 : lx;
   const int nsteps = (int)((wb1 - wb0 + GB - 1) / GB);
   const int rpt = (R + 31) / 32;  // 32-row pieces of the K passes (A is zero beyond R)
   auto step_g0 = [&](int i) { return wb0 + (long long)i * GB; };
@@ -284,8 +262,8 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : (RM <= RM_SMALL ? 3 : 2)
   const int sc_c = tid >> 1, sc_h = tid & 1;
   const bool svalid = sc_c < CR;
   const long long srow = svalid ? (long long)sm.chj[sc_c] * nbcap : 0;
-  // VEC: byte offsets; in the last step clamped to the capacity (the words past
-  // it are never used)
+  // byte offsets; in the last step clamped to the row's stride (the words
+  // past the step's blocks are never used)
   uint32_t soff = OUT_OF_RANGE, soff_last = OUT_OF_RANGE;
   if (svalid) {
     soff = (uint32_t)((srow + 8 * sc_h) * 2);
@@ -295,19 +273,7 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : (RM <= RM_SMALL ? 3 : 2)
   u32x4 sw;  // scales of the next step to write
   auto issue_scales = [&](int i) {
     const auto rs = scale_rsrc(i);
-    if constexpr (VEC) {
-      sw = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(i >= nsteps - 1 ? soff_last : soff), 0, 0);
-    } else {
-      const long long f = step_first(i);
-      uint32_t v[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int b = 0; b < 8; ++b) {
-        const long long w = (f + 8 * sc_h + b) < nbcap ? (f + 8 * sc_h + b) : nbcap - 1;
-        const uint32_t o = svalid ? (uint32_t)((srow + w - f) * 2) : OUT_OF_RANGE;
-        v[b >> 1] |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, (int)o, 0, 0) << (16 * (b & 1));
-      }
-      sw = u32x4{v[0], v[1], v[2], v[3]};
-    }
+    sw = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(i >= nsteps - 1 ? soff_last : soff), 0, 0);
   };
   auto write_scales = [&](int i) {  // scales of step i and their per-channel max
     const int b3 = i % 3;
@@ -335,35 +301,16 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : (RM <= RM_SMALL ? 3 : 2)
     }
   };
 
-  // Frames of a step.  With 16-byte plane loads (VEC) one wavefront computes
-  // them for every head: 16-lane row r takes head 4 k + r, and lane b of the
-  // row takes block b of the step and the read channels 8 b .. 8 b + 7; the
-  // thresholds of the heads and |q_hj| 8 of every head and read channel go to
-  // LDS once (seen by the frames after the prologue's barrier).  Otherwise
-  // (more registers live) wavefront w computes those of its heads w, w + 4
-  // from registers: the threshold, and |q_hj| 8 of read channels lane,
-  // lane + 64.
-  if constexpr (VEC) {
-    if (tid < FastSmem<HG, RM>::GP)
-      sm.theta[tid] = (MODE == SCAN_CAND && tid < G) ? key_to_float(a.thresh[(long long)u * G + tid]) : 0.f;
-    for (int e = tid; e < FastSmem<HG, RM>::GP * 128; e += SCAN_THREADS) {
-      const int h = e >> 7, c = e & 127;
-      sm.qa8[h][c] = (h < G && c < CR) ? fabsf(sm.q[h][sm.chj[c]]) * 8.f : 0.f;
-    }
-  }
-  float theta_k[VEC ? 1 : HG];
-  float qa8[VEC ? 1 : HG][2];
-  if constexpr (!VEC) {
-#pragma unroll
-    for (int k = 0; k < HG; ++k) {
-      const int h = wave + 4 * k;
-      theta_k[k] = (MODE == SCAN_CAND && h < G) ? key_to_float(a.thresh[(long long)u * G + h]) : 0.f;
-#pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-        const int c = lane + 64 * cc;
-        qa8[k][cc] = (h < G && c < CR) ? fabsf(sm.q[h][sm.chj[c]]) * 8.f : 0.f;
-      }
-    }
+  // Frames of a step: one wavefront computes them for every head: 16-lane row
+  // r takes head 4 k + r, and lane b of the row takes block b of the step and
+  // the read channels 8 b .. 8 b + 7; the thresholds of the heads and |q_hj| 8
+  // of every head and read channel go to LDS once (seen by the frames after
+  // the prologue's barrier).
+  if (tid < FastSmem<HG, RM>::GP)
+    sm.theta[tid] = (MODE == SCAN_CAND && tid < G) ? key_to_float(a.thresh[(long long)u * G + tid]) : 0.f;
+  for (int e = tid; e < FastSmem<HG, RM>::GP * 128; e += SCAN_THREADS) {
+    const int h = e >> 7, c = e & 127;
+    sm.qa8[h][c] = (h < G && c < CR) ? fabsf(sm.q[h][sm.chj[c]]) * 8.f : 0.f;
   }
 
   // the frame of (head h, block blk): E of the step (from the largest key,
@@ -374,7 +321,7 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : (RM <= RM_SMALL ? 3 : 2)
     // an upper bound of the largest |q| 8 smax, and the channel that reaches it
     const float best = key ? __uint_as_float((key & 0xFFFFFF00u) + 0x100u) : 0.f;
     const int cs = (int)(key & 0xFFu);
-    const int E = frame_exp(best, lx);
+    const int E = frame_exp(best, FRAME_BITS);
     int eb = E;
     own = false;
     if (blk < gblk && best > 0.f) {
@@ -384,65 +331,40 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : (RM <= RM_SMALL ? 3 : 2)
         float mb = 0.f;
         for (int c = 0; c < CR; ++c)
           mb = fmaxf(mb, fabsf(sm.q[h][sm.chj[c]]) * 8.f * half_bits_to_f32(sm.sc[b3][c][blk]));
-        eb = frame_exp(mb, lx);
+        eb = frame_exp(mb, FRAME_BITS);
         own = eb != E;
       }
     }
     if (h < G && blk < GB) {
       sm.ex[par][h][blk] = eb;
-      if constexpr (MODE == SCAN_CAND) sm.tlo[par][h][blk] = cand_threshold(theta, eb);
+      if constexpr (MODE == SCAN_CAND) sm.tlo[par][h][blk] = cand_tau(theta, eb, R) + 1;
     }
     return E;
   };
 
-  // ---- frames of step i (VEC: by the calling wavefront for every head;
-  // otherwise its own heads); every lane of the wavefront must be active ----
+  // ---- frames of step i, by the calling wavefront for every head; every
+  // lane of the wavefront must be active ----
   auto compute_frame = [&](int i) {
     const int par = i & 1, b3 = i % 3, gblk = step_blocks(i);
-    if constexpr (VEC) {
-      const int frow = lane >> 4, fblk = lane & 15;
+    const int frow = lane >> 4, fblk = lane & 15;
 #pragma unroll
-      for (int k = 0; k < HG; ++k) {
-        const int h = 4 * k + frow;  // heads past G compute zeros and write nothing
-        uint32_t key = 0;
+    for (int k = 0; k < HG; ++k) {
+      const int h = 4 * k + frow;  // heads past G compute zeros and write nothing
+      uint32_t key = 0;
 #pragma unroll
-        for (int m = 0; m < 8; ++m) {
-          const int c = 8 * fblk + m;
-          const float v = sm.qa8[h][c] * (c < CR ? sm.smax[b3][c] : 0.f);
-          const uint32_t kk = v > 0.f ? (__float_as_uint(v) & 0xFFFFFF00u) | (uint32_t)c : 0u;
-          key = kk > key ? kk : key;
-        }
-        key = row_max_u32_dpp(key);
-        bool own;
-        const int E = frame_write(par, b3, gblk, h, fblk, key, sm.theta[h], own);
-        const uint64_t ob = __ballot(own);
-        if (h < G && fblk == 0) {
-          sm.exh[par][h] = E;
-          sm.own[par][h] = ((ob >> (16 * frow)) & 0xFFFFull) != 0ull;
-        }
+      for (int m = 0; m < 8; ++m) {
+        const int c = 8 * fblk + m;
+        const float v = sm.qa8[h][c] * (c < CR ? sm.smax[b3][c] : 0.f);
+        const uint32_t kk = v > 0.f ? (__float_as_uint(v) & 0xFFFFFF00u) | (uint32_t)c : 0u;
+        key = kk > key ? kk : key;
       }
-    } else {
-#pragma unroll
-      for (int k = 0; k < HG; ++k) {
-        const int h = wave + 4 * k;
-        if (h >= G) continue;  // wavefront-uniform
-        uint32_t key = 0;
-#pragma unroll
-        for (int cc = 0; cc < 2; ++cc) {
-          const int c = lane + 64 * cc;
-          if (cc == 1 && CR <= 64) break;  // uniform
-          const float v = qa8[k][cc] * (c < CR ? sm.smax[b3][c] : 0.f);
-          const uint32_t kk = v > 0.f ? (__float_as_uint(v) & 0xFFFFFF00u) | (uint32_t)c : 0u;
-          key = kk > key ? kk : key;
-        }
-        key = wave_max_u32_dpp(key);
-        bool own;
-        const int E = frame_write(par, b3, gblk, h, lane, key, theta_k[k], own);
-        const bool any_own = __ballot(own) != 0ull;
-        if (lane == 0) {
-          sm.exh[par][h] = E;
-          sm.own[par][h] = any_own;
-        }
+      key = row_max_u32_dpp(key);
+      bool own;
+      const int E = frame_write(par, b3, gblk, h, fblk, key, sm.theta[h], own);
+      const uint64_t ob = __ballot(own);
+      if (h < G && fblk == 0) {
+        sm.exh[par][h] = E;
+        sm.own[par][h] = ((ob >> (16 * frow)) & 0xFFFFull) != 0ull;
       }
     }
   };
@@ -475,26 +397,8 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : (RM <= RM_SMALL ? 3 : 2)
       const auto rs = plane_rsrc(i);
       const bool last = i >= nsteps - 1;
 #pragma unroll
-      for (int k = 0; k < PL; ++k) {
-        if constexpr (VEC) {
-          pw[k] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(last ? poff_last[k] : poff[k]), 0, 0);
-        } else {
-          // 8-byte aligned rows: two 8-byte loads, each word clamped to the capacity
-          const long long f = step_first(i);
-          const int e = tid + k * SCAN_THREADS, r = e >> 3, part = 2 * (e & 7);
-          u32x2 wv[2];
-#pragma unroll
-          for (int x = 0; x < 2; ++x) {
-            uint32_t o = OUT_OF_RANGE;
-            if (r < R) {
-              const long long w = (f + part + x) < nbcap ? (f + part + x) : nbcap - 1;
-              o = (uint32_t)((long long)poff[k] + (w - f - part) * 8);
-            }
-            wv[x] = __builtin_amdgcn_raw_buffer_load_b64(rs, (int)o, 0, 0);
-          }
-          pw[k] = u32x4{wv[0].x, wv[0].y, wv[1].x, wv[1].y};
-        }
-      }
+      for (int k = 0; k < PL; ++k)
+        pw[k] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(last ? poff_last[k] : poff[k]), 0, 0);
     };
     auto write_planes = [&](int i) {  // rows are 8-byte aligned
 #pragma unroll
@@ -509,7 +413,11 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : (RM <= RM_SMALL ? 3 : 2)
     // builder items: pass m covers row RPP m + lane / NPAIR and heads
     // 2 (lane % NPAIR), +1; rows >= R have zero weights, hence zero digits
     const int prow = lane / NPAIR, ppair = lane % NPAIR;
-    float fq0[NPASS][2];  // q_hj 2^(3-p) of the item's row and heads
+    // q_hj 2^(3-p+E_h) of the item's row and heads in the current step's frames
+    // (exact power-of-two rescalings from step to step; the frame exponents
+    // they are in are fexp)
+    double fqe[NPASS][2];
+    int fexp[2] = {0, 0};
     int soffm[NPASS];     // the item's row's scales in sc[.]: read channel * SCS
 #pragma unroll
     for (int m = 0; m < NPASS; ++m) {
@@ -518,7 +426,7 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : (RM <= RM_SMALL ? 3 : 2)
 #pragma unroll
       for (int x = 0; x < 2; ++x) {
         const int h = 2 * ppair + x;
-        fq0[m][x] = (r < R && h < G) ? ldexpf(sm.q[h][sm.chj[sm.rowc[r]]], 3 - sm.rowp[r]) : 0.f;
+        fqe[m][x] = (r < R && h < G) ? ldexp((double)sm.q[h][sm.chj[sm.rowc[r]]], 3 - sm.rowp[r]) : 0.0;
       }
     }
 
@@ -526,17 +434,18 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : (RM <= RM_SMALL ? 3 : 2)
     // a transposing read takes, in each 16-lane group, row r0 + (l % 16) / 2
     const int kg = lane >> 4, s16 = lane & 15;
     const int rsub = s16 >> 1, ahalf = 8 * (s16 & 1), hb = s16 >> 3;
-    uint32_t bmask[4];
-    int shy[4];  // 8 - bp, bp = 2c + hb the bit that column n keeps
+    uint32_t bmask[4];  // product c keeps bit bp = 2c + hb of each byte in column n
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      bmask[c] = 0x01010101u << (2 * c + hb);
-      shy[c] = 8 - 2 * c - hb;
-    }
-    const uint32_t neg7 = hb ? 0xFFFFFFFFu : 0u;  // lanes whose c = 3 column keeps bit 7
+    for (int c = 0; c < 4; ++c) bmask[c] = 0x01010101u << (2 * c + hb);
+    const int neg3 = hb ? -1 : 0;  // lanes whose c = 3 column keeps bit 7 (v = -128)
     const i32x4 ones4 = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
-    const i32x4 ones2x = {0x01010101, 0x01010101, 0, 0};
     const i32x4 zero4 = {0, 0, 0, 0};
+    // a register pair whose contents never matter: it only meets zero A bytes
+    auto junk2 = []() {
+      i32x2 v;
+      asm volatile("" : "=v"(v));
+      return v;
+    };
 
     // fp16 scale of block b (0..3) of the wavefront's four, from a pass's 8 bytes
     auto scale_of = [](const u32x2& v, int b) {
@@ -544,30 +453,30 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : (RM <= RM_SMALL ? 3 : 2)
       return __builtin_bit_cast(_Float16, (uint16_t)((b & 1) ? (w >> 16) : w));
     };
     // A records of the wavefront's block b
-    auto build = [&](int b, const float (&fqe)[NPASS][2], const u32x2 (&scl)[NPASS]) {
+    auto build = [&](int b, const double (&fqe)[NPASS][2], const u32x2 (&scl)[NPASS]) {
       uint8_t* rec = &sm.atab[wave][prow][8 * ppair];
 #pragma unroll
       for (int m = 0; m < NPASS; ++m) {
-        const _Float16 sv = scale_of(scl[m], b);
+        const double sv = (double)(float)scale_of(scl[m], b);
         *reinterpret_cast<uint2*>(rec + m * RPP * (16 * HG)) =
-            make_uint2(x_digits(fqe[m][0], sv), x_digits(fqe[m][1], sv));
+            make_uint2(x_digits4(fqe[m][0], sv), x_digits4(fqe[m][1], sv));
       }
     };
     // the same for a step where some (head, block) has a frame of its own
-    auto build_own = [&](int par, int wb, int b, const float (&fqe)[NPASS][2],
+    auto build_own = [&](int par, int wb, int b, const double (&fqe)[NPASS][2],
                          const u32x2 (&scl)[NPASS], const int (&exh2)[2]) {
-      float g[2];
+      double g[2];
 #pragma unroll
       for (int x = 0; x < 2; ++x) {
         const int h = 2 * ppair + x;
-        g[x] = h < G ? ldexpf(1.f, sm.ex[par][h][wb + b] - exh2[x]) : 0.f;
+        g[x] = h < G ? ldexp(1.0, sm.ex[par][h][wb + b] - exh2[x]) : 0.0;
       }
       uint8_t* rec = &sm.atab[wave][prow][8 * ppair];
 #pragma unroll
       for (int m = 0; m < NPASS; ++m) {
-        const _Float16 sv = scale_of(scl[m], b);
+        const double sv = (double)(float)scale_of(scl[m], b);
         *reinterpret_cast<uint2*>(rec + m * RPP * (16 * HG)) =
-            make_uint2(x_digits(fqe[m][0] * g[0], sv), x_digits(fqe[m][1] * g[1], sv));
+            make_uint2(x_digits4(fqe[m][0] * g[0], sv), x_digits4(fqe[m][1] * g[1], sv));
       }
     };
     // operands of block blk (planes pl, the wavefront's A records), read from LDS
@@ -576,7 +485,7 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : (RM <= RM_SMALL ? 3 : 2)
       i32x4 b[N64 ? N64 : 1];
       i32x4 a[N64 ? N64 : 1][HG];
       i32x2 b32;
-      i32x2 a32[HG];
+      i32x4 a32[HG];  // 32 rows in the lower half of each K group, zeros above
     };
     auto fetch = [&](const uint8_t* pl, int blk, Ops& o) {
       const uint8_t* at = &sm.atab[wave][0][0];
@@ -597,7 +506,11 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : (RM <= RM_SMALL ? 3 : 2)
         const int r0 = 64 * N64 + 8 * kg + rsub;
         o.b32 = tr8(pl + r0 * PSTRIDE + 8 * blk);
 #pragma unroll
-        for (int hg = 0; hg < HG; ++hg) o.a32[hg] = tr8(at + r0 * (16 * HG) + 16 * hg + ahalf);
+        for (int hg = 0; hg < HG; ++hg) {
+          const i32x2 a0 = tr8(at + r0 * (16 * HG) + 16 * hg + ahalf);
+          const i32x2 a1 = tr8(&sm.azero[rsub][16 * hg + ahalf]);
+          o.a32[hg] = i32x4{a0.x, a0.y, a1.x, a1.y};
+        }
       }
     };
     auto mask4 = [](const i32x4& v, uint32_t m) {
@@ -618,40 +531,42 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : (RM <= RM_SMALL ? 3 : 2)
         }
       }
       if constexpr (HAS32) {
-        // the 32-row remainder as a K = 64 product whose upper 8 bytes per lane
-        // are zero (the K = 32 form's result latency is not reliably waited for)
+        // the 32-row remainder as a K = 64 product whose A bytes are zero in
+        // the upper half of each lane (the K = 32 form's result latency is not
+        // reliably waited for); B's upper half is left as it is
 #pragma unroll
         for (int hg = 0; hg < HG; ++hg) {
-          const i32x4 av = {o.a32[hg].x, o.a32[hg].y, 0, 0};
+          const i32x4& av = o.a32[hg];
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
             const int m = (int)bmask[c];
-            acc[hg][c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, i32x4{o.b32.x & m, o.b32.y & m, 0, 0},
+            const i32x2 j = junk2();
+            acc[hg][c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, i32x4{o.b32.x & m, o.b32.y & m, j.x, j.y},
                                                                N64 ? acc[hg][c] : zero4, 0, 0, 0);
           }
-          accc[hg] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, ones2x, N64 ? accc[hg] : zero4, 0, 0, 0);
+          accc[hg] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, ones4, N64 ? accc[hg] : zero4, 0, 0, 0);
         }
       }
     };
-    // exact score of column c: S = sum_r X_r b_r, T = 2 S - C, s_hat = T 2^-(e+1)
-    auto exact_score = [&](const i32x4& d, int c, uint32_t cc, int eb) {
-      const uint32_t sS = ((((uint32_t)d.z << 8) + (uint32_t)d.y) << shy[c]) +
-                          (uint32_t)(d.x >> (8 - shy[c]));
-      uint32_t s2 = 2u * sS;
-      if (c == 3) s2 = (s2 ^ neg7) - neg7;  // bit 7 kept as the int8 byte 0x80 = -128
-      return ldexpf((float)(int)(s2 - cc), -(eb + 1));
+    // exact score of column c of product c
+    auto exact_score = [&](const i32x4& d, const i32x4& dc, int c, int eb) {
+      return score4(d, dc, 2 * c + hb, c == 3 && hb, eb);
     };
     // scores of block blk: lane <-> (head 4 hg + l / 16, column l % 16)
-    // candidates: wavefront w fills part w of each head's region; wcnt[hg]
-    // counts those of head 4 hg + kg (the same in the 16 lanes of the head).
-    // Offsets within the unit's buffers fit 32 bits (capacity <= FAST_MAX_CAP).
-    float* cand_val_u = MODE == SCAN_CAND ? a.cand_val + (long long)u * G * a.regions * CAND_SLOTS : nullptr;
-    int32_t* cand_idx_u = MODE == SCAN_CAND ? a.cand_idx + (long long)u * G * a.regions * CAND_SLOTS : nullptr;
-    const int cand_head_ld = (int)(a.regions * CAND_SLOTS);
+    // candidates: wavefront w fills part w of each head's region, its slots
+    // handed out by its own LDS counter per head (sm.wcount[w][h]; the count
+    // may pass the part's size, which the selection flags).  Offsets within
+    // the unit's buffers fit 32 bits (capacity <= FAST_MAX_CAP).
+    const uint32_t cand_bytes = MODE == SCAN_CAND ? (uint32_t)(G * a.regions * CAND_SLOTS * 4) : 0u;
+    const auto cval_rsrc =
+        make_rsrc(MODE == SCAN_CAND ? a.cand_val + (long long)u * G * a.regions * CAND_SLOTS : a.out, cand_bytes);
+    const auto cidx_rsrc =
+        make_rsrc(MODE == SCAN_CAND ? (const void*)(a.cand_idx + (long long)u * G * a.regions * CAND_SLOTS)
+                                    : (const void*)a.out,
+                  cand_bytes);
+    // head h's slots start at h * head_ld, this wavefront's part at part_off
+    const int head_ld = (int)(a.regions * CAND_SLOTS);
     const int part_off = (int)(blockIdx.x * CAND_PARTS + wave) * a.part_slots;
-    int wcnt[HG];
-#pragma unroll
-    for (int hg = 0; hg < HG; ++hg) wcnt[hg] = 0;
     auto scores = [&](int par, long long g0, int blk, const i32x4 (&acc)[HG][4], const i32x4 (&accc)[HG],
                       const int (&tl)[HG], const int (&exb)[HG]) {
       const long long tok0 = (g0 + blk) * BLK + 8 * (s16 & 7) + hb;
@@ -659,16 +574,20 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : (RM <= RM_SMALL ? 3 : 2)
       for (int hg = 0; hg < HG; ++hg) {
         const int h = 4 * hg + kg;
         const i32x4 dc = accc[hg];
-        const uint32_t cc = ((uint32_t)dc.z << 16) + ((uint32_t)dc.y << 8) + (uint32_t)dc.x;  // C
         if constexpr (MODE == SCAN_CAND) {
-          const int tA = (tl[hg] + (int)cc) >> 1;
-          const int tA3 = tA + (int)neg7;  // for c = 3 the high lanes hold -S: ~(-S) = S - 1
+          // 2 P' - C_hi >= tau  <=>  P' >= kap = ceil((tau + C_hi) / 2), with
+          // P = v P' the raw high digit sums: P >= kap 2^bp, or for v = -128
+          // (c = 3, bit 7) -P >= kap 2^7, i.e. ~P >= kap 2^7 - 1
+          const int kap = (tl[hg] + (dc.w * 256 + dc.z)) >> 1;  // tl = tau + 1
+          const uint32_t kh = (uint32_t)kap << hb;
           bool pass[4];
+          int p[4];
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
             const i32x4 d = acc[hg][c];
-            const uint32_t sa = (((uint32_t)d.z << 8) + (uint32_t)d.y) << shy[c];
-            pass[c] = c == 3 ? (int)(sa ^ neg7) >= tA3 : (int)sa >= tA;
+            p[c] = d.w * 256 + d.z;
+            const int th = (int)((kh << (2 * c)) + (uint32_t)(c == 3 ? neg3 : 0));
+            pass[c] = (c == 3 ? (p[c] ^ neg3) : p[c]) >= th;
           }
           if (__ballot(pass[0] || pass[1] || pass[2] || pass[3]) != 0ull) {
             // tokens outside [4, cand_hi) are never candidates: only the unit's
@@ -680,34 +599,37 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : (RM <= RM_SMALL ? 3 : 2)
                 pass[c] = pass[c] && tok >= 4 && tok < cand_hi;
               }
             }
-            // slot of a passing (lane, c): the head's passing pairs before it,
-            // c-major, after the wavefront's earlier ones; a column with no
-            // passing lane is skipped as a whole
-            const uint64_t gm = 0xFFFFull << (16 * kg);
-            int before = 0;
+            // exact score: T_hi = 2 P' - C_hi, T_lo = 2 S_lo - C_lo (units of
+            // 2^16 and 1), with P' = P / v and S_lo = (2^8 D1 + D0) / v; the
+            // raw sums are multiples of 2^bp and, for R <= 128, within 2^29
+            const int nchi = -(dc.w * 256 + dc.z);
+            const int nclo = -(dc.y * 256 + dc.x);
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-              const uint64_t mw = __ballot(pass[c]);
-              if (mw == 0ull) continue;  // uniform
-              const uint64_t mc = mw & gm;
               if (pass[c]) {
-                const int slot = wcnt[hg] + before +
-                                 (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mc >> 32),
-                                                                __builtin_amdgcn_mbcnt_lo((uint32_t)mc, 0u));
+                const int slot = atomicAdd(&sm.wcount[wave][h], 1);
                 if (slot < a.part_slots) {
-                  const int off = h * cand_head_ld + part_off + slot;
-                  cand_val_u[off] = exact_score(acc[hg][c], c, cc, exb[hg]);
-                  cand_idx_u[off] = (int32_t)(tok0 + 2 * c);
+                  const int bp = 2 * c + hb;
+                  const i32x4 d = acc[hg][c];
+                  int ph = p[c] >> bp;
+                  int pl = (d.y * 256 + d.x) >> bp;
+                  if (c == 3) {  // v = -128 on the lanes with hb = 1
+                    ph = (ph ^ neg3) - neg3;
+                    pl = (pl ^ neg3) - neg3;
+                  }
+                  const float th = (float)(2 * ph + nchi), tlo = (float)(2 * pl + nclo);
+                  const float sc = ldexpf(__builtin_fmaf(th, 65536.f, tlo), -(exb[hg] + 1));
+                  const int off = (h * head_ld + part_off + slot) * 4;
+                  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), cval_rsrc, off, 0, 0);
+                  __builtin_amdgcn_raw_buffer_store_b32((uint32_t)(tok0 + 2 * c), cidx_rsrc, off, 0, 0);
                 }
               }
-              before += __popcll(mc);
             }
-            wcnt[hg] += before;
           }
         } else {
 #pragma unroll
           for (int c = 0; c < 4; ++c)
-            if (h < G) store(tok0 + 2 * c, h, exact_score(acc[hg][c], c, cc, exb[hg]));
+            if (h < G) store(tok0 + 2 * c, h, exact_score(acc[hg][c], dc, c, exb[hg]));
         }
       }
     };
@@ -721,7 +643,6 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : (RM <= RM_SMALL ? 3 : 2)
       if (nblk <= 0) return;
       // the rows' weights in this step's frames, and the rows' scales of the
       // wavefront's four blocks
-      float fqe[NPASS][2];
       u32x2 scl[NPASS];
       int exh2[2];
 #pragma unroll
@@ -729,9 +650,11 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : (RM <= RM_SMALL ? 3 : 2)
 #pragma unroll
       for (int m = 0; m < NPASS; ++m) {
 #pragma unroll
-        for (int x = 0; x < 2; ++x) fqe[m][x] = ldexpf(fq0[m][x], exh2[x]);
+        for (int x = 0; x < 2; ++x) fqe[m][x] = ldexp(fqe[m][x], exh2[x] - fexp[x]);
         scl[m] = *reinterpret_cast<const u32x2*>(&sm.sc[b3][0][0] + soffm[m] + wb);
       }
+      fexp[0] = exh2[0];
+      fexp[1] = exh2[1];
       bool own_any = false;
 #pragma unroll
       for (int h = 0; h < G; ++h) own_any |= sm.own[par][h] != 0;
@@ -803,7 +726,7 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : (RM <= RM_SMALL ? 3 : 2)
     write_scales(0);
     issue_scales(1);
     __syncthreads();
-    if (!VEC || wave == 0) compute_frame(0);
+    if (wave == 0) compute_frame(0);
 
     // ---- steps: the loads of step i + 1 (planes) and i + 2 (scales) are in
     // flight while step i is computed ----
@@ -813,15 +736,18 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : (RM <= RM_SMALL ? 3 : 2)
       __syncthreads();  // planes of i, scales of i + 1 and frames of i are in LDS
       issue_planes(i + 1);
       issue_scales(i + 2);
-      if (i + 1 < nsteps && (!VEC || wave == ((i + 1) & 3))) compute_frame(i + 1);  // VEC: by turns
+      if (i + 1 < nsteps && wave == ((i + 1) & 3)) compute_frame(i + 1);  // by turns
       blocks(i);
     }
     if constexpr (MODE == SCAN_CAND) {
+      // the counters of this wavefront's part (its own LDS atomics completed
+      // in order before this read)
 #pragma unroll
       for (int hg = 0; hg < HG; ++hg) {
         const int h = 4 * hg + kg;
         if (s16 == 0 && h < G)
-          a.cand_count[(((long long)u * G + h) * a.regions + blockIdx.x) * CAND_PARTS + wave] = wcnt[hg];
+          a.cand_count[(((long long)u * G + h) * a.regions + blockIdx.x) * CAND_PARTS + wave] =
+              sm.wcount[wave][h];
       }
     }
   };
@@ -858,15 +784,12 @@ hipError_t launch_fast(const ScanArgs& a0, int rows, hipStream_t st) {
     a.wg_blocks = wb;
     grid = dim3((unsigned)((maxnb + wb - 1) / wb), (unsigned)a.g.units());
   }
-  const bool vec = a.g.nbcap() % 8 == 0;
   if (rows <= RM_SMALL) {  // known and small, or not known: the small variant first
-    if (vec) scan_fast_kernel<G, MODE, true, RM_SMALL><<<grid, SCAN_THREADS, 0, st>>>(a);
-    else scan_fast_kernel<G, MODE, false, RM_SMALL><<<grid, SCAN_THREADS, 0, st>>>(a);
+    scan_fast_kernel<G, MODE, RM_SMALL><<<grid, SCAN_THREADS, 0, st>>>(a);
     if (rows >= 0) return hipGetLastError();
     a.rows_above = RM_SMALL;  // not known: the large variant takes the rest
   }
-  if (vec) scan_fast_kernel<G, MODE, true, SCAN_FAST_ROWS><<<grid, SCAN_THREADS, 0, st>>>(a);
-  else scan_fast_kernel<G, MODE, false, SCAN_FAST_ROWS><<<grid, SCAN_THREADS, 0, st>>>(a);
+  scan_fast_kernel<G, MODE, SCAN_FAST_ROWS><<<grid, SCAN_THREADS, 0, st>>>(a);
   return hipGetLastError();
 }
 

@@ -11,14 +11,19 @@ namespace bpk {
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-// 16-byte global words of rows that are only 8-byte aligned (odd capacity / 64)
-typedef uint32_t u32x4_a8 __attribute__((ext_vector_type(4), aligned(8)));
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 
 constexpr int SCAN_THREADS = 256;
 constexpr int SCAN_GB = 16;              // blocks per step (128-byte reads of a plane row)
 constexpr int SCAN_WIDE_SPAN = 1024;     // blocks per workgroup of a wide scan when launched blind
-constexpr float DIGIT_BIAS = 8421504.f;  // 0x808080: X + bias holds three balanced digits + 128 each
+// Fixed-point frame of the row weights: |X_r| < 2^FRAME_BITS (four balanced
+// int8 digits; the top one within [-32, 32]).
+constexpr int FRAME_BITS = 29;
+// 2^52 + 2^51 + 0x80808080: an fp64 sum with it lies in [2^52, 2^53), where
+// the ulp is 1 and the low 32 bits of the bit pattern are X + 0x80808080
+constexpr double DIGIT_MAGIC64 = 6755401596960896.0;
+// bound of |2^8 d1 + d0| for the two low digits of one row
+constexpr int LOW_DIGITS_MAX = 128 * 256 + 128;
 static_assert(SCAN_MIN_WG_BLOCKS == SCAN_GB, "a workgroup takes whole steps");
 static_assert(SAMPLE_GROUP % SCAN_GB == 0 && SAMPLE_STRIDE % SAMPLE_GROUP == 0, "sample plan");
 
@@ -117,6 +122,57 @@ __device__ __forceinline__ int frame_exp(float m, int lx) {
   frexpf(m, &e);  // m < 2^e
   int E = lx - e;
   return E < -100 ? -100 : (E > 100 ? 100 : E);
+}
+
+// The four balanced signed digits of X = round(f s) (to nearest, ties to
+// even; |X| < 2^29), packed little-endian: X = d0 + 2^8 d1 + 2^16 d2 + 2^24 d3.
+// f s is exact in fp64 (f carries at most 24 significant bits, s 11), so the
+// fma rounds once; the low word of the result is X + 0x80808080, whose bytes
+// are the digits + 128 each (no carries), and the xor turns each into the
+// digit's two's-complement byte.
+__device__ __forceinline__ uint32_t x_digits4(double f, double s) {
+  const double r = __builtin_fma(f, s, DIGIT_MAGIC64);
+  return (uint32_t)__builtin_bit_cast(unsigned long long, r) ^ 0x80808080u;
+}
+
+// Column arithmetic of the scan's integer contraction.  A column of the
+// products keeps bit bp of each plane byte, so its digit sums carry the
+// factor v = 2^bp (bp < 7), or v = -128 for bp = 7 (the int8 byte 0x80);
+// d = (D0, D1, D2, D3) are the column's digit sums of sum_r X_r b_r times v,
+// dc = (C0 .. C3) the digit sums of C = sum_r X_r (all-one bytes).  The score
+// is (2 S - C) 2^-(e+1), formed from the high and low halves
+// T_hi = 2 P' - C_hi (units of 2^16) and T_lo = 2 S_lo - C_lo, each exact in
+// int32, by one fma (T_lo is exact in fp32 while 3 R 2^15 < 2^24, R < 170;
+// beyond, it rounds by at most 3 units).
+__device__ __forceinline__ float score4(const i32x4& d, const i32x4& dc, int bp, bool neg, int e) {
+  int ph = (d.w >> bp) * 256 + (d.z >> bp);  // P' v / |v|
+  int pl = (d.y >> bp) * 256 + (d.x >> bp);  // S_lo v / |v|
+  if (neg) {
+    ph = -ph;
+    pl = -pl;
+  }
+  const int th = 2 * ph - (dc.w * 256 + dc.z);
+  const int tl = 2 * pl - (dc.y * 256 + dc.x);
+  return ldexpf(__builtin_fmaf((float)th, 65536.f, (float)tl), -(e + 1));
+}
+
+// Candidate test threshold of a (head, block) with frame exponent e, for R
+// rows: tau such that every token whose written score is >= theta has
+// 2 P' - C_hi >= tau (P' = sum_r (2^8 d3 + d2) b_r, C_hi = 2^8 C3 + C2).
+// The written score needs T = 2 S - C >= tp - |tp| 2^-22 - 16 with
+// tp = theta 2^(e+1) (the two fp32 roundings of score4 move T by at most
+// |tp| 2^-23 + 4), and the dropped low halves move 2^16 (2 P' - C_hi) below T by
+// at most 3 R LOW_DIGITS_MAX.  Clamped to +-2^24 (beyond every value of
+// 2 P' - C_hi: nobody / everybody passes); the caller keeps tau + 1.
+__device__ __forceinline__ int cand_tau(float theta, int e, int R) {
+  if (theta == -__builtin_inff()) return -(1 << 24);
+  if (!(theta < __builtin_inff())) return 1 << 24;  // +inf or NaN: nothing passes
+  const double tp = ldexp((double)theta, e + 1);
+  const double need = tp - fabs(tp) * 0x1p-22 - 16.0 - 3.0 * LOW_DIGITS_MAX * (double)R;
+  const double t = floor(need * 0x1p-16);
+  if (t <= -16777216.0) return -(1 << 24);
+  if (t >= 16777216.0) return 1 << 24;
+  return (int)t;
 }
 
 // Inverse of order_key; 0 and ~0 (everything / nothing is a candidate) map to

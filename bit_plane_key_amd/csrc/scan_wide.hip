@@ -11,17 +11,11 @@
 //   s_hat = sum_j q_hj s_bj m_ij = sum_r w_r (b_r - 1/2) = S - C/2,
 //   S = sum_r w_r b_r,  C = sum_r w_r.
 // The weights of one 16-block step and head are put in a common fixed-point
-// frame, X_r = round(w_r 2^E), with E chosen so that sum_r |X_r| < 2^29, and
-// each X_r (|X_r| < 2^23) is split into three balanced signed bytes.  S and C
-// are then exact integer contractions of int8 digits with 0/1 bits, and the
-// score is s_hat = (2 S - C) 2^-(E+1).  The only rounding is that of X_r (half
-// a unit), far below the 1e-4 tolerance relative to the score's own L1 mass
-// as long as the frame is within a few bits of each block's largest weight.
-// E comes from max_j |q_hj| 8 smax_j over the step (smax_j = the largest scale
-// of channel j in the step); a block whose own largest weight may be more
-// than 4x smaller (tested on the channel that sets the frame) gets a frame of
-// its own.  Frames depend only on the step's blocks, so scores are
-// bit-identical in every launch mode.
+// frame, X_r = round(w_r 2^E) with |X_r| < 2^29, each split into four balanced
+// signed bytes, and the score is s_hat = (2 S - C) 2^-(E+1), with the frames,
+// digits, error bound and candidate test of the fast kernel (scan.hip; the
+// shared pieces are in scan_common.h).  For R <= 512 rows the rounding error
+// stays below (R/4 + 4) 2^-22 + 2^-23 <= 4e-5 of the token's L1 mass.
 //
 // Mapping onto gfx950:
 // * A workgroup (4 wavefronts) owns a range of blocks of one unit and walks
@@ -40,10 +34,9 @@
 //   tokens of the block, token 8 (n % 8) + 2c + n / 8 in column n, each
 //   scaled by 2^(2c + n / 8) (by -2^7 for bit 7: the int8 byte 0x80 is
 //   -128).  A fifth product with all-one bytes gives C.
-// * Lane l ends with the four digit sums of head 4 hg + l / 16 for its token,
-//   and recombines them with shifts into the int32 S.  In the candidate mode
-//   the test score >= threshold is the exact integer test 2 S - C >= I on
-//   the same value the score would be written as.
+// * Lane l ends with the four digit sums of head 4 hg + l / 16 for its token;
+//   in the candidate mode the two high ones are tested against the
+//   per-(head, block) threshold and passing tokens get their exact scores.
 #include "scan_common.h"
 
 namespace bpk {
@@ -65,7 +58,7 @@ struct ScanSmem {
   float smax[2][CMAX];                            // per step parity: largest scale of a read channel
   float q[GP][D];                                 // the unit's query heads (0 beyond G)
   int ex[2][GP][GB];                              // per step parity: frame exponent of (head, block)
-  int ith[2][GP][GB];                             // per step parity: integer threshold of (head, block)
+  int ith[2][GP][GB];                             // per step parity: cand_tau + 1 of (head, block)
   int exh[2][GP];                                 // per step parity: frame exponent of the step
   int own[2][GP];                                 // per step parity: some block has a frame of its own
   int scan_buf[D];                                // plan: prefix sums of (depth, read flag)
@@ -74,22 +67,6 @@ struct ScanSmem {
   uint8_t chj[CMAX];                              // channel of each read channel
   int ccount[GP];                                 // candidates of this workgroup per head
 };
-
-// Smallest integer T with ldexp((float)T, -(E+1)) >= theta, clamped to
-// [-2^30, 2^30] (every |T| here is below 2^29).
-__device__ int int_threshold(float theta, int E) {
-  if (theta == -__builtin_inff()) return -(1 << 30);
-  if (!(theta < __builtin_inff())) return 1 << 30;
-  const double tp = ldexp((double)theta, E + 1);
-  if (tp <= -1073741824.0) return -(1 << 30);
-  if (tp >= 1073741824.0) return 1 << 30;
-  int t = (int)ceil(tp);
-  // (float) rounds to nearest, so a few integers below ceil(tp) may still
-  // convert to a value >= tp; the predicate is monotone in t
-  for (int d = 64; d >= 1; d >>= 1)
-    if ((double)(float)(t - d) >= tp) t -= d;
-  return t;
-}
 
 template <int G, int MODE>
 __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : 2) void scan_wide_kernel(ScanArgs a) {
@@ -206,10 +183,6 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : 2) void scan_wide_kernel
     return;
   }
 
-  // frame size: |X| < 2^lx and R 2^lx <= 2^29
-  int lx = 29;
-  for (int r = R - 1; r > 0; r >>= 1) --lx;  // 29 - ceil(log2 R)
-  lx = lx > 22 ? 22 : lx;
   const int nseg = (R + SEG - 1) / SEG;
   const int nsteps = (int)((wb1 - wb0 + GB - 1) / GB);
   const int ntask = nsteps * nseg;
@@ -223,7 +196,6 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : 2) void scan_wide_kernel
   // ---- loads (global -> registers; written to LDS at the top of a task) ----
   u32x4 pw[PL];        // plane words: row e / 8 of the segment, words 2 (e % 8), +1
   u32x4 sw;            // scales: read channel tid / 2, blocks 8 (tid % 2) .. +7
-  const bool vec_scales = (nbcap % 8) == 0;
   auto issue_planes = [&](int task) {
     const int i = task / nseg, s = task % nseg;
     const long long g0 = step_g0(i);
@@ -239,7 +211,7 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : 2) void scan_wide_kernel
         const uint64_t* src =
             a.planes + ((uint64_t)(gu * D + sm.chj[sm.rowc[r]]) * NP + sm.rowp[r]) * nbcap + g0 + 2 * part;
         if (2 * part + 1 < gblk) {
-          pw[k] = *reinterpret_cast<const u32x4_a8*>(src);
+          pw[k] = *reinterpret_cast<const u32x4*>(src);
         } else if (2 * part < gblk) {
           const uint64_t w0 = src[0];
           pw[k] = u32x4{(uint32_t)w0, (uint32_t)(w0 >> 32), 0u, 0u};
@@ -254,7 +226,7 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : 2) void scan_wide_kernel
     const long long g0 = step_g0(i) + 8 * hf;
     const int gblk = step_blocks(i) - 8 * hf;
     const uint16_t* src = a.scales + (uint64_t)(gu * D + sm.chj[c]) * nbcap + g0;
-    if (vec_scales && gblk >= 8) {
+    if (gblk >= 8) {
       sw = *reinterpret_cast<const u32x4*>(src);
     } else {
       uint32_t v[4] = {0u, 0u, 0u, 0u};
@@ -305,7 +277,7 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : 2) void scan_wide_kernel
       best = wave_max(best);
       bkey = wave_max_u32(bkey);
       const int cs = (int)(bkey & 0xFFu);
-      const int E = frame_exp(best, lx);
+      const int E = frame_exp(best, FRAME_BITS);
       int eb = E;
       bool own = false;
       if (lane < GB && lane < gblk && best > 0.f) {
@@ -315,14 +287,14 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : 2) void scan_wide_kernel
           float mb = 0.f;
           for (int c = 0; c < CR; ++c)
             mb = fmaxf(mb, fabsf(sm.q[h][sm.chj[c]]) * 8.f * half_bits_to_f32(sm.sc[par][c][lane]));
-          eb = frame_exp(mb, lx);
+          eb = frame_exp(mb, FRAME_BITS);
           own = eb != E;
         }
       }
       if (lane < GB) {
         sm.ex[par][h][lane] = eb;
         sm.ith[par][h][lane] =
-            MODE == SCAN_CAND ? int_threshold(key_to_float(a.thresh[(long long)u * G + h]), eb) : 0;
+            MODE == SCAN_CAND ? cand_tau(key_to_float(a.thresh[(long long)u * G + h]), eb, R) + 1 : 0;
       }
       const bool any_own = __ballot(own) != 0ull;
       if (lane == 0) {
@@ -368,7 +340,7 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : 2) void scan_wide_kernel
   uint32_t bmask[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) bmask[c] = 0x01010101u << (2 * c + (s16 >> 3));
-  const uint32_t neg7 = (s16 >> 3) ? 0xFFFFFFFFu : 0u;  // lanes whose c = 3 column keeps bit 7
+  const int neg3 = (s16 >> 3) ? -1 : 0;  // lanes whose c = 3 column keeps bit 7 (v = -128)
   const i32x4 ones4 = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
   const i32x4 ones2x = {0x01010101, 0x01010101, 0, 0};
 
@@ -421,8 +393,7 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : 2) void scan_wide_kernel
             }
           }
 #pragma unroll
-          for (int x = 0; x < 4; ++x)
-            rec[hg][x] = (uint32_t)__builtin_fmaf(fv[x], sv, DIGIT_BIAS) ^ 0x808080u;
+          for (int x = 0; x < 4; ++x) rec[hg][x] = x_digits4((double)fv[x], (double)sv);
         }
       }
 #pragma unroll
@@ -508,26 +479,24 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : 2) void scan_wide_kernel
         for (int hg = 0; hg < HG; ++hg) {
           const int h = 4 * hg + kg;
           const i32x4 dc = accc[b][hg];
-          const uint32_t cc = ((uint32_t)dc.z << 16) + ((uint32_t)dc.y << 8) + (uint32_t)dc.x;  // C
           const int eb = sm.ex[par][h < G ? h : 0][blk];
-          const int ith = sm.ith[par][h < G ? h : 0][blk];
+          // the candidate test of scan.hip: P >= kap 2^bp (~P >= kap 2^7 - 1 for bit 7)
+          const int kap = MODE == SCAN_CAND && h < G
+                              ? (sm.ith[par][h][blk] + (dc.w * 256 + dc.z)) >> 1
+                              : 0;
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
             const int bp = 2 * c + (s16 >> 3);
             const i32x4 d = acc[b][hg][c];
-            // S = sum_r X_r b_r (the digit sums are multiples of 2^bp); T = 2 S - C
-            const uint32_t sS = ((uint32_t)d.z << (16 - bp)) + ((uint32_t)d.y << (8 - bp)) +
-                                (uint32_t)(d.x >> bp);
-            uint32_t s2 = 2u * sS;
-            if (c == 3) s2 = (s2 ^ neg7) - neg7;  // bit 7 kept as the int8 byte 0x80 = -128
-            const int t = (int)(s2 - cc);
             const long long tok = tok0 + 2 * c;
             if constexpr (MODE == SCAN_CAND) {
-              const bool pass = h < G && t >= ith;
+              const int p = d.w * 256 + d.z;
+              const int th = (int)(((uint32_t)kap << bp) + (uint32_t)(c == 3 ? neg3 : 0));
+              const bool pass = h < G && (c == 3 ? (p ^ neg3) : p) >= th;
               if (__ballot(pass) != 0ull && pass)
-                append(tok, h, ldexpf((float)t, -(eb + 1)));
+                append(tok, h, score4(d, dc, bp, c == 3 && neg3 != 0, eb));
             } else {
-              if (h < G) store(tok, h, ldexpf((float)t, -(eb + 1)));
+              if (h < G) store(tok, h, score4(d, dc, bp, c == 3 && neg3 != 0, eb));
             }
           }
         }

@@ -46,6 +46,8 @@ extern "C" {
 #define BPK_MAX_SEQS 64
 #define BPK_MAX_K 4096   /* largest top-k per query head */
 #define BPK_MAX_SELECTED 8192 /* largest group * k */
+/* words per plane row and scales per scale row of a cache of `cap` tokens */
+#define BPK_BLOCK_STRIDE(cap) ((((cap) / BPK_BLOCK) + 7) / 8 * 8)
 
 enum bpk_status {
   BPK_OK = 0,
@@ -66,12 +68,15 @@ enum bpk_op { BPK_OP_SELECT = 3, BPK_OP_ATTEND = 4, BPK_OP_DECODE = 5 };
  *
  * k_rows   [S][L][H][capacity][128]  key rows, fp32 or bf16 (k_dtype).
  * v_rows   [S][L][H][capacity][128]  value rows, bf16 bit patterns.
- * planes   [S][L][H][128][4][capacity/64] uint64.  Word (j, p, b) holds bit p
+ * planes   [S][L][H][128][4][NBS] uint64, NBS = BPK_BLOCK_STRIDE(capacity) (the
+ *          capacity in blocks rounded up to a multiple of 8, so that every row
+ *          starts 64-byte aligned; words past capacity/64 are never read or
+ *          written).  Word (j, p, b) holds bit p
  *          (p = 0 is the most significant bit, i.e. the sign) of the 4-bit
  *          codes of channel j over the 64 tokens of block b; bit i of the word
  *          belongs to token 64 b + i.  Channel-major, so the first t planes of
  *          a channel are contiguous (Fathom §3.2).
- * scales   [S][L][H][128][capacity/64] fp16 bit patterns, one per (channel,
+ * scales   [S][L][H][128][NBS] fp16 bit patterns, one per (channel,
  *          block): the block's max |k| divided by 8 (Fathom §3.2).
  * chan_var [S][L][H][128] fp32: the variance of each key channel in the scan
  *          basis, used by the depth rule (Fathom §1, observation 1).
