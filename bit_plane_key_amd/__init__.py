@@ -18,6 +18,7 @@ from ._lib import (  # noqa: F401
     Cache,
     alloc_depth,
     decode_step,
+    decode_fallback_units,
     decode_step_noalloc,
     NOALLOC_SCRATCH_BYTES,
     encode_append,

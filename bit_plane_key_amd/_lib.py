@@ -24,7 +24,7 @@ BPK_OP_SELECT, BPK_OP_ATTEND, BPK_OP_DECODE = 3, 4, 5
 HEAD_DIM, BLOCK, PLANES = 128, 64, 4
 
 EXPORTS = ("bpk_encode_append", "bpk_alloc_depth", "bpk_scan_scores", "bpk_select_topk",
-           "bpk_sparse_attend", "bpk_decode_step", "bpk_decode_step_noalloc", "bpk_workspace_bytes", "bpk_last_error",
+           "bpk_sparse_attend", "bpk_decode_step", "bpk_decode_step_noalloc", "bpk_decode_fallback_units", "bpk_workspace_bytes", "bpk_last_error",
            "bpk_trace_enable", "bpk_trace_read")
 STAGES = ("alloc", "sample", "threshold", "scan", "select", "fallback", "attend")
 
@@ -74,6 +74,7 @@ def _load() -> ctypes.CDLL:
         "bpk_sparse_attend": (ctypes.c_int, [C, P, P, I32, I32, I32, F, P, P, SZ, P]),
         "bpk_decode_step": (ctypes.c_int, [C, P, I32, I32, I32, I32, F, P, P, P, P, SZ, P]),
         "bpk_decode_step_noalloc": (ctypes.c_int, [C, P, I32, I32, I32, I32, F, P, P, P, P]),
+        "bpk_decode_fallback_units": (ctypes.c_int, [C, I32, I32, I32, P, SZ, P, P]),
         "bpk_workspace_bytes": (ctypes.c_size_t, [C, I32, I32, I32, I32]),
         "bpk_last_error": (ctypes.c_char_p, []),
         "bpk_trace_enable": (ctypes.c_int, [I32]),
@@ -264,6 +265,16 @@ def decode_step(cache: Cache, q: torch.Tensor, l0: int, l1: int, budget: int, k:
                                float(softmax_scale), out.data_ptr(), _ptr(depth_out),
                                _ptr(idx_out), ws.data_ptr(), ws.numel(), _stream(stream)))
     return out
+
+
+def decode_fallback_units(cache: Cache, l0: int, l1: int, k: int, ws: torch.Tensor,
+                          stream=None) -> int:
+    """Units that the last decode_step on ``ws`` redid unfused (see bpk.h);
+    waits for the stream."""
+    out = torch.zeros(1, dtype=torch.int32, device=ws.device)
+    _check(LIB.bpk_decode_fallback_units(cache.struct(), l0, l1, int(k), ws.data_ptr(),
+                                         ws.numel(), out.data_ptr(), _stream(stream)))
+    return int(out.item())
 
 
 NOALLOC_SCRATCH_BYTES = 32 << 20

@@ -156,8 +156,9 @@ DecodeWs decode_ws(const bpk::Geom& g, int k) {
   const long long groups = (g.nbcap() + bpk::SAMPLE_STRIDE - 1) / bpk::SAMPLE_STRIDE;
   w.sample_ld = groups * bpk::SAMPLE_GROUP * bpk::BLK;
   // candidate regions of 16 blocks (a scan workgroup of wb blocks takes wb / 16
-  // of them); the capacity rounded up to 256 blocks fits every workgroup size
-  w.regions = (g.nbcap() + 255) / 256 * (256 / bpk::SCAN_MIN_WG_BLOCKS);
+  // of them); the capacity rounded up to the largest span fits every span
+  w.regions = (g.nbcap() + bpk::SCAN_MAX_WG_BLOCKS - 1) / bpk::SCAN_MAX_WG_BLOCKS *
+              (bpk::SCAN_MAX_WG_BLOCKS / bpk::SCAN_MIN_WG_BLOCKS);
   const size_t slots = uh * (size_t)w.regions * bpk::CAND_SLOTS;
   size_t off = 0;
   w.q_basis = off; off += align256(uh * bpk::D * sizeof(float));
@@ -432,6 +433,25 @@ int bpk_decode_step_noalloc(const bpk_cache_t* c, const uint16_t* q, int32_t l0,
   if (rc) return rc;
   return decode_step_impl(c, g, q, budget_planes, k, softmax_scale, out, depth_out, idx_out, base,
                           false, static_cast<hipStream_t>(stream));
+}
+
+int bpk_decode_fallback_units(const bpk_cache_t* c, int32_t l0, int32_t l1, int32_t k,
+                              const void* ws, size_t ws_bytes, int32_t* count, void* stream) {
+  bpk::Geom g;
+  int rc = check_cache(c, l0, l1, &g);
+  if (rc) return rc;
+  if (!count) return fail(BPK_EINVAL, "count must be non-NULL");
+  rc = check_k(c, k);
+  if (rc) return rc;
+  const DecodeWs w = decode_ws(g, k);
+  if (!ws || ws_bytes < w.total)
+    return fail(BPK_EWORKSPACE, "workspace of %zu bytes < %zu needed", ws_bytes, w.total);
+  const int32_t* flag =
+      reinterpret_cast<const int32_t*>(static_cast<const char*>(ws) + w.flag);
+  // the unfused path (k > FUSED_MAX_K) flags nothing: count no unit
+  const int units = k > bpk::FUSED_MAX_K ? 0 : g.units();
+  return hip_status(bpk::launch_count_flags(units, flag, count, static_cast<hipStream_t>(stream)),
+                    "decode_fallback_units");
 }
 
 int bpk_trace_enable(int32_t on) {

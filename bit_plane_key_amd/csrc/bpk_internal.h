@@ -90,14 +90,18 @@ struct CandBufs {
   int32_t* flag;        // [units] 1 = redo this unit unfused
 };
 
-// blocks per workgroup of a scan over g: 16, doubled up to 256 while the
-// launch keeps at least 4096 workgroups
+// blocks per workgroup of a scan over g: 16, doubled up to SCAN_MAX_WG_BLOCKS
+// while the launch keeps at least 2048 workgroups (each workgroup's set-up is
+// then spread over up to 1024 blocks), and further while a unit would have
+// more than 1024 workgroups (the candidate selection indexes at most 4096
+// region parts, four per workgroup, per head)
+constexpr int SCAN_MAX_WG_BLOCKS = 1024;
 inline int scan_wg_blocks(const Geom& g) {
   long long maxnb = 0;
   for (int s = 0; s < g.S; ++s) maxnb = g.n[s] / BPK_BLOCK > maxnb ? g.n[s] / BPK_BLOCK : maxnb;
   const long long total = maxnb * g.units();
   int wb = SCAN_MIN_WG_BLOCKS;
-  while (wb < 256 && total / (2 * wb) >= 4096) wb *= 2;
+  while (wb < SCAN_MAX_WG_BLOCKS && (total / (2 * wb) >= 2048 || maxnb > 1024ll * wb)) wb *= 2;
   return wb;
 }
 
@@ -126,6 +130,8 @@ hipError_t launch_scan_flagged(const Geom& g, const float* q_basis, const uint8_
                                const int32_t* flag, int rows, hipStream_t st);
 hipError_t launch_topk_flagged(const Geom& g, const float* scores, int k, int32_t* idx,
                                const int32_t* flag, hipStream_t st);
+// the number of set flags among flag[0 .. units), into *count (device)
+hipError_t launch_count_flags(int units, const int32_t* flag, int32_t* count, hipStream_t st);
 
 size_t attend_ws_bytes(const Geom& g, int k);
 hipError_t launch_attend(const Geom& g, int k_dtype, const void* k_rows, const uint16_t* v_rows,

@@ -700,7 +700,26 @@ __global__ __launch_bounds__(CS_WAVES * 64) void cand_select_kernel(CandArgs a) 
   for (long long i = lane; 4 + nk + i < k; i += 64) out[4 + nk + i] = (int32_t)(hi + i);
 }
 
+// number of units whose flag is set, into *count (one workgroup; every
+// thread reaches the reduction)
+__global__ __launch_bounds__(256) void count_flags_kernel(const int32_t* flag, int units,
+                                                          int32_t* count) {
+  __shared__ int part[4];
+  int c = 0;
+  for (int u = threadIdx.x; u < units; u += 256) c += flag[u] != 0;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = c;
+  __syncthreads();
+  if (threadIdx.x == 0) *count = part[0] + part[1] + part[2] + part[3];
+}
+
 }  // namespace
+
+hipError_t launch_count_flags(int units, const int32_t* flag, int32_t* count, hipStream_t st) {
+  count_flags_kernel<<<1, 256, 0, st>>>(flag, units, count);
+  return hipGetLastError();
+}
 
 hipError_t launch_topk(const Geom& g, const float* scores, int k, int32_t* idx, hipStream_t st) {
   TopkArgs a{g, scores, k, idx, nullptr};

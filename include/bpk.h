@@ -218,6 +218,20 @@ int bpk_decode_step_noalloc(const bpk_cache_t* cache, const uint16_t* q, int32_t
                             uint8_t* depth_out, int32_t* idx_out, void* stream);
 
 /*
+ * Diagnostic of the fused selection inside bpk_decode_step (k <= 1024): that
+ * step takes a sampled score threshold, keeps the tokens at or above it, and
+ * picks the top-k among those; a unit whose kept tokens are too few (or
+ * overflow their buffers) is redone by a full scan and radix select, with the
+ * same result.  This call writes to *count (a DEVICE int32) how many units
+ * of the last bpk_decode_step that used `ws` with the same cache, layer range
+ * and k were redone that way (0 for k > 1024, which never takes the fused
+ * path).  Enqueued on `stream` after that step.
+ * Errors: BPK_EINVAL, BPK_EWORKSPACE.
+ */
+int bpk_decode_fallback_units(const bpk_cache_t* cache, int32_t l0, int32_t l1, int32_t k,
+                              const void* ws, size_t ws_bytes, int32_t* count, void* stream);
+
+/*
  * Workspace bytes an entry point needs for layers [l0, l1) and top-k k
  * (op = BPK_OP_SELECT, BPK_OP_ATTEND or BPK_OP_DECODE).  Returns 0 for an
  * invalid cache or op.

@@ -20,8 +20,10 @@ from tests import parity as P
 pytestmark = pytest.mark.gpu
 
 # the plan of the fused path: the first 64 blocks of every 4096 are sampled;
-# each scan workgroup keeps at most 128 candidates per head
-SAMPLE_STRIDE, SAMPLE_GROUP, SLOTS = 4096, 64, 128
+# a scan workgroup of wb blocks keeps its candidates per head in four parts
+# (one per wavefront: wavefront w scores blocks 4w .. 4w+3 of every 16), each
+# of 2 wb slots; more than 4096 candidates per head are not taken
+SAMPLE_STRIDE, SAMPLE_GROUP, CAND_CAP = 4096, 64, 4096
 
 
 def _say(*a):
@@ -55,22 +57,26 @@ def _unfused(b, cache, q, budget, k, scale):
 
 
 def _fused(b, cache, q, budget, k, scale, group):
+    """decode_step on a workspace of its own; also returns how many units it
+    redid unfused."""
     idx = torch.empty((1, 1, 1, group, k), dtype=torch.int32, device="cuda")
-    out = b.decode_step(cache, q, 0, 1, budget, k, scale, idx_out=idx)
-    return idx, out
+    ws = torch.empty(b.workspace_bytes(cache, b.BPK_OP_DECODE, 0, 1, k), dtype=torch.uint8,
+                     device="cuda")
+    out = b.decode_step(cache, q, 0, 1, budget, k, scale, idx_out=idx, ws=ws)
+    return idx, out, b.decode_fallback_units(cache, 0, 1, k, ws)
 
 
 def _wg_blocks(nb, units=1):
     wb = 16
-    while wb < 256 and nb * units // (2 * wb) >= 4096:
+    while wb < 1024 and (nb * units // (2 * wb) >= 2048 or nb > 1024 * wb):
         wb *= 2
     return wb
 
 
-def _fused_needs_fallback(scores_h, n, k):
-    """Whether the fused plan cannot settle this head (one unit): fewer than
-    k - 4 - W tokens at or above the sampled threshold, more than 4096, or
-    more than 128 in one scan workgroup's range."""
+def _fused_plan(scores_h, n, k, units=1):
+    """The fused plan on one head's exact scores: (tokens at or above the
+    sampled threshold, the largest count of them in one wavefront part, the
+    part size).  The scan's own test may keep a few more just below it."""
     w = O.kept_tail(n)
     hi, want = n - w, k - 4 - w
     nb = n // 64
@@ -79,14 +85,15 @@ def _fused_needs_fallback(scores_h, n, k):
                            for g in range((nb + SAMPLE_STRIDE - 1) // SAMPLE_STRIDE)])
     toks = toks[(toks >= 4) & (toks < hi)]
     m, nc = len(toks), hi - 4
-    r = (3 * want * m + nc - 1) // nc + 8
+    r = (2 * want * m + nc - 1) // nc + 8
     tau = -np.inf if r > m else np.sort(scores_h[toks])[::-1][r - 1]
-    passed = np.zeros(n, dtype=bool)
+    passed = np.zeros(nb * 64, dtype=bool)
     passed[4:hi] = scores_h[4:hi] >= tau
-    count = int(passed.sum())
-    wb = _wg_blocks(nb) * 64
-    per_wg = np.add.reduceat(passed[: nb * 64], np.arange(0, nb * 64, wb))
-    return count < want or count > 4096 or int(per_wg.max()) > SLOTS
+    wb = _wg_blocks(nb, units)
+    blk = np.arange(nb * 64) // 64
+    part = (blk // wb) * 4 + (blk % 16) // 4
+    per_part = np.bincount(part[passed], minlength=part.max() + 1)
+    return int(passed.sum()), int(per_part.max()), 2 * wb
 
 
 @pytest.mark.parametrize("budget", [64, 88, 128])
@@ -121,7 +128,7 @@ def test_fused_many_sample_groups_against_oracle(bpk, n, group):
     cache = _unit_cache(b, kb, vb, var, group)
     q = _to_dev(qb)[None, None, None]
     k, budget, scale = 512 if group < 8 else 256, 88, 1 / math.sqrt(128)
-    idx, out = _fused(b, cache, q, budget, k, scale, group)
+    idx, out, flagged = _fused(b, cache, q, budget, k, scale, group)
     scores, idx2 = _unfused(b, cache, q, budget, k, scale)
     torch.cuda.synchronize()
     assert torch.equal(idx, idx2)
@@ -131,7 +138,11 @@ def test_fused_many_sample_groups_against_oracle(bpk, n, group):
     P.check_selection(ix, ref["idx"], ref["scores"], ref["l1"], n, k, f"n={n}")
     P.check_attention(out[0, 0, 0].cpu().numpy(), O.attend(qv, kv, vv, ix, scale), f"n={n}")
     sc = scores[0, 0, 0].cpu().numpy()
-    assert not any(_fused_needs_fallback(sc[h], n, k) for h in range(group))
+    for h in range(group):
+        count, part_max, part_size = _fused_plan(sc[h], n, k)
+        # comfortably inside the plan's limits: the fused path settles it
+        assert k - 4 - O.kept_tail(n) <= count <= CAND_CAP // 2 and part_max <= part_size // 2
+    assert flagged == 0
 
 
 def test_fused_too_few_candidates_falls_back(bpk):
@@ -152,11 +163,14 @@ def test_fused_too_few_candidates_falls_back(bpk):
     cache = _unit_cache(b, kb, vb, var, group)
     q = _to_dev(qb)[None, None, None]
     scale = 1 / math.sqrt(128)
-    idx, out = _fused(b, cache, q, budget, k, scale, group)
+    idx, out, flagged = _fused(b, cache, q, budget, k, scale, group)
     scores, idx2 = _unfused(b, cache, q, budget, k, scale)
     torch.cuda.synchronize()
     sc = scores[0, 0, 0].cpu().numpy()
-    assert all(_fused_needs_fallback(sc[h], n, k) for h in range(group))
+    for h in range(group):
+        count, _, _ = _fused_plan(sc[h], n, k)
+        assert count < k - 4 - O.kept_tail(n)   # too few at or above the threshold
+    assert flagged == 1
     assert torch.equal(idx, idx2)
     P.check_topk_valid(sc[:, :n].astype(np.float64), idx[0, 0, 0].cpu().numpy(), n, k, "few")
 
@@ -170,8 +184,9 @@ def test_fused_overflow_falls_back(bpk):
     kb = f32_to_bf16_bits(rng.standard_normal((n, 128)).astype(np.float32))
     cache = _unit_cache(b, kb, kb, np.ones(128, dtype=np.float32), 4)
     q = _to_dev(f32_to_bf16_bits(rng.standard_normal((4, 128)).astype(np.float32)))[None, None, None]
-    idx, out = _fused(b, cache, q, 0, k, 1 / math.sqrt(128), 4)
+    idx, out, flagged = _fused(b, cache, q, 0, k, 1 / math.sqrt(128), 4)
     torch.cuda.synchronize()
+    assert flagged == 1
     want = np.concatenate([np.arange(4), np.arange(4, 4 + k - 36), np.arange(n - 32, n)])
     for h in range(4):
         assert np.array_equal(idx[0, 0, 0, h].cpu().numpy(), want)
@@ -187,7 +202,43 @@ def test_large_k_takes_unfused_path(bpk):
     cache = _unit_cache(b, kb, vb, np.ones(128, dtype=np.float32), 2)
     q = _to_dev(f32_to_bf16_bits(rng.standard_normal((2, 128)).astype(np.float32)))[None, None, None]
     scale = 1 / math.sqrt(128)
-    idx, out = _fused(b, cache, q, 88, k, scale, 2)
+    idx, out, flagged = _fused(b, cache, q, 88, k, scale, 2)
     scores, idx2 = _unfused(b, cache, q, 88, k, scale)
     torch.cuda.synchronize()
     assert torch.equal(idx, idx2)
+    assert flagged == 0
+
+
+def test_fused_long_unit_radix_threshold(bpk):
+    """One unit of 1,310,720 tokens: its sample (5 groups of 64 blocks, 20480
+    scores per head) is too large for the register threshold kernels, so the
+    radix threshold kernel sets the thresholds.  Fused = unfused, no unit
+    redone, the selection a valid top-k of the scores, and the scores right
+    on a seeded sample of tokens against the oracle."""
+    b, wl = bpk
+    n, group, k, budget = 1310720, 4, 512, 88
+    _say(f"fused long unit n={n}")
+    rng = np.random.default_rng(1310720)
+    sig = np.exp(rng.uniform(math.log(0.1), math.log(4.0), 128))
+    kb = f32_to_bf16_bits((rng.standard_normal((n, 128)) * sig).astype(np.float32))
+    vb = f32_to_bf16_bits(rng.standard_normal((n, 128)).astype(np.float32))
+    qb = f32_to_bf16_bits(rng.standard_normal((group, 128)).astype(np.float32))
+    var = (sig ** 2).astype(np.float32)
+    cache = _unit_cache(b, kb, vb, var, group)
+    q = _to_dev(qb)[None, None, None]
+    scale = 1 / math.sqrt(128)
+    idx, out, flagged = _fused(b, cache, q, budget, k, scale, group)
+    scores, idx2 = _unfused(b, cache, q, budget, k, scale)
+    torch.cuda.synchronize()
+    assert flagged == 0
+    assert torch.equal(idx, idx2)
+    sc = scores[0, 0, 0, :, :n].cpu().numpy()
+    P.check_topk_valid(sc.astype(np.float64), idx[0, 0, 0].cpu().numpy(), n, k, "long unit")
+    qv, kv = bf16_bits_to_f32(qb), bf16_bits_to_f32(kb)
+    depth = O.alloc_depth(qv, var, budget)
+    assert np.array_equal(b.alloc_depth(cache, q, 0, 1, budget)[0][0, 0, 0].cpu().numpy(), depth)
+    blocks = np.sort(rng.choice(n // 64, 64, replace=False))
+    toks = (blocks[:, None] * 64 + np.arange(64)[None, :]).ravel()
+    planes, scales = O.encode_unit(kv[toks])      # the sampled blocks, re-encoded
+    ref, l1 = O.scan_scores(qv, depth, planes, scales, len(toks))
+    P.check_scores(sc[:, toks], ref, l1, "long unit sample")
