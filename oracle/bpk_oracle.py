@@ -42,7 +42,8 @@ __all__ = [
     "D", "BLOCK", "PLANES", "FIRST_KEPT", "LAST_KEPT",
     "bf16_bits_to_f32", "block_scales", "quantize_codes", "encode_unit",
     "codes_from_planes", "prefix_values", "channel_gains", "alloc_depth",
-    "alloc_depth_greedy", "scan_scores", "kept_tail", "select_topk",
+    "alloc_depth_greedy", "sparq_depth", "double_sparsity_channels", "channel_set_depth",
+    "uniform_depth", "scan_scores", "kept_tail", "select_topk",
     "attend", "dense_attention", "rotate_basis", "decode_unit",
     "scan_bits_per_token", "scan_bytes_unit",
 ]
@@ -204,6 +205,59 @@ def alloc_depth_greedy(q_basis: np.ndarray, chan_var: np.ndarray, budget: int) -
                     best, best_v = jj, val
         depth[best] += 1
     return depth.astype(np.uint8)
+
+
+# ----------------------------------------------------------------------------
+# fixed-depth baselines on the same planes
+# ----------------------------------------------------------------------------
+
+def sparq_depth(q_basis: np.ndarray, r: int) -> np.ndarray:
+    """SparQ's channel choice as a depth vector: depth 4 on r channels, 0 elsewhere.
+
+    [Fathom §2, SparQ] each query picks the r channels of largest |q_j|; under
+    grouped-query attention the public rule first sums |q| over the query
+    heads that share the KV head, so one set of r channels is read per KV
+    head, at full (4-bit) depth.  Reading: the sum runs in fp32, heads in
+    ascending order; equal sums go to the lower channel index.
+    """
+    q = np.asarray(q_basis, dtype=np.float32)
+    acc = np.zeros(q.shape[1], dtype=np.float32)
+    for h in range(q.shape[0]):
+        acc = (acc + np.abs(q[h])).astype(np.float32)
+    nd = q.shape[1]
+    take = min(max(int(r), 0), nd)
+    order = np.lexsort((np.arange(nd), -acc.astype(np.float64)))
+    depth = np.zeros(nd, dtype=np.uint8)
+    depth[order[:take]] = PLANES
+    return depth
+
+
+def double_sparsity_channels(mean_abs_q: np.ndarray, mean_abs_k: np.ndarray, c: int) -> np.ndarray:
+    """Double Sparsity's static channel set of one KV head, ascending.
+
+    [Fathom §2, Double Sparsity] c channels chosen offline per head from
+    calibration statistics: the product of the mean |q| and the mean |k| of
+    each channel.  Reading: the c largest products (fp64), equal products to
+    the lower channel index.
+    """
+    score = np.asarray(mean_abs_q, dtype=np.float64) * np.asarray(mean_abs_k, dtype=np.float64)
+    nd = score.shape[0]
+    order = np.lexsort((np.arange(nd), -score))
+    return np.sort(order[: min(max(int(c), 0), nd)])
+
+
+def channel_set_depth(channels, nd: int = D) -> np.ndarray:
+    """Depth 4 on the given channels (Double Sparsity reads its c channels at
+    4 bits [Fathom §2]), 0 elsewhere."""
+    depth = np.zeros(nd, dtype=np.uint8)
+    depth[np.asarray(channels, dtype=np.int64)] = PLANES
+    return depth
+
+
+def uniform_depth(t: int, nd: int = D) -> np.ndarray:
+    """Every channel at depth t; t = 2 is the 2-bit thumbnail scan, which
+    reads the top two planes of all channels [Fathom §2, thumbnail scan]."""
+    return np.full(nd, min(max(int(t), 0), PLANES), dtype=np.uint8)
 
 
 # ----------------------------------------------------------------------------

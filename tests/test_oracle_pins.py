@@ -445,6 +445,73 @@ def test_rotation_matches_matmul_and_inverts(rng):
 # byte accounting (Fathom §1, §2; numbers the page prints)
 # --------------------------------------------------------------------------
 
+# --------------------------------------------------------------------------
+# fixed-depth baselines (Fathom §2: SparQ, Double Sparsity, thumbnail scan)
+# --------------------------------------------------------------------------
+
+def test_baseline_depths_cost_the_page_bits(rng):
+    """The depth vectors of the baselines cost the bits the page prints:
+    SparQ r = 16 / 32 at 4 bits 68 / 136, Double Sparsity c = 32 136 bits
+    = 17 bytes, the thumbnail (all channels, two planes) 288."""
+    g = json.load(open(os.path.join(GOLDEN, "fathom_bit_accounting.json")))
+    q = rng.standard_normal((4, 128)).astype(np.float32)
+    assert O.scan_bits_per_token(O.sparq_depth(q, g["sparq_68"]["channels"])) == \
+        g["sparq_68"]["bits_per_token"]
+    assert O.scan_bits_per_token(O.sparq_depth(q, g["scan_136"]["channels"])) == \
+        g["scan_136"]["bits_per_token"]
+    chans = O.double_sparsity_channels(rng.uniform(0.1, 1, 128), rng.uniform(0.1, 4, 128),
+                                       g["label_cache_bytes_per_token"]["channels"])
+    t = O.channel_set_depth(chans)
+    assert O.scan_bits_per_token(t) == g["scan_136"]["bits_per_token"]
+    assert O.scan_bits_per_token(t) / 8 == g["label_cache_bytes_per_token"]["bytes"]
+    assert O.scan_bits_per_token(O.uniform_depth(g["thumbnail_288"]["depth"])) == \
+        g["thumbnail_288"]["bits_per_token"]
+
+
+def test_sparq_sums_abs_q_over_the_group():
+    """Fathom §2 SparQ: |q| summed over the heads sharing the KV head, not
+    q^2 and not per head.  Channel 0: one head at 3 (sum |q| 3, sum q^2 9);
+    channel 1: four heads at 1 (sum |q| 4, sum q^2 4); channel 2: -2.5 on two
+    heads (5, 12.5).  r = 1 takes channel 2, r = 2 adds channel 1 (a rule on
+    q^2 would add channel 0)."""
+    q = np.zeros((4, 6), dtype=np.float32)
+    q[0, 0] = 3.0
+    q[:, 1] = 1.0
+    q[1:3, 2] = -2.5
+    assert list(O.sparq_depth(q, 1)) == [0, 0, 4, 0, 0, 0]
+    assert list(O.sparq_depth(q, 2)) == [0, 4, 4, 0, 0, 0]
+    assert list(O.sparq_depth(q, 3)) == [4, 4, 4, 0, 0, 0]
+    # equal sums: the lower channel first (channels 3..5 all zero)
+    assert list(O.sparq_depth(q, 4)) == [4, 4, 4, 4, 0, 0]
+    assert list(O.sparq_depth(q, 9)) == [4] * 6
+
+
+def test_double_sparsity_ranks_the_product():
+    """Fathom §2 Double Sparsity: channels ranked by mean|q| x mean|k|."""
+    mq = np.array([1.0, 0.5, 2.0, 0.1, 1.0])
+    mk = np.array([1.0, 3.0, 0.4, 9.0, 1.0])
+    # products 1, 1.5, 0.8, 0.9, 1: the two largest are channels 1 and 0 (0 before 4)
+    assert list(O.double_sparsity_channels(mq, mk, 2)) == [0, 1]
+    assert list(O.double_sparsity_channels(mq, mk, 3)) == [0, 1, 4]
+    assert list(O.channel_set_depth([0, 4], 5)) == [4, 0, 0, 0, 4]
+
+
+def test_uniform_full_depth_scan_is_the_4bit_dot(rng):
+    """At t = 4 on every channel the scan is the dot with the dequantized
+    4-bit keys; at t = 2 each key is its 2-bit quantizer's cell midpoint."""
+    k = _blocks(rng, 3, 128, sigma=np.exp(rng.uniform(-2, 1.4, 128)))
+    q = rng.standard_normal((4, 128)).astype(np.float32)
+    planes, scales = O.encode_unit(k)
+    s4, _ = O.scan_scores(q, O.uniform_depth(4), planes, scales, k.shape[0])
+    codes = np.stack([O.quantize_codes(k[b * 64:(b + 1) * 64], O.block_scales(k[b * 64:(b + 1) * 64]))
+                      for b in range(3)]).reshape(-1, 128).astype(np.float64)
+    deq = (codes - 8.0 + 0.5) * np.repeat(scales.T.astype(np.float64), 64, axis=0)
+    np.testing.assert_allclose(s4, q.astype(np.float64) @ deq.T, rtol=1e-12, atol=1e-12)
+    s2, _ = O.scan_scores(q, O.uniform_depth(2), planes, scales, k.shape[0])
+    mid2 = (np.floor(codes / 4) * 4 + 2 - 8) * np.repeat(scales.T.astype(np.float64), 64, axis=0)
+    np.testing.assert_allclose(s2, q.astype(np.float64) @ mid2.T, rtol=1e-12, atol=1e-12)
+
+
 def test_bit_accounting_matches_page():
     g = json.load(open(os.path.join(GOLDEN, "fathom_bit_accounting.json")))
     m = g["model"]
