@@ -22,6 +22,7 @@ import argparse
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
@@ -83,54 +84,90 @@ def counted_valu(config: str, budget: int):
 
 
 def time_launches(fn, steps: int):
+    """Median milliseconds of `steps` calls of fn, each between two HIP events
+    recorded on the current stream (the stream the library's calls run on)."""
     import torch
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
     torch.cuda.synchronize()
-    start.record()
-    for _ in range(steps):
+    for a, b in ev:
+        a.record()
         fn()
-    end.record()
+        b.record()
     torch.cuda.synchronize()
-    return start.elapsed_time(end) / steps  # ms
+    return float(statistics.median(a.elapsed_time(b) for a, b in ev))
 
 
-def cpu_baseline(cfg, cache, budget: int, tokens: int, units, n: int, step_units: int):
-    """The oracle's scan (depth allocation + prefix-plane scores) timed on one
-    host core over a bounded sample of the workload: the first ``tokens``
-    tokens of each of ``units``.  The sample's key rows are the generator's
-    (read back from the rows it drew on the device) and are encoded by the
-    oracle itself, outside the timed region."""
+def _oracle_unit_step(job):
+    """One unit of the oracle's decode step (allocation, scan, selection,
+    attention) on a host sample; returns (seconds, scan bytes).  Runs in a
+    worker process with one BLAS thread; the unit's rows come from the host
+    generator (the same bits the device generator wrote)."""
+    cfg_name, s, l, h, tokens, budget, topk, scale = job
     import numpy as np
-    import torch
-    from threadpoolctl import threadpool_limits
 
     import oracle as O
+    from synth import config_by_name
     from synth import workload as W
-    total_bytes, total_s = 0.0, 0.0
-    with threadpool_limits(limits=1):
-        for (s, l, h) in units:
-            kb = cache.k_rows[s, l, h, :tokens].view(torch.int16).cpu().numpy().view(np.uint16)
-            k = W.bf16_bits_to_f32(kb)
-            _, q = W.query(cfg, s, l, h)
-            var = cfg.chan_var(s, l, h)
-            planes, scales = O.encode_unit(k)
-            t0 = time.perf_counter()
-            depth = O.alloc_depth(q, var, budget)
-            O.scan_scores(q, depth, planes, scales, tokens)
-            total_s += time.perf_counter() - t0
-            total_bytes += O.scan_bytes_unit(depth, tokens)
-    per_unit_s = total_s / len(units)
-    return {"value": round(total_bytes / total_s / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
-            "keys_per_s": round(tokens * len(units) / total_s, 1),
+    cfg = config_by_name(cfg_name)
+    rows = np.arange(tokens)
+    _, k = W.key_rows(cfg, s, l, h, rows)
+    _, v = W.value_rows(cfg, s, l, h, rows)
+    _, q = W.query(cfg, s, l, h)
+    var = cfg.chan_var(s, l, h)
+    planes, scales = O.encode_unit(k)
+    t0 = time.perf_counter()
+    depth = O.alloc_depth(q, var, budget)
+    sc, _ = O.scan_scores(q, depth, planes, scales, tokens)
+    idx = O.select_topk(sc, tokens, topk)
+    O.attend(q, k, v, idx, scale)
+    return time.perf_counter() - t0, O.scan_bytes_unit(depth, tokens)
+
+
+def cpu_baseline(cfg, budget: int, tokens: int, units, n: int, step_units: int, k: int,
+                 scale: float):
+    """The oracle's decode step (depth allocation, scan, top-k, attention;
+    the encoding of the sample is not timed) on the host cores, over a
+    bounded sample of the workload: the first ``tokens`` tokens of each of
+    ``units``, one unit at a time per worker process.  Reported in the
+    metric's unit: scan bytes over seconds, on all the cores used."""
+    import concurrent.futures as cf
+    import multiprocessing as mp
+    jobs = [(cfg.name, s, l, h, tokens, budget, k, scale) for (s, l, h) in units]
+    # a GPU box's host share is 16 cores, whatever the machine reports
+    cores = min(len(jobs), os.cpu_count() or 1, 16)
+    env = {"OMP_NUM_THREADS": "1", "OPENBLAS_NUM_THREADS": "1", "MKL_NUM_THREADS": "1"}
+    old = {x: os.environ.get(x) for x in env}
+    os.environ.update(env)
+    try:
+        t0 = time.perf_counter()
+        with cf.ProcessPoolExecutor(cores, mp_context=mp.get_context("spawn")) as ex:
+            res = list(ex.map(_oracle_unit_step, jobs))
+        wall = time.perf_counter() - t0
+    finally:
+        for x, val in old.items():
+            if val is None:
+                os.environ.pop(x, None)
+            else:
+                os.environ[x] = val
+    secs = sum(r[0] for r in res)
+    total_bytes = sum(r[1] for r in res)
+    per_unit_s = secs / len(res)
+    # the cores work on units side by side: throughput = cores x one core's rate
+    return {"value": round(total_bytes / secs * cores / 1e9, 4), "unit": "GB/s",
+            "cores": cores, "kind": "oracle",
+            "keys_per_s": round(tokens * cores / per_unit_s, 1),
             "per_unit_ms": round(per_unit_s * 1e3, 2),
-            # the sample's per-unit time scaled to every unit of the step and
-            # all n tokens: an extrapolation, not a measurement
-            "step_s_extrapolated": round(per_unit_s * (n / tokens) * step_units, 2),
-            "sample": (f"oracle depth allocation + scan of {len(units)} units (sequence 0, "
-                       f"layers {sorted({u[1] for u in units})}, all KV heads) of the same "
-                       f"workload, first {tokens} tokens each, P={budget}, one thread; "
-                       f"{total_s:.1f} s timed")}
+            "cpu_s": round(secs, 1),
+            # the sample's per-unit time scaled to every unit of the step, all n
+            # tokens and the cores used: an extrapolation, not a measurement
+            "step_s_extrapolated": round(per_unit_s * (n / tokens) * step_units / cores, 2),
+            "sample": (f"oracle decode step (depth allocation, scan, top-k, attention; not the "
+                       f"encoding) of {len(units)} units (sequence 0, layers "
+                       f"{sorted({u[1] for u in units})}, all KV heads) of the same workload, "
+                       f"first {tokens} tokens each, P={budget}, k={k}, one unit at a time per "
+                       f"process on {cores} host cores; {secs:.1f} s of CPU work, "
+                       f"{wall:.1f} s wall")}
 
 
 def main() -> int:
@@ -143,8 +180,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the sweep over the workload's plane budgets (profiling runs)")
-    ap.add_argument("--cpu-tokens", type=int, default=1 << 20)
-    ap.add_argument("--cpu-layers", type=int, default=2)
+    ap.add_argument("--cpu-tokens", type=int, default=1 << 18)
+    ap.add_argument("--cpu-layers", type=int, default=4)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -189,27 +226,56 @@ def main() -> int:
                 bpk.encode_append(cache, s, None, None, 1)
         bpk.decode_step(cache, q, 0, L, p, k, scale, out=out, ws=ws)
 
-    def traced(p, steps):
-        """Per-stage milliseconds of `steps` decode steps at budget p (stage
-        tracing: HIP events around each stage on the step's stream)."""
+    def traced(steps, fn):
+        """Median milliseconds of each decode-step stage over `steps` calls of
+        fn (stage tracing: HIP events the library records around each stage
+        on the step's stream, read back after every call)."""
+        per = {name: [] for name in bpk.STAGES}
         bpk.trace_enable(True)
         try:
             for _ in range(steps):
-                step(p)
-            ms, calls = bpk.trace_read()
+                fn()
+                ms, calls = bpk.trace_read(reset=True)
+                for name, v in ms.items():
+                    per[name].append(v / max(calls, 1))
         finally:
             bpk.trace_enable(False)
-        return {name: v / calls for name, v in ms.items()}
+        return {name: float(statistics.median(v)) if v else 0.0 for name, v in per.items()}
+
+    def bits_of(d_np):
+        return float(np.mean([float(t.sum()) + 0.25 * float((t > 0).sum())
+                              for t in d_np.reshape(-1, 128)]))
+
+    def kernel_label(d_np):
+        rows = int(d_np.reshape(-1, 128).sum(axis=1).max())
+        if rows <= 96:
+            return f"scan_fast_kernel<{cfg.group}, 2, 96>"
+        if rows <= 128:
+            return f"scan_fast_kernel<{cfg.group}, 2, 128>"
+        return f"scan_wide_kernel<{cfg.group}, 2>"
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     log("warmup done")
     ms_step = time_launches(step, args.steps)
-    log(f"decode step: {ms_step * 1e3:.1f} us")
-    stage_ms = traced(budget, args.steps)
+    log(f"decode step (median): {ms_step * 1e3:.1f} us")
+    stage_ms = traced(args.steps, step)
     ms_scan = stage_ms["scan"]
-    log("stages (us): " + " ".join(f"{n} {v * 1e3:.1f}" for n, v in stage_ms.items()))
+    log("stages, median us: " + " ".join(f"{nm} {v * 1e3:.1f}" for nm, v in stage_ms.items()))
+    flagged = bpk.decode_fallback_units(cache, 0, L, k, ws)
+    log(f"units redone unfused in the last step: {flagged} of {cfg.units}")
+
+    # attention: the union of the heads' selections, fetched once per unit
+    idx = torch.empty((cfg.seqs, L, cfg.heads, cfg.group, k), dtype=torch.int32, device="cuda")
+    bpk.decode_step(cache, q, 0, L, budget, k, scale, out=out, idx_out=idx, ws=ws)
+    srt = idx.reshape(-1, cfg.group * k).sort(dim=1).values
+    uniq = (srt[:, 1:] != srt[:, :-1]).sum(dim=1) + 1
+    union_rows = int(uniq.sum().item())
+    row_bytes = 128 * (4 if cfg.k_dtype == "f32" else 2) + 128 * 2
+    attend_bytes = union_rows * row_bytes
+    log(f"union rows {union_rows} ({union_rows / cfg.units:.0f} per unit), "
+        f"attention {attend_bytes / (stage_ms['attend'] * 1e-3) / 1e9:.0f} GB/s")
 
     # the workload's other plane budgets: does the step scale with the bits read?
     sweep = {}
@@ -217,17 +283,51 @@ def main() -> int:
         for p in cfg.budgets:
             d_p, _ = bpk.alloc_depth(cache, q, 0, L, p)
             d_np = d_p.cpu().numpy()
-            bits_p = float(np.mean([float(t.sum()) + 0.25 * float((t > 0).sum())
-                                    for t in d_np.reshape(-1, 128)]))
             for _ in range(2):
                 step(p)
             ms_p = time_launches(lambda: step(p), args.steps)
-            st_p = traced(p, args.steps)
-            sweep[str(p)] = {"bits_per_token": round(bits_p, 2),
+            st_p = traced(args.steps, lambda: step(p))
+            sweep[str(p)] = {"bits_per_token": round(bits_of(d_np), 2),
                              "decode_step_us": round(ms_p * 1e3, 1),
                              "scan_us": round(st_p["scan"] * 1e3, 1),
                              "scan_gbs": round(scan_bytes(d_np, n) / (st_p["scan"] * 1e-3) / 1e9, 2)}
             log(f"P={p}: {sweep[str(p)]}")
+
+    # the fixed-depth scans the Fathom page compares against (§2), on the
+    # same planes and through the same scan, selection and attention:
+    # SparQ r = 16 and 32, Double Sparsity's static c = 32 channels, the
+    # 2-bit thumbnail.  Double Sparsity's offline channel sets come from the
+    # workload's own statistics (mean|q| equal on every channel, mean|k_j|
+    # proportional to sigma_j).
+    baselines = {}
+    if not appends and not args.no_sweep:
+        ds = np.zeros((L, cfg.heads, 32), dtype=np.uint8)
+        for l in range(L):
+            for h in range(cfg.heads):
+                ds[l, h] = np.sort(np.lexsort((np.arange(128), -cfg.chan_var(0, l, h)))[:32])
+        ds_t = torch.from_numpy(ds).cuda()
+        rules = {"sparq_r16": (bpk.BPK_DEPTH_SPARQ, 16, None),
+                 "sparq_r32": (bpk.BPK_DEPTH_SPARQ, 32, None),
+                 "double_sparsity_c32": (bpk.BPK_DEPTH_CHANNELS, 32, ds_t),
+                 "thumbnail_2bit": (bpk.BPK_DEPTH_UNIFORM, 2, None)}
+        dq = torch.empty((cfg.seqs, L, cfg.heads, 128), dtype=torch.uint8, device="cuda")
+        qbq = torch.empty((cfg.seqs, L, cfg.heads, cfg.group, 128), dtype=torch.float32,
+                          device="cuda")
+        for name, (rule, param, ch) in rules.items():
+            def bstep(rule=rule, param=param, ch=ch):
+                bpk.fixed_depth(cache, q, 0, L, rule, param, channels=ch, depth=dq, q_basis=qbq)
+                bpk.decode_step_depth(cache, q, qbq, dq, 0, L, k, scale, out=out, ws=ws)
+            for _ in range(2):
+                bstep()
+            ms_b = time_launches(bstep, args.steps)
+            st_b = traced(args.steps, bstep)
+            d_np = dq.cpu().numpy()
+            baselines[name] = {"bits_per_token": round(bits_of(d_np), 2),
+                               "decode_step_us": round(ms_b * 1e3, 1),
+                               "scan_us": round(st_b["scan"] * 1e3, 1),
+                               "scan_gbs": round(scan_bytes(d_np, n) / (st_b["scan"] * 1e-3) / 1e9, 2),
+                               "units_redone": bpk.decode_fallback_units(cache, 0, L, k, ws)}
+            log(f"{name}: {baselines[name]}")
 
     # the standalone full scan (scan_scores writes every score: same reads,
     # plus 16 bytes of scores per token)
@@ -242,19 +342,26 @@ def main() -> int:
     del scores
     log(f"standalone full scan: {ms_full * 1e3:.1f} us")
 
-    # the practical streaming ceiling: a plain device copy of 2 GiB (read + write),
-    # also the known-size kernel the HBM byte counters are scaled by
+    # streaming ceilings on this GPU: a plain copy of 2 GiB (read + write;
+    # also the known-size kernel the HBM byte counters are scaled by) and a
+    # plain streaming read of 4 GiB (16-byte loads, four in flight a thread)
     cx = torch.ones(1 << 29, dtype=torch.float32, device="cuda")
     cy = torch.empty_like(cx)
     torch.mul(cx, 1.0, out=cy)  # the first launch loads the kernel's code object
     ms_copy = time_launches(lambda: torch.mul(cx, 1.0, out=cy), args.steps)
     copy_gbs = 2 * cx.numel() * 4 / (ms_copy * 1e-3) / 1e9
     del cx, cy
-    log(f"plain copy of 2 GiB: {ms_copy * 1e3:.1f} us, {copy_gbs:.0f} GB/s")
+    from synth import device as synth_device
+    rx = torch.ones(1 << 30, dtype=torch.float32, device="cuda")
+    acc = torch.empty(4096, dtype=torch.int32, device="cuda")
+    synth_device.stream_read(rx, acc)
+    ms_read = time_launches(lambda: synth_device.stream_read(rx, acc), args.steps)
+    read_gbs = rx.numel() * 4 / (ms_read * 1e-3) / 1e9
+    del rx, acc
+    log(f"plain copy of 2 GiB: {copy_gbs:.0f} GB/s; streaming read of 4 GiB: {read_gbs:.0f} GB/s")
 
     d = depth.cpu().numpy()
     sbytes = scan_bytes(d, n)
-    bits = [float(t.sum()) + 0.25 * float((t > 0).sum()) for t in d.reshape(-1, 128)]
     scan_gbs = sbytes / (ms_scan * 1e-3) / 1e9
     units = cfg.units
     keys_per_s = units * n / (ms_scan * 1e-3)
@@ -270,7 +377,9 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "i8",
+        # int8 digits of 29-bit fixed-point weights times 0/1 plane bits,
+        # accumulated exactly in int32 on the matrix cores
+        "dtype": "i8xbit->i32 (29-bit fixed point)",
         "data": "synthetic",
         "config": {
             "workload": (f"{cfg.name}: {cfg.seqs} seq x {cfg.layers} layers x {cfg.heads} KV "
@@ -286,24 +395,30 @@ def main() -> int:
             "traffic": counted_traffic(cfg.name, budget),
             "valu_busy_percent": counted_valu(cfg.name, budget)[0],
             "valu_insts_per_block": counted_valu(cfg.name, budget)[1],
-            "kernel": "scan_fast_kernel<4, 2, true, 96> (the decode step's candidate scan)",
+            "kernel": kernel_label(d) + " (the decode step's candidate scan)",
             "bytes_per_launch": sbytes,
             "avg_launch_us": round(ms_scan * 1e3, 2),
+            "timing": "median of HIP-event stage times",
         },
         "decode_step_us": round(ms_step * 1e3, 1),
         "stage_us": {name: round(v * 1e3, 1) for name, v in stage_ms.items()},
+        "units_redone_unfused": flagged,
+        "attend": {"union_rows": union_rows, "bytes": attend_bytes,
+                   "gbs": round(attend_bytes / (stage_ms["attend"] * 1e-3) / 1e9, 1)},
         "full_scan_us": round(ms_full * 1e3, 1),
         "full_scan_gbs": round(sbytes / (ms_full * 1e-3) / 1e9, 2),
         "keys_per_s": round(keys_per_s, 0),
         "copy_gbs": round(copy_gbs, 1),
-        "scan_bits_per_token_mean": round(float(np.mean(bits)), 2),
+        "read_ceiling_gbs": round(read_gbs, 1),
+        "scan_bits_per_token_mean": round(bits_of(d), 2),
         "budget_sweep": sweep,
+        "baselines": baselines,
     }
     if not args.no_cpu_baseline:
         log("timing the oracle on a CPU sample")
         sample_units = [(0, l, h) for l in range(min(args.cpu_layers, L)) for h in range(cfg.heads)]
-        result["cpu_baseline"] = cpu_baseline(cfg, cache, budget, min(args.cpu_tokens, n),
-                                              sample_units, n, cfg.units)
+        result["cpu_baseline"] = cpu_baseline(cfg, budget, min(args.cpu_tokens, n),
+                                              sample_units, n, cfg.units, k, scale)
     print(json.dumps(result), flush=True)
     return 0
 

@@ -9,6 +9,10 @@ from ._lib import (  # noqa: F401
     BPK_OP_ATTEND,
     BPK_OP_DECODE,
     BPK_OP_SELECT,
+    BPK_DEPTH_CHANNELS,
+    BPK_DEPTH_SPARQ,
+    BPK_DEPTH_UNIFORM,
+    BPK_DEPTH_WATERFILL,
     EXPORTS,
     HEAD_DIM,
     LIB_PATH,
@@ -18,6 +22,8 @@ from ._lib import (  # noqa: F401
     Cache,
     alloc_depth,
     decode_step,
+    decode_step_depth,
+    fixed_depth,
     decode_fallback_units,
     decode_step_noalloc,
     NOALLOC_SCRATCH_BYTES,

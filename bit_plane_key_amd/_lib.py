@@ -21,10 +21,11 @@ LIB_PATH = os.path.join(_HERE, "libbpk.so")
 BPK_OK, BPK_EINVAL, BPK_EUNSUPPORTED, BPK_EWORKSPACE, BPK_ECAPACITY, BPK_EHIP = 0, -1, -2, -3, -4, -5
 BPK_F32, BPK_BF16 = 0, 1
 BPK_OP_SELECT, BPK_OP_ATTEND, BPK_OP_DECODE = 3, 4, 5
+BPK_DEPTH_WATERFILL, BPK_DEPTH_SPARQ, BPK_DEPTH_CHANNELS, BPK_DEPTH_UNIFORM = 0, 1, 2, 3
 HEAD_DIM, BLOCK, PLANES = 128, 64, 4
 
-EXPORTS = ("bpk_encode_append", "bpk_alloc_depth", "bpk_scan_scores", "bpk_select_topk",
-           "bpk_sparse_attend", "bpk_decode_step", "bpk_decode_step_noalloc", "bpk_decode_fallback_units", "bpk_workspace_bytes", "bpk_last_error",
+EXPORTS = ("bpk_encode_append", "bpk_alloc_depth", "bpk_fixed_depth", "bpk_scan_scores", "bpk_select_topk",
+           "bpk_sparse_attend", "bpk_decode_step", "bpk_decode_step_depth", "bpk_decode_step_noalloc", "bpk_decode_fallback_units", "bpk_workspace_bytes", "bpk_last_error",
            "bpk_trace_enable", "bpk_trace_read")
 STAGES = ("alloc", "sample", "threshold", "scan", "select", "fallback", "attend")
 
@@ -69,10 +70,12 @@ def _load() -> ctypes.CDLL:
     sig = {
         "bpk_encode_append": (ctypes.c_int, [C, I32, P, P, I64, P]),
         "bpk_alloc_depth": (ctypes.c_int, [C, P, I32, I32, I32, P, P, P]),
+        "bpk_fixed_depth": (ctypes.c_int, [C, P, I32, I32, I32, I32, P, P, P, P]),
         "bpk_scan_scores": (ctypes.c_int, [C, P, P, I32, I32, P, P]),
         "bpk_select_topk": (ctypes.c_int, [C, P, I32, I32, I32, P, P, SZ, P]),
         "bpk_sparse_attend": (ctypes.c_int, [C, P, P, I32, I32, I32, F, P, P, SZ, P]),
         "bpk_decode_step": (ctypes.c_int, [C, P, I32, I32, I32, I32, F, P, P, P, P, SZ, P]),
+        "bpk_decode_step_depth": (ctypes.c_int, [C, P, P, P, I32, I32, I32, F, P, P, P, SZ, P]),
         "bpk_decode_step_noalloc": (ctypes.c_int, [C, P, I32, I32, I32, I32, F, P, P, P, P]),
         "bpk_decode_fallback_units": (ctypes.c_int, [C, I32, I32, I32, P, SZ, P, P]),
         "bpk_workspace_bytes": (ctypes.c_size_t, [C, I32, I32, I32, I32]),
@@ -203,6 +206,26 @@ def alloc_depth(cache: Cache, q: torch.Tensor, l0: int, l1: int, budget: int, de
     return depth, q_basis
 
 
+def fixed_depth(cache: Cache, q: torch.Tensor, l0: int, l1: int, rule: int, param: int,
+                channels=None, depth=None, q_basis=None, stream=None):
+    """A baseline depth rule (BPK_DEPTH_SPARQ / _CHANNELS / _UNIFORM, see bpk.h);
+    channels: uint8 [L][H][param] on the GPU for BPK_DEPTH_CHANNELS."""
+    u = (cache.S, l1 - l0, cache.H)
+    _need(q, "q", torch.bfloat16, (*u, cache.G, HEAD_DIM))
+    if depth is None:
+        depth = torch.empty((*u, HEAD_DIM), dtype=torch.uint8, device=q.device)
+    if q_basis is None:
+        q_basis = torch.empty((*u, cache.G, HEAD_DIM), dtype=torch.float32, device=q.device)
+    _need(depth, "depth", torch.uint8, (*u, HEAD_DIM))
+    _need(q_basis, "q_basis", torch.float32, (*u, cache.G, HEAD_DIM))
+    if channels is not None:
+        _need(channels, "channels", torch.uint8, (cache.L, cache.H, param))
+    _check(LIB.bpk_fixed_depth(cache.struct(), q.data_ptr(), l0, l1, int(rule), int(param),
+                               _ptr(channels), depth.data_ptr(), q_basis.data_ptr(),
+                               _stream(stream)))
+    return depth, q_basis
+
+
 def scan_scores(cache: Cache, q_basis: torch.Tensor, depth: torch.Tensor, l0: int, l1: int,
                 scores=None, stream=None):
     u = (cache.S, l1 - l0, cache.H)
@@ -264,6 +287,29 @@ def decode_step(cache: Cache, q: torch.Tensor, l0: int, l1: int, budget: int, k:
     _check(LIB.bpk_decode_step(cache.struct(), q.data_ptr(), l0, l1, int(budget), int(k),
                                float(softmax_scale), out.data_ptr(), _ptr(depth_out),
                                _ptr(idx_out), ws.data_ptr(), ws.numel(), _stream(stream)))
+    return out
+
+
+def decode_step_depth(cache: Cache, q: torch.Tensor, q_basis: torch.Tensor, depth: torch.Tensor,
+                      l0: int, l1: int, k: int, softmax_scale: float, out=None, idx_out=None,
+                      ws=None, stream=None):
+    """decode_step on given depths (from alloc_depth or fixed_depth)."""
+    u = (cache.S, l1 - l0, cache.H)
+    _need(q, "q", torch.bfloat16, (*u, cache.G, HEAD_DIM))
+    _need(q_basis, "q_basis", torch.float32, (*u, cache.G, HEAD_DIM))
+    _need(depth, "depth", torch.uint8, (*u, HEAD_DIM))
+    if out is None:
+        out = torch.empty((*u, cache.G, HEAD_DIM), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.float32, (*u, cache.G, HEAD_DIM))
+    if idx_out is not None:
+        _need(idx_out, "idx_out", torch.int32, (*u, cache.G, k))
+    need = workspace_bytes(cache, BPK_OP_DECODE, l0, l1, k)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(LIB.bpk_decode_step_depth(cache.struct(), q.data_ptr(), q_basis.data_ptr(),
+                                     depth.data_ptr(), l0, l1, int(k), float(softmax_scale),
+                                     out.data_ptr(), _ptr(idx_out), ws.data_ptr(), ws.numel(),
+                                     _stream(stream)))
     return out
 
 

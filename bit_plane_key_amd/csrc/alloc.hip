@@ -5,6 +5,12 @@
 // candidate is found by a 41-step bitwise search over the totally ordered keys
 // (value bits << 9 | 511 - (4 j + t)), counting with wave ballots, and a
 // channel's depth is the number of its candidates at or above that key.
+//
+// The same kernel also writes the fixed depth vectors of the baselines the
+// Fathom page compares against (§2): SparQ's r channels of largest summed
+// |q| over the group at full depth (the r-th largest found by the same kind
+// of bitwise search), a static channel set at full depth (Double Sparsity),
+// or one depth for every channel (t = 2: the 2-bit thumbnail scan).
 #include "bpk_internal.h"
 
 namespace bpk {
@@ -15,14 +21,17 @@ struct AllocArgs {
   const uint16_t* q;
   const float* chan_var;
   const float* rot;
-  int budget;
+  int budget;  // WATERFILL: planes; SPARQ: r; CHANNELS: c; UNIFORM: t
   uint8_t* depth;
   float* q_basis;
+  int rule;                 // BPK_DEPTH_*
+  const uint8_t* channels;  // CHANNELS: [L][H][c] channel indices
 };
 
 template <int G, bool ROT>
 __global__ __launch_bounds__(64) void alloc_kernel(AllocArgs a) {
   __shared__ float sq[ROT ? G : 1][ROT ? D : 1];
+  __shared__ uint8_t chosen[D];
   const int u = blockIdx.x;
   const long long gu = a.g.global_unit(u);
   const int lane = threadIdx.x;
@@ -66,6 +75,51 @@ __global__ __launch_bounds__(64) void alloc_kernel(AllocArgs a) {
 #pragma unroll
     for (int c = 0; c < 2; ++c) qbo[h * D + 2 * lane + c] = qb[h][c];
 
+  uint8_t* dep = a.depth + (long long)u * D;
+  if (a.rule == BPK_DEPTH_UNIFORM) {
+    const uint8_t v = (uint8_t)(a.budget < 0 ? 0 : (a.budget > NP ? NP : a.budget));
+    dep[2 * lane] = v;
+    dep[2 * lane + 1] = v;
+    return;
+  }
+  if (a.rule == BPK_DEPTH_CHANNELS) {
+    const int c = a.budget < 0 ? 0 : (a.budget > D ? D : a.budget);
+    const int l = a.g.l0 + (u / a.g.H) % a.g.nl;
+    const uint8_t* list = a.channels + (long long)(l * a.g.H + u % a.g.H) * c;
+    chosen[2 * lane] = chosen[2 * lane + 1] = 0;
+    __syncthreads();
+    for (int e = lane; e < c; e += 64)
+      if (list[e] < D) chosen[list[e]] = 1;  // indices past the head size are ignored
+    __syncthreads();
+    dep[2 * lane] = chosen[2 * lane] ? NP : 0;
+    dep[2 * lane + 1] = chosen[2 * lane + 1] ? NP : 0;
+    return;
+  }
+  if (a.rule == BPK_DEPTH_SPARQ) {
+    // s_j = |q_0j| + |q_1j| + ... (fp32, heads ascending); the r largest
+    // (s, then the lower channel) are read at full depth
+    const int take = a.budget < 0 ? 0 : (a.budget > D ? D : a.budget);
+    uint64_t key[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      float acc = 0.f;
+#pragma unroll
+      for (int h = 0; h < G; ++h) acc = __fadd_rn(acc, fabsf(qb[h][c]));
+      key[c] = ((uint64_t)__float_as_uint(acc) << 7) | (uint64_t)(127u - (2 * lane + c));
+    }
+    uint64_t prefix = 0;
+    if (take > 0) {
+      for (int b = 38; b >= 0; --b) {
+        const uint64_t cand = prefix | (1ull << b);
+        const int cnt = __popcll(__ballot(key[0] >= cand)) + __popcll(__ballot(key[1] >= cand));
+        if (cnt >= take) prefix = cand;
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < 2; ++c) dep[2 * lane + c] = (take > 0 && key[c] >= prefix) ? NP : 0;
+    return;
+  }
+
   // g_j = var_j * (((q_0j^2 + q_1j^2) + ...) + q_(G-1)j^2), one rounding per op
   float gain[2];
 #pragma unroll
@@ -76,7 +130,6 @@ __global__ __launch_bounds__(64) void alloc_kernel(AllocArgs a) {
     gain[c] = __fmul_rn(a.chan_var[gu * D + 2 * lane + c], acc);
   }
 
-  uint8_t* dep = a.depth + (long long)u * D;
   const int take = a.budget < NP * D ? a.budget : NP * D;
   if (take <= 0 || take >= NP * D) {
     const uint8_t v = take <= 0 ? 0 : NP;
@@ -126,8 +179,9 @@ void launch_g(const AllocArgs& a, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_alloc(const Geom& g, const uint16_t* q, const float* chan_var, const float* rot,
-                        int budget, uint8_t* depth, float* q_basis, hipStream_t st) {
-  AllocArgs a{g, q, chan_var, rot, budget, depth, q_basis};
+                        int budget, uint8_t* depth, float* q_basis, hipStream_t st, int rule,
+                        const uint8_t* channels) {
+  AllocArgs a{g, q, chan_var, rot, budget, depth, q_basis, rule, channels};
   switch (g.G) {
     case 1: launch_g<1>(a, st); break;
     case 2: launch_g<2>(a, st); break;

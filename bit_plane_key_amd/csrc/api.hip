@@ -232,6 +232,33 @@ int bpk_alloc_depth(const bpk_cache_t* c, const uint16_t* q, int32_t l0, int32_t
                     "alloc_depth");
 }
 
+int bpk_fixed_depth(const bpk_cache_t* c, const uint16_t* q, int32_t l0, int32_t l1,
+                    int32_t rule, int32_t param, const uint8_t* channels, uint8_t* depth,
+                    float* q_basis, void* stream) {
+  bpk::Geom g;
+  int rc = check_cache(c, l0, l1, &g);
+  if (rc) return rc;
+  if (!q || !depth || !q_basis) return fail(BPK_EINVAL, "q, depth and q_basis must be non-NULL");
+  switch (rule) {
+    case BPK_DEPTH_SPARQ:
+    case BPK_DEPTH_CHANNELS:
+      if (param < 0 || param > bpk::D)
+        return fail(BPK_EINVAL, "param %d outside [0, %d]", param, bpk::D);
+      if (rule == BPK_DEPTH_CHANNELS && !channels && param > 0)
+        return fail(BPK_EINVAL, "channels must be non-NULL");
+      break;
+    case BPK_DEPTH_UNIFORM:
+      if (param < 0 || param > bpk::NP)
+        return fail(BPK_EINVAL, "depth %d outside [0, %d]", param, bpk::NP);
+      break;
+    default:
+      return fail(BPK_EINVAL, "depth rule %d invalid", rule);
+  }
+  return hip_status(bpk::launch_alloc(g, q, c->chan_var, c->rot, param, depth, q_basis,
+                                      static_cast<hipStream_t>(stream), rule, channels),
+                    "fixed_depth");
+}
+
 int bpk_scan_scores(const bpk_cache_t* c, const float* q_basis, const uint8_t* depth, int32_t l0,
                     int32_t l1, float* scores, void* stream) {
   bpk::Geom g;
@@ -281,21 +308,26 @@ namespace {
 
 // The decode step on a workspace the caller has checked (ws holds at least
 // decode_ws(g, k).total bytes); `traced` lets stage tracing record events.
+// With depth_in and qb_in given, the allocation is skipped and those are scanned.
 int decode_step_impl(const bpk_cache_t* c, const bpk::Geom& g, const uint16_t* q,
                      int32_t budget_planes, int32_t k, float softmax_scale, float* out,
                      uint8_t* depth_out, int32_t* idx_out, char* base, bool traced,
-                     hipStream_t st) {
+                     hipStream_t st, const uint8_t* depth_in = nullptr,
+                     const float* qb_in = nullptr) {
   const DecodeWs w = decode_ws(g, k);
-  float* q_basis = reinterpret_cast<float*>(base + w.q_basis);
-  uint8_t* depth = depth_out ? depth_out : reinterpret_cast<uint8_t*>(base + w.depth);
+  const bool given = depth_in != nullptr;
+  float* q_basis = given ? const_cast<float*>(qb_in) : reinterpret_cast<float*>(base + w.q_basis);
+  uint8_t* depth = given ? const_cast<uint8_t*>(depth_in)
+                         : depth_out ? depth_out : reinterpret_cast<uint8_t*>(base + w.depth);
   float* scores = reinterpret_cast<float*>(base + w.scores);
   int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(base + w.idx);
   int rc = BPK_OK;
-  // alloc_depth hands out exactly min(P, 4D) planes per unit
-  const int rows = budget_planes < 4 * bpk::D ? budget_planes : 4 * bpk::D;
+  // alloc_depth hands out exactly min(P, 4D) planes per unit; given depths:
+  // not known on the host
+  const int rows = given ? -1 : budget_planes < 4 * bpk::D ? budget_planes : 4 * bpk::D;
   if (traced && g_trace.on) ++g_trace.calls;
   auto timer = [&](int stage) { return StageTimer(stage, st, traced); };
-  {
+  if (!given) {
     auto t = timer(BPK_STAGE_ALLOC);
     rc = hip_status(bpk::launch_alloc(g, q, c->chan_var, c->rot, budget_planes, depth, q_basis, st),
                     "decode_step/alloc");
@@ -414,6 +446,22 @@ int bpk_decode_step(const bpk_cache_t* c, const uint16_t* q, int32_t l0, int32_t
     return fail(BPK_EWORKSPACE, "workspace of %zu bytes < %zu needed", ws_bytes, need);
   return decode_step_impl(c, g, q, budget_planes, k, softmax_scale, out, depth_out, idx_out,
                           static_cast<char*>(ws), true, static_cast<hipStream_t>(stream));
+}
+
+int bpk_decode_step_depth(const bpk_cache_t* c, const uint16_t* q, const float* q_basis,
+                          const uint8_t* depth, int32_t l0, int32_t l1, int32_t k,
+                          float softmax_scale, float* out, int32_t* idx_out, void* ws,
+                          size_t ws_bytes, void* stream) {
+  bpk::Geom g;
+  int rc = check_decode(c, l0, l1, q, 0, k, out, &g);
+  if (rc) return rc;
+  if (!q_basis || !depth) return fail(BPK_EINVAL, "q_basis and depth must be non-NULL");
+  const size_t need = decode_ws(g, k).total;
+  if (!ws || ws_bytes < need)
+    return fail(BPK_EWORKSPACE, "workspace of %zu bytes < %zu needed", ws_bytes, need);
+  return decode_step_impl(c, g, q, 0, k, softmax_scale, out, nullptr, idx_out,
+                          static_cast<char*>(ws), true, static_cast<hipStream_t>(stream), depth,
+                          q_basis);
 }
 
 int bpk_decode_step_noalloc(const bpk_cache_t* c, const uint16_t* q, int32_t l0, int32_t l1,

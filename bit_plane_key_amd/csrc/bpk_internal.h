@@ -43,8 +43,11 @@ hipError_t launch_append_rows(const Geom& g, int seq, int k_dtype, const void* k
                               const uint16_t* v_new, long long n0, long long n_new, void* k_rows,
                               uint16_t* v_rows, hipStream_t st);
 
+// depth allocation (rule BPK_DEPTH_WATERFILL, budget = planes) or a fixed
+// baseline depth rule (budget = its parameter, channels its channel lists)
 hipError_t launch_alloc(const Geom& g, const uint16_t* q, const float* chan_var, const float* rot,
-                        int budget, uint8_t* depth, float* q_basis, hipStream_t st);
+                        int budget, uint8_t* depth, float* q_basis, hipStream_t st,
+                        int rule = BPK_DEPTH_WATERFILL, const uint8_t* channels = nullptr);
 
 // Every scan launcher takes `rows`, the number of plane rows every unit of
 // the call reads (min(P, 4D) after alloc_depth), or -1 when it is not known:

@@ -137,6 +137,34 @@ int bpk_encode_append(const bpk_cache_t* cache, int32_t seq, const void* k_new,
 int bpk_alloc_depth(const bpk_cache_t* cache, const uint16_t* q, int32_t l0, int32_t l1,
                     int32_t budget_planes, uint8_t* depth, float* q_basis, void* stream);
 
+/* Depth rules of bpk_fixed_depth: the fixed-depth scans the Fathom page
+ * compares its per-query depths against (§2), run on the same planes. */
+enum bpk_depth_rule {
+  BPK_DEPTH_WATERFILL = 0, /* bpk_alloc_depth's rule (not accepted by bpk_fixed_depth) */
+  BPK_DEPTH_SPARQ = 1,     /* param r: the r channels of largest sum_h |q_hj| at depth 4 */
+  BPK_DEPTH_CHANNELS = 2,  /* param c: a static set of c channels at depth 4 (Double Sparsity) */
+  BPK_DEPTH_UNIFORM = 3    /* param t: every channel at depth t (t = 2: the 2-bit thumbnail) */
+};
+
+/*
+ * Fixed-depth baselines (Fathom §2, "SparQ", "Double Sparsity", thumbnail
+ * scan), written in the form bpk_alloc_depth writes, so that bpk_scan_scores
+ * and bpk_decode_step_depth run them on the same planes:
+ * - BPK_DEPTH_SPARQ, param r in [0, 128]: s_j = sum_h |q_hj| over the group's
+ *   query heads (fp32, heads ascending, in the scan basis); the r largest
+ *   (equal sums: lower channel first) get depth 4, the others 0.
+ * - BPK_DEPTH_CHANNELS, param c in [0, 128]: channels, DEVICE [L][H][c] uint8,
+ *   the channel indices of each (layer, KV head), chosen offline; those get
+ *   depth 4, the others 0 (indices >= 128 are ignored).
+ * - BPK_DEPTH_UNIFORM, param t in [0, 4]: every channel gets depth t.
+ * q, q_basis and depth as in bpk_alloc_depth (q_basis is written for every
+ * rule).  channels is only read by BPK_DEPTH_CHANNELS (may be NULL otherwise).
+ * Errors: BPK_EINVAL (bad rule, param out of range, NULL pointer).
+ */
+int bpk_fixed_depth(const bpk_cache_t* cache, const uint16_t* q, int32_t l0, int32_t l1,
+                    int32_t rule, int32_t param, const uint8_t* channels, uint8_t* depth,
+                    float* q_basis, void* stream);
+
 /*
  * Key scan (Fathom §1, §3.2): approximate scores of every token of every
  * complete block, reading only planes p < depth_j of each channel and the
@@ -194,6 +222,20 @@ int bpk_decode_step(const bpk_cache_t* cache, const uint16_t* q, int32_t l0, int
                     int32_t budget_planes, int32_t k, float softmax_scale, float* out,
                     uint8_t* depth_out, int32_t* idx_out, void* ws, size_t ws_bytes,
                     void* stream);
+
+/*
+ * bpk_decode_step on depths the caller gives (for instance from
+ * bpk_fixed_depth) instead of its own allocation: scan -> select -> attend
+ * exactly as bpk_decode_step does after bpk_alloc_depth.  q_basis
+ * [S][nl][H][G][128] fp32 and depth [S][nl][H][128] uint8 as bpk_alloc_depth
+ * or bpk_fixed_depth writes them; q bf16 for the attention; the other
+ * arguments, the workspace (bpk_workspace_bytes(.., BPK_OP_DECODE, ..)) and
+ * the errors as bpk_decode_step.
+ */
+int bpk_decode_step_depth(const bpk_cache_t* cache, const uint16_t* q, const float* q_basis,
+                          const uint8_t* depth, int32_t l0, int32_t l1, int32_t k,
+                          float softmax_scale, float* out, int32_t* idx_out, void* ws,
+                          size_t ws_bytes, void* stream);
 
 /*
  * bpk_decode_step without a workspace argument, for callers that cannot

@@ -98,9 +98,46 @@ __global__ __launch_bounds__(128) void fill_kernel(FillArgs a) {
   }
 }
 
+// Streaming-read probe of the benchmark: every thread reads 16-byte words
+// in a grid-stride loop (four loads in flight) and folds them into one word
+// per workgroup, so the loads cannot be dropped.  Reads n16 words of buf.
+__global__ __launch_bounds__(256) void stream_read_kernel(const uint4* __restrict__ buf,
+                                                          long long n16, uint32_t* out) {
+  __shared__ uint32_t part[4];
+  const long long stride = (long long)gridDim.x * 256;
+  long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  uint32_t acc = 0;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const uint4 a = buf[i], b = buf[i + stride], c = buf[i + 2 * stride], d = buf[i + 3 * stride];
+    acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^
+           d.z ^ d.w;
+  }
+  for (; i < n16; i += stride) {
+    const uint4 a = buf[i];
+    acc ^= a.x ^ a.y ^ a.z ^ a.w;
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) acc ^= (uint32_t)__shfl_xor((int)acc, off);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) out[blockIdx.x] = part[0] ^ part[1] ^ part[2] ^ part[3];
+}
+
 }  // namespace
 
 extern "C" {
+
+// Read n16 16-byte words of buf (16-byte aligned) with `blocks` workgroups
+// of 256 threads, writing one word per workgroup to out[blocks].  Returns 0,
+// -1 for bad arguments or -5 for a launch error.
+int synth_stream_read(const void* buf, long long n16, int blocks, uint32_t* out, void* stream) {
+  if (!buf || !out || n16 < 0 || blocks < 1 || blocks > 65535 ||
+      (reinterpret_cast<uintptr_t>(buf) & 15) != 0)
+    return -1;
+  stream_read_kernel<<<blocks, 256, 0, static_cast<hipStream_t>(stream)>>>(
+      static_cast<const uint4*>(buf), n16, out);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
 
 // Fill rows [row0, row0 + rows) of `units` units of a [units][cap][128] array.
 // keys [units][2] uint32 and mult [units][128] fp32 are device pointers; rot is

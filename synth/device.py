@@ -28,6 +28,8 @@ def _load():
         P, I, LL = ctypes.c_void_p, ctypes.c_int, ctypes.c_longlong
         lib.synth_fill_rows.restype = ctypes.c_int
         lib.synth_fill_rows.argtypes = [P, P, P, I, I, LL, LL, LL, I, I, P, P]
+        lib.synth_stream_read.restype = ctypes.c_int
+        lib.synth_stream_read.argtypes = [P, LL, I, P, P]
         _lib = lib
     return _lib
 
@@ -61,3 +63,14 @@ def fill_rows(cfg: Config, out: torch.Tensor, which: str, row0: int, rows: int,
     if rc != 0:
         raise RuntimeError(f"synth_fill_rows failed ({rc})")
     torch.cuda.current_stream().synchronize()
+
+
+def stream_read(buf: torch.Tensor, out: torch.Tensor) -> None:
+    """Read every byte of ``buf`` (a benchmark probe of the read bandwidth);
+    ``out`` is an int32 tensor of one word per workgroup."""
+    lib = _load()
+    rc = lib.synth_stream_read(buf.data_ptr(), buf.numel() * buf.element_size() // 16,
+                               out.numel(), out.data_ptr(),
+                               torch.cuda.current_stream().cuda_stream)
+    if rc != 0:
+        raise RuntimeError(f"synth_stream_read failed ({rc})")

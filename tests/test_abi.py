@@ -137,6 +137,24 @@ def test_noalloc_refuses_more_than_its_scratch(lib):
     assert rc == -1
 
 
+def test_fixed_depth_validates(lib):
+    s, n = _cache(lib)
+    c = ctypes.pointer(s)
+    assert lib.LIB.bpk_fixed_depth(c, FAKE, 0, 1, 0, 88, None, FAKE, FAKE, None) == -1   # waterfill
+    assert lib.LIB.bpk_fixed_depth(c, FAKE, 0, 1, 9, 1, None, FAKE, FAKE, None) == -1
+    assert lib.LIB.bpk_fixed_depth(c, FAKE, 0, 1, lib.BPK_DEPTH_SPARQ, 129, None, FAKE, FAKE,
+                                   None) == -1
+    assert lib.LIB.bpk_fixed_depth(c, FAKE, 0, 1, lib.BPK_DEPTH_UNIFORM, 5, None, FAKE, FAKE,
+                                   None) == -1
+    assert lib.LIB.bpk_fixed_depth(c, FAKE, 0, 1, lib.BPK_DEPTH_CHANNELS, 32, None, FAKE, FAKE,
+                                   None) == -1
+    assert lib.LIB.bpk_fixed_depth(c, None, 0, 1, lib.BPK_DEPTH_UNIFORM, 2, None, FAKE, FAKE,
+                                   None) == -1
+    rc = lib.LIB.bpk_decode_step_depth(c, FAKE, None, FAKE, 0, 1, 512, 0.088, FAKE, None, FAKE,
+                                       1 << 30, None)
+    assert rc == -1
+
+
 def test_product_has_no_cpu_path():
     """The package never imports the oracle or any CPU implementation."""
     pkg = os.path.join(ROOT, "bit_plane_key_amd")
