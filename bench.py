@@ -182,6 +182,11 @@ def main() -> int:
                     help="skip the sweep over the workload's plane budgets (profiling runs)")
     ap.add_argument("--cpu-tokens", type=int, default=1 << 18)
     ap.add_argument("--cpu-layers", type=int, default=4)
+    ap.add_argument("--host-resident", action="store_true",
+                    help="rows, planes and scales in pinned host memory, read over the host "
+                         "link (the regime of the Fathom page's measurements)")
+    ap.add_argument("--layers", type=int, default=0,
+                    help="use only the workload's first LAYERS layers (0: all)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -197,11 +202,14 @@ def main() -> int:
     from synth import config_by_name
 
     cfg = config_by_name(args.config)
+    if args.layers:
+        import dataclasses
+        cfg = dataclasses.replace(cfg, layers=min(args.layers, cfg.layers))
     budget, k, n = args.budget, cfg.k, cfg.n
     torch.cuda.set_device(0)
     t0 = time.perf_counter()
     log(f"building {cfg.name}: {cfg.description}")
-    cache = workloads.build_cache(cfg)
+    cache = workloads.build_cache(cfg, host_resident=args.host_resident)
     log(f"cache built in {time.perf_counter() - t0:.1f} s")
     q = workloads.queries(cfg)
     scale = workloads.softmax_scale(cfg)
@@ -359,6 +367,18 @@ def main() -> int:
     read_gbs = rx.numel() * 4 / (ms_read * 1e-3) / 1e9
     del rx, acc
     log(f"plain copy of 2 GiB: {copy_gbs:.0f} GB/s; streaming read of 4 GiB: {read_gbs:.0f} GB/s")
+    link_gbs = None
+    if args.host_resident:
+        # the host link's read ceiling: the same probe over 1 GiB of pinned host memory
+        from bit_plane_key_amd._lib import _device_pointer
+        hx = torch.ones(1 << 28, dtype=torch.float32, pin_memory=True)
+        acc = torch.empty(4096, dtype=torch.int32, device="cuda")
+        synth_device.stream_read(hx, acc, ptr=_device_pointer(hx))
+        ms_link = time_launches(lambda: synth_device.stream_read(hx, acc, ptr=_device_pointer(hx)),
+                                max(3, args.steps // 4))
+        link_gbs = hx.numel() * 4 / (ms_link * 1e-3) / 1e9
+        del hx, acc
+        log(f"streaming read of 1 GiB of pinned host memory: {link_gbs:.1f} GB/s")
 
     d = depth.cpu().numpy()
     sbytes = scan_bytes(d, n)
@@ -383,7 +403,9 @@ def main() -> int:
         "data": "synthetic",
         "config": {
             "workload": (f"{cfg.name}: {cfg.seqs} seq x {cfg.layers} layers x {cfg.heads} KV "
-                         f"heads, G={cfg.group}, D=128, n={n}, P={budget}, k={k}"),
+                         f"heads, G={cfg.group}, D=128, n={n}, P={budget}, k={k}"
+                         + (", rows/planes/scales in pinned host memory" if args.host_resident
+                            else "")),
             "units": units, "n": n, "budget_planes": budget, "k": k,
         },
         "roofline": {
@@ -410,6 +432,7 @@ def main() -> int:
         "keys_per_s": round(keys_per_s, 0),
         "copy_gbs": round(copy_gbs, 1),
         "read_ceiling_gbs": round(read_gbs, 1),
+        "host_link_read_gbs": None if link_gbs is None else round(link_gbs, 1),
         "scan_bits_per_token_mean": round(bits_of(d), 2),
         "budget_sweep": sweep,
         "baselines": baselines,

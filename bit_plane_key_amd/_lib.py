@@ -122,27 +122,58 @@ def _need(t: torch.Tensor, name: str, dtype, shape) -> None:
         raise ValueError(f"{name}: must be a GPU tensor")
 
 
+_HIP = None
+
+
+def _device_pointer(t: torch.Tensor) -> int:
+    """The device address of a tensor: its data pointer on the GPU, or for a
+    pinned host tensor (hipHostMalloc memory) the address under which the
+    GPU reads it over the host link."""
+    global _HIP
+    if t.device.type == "cuda":
+        return t.data_ptr()
+    if not t.is_pinned():
+        raise ValueError("host arrays of a cache must be pinned (pin_memory=True)")
+    if _HIP is None:
+        _HIP = ctypes.CDLL("libamdhip64.so")
+        _HIP.hipHostGetDevicePointer.restype = ctypes.c_int
+        _HIP.hipHostGetDevicePointer.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p,
+                                                 ctypes.c_uint]
+    dptr = ctypes.c_void_p()
+    rc = _HIP.hipHostGetDevicePointer(ctypes.byref(dptr), ctypes.c_void_p(t.data_ptr()), 0)
+    if rc != 0:
+        raise RuntimeError(f"hipHostGetDevicePointer failed ({rc})")
+    return dptr.value
+
+
 class Cache:
     """Caller-owned storage of a bit-plane key cache (see include/bpk.h).
 
-    Device arrays are torch tensors; ``n_tokens`` is a host int64 array the
+    Arrays are torch tensors on the GPU; with ``host_resident`` the key and
+    value rows, the planes and the scales are pinned host memory instead,
+    which the GPU reads over the host link (the regime of the Fathom page's
+    measurements, §1 and §3.1).  ``n_tokens`` is a host int64 array the
     caller advances after appends.
     """
 
     def __init__(self, num_seqs: int, num_layers: int, num_kv_heads: int, capacity: int,
                  group: int = 4, k_dtype: str = "bf16", rotated: bool = False,
-                 device: str = "cuda"):
+                 device: str = "cuda", host_resident: bool = False):
         if capacity % BLOCK:
             raise ValueError("capacity must be a multiple of 64")
         S, L, H, D = num_seqs, num_layers, num_kv_heads, HEAD_DIM
         self.S, self.L, self.H, self.G, self.capacity = S, L, H, group, capacity
         self.k_dtype = k_dtype
+        self.host_resident = host_resident
         kt = torch.float32 if k_dtype == "f32" else torch.bfloat16
-        self.k_rows = torch.empty((S, L, H, capacity, D), dtype=kt, device=device)
-        self.v_rows = torch.empty((S, L, H, capacity, D), dtype=torch.bfloat16, device=device)
+        big = dict(device="cpu", pin_memory=True) if host_resident else dict(device=device)
+        self.k_rows = torch.empty((S, L, H, capacity, D), dtype=kt, **big)
+        self.v_rows = torch.empty((S, L, H, capacity, D), dtype=torch.bfloat16, **big)
         nb = block_stride(capacity)
-        self.planes = torch.zeros((S, L, H, D, PLANES, nb), dtype=torch.int64, device=device)
-        self.scales = torch.zeros((S, L, H, D, nb), dtype=torch.float16, device=device)
+        self.planes = torch.zeros((S, L, H, D, PLANES, nb), dtype=torch.int64, **big)
+        self.scales = torch.zeros((S, L, H, D, nb), dtype=torch.float16, **big)
+        self._ptrs = {name: _device_pointer(getattr(self, name))
+                      for name in ("k_rows", "v_rows", "planes", "scales")}
         self.chan_var = torch.ones((S, L, H, D), dtype=torch.float32, device=device)
         self.rot = (torch.empty((L, H, D, D), dtype=torch.float32, device=device)
                     if rotated else None)
@@ -156,8 +187,8 @@ class Cache:
         s.k_dtype = BPK_F32 if self.k_dtype == "f32" else BPK_BF16
         s.capacity = self.capacity
         s.n_tokens = self.n_tokens.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
-        s.k_rows, s.v_rows = self.k_rows.data_ptr(), self.v_rows.data_ptr()
-        s.planes, s.scales = self.planes.data_ptr(), self.scales.data_ptr()
+        s.k_rows, s.v_rows = self._ptrs["k_rows"], self._ptrs["v_rows"]
+        s.planes, s.scales = self._ptrs["planes"], self._ptrs["scales"]
         s.chan_var = self.chan_var.data_ptr()
         s.rot = None if self.rot is None else self.rot.data_ptr()
         return ctypes.pointer(s)

@@ -19,9 +19,25 @@ from synth import workload as synth_workload
 from ._lib import Cache, encode_append
 
 
-def build_cache(cfg: Config, n: int | None = None, device: str = "cuda") -> Cache:
-    """Allocate the cache of ``cfg``, fill n tokens of rows and encode them."""
+def build_cache(cfg: Config, n: int | None = None, device: str = "cuda",
+                host_resident: bool = False) -> Cache:
+    """Allocate the cache of ``cfg``, fill n tokens of rows and encode them.
+    With host_resident the rows, planes and scales end in pinned host memory
+    (built on the GPU, then copied)."""
     n = cfg.n if n is None else n
+    if host_resident:
+        dev = build_cache(cfg, n, device)
+        cache = Cache(cfg.seqs, cfg.layers, cfg.heads, cfg.capacity, group=cfg.group,
+                      k_dtype=cfg.k_dtype, rotated=cfg.rotated, device=device,
+                      host_resident=True)
+        for name in ("k_rows", "v_rows", "planes", "scales", "chan_var"):
+            getattr(cache, name).copy_(getattr(dev, name))
+        if cfg.rotated:
+            cache.rot.copy_(dev.rot)
+        cache.n_tokens[:] = dev.n_tokens
+        del dev
+        torch.cuda.synchronize()
+        return cache
     cache = Cache(cfg.seqs, cfg.layers, cfg.heads, cfg.capacity, group=cfg.group,
                   k_dtype=cfg.k_dtype, rotated=cfg.rotated, device=device)
     var = np.zeros((cfg.seqs, cfg.layers, cfg.heads, cfg.dim), dtype=np.float32)

@@ -65,11 +65,13 @@ def fill_rows(cfg: Config, out: torch.Tensor, which: str, row0: int, rows: int,
     torch.cuda.current_stream().synchronize()
 
 
-def stream_read(buf: torch.Tensor, out: torch.Tensor) -> None:
+def stream_read(buf: torch.Tensor, out: torch.Tensor, ptr: int | None = None) -> None:
     """Read every byte of ``buf`` (a benchmark probe of the read bandwidth);
-    ``out`` is an int32 tensor of one word per workgroup."""
+    ``out`` is an int32 tensor of one word per workgroup; ``ptr`` is the
+    address the GPU reads buf at (default buf.data_ptr())."""
     lib = _load()
-    rc = lib.synth_stream_read(buf.data_ptr(), buf.numel() * buf.element_size() // 16,
+    rc = lib.synth_stream_read(buf.data_ptr() if ptr is None else ptr,
+                               buf.numel() * buf.element_size() // 16,
                                out.numel(), out.data_ptr(),
                                torch.cuda.current_stream().cuda_stream)
     if rc != 0:
