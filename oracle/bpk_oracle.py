@@ -42,7 +42,7 @@ __all__ = [
     "D", "BLOCK", "PLANES", "FIRST_KEPT", "LAST_KEPT",
     "bf16_bits_to_f32", "block_scales", "quantize_codes", "encode_unit",
     "codes_from_planes", "prefix_values", "channel_gains", "alloc_depth",
-    "alloc_depth_greedy", "sparq_depth", "double_sparsity_channels", "channel_set_depth",
+    "alloc_depth_greedy", "pooled_plane_counts", "calibrate_layer_budgets", "sparq_depth", "double_sparsity_channels", "channel_set_depth",
     "uniform_depth", "scan_scores", "kept_tail", "select_topk",
     "attend", "dense_attention", "rotate_basis", "decode_unit",
     "scan_bits_per_token", "scan_bytes_unit",
@@ -205,6 +205,57 @@ def alloc_depth_greedy(q_basis: np.ndarray, chan_var: np.ndarray, budget: int) -
                     best, best_v = jj, val
         depth[best] += 1
     return depth.astype(np.uint8)
+
+
+# ----------------------------------------------------------------------------
+# per-layer budget calibration
+# ----------------------------------------------------------------------------
+
+def pooled_plane_counts(gains: np.ndarray, budget: int) -> np.ndarray:
+    """Planes each unit receives when the whole budget of units * budget
+    planes is water-filled across units at once.
+
+    [Fathom §3, per-layer budget calibration; the rule itself is not on the
+    page] Reading: the value of a unit's t-th plane of channel j is
+    g_uj * 4^-t as within one unit (Fathom §1 observation 1), and the pooled
+    budget goes to the most valuable (unit, channel, plane) candidates, equal
+    values to the lower unit, then channel, then plane.  ``gains`` is
+    float32 [units][D]; returns int64 [units].
+    """
+    g = np.asarray(gains, dtype=np.float32)
+    nu, nd = g.shape
+    take = min(max(int(budget), 0) * nu, PLANES * nd * nu)
+    u = np.repeat(np.arange(nu), nd * PLANES)
+    j = np.tile(np.repeat(np.arange(nd), PLANES), nu)
+    t = np.tile(np.arange(PLANES), nd * nu)
+    v = (g[u, j] * np.float32(0.25) ** t.astype(np.float32)).astype(np.float32)
+    order = np.lexsort((t, j, u, -v.astype(np.float64)))
+    counts = np.zeros(nu, dtype=np.int64)
+    np.add.at(counts, u[order[:take]], 1)
+    return counts
+
+
+def calibrate_layer_budgets(plane_counts: np.ndarray, budget: int) -> np.ndarray:
+    """Per-layer plane budgets from pooled allocations of calibration queries.
+
+    ``plane_counts`` is [queries][layers][units per layer] (the pooled
+    allocation of each calibration query, pooled over every unit of every
+    layer).  Reading: a layer's budget is the mean count of its units over
+    the queries, rounded by largest remainder (ties to the lower layer) so
+    that the budgets sum to layers * budget, the total a uniform budget
+    spends.
+    """
+    c = np.asarray(plane_counts, dtype=np.int64)
+    nl = c.shape[1]
+    per = c.sum(axis=(0, 2))                       # planes of each layer, all queries
+    denom = c.shape[0] * c.shape[2]
+    base = per // denom
+    rem = per - base * denom
+    short = nl * int(budget) - int(base.sum())
+    order = np.lexsort((np.arange(nl), -rem))
+    out = base.copy()
+    out[order[:short]] += 1
+    return out
 
 
 # ----------------------------------------------------------------------------

@@ -446,6 +446,57 @@ def test_rotation_matches_matmul_and_inverts(rng):
 # --------------------------------------------------------------------------
 
 # --------------------------------------------------------------------------
+# per-layer budget calibration (Fathom §3; the rule is a reading)
+# --------------------------------------------------------------------------
+
+def test_pooled_allocation_of_one_unit_is_the_unit_rule(rng):
+    q = rng.standard_normal((4, 128)).astype(np.float32)
+    var = np.exp(rng.uniform(-4.6, 2.8, 128)).astype(np.float32)
+    g = O.channel_gains(q, var)[None, :]
+    for p in (0, 1, 64, 88, 512, 700):
+        assert list(O.pooled_plane_counts(g, p)) == [int(O.alloc_depth(q, var, p).sum())]
+
+
+def test_pooled_allocation_brute_force_optimal(rng):
+    """Two units of two channels: with the pooled counts, the units' own
+    depth rule reaches the best summed error sum_u sum_j g_uj 4^-t_uj over
+    every split of the pooled budget (brute force over {0..4}^4)."""
+    import itertools
+
+    def err(g, t):
+        return sum(Fraction(float(g[i // 2, i % 2])) / 4 ** t[i] for i in range(4))
+
+    for trial in range(8):
+        g = np.exp(rng.uniform(-3, 3, (2, 2))).astype(np.float32)
+        if trial == 0:
+            g[:] = 1.0          # ties everywhere
+        allt = list(itertools.product(range(5), repeat=4))
+        for p in range(0, 9):
+            counts = O.pooled_plane_counts(g, p)
+            total = min(2 * p, 16)
+            assert counts.sum() == total
+            best = min(err(g, t) for t in allt if sum(t) == total)
+            with_counts = min(err(g, t) for t in allt
+                              if t[0] + t[1] == counts[0] and t[2] + t[3] == counts[1])
+            assert with_counts == best, (g, p, counts)
+
+
+def test_layer_budgets_sum_and_follow_the_gains():
+    """Largest-remainder rounding keeps the total L * P; a layer whose units
+    take more planes in the pooled allocations gets the larger budget.
+    Hand-worked: 3 layers x 2 units, P = 88, two queries whose pooled counts
+    each sum to 528; per-layer means 97.5, 52.5, 114 -> floors 97, 52, 114
+    (263), the one plane left goes to the larger remainder, the lower layer
+    on the tie between layers 0 and 1."""
+    counts = np.array([[[100, 90], [60, 50], [118, 110]],
+                       [[110, 90], [50, 50], [108, 120]]])
+    assert (counts.sum(axis=(1, 2)) == 528).all()
+    assert list(O.calibrate_layer_budgets(counts, 88)) == [98, 52, 114]
+    flat = np.full((1, 4, 8), 88)
+    assert list(O.calibrate_layer_budgets(flat, 88)) == [88, 88, 88, 88]
+
+
+# --------------------------------------------------------------------------
 # fixed-depth baselines (Fathom §2: SparQ, Double Sparsity, thumbnail scan)
 # --------------------------------------------------------------------------
 
