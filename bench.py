@@ -337,6 +337,60 @@ def main() -> int:
                                "units_redone": bpk.decode_fallback_units(cache, 0, L, k, ws)}
             log(f"{name}: {baselines[name]}")
 
+    # per-layer budget calibration (Fathom §3's optional add-on; the rule is a
+    # reading): four calibration queries (decode steps 1-4) water-filled over
+    # every unit of every layer, per-layer budgets keeping the total 36 * P;
+    # the step then runs one decode call per layer at its budget.  Reported:
+    # the budgets, the step time (per-layer calls, against the same per-layer
+    # loop at the uniform budget) and the predicted squared-error proxy
+    # sum_u sum_j g_uj 4^-t_uj of the held-out query (step 0) under both.
+    calibration = None
+    if not appends and not args.no_sweep and cfg.seqs == 1:
+        from synth import workload as W
+        cq = torch.stack([workloads.queries(cfg, step=s) for s in range(1, 5)])
+        counts = torch.stack([bpk.pooled_planes(cache, cq[i], 0, L, budget) for i in range(4)])
+        lb = bpk.layer_budgets(cache, counts, 0, L, budget).cpu().numpy()
+        q_l = [q[:, l:l + 1].contiguous() for l in range(L)]
+        out_l = [out[:, l:l + 1].contiguous() for l in range(L)]
+
+        def layer_loop(budgets):
+            for l in range(L):
+                bpk.decode_step(cache, q_l[l], l, l + 1, int(budgets[l]), k, scale, out=out_l[l],
+                                ws=ws)
+        uni = np.full(L, budget)
+        lb_t = torch.from_numpy(lb.astype(np.int32)).cuda()
+        dl = torch.empty((cfg.seqs, L, cfg.heads, 128), dtype=torch.uint8, device="cuda")
+        ql = torch.empty((cfg.seqs, L, cfg.heads, cfg.group, 128), dtype=torch.float32,
+                         device="cuda")
+
+        def one_call():  # every layer at its budget in one call
+            bpk.alloc_depth_layers(cache, q, 0, L, lb_t, depth=dl, q_basis=ql)
+            bpk.decode_step_depth(cache, q, ql, dl, 0, L, k, scale, out=out, ws=ws)
+        for _ in range(2):
+            layer_loop(lb)
+            layer_loop(uni)
+            one_call()
+        ms_cal = time_launches(lambda: layer_loop(lb), args.steps)
+        ms_uni = time_launches(lambda: layer_loop(uni), args.steps)
+        ms_one = time_launches(one_call, args.steps)
+
+        def proxy(budgets):
+            tot = 0.0
+            for l in range(L):
+                d, _ = bpk.alloc_depth(cache, q_l[l], l, l + 1, int(budgets[l]))
+                d = d.cpu().numpy().reshape(cfg.heads, 128).astype(np.float64)
+                for h in range(cfg.heads):
+                    qh = W.query(cfg, 0, l, h, 0)[1].astype(np.float64)
+                    g = cfg.chan_var(0, l, h).astype(np.float64) * (qh * qh).sum(axis=0)
+                    tot += float((g * 0.25 ** d[h]).sum())
+            return tot
+        calibration = {"layer_budgets": [int(x) for x in lb],
+                       "decode_step_us": round(ms_one * 1e3, 1),
+                       "per_layer_calls_step_us": round(ms_cal * 1e3, 1),
+                       "uniform_per_layer_calls_step_us": round(ms_uni * 1e3, 1),
+                       "error_proxy_ratio": round(proxy(lb) / proxy(uni), 4)}
+        log(f"calibrated budgets {min(lb)}..{max(lb)}: {calibration}")
+
     # the standalone full scan (scan_scores writes every score: same reads,
     # plus 16 bytes of scores per token)
     del ws
@@ -436,6 +490,7 @@ def main() -> int:
         "scan_bits_per_token_mean": round(bits_of(d), 2),
         "budget_sweep": sweep,
         "baselines": baselines,
+        "layer_calibration": calibration,
     }
     if not args.no_cpu_baseline:
         log("timing the oracle on a CPU sample")

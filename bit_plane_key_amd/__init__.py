@@ -8,6 +8,7 @@ from ._lib import (  # noqa: F401
     BLOCK,
     BPK_OP_ATTEND,
     BPK_OP_DECODE,
+    BPK_OP_POOLED,
     BPK_OP_SELECT,
     BPK_DEPTH_CHANNELS,
     BPK_DEPTH_SPARQ,
@@ -21,9 +22,12 @@ from ._lib import (  # noqa: F401
     BpkError,
     Cache,
     alloc_depth,
+    alloc_depth_layers,
     decode_step,
     decode_step_depth,
     fixed_depth,
+    layer_budgets,
+    pooled_planes,
     decode_fallback_units,
     decode_step_noalloc,
     NOALLOC_SCRATCH_BYTES,

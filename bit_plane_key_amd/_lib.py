@@ -20,11 +20,12 @@ LIB_PATH = os.path.join(_HERE, "libbpk.so")
 
 BPK_OK, BPK_EINVAL, BPK_EUNSUPPORTED, BPK_EWORKSPACE, BPK_ECAPACITY, BPK_EHIP = 0, -1, -2, -3, -4, -5
 BPK_F32, BPK_BF16 = 0, 1
-BPK_OP_SELECT, BPK_OP_ATTEND, BPK_OP_DECODE = 3, 4, 5
+BPK_OP_SELECT, BPK_OP_ATTEND, BPK_OP_DECODE, BPK_OP_POOLED = 3, 4, 5, 6
 BPK_DEPTH_WATERFILL, BPK_DEPTH_SPARQ, BPK_DEPTH_CHANNELS, BPK_DEPTH_UNIFORM = 0, 1, 2, 3
 HEAD_DIM, BLOCK, PLANES = 128, 64, 4
 
-EXPORTS = ("bpk_encode_append", "bpk_alloc_depth", "bpk_fixed_depth", "bpk_scan_scores", "bpk_select_topk",
+EXPORTS = ("bpk_encode_append", "bpk_alloc_depth", "bpk_fixed_depth", "bpk_pooled_planes",
+           "bpk_layer_budgets", "bpk_alloc_depth_layers", "bpk_scan_scores", "bpk_select_topk",
            "bpk_sparse_attend", "bpk_decode_step", "bpk_decode_step_depth", "bpk_decode_step_noalloc", "bpk_decode_fallback_units", "bpk_workspace_bytes", "bpk_last_error",
            "bpk_trace_enable", "bpk_trace_read")
 STAGES = ("alloc", "sample", "threshold", "scan", "select", "fallback", "attend")
@@ -71,6 +72,9 @@ def _load() -> ctypes.CDLL:
         "bpk_encode_append": (ctypes.c_int, [C, I32, P, P, I64, P]),
         "bpk_alloc_depth": (ctypes.c_int, [C, P, I32, I32, I32, P, P, P]),
         "bpk_fixed_depth": (ctypes.c_int, [C, P, I32, I32, I32, I32, P, P, P, P]),
+        "bpk_pooled_planes": (ctypes.c_int, [C, P, I32, I32, I32, P, P, SZ, P]),
+        "bpk_layer_budgets": (ctypes.c_int, [C, P, I32, I32, I32, I32, P, P]),
+        "bpk_alloc_depth_layers": (ctypes.c_int, [C, P, I32, I32, P, P, P, P]),
         "bpk_scan_scores": (ctypes.c_int, [C, P, P, I32, I32, P, P]),
         "bpk_select_topk": (ctypes.c_int, [C, P, I32, I32, I32, P, P, SZ, P]),
         "bpk_sparse_attend": (ctypes.c_int, [C, P, P, I32, I32, I32, F, P, P, SZ, P]),
@@ -254,6 +258,53 @@ def fixed_depth(cache: Cache, q: torch.Tensor, l0: int, l1: int, rule: int, para
     _check(LIB.bpk_fixed_depth(cache.struct(), q.data_ptr(), l0, l1, int(rule), int(param),
                                _ptr(channels), depth.data_ptr(), q_basis.data_ptr(),
                                _stream(stream)))
+    return depth, q_basis
+
+
+def pooled_planes(cache: Cache, q: torch.Tensor, l0: int, l1: int, budget: int, counts=None,
+                  ws=None, stream=None):
+    """Planes each unit of layers [l0, l1) gets when the call's whole budget
+    is water-filled over all its units (int32 [S][nl][H])."""
+    u = (cache.S, l1 - l0, cache.H)
+    _need(q, "q", torch.bfloat16, (*u, cache.G, HEAD_DIM))
+    if counts is None:
+        counts = torch.empty(u, dtype=torch.int32, device=q.device)
+    _need(counts, "counts", torch.int32, u)
+    if ws is None:
+        ws = torch.empty(workspace_bytes(cache, BPK_OP_POOLED, l0, l1, 1), dtype=torch.uint8,
+                         device=q.device)
+    _check(LIB.bpk_pooled_planes(cache.struct(), q.data_ptr(), l0, l1, int(budget),
+                                 counts.data_ptr(), ws.data_ptr(), ws.numel(), _stream(stream)))
+    return counts
+
+
+def layer_budgets(cache: Cache, counts: torch.Tensor, l0: int, l1: int, budget: int, out=None,
+                  stream=None):
+    """Per-layer budgets [nl] from pooled counts [queries][S][nl][H]."""
+    nq = counts.shape[0]
+    _need(counts, "counts", torch.int32, (nq, cache.S, l1 - l0, cache.H))
+    if out is None:
+        out = torch.empty(l1 - l0, dtype=torch.int32, device=counts.device)
+    _need(out, "out", torch.int32, (l1 - l0,))
+    _check(LIB.bpk_layer_budgets(cache.struct(), counts.data_ptr(), nq, l0, l1, int(budget),
+                                 out.data_ptr(), _stream(stream)))
+    return out
+
+
+def alloc_depth_layers(cache: Cache, q: torch.Tensor, l0: int, l1: int, budgets: torch.Tensor,
+                       depth=None, q_basis=None, stream=None):
+    """alloc_depth with a budget per layer (int32 [l1 - l0] on the GPU)."""
+    u = (cache.S, l1 - l0, cache.H)
+    _need(q, "q", torch.bfloat16, (*u, cache.G, HEAD_DIM))
+    _need(budgets, "budgets", torch.int32, (l1 - l0,))
+    if depth is None:
+        depth = torch.empty((*u, HEAD_DIM), dtype=torch.uint8, device=q.device)
+    if q_basis is None:
+        q_basis = torch.empty((*u, cache.G, HEAD_DIM), dtype=torch.float32, device=q.device)
+    _need(depth, "depth", torch.uint8, (*u, HEAD_DIM))
+    _need(q_basis, "q_basis", torch.float32, (*u, cache.G, HEAD_DIM))
+    _check(LIB.bpk_alloc_depth_layers(cache.struct(), q.data_ptr(), l0, l1, budgets.data_ptr(),
+                                      depth.data_ptr(), q_basis.data_ptr(), _stream(stream)))
     return depth, q_basis
 
 

@@ -26,6 +26,8 @@ struct AllocArgs {
   float* q_basis;
   int rule;                 // BPK_DEPTH_*
   const uint8_t* channels;  // CHANNELS: [L][H][c] channel indices
+  float* gains;             // WATERFILL, if set: g_j of every unit [units][D]
+  const int32_t* layer_budget;  // WATERFILL, if set: the budget of each layer of the call [nl]
 };
 
 template <int G, bool ROT>
@@ -129,8 +131,13 @@ __global__ __launch_bounds__(64) void alloc_kernel(AllocArgs a) {
     for (int h = 0; h < G; ++h) acc = __fadd_rn(acc, __fmul_rn(qb[h][c], qb[h][c]));
     gain[c] = __fmul_rn(a.chan_var[gu * D + 2 * lane + c], acc);
   }
+  if (a.gains) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) a.gains[(long long)u * D + 2 * lane + c] = gain[c];
+  }
 
-  const int take = a.budget < NP * D ? a.budget : NP * D;
+  const int budget = a.layer_budget ? a.layer_budget[(u / a.g.H) % a.g.nl] : a.budget;
+  const int take = budget < NP * D ? budget : NP * D;
   if (take <= 0 || take >= NP * D) {
     const uint8_t v = take <= 0 ? 0 : NP;
     dep[2 * lane] = v;
@@ -176,12 +183,120 @@ void launch_g(const AllocArgs& a, hipStream_t st) {
     alloc_kernel<G, false><<<a.g.units(), 64, 0, st>>>(a);
 }
 
+// Pooled water-filling over every unit of the call (per-layer budget
+// calibration): the budget of units * P planes goes to the most valuable
+// (unit, channel, plane) candidates g_uj 4^-t, equal values to the lower
+// unit, channel, plane.  One workgroup: the threshold key is found bit by
+// bit from the top (57-bit keys: value bits, then the candidate index
+// complemented), each probe counting every candidate; then each unit's
+// count of candidates at or above it.
+constexpr int POOL_THREADS = 1024;
+__global__ __launch_bounds__(POOL_THREADS) void pooled_kernel(const float* __restrict__ gains,
+                                                              int units, long long take,
+                                                              int32_t* __restrict__ counts) {
+  __shared__ unsigned long long part[POOL_THREADS / 64];
+  const int tid = threadIdx.x;
+  const long long ncand = (long long)units * D * NP;
+  const float qp[NP] = {1.0f, 0.25f, 0.0625f, 0.015625f};
+  auto key = [&](long long c) {  // candidate c = (u * D + j) * NP + t
+    const float v = __fmul_rn(gains[c / NP], qp[c % NP]);
+    return ((unsigned long long)__float_as_uint(v) << 25) |
+           ((unsigned long long)(0x1FFFFFFll - c) & 0x1FFFFFFull);
+  };
+  unsigned long long prefix = 0;
+  if (take >= ncand) {
+    prefix = 0;  // everything is taken
+  } else if (take > 0) {
+    for (int b = 56; b >= 0; --b) {
+      const unsigned long long cand = prefix | (1ull << b);
+      unsigned long long cnt = 0;
+      for (long long c = tid; c < ncand; c += POOL_THREADS) cnt += key(c) >= cand;
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1)
+        cnt += (unsigned long long)__shfl_xor((long long)cnt, off);
+      if ((tid & 63) == 0) part[tid >> 6] = cnt;
+      __syncthreads();
+      unsigned long long tot = 0;
+#pragma unroll
+      for (int w = 0; w < POOL_THREADS / 64; ++w) tot += part[w];
+      __syncthreads();
+      if (tot >= (unsigned long long)take) prefix = cand;
+    }
+  }
+  for (int u = tid; u < units; u += POOL_THREADS) {
+    int c = 0;
+    if (take >= ncand) {
+      c = D * NP;
+    } else if (take > 0) {
+      for (int e = 0; e < D * NP; ++e) c += key((long long)u * D * NP + e) >= prefix;
+    }
+    counts[u] = c;
+  }
+}
+
+// Per-layer budgets from pooled counts [queries][units]: a layer's budget is
+// the mean count of its units, rounded by largest remainder (ties to the
+// lower layer) so that the budgets sum to nl * P.  One wavefront.
+__global__ __launch_bounds__(64) void layer_budget_kernel(Geom g, const int32_t* __restrict__ counts,
+                                                          int queries, int budget,
+                                                          int32_t* __restrict__ out) {
+  __shared__ long long per[256];
+  __shared__ long long rem[256];
+  __shared__ int base[256];
+  const int lane = threadIdx.x;
+  const int units = g.units();
+  const long long denom = (long long)queries * g.S * g.H;
+  for (int l = lane; l < g.nl; l += 64) {
+    long long sum = 0;
+    for (int qi = 0; qi < queries; ++qi)
+      for (int s = 0; s < g.S; ++s)
+        for (int h = 0; h < g.H; ++h) sum += counts[(long long)qi * units + (s * g.nl + l) * g.H + h];
+    per[l] = sum;
+    base[l] = (int)(sum / denom);
+    rem[l] = sum - (long long)base[l] * denom;
+  }
+  __syncthreads();
+  if (lane == 0) {
+    long long used = 0;
+    for (int l = 0; l < g.nl; ++l) used += base[l];
+    long long shortfall = (long long)g.nl * budget - used;
+    // hand out the shortfall one plane at a time: largest remainder first,
+    // the lower layer on ties (a layer gets at most one)
+    while (shortfall > 0) {
+      int best = -1;
+      for (int l = 0; l < g.nl; ++l)
+        if (rem[l] >= 0 && (best < 0 || rem[l] > rem[best])) best = l;
+      if (best < 0) break;
+      ++base[best];
+      rem[best] = -1;
+      --shortfall;
+    }
+  }
+  __syncthreads();
+  for (int l = lane; l < g.nl; l += 64) out[l] = base[l];
+}
+
 }  // namespace
+
+hipError_t launch_pooled(const Geom& g, const float* gains, int budget, int32_t* counts,
+                         hipStream_t st) {
+  const int units = g.units();
+  if (units == 0) return hipSuccess;
+  const long long take = (long long)(budget < NP * D ? budget : NP * D) * units;
+  pooled_kernel<<<1, POOL_THREADS, 0, st>>>(gains, units, take, counts);
+  return hipGetLastError();
+}
+
+hipError_t launch_layer_budgets(const Geom& g, const int32_t* counts, int queries, int budget,
+                                int32_t* out, hipStream_t st) {
+  layer_budget_kernel<<<1, 64, 0, st>>>(g, counts, queries, budget, out);
+  return hipGetLastError();
+}
 
 hipError_t launch_alloc(const Geom& g, const uint16_t* q, const float* chan_var, const float* rot,
                         int budget, uint8_t* depth, float* q_basis, hipStream_t st, int rule,
-                        const uint8_t* channels) {
-  AllocArgs a{g, q, chan_var, rot, budget, depth, q_basis, rule, channels};
+                        const uint8_t* channels, float* gains, const int32_t* layer_budget) {
+  AllocArgs a{g, q, chan_var, rot, budget, depth, q_basis, rule, channels, gains, layer_budget};
   switch (g.G) {
     case 1: launch_g<1>(a, st); break;
     case 2: launch_g<2>(a, st); break;

@@ -176,6 +176,13 @@ DecodeWs decode_ws(const bpk::Geom& g, int k) {
   return w;
 }
 
+// bpk_pooled_planes' workspace: q in the scan basis, depths (unused), gains
+size_t pooled_ws(const bpk::Geom& g) {
+  const size_t units = (size_t)g.units();
+  return align256(units * g.G * bpk::D * sizeof(float)) + align256(units * bpk::D) +
+         align256(units * bpk::D * sizeof(float));
+}
+
 }  // namespace
 
 extern "C" {
@@ -190,6 +197,7 @@ size_t bpk_workspace_bytes(const bpk_cache_t* c, int32_t op, int32_t l0, int32_t
     case BPK_OP_SELECT: return 0;
     case BPK_OP_ATTEND: return bpk::attend_ws_bytes(g, k);
     case BPK_OP_DECODE: return decode_ws(g, k).total;
+    case BPK_OP_POOLED: return pooled_ws(g);
     default: return 0;
   }
 }
@@ -257,6 +265,63 @@ int bpk_fixed_depth(const bpk_cache_t* c, const uint16_t* q, int32_t l0, int32_t
   return hip_status(bpk::launch_alloc(g, q, c->chan_var, c->rot, param, depth, q_basis,
                                       static_cast<hipStream_t>(stream), rule, channels),
                     "fixed_depth");
+}
+
+int bpk_pooled_planes(const bpk_cache_t* c, const uint16_t* q, int32_t l0, int32_t l1,
+                      int32_t budget_planes, int32_t* plane_counts, void* ws, size_t ws_bytes,
+                      void* stream) {
+  bpk::Geom g;
+  int rc = check_cache(c, l0, l1, &g);
+  if (rc) return rc;
+  if (!q || !plane_counts) return fail(BPK_EINVAL, "q and plane_counts must be non-NULL");
+  if (budget_planes < 0) return fail(BPK_EINVAL, "budget_planes < 0");
+  const size_t need = pooled_ws(g);
+  if (!ws || ws_bytes < need)
+    return fail(BPK_EWORKSPACE, "workspace of %zu bytes < %zu needed", ws_bytes, need);
+  char* base = static_cast<char*>(ws);
+  const size_t units = (size_t)g.units();
+  float* qb = reinterpret_cast<float*>(base);
+  uint8_t* depth = reinterpret_cast<uint8_t*>(base + align256(units * g.G * bpk::D * sizeof(float)));
+  float* gains = reinterpret_cast<float*>(base + align256(units * g.G * bpk::D * sizeof(float)) +
+                                          align256(units * bpk::D));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // the gains of every unit (an allocation with no budget writes them)
+  rc = hip_status(bpk::launch_alloc(g, q, c->chan_var, c->rot, 0, depth, qb, st,
+                                    BPK_DEPTH_WATERFILL, nullptr, gains),
+                  "pooled_planes/gains");
+  if (rc) return rc;
+  return hip_status(bpk::launch_pooled(g, gains, budget_planes, plane_counts, st),
+                    "pooled_planes");
+}
+
+int bpk_alloc_depth_layers(const bpk_cache_t* c, const uint16_t* q, int32_t l0, int32_t l1,
+                           const int32_t* layer_budgets, uint8_t* depth, float* q_basis,
+                           void* stream) {
+  bpk::Geom g;
+  int rc = check_cache(c, l0, l1, &g);
+  if (rc) return rc;
+  if (!q || !layer_budgets || !depth || !q_basis)
+    return fail(BPK_EINVAL, "q, layer_budgets, depth and q_basis must be non-NULL");
+  return hip_status(bpk::launch_alloc(g, q, c->chan_var, c->rot, 0, depth, q_basis,
+                                      static_cast<hipStream_t>(stream), BPK_DEPTH_WATERFILL,
+                                      nullptr, nullptr, layer_budgets),
+                    "alloc_depth_layers");
+}
+
+int bpk_layer_budgets(const bpk_cache_t* c, const int32_t* plane_counts, int32_t n_queries,
+                      int32_t l0, int32_t l1, int32_t budget_planes, int32_t* layer_budgets,
+                      void* stream) {
+  bpk::Geom g;
+  int rc = check_cache(c, l0, l1, &g);
+  if (rc) return rc;
+  if (!plane_counts || !layer_budgets)
+    return fail(BPK_EINVAL, "plane_counts and layer_budgets must be non-NULL");
+  if (n_queries < 1) return fail(BPK_EINVAL, "n_queries < 1");
+  if (budget_planes < 0) return fail(BPK_EINVAL, "budget_planes < 0");
+  if (g.nl > 256) return fail(BPK_EINVAL, "more than 256 layers in one call");
+  return hip_status(bpk::launch_layer_budgets(g, plane_counts, n_queries, budget_planes,
+                                              layer_budgets, static_cast<hipStream_t>(stream)),
+                    "layer_budgets");
 }
 
 int bpk_scan_scores(const bpk_cache_t* c, const float* q_basis, const uint8_t* depth, int32_t l0,

@@ -47,7 +47,14 @@ hipError_t launch_append_rows(const Geom& g, int seq, int k_dtype, const void* k
 // baseline depth rule (budget = its parameter, channels its channel lists)
 hipError_t launch_alloc(const Geom& g, const uint16_t* q, const float* chan_var, const float* rot,
                         int budget, uint8_t* depth, float* q_basis, hipStream_t st,
-                        int rule = BPK_DEPTH_WATERFILL, const uint8_t* channels = nullptr);
+                        int rule = BPK_DEPTH_WATERFILL, const uint8_t* channels = nullptr,
+                        float* gains = nullptr, const int32_t* layer_budget = nullptr);
+// per-layer budget calibration: pooled plane counts of every unit, and the
+// per-layer budgets of counts from several queries
+hipError_t launch_pooled(const Geom& g, const float* gains, int budget, int32_t* counts,
+                         hipStream_t st);
+hipError_t launch_layer_budgets(const Geom& g, const int32_t* counts, int queries, int budget,
+                                int32_t* out, hipStream_t st);
 
 // Every scan launcher takes `rows`, the number of plane rows every unit of
 // the call reads (min(P, 4D) after alloc_depth), or -1 when it is not known:

@@ -60,7 +60,7 @@ enum bpk_status {
 
 enum bpk_dtype { BPK_F32 = 0, BPK_BF16 = 1 };
 
-enum bpk_op { BPK_OP_SELECT = 3, BPK_OP_ATTEND = 4, BPK_OP_DECODE = 5 };
+enum bpk_op { BPK_OP_SELECT = 3, BPK_OP_ATTEND = 4, BPK_OP_DECODE = 5, BPK_OP_POOLED = 6 };
 
 /*
  * The cache: storage shared by every entry point.  All arrays are
@@ -164,6 +164,41 @@ enum bpk_depth_rule {
 int bpk_fixed_depth(const bpk_cache_t* cache, const uint16_t* q, int32_t l0, int32_t l1,
                     int32_t rule, int32_t param, const uint8_t* channels, uint8_t* depth,
                     float* q_basis, void* stream);
+
+/*
+ * Per-layer budget calibration (Fathom §3 names it as optional; the rule is
+ * not on the page, so this is a reading): a calibration query is water-filled
+ * over every unit of layers [l0, l1) at once, the budget of units *
+ * budget_planes planes going to the most valuable (unit, channel, plane)
+ * candidates g_uj 4^-t (g as in bpk_alloc_depth; equal values to the lower
+ * unit, channel, plane).  bpk_pooled_planes writes the planes each unit gets,
+ * plane_counts [S][nl][H] int32 (DEVICE).  ws: bpk_workspace_bytes(..,
+ * BPK_OP_POOLED, ..) bytes (k ignored).  One workgroup: a calibration call,
+ * not a decode-path call.
+ * bpk_layer_budgets turns the counts of n_queries calibration queries,
+ * [n_queries][S][nl][H] int32 (DEVICE), into per-layer budgets [nl] int32
+ * (DEVICE): a layer's budget is the mean count of its units, rounded by
+ * largest remainder (ties to the lower layer) so that the budgets sum to
+ * nl * budget_planes.  Decoding then calls bpk_decode_step per layer with
+ * its budget.  Errors: BPK_EINVAL (NULL pointers, budget_planes < 0,
+ * n_queries < 1, more than 256 layers), BPK_EWORKSPACE.
+ */
+int bpk_pooled_planes(const bpk_cache_t* cache, const uint16_t* q, int32_t l0, int32_t l1,
+                      int32_t budget_planes, int32_t* plane_counts, void* ws, size_t ws_bytes,
+                      void* stream);
+int bpk_layer_budgets(const bpk_cache_t* cache, const int32_t* plane_counts, int32_t n_queries,
+                      int32_t l0, int32_t l1, int32_t budget_planes, int32_t* layer_budgets,
+                      void* stream);
+/*
+ * bpk_alloc_depth with a budget per layer: layer_budgets [nl] int32 (DEVICE,
+ * for instance from bpk_layer_budgets; values below 0 count as 0); the units
+ * of layer l0 + i get min(layer_budgets[i], 512) planes.  Decoding all layers
+ * at their budgets in one call: this, then bpk_decode_step_depth.
+ * Errors: BPK_EINVAL (NULL pointer, bad layer range).
+ */
+int bpk_alloc_depth_layers(const bpk_cache_t* cache, const uint16_t* q, int32_t l0, int32_t l1,
+                           const int32_t* layer_budgets, uint8_t* depth, float* q_basis,
+                           void* stream);
 
 /*
  * Key scan (Fathom §1, §3.2): approximate scores of every token of every
@@ -275,7 +310,7 @@ int bpk_decode_fallback_units(const bpk_cache_t* cache, int32_t l0, int32_t l1, 
 
 /*
  * Workspace bytes an entry point needs for layers [l0, l1) and top-k k
- * (op = BPK_OP_SELECT, BPK_OP_ATTEND or BPK_OP_DECODE).  Returns 0 for an
+ * (op = BPK_OP_SELECT, BPK_OP_ATTEND, BPK_OP_DECODE or BPK_OP_POOLED).  Returns 0 for an
  * invalid cache or op.
  */
 size_t bpk_workspace_bytes(const bpk_cache_t* cache, int32_t op, int32_t l0, int32_t l1,
