@@ -251,7 +251,7 @@ def calibrate_layer_budgets(plane_counts: np.ndarray, budget: int) -> np.ndarray
     denom = c.shape[0] * c.shape[2]
     base = per // denom
     rem = per - base * denom
-    short = nl * int(budget) - int(base.sum())
+    short = max(nl * int(budget) - int(base.sum()), 0)
     order = np.lexsort((np.arange(nl), -rem))
     out = base.copy()
     out[order[:short]] += 1
