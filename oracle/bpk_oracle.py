@@ -15,7 +15,8 @@ Sources (cited by section; no sentence of them is reproduced):
   prefix-decode formula follow the plainest reading listed in the design doc.
 * [ReadKV] the page "AI存储论文解读:ReadKV：KV 存得更细、每步少读..." --
   §5.2 (key-channel importance summed over the query heads that share a KV
-  head), §5.4 (greedy allocation by largest predicted error drop),
+  head), §5.3 (value depth per token from the heads' squared attention
+  probabilities), §5.4 (greedy allocation by largest predicted error drop),
   §6.1 (append-only planes).
 
 Every floating-point decision that produces an integer (a code, a depth) is
@@ -45,7 +46,8 @@ __all__ = [
     "alloc_depth_greedy", "pooled_plane_counts", "calibrate_layer_budgets", "sparq_depth", "double_sparsity_channels", "channel_set_depth",
     "uniform_depth", "scan_scores", "kept_tail", "select_topk",
     "attend", "dense_attention", "rotate_basis", "decode_unit",
-    "scan_bits_per_token", "scan_bytes_unit",
+    "scan_bits_per_token", "scan_bytes_unit", "encode_values", "value_prefix_rows",
+    "value_gains", "alloc_value_depth", "attend_values", "value_bytes",
 ]
 
 
@@ -483,3 +485,139 @@ def scan_bytes_unit(depth: np.ndarray, n: int) -> float:
     t = np.asarray(depth, dtype=np.int64)
     nb = n // BLOCK
     return float(t.sum()) * nb * 8.0 + float((t > 0).sum()) * nb * 2.0
+
+
+# ----------------------------------------------------------------------------
+# value-side depths (ReadKV stage 2)
+# ----------------------------------------------------------------------------
+
+def encode_values(v_rows: np.ndarray):
+    """Per-token value planes and scales.
+
+    [ReadKV §5.3] value precision is chosen per token, every channel of a
+    token sharing one depth; [ReadKV §6.1] new tokens are appended as
+    progressive planes.  Reading on this storage: each value row is coded
+    like a key block turned on its side -- one fp16 scale per token,
+    s_i = fp16_rne(max_j |v_ij| / 8) (saturating), and the same symmetric
+    4-bit code c_ij = clip(floor(v_ij / s_i), -8, 7) + 8 with the exact floor.
+    Plane p of a token holds bit 3 - p of its 128 codes: channel j is bit
+    j % 8 of byte j // 8.  Every token is coded as soon as it arrives (no
+    block to wait for).  Returns ``planes`` uint8 [n][4][D / 8] and
+    ``scales`` float16 [n].
+    """
+    v = np.asarray(v_rows, dtype=np.float32)
+    s = block_scales(v.T)                      # the row maxima
+    c = quantize_codes(v.T, s).T               # [n][D]
+    planes = np.zeros((v.shape[0], PLANES, v.shape[1] // 8), dtype=np.uint8)
+    for p in range(PLANES):
+        bit = ((c >> (PLANES - 1 - p)) & 1).astype(np.uint8)
+        planes[:, p, :] = np.packbits(bit, axis=1, bitorder="little")
+    return planes, s
+
+
+def value_prefix_rows(vplanes: np.ndarray, vscales: np.ndarray, rows, depth) -> np.ndarray:
+    """Value rows rebuilt from the first t_i planes of each token, fp64.
+
+    The t-plane prefix of a code is its t-bit quantizer cell, rebuilt at the
+    cell midpoint (as for keys, Fathom §1 observation 2) times the token's
+    scale; depth 0 reads nothing and rebuilds 0, the mean of the symmetric
+    code.  Returns [len(rows)][D].
+    """
+    nd = vplanes.shape[2] * 8
+    out = np.zeros((len(rows), nd), dtype=np.float64)
+    for r, (i, t) in enumerate(zip(rows, depth)):
+        t = int(t)
+        if t == 0:
+            continue
+        pre = np.zeros(nd, dtype=np.int64)
+        for p in range(t):
+            pre = pre * 2 + np.unpackbits(vplanes[i, p], bitorder="little").astype(np.int64)
+        out[r] = float(vscales[i]) * prefix_values(pre, t)
+    return out
+
+
+def value_gains(weights: np.ndarray, vscales: np.ndarray) -> np.ndarray:
+    """w_i = a_i * s_i^2 in fp32 (s_i^2 is exact, one rounding for the product).
+
+    [ReadKV §5.3, §5.4] a_i is token i's importance, the sum over the query
+    heads sharing the KV head of its squared attention probabilities (every
+    head weighted 1).  The predicted error of rebuilding the token from t
+    planes is proportional to s_i^2 4^-t (the uniform cell of width
+    16 s_i 2^-t has mean squared error (16 s_i 2^-t)^2 / 12 per channel, and
+    the depth-0 rebuild of a value spread over the whole range errs by the
+    same formula at t = 0).  Reading: the token's own scale is the
+    standardised unit of this storage, so it enters the gain squared.
+    """
+    s = np.asarray(vscales, dtype=np.float16).astype(np.float32)
+    return (np.asarray(weights, dtype=np.float32) * (s * s)).astype(np.float32)
+
+
+def _fill_rows(w: np.ndarray, budget: int) -> np.ndarray:
+    """Token depths from gains w (fp32 or fp64, values in that precision)."""
+    n = w.shape[0]
+    i = np.repeat(np.arange(n), PLANES)
+    t = np.tile(np.arange(PLANES), n)
+    v = (w[i] * w.dtype.type(0.25) ** t.astype(w.dtype)).astype(w.dtype)
+    order = np.lexsort((t, i, -v.astype(np.float64)))
+    order = order[v[order] > 0]                # no plane without a positive gain
+    take = order[: max(int(budget), 0)]
+    depth = np.zeros(n, dtype=np.int64)
+    np.add.at(depth, i[take], 1)
+    return depth.astype(np.uint8)
+
+
+def alloc_value_depth(weights: np.ndarray, vscales: np.ndarray, budget: int) -> np.ndarray:
+    """Per-token value depths from importances a_i (fp32) and scales s_i.
+
+    [ReadKV §5.4] the greedy allocator grants one plane at a time to the
+    object whose next plane lowers the predicted error the most, until the
+    budget is spent or no grant helps.  The next plane of token i at depth t
+    lowers a_i s_i^2 4^-t by 3/4 of itself, so the grants are the candidates
+    (i, t) of largest value w_i 4^-t (fp32), taken in value order while the
+    value is positive; equal values go to the lower token, then the lower
+    plane.  Rows are in token order.  Returns uint8 depths.
+    """
+    return _fill_rows(value_gains(weights, vscales), budget)
+
+
+def attend_values(q: np.ndarray, k_rows: np.ndarray, vplanes: np.ndarray,
+                  vscales: np.ndarray, idx: np.ndarray, scale: float, v_budget: int):
+    """Attention over each head's selected rows with value rows read at
+    per-token depths, fp64.
+
+    [Fathom §2] each head's softmax is over its own selected set, from exact
+    keys; [ReadKV §5.3] the probabilities then fix the value depths: the rows
+    of the union of the heads' sets (token order) get importances
+    a_i = sum_h p_hi^2 (p_hi = 0 for a head that did not select i), the
+    budget of v_budget planes is allocated as in alloc_value_depth (values
+    w_i 4^-t in fp64 here), and o_h = sum_i p_hi v_hat_i with v_hat_i the
+    t_i-plane rebuild.  ``idx`` entries < 0 are padding.
+    Returns a dict with out [G][D], union rows, depth, p [G][union], a.
+    """
+    q64 = np.asarray(q, dtype=np.float64)
+    g = q64.shape[0]
+    sel = [idx[h][idx[h] >= 0] for h in range(g)]
+    union = np.unique(np.concatenate(sel)) if g else np.zeros(0, dtype=np.int64)
+    union = union.astype(np.int64)
+    pos = {int(tok): r for r, tok in enumerate(union)}
+    p = np.zeros((g, len(union)), dtype=np.float64)
+    for h in range(g):
+        if len(sel[h]) == 0:
+            continue
+        logits = (k_rows[sel[h]].astype(np.float64) @ q64[h]) * scale
+        e = np.exp(logits - logits.max())
+        for tok, val in zip(sel[h], e / e.sum()):
+            p[h, pos[int(tok)]] = val
+    a = (p * p).sum(axis=0)
+    s = np.asarray(vscales, dtype=np.float16)[union].astype(np.float64)
+    depth = _fill_rows(a * s * s, v_budget)
+    vhat = value_prefix_rows(vplanes, vscales, union, depth)
+    out = p @ vhat if len(union) else np.zeros((g, vplanes.shape[2] * 8))
+    return dict(out=out, union=union, depth=depth, p=p, a=a)
+
+
+def value_bytes(depth: np.ndarray) -> float:
+    """Algorithmic bytes of reading value rows at depths t_i: 16 bytes per
+    plane (128 channels) plus the 2-byte scale of every row read at all."""
+    t = np.asarray(depth, dtype=np.int64)
+    return float(t.sum()) * 16.0 + float((t > 0).sum()) * 2.0

@@ -582,3 +582,228 @@ def test_bit_accounting_matches_page():
     dense = 2 * n32 * m["head_dim"] * 2 * pairs
     assert round(dense / 1e9, 1) == g["dense_kv_bytes_per_step_32k"]["gigabytes"]
     assert m["q_per_kv"] * g["union_rows_per_kv_head_max"]["k"] == g["union_rows_per_kv_head_max"]["rows"]
+
+
+# --------------------------------------------------------------------------
+# value-side depths (ReadKV §5.3, §5.4)
+# --------------------------------------------------------------------------
+
+def _value_rows(rng, n, row_scale=None):
+    sc = np.ones(n) if row_scale is None else row_scale
+    return (rng.standard_normal((n, 128)) * sc[:, None]).astype(np.float32)
+
+
+def test_value_planes_hand_worked():
+    """One row: channel 0 = 4, channel 9 = -4, the rest 0.  The row maximum 4
+    gives s = 0.5; codes are floor(v / s) + 8 clipped: channel 0 -> 8 + 8 = 16
+    -> 15 (0b1111), channel 9 -> -8 + 8 = 0 (0b0000), zeros -> 8 (0b1000).
+    Plane 0 (the top bit) is 1 everywhere but channel 9 (byte 1, bit 1):
+    bytes FF FD FF ...; planes 1-3 are 1 only on channel 0: byte 0 = 01."""
+    v = np.zeros((1, 128), dtype=np.float32)
+    v[0, 0], v[0, 9] = 4.0, -4.0
+    planes, scales = O.encode_values(v)
+    assert float(scales[0]) == 0.5
+    assert list(planes[0, 0, :3]) == [0xFF, 0xFD, 0xFF] and np.all(planes[0, 0, 2:] == 0xFF)
+    for p in (1, 2, 3):
+        assert planes[0, p, 0] == 0x01 and np.all(planes[0, p, 1:] == 0)
+
+
+def test_value_plane_bit_layout(rng):
+    """Channel j of plane p is bit j % 8 of byte j // 8 and carries bit 3 - p
+    of the code, read back here with explicit shifts (no bit packing)."""
+    v = _value_rows(rng, 5, np.exp(rng.uniform(-3, 3, 5)))
+    planes, scales = O.encode_values(v)
+    for i in range(5):
+        s = Fraction(float(scales[i]))
+        assert s == Fraction(float(np.float16(np.max(np.abs(v[i])) / np.float32(8))))
+        for j in range(128):
+            code = min(max(math.floor(Fraction(float(v[i, j])) / s), -8), 7) + 8
+            for p in range(4):
+                bit = (int(planes[i, p, j // 8]) >> (j % 8)) & 1
+                assert bit == (code >> (3 - p)) & 1
+
+
+@pytest.mark.parametrize("t", [0, 1, 2, 3, 4])
+def test_value_prefix_is_the_t_bit_quantizer(rng, t):
+    """Rebuilding a token from t planes equals quantising its values directly
+    with t bits and cell s_i 2^(4-t) (exact rationals)."""
+    v = _value_rows(rng, 6, np.exp(rng.uniform(-2, 2, 6)))
+    planes, scales = O.encode_values(v)
+    rec = O.value_prefix_rows(planes, scales, np.arange(6), [t] * 6)
+    for i in range(6):
+        s = Fraction(float(scales[i]))
+        for j in range(0, 128, 7):
+            if t == 0:
+                expect = Fraction(0)
+            else:
+                w = s * 2 ** (4 - t)
+                half = 2 ** (t - 1)
+                cell = min(max(math.floor(Fraction(float(v[i, j])) / w), -half), half - 1)
+                expect = (cell + Fraction(1, 2)) * w
+            assert Fraction(rec[i, j]) == expect
+
+
+def _value_objective(w, t):
+    return sum(Fraction(float(wi)) / 4 ** int(ti) for wi, ti in zip(w, t))
+
+
+def test_value_alloc_brute_force_optimal(rng):
+    """ReadKV §5.4: for non-negative diminishing gains the greedy grants are
+    optimal for the proxy.  Every depth vector of up to four tokens is tried;
+    the allocation must reach the least sum_i w_i 4^-t_i and spend
+    min(budget, planes with a positive gain)."""
+    import itertools
+    for trial in range(40):
+        n = int(rng.integers(1, 5))
+        a = (rng.uniform(0, 1, n) ** 3).astype(np.float32)
+        if trial % 4 == 0:
+            a[rng.integers(0, n)] = 0.0
+        s = np.float16(np.exp(rng.uniform(-3, 2, n)))
+        w = O.value_gains(a, s)
+        for budget in range(0, 4 * n + 2):
+            t = O.alloc_value_depth(a, s, budget)
+            useful = 4 * int(np.count_nonzero(w > 0))
+            assert int(t.sum()) == min(budget, useful)
+            best = min(_value_objective(w, c) for c in itertools.product(range(5), repeat=n)
+                       if sum(c) <= budget)
+            assert _value_objective(w, t) == best
+
+
+def test_value_alloc_literal_greedy_loop(rng):
+    """The sort form equals the literal loop: grant the next plane to the token
+    whose next plane is worth the most (lower token on ties), stop when the
+    budget is spent or nothing is worth more than zero."""
+    for trial in range(6):
+        n = 40
+        a = (rng.uniform(0, 1, n) ** 4).astype(np.float32)
+        a[::7] = 0.0
+        a[3] = a[5]                         # an exact tie between two tokens
+        s = np.float16(np.exp(rng.uniform(-2, 2, n)))
+        s[5] = s[3]
+        s[11] = 0
+        w = O.value_gains(a, s)
+        for budget in (0, 1, 17, 60, 200):
+            depth = np.zeros(n, dtype=np.int64)
+            for _ in range(budget):
+                best, best_v = -1, 0.0
+                for i in range(n):
+                    if depth[i] < 4:
+                        val = float(np.float32(w[i] * np.float32(0.25) ** np.float32(depth[i])))
+                        if val > best_v:
+                            best, best_v = i, val
+                if best < 0:
+                    break
+                depth[best] += 1
+            np.testing.assert_array_equal(O.alloc_value_depth(a, s, budget), depth)
+
+
+def test_value_alloc_equal_gains_round_robin():
+    """Equal gains: plane 0 of every token outranks every plane 1, so the
+    budget goes round the tokens in order: t_i = B // n + (i < B % n)."""
+    n = 7
+    a = np.full(n, 0.125, dtype=np.float32)
+    s = np.full(n, 2.0, dtype=np.float16)
+    for budget in range(0, 4 * n + 3):
+        b = min(budget, 4 * n)
+        expect = [b // n + (i < b % n) for i in range(n)]
+        assert list(O.alloc_value_depth(a, s, budget)) == expect
+
+
+def test_value_gain_predicts_output_error(rng):
+    """ReadKV §5.3/§5.4: with independent per-token rebuild errors, the summed
+    squared output error over the heads is sum_i (sum_h p_hi^2) E|e_i|^2, and
+    a uniform cell of width 16 s 2^-t gives E|e_i|^2 = D (64/3) s_i^2 4^-t.
+    Measured with the encoder on value rows spread over their whole range,
+    for scales and depths that differ per token: the ratio of the measured
+    error to (64 D / 3) sum_i w_i 4^-t_i must be 1 (a gain that squares no
+    probability, drops s^2 or halves per bit fails)."""
+    g, n, trials = 4, 12, 300
+    logits = rng.standard_normal((g, n)) * 1.5
+    p = np.exp(logits) / np.exp(logits).sum(axis=1, keepdims=True)
+    a = (p * p).sum(axis=0).astype(np.float32)
+    row_scale = np.exp(rng.uniform(-2, 2, n))
+    for depth in ([0] * n, [4] * n, list(rng.integers(0, 5, n))):
+        err = 0.0
+        pred = 0.0
+        for _ in range(trials):
+            v = (rng.uniform(-1, 1, (n, 128)) * row_scale[:, None]).astype(np.float32)
+            planes, scales = O.encode_values(v)
+            rec = O.value_prefix_rows(planes, scales, np.arange(n), depth)
+            e = v.astype(np.float64) - rec
+            err += float(np.sum((p @ e) ** 2))
+            w = O.value_gains(a, scales).astype(np.float64)
+            pred += 128 * 64 / 3 * float(np.sum(w * 0.25 ** np.asarray(depth, dtype=np.float64)))
+        assert abs(err / pred - 1) < 0.06, (depth, err / pred)
+
+
+def _attend_values_case(rng, g=4, n=300, k=40):
+    q = rng.standard_normal((g, 128)).astype(np.float32)
+    keys = rng.standard_normal((n, 128)).astype(np.float32)
+    vals = _value_rows(rng, n, np.exp(rng.uniform(-1, 1, n)))
+    idx = np.stack([np.sort(rng.choice(n, k, replace=False)) for _ in range(g)])
+    return q, keys, vals, idx
+
+
+def test_attend_values_full_budget_is_4bit_values(rng):
+    """A budget that covers every plane rebuilds every union row at full
+    depth, the 4-bit cell midpoints s_i (c - 7.5), so the output is plain
+    attention over those rows (computed here by the dense routine)."""
+    q, keys, vals, idx = _attend_values_case(rng)
+    planes, scales = O.encode_values(vals)
+    r = O.attend_values(q, keys, planes, scales, idx, 0.09, 10 ** 6)
+    assert np.all(r["depth"] == 4)
+    s = scales.astype(np.float64)[:, None]
+    codes = np.clip(np.floor(vals.astype(np.float64) / s), -8, 7) + 8
+    v4 = s * (codes - 7.5)
+    for h in range(q.shape[0]):
+        expect = O.attend(q[h:h + 1], keys, v4, idx[h:h + 1], 0.09)
+        np.testing.assert_allclose(r["out"][h], expect[0], rtol=1e-12, atol=1e-12)
+    assert list(r["union"]) == sorted(set(idx.ravel().tolist()))
+
+
+def test_attend_values_zero_budget_is_zero(rng):
+    q, keys, vals, idx = _attend_values_case(rng)
+    planes, scales = O.encode_values(vals)
+    r = O.attend_values(q, keys, planes, scales, idx, 0.09, 0)
+    assert np.all(r["depth"] == 0) and np.all(r["out"] == 0)
+
+
+def test_attend_values_error_within_cell_bound(rng):
+    """|o_hd - o_exact_hd| <= sum_i p_hi s_i 2^(3 - t_i) (half a cell; the
+    depth-0 rebuild errs by at most |v| <= 8 s), whatever the budget."""
+    q, keys, vals, idx = _attend_values_case(rng)
+    planes, scales = O.encode_values(vals)
+    exact = O.attend(q, keys, vals, idx, 0.09)
+    for budget in (0, 30, 100, 250, 400):
+        r = O.attend_values(q, keys, planes, scales, idx, 0.09, budget)
+        s = scales[r["union"]].astype(np.float64)
+        bound = r["p"] @ (s * 2.0 ** (3 - r["depth"].astype(np.float64)))
+        assert np.all(np.abs(r["out"] - exact) <= bound[:, None] * (1 + 1e-3) + 1e-12)
+
+
+def test_attend_values_hand_worked_union_weights():
+    """Two heads: head 0 selects tokens {0, 1}, head 1 selects {1, 2}, every
+    logit equal, so each head puts 1/2 on each of its rows.  The union
+    0, 1, 2 has a = (1/4, 1/2, 1/4); all scales are 1 (row maximum 8).
+    Plane values: token 1: 1/2, 1/8, ...; tokens 0 and 2: 1/4, 1/16, ...
+    Budget 2 -> (1, 1, 0) (the tie goes to the lower token); budget 3 ->
+    (1, 1, 1); budget 4 -> (1, 2, 1); budget 5 -> (2, 2, 1)."""
+    q = np.zeros((2, 128), dtype=np.float32)
+    keys = np.ones((3, 128), dtype=np.float32)
+    vals = np.zeros((3, 128), dtype=np.float32)
+    vals[:, 0] = 8.0
+    idx = np.array([[0, 1], [1, 2]])
+    planes, scales = O.encode_values(vals)
+    assert np.all(scales == 1.0)
+    expect = {2: [1, 1, 0], 3: [1, 1, 1], 4: [1, 2, 1], 5: [2, 2, 1]}
+    for budget, dep in expect.items():
+        r = O.attend_values(q, keys, planes, scales, idx, 1.0, budget)
+        np.testing.assert_allclose(r["a"], [0.25, 0.5, 0.25])
+        assert list(r["depth"]) == dep, budget
+
+
+def test_value_bytes_full_depth():
+    """Four planes of 128 bits and a 2-byte scale: 66 bytes against the
+    256 bytes of a bf16 row; depth 0 reads nothing."""
+    assert O.value_bytes([4]) == 66.0 and O.value_bytes([0, 0]) == 0.0
+    assert O.value_bytes([1, 2, 0]) == 16 * 3 + 2 * 2
