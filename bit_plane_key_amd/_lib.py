@@ -21,12 +21,15 @@ LIB_PATH = os.path.join(_HERE, "libbpk.so")
 BPK_OK, BPK_EINVAL, BPK_EUNSUPPORTED, BPK_EWORKSPACE, BPK_ECAPACITY, BPK_EHIP = 0, -1, -2, -3, -4, -5
 BPK_F32, BPK_BF16 = 0, 1
 BPK_OP_SELECT, BPK_OP_ATTEND, BPK_OP_DECODE, BPK_OP_POOLED = 3, 4, 5, 6
+BPK_OP_ATTEND_V, BPK_OP_DECODE_V = 7, 8
 BPK_DEPTH_WATERFILL, BPK_DEPTH_SPARQ, BPK_DEPTH_CHANNELS, BPK_DEPTH_UNIFORM = 0, 1, 2, 3
 HEAD_DIM, BLOCK, PLANES = 128, 64, 4
 
 EXPORTS = ("bpk_encode_append", "bpk_alloc_depth", "bpk_fixed_depth", "bpk_pooled_planes",
            "bpk_layer_budgets", "bpk_alloc_depth_layers", "bpk_scan_scores", "bpk_select_topk",
-           "bpk_sparse_attend", "bpk_decode_step", "bpk_decode_step_depth", "bpk_decode_step_noalloc", "bpk_decode_fallback_units", "bpk_workspace_bytes", "bpk_last_error",
+           "bpk_sparse_attend", "bpk_decode_step", "bpk_decode_step_depth",
+           "bpk_decode_step_noalloc", "bpk_decode_fallback_units", "bpk_value_depth",
+           "bpk_sparse_attend_v", "bpk_decode_step_v", "bpk_workspace_bytes", "bpk_last_error",
            "bpk_trace_enable", "bpk_trace_read")
 STAGES = ("alloc", "sample", "threshold", "scan", "select", "fallback", "attend")
 
@@ -58,6 +61,8 @@ class BpkCacheStruct(ctypes.Structure):
         ("scales", ctypes.c_void_p),
         ("chan_var", ctypes.c_void_p),
         ("rot", ctypes.c_void_p),
+        ("v_planes", ctypes.c_void_p),
+        ("v_scales", ctypes.c_void_p),
     ]
 
 
@@ -82,6 +87,10 @@ def _load() -> ctypes.CDLL:
         "bpk_decode_step_depth": (ctypes.c_int, [C, P, P, P, I32, I32, I32, F, P, P, P, SZ, P]),
         "bpk_decode_step_noalloc": (ctypes.c_int, [C, P, I32, I32, I32, I32, F, P, P, P, P]),
         "bpk_decode_fallback_units": (ctypes.c_int, [C, I32, I32, I32, P, SZ, P, P]),
+        "bpk_value_depth": (ctypes.c_int, [C, I32, I32, P, P, I32, P, I32, P, P]),
+        "bpk_sparse_attend_v": (ctypes.c_int, [C, P, P, I32, I32, I32, F, I32, P, P, P, P, SZ, P]),
+        "bpk_decode_step_v": (ctypes.c_int, [C, P, I32, I32, I32, I32, F, I32, P, P, P, P, P, P,
+                                             SZ, P]),
         "bpk_workspace_bytes": (ctypes.c_size_t, [C, I32, I32, I32, I32]),
         "bpk_last_error": (ctypes.c_char_p, []),
         "bpk_trace_enable": (ctypes.c_int, [I32]),
@@ -156,13 +165,14 @@ class Cache:
     Arrays are torch tensors on the GPU; with ``host_resident`` the key and
     value rows, the planes and the scales are pinned host memory instead,
     which the GPU reads over the host link (the regime of the Fathom page's
-    measurements, §1 and §3.1).  ``n_tokens`` is a host int64 array the
-    caller advances after appends.
+    measurements, §1 and §3.1).  With ``values`` the cache also holds value
+    planes and per-token value scales (ReadKV §5.3), coded on append.
+    ``n_tokens`` is a host int64 array the caller advances after appends.
     """
 
     def __init__(self, num_seqs: int, num_layers: int, num_kv_heads: int, capacity: int,
                  group: int = 4, k_dtype: str = "bf16", rotated: bool = False,
-                 device: str = "cuda", host_resident: bool = False):
+                 device: str = "cuda", host_resident: bool = False, values: bool = False):
         if capacity % BLOCK:
             raise ValueError("capacity must be a multiple of 64")
         S, L, H, D = num_seqs, num_layers, num_kv_heads, HEAD_DIM
@@ -176,8 +186,14 @@ class Cache:
         nb = block_stride(capacity)
         self.planes = torch.zeros((S, L, H, D, PLANES, nb), dtype=torch.int64, **big)
         self.scales = torch.zeros((S, L, H, D, nb), dtype=torch.float16, **big)
-        self._ptrs = {name: _device_pointer(getattr(self, name))
-                      for name in ("k_rows", "v_rows", "planes", "scales")}
+        self.v_planes = self.v_scales = None
+        names = ["k_rows", "v_rows", "planes", "scales"]
+        if values:
+            self.v_planes = torch.zeros((S, L, H, capacity, PLANES, D // 8), dtype=torch.uint8,
+                                        **big)
+            self.v_scales = torch.zeros((S, L, H, capacity), dtype=torch.float16, **big)
+            names += ["v_planes", "v_scales"]
+        self._ptrs = {name: _device_pointer(getattr(self, name)) for name in names}
         self.chan_var = torch.ones((S, L, H, D), dtype=torch.float32, device=device)
         self.rot = (torch.empty((L, H, D, D), dtype=torch.float32, device=device)
                     if rotated else None)
@@ -195,6 +211,8 @@ class Cache:
         s.planes, s.scales = self._ptrs["planes"], self._ptrs["scales"]
         s.chan_var = self.chan_var.data_ptr()
         s.rot = None if self.rot is None else self.rot.data_ptr()
+        s.v_planes = self._ptrs.get("v_planes")
+        s.v_scales = self._ptrs.get("v_scales")
         return ctypes.pointer(s)
 
     def units(self, l0: int, l1: int) -> int:
@@ -423,6 +441,75 @@ def decode_step_noalloc(cache: Cache, q: torch.Tensor, l0: int, l1: int, budget:
     _check(LIB.bpk_decode_step_noalloc(cache.struct(), q.data_ptr(), l0, l1, int(budget), int(k),
                                        float(softmax_scale), out.data_ptr(), _ptr(depth_out),
                                        _ptr(idx_out), _stream(stream)))
+    return out
+
+
+def value_depth(cache: Cache, l0: int, l1: int, rows: torch.Tensor, n_rows: torch.Tensor,
+                weights: torch.Tensor, v_budget: int, depth=None, stream=None):
+    """Per-row value depths from given importances (see bpk.h)."""
+    u = (cache.S, l1 - l0, cache.H)
+    ld = rows.shape[-1]
+    _need(rows, "rows", torch.int32, (*u, ld))
+    _need(n_rows, "n_rows", torch.int32, u)
+    _need(weights, "weights", torch.float32, (*u, ld))
+    if depth is None:
+        depth = torch.empty((*u, ld), dtype=torch.uint8, device=rows.device)
+    _need(depth, "depth", torch.uint8, (*u, ld))
+    _check(LIB.bpk_value_depth(cache.struct(), l0, l1, rows.data_ptr(), n_rows.data_ptr(), int(ld),
+                               weights.data_ptr(), int(v_budget), depth.data_ptr(),
+                               _stream(stream)))
+    return depth
+
+
+def _value_outputs(cache, u, k, union_out, v_depth_out):
+    if union_out is not None:
+        _need(union_out, "union_out", torch.int32, (*u, cache.G * k))
+    if v_depth_out is not None:
+        _need(v_depth_out, "v_depth_out", torch.uint8, (*u, cache.G * k))
+
+
+def sparse_attend_v(cache: Cache, q: torch.Tensor, idx: torch.Tensor, l0: int, l1: int, k: int,
+                    softmax_scale: float, v_budget: int, out=None, union_out=None,
+                    v_depth_out=None, ws=None, stream=None):
+    """Sparse attention with value rows read at per-token depths."""
+    u = (cache.S, l1 - l0, cache.H)
+    _need(q, "q", torch.bfloat16, (*u, cache.G, HEAD_DIM))
+    _need(idx, "idx", torch.int32, (*u, cache.G, k))
+    if out is None:
+        out = torch.empty((*u, cache.G, HEAD_DIM), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.float32, (*u, cache.G, HEAD_DIM))
+    _value_outputs(cache, u, k, union_out, v_depth_out)
+    need = workspace_bytes(cache, BPK_OP_ATTEND_V, l0, l1, k)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(LIB.bpk_sparse_attend_v(cache.struct(), q.data_ptr(), idx.data_ptr(), l0, l1, int(k),
+                                   float(softmax_scale), int(v_budget), out.data_ptr(),
+                                   _ptr(union_out), _ptr(v_depth_out), ws.data_ptr(), ws.numel(),
+                                   _stream(stream)))
+    return out
+
+
+def decode_step_v(cache: Cache, q: torch.Tensor, l0: int, l1: int, budget: int, k: int,
+                  softmax_scale: float, v_budget: int, out=None, depth_out=None, idx_out=None,
+                  union_out=None, v_depth_out=None, ws=None, stream=None):
+    """decode_step whose attention reads the value rows at per-token depths."""
+    u = (cache.S, l1 - l0, cache.H)
+    _need(q, "q", torch.bfloat16, (*u, cache.G, HEAD_DIM))
+    if out is None:
+        out = torch.empty((*u, cache.G, HEAD_DIM), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.float32, (*u, cache.G, HEAD_DIM))
+    if depth_out is not None:
+        _need(depth_out, "depth_out", torch.uint8, (*u, HEAD_DIM))
+    if idx_out is not None:
+        _need(idx_out, "idx_out", torch.int32, (*u, cache.G, k))
+    _value_outputs(cache, u, k, union_out, v_depth_out)
+    need = workspace_bytes(cache, BPK_OP_DECODE_V, l0, l1, k)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(LIB.bpk_decode_step_v(cache.struct(), q.data_ptr(), l0, l1, int(budget), int(k),
+                                 float(softmax_scale), int(v_budget), out.data_ptr(),
+                                 _ptr(depth_out), _ptr(idx_out), _ptr(union_out),
+                                 _ptr(v_depth_out), ws.data_ptr(), ws.numel(), _stream(stream)))
     return out
 
 

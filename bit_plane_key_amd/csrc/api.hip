@@ -106,6 +106,8 @@ int check_cache(const bpk_cache_t* c, int l0, int l1, bpk::Geom* g) {
   if (!c->n_tokens) return fail(BPK_EINVAL, "n_tokens is NULL");
   if (!c->k_rows || !c->v_rows || !c->planes || !c->scales || !c->chan_var)
     return fail(BPK_EINVAL, "cache array pointer is NULL");
+  if ((c->v_planes == nullptr) != (c->v_scales == nullptr))
+    return fail(BPK_EINVAL, "v_planes and v_scales must both be set or both be NULL");
   for (int s = 0; s < c->num_seqs; ++s)
     if (c->n_tokens[s] < 0 || c->n_tokens[s] > c->capacity)
       return fail(BPK_EINVAL, "n_tokens[%d] = %lld outside [0, capacity]", s,
@@ -149,7 +151,8 @@ struct DecodeWs {
   size_t total;
 };
 
-DecodeWs decode_ws(const bpk::Geom& g, int k) {
+// With `values` the attention region fits the value-depth attention.
+DecodeWs decode_ws(const bpk::Geom& g, int k, bool values = false) {
   DecodeWs w;
   const size_t units = (size_t)g.units();
   const size_t uh = units * g.G;
@@ -165,7 +168,8 @@ DecodeWs decode_ws(const bpk::Geom& g, int k) {
   w.depth = off;   off += align256(units * bpk::D);
   w.scores = off;  off += align256(uh * (size_t)g.cap * sizeof(float));
   w.idx = off;     off += align256(uh * (size_t)k * sizeof(int32_t));
-  w.attend = off;  off += align256(bpk::attend_ws_bytes(g, k));
+  w.attend = off;
+  off += align256(values ? bpk::attend_v_ws_bytes(g, k) : bpk::attend_ws_bytes(g, k));
   w.sample = off;  off += align256(uh * (size_t)w.sample_ld * sizeof(float));
   w.thresh = off;  off += align256(uh * sizeof(uint32_t));
   w.count = off;   off += align256(uh * (size_t)w.regions * bpk::CAND_PARTS * sizeof(int32_t));
@@ -198,6 +202,8 @@ size_t bpk_workspace_bytes(const bpk_cache_t* c, int32_t op, int32_t l0, int32_t
     case BPK_OP_ATTEND: return bpk::attend_ws_bytes(g, k);
     case BPK_OP_DECODE: return decode_ws(g, k).total;
     case BPK_OP_POOLED: return pooled_ws(g);
+    case BPK_OP_ATTEND_V: return bpk::attend_v_ws_bytes(g, k);
+    case BPK_OP_DECODE_V: return decode_ws(g, k, true).total;
     default: return 0;
   }
 }
@@ -223,9 +229,12 @@ int bpk_encode_append(const bpk_cache_t* c, int32_t seq, const void* k_new, cons
     if (rc) return rc;
   }
   const long long b0 = n0 / BPK_BLOCK, b1 = (n0 + n_new) / BPK_BLOCK;
-  return hip_status(bpk::launch_encode(g, seq, c->k_dtype, c->k_rows, c->rot, c->planes,
-                                       c->scales, b0, b1 - b0, st),
-                    "encode");
+  rc = hip_status(bpk::launch_encode(g, seq, c->k_dtype, c->k_rows, c->rot, c->planes, c->scales,
+                                     b0, b1 - b0, st),
+                  "encode");
+  if (rc || !c->v_planes) return rc;
+  return hip_status(bpk::launch_vencode(g, seq, c->v_rows, c->v_planes, c->v_scales, n0, n_new, st),
+                    "encode values");
 }
 
 int bpk_alloc_depth(const bpk_cache_t* c, const uint16_t* q, int32_t l0, int32_t l1,
@@ -367,6 +376,44 @@ int bpk_sparse_attend(const bpk_cache_t* c, const uint16_t* q, const int32_t* id
                     "sparse_attend");
 }
 
+int bpk_value_depth(const bpk_cache_t* c, int32_t l0, int32_t l1, const int32_t* rows,
+                    const int32_t* n_rows, int32_t row_ld, const float* weights,
+                    int32_t v_budget, uint8_t* depth, void* stream) {
+  bpk::Geom g;
+  int rc = check_cache(c, l0, l1, &g);
+  if (rc) return rc;
+  if (!c->v_planes) return fail(BPK_EINVAL, "the cache has no value planes");
+  if (!rows || !n_rows || !weights || !depth)
+    return fail(BPK_EINVAL, "rows, n_rows, weights and depth must be non-NULL");
+  if (row_ld < 1 || row_ld > BPK_MAX_SELECTED)
+    return fail(BPK_EINVAL, "row_ld %d outside [1, %d]", row_ld, BPK_MAX_SELECTED);
+  if (v_budget < 0) return fail(BPK_EINVAL, "v_budget < 0");
+  return hip_status(bpk::launch_value_depth(g, rows, n_rows, row_ld, weights, c->v_scales,
+                                            v_budget, depth, static_cast<hipStream_t>(stream)),
+                    "value_depth");
+}
+
+int bpk_sparse_attend_v(const bpk_cache_t* c, const uint16_t* q, const int32_t* idx, int32_t l0,
+                        int32_t l1, int32_t k, float softmax_scale, int32_t v_budget, float* out,
+                        int32_t* union_out, uint8_t* v_depth_out, void* ws, size_t ws_bytes,
+                        void* stream) {
+  bpk::Geom g;
+  int rc = check_cache(c, l0, l1, &g);
+  if (rc) return rc;
+  if (!q || !idx || !out) return fail(BPK_EINVAL, "q, idx and out must be non-NULL");
+  if (!c->v_planes) return fail(BPK_EINVAL, "the cache has no value planes");
+  if (v_budget < 0) return fail(BPK_EINVAL, "v_budget < 0");
+  rc = check_k(c, k);
+  if (rc) return rc;
+  const size_t need = bpk::attend_v_ws_bytes(g, k);
+  if (!ws || ws_bytes < need)
+    return fail(BPK_EWORKSPACE, "workspace of %zu bytes < %zu needed", ws_bytes, need);
+  return hip_status(bpk::launch_attend_v(g, c->k_dtype, c->k_rows, c->v_planes, c->v_scales, q,
+                                         idx, k, softmax_scale, v_budget, out, union_out,
+                                         v_depth_out, ws, static_cast<hipStream_t>(stream)),
+                    "sparse_attend_v");
+}
+
 }  // extern "C"
 
 namespace {
@@ -378,8 +425,9 @@ int decode_step_impl(const bpk_cache_t* c, const bpk::Geom& g, const uint16_t* q
                      int32_t budget_planes, int32_t k, float softmax_scale, float* out,
                      uint8_t* depth_out, int32_t* idx_out, char* base, bool traced,
                      hipStream_t st, const uint8_t* depth_in = nullptr,
-                     const float* qb_in = nullptr) {
-  const DecodeWs w = decode_ws(g, k);
+                     const float* qb_in = nullptr, int v_budget = -1,
+                     int32_t* union_out = nullptr, uint8_t* vdepth_out = nullptr) {
+  const DecodeWs w = decode_ws(g, k, v_budget >= 0);
   const bool given = depth_in != nullptr;
   float* q_basis = given ? const_cast<float*>(qb_in) : reinterpret_cast<float*>(base + w.q_basis);
   uint8_t* depth = given ? const_cast<uint8_t*>(depth_in)
@@ -460,6 +508,11 @@ int decode_step_impl(const bpk_cache_t* c, const bpk::Geom& g, const uint16_t* q
     if (rc) return rc;
   }
   auto t = timer(BPK_STAGE_ATTEND);
+  if (v_budget >= 0)
+    return hip_status(bpk::launch_attend_v(g, c->k_dtype, c->k_rows, c->v_planes, c->v_scales, q,
+                                           idx, k, softmax_scale, v_budget, out, union_out,
+                                           vdepth_out, base + w.attend, st),
+                      "decode_step/attend_v");
   return hip_status(bpk::launch_attend(g, c->k_dtype, c->k_rows, c->v_rows, q, idx, k,
                                        softmax_scale, out, base + w.attend, st),
                     "decode_step/attend");
@@ -511,6 +564,23 @@ int bpk_decode_step(const bpk_cache_t* c, const uint16_t* q, int32_t l0, int32_t
     return fail(BPK_EWORKSPACE, "workspace of %zu bytes < %zu needed", ws_bytes, need);
   return decode_step_impl(c, g, q, budget_planes, k, softmax_scale, out, depth_out, idx_out,
                           static_cast<char*>(ws), true, static_cast<hipStream_t>(stream));
+}
+
+int bpk_decode_step_v(const bpk_cache_t* c, const uint16_t* q, int32_t l0, int32_t l1,
+                      int32_t budget_planes, int32_t k, float softmax_scale, int32_t v_budget,
+                      float* out, uint8_t* depth_out, int32_t* idx_out, int32_t* union_out,
+                      uint8_t* v_depth_out, void* ws, size_t ws_bytes, void* stream) {
+  bpk::Geom g;
+  int rc = check_decode(c, l0, l1, q, budget_planes, k, out, &g);
+  if (rc) return rc;
+  if (!c->v_planes) return fail(BPK_EINVAL, "the cache has no value planes");
+  if (v_budget < 0) return fail(BPK_EINVAL, "v_budget < 0");
+  const size_t need = decode_ws(g, k, true).total;
+  if (!ws || ws_bytes < need)
+    return fail(BPK_EWORKSPACE, "workspace of %zu bytes < %zu needed", ws_bytes, need);
+  return decode_step_impl(c, g, q, budget_planes, k, softmax_scale, out, depth_out, idx_out,
+                          static_cast<char*>(ws), true, static_cast<hipStream_t>(stream), nullptr,
+                          nullptr, v_budget, union_out, v_depth_out);
 }
 
 int bpk_decode_step_depth(const bpk_cache_t* c, const uint16_t* q, const float* q_basis,

@@ -15,6 +15,8 @@
 //    the same way and accumulated for every head with its weights.  The split
 //    writes (max, sum, unnormalised output) per head.
 // 3. combine_kernel: log-sum-exp merge of the splits per (unit, head).
+// launch_union_logits runs 1 and the logits half of 2 for the value-depth
+// attention (values.hip).
 #include <limits.h>
 
 #include "bpk_internal.h"
@@ -198,6 +200,7 @@ struct AttArgs {
   const int32_t* ucount;
   float* part;
   int nsplit;
+  float* logits;  // logits-only launches: [unit][G][G * k], by union position
 };
 
 // sum over the 16 lanes of a DPP row (every lane of the row gets it; the
@@ -214,8 +217,10 @@ __device__ __forceinline__ float row16_sum(float v) {
 // One workgroup per (split of ATT_ROWS union rows, unit).  Rows are read whole
 // and coalesced: in each wavefront, lane l takes 16-byte chunk l % 16 (8
 // channels) of row 4 it + l / 16 of the wavefront's 64, for it = 0..15, with
-// all 16 loads in flight before the arithmetic.
-template <int G, bool F32>
+// all 16 loads in flight before the arithmetic.  With LG the kernel stops
+// after the logits and writes them (-inf where a head did not select the
+// row) for the value-depth attention.
+template <int G, bool F32, bool LG>
 __global__ __launch_bounds__(ATT_THREADS) void attend_kernel(AttArgs a) {
   constexpr int RPW = ATT_ROWS / (ATT_THREADS / 64);  // rows per wavefront (64)
   constexpr int IT = RPW / 4;                          // 4 rows per wavefront load
@@ -234,7 +239,7 @@ __global__ __launch_bounds__(ATT_THREADS) void attend_kernel(AttArgs a) {
   const int nr = count - r0 < ATT_ROWS ? (count - r0 > 0 ? count - r0 : 0) : ATT_ROWS;
   float* part = a.part + (((long long)u * a.nsplit + split) * G) * (D + 2);
   if (nr == 0) {  // an empty split contributes nothing
-    if (tid < G) part[tid * (D + 2)] = -INFINITY;
+    if (!LG && tid < G) part[tid * (D + 2)] = -INFINITY;
     return;
   }
   {
@@ -305,6 +310,14 @@ __global__ __launch_bounds__(ATT_THREADS) void attend_kernel(AttArgs a) {
       d = row16_sum(d);
       if (ch == 0) p[r][h] = ((mask >> h) & 1) ? d * a.scale : -INFINITY;
     }
+  }
+  if constexpr (LG) {
+    __syncthreads();
+    for (int e = tid; e < G * ATT_ROWS; e += ATT_THREADS) {
+      const int h = e / ATT_ROWS, r = e % ATT_ROWS;
+      if (r < nr) a.logits[((long long)u * G + h) * sel + r0 + r] = p[r][h];
+    }
+    return;
   }
   // the V rows (same mapping), in flight during the softmax reductions
   uint4 vv[IT];
@@ -412,11 +425,29 @@ __global__ __launch_bounds__(G * D) void combine_kernel(const Geom g, const floa
 template <int G>
 void launch_att_g(const AttArgs& a, int k_dtype, float* out, hipStream_t st) {
   dim3 grid((unsigned)a.nsplit, (unsigned)a.g.units());
+  if (a.logits) {
+    if (k_dtype == BPK_F32)
+      attend_kernel<G, true, true><<<grid, ATT_THREADS, 0, st>>>(a);
+    else
+      attend_kernel<G, false, true><<<grid, ATT_THREADS, 0, st>>>(a);
+    return;
+  }
   if (k_dtype == BPK_F32)
-    attend_kernel<G, true><<<grid, ATT_THREADS, 0, st>>>(a);
+    attend_kernel<G, true, false><<<grid, ATT_THREADS, 0, st>>>(a);
   else
-    attend_kernel<G, false><<<grid, ATT_THREADS, 0, st>>>(a);
+    attend_kernel<G, false, false><<<grid, ATT_THREADS, 0, st>>>(a);
   combine_kernel<G><<<a.g.units(), G * D, 0, st>>>(a.g, a.part, a.nsplit, out);
+}
+
+hipError_t launch_att(const AttArgs& aa, int k_dtype, float* out, hipStream_t st) {
+  switch (aa.g.G) {
+    case 1: launch_att_g<1>(aa, k_dtype, out, st); break;
+    case 2: launch_att_g<2>(aa, k_dtype, out, st); break;
+    case 4: launch_att_g<4>(aa, k_dtype, out, st); break;
+    case 8: launch_att_g<8>(aa, k_dtype, out, st); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -435,15 +466,19 @@ hipError_t launch_attend(const Geom& g, int k_dtype, const void* k_rows, const u
   float* part = reinterpret_cast<float*>(base + w.part);
   UnionArgs ua{g, idx, k, uidx, umask, ucount};
   union_kernel<<<g.units(), UNION_THREADS, 0, st>>>(ua);
-  AttArgs aa{g, k_rows, v_rows, q, k, scale, uidx, umask, ucount, part, w.nsplit};
-  switch (g.G) {
-    case 1: launch_att_g<1>(aa, k_dtype, out, st); break;
-    case 2: launch_att_g<2>(aa, k_dtype, out, st); break;
-    case 4: launch_att_g<4>(aa, k_dtype, out, st); break;
-    case 8: launch_att_g<8>(aa, k_dtype, out, st); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+  AttArgs aa{g, k_rows, v_rows, q, k, scale, uidx, umask, ucount, part, w.nsplit, nullptr};
+  return launch_att(aa, k_dtype, out, st);
+}
+
+hipError_t launch_union_logits(const Geom& g, int k_dtype, const void* k_rows, const uint16_t* q,
+                               const int32_t* idx, int k, float scale, int32_t* uidx,
+                               uint8_t* umask, int32_t* ucount, float* logits, hipStream_t st) {
+  if (g.units() == 0) return hipSuccess;
+  UnionArgs ua{g, idx, k, uidx, umask, ucount};
+  union_kernel<<<g.units(), UNION_THREADS, 0, st>>>(ua);
+  const int nsplit = (int)(((long long)g.G * k + ATT_ROWS - 1) / ATT_ROWS);
+  AttArgs aa{g, k_rows, nullptr, q, k, scale, uidx, umask, ucount, nullptr, nsplit, logits};
+  return launch_att(aa, k_dtype, nullptr, st);
 }
 
 }  // namespace bpk

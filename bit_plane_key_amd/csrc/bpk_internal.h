@@ -148,9 +148,51 @@ hipError_t launch_attend(const Geom& g, int k_dtype, const void* k_rows, const u
                          const uint16_t* q, const int32_t* idx, int k, float scale, float* out,
                          void* ws, hipStream_t st);
 
+// union of the heads' selections and the logits of every union row
+// ([unit][G][G * k], -inf where a head did not select the row), as the first
+// half of launch_attend; uidx / umask / ucount as its union stage
+hipError_t launch_union_logits(const Geom& g, int k_dtype, const void* k_rows, const uint16_t* q,
+                               const int32_t* idx, int k, float scale, int32_t* uidx,
+                               uint8_t* umask, int32_t* ucount, float* logits, hipStream_t st);
+
+// ---- value-side depths (values.hip) ----
+// code the value rows of tokens [n0, n0 + n_new) of sequence seq
+hipError_t launch_vencode(const Geom& g, int seq, const uint16_t* v_rows, uint8_t* vplanes,
+                          uint16_t* vscales, long long n0, long long n_new, hipStream_t st);
+size_t attend_v_ws_bytes(const Geom& g, int k);
+hipError_t launch_attend_v(const Geom& g, int k_dtype, const void* k_rows, const uint8_t* vplanes,
+                           const uint16_t* vscales, const uint16_t* q, const int32_t* idx, int k,
+                           float scale, int v_budget, float* out, int32_t* union_out,
+                           uint8_t* vdepth_out, void* ws, hipStream_t st);
+hipError_t launch_value_depth(const Geom& g, const int32_t* rows, const int32_t* n_rows,
+                              int row_ld, const float* weights, const uint16_t* vscales,
+                              int v_budget, uint8_t* depth, hipStream_t st);
+
 // ---- small device helpers ----
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(((uint32_t)b) << 16);
+}
+
+// Code of one value: clip(floor(v / s), -8, 7) + 8 with the exact real floor.
+// m * s and (m + 1) * s are exact in fp32 (|m| < 2^5, s has 11 significant
+// bits), so the correction removes any rounding of the quotient.
+__device__ __forceinline__ uint32_t quant_code(float v, float s) {
+  if (s == 0.f) return 8u;
+  float m = floorf(v / s);
+  if (m * s > v)
+    m -= 1.f;
+  else if ((m + 1.f) * s <= v)
+    m += 1.f;
+  m = fminf(fmaxf(m, -8.f), 7.f);
+  return (uint32_t)((int)m + 8);
+}
+
+// fp16 scale of a maximum magnitude: amax / 8 rounded to nearest even,
+// saturated at 65504 (amax / 8 is exact in fp32)
+__device__ __forceinline__ _Float16 scale_of_max(float amax) {
+  _Float16 hs = (_Float16)(amax * 0.125f);
+  if (__builtin_isinf((float)hs)) hs = (_Float16)65504.0f;
+  return hs;
 }
 
 // monotone map float -> uint32 (larger float, larger key); -0 is mapped to +0

@@ -22,20 +22,6 @@ struct EncArgs {
   uint16_t* scales;
 };
 
-// Code of one value: clip(floor(v / s), -8, 7) + 8 with the exact real floor.
-// m * s and (m + 1) * s are exact in fp32 (|m| < 2^5, s has 11 significant
-// bits), so the correction removes any rounding of the quotient.
-__device__ __forceinline__ uint32_t quant_code(float v, float s) {
-  if (s == 0.f) return 8u;
-  float m = floorf(v / s);
-  if (m * s > v)
-    m -= 1.f;
-  else if ((m + 1.f) * s <= v)
-    m += 1.f;
-  m = fminf(fmaxf(m, -8.f), 7.f);
-  return (uint32_t)((int)m + 8);
-}
-
 template <bool F32, bool ROT>
 __global__ __launch_bounds__(128) void encode_kernel(EncArgs a) {
   __shared__ float tile[ROT ? BLK : 1][ROT ? D : 1];
@@ -76,8 +62,7 @@ __global__ __launch_bounds__(128) void encode_kernel(EncArgs a) {
   float amax = 0.f;
 #pragma unroll
   for (int i = 0; i < BLK; ++i) amax = fmaxf(amax, fabsf(v[i]));
-  _Float16 hs = (_Float16)(amax * 0.125f);  // round to nearest even
-  if (__builtin_isinf((float)hs)) hs = (_Float16)65504.0f;
+  const _Float16 hs = scale_of_max(amax);
   const float s = (float)hs;
 
   uint64_t w0 = 0, w1 = 0, w2 = 0, w3 = 0;

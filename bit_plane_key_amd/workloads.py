@@ -20,17 +20,20 @@ from ._lib import Cache, encode_append
 
 
 def build_cache(cfg: Config, n: int | None = None, device: str = "cuda",
-                host_resident: bool = False) -> Cache:
+                host_resident: bool = False, values: bool = False) -> Cache:
     """Allocate the cache of ``cfg``, fill n tokens of rows and encode them.
     With host_resident the rows, planes and scales end in pinned host memory
-    (built on the GPU, then copied)."""
+    (built on the GPU, then copied); with values the cache also holds value
+    planes."""
     n = cfg.n if n is None else n
     if host_resident:
-        dev = build_cache(cfg, n, device)
+        dev = build_cache(cfg, n, device, values=values)
         cache = Cache(cfg.seqs, cfg.layers, cfg.heads, cfg.capacity, group=cfg.group,
                       k_dtype=cfg.k_dtype, rotated=cfg.rotated, device=device,
-                      host_resident=True)
-        for name in ("k_rows", "v_rows", "planes", "scales", "chan_var"):
+                      host_resident=True, values=values)
+        names = ["k_rows", "v_rows", "planes", "scales", "chan_var"]
+        names += ["v_planes", "v_scales"] if values else []
+        for name in names:
             getattr(cache, name).copy_(getattr(dev, name))
         if cfg.rotated:
             cache.rot.copy_(dev.rot)
@@ -39,7 +42,7 @@ def build_cache(cfg: Config, n: int | None = None, device: str = "cuda",
         torch.cuda.synchronize()
         return cache
     cache = Cache(cfg.seqs, cfg.layers, cfg.heads, cfg.capacity, group=cfg.group,
-                  k_dtype=cfg.k_dtype, rotated=cfg.rotated, device=device)
+                  k_dtype=cfg.k_dtype, rotated=cfg.rotated, device=device, values=values)
     var = np.zeros((cfg.seqs, cfg.layers, cfg.heads, cfg.dim), dtype=np.float32)
     for s in range(cfg.seqs):
         for l in range(cfg.layers):

@@ -60,7 +60,14 @@ enum bpk_status {
 
 enum bpk_dtype { BPK_F32 = 0, BPK_BF16 = 1 };
 
-enum bpk_op { BPK_OP_SELECT = 3, BPK_OP_ATTEND = 4, BPK_OP_DECODE = 5, BPK_OP_POOLED = 6 };
+enum bpk_op {
+  BPK_OP_SELECT = 3,
+  BPK_OP_ATTEND = 4,
+  BPK_OP_DECODE = 5,
+  BPK_OP_POOLED = 6,
+  BPK_OP_ATTEND_V = 7,
+  BPK_OP_DECODE_V = 8
+};
 
 /*
  * The cache: storage shared by every entry point.  All arrays are
@@ -70,8 +77,9 @@ enum bpk_op { BPK_OP_SELECT = 3, BPK_OP_ATTEND = 4, BPK_OP_DECODE = 5, BPK_OP_PO
  * v_rows   [S][L][H][capacity][128]  value rows, bf16 bit patterns.
  * planes   [S][L][H][128][4][NBS] uint64, NBS = BPK_BLOCK_STRIDE(capacity) (the
  *          capacity in blocks rounded up to a multiple of 8, so that every row
- *          starts 64-byte aligned; words past capacity/64 are never read or
- *          written).  Word (j, p, b) holds bit p
+ *          starts 64-byte aligned; words past capacity/64 are never written,
+ *          may be loaded by whole-row reads, and never change a result).
+ *          Word (j, p, b) holds bit p
  *          (p = 0 is the most significant bit, i.e. the sign) of the 4-bit
  *          codes of channel j over the 64 tokens of block b; bit i of the word
  *          belongs to token 64 b + i.  Channel-major, so the first t planes of
@@ -85,6 +93,16 @@ enum bpk_op { BPK_OP_SELECT = 3, BPK_OP_ATTEND = 4, BPK_OP_DECODE = 5, BPK_OP_PO
  *          basis z = R^T x (the KLT basis of Fathom §1, contributions).
  * n_tokens HOST [S]: tokens present in each sequence, including the tokens of
  *          an open (incomplete) trailing block, which have rows but no planes.
+ * v_planes NULL, or [S][L][H][capacity][4][16] uint8: value planes for the
+ *          value-depth entry points (ReadKV §5.3: every channel of a token
+ *          shares one depth; §6.1: progressive planes).  Each token's value
+ *          row is coded with one scale and the same 4-bit symmetric code as
+ *          the keys; the 16 bytes of plane p hold bit 3 - p of its 128 codes,
+ *          channel j in bit j % 8 of byte j / 8.  A token's 64 bytes are
+ *          contiguous, so reading it at depth t reads its first 16 t bytes.
+ * v_scales NULL, or [S][L][H][capacity] fp16 bit patterns: per token, its
+ *          max |v| divided by 8 (round to nearest even, saturated at 65504).
+ *          v_planes and v_scales are both set or both NULL.
  */
 typedef struct bpk_cache {
   int32_t num_seqs;
@@ -101,6 +119,8 @@ typedef struct bpk_cache {
   uint16_t* scales;
   const float* chan_var;
   const float* rot;
+  uint8_t* v_planes;
+  uint16_t* v_scales;
 } bpk_cache_t;
 
 /*
@@ -115,6 +135,9 @@ typedef struct bpk_cache {
  * 65504) and the codes c = clip(floor(k / s), -8, 7) + 8 with the exact real
  * floor (c = 8 when s = 0), packed into the four plane words.  With rot set,
  * k is first mapped to z = R^T k (fp64 sum over d ascending, rounded to fp32).
+ * With v_planes set, every appended token's value row is coded at once
+ * (there is no block to wait for): s = fp16_rne(max_j |v_j| / 8) and the
+ * same codes, written as the token's four planes.
  * The caller advances n_tokens[seq] by n_new afterwards.
  * Errors: BPK_EINVAL (seq out of range, n_new < 0, only one of k_new / v_new
  * given), BPK_ECAPACITY (n_tokens[seq] + n_new > capacity).
@@ -309,9 +332,63 @@ int bpk_decode_fallback_units(const bpk_cache_t* cache, int32_t l0, int32_t l1, 
                               const void* ws, size_t ws_bytes, int32_t* count, void* stream);
 
 /*
+ * Value-side depths (ReadKV §5.3, §5.4) from given importances: for each
+ * unit, rows[u][0 .. n_rows[u]) are tokens of its sequence and
+ * weights[u][r] their importances a_r (fp32, finite and >= 0; anything else
+ * counts as 0).  The gain of row r is w_r = a_r * s_r^2 (fp32, s_r the
+ * token's value scale) and its t-th plane is worth w_r * 4^-t (fp32); the
+ * v_budget planes go to the candidates (r, t) of largest positive value,
+ * equal values to the lower row, then the lower plane, and no plane goes to
+ * a candidate worth 0.  Writes depth[u][r] = planes granted to row r for
+ * r < row_ld (0 past n_rows[u]).  Pass the rows in token order for the
+ * lower-token tie rule.  A token outside [0, n_tokens) gets no plane.
+ * rows, weights, depth: [S][nl][H][row_ld]; n_rows: [S][nl][H] int32
+ * (device), clamped to [0, row_ld].
+ * Errors: BPK_EINVAL (NULL pointer, v_budget < 0, row_ld outside
+ * [1, BPK_MAX_SELECTED], no value planes in the cache).
+ */
+int bpk_value_depth(const bpk_cache_t* cache, int32_t l0, int32_t l1, const int32_t* rows,
+                    const int32_t* n_rows, int32_t row_ld, const float* weights,
+                    int32_t v_budget, uint8_t* depth, void* stream);
+
+/*
+ * Sparse attention with the value rows read at per-token depths (Fathom §2
+ * for the selection and the per-head softmax from exact keys; ReadKV §5.3
+ * for the value stage).  Per unit: the union of the G heads' selected rows
+ * (token order), each head's softmax p_h over its own rows, importances
+ * a_r = sum_h p_hr^2 (p_hr = 0 where head h did not select r), depths as
+ * bpk_value_depth with budget v_budget, and
+ * out_h = sum_r p_hr v_hat_r, v_hat_r the row rebuilt from its first t_r
+ * value planes (cell midpoints times the token's scale; 0 at depth 0).
+ * q, idx, out and the errors as bpk_sparse_attend; union_out
+ * ([S][nl][H][G * k] int32: the union's tokens in order, -1 past its end)
+ * and v_depth_out ([S][nl][H][G * k] uint8: each union row's depth, 0 past
+ * the end) are optional.  ws: bpk_workspace_bytes(.., BPK_OP_ATTEND_V, ..).
+ * The probabilities are fp32 (expf), so a depth can differ from an exact
+ * computation's only where two plane values are within rounding of each
+ * other.  Errors as bpk_sparse_attend, and BPK_EINVAL for v_budget < 0 or
+ * no value planes.
+ */
+int bpk_sparse_attend_v(const bpk_cache_t* cache, const uint16_t* q, const int32_t* idx,
+                        int32_t l0, int32_t l1, int32_t k, float softmax_scale,
+                        int32_t v_budget, float* out, int32_t* union_out,
+                        uint8_t* v_depth_out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * bpk_decode_step with bpk_sparse_attend_v as its attention stage: alloc ->
+ * scan -> select -> attention with value depths.  Arguments as
+ * bpk_decode_step, plus v_budget, union_out and v_depth_out as
+ * bpk_sparse_attend_v; ws: bpk_workspace_bytes(.., BPK_OP_DECODE_V, ..).
+ */
+int bpk_decode_step_v(const bpk_cache_t* cache, const uint16_t* q, int32_t l0, int32_t l1,
+                      int32_t budget_planes, int32_t k, float softmax_scale, int32_t v_budget,
+                      float* out, uint8_t* depth_out, int32_t* idx_out, int32_t* union_out,
+                      uint8_t* v_depth_out, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Workspace bytes an entry point needs for layers [l0, l1) and top-k k
- * (op = BPK_OP_SELECT, BPK_OP_ATTEND, BPK_OP_DECODE or BPK_OP_POOLED).  Returns 0 for an
- * invalid cache or op.
+ * (op = BPK_OP_SELECT, BPK_OP_ATTEND, BPK_OP_DECODE, BPK_OP_POOLED,
+ * BPK_OP_ATTEND_V or BPK_OP_DECODE_V).  Returns 0 for an invalid cache or op.
  */
 size_t bpk_workspace_bytes(const bpk_cache_t* cache, int32_t op, int32_t l0, int32_t l1,
                            int32_t k);

@@ -172,3 +172,37 @@ def test_trace_calls_validate_and_start_empty(lib):
     ms, calls = lib.trace_read()
     assert calls == 0 and set(ms) == set(lib.STAGES) and all(v == 0.0 for v in ms.values())
     assert lib.LIB.bpk_trace_enable(0) == 0
+
+
+def test_value_entry_points_validate(lib):
+    """Value-depth calls need value planes, a non-negative budget and a row
+    stride within [1, BPK_MAX_SELECTED]; v_planes and v_scales go together."""
+    s, n = _cache(lib)
+    c = ctypes.pointer(s)
+    # no value planes in the cache
+    assert lib.LIB.bpk_value_depth(c, 0, 1, FAKE, FAKE, 64, FAKE, 10, FAKE, None) == -1
+    assert "value planes" in lib.last_error()
+    assert lib.LIB.bpk_sparse_attend_v(c, FAKE, FAKE, 0, 1, 512, 0.088, 10, FAKE, None, None,
+                                       FAKE, 1 << 30, None) == -1
+    assert lib.LIB.bpk_decode_step_v(c, FAKE, 0, 1, 88, 512, 0.088, 10, FAKE, None, None, None,
+                                     None, FAKE, 1 << 30, None) == -1
+    s, n = _cache(lib, v_planes=FAKE)            # scales missing
+    assert lib.LIB.bpk_alloc_depth(ctypes.pointer(s), FAKE, 0, 1, 88, FAKE, FAKE, None) == -1
+    s, n = _cache(lib, v_planes=FAKE, v_scales=FAKE)
+    c = ctypes.pointer(s)
+    assert lib.LIB.bpk_value_depth(c, 0, 1, FAKE, FAKE, 0, FAKE, 10, FAKE, None) == -1
+    assert lib.LIB.bpk_value_depth(c, 0, 1, FAKE, FAKE, 8193, FAKE, 10, FAKE, None) == -1
+    assert lib.LIB.bpk_value_depth(c, 0, 1, FAKE, FAKE, 64, FAKE, -1, FAKE, None) == -1
+    assert lib.LIB.bpk_value_depth(c, 0, 1, FAKE, None, 64, FAKE, 1, FAKE, None) == -1
+    assert lib.LIB.bpk_sparse_attend_v(c, FAKE, FAKE, 0, 1, 512, 0.088, -1, FAKE, None, None,
+                                       FAKE, 1 << 30, None) == -1
+    need = lib.LIB.bpk_workspace_bytes(c, lib.BPK_OP_ATTEND_V, 0, 1, 512)
+    assert need > lib.LIB.bpk_workspace_bytes(c, lib.BPK_OP_ATTEND, 0, 1, 512)
+    assert lib.LIB.bpk_sparse_attend_v(c, FAKE, FAKE, 0, 1, 512, 0.088, 10, FAKE, None, None,
+                                       FAKE, need - 1, None) == -3
+    need_d = lib.LIB.bpk_workspace_bytes(c, lib.BPK_OP_DECODE_V, 0, 1, 512)
+    assert need_d >= lib.LIB.bpk_workspace_bytes(c, lib.BPK_OP_DECODE, 0, 1, 512)
+    assert lib.LIB.bpk_decode_step_v(c, FAKE, 0, 1, 88, 512, 0.088, 10, FAKE, None, None, None,
+                                     None, FAKE, need_d - 1, None) == -3
+    assert lib.LIB.bpk_decode_step_v(c, FAKE, 0, 1, 88, 512, 0.088, -2, FAKE, None, None, None,
+                                     None, FAKE, need_d, None) == -1
