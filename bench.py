@@ -209,7 +209,8 @@ def main() -> int:
     torch.cuda.set_device(0)
     t0 = time.perf_counter()
     log(f"building {cfg.name}: {cfg.description}")
-    cache = workloads.build_cache(cfg, host_resident=args.host_resident)
+    cache = workloads.build_cache(cfg, host_resident=args.host_resident,
+                                  values=not args.host_resident and not args.no_sweep)
     log(f"cache built in {time.perf_counter() - t0:.1f} s")
     q = workloads.queries(cfg)
     scale = workloads.softmax_scale(cfg)
@@ -391,6 +392,44 @@ def main() -> int:
                        "error_proxy_ratio": round(proxy(lb) / proxy(uni), 4)}
         log(f"calibrated budgets {min(lb)}..{max(lb)}: {calibration}")
 
+    # value-side depths (ReadKV §5.3, §5.4): the same step with every union
+    # row's value read at a per-token depth from its planes, for budgets of
+    # v planes per unit; against the exact-value step: the attention stage's
+    # time, the value bytes read (16 per plane plus the 2-byte scale of each
+    # row read at all, against 256 per bf16 row) and the output's deviation
+    # (max |difference| / max |exact output| per query head)
+    value_depths = {}
+    if cache.v_planes is not None and not appends:
+        bpk.decode_step(cache, q, 0, L, budget, k, scale, out=out, ws=ws)
+        ref_out = out.clone()
+        wsv = torch.empty(bpk.workspace_bytes(cache, bpk.BPK_OP_DECODE_V, 0, L, k),
+                          dtype=torch.uint8, device="cuda")
+        outv = torch.empty_like(out)
+        vdep = torch.empty((cfg.seqs, L, cfg.heads, cfg.group * k), dtype=torch.uint8,
+                           device="cuda")
+        for vb in (k // 2, k, 2 * k, 4 * k, 4 * cfg.group * k):
+            def vstep(vb=vb):
+                bpk.decode_step_v(cache, q, 0, L, budget, k, scale, vb, out=outv,
+                                  v_depth_out=vdep, ws=wsv)
+            for _ in range(2):
+                vstep()
+            ms_v = time_launches(vstep, args.steps)
+            st_v = traced(args.steps, vstep)
+            dv = vdep.to(torch.int64)
+            vbytes = int((16 * dv.sum() + 2 * (dv > 0).sum()).item())
+            dev = ((outv - ref_out).abs().amax(dim=-1)
+                   / ref_out.abs().amax(dim=-1).clamp_min(1e-30)).flatten()
+            value_depths[str(vb)] = {
+                "mean_depth": round(float(dv.sum().item()) / union_rows, 3),
+                "decode_step_us": round(ms_v * 1e3, 1),
+                "attend_us": round(st_v["attend"] * 1e3, 1),
+                "value_bytes": vbytes,
+                "value_bytes_bf16_rows": union_rows * 256,
+                "out_deviation_median": round(float(dev.median().item()), 5),
+                "out_deviation_max": round(float(dev.max().item()), 5)}
+            log(f"value budget {vb}: {value_depths[str(vb)]}")
+        del wsv, outv, vdep, ref_out
+
     # the standalone full scan (scan_scores writes every score: same reads,
     # plus 16 bytes of scores per token)
     del ws
@@ -491,6 +530,7 @@ def main() -> int:
         "budget_sweep": sweep,
         "baselines": baselines,
         "layer_calibration": calibration,
+        "value_depths": value_depths,
     }
     if not args.no_cpu_baseline:
         log("timing the oracle on a CPU sample")

@@ -15,8 +15,8 @@
 //    the same way and accumulated for every head with its weights.  The split
 //    writes (max, sum, unnormalised output) per head.
 // 3. combine_kernel: log-sum-exp merge of the splits per (unit, head).
-// launch_union_logits runs 1 and the logits half of 2 for the value-depth
-// attention (values.hip).
+// launch_union_logits runs 1 and 2 up to the split's softmax statistics for
+// the value-depth attention (values.hip).
 #include <limits.h>
 
 #include "bpk_internal.h"
@@ -25,7 +25,7 @@ namespace bpk {
 namespace {
 
 constexpr int UNION_THREADS = 1024;
-constexpr int ATT_ROWS = 256;
+constexpr int ATT_ROWS = ATT_SPLIT_ROWS;
 constexpr int ATT_THREADS = 256;
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -200,7 +200,8 @@ struct AttArgs {
   const int32_t* ucount;
   float* part;
   int nsplit;
-  float* logits;  // logits-only launches: [unit][G][G * k], by union position
+  float* e;       // LG launches: [unit][G][G * k] exp(logit - split max), by union position
+  float* stats;   // LG launches: [unit][nsplit][G][2] split max and exp-sum
 };
 
 // sum over the 16 lanes of a DPP row (every lane of the row gets it; the
@@ -218,8 +219,9 @@ __device__ __forceinline__ float row16_sum(float v) {
 // and coalesced: in each wavefront, lane l takes 16-byte chunk l % 16 (8
 // channels) of row 4 it + l / 16 of the wavefront's 64, for it = 0..15, with
 // all 16 loads in flight before the arithmetic.  With LG the kernel stops
-// after the logits and writes them (-inf where a head did not select the
-// row) for the value-depth attention.
+// after the split's softmax statistics and writes, for the value-depth
+// attention, e_hr = exp(l_hr - m_h) of every row (0 where head h did not
+// select it) and the split's (m_h, sum_r e_hr).
 template <int G, bool F32, bool LG>
 __global__ __launch_bounds__(ATT_THREADS) void attend_kernel(AttArgs a) {
   constexpr int RPW = ATT_ROWS / (ATT_THREADS / 64);  // rows per wavefront (64)
@@ -311,20 +313,14 @@ __global__ __launch_bounds__(ATT_THREADS) void attend_kernel(AttArgs a) {
       if (ch == 0) p[r][h] = ((mask >> h) & 1) ? d * a.scale : -INFINITY;
     }
   }
-  if constexpr (LG) {
-    __syncthreads();
-    for (int e = tid; e < G * ATT_ROWS; e += ATT_THREADS) {
-      const int h = e / ATT_ROWS, r = e % ATT_ROWS;
-      if (r < nr) a.logits[((long long)u * G + h) * sel + r0 + r] = p[r][h];
-    }
-    return;
-  }
   // the V rows (same mapping), in flight during the softmax reductions
-  uint4 vv[IT];
+  uint4 vv[LG ? 1 : IT];
+  if constexpr (!LG) {
 #pragma unroll
-  for (int it = 0; it < IT; ++it)
-    vv[it] = *reinterpret_cast<const uint4*>(
-        a.v_rows + (gu * a.g.cap + rows[RPW * wave + 4 * it + rs]) * D + 8 * ch);
+    for (int it = 0; it < IT; ++it)
+      vv[it] = *reinterpret_cast<const uint4*>(
+          a.v_rows + (gu * a.g.cap + rows[RPW * wave + 4 * it + rs]) * D + 8 * ch);
+  }
   __syncthreads();
 
   // ---- per-head max and exp-sum over the split (thread tid <-> row tid) ----
@@ -358,6 +354,17 @@ __global__ __launch_bounds__(ATT_THREADS) void attend_kernel(AttArgs a) {
     float v = 0.f;
     for (int w = 0; w < ATT_THREADS / 64; ++w) v += red[w][h];
     sum[h] = v;
+  }
+  if constexpr (LG) {
+    if (tid < nr)
+#pragma unroll
+      for (int h = 0; h < G; ++h) a.e[((long long)u * G + h) * sel + r0 + tid] = p[tid][h];
+    if (tid < G) {
+      float* st = a.stats + (((long long)u * a.nsplit + split) * G + tid) * 2;
+      st[0] = mx[tid];
+      st[1] = sum[tid];
+    }
+    return;
   }
 
   // ---- V (loaded above): the same row mapping; lane accumulates its 8
@@ -425,7 +432,7 @@ __global__ __launch_bounds__(G * D) void combine_kernel(const Geom g, const floa
 template <int G>
 void launch_att_g(const AttArgs& a, int k_dtype, float* out, hipStream_t st) {
   dim3 grid((unsigned)a.nsplit, (unsigned)a.g.units());
-  if (a.logits) {
+  if (a.e) {
     if (k_dtype == BPK_F32)
       attend_kernel<G, true, true><<<grid, ATT_THREADS, 0, st>>>(a);
     else
@@ -466,18 +473,20 @@ hipError_t launch_attend(const Geom& g, int k_dtype, const void* k_rows, const u
   float* part = reinterpret_cast<float*>(base + w.part);
   UnionArgs ua{g, idx, k, uidx, umask, ucount};
   union_kernel<<<g.units(), UNION_THREADS, 0, st>>>(ua);
-  AttArgs aa{g, k_rows, v_rows, q, k, scale, uidx, umask, ucount, part, w.nsplit, nullptr};
+  AttArgs aa{g, k_rows, v_rows, q, k, scale, uidx, umask, ucount, part, w.nsplit, nullptr,
+             nullptr};
   return launch_att(aa, k_dtype, out, st);
 }
 
 hipError_t launch_union_logits(const Geom& g, int k_dtype, const void* k_rows, const uint16_t* q,
                                const int32_t* idx, int k, float scale, int32_t* uidx,
-                               uint8_t* umask, int32_t* ucount, float* logits, hipStream_t st) {
+                               uint8_t* umask, int32_t* ucount, float* e, float* stats,
+                               hipStream_t st) {
   if (g.units() == 0) return hipSuccess;
   UnionArgs ua{g, idx, k, uidx, umask, ucount};
   union_kernel<<<g.units(), UNION_THREADS, 0, st>>>(ua);
   const int nsplit = (int)(((long long)g.G * k + ATT_ROWS - 1) / ATT_ROWS);
-  AttArgs aa{g, k_rows, nullptr, q, k, scale, uidx, umask, ucount, nullptr, nsplit, logits};
+  AttArgs aa{g, k_rows, nullptr, q, k, scale, uidx, umask, ucount, nullptr, nsplit, e, stats};
   return launch_att(aa, k_dtype, nullptr, st);
 }
 

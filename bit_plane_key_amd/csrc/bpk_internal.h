@@ -148,12 +148,15 @@ hipError_t launch_attend(const Geom& g, int k_dtype, const void* k_rows, const u
                          const uint16_t* q, const int32_t* idx, int k, float scale, float* out,
                          void* ws, hipStream_t st);
 
-// union of the heads' selections and the logits of every union row
-// ([unit][G][G * k], -inf where a head did not select the row), as the first
-// half of launch_attend; uidx / umask / ucount as its union stage
+// union of the heads' selections and, per split of 256 union rows, the
+// softmax terms e_hr = exp(l_hr - m_h) ([unit][G][G * k], 0 where head h did
+// not select row r) and the split's (m_h, sum_r e_hr) ([unit][split][G][2]),
+// as the first half of launch_attend; uidx / umask / ucount as its union stage
+constexpr int ATT_SPLIT_ROWS = 256;
 hipError_t launch_union_logits(const Geom& g, int k_dtype, const void* k_rows, const uint16_t* q,
                                const int32_t* idx, int k, float scale, int32_t* uidx,
-                               uint8_t* umask, int32_t* ucount, float* logits, hipStream_t st);
+                               uint8_t* umask, int32_t* ucount, float* e, float* stats,
+                               hipStream_t st);
 
 // ---- value-side depths (values.hip) ----
 // code the value rows of tokens [n0, n0 + n_new) of sequence seq

@@ -6,21 +6,22 @@
 //   the row maximum by a DPP reduction inside the 16 lanes, then lane c writes
 //   byte c (its 8 channels) of each of the row's four planes.
 // Attention with value depths (launch_attend_v):
-// 1. the union of the heads' rows and the logits of every union row
+// 1. the union of the heads' rows, and per split of 256 union rows the
+//    softmax terms e_hr = exp(l_hr - m_sh) and the split's (m_sh, sum e)
 //    (attend.hip, launch_union_logits);
-// 2. vdepth_kernel, one workgroup per unit: each head's softmax over its rows
-//    (probabilities written back over the logits), importances
-//    a_r = sum_h p_hr^2, gains w_r = a_r s_r^2, and the depth search: the
-//    budget-th largest plane value w_r 4^-t found bit by bit over the fp32
-//    bit patterns, then the candidates equal to it handed out in (row, plane)
-//    order by a prefix count over the threads (thread t owns a contiguous run
-//    of rows);
+// 2. vdepth_kernel, one workgroup per unit: the splits' softmax statistics
+//    merged into one factor f_sh = exp(m_sh - M_h) / L_h per (split, head),
+//    so that p_hr = e_hr f_sh; importances a_r = sum_h p_hr^2, gains
+//    w_r = a_r s_r^2, and the depth search: the budget-th largest plane value
+//    w_r 4^-t found two bits a pass over the fp32 bit patterns, then the
+//    candidates equal to it handed out in (row, plane) order (a prefix count
+//    over the threads, only when there are more of them than needed);
 // 3. vaccum_kernel, one workgroup per (split of 256 union rows, unit), the
 //    row mapping of the exact attention (16 lanes per row, 8 channels a lane):
 //    the 16 lanes load the row's planes as 16 dwords (only the dwords of the
 //    first t planes), a lane permute hands lane c byte c of every plane, and
 //    the 8 channels are rebuilt as s (2^(3-t) - 8 + 8 b0 + 4 b1 + 2 b2 + b3)
-//    and accumulated with each head's probability;
+//    and accumulated with each head's probability e_hr f_sh;
 // 4. vsum_kernel: the splits' partial outputs added in split order.
 #include <float.h>
 
@@ -31,9 +32,10 @@ namespace bpk {
 namespace {
 
 constexpr int VENC_ROWS = 16;         // value rows per encode workgroup (4 per wavefront)
-constexpr int VD_THREADS = 1024;      // depth search: one workgroup per unit
-constexpr int VD_PER = BPK_MAX_SELECTED / VD_THREADS;  // rows a thread owns at most
-constexpr int VA_ROWS = 256;          // union rows per accumulation workgroup
+constexpr int VD_THREADS = 256;       // depth search: one workgroup per unit
+constexpr int VD_PER = BPK_MAX_SELECTED / VD_THREADS;  // rows a thread owns at most (32)
+constexpr int VD_SPLITS = BPK_MAX_SELECTED / ATT_SPLIT_ROWS;  // attention splits at most (32)
+constexpr int VA_ROWS = ATT_SPLIT_ROWS;  // union rows per accumulation workgroup (one split)
 constexpr int VA_THREADS = 256;
 constexpr int VREC = NP * D / 8;      // bytes of a token's four value planes (64)
 
@@ -107,10 +109,14 @@ struct VDepthArgs {
   long long ld;             // rows stride per unit
   const int32_t* count;     // [units] rows of each unit
   const int32_t* rows;      // [units][ld] token of each row
-  float* pw;                // attention: [units][G][ld] logits in, probabilities out
+  const float* e;           // attention: [units][G][ld] exp(l - split max)
+  const float* stats;       // attention: [units][nsplit][G][2] split max, exp-sum
+  float* fac;               // attention: [units][nsplit][G] exp(m_s - M) / L, written
+  int nsplit;
   const float* weights;     // given importances: [units][ld]
   const uint16_t* vscales;
   int budget;
+  float* scale_out;         // attention: [units][ld] each row's value scale, written
   uint8_t* depth;           // [units][ld]
   uint8_t* depth_copy;      // optional second copy of depth
   int32_t* rows_copy;       // optional copy of rows, -1 past the count
@@ -134,6 +140,27 @@ __device__ __forceinline__ int block_sum_i(int v, int* red) {
   return t;
 }
 
+// three sums over the workgroup at once (every thread gets them)
+__device__ __forceinline__ void block_sum3_i(int& x, int& y, int& z, int (*red)[3]) {
+  x = wave_sum_i(x);
+  y = wave_sum_i(y);
+  z = wave_sum_i(z);
+  __syncthreads();  // the previous use of red is over
+  if ((threadIdx.x & 63) == 0) {
+    red[threadIdx.x >> 6][0] = x;
+    red[threadIdx.x >> 6][1] = y;
+    red[threadIdx.x >> 6][2] = z;
+  }
+  __syncthreads();
+  x = y = z = 0;
+#pragma unroll
+  for (int w = 0; w < VD_THREADS / 64; ++w) {
+    x += red[w][0];
+    y += red[w][1];
+    z += red[w][2];
+  }
+}
+
 // exclusive prefix sum over the threads in thread order
 __device__ __forceinline__ int block_prefix_i(int v, int* red) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -151,170 +178,217 @@ __device__ __forceinline__ int block_prefix_i(int v, int* red) {
   return before + incl - v;
 }
 
-template <int G, bool MAX>
-__device__ __forceinline__ void block_reduce_g(float (&v)[G], float (*red)[G]) {
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      const float o = __shfl_xor(v[h], off);
-      v[h] = MAX ? fmaxf(v[h], o) : v[h] + o;
-    }
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0)
-#pragma unroll
-    for (int h = 0; h < G; ++h) red[threadIdx.x >> 6][h] = v[h];
-  __syncthreads();
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float t = red[0][h];
-    for (int w = 1; w < VD_THREADS / 64; ++w) t = MAX ? fmaxf(t, red[w][h]) : t + red[w][h];
-    v[h] = t;
-  }
-}
-
-// GIVEN: importances from a.weights (G unused); otherwise from the softmax of
-// the logits in a.pw, which are replaced by the probabilities.
-template <int G, bool GIVEN>
+// One workgroup of VD_THREADS per unit; thread t owns rows r = VD_THREADS j + t
+// (j < PER), so every load of a row array is coalesced.  GIVEN: importances from a.weights (G unused);
+// otherwise p_hr = e_hr f_jh with f_jh = exp(m_jh - M_h) / L_h merged from
+// the splits' statistics, and a_r = sum_h p_hr^2.
+template <int G, int PER, bool GIVEN>
 __global__ __launch_bounds__(VD_THREADS) void vdepth_kernel(VDepthArgs a) {
   __shared__ int redi[VD_THREADS / 64];
-  __shared__ float redf[VD_THREADS / 64][G];
+  __shared__ int red3[VD_THREADS / 64][3];
+  __shared__ float fs[VD_SPLITS][G];
+  __shared__ float smax[VD_SPLITS][G], ssum[VD_SPLITS][G];
   const int tid = threadIdx.x, u = blockIdx.x;
   const long long gu = a.g.global_unit(u);
   const long long n = a.g.n[a.g.seq_of(u)];
   const long long ubase = (long long)u * a.ld;
   int count = a.count[u];
   count = count < 0 ? 0 : (count > a.ld ? (int)a.ld : count);
-  const int per = (count + VD_THREADS - 1) / VD_THREADS;  // <= VD_PER (ld <= 8192)
-  const int r0 = tid * per;
-  auto owned = [&](int i) { return i < per && r0 + i < count; };
 
-  float w[VD_PER];
-  if constexpr (GIVEN) {
-#pragma unroll
-    for (int i = 0; i < VD_PER; ++i) {
-      float x = 0.f;
-      if (owned(i)) {
-        const int t = a.rows[ubase + r0 + i];
-        const float wt = a.weights[ubase + r0 + i];
-        if (t >= 0 && t < n && wt > 0.f && wt <= FLT_MAX) {
-          const float s = half_bits_to_f32(a.vscales[gu * a.g.cap + t]);
-          x = wt * (s * s);
-        }
-      }
-      w[i] = x;
+  if constexpr (!GIVEN) {
+    const int ns = (count + ATT_SPLIT_ROWS - 1) / ATT_SPLIT_ROWS;  // splits holding rows
+    if (tid < ns * G) {
+      const float* st = a.stats + ((long long)u * a.nsplit * G + tid) * 2;
+      smax[tid / G][tid % G] = st[0];
+      ssum[tid / G][tid % G] = st[1];
     }
-  } else {
-    float mx[G], sm[G];
+    __syncthreads();
+    float M[G], Ls[G];
 #pragma unroll
-    for (int h = 0; h < G; ++h) mx[h] = -INFINITY;
+    for (int h = 0; h < G; ++h) {
+      M[h] = -INFINITY;
+      Ls[h] = 0.f;
+    }
+    for (int sp = 0; sp < ns; ++sp)
 #pragma unroll
-    for (int i = 0; i < VD_PER; ++i)
-      if (owned(i))
+      for (int h = 0; h < G; ++h) M[h] = fmaxf(M[h], smax[sp][h]);
+    for (int sp = 0; sp < ns; ++sp)
 #pragma unroll
-        for (int h = 0; h < G; ++h) mx[h] = fmaxf(mx[h], a.pw[(ubase * G) + h * a.ld + r0 + i]);
-    block_reduce_g<G, true>(mx, redf);
+      for (int h = 0; h < G; ++h) {
+        const float m = smax[sp][h];
+        if (m != -INFINITY) Ls[h] = fmaf(ssum[sp][h], expf(m - M[h]), Ls[h]);
+      }
+    if (tid < ns)
 #pragma unroll
-    for (int h = 0; h < G; ++h) sm[h] = 0.f;
+      for (int h = 0; h < G; ++h) {
+        const float m = smax[tid][h];
+        const float f = (m == -INFINITY || !(Ls[h] > 0.f)) ? 0.f : expf(m - M[h]) / Ls[h];
+        fs[tid][h] = f;
+        a.fac[((long long)u * a.nsplit + tid) * G + h] = f;
+      }
+    __syncthreads();
+  }
+
+  // gains of the owned rows.  The loads go in two batches (the tokens, then
+  // the scales and softmax terms) with no branch around them: a row index
+  // past the count reads row 0 and a token outside [0, n) reads token 0,
+  // both masked afterwards.
+  float w[PER];
+  int tok[PER];
+  float wgt[GIVEN ? PER : 1];
 #pragma unroll
-    for (int i = 0; i < VD_PER; ++i)
-      if (owned(i))
+  for (int j = 0; j < PER; ++j) {
+    const int r = j * VD_THREADS + tid;
+    const long long rr = ubase + (r < count ? r : 0);
+    tok[j] = a.rows[rr];
+    if constexpr (GIVEN) wgt[j] = a.weights[rr];
+  }
+  constexpr int JB = PER < 8 ? PER : (G > 4 ? 4 : 8);  // rows per batch of the second loads
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const float lg = a.pw[(ubase * G) + h * a.ld + r0 + i];
-          if (lg != -INFINITY) sm[h] += expf(lg - mx[h]);
-        }
-    block_reduce_g<G, false>(sm, redf);
+  for (int j0 = 0; j0 < PER; j0 += JB) {
+    uint32_t sbits[JB];
+    float ev[GIVEN ? 1 : JB][G];
 #pragma unroll
-    for (int i = 0; i < VD_PER; ++i) {
-      float x = 0.f;
-      if (owned(i)) {
+    for (int jj = 0; jj < JB; ++jj) {
+      const int j = j0 + jj;
+      const int r = j * VD_THREADS + tid;
+      const int t = tok[j];
+      const bool tok_ok = t >= 0 && t < n;
+      sbits[jj] = a.vscales[gu * a.g.cap + (tok_ok ? t : 0)];
+      if constexpr (!GIVEN)
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+          ev[jj][h] = a.e[((long long)u * G + h) * a.ld + (r < count ? r : 0)];
+    }
+#pragma unroll
+    for (int jj = 0; jj < JB; ++jj) {
+      const int j = j0 + jj;
+      const int r = j * VD_THREADS + tid;
+      const bool in = r < count;
+      const float s = half_bits_to_f32((uint16_t)sbits[jj]);
+      if constexpr (GIVEN) {
+        const int t = tok[j];
+        const float wt = wgt[j];
+        const bool ok = in && t >= 0 && t < n && wt > 0.f && wt <= FLT_MAX;
+        w[j] = ok ? wt * (s * s) : 0.f;
+      } else {
         float acc = 0.f;
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-          float* pp = a.pw + (ubase * G) + h * a.ld + r0 + i;
-          const float lg = *pp;
-          // a finite logit implies mx[h] finite and sm[h] >= 1
-          const float p = lg == -INFINITY ? 0.f : expf(lg - mx[h]) / sm[h];
-          *pp = p;
+          const float p = ev[jj][h] * fs[r / ATT_SPLIT_ROWS][h];
           acc = fmaf(p, p, acc);
         }
-        const int t = a.rows[ubase + r0 + i];
-        const float s = half_bits_to_f32(a.vscales[gu * a.g.cap + t]);
-        x = acc * (s * s);
+        w[j] = in ? acc * (s * s) : 0.f;
+        if (in) a.scale_out[ubase + r] = s;
       }
-      w[i] = x;
     }
   }
 
-  // bit patterns of the plane values w 4^-t (0: no positive gain)
+  // plane values w 4^-t as fp32 bit patterns (0: no positive gain)
+  // (kept in registers for up to 8 rows a thread, recomputed beyond)
   constexpr float quarter[NP] = {1.f, 0.25f, 0.0625f, 0.015625f};
-  uint32_t kb[VD_PER][NP];
+  constexpr bool KEEP = PER <= 8;
+  uint32_t kb[KEEP ? PER : 1][NP];
+  auto make = [&](int j, int t) {
+    const float v = w[j] * quarter[t];
+    return v > 0.f ? __float_as_uint(v) : 0u;
+  };
+  if constexpr (KEEP)
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+#pragma unroll
+      for (int t = 0; t < NP; ++t) kb[j][t] = make(j, t);
+  auto key = [&](int j, int t) {
+    if constexpr (KEEP) return kb[j][t];
+    else return make(j, t);
+  };
   int npos = 0;
 #pragma unroll
-  for (int i = 0; i < VD_PER; ++i)
+  for (int j = 0; j < PER; ++j)
 #pragma unroll
-    for (int t = 0; t < NP; ++t) {
-      const float v = w[i] * quarter[t];
-      kb[i][t] = v > 0.f ? __float_as_uint(v) : 0u;
-      npos += kb[i][t] != 0u;
-    }
+    for (int t = 0; t < NP; ++t) npos += key(j, t) != 0u;
   const int total = block_sum_i(npos, redi);
   // every candidate above T is taken, and the first `need` equal to T in
   // (row, plane) order; T = 0 (every positive candidate) when the budget
-  // covers them all
+  // covers them all, ~0 (nothing) for a zero budget
   uint32_t T = 0;
   int need = 0;
   if (a.budget == 0) {
     T = 0xFFFFFFFFu;
   } else if (total > a.budget) {
-    for (int bit = 30; bit >= 0; --bit) {  // positive floats: bit 31 clear
-      const uint32_t c = T | (1u << bit);
+    // the largest T with at least `budget` candidates >= T, bit 30 first,
+    // then two bits a pass (positive floats: bit 31 clear)
+    {
       int cnt = 0;
 #pragma unroll
-      for (int i = 0; i < VD_PER; ++i)
+      for (int j = 0; j < PER; ++j)
 #pragma unroll
-        for (int t = 0; t < NP; ++t) cnt += kb[i][t] >= c;
-      if (block_sum_i(cnt, redi) >= a.budget) T = c;
+        for (int t = 0; t < NP; ++t) cnt += key(j, t) >= (1u << 30);
+      if (block_sum_i(cnt, redi) >= a.budget) T = 1u << 30;
+    }
+    for (int lo = 28; lo >= 0; lo -= 2) {
+      const uint32_t t1 = T | (1u << lo), t2 = T | (2u << lo), t3 = T | (3u << lo);
+      int c1 = 0, c2 = 0, c3 = 0;
+#pragma unroll
+      for (int j = 0; j < PER; ++j)
+#pragma unroll
+        for (int t = 0; t < NP; ++t) {
+          const uint32_t x = key(j, t);
+          c1 += x >= t1;
+          c2 += x >= t2;
+          c3 += x >= t3;
+        }
+      block_sum3_i(c1, c2, c3, red3);
+      T = c3 >= a.budget ? t3 : c2 >= a.budget ? t2 : c1 >= a.budget ? t1 : T;
     }
     int above = 0;
 #pragma unroll
-    for (int i = 0; i < VD_PER; ++i)
+    for (int j = 0; j < PER; ++j)
 #pragma unroll
-      for (int t = 0; t < NP; ++t) above += kb[i][t] > T;
+      for (int t = 0; t < NP; ++t) above += key(j, t) > T;
     need = a.budget - block_sum_i(above, redi);
   }
-  int eq = 0;
-  if (T != 0u && T != 0xFFFFFFFFu)
+  const bool partial = T != 0u && T != 0xFFFFFFFFu;
+  int eq_all = 0;
+  if (partial)
 #pragma unroll
-    for (int i = 0; i < VD_PER; ++i)
+    for (int j = 0; j < PER; ++j)
 #pragma unroll
-      for (int t = 0; t < NP; ++t) eq += kb[i][t] == T;
-  int before = block_prefix_i(eq, redi);
+      for (int t = 0; t < NP; ++t) eq_all += key(j, t) == T;
+  // with more candidates equal to T than needed (an exact tie), rank them in
+  // (row, plane) order: chunk j, then thread, then plane
+  const bool ranked = partial && block_sum_i(eq_all, redi) > need;
+  int base = 0;
 #pragma unroll
-  for (int i = 0; i < VD_PER; ++i) {
-    if (!owned(i)) continue;
+  for (int j = 0; j < PER; ++j) {
+    const int r = j * VD_THREADS + tid;
     int d = 0;
+    if (ranked) {
+      int eq = 0;
 #pragma unroll
-    for (int t = 0; t < NP; ++t) {
-      const uint32_t x = kb[i][t];
-      if (T == 0xFFFFFFFFu) break;
-      if (x > T) {
-        ++d;
-      } else if (T != 0u && x == T) {
-        d += before < need;
-        ++before;
+      for (int t = 0; t < NP; ++t) eq += key(j, t) == T;
+      int rank = base + block_prefix_i(eq, redi);
+      base += block_sum_i(eq, redi);
+#pragma unroll
+      for (int t = 0; t < NP; ++t) {
+        const uint32_t x = key(j, t);
+        if (x > T) {
+          ++d;
+        } else if (x == T) {
+          d += rank < need;
+          ++rank;
+        }
       }
+    } else if (T != 0xFFFFFFFFu) {
+#pragma unroll
+      for (int t = 0; t < NP; ++t) d += key(j, t) > T || (partial && key(j, t) == T);
     }
-    a.depth[ubase + r0 + i] = (uint8_t)d;
-    if (a.depth_copy) a.depth_copy[ubase + r0 + i] = (uint8_t)d;
-  }
-  for (long long r = tid; r < a.ld; r += VD_THREADS) {
-    if (r >= count) {
-      a.depth[ubase + r] = 0;
-      if (a.depth_copy) a.depth_copy[ubase + r] = 0;
+    if (r < a.ld) {
+      const uint8_t dv = r < count ? (uint8_t)d : (uint8_t)0;
+      a.depth[ubase + r] = dv;
+      if (a.depth_copy) a.depth_copy[ubase + r] = dv;
+      if (a.rows_copy) a.rows_copy[ubase + r] = r < count ? a.rows[ubase + r] : -1;
     }
-    if (a.rows_copy) a.rows_copy[ubase + r] = r < count ? a.rows[ubase + r] : -1;
   }
 }
 
@@ -325,7 +399,9 @@ struct VAccArgs {
   long long ld;  // G * k
   const int32_t* uidx;
   const int32_t* ucount;
-  const float* pw;       // [units][G][ld] probabilities
+  const float* e;        // [units][G][ld] exp(l - split max)
+  const float* fac;      // [units][nsplit][G]
+  const float* scale;    // [units][ld] value scale of each row
   const uint8_t* depth;  // [units][ld]
   const uint8_t* vplanes;
   const uint16_t* vscales;
@@ -347,6 +423,7 @@ __global__ __launch_bounds__(VA_THREADS) void vaccum_kernel(VAccArgs a) {
   constexpr int IT = RPW / 4;                        // 4 rows per wavefront step
   __shared__ int32_t rows[VA_ROWS];
   __shared__ int deps[VA_ROWS];
+  __shared__ float scl[VA_ROWS];
   __shared__ float pr[VA_ROWS][G];
   __shared__ float oacc[VA_THREADS / 16][G][D];
   const int tid = threadIdx.x;
@@ -362,29 +439,36 @@ __global__ __launch_bounds__(VA_THREADS) void vaccum_kernel(VAccArgs a) {
     return;
   }
   {
-    int row = 0, dep = 0;  // rows past nr: depth 0, nothing read
-    if (tid < nr) {
-      row = a.uidx[(long long)u * a.ld + r0 + tid];
-      dep = a.depth[(long long)u * a.ld + r0 + tid];
-    }
-    rows[tid] = row;
-    deps[tid] = dep;
+    // rows past nr: depth 0, weight 0 (their loads read row r0, masked)
+    const bool in = tid < nr;
+    const long long rr = (long long)u * a.ld + r0 + (in ? tid : 0);
+    const int row = a.uidx[rr];
+    const int dep = a.depth[rr];
+    const float sc = a.scale[rr];
+    rows[tid] = in ? row : 0;
+    deps[tid] = in ? dep : 0;
+    scl[tid] = in ? sc : 0.f;
+    const float* f = a.fac + ((long long)u * a.nsplit + split) * G;
+    float ev[G], fv[G];
 #pragma unroll
-    for (int h = 0; h < G; ++h)
-      pr[tid][h] = tid < nr ? a.pw[((long long)u * G + h) * a.ld + r0 + tid] : 0.f;
+    for (int h = 0; h < G; ++h) {
+      ev[h] = a.e[((long long)u * G + h) * a.ld + r0 + (in ? tid : 0)];
+      fv[h] = f[h];
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) pr[tid][h] = in ? ev[h] * fv[h] : 0.f;
   }
   __syncthreads();
   // lane c of a row group loads dword c of the row's planes (plane c / 4)
   // when that plane is read; every load is issued before the arithmetic
   uint32_t dw[IT];
-  float sc[IT];
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
     const int r = RPW * wave + 4 * it + rs;
     const int t = deps[r];
     const long long rec = gu * a.g.cap + rows[r];
-    dw[it] = (ch >> 2) < t ? reinterpret_cast<const uint32_t*>(a.vplanes + rec * VREC)[ch] : 0u;
-    sc[it] = t > 0 ? half_bits_to_f32(a.vscales[rec]) : 0.f;
+    dw[it] = 0u;
+    if ((ch >> 2) < t) dw[it] = reinterpret_cast<const uint32_t*>(a.vplanes + rec * VREC)[ch];
   }
   float o[G][8];
 #pragma unroll
@@ -401,7 +485,7 @@ __global__ __launch_bounds__(VA_THREADS) void vaccum_kernel(VAccArgs a) {
       const uint32_t x = (uint32_t)__shfl((int)dw[it], (lane & ~15) + 4 * p + (ch >> 2));
       code |= spread4((x >> (8 * (ch & 3))) & 0xFFu) << (NP - 1 - p);
     }
-    const float s = sc[it];
+    const float s = scl[r];
     const int t = deps[r];
     const float off = s * (t == 0 ? 0.f : ldexpf(1.f, 3 - t) - 8.f);  // s (2^(3-t) - 8), exact
     float vf[8];
@@ -436,7 +520,7 @@ __global__ __launch_bounds__(G * D) void vsum_kernel(const float* part, int nspl
 }
 
 struct VWs {
-  size_t uidx, umask, ucount, pw, vdep, part, total;
+  size_t uidx, umask, ucount, e, stats, fac, scale, vdep, part, total;
   int nsplit;
 };
 
@@ -449,17 +533,33 @@ VWs vws_layout(const Geom& g, int k) {
   w.uidx = off;   off += align256(units * sel * sizeof(int32_t));
   w.umask = off;  off += align256(units * sel);
   w.ucount = off; off += align256(units * sizeof(int32_t));
-  w.pw = off;     off += align256(units * g.G * sel * sizeof(float));
+  w.e = off;      off += align256(units * g.G * sel * sizeof(float));
+  w.stats = off;  off += align256(units * (size_t)w.nsplit * g.G * 2 * sizeof(float));
+  w.fac = off;    off += align256(units * (size_t)w.nsplit * g.G * sizeof(float));
+  w.scale = off;  off += align256(units * sel * sizeof(float));
   w.vdep = off;   off += align256(units * sel);
   w.part = off;   off += align256(units * (size_t)w.nsplit * g.G * D * sizeof(float));
   w.total = off;
   return w;
 }
 
+// rows per depth-search thread for a row stride of ld
+inline int vd_per(long long ld) { return ld <= 2 * VD_THREADS ? 2 : ld <= 8 * VD_THREADS ? 8 : VD_PER; }
+
+template <int G, bool GIVEN>
+void launch_vdepth(const VDepthArgs& da, hipStream_t st) {
+  const int units = da.g.units();
+  switch (vd_per(da.ld)) {
+    case 2: vdepth_kernel<G, 2, GIVEN><<<units, VD_THREADS, 0, st>>>(da); break;
+    case 8: vdepth_kernel<G, 8, GIVEN><<<units, VD_THREADS, 0, st>>>(da); break;
+    default: vdepth_kernel<G, VD_PER, GIVEN><<<units, VD_THREADS, 0, st>>>(da); break;
+  }
+}
+
 template <int G>
 void launch_v_g(const VDepthArgs& da, const VAccArgs& va, float* out, hipStream_t st) {
   const int units = da.g.units();
-  vdepth_kernel<G, false><<<units, VD_THREADS, 0, st>>>(da);
+  launch_vdepth<G, false>(da, st);
   vaccum_kernel<G><<<dim3((unsigned)va.nsplit, (unsigned)units), VA_THREADS, 0, st>>>(va);
   vsum_kernel<G><<<units, G * D, 0, st>>>(va.part, va.nsplit, out);
 }
@@ -487,15 +587,20 @@ hipError_t launch_attend_v(const Geom& g, int k_dtype, const void* k_rows, const
   int32_t* uidx = reinterpret_cast<int32_t*>(base + w.uidx);
   uint8_t* umask = reinterpret_cast<uint8_t*>(base + w.umask);
   int32_t* ucount = reinterpret_cast<int32_t*>(base + w.ucount);
-  float* pw = reinterpret_cast<float*>(base + w.pw);
+  float* ev = reinterpret_cast<float*>(base + w.e);
+  float* stats = reinterpret_cast<float*>(base + w.stats);
+  float* fac = reinterpret_cast<float*>(base + w.fac);
   uint8_t* vdep = reinterpret_cast<uint8_t*>(base + w.vdep);
   float* part = reinterpret_cast<float*>(base + w.part);
-  hipError_t e =
-      launch_union_logits(g, k_dtype, k_rows, q, idx, k, scale, uidx, umask, ucount, pw, st);
+  hipError_t e = launch_union_logits(g, k_dtype, k_rows, q, idx, k, scale, uidx, umask, ucount,
+                                     ev, stats, st);
   if (e != hipSuccess) return e;
   const long long sel = (long long)g.G * k;
-  VDepthArgs da{g, sel, ucount, uidx, pw, nullptr, vscales, v_budget, vdep, vdepth_out, union_out};
-  VAccArgs va{g, sel, uidx, ucount, pw, vdep, vplanes, vscales, part, w.nsplit};
+  float* vsc = reinterpret_cast<float*>(base + w.scale);
+  VDepthArgs da{g,       sel,      ucount,  uidx,     ev,   stats,      fac,
+                w.nsplit, nullptr, vscales, v_budget, vsc,  vdep,       vdepth_out,
+                union_out};
+  VAccArgs va{g, sel, uidx, ucount, ev, fac, vsc, vdep, vplanes, vscales, part, w.nsplit};
   switch (g.G) {
     case 1: launch_v_g<1>(da, va, out, st); break;
     case 2: launch_v_g<2>(da, va, out, st); break;
@@ -510,9 +615,10 @@ hipError_t launch_value_depth(const Geom& g, const int32_t* rows, const int32_t*
                               int row_ld, const float* weights, const uint16_t* vscales,
                               int v_budget, uint8_t* depth, hipStream_t st) {
   if (g.units() == 0) return hipSuccess;
-  VDepthArgs da{g, row_ld, n_rows, rows, nullptr, weights, vscales, v_budget, depth, nullptr,
+  VDepthArgs da{g,       row_ld,  n_rows,   rows,     nullptr, nullptr, nullptr,
+                0,       weights, vscales,  v_budget, nullptr, depth,   nullptr,
                 nullptr};
-  vdepth_kernel<1, true><<<g.units(), VD_THREADS, 0, st>>>(da);
+  launch_vdepth<1, true>(da, st);
   return hipGetLastError();
 }
 
