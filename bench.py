@@ -210,7 +210,7 @@ def main() -> int:
     t0 = time.perf_counter()
     log(f"building {cfg.name}: {cfg.description}")
     cache = workloads.build_cache(cfg, host_resident=args.host_resident,
-                                  values=not args.host_resident and not args.no_sweep)
+                                  values=not args.no_sweep)
     log(f"cache built in {time.perf_counter() - t0:.1f} s")
     q = workloads.queries(cfg)
     scale = workloads.softmax_scale(cfg)

@@ -16,7 +16,8 @@
 //    writes (max, sum, unnormalised output) per head.
 // 3. combine_kernel: log-sum-exp merge of the splits per (unit, head).
 // launch_union_logits runs 1 and 2 up to the split's softmax statistics for
-// the value-depth attention (values.hip).
+// the value-depth attention (values.hip), and fetches each union row's value
+// scale along with its key row.
 #include <limits.h>
 
 #include "bpk_internal.h"
@@ -202,6 +203,8 @@ struct AttArgs {
   int nsplit;
   float* e;       // LG launches: [unit][G][G * k] exp(logit - split max), by union position
   float* stats;   // LG launches: [unit][nsplit][G][2] split max and exp-sum
+  const uint16_t* vscales;  // LG launches: the cache's value scales
+  float* vsc;               // LG launches: [unit][G * k] each union row's value scale
 };
 
 // sum over the 16 lanes of a DPP row (every lane of the row gets it; the
@@ -251,6 +254,9 @@ __global__ __launch_bounds__(ATT_THREADS) void attend_kernel(AttArgs a) {
       mask = a.umask[(long long)u * sel + r0 + tid];
     }
     rows[tid] = row;
+    if (LG && tid < nr)  // the row's value scale, fetched with its key row
+      a.vsc[(long long)u * sel + r0 + tid] =
+          (float)__builtin_bit_cast(_Float16, a.vscales[gu * a.g.cap + row]);
     masks[tid] = mask;
   }
   // the lane's 8 channels of each query head
@@ -474,19 +480,20 @@ hipError_t launch_attend(const Geom& g, int k_dtype, const void* k_rows, const u
   UnionArgs ua{g, idx, k, uidx, umask, ucount};
   union_kernel<<<g.units(), UNION_THREADS, 0, st>>>(ua);
   AttArgs aa{g, k_rows, v_rows, q, k, scale, uidx, umask, ucount, part, w.nsplit, nullptr,
-             nullptr};
+             nullptr, nullptr, nullptr};
   return launch_att(aa, k_dtype, out, st);
 }
 
 hipError_t launch_union_logits(const Geom& g, int k_dtype, const void* k_rows, const uint16_t* q,
                                const int32_t* idx, int k, float scale, int32_t* uidx,
                                uint8_t* umask, int32_t* ucount, float* e, float* stats,
-                               hipStream_t st) {
+                               const uint16_t* vscales, float* vsc, hipStream_t st) {
   if (g.units() == 0) return hipSuccess;
   UnionArgs ua{g, idx, k, uidx, umask, ucount};
   union_kernel<<<g.units(), UNION_THREADS, 0, st>>>(ua);
   const int nsplit = (int)(((long long)g.G * k + ATT_ROWS - 1) / ATT_ROWS);
-  AttArgs aa{g, k_rows, nullptr, q, k, scale, uidx, umask, ucount, nullptr, nsplit, e, stats};
+  AttArgs aa{g, k_rows, nullptr, q, k, scale, uidx, umask, ucount, nullptr, nsplit, e, stats,
+             vscales, vsc};
   return launch_att(aa, k_dtype, nullptr, st);
 }
 

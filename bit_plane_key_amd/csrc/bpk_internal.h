@@ -153,10 +153,11 @@ hipError_t launch_attend(const Geom& g, int k_dtype, const void* k_rows, const u
 // not select row r) and the split's (m_h, sum_r e_hr) ([unit][split][G][2]),
 // as the first half of launch_attend; uidx / umask / ucount as its union stage
 constexpr int ATT_SPLIT_ROWS = 256;
+// (and each union row's value scale, as fp32 [unit][G * k])
 hipError_t launch_union_logits(const Geom& g, int k_dtype, const void* k_rows, const uint16_t* q,
                                const int32_t* idx, int k, float scale, int32_t* uidx,
                                uint8_t* umask, int32_t* ucount, float* e, float* stats,
-                               hipStream_t st);
+                               const uint16_t* vscales, float* vsc, hipStream_t st);
 
 // ---- value-side depths (values.hip) ----
 // code the value rows of tokens [n0, n0 + n_new) of sequence seq

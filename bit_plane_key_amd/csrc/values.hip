@@ -10,7 +10,9 @@
 //    softmax terms e_hr = exp(l_hr - m_sh) and the split's (m_sh, sum e)
 //    (attend.hip, launch_union_logits);
 // 2. vdepth_kernel, one workgroup per unit: the splits' softmax statistics
-//    merged into one factor f_sh = exp(m_sh - M_h) / L_h per (split, head),
+//    merged into one factor f_sh = exp(m_sh - M_h) / L_h per (split, head)
+//    (the rows' value scales come from the key pass, which fetched them with
+//    the key rows),
 //    so that p_hr = e_hr f_sh; importances a_r = sum_h p_hr^2, gains
 //    w_r = a_r s_r^2, and the depth search: the budget-th largest plane value
 //    w_r 4^-t found two bits a pass over the fp32 bit patterns, then the
@@ -116,7 +118,7 @@ struct VDepthArgs {
   const float* weights;     // given importances: [units][ld]
   const uint16_t* vscales;
   int budget;
-  float* scale_out;         // attention: [units][ld] each row's value scale, written
+  const float* scale_in;    // attention: [units][ld] each row's value scale
   uint8_t* depth;           // [units][ld]
   uint8_t* depth_copy;      // optional second copy of depth
   int32_t* rows_copy;       // optional copy of rows, -1 past the count
@@ -229,20 +231,22 @@ __global__ __launch_bounds__(VD_THREADS) void vdepth_kernel(VDepthArgs a) {
     __syncthreads();
   }
 
-  // gains of the owned rows.  The loads go in two batches (the tokens, then
-  // the scales and softmax terms) with no branch around them: a row index
+  // gains of the owned rows.  Given importances: the tokens and weights,
+  // then the tokens' scales; in the attention, the softmax terms and the
+  // scales the key pass fetched.  No branch around the loads: a row index
   // past the count reads row 0 and a token outside [0, n) reads token 0,
   // both masked afterwards.
   float w[PER];
-  int tok[PER];
+  int tok[GIVEN ? PER : 1];
   float wgt[GIVEN ? PER : 1];
+  if constexpr (GIVEN)
 #pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const int r = j * VD_THREADS + tid;
-    const long long rr = ubase + (r < count ? r : 0);
-    tok[j] = a.rows[rr];
-    if constexpr (GIVEN) wgt[j] = a.weights[rr];
-  }
+    for (int j = 0; j < PER; ++j) {
+      const int r = j * VD_THREADS + tid;
+      const long long rr = ubase + (r < count ? r : 0);
+      tok[j] = a.rows[rr];
+      wgt[j] = a.weights[rr];
+    }
   constexpr int JB = PER < 8 ? PER : (G > 4 ? 4 : 8);  // rows per batch of the second loads
 #pragma unroll
   for (int j0 = 0; j0 < PER; j0 += JB) {
@@ -252,9 +256,13 @@ __global__ __launch_bounds__(VD_THREADS) void vdepth_kernel(VDepthArgs a) {
     for (int jj = 0; jj < JB; ++jj) {
       const int j = j0 + jj;
       const int r = j * VD_THREADS + tid;
-      const int t = tok[j];
-      const bool tok_ok = t >= 0 && t < n;
-      sbits[jj] = a.vscales[gu * a.g.cap + (tok_ok ? t : 0)];
+      if constexpr (GIVEN) {
+        const int t = tok[j];
+        const bool tok_ok = t >= 0 && t < n;
+        sbits[jj] = a.vscales[gu * a.g.cap + (tok_ok ? t : 0)];
+      } else {
+        sbits[jj] = __float_as_uint(a.scale_in[ubase + (r < count ? r : 0)]);
+      }
       if constexpr (!GIVEN)
 #pragma unroll
         for (int h = 0; h < G; ++h)
@@ -265,7 +273,7 @@ __global__ __launch_bounds__(VD_THREADS) void vdepth_kernel(VDepthArgs a) {
       const int j = j0 + jj;
       const int r = j * VD_THREADS + tid;
       const bool in = r < count;
-      const float s = half_bits_to_f32((uint16_t)sbits[jj]);
+      const float s = GIVEN ? half_bits_to_f32((uint16_t)sbits[jj]) : __uint_as_float(sbits[jj]);
       if constexpr (GIVEN) {
         const int t = tok[j];
         const float wt = wgt[j];
@@ -279,7 +287,6 @@ __global__ __launch_bounds__(VD_THREADS) void vdepth_kernel(VDepthArgs a) {
           acc = fmaf(p, p, acc);
         }
         w[j] = in ? acc * (s * s) : 0.f;
-        if (in) a.scale_out[ubase + r] = s;
       }
     }
   }
@@ -592,11 +599,11 @@ hipError_t launch_attend_v(const Geom& g, int k_dtype, const void* k_rows, const
   float* fac = reinterpret_cast<float*>(base + w.fac);
   uint8_t* vdep = reinterpret_cast<uint8_t*>(base + w.vdep);
   float* part = reinterpret_cast<float*>(base + w.part);
+  float* vsc = reinterpret_cast<float*>(base + w.scale);
   hipError_t e = launch_union_logits(g, k_dtype, k_rows, q, idx, k, scale, uidx, umask, ucount,
-                                     ev, stats, st);
+                                     ev, stats, vscales, vsc, st);
   if (e != hipSuccess) return e;
   const long long sel = (long long)g.G * k;
-  float* vsc = reinterpret_cast<float*>(base + w.scale);
   VDepthArgs da{g,       sel,      ucount,  uidx,     ev,   stats,      fac,
                 w.nsplit, nullptr, vscales, v_budget, vsc,  vdep,       vdepth_out,
                 union_out};
