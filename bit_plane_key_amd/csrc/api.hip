@@ -170,7 +170,7 @@ DecodeWs decode_ws(const bpk::Geom& g, int k, bool values = false) {
   w.idx = off;     off += align256(uh * (size_t)k * sizeof(int32_t));
   w.attend = off;
   off += align256(values ? bpk::attend_v_ws_bytes(g, k) : bpk::attend_ws_bytes(g, k));
-  w.sample = off;  off += align256(uh * (size_t)w.sample_ld * sizeof(float));
+  w.sample = off;  off += align256(uh * (size_t)w.sample_ld * sizeof(uint16_t));
   w.thresh = off;  off += align256(uh * sizeof(uint32_t));
   w.count = off;   off += align256(uh * (size_t)w.regions * bpk::CAND_PARTS * sizeof(int32_t));
   w.cval = off;    off += align256(slots * sizeof(float));
@@ -410,7 +410,7 @@ int bpk_sparse_attend_v(const bpk_cache_t* c, const uint16_t* q, const int32_t* 
     return fail(BPK_EWORKSPACE, "workspace of %zu bytes < %zu needed", ws_bytes, need);
   return hip_status(bpk::launch_attend_v(g, c->k_dtype, c->k_rows, c->v_planes, c->v_scales, q,
                                          idx, k, softmax_scale, v_budget, out, union_out,
-                                         v_depth_out, ws, static_cast<hipStream_t>(stream)),
+                                         v_depth_out, ws, false, static_cast<hipStream_t>(stream)),
                     "sparse_attend_v");
 }
 
@@ -446,11 +446,16 @@ int decode_step_impl(const bpk_cache_t* c, const bpk::Geom& g, const uint16_t* q
                     "decode_step/alloc");
   }
   if (rc) return rc;
+  const bool values = v_budget >= 0;
+  char* att_ws = base + w.attend;
+  // the union arrays of the attention workspace
+  const bpk::UnionBufs ub = bpk::union_bufs(g, k, att_ws);
+  bool union_ready = false;  // the selection merged every unflagged unit's lists
   if (k <= bpk::FUSED_MAX_K) {
     // sampled threshold -> scan keeping candidates -> exact top-k among them;
     // flagged units (too few candidates, or too many) are redone unfused
     bpk::CandBufs cb;
-    cb.sample = reinterpret_cast<float*>(base + w.sample);
+    cb.sample = reinterpret_cast<uint16_t*>(base + w.sample);
     cb.sample_ld = w.sample_ld;
     cb.thresh = reinterpret_cast<uint32_t*>(base + w.thresh);
     cb.wg_blocks = bpk::scan_wg_blocks(g);
@@ -481,7 +486,8 @@ int decode_step_impl(const bpk_cache_t* c, const bpk::Geom& g, const uint16_t* q
     if (rc) return rc;
     {
       auto t = timer(BPK_STAGE_SELECT);
-      rc = hip_status(bpk::launch_cand_select(g, k, cb, idx, st), "decode_step/select");
+      rc = hip_status(bpk::launch_cand_select(g, k, cb, idx, &ub, &union_ready, st),
+                      "decode_step/select");
     }
     if (rc) return rc;
     {
@@ -489,8 +495,9 @@ int decode_step_impl(const bpk_cache_t* c, const bpk::Geom& g, const uint16_t* q
       rc = hip_status(bpk::launch_scan_flagged(g, q_basis, depth, c->planes, c->scales, scores,
                                                cb.flag, rows, st),
                       "decode_step/fallback scan");
-      if (!rc)
-        rc = hip_status(bpk::launch_topk_flagged(g, scores, k, idx, cb.flag, st),
+      if (!rc)  // (and the flagged units' union when the selection merged the others')
+        rc = hip_status(bpk::launch_topk_flagged(g, scores, k, idx, cb.flag,
+                                                 union_ready ? &ub : nullptr, st),
                         "decode_step/fallback select");
     }
     if (rc) return rc;
@@ -508,13 +515,17 @@ int decode_step_impl(const bpk_cache_t* c, const bpk::Geom& g, const uint16_t* q
     if (rc) return rc;
   }
   auto t = timer(BPK_STAGE_ATTEND);
-  if (v_budget >= 0)
+  if (values)
     return hip_status(bpk::launch_attend_v(g, c->k_dtype, c->k_rows, c->v_planes, c->v_scales, q,
                                            idx, k, softmax_scale, v_budget, out, union_out,
-                                           vdepth_out, base + w.attend, st),
+                                           vdepth_out, att_ws, union_ready, st),
                       "decode_step/attend_v");
+  if (union_ready)
+    return hip_status(bpk::launch_attend_rows(g, c->k_dtype, c->k_rows, c->v_rows, q, k,
+                                              softmax_scale, out, att_ws, st),
+                      "decode_step/attend");
   return hip_status(bpk::launch_attend(g, c->k_dtype, c->k_rows, c->v_rows, q, idx, k,
-                                       softmax_scale, out, base + w.attend, st),
+                                       softmax_scale, out, att_ws, st),
                     "decode_step/attend");
 }
 

@@ -2,11 +2,13 @@
 // of its query heads' winners (Fathom §1: at most G*k rows per KV head;
 // Fathom §2: each head's output is softmax attention over its own set).
 //
-// 1. union_kernel (one workgroup per unit): the G index lists, as
-//    (token << 3 | head) keys in LDS, are merged by rank when each is strictly
-//    ascending (as select_topk writes them) and sorted with a bitonic network
-//    otherwise; runs of equal tokens collapse to one union row carrying a
-//    G-bit head mask.
+// 1. union_kernel (one workgroup per unit, union_of_lists): the G index
+//    lists, as (token << 3 | head) keys in LDS, are merged by rank when each
+//    is strictly ascending (as select_topk writes them) and sorted with a
+//    bitonic network otherwise; runs of equal tokens collapse to one union row
+//    carrying a G-bit head mask.  decode_step's selection workgroups merge
+//    their own unit's lists the same way, and launch_attend_rows starts here
+//    at 2.
 // 2. attend_kernel (one workgroup per (split of ATT_ROWS union rows, unit)):
 //    every K row of the split is read once, whole and coalesced (16 lanes of a
 //    wavefront per row, 16 bytes a lane, all of a wavefront's loads in flight
@@ -21,11 +23,11 @@
 #include <limits.h>
 
 #include "bpk_internal.h"
+#include "union_common.h"
 
 namespace bpk {
 namespace {
 
-constexpr int UNION_THREADS = 1024;
 constexpr int ATT_ROWS = ATT_SPLIT_ROWS;
 constexpr int ATT_THREADS = 256;
 
@@ -60,133 +62,10 @@ struct UnionArgs {
 };
 
 __global__ __launch_bounds__(UNION_THREADS) void union_kernel(UnionArgs a) {
-  __shared__ uint32_t keys[BPK_MAX_SELECTED];
-  __shared__ int scan[UNION_THREADS];
-  __shared__ uint32_t masks[BPK_MAX_SELECTED / 4];  // one byte per union row
-  const int tid = threadIdx.x;
   const int u = blockIdx.x;
-  const int G = a.g.G;
-  const int sel = G * a.k;
-  int m = 1;
-  while (m < sel) m <<= 1;
-  const int32_t* src = a.idx + (long long)u * sel;
-  const long long n = a.g.n[a.g.seq_of(u)];
-  for (int e = tid; e < m; e += UNION_THREADS) {
-    uint32_t key = 0xFFFFFFFFu;
-    if (e < sel) {
-      const int32_t t = src[e];
-      // entries outside [0, n) are padding (never a row read out of range)
-      if (t >= 0 && t < n) key = ((uint32_t)t << 3) | (uint32_t)(e / a.k);
-    }
-    keys[e] = key;
-  }
-  for (int e = tid; e < BPK_MAX_SELECTED / 4; e += UNION_THREADS) masks[e] = 0;
-  __syncthreads();
-  // select_topk's lists are strictly ascending with padding at the end: then
-  // the merged position of an entry is its index in its list plus the number
-  // of smaller keys in each other list (a binary search).  Any other input is
-  // sorted whole.
-  bool bad = false;
-  for (int e = tid; e < sel; e += UNION_THREADS) {
-    if ((e + 1) % a.k == 0) continue;
-    const uint32_t x = keys[e], y = keys[e + 1];
-    bad |= !(x < y || (x == 0xFFFFFFFFu && y == 0xFFFFFFFFu));
-  }
-  if (!__syncthreads_or(bad)) {
-    uint32_t mk[BPK_MAX_SELECTED / UNION_THREADS];
-    int pos[BPK_MAX_SELECTED / UNION_THREADS];
-    int nv = 0;  // valid entries over all lists
-    for (int h = 0; h < G; ++h) {
-      int lo = 0, hi = a.k;  // first padding entry of list h
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (keys[h * a.k + mid] != 0xFFFFFFFFu) lo = mid + 1;
-        else hi = mid;
-      }
-      nv += lo;
-    }
-    int c = 0;
-    for (int e = tid; e < sel; e += UNION_THREADS, ++c) {
-      const uint32_t x = keys[e];
-      mk[c] = x;
-      pos[c] = -1;
-      if (x == 0xFFFFFFFFu) continue;
-      const int h = e / a.k;
-      int p = e - h * a.k;
-      for (int b = 0; b < G; ++b) {
-        if (b == h) continue;
-        int lo = 0, hi = a.k;  // keys of list b below x
-        while (lo < hi) {
-          const int mid = (lo + hi) >> 1;
-          if (keys[b * a.k + mid] < x) lo = mid + 1;
-          else hi = mid;
-        }
-        p += lo;
-      }
-      pos[c] = p;
-    }
-    __syncthreads();
-    c = 0;
-    for (int e = tid; e < sel; e += UNION_THREADS, ++c)
-      if (pos[c] >= 0) keys[pos[c]] = mk[c];
-    for (int e = nv + tid; e < m; e += UNION_THREADS) keys[e] = 0xFFFFFFFFu;
-    __syncthreads();
-  } else {
-  for (int size = 2; size <= m; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = tid; i < m / 2; i += UNION_THREADS) {
-        const int lo = 2 * i - (i & (stride - 1));
-        const int hi = lo + stride;
-        const bool up = ((lo & size) == 0);
-        const uint32_t x = keys[lo], y = keys[hi];
-        if ((x > y) == up) {
-          keys[lo] = y;
-          keys[hi] = x;
-        }
-      }
-      __syncthreads();
-    }
-  }
-  }
-  // thread t owns a contiguous run of `per` sorted positions
-  const int per = (m + UNION_THREADS - 1) / UNION_THREADS;
-  const int e0 = tid * per;
-  int own = 0;
-  for (int e = e0; e < e0 + per && e < m; ++e) {
-    const uint32_t key = keys[e];
-    if (key != 0xFFFFFFFFu && (e == 0 || (keys[e - 1] >> 3) != (key >> 3))) ++own;
-  }
-  // exclusive prefix of `own` over the workgroup: a scan inside each
-  // wavefront, then the wavefronts' totals
-  const int lane = tid & 63, wv = tid >> 6;
-  int incl = own;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(incl, off);
-    if (lane >= off) incl += y;
-  }
-  if (lane == 63) scan[wv] = incl;
-  __syncthreads();
-  int before = 0, total = 0;
-  for (int x = 0; x < UNION_THREADS / 64; ++x) {
-    const int t = scan[x];
-    before += x < wv ? t : 0;
-    total += t;
-  }
-  int pos = before + incl - own - 1;  // union position of the current run
-  for (int e = e0; e < e0 + per && e < m; ++e) {
-    const uint32_t key = keys[e];
-    if (key == 0xFFFFFFFFu) break;
-    if (e == 0 || (keys[e - 1] >> 3) != (key >> 3)) {
-      ++pos;
-      a.uidx[(long long)u * sel + pos] = (int32_t)(key >> 3);
-    }
-    atomicOr(&masks[pos >> 2], (1u << (key & 7u)) << (8 * (pos & 3)));
-  }
-  __syncthreads();
-  for (int e = tid; e < total; e += UNION_THREADS)
-    a.umask[(long long)u * sel + e] = (uint8_t)(masks[e >> 2] >> (8 * (e & 3)));
-  if (tid == 0) a.ucount[u] = total;
+  const long long sel = (long long)a.g.G * a.k;
+  union_of_lists(a.idx + u * sel, a.g.G, a.k, a.g.n[a.g.seq_of(u)], a.uidx + u * sel,
+                 a.umask + u * sel, a.ucount + u);
 }
 
 struct AttArgs {
@@ -201,6 +80,7 @@ struct AttArgs {
   const int32_t* ucount;
   float* part;
   int nsplit;
+  float* out;  // [unit][G][D] (not LG)
   float* e;       // LG launches: [unit][G][G * k] exp(logit - split max), by union position
   float* stats;   // LG launches: [unit][nsplit][G][2] split max and exp-sum
   const uint16_t* vscales;  // LG launches: the cache's value scales
@@ -436,7 +316,7 @@ __global__ __launch_bounds__(G * D) void combine_kernel(const Geom g, const floa
 }
 
 template <int G>
-void launch_att_g(const AttArgs& a, int k_dtype, float* out, hipStream_t st) {
+void launch_att_g(const AttArgs& a, int k_dtype, hipStream_t st) {
   dim3 grid((unsigned)a.nsplit, (unsigned)a.g.units());
   if (a.e) {
     if (k_dtype == BPK_F32)
@@ -449,15 +329,15 @@ void launch_att_g(const AttArgs& a, int k_dtype, float* out, hipStream_t st) {
     attend_kernel<G, true, false><<<grid, ATT_THREADS, 0, st>>>(a);
   else
     attend_kernel<G, false, false><<<grid, ATT_THREADS, 0, st>>>(a);
-  combine_kernel<G><<<a.g.units(), G * D, 0, st>>>(a.g, a.part, a.nsplit, out);
+  combine_kernel<G><<<a.g.units(), G * D, 0, st>>>(a.g, a.part, a.nsplit, a.out);
 }
 
-hipError_t launch_att(const AttArgs& aa, int k_dtype, float* out, hipStream_t st) {
+hipError_t launch_att(const AttArgs& aa, int k_dtype, hipStream_t st) {
   switch (aa.g.G) {
-    case 1: launch_att_g<1>(aa, k_dtype, out, st); break;
-    case 2: launch_att_g<2>(aa, k_dtype, out, st); break;
-    case 4: launch_att_g<4>(aa, k_dtype, out, st); break;
-    case 8: launch_att_g<8>(aa, k_dtype, out, st); break;
+    case 1: launch_att_g<1>(aa, k_dtype, st); break;
+    case 2: launch_att_g<2>(aa, k_dtype, st); break;
+    case 4: launch_att_g<4>(aa, k_dtype, st); break;
+    case 8: launch_att_g<8>(aa, k_dtype, st); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -467,34 +347,55 @@ hipError_t launch_att(const AttArgs& aa, int k_dtype, float* out, hipStream_t st
 
 size_t attend_ws_bytes(const Geom& g, int k) { return ws_layout(g, k).total; }
 
+UnionBufs union_bufs(const Geom& g, int k, void* ws) {
+  const WsLayout w = ws_layout(g, k);
+  char* base = static_cast<char*>(ws);
+  return UnionBufs{reinterpret_cast<int32_t*>(base + w.uidx), reinterpret_cast<uint8_t*>(base + w.umask),
+                   reinterpret_cast<int32_t*>(base + w.ucount)};
+}
+
+hipError_t launch_union(const Geom& g, const int32_t* idx, int k, const UnionBufs& ub,
+                        hipStream_t st) {
+  if (g.units() == 0) return hipSuccess;
+  UnionArgs ua{g, idx, k, ub.uidx, ub.umask, ub.ucount};
+  union_kernel<<<g.units(), UNION_THREADS, 0, st>>>(ua);
+  return hipGetLastError();
+}
+
+hipError_t launch_attend_rows(const Geom& g, int k_dtype, const void* k_rows,
+                              const uint16_t* v_rows, const uint16_t* q, int k, float scale,
+                              float* out, void* ws, hipStream_t st) {
+  if (g.units() == 0) return hipSuccess;
+  const WsLayout w = ws_layout(g, k);
+  const UnionBufs ub = union_bufs(g, k, ws);
+  float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + w.part);
+  AttArgs aa{g,    k_rows,   v_rows, q,       k,       scale,   ub.uidx, ub.umask, ub.ucount,
+             part, w.nsplit, out,    nullptr, nullptr, nullptr, nullptr};
+  return launch_att(aa, k_dtype, st);
+}
+
 hipError_t launch_attend(const Geom& g, int k_dtype, const void* k_rows, const uint16_t* v_rows,
                          const uint16_t* q, const int32_t* idx, int k, float scale, float* out,
                          void* ws, hipStream_t st) {
-  if (g.units() == 0) return hipSuccess;
-  const WsLayout w = ws_layout(g, k);
-  char* base = static_cast<char*>(ws);
-  int32_t* uidx = reinterpret_cast<int32_t*>(base + w.uidx);
-  uint8_t* umask = reinterpret_cast<uint8_t*>(base + w.umask);
-  int32_t* ucount = reinterpret_cast<int32_t*>(base + w.ucount);
-  float* part = reinterpret_cast<float*>(base + w.part);
-  UnionArgs ua{g, idx, k, uidx, umask, ucount};
-  union_kernel<<<g.units(), UNION_THREADS, 0, st>>>(ua);
-  AttArgs aa{g, k_rows, v_rows, q, k, scale, uidx, umask, ucount, part, w.nsplit, nullptr,
-             nullptr, nullptr, nullptr};
-  return launch_att(aa, k_dtype, out, st);
+  hipError_t e = launch_union(g, idx, k, union_bufs(g, k, ws), st);
+  if (e != hipSuccess) return e;
+  return launch_attend_rows(g, k_dtype, k_rows, v_rows, q, k, scale, out, ws, st);
 }
 
 hipError_t launch_union_logits(const Geom& g, int k_dtype, const void* k_rows, const uint16_t* q,
                                const int32_t* idx, int k, float scale, int32_t* uidx,
                                uint8_t* umask, int32_t* ucount, float* e, float* stats,
-                               const uint16_t* vscales, float* vsc, hipStream_t st) {
+                               const uint16_t* vscales, float* vsc, bool union_ready,
+                               hipStream_t st) {
   if (g.units() == 0) return hipSuccess;
-  UnionArgs ua{g, idx, k, uidx, umask, ucount};
-  union_kernel<<<g.units(), UNION_THREADS, 0, st>>>(ua);
+  if (!union_ready) {
+    UnionArgs ua{g, idx, k, uidx, umask, ucount};
+    union_kernel<<<g.units(), UNION_THREADS, 0, st>>>(ua);
+  }
   const int nsplit = (int)(((long long)g.G * k + ATT_ROWS - 1) / ATT_ROWS);
-  AttArgs aa{g, k_rows, nullptr, q, k, scale, uidx, umask, ucount, nullptr, nsplit, e, stats,
-             vscales, vsc};
-  return launch_att(aa, k_dtype, nullptr, st);
+  AttArgs aa{g,       k_rows, nullptr, q, k,     scale,   uidx, umask, ucount,
+             nullptr, nsplit, nullptr, e, stats, vscales, vsc};
+  return launch_att(aa, k_dtype, st);
 }
 
 }  // namespace bpk

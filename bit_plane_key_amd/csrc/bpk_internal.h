@@ -88,7 +88,7 @@ constexpr int FUSED_MAX_K = 1024;    // larger k take the unfused path
 constexpr int SCAN_MIN_WG_BLOCKS = 16;
 
 struct CandBufs {
-  float* sample;        // [units][G][sample_ld] scores of the sampled blocks
+  uint16_t* sample;     // [units][G][sample_ld] upper halves of the sampled scores' order keys
   long long sample_ld;  // sample_groups * SAMPLE_GROUP * 64
   uint32_t* thresh;     // [units][G] order key of the threshold
   int wg_blocks;        // blocks per workgroup of the candidate scan
@@ -132,14 +132,31 @@ hipError_t launch_threshold(const Geom& g, int k, const CandBufs& cb, hipStream_
 hipError_t launch_scan_cand(const Geom& g, const float* q_basis, const uint8_t* depth,
                             const uint64_t* planes, const uint16_t* scales, int k,
                             const CandBufs& cb, int rows, hipStream_t st);
+// The union of a unit's G lists of k selected rows, written by union_kernel
+// (attend.hip) or merged by the selection's workgroup itself: uidx [unit][G k]
+// ascending rows, umask [unit][G k] the heads holding each row, ucount [unit].
+struct UnionBufs {
+  int32_t* uidx;
+  uint8_t* umask;
+  int32_t* ucount;
+};
+// the union arrays at the start of an attention workspace (launch_attend's
+// and the value-depth attention's begin alike)
+UnionBufs union_bufs(const Geom& g, int k, void* ws);
+// largest LDS of a selection workgroup that also merges its unit's lists
+constexpr size_t CAND_FUSED_LDS = 65536;
+// exact top-k among the candidates; with un, also the union of every
+// unflagged unit (when its lists and merge fit CAND_FUSED_LDS; the return's
+// *fused says whether they did)
 hipError_t launch_cand_select(const Geom& g, int k, const CandBufs& cb, int32_t* idx,
-                              hipStream_t st);
+                              const UnionBufs* un, bool* fused, hipStream_t st);
 // full scan and radix select of the flagged units only
 hipError_t launch_scan_flagged(const Geom& g, const float* q_basis, const uint8_t* depth,
                                const uint64_t* planes, const uint16_t* scales, float* scores,
                                const int32_t* flag, int rows, hipStream_t st);
+// (with un, also the union of each flagged unit's lists)
 hipError_t launch_topk_flagged(const Geom& g, const float* scores, int k, int32_t* idx,
-                               const int32_t* flag, hipStream_t st);
+                               const int32_t* flag, const UnionBufs* un, hipStream_t st);
 // the number of set flags among flag[0 .. units), into *count (device)
 hipError_t launch_count_flags(int units, const int32_t* flag, int32_t* count, hipStream_t st);
 
@@ -147,6 +164,13 @@ size_t attend_ws_bytes(const Geom& g, int k);
 hipError_t launch_attend(const Geom& g, int k_dtype, const void* k_rows, const uint16_t* v_rows,
                          const uint16_t* q, const int32_t* idx, int k, float scale, float* out,
                          void* ws, hipStream_t st);
+// the union stage alone, into ub
+hipError_t launch_union(const Geom& g, const int32_t* idx, int k, const UnionBufs& ub,
+                        hipStream_t st);
+// launch_attend after its union stage (the workspace already holds the union)
+hipError_t launch_attend_rows(const Geom& g, int k_dtype, const void* k_rows,
+                              const uint16_t* v_rows, const uint16_t* q, int k, float scale,
+                              float* out, void* ws, hipStream_t st);
 
 // union of the heads' selections and, per split of 256 union rows, the
 // softmax terms e_hr = exp(l_hr - m_h) ([unit][G][G * k], 0 where head h did
@@ -154,20 +178,23 @@ hipError_t launch_attend(const Geom& g, int k_dtype, const void* k_rows, const u
 // as the first half of launch_attend; uidx / umask / ucount as its union stage
 constexpr int ATT_SPLIT_ROWS = 256;
 // (and each union row's value scale, as fp32 [unit][G * k])
+// (union_ready: uidx / umask / ucount already hold the union, idx is not read)
 hipError_t launch_union_logits(const Geom& g, int k_dtype, const void* k_rows, const uint16_t* q,
                                const int32_t* idx, int k, float scale, int32_t* uidx,
                                uint8_t* umask, int32_t* ucount, float* e, float* stats,
-                               const uint16_t* vscales, float* vsc, hipStream_t st);
+                               const uint16_t* vscales, float* vsc, bool union_ready,
+                               hipStream_t st);
 
 // ---- value-side depths (values.hip) ----
 // code the value rows of tokens [n0, n0 + n_new) of sequence seq
 hipError_t launch_vencode(const Geom& g, int seq, const uint16_t* v_rows, uint8_t* vplanes,
                           uint16_t* vscales, long long n0, long long n_new, hipStream_t st);
 size_t attend_v_ws_bytes(const Geom& g, int k);
+// (union_ready: the workspace's union arrays already hold the union of idx)
 hipError_t launch_attend_v(const Geom& g, int k_dtype, const void* k_rows, const uint8_t* vplanes,
                            const uint16_t* vscales, const uint16_t* q, const int32_t* idx, int k,
                            float scale, int v_budget, float* out, int32_t* union_out,
-                           uint8_t* vdepth_out, void* ws, hipStream_t st);
+                           uint8_t* vdepth_out, void* ws, bool union_ready, hipStream_t st);
 hipError_t launch_value_depth(const Geom& g, const int32_t* rows, const int32_t* n_rows,
                               int row_ld, const float* weights, const uint16_t* vscales,
                               int v_budget, uint8_t* depth, hipStream_t st);

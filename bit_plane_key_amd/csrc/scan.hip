@@ -147,7 +147,8 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : (RM <= RM_SMALL ? 3 : 2)
     if constexpr (MODE == SCAN_FULL) {
       a.out[uh * a.out_ld + tok] = s;
     } else {
-      a.out[uh * a.out_ld + (long long)blockIdx.x * (SAMPLE_GROUP * BLK) + (tok - wb0 * BLK)] = s;
+      a.sample[uh * a.out_ld + (long long)blockIdx.x * (SAMPLE_GROUP * BLK) + (tok - wb0 * BLK)] =
+          (uint16_t)(order_key(s) >> 16);
     }
   };
   // (only where nothing is read) the workgroup's candidates fill each head's
@@ -858,7 +859,7 @@ hipError_t launch_scan_sample(const Geom& g, const float* q_basis, const uint8_t
                               const uint64_t* planes, const uint16_t* scales, const CandBufs& cb,
                               int rows, hipStream_t st) {
   ScanArgs a = base_args(g, q_basis, depth, planes, scales);
-  a.out = cb.sample;
+  a.sample = cb.sample;
   a.out_ld = cb.sample_ld;
   return dispatch<SCAN_SAMPLE>(a, rows, st);
 }

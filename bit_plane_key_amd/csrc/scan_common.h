@@ -30,7 +30,8 @@ static_assert(SAMPLE_GROUP % SCAN_GB == 0 && SAMPLE_STRIDE % SAMPLE_GROUP == 0, 
 // What a launch does with the scores it computes:
 // * SCAN_FULL writes every score ([unit][G][cap]);
 // * SCAN_SAMPLE scores only the first SAMPLE_GROUP blocks of every
-//   SAMPLE_STRIDE (one workgroup per sampled group) into [unit][G][sample_ld];
+//   SAMPLE_STRIDE (one workgroup per sampled group) and writes the upper 16
+//   bits of each score's order key into [unit][G][sample_ld];
 // * SCAN_CAND appends (score, token) of the tokens of [4, n - W) whose score
 //   is at or above the head's threshold to the workgroup's candidate region
 //   of that head (slots handed out by an LDS counter; the count, which may
@@ -43,8 +44,9 @@ struct ScanArgs {
   const uint8_t* __restrict__ depth;
   const uint64_t* __restrict__ planes;
   const uint16_t* __restrict__ scales;
-  float* __restrict__ out;          // scores (FULL) or sampled scores (SAMPLE)
-  long long out_ld;                 // per (unit, head) row length of out
+  float* __restrict__ out;          // scores (FULL)
+  uint16_t* __restrict__ sample;    // SAMPLE: upper halves of the sampled scores' order keys
+  long long out_ld;                 // per (unit, head) row length of out or sample
   int wg_blocks;                    // blocks per workgroup (multiple of SCAN_GB)
   int k;                            // top-k (CAND: units with n <= k are skipped)
   const int32_t* __restrict__ unit_flag;  // FULL: if set, only units with flag != 0

@@ -111,7 +111,8 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : 2) void scan_wide_kernel
     if constexpr (MODE == SCAN_FULL) {
       a.out[uh * a.out_ld + tok] = s;
     } else {
-      a.out[uh * a.out_ld + (long long)blockIdx.x * (SAMPLE_GROUP * BLK) + (tok - wb0 * BLK)] = s;
+      a.sample[uh * a.out_ld + (long long)blockIdx.x * (SAMPLE_GROUP * BLK) + (tok - wb0 * BLK)] =
+          (uint16_t)(order_key(s) >> 16);
     }
   };
   auto append = [&](long long tok, int h, float s) {  // CAND, lanes whose test passed

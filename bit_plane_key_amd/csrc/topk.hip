@@ -15,18 +15,27 @@
 //   samples over 16384 scores): per (unit, head), the r-th largest of the
 //   sampled scores of candidate tokens, with r chosen so that about
 //   2 (k - 4 - W) tokens of the whole range are expected at or above it (plus
-//   8 for the sampling noise of small r);
-// * cand_select_kernel: per (unit, head), one wavefront takes the exact top
-//   (k - 4 - W) of the candidates (every token at or above the threshold, and
-//   possibly a few just below it, so the k - 4 - W largest of the whole range
-//   are among them whenever at least that many are at or above it) by a
-//   bit-by-bit counting search over its register-resident keys, and sorts the
-//   winners by index.  A head with too few candidates at or above the
-//   threshold, or more than the buffers hold, flags its unit for the full scan
-//   and radix select.
+//   8 for the sampling noise of small r).  The sample holds the upper 16 bits
+//   of each score's order key, so the threshold is that score with its low
+//   16 key bits cleared: at most 2^-7 of it below the sampled score (never
+//   above), a few more candidates and never fewer;
+// * cand_select_kernel: one workgroup per unit; for each query head one
+//   wavefront takes the exact top (k - 4 - W) of the candidates (every token
+//   at or above the threshold, and possibly a few just below it, so the
+//   k - 4 - W largest of the whole range are among them whenever at least
+//   that many are at or above it) by a bit-by-bit counting search over its
+//   register-resident keys, and sorts the winners by index.  A head with too
+//   few candidates at or above the threshold, or more than the buffers hold,
+//   flags its unit for the full scan and radix select.  Otherwise the
+//   workgroup also merges the unit's G lists into the union of rows that the
+//   attention reads (the union stage of attend.hip, for the flagged units
+//   only, runs after their full selection).
 #include <limits.h>
 
+#include <type_traits>
+
 #include "bpk_internal.h"
+#include "union_common.h"
 
 namespace bpk {
 namespace {
@@ -145,11 +154,10 @@ __device__ void sort_and_write(int32_t* buf, int k, int32_t* out) {
   for (int i = tid; i < k; i += TK_THREADS) out[i] = buf[i];
 }
 
-__global__ __launch_bounds__(TK_THREADS) void topk_kernel(TopkArgs a) {
-  __shared__ TkSmem sm;
+// the top-k of query head h of unit u, by the TK_THREADS threads of a
+// workgroup (every thread calls it)
+__device__ __forceinline__ void topk_head(TkSmem& sm, const TopkArgs& a, int u, int h) {
   const int G = a.g.G;
-  const int u = blockIdx.x / G, h = blockIdx.x % G;
-  if (a.unit_flag && a.unit_flag[u] == 0) return;
   const long long n = a.g.n[a.g.seq_of(u)];
   const int k = a.k;
   const int tid = threadIdx.x;
@@ -194,6 +202,30 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(TopkArgs a) {
   }
   __syncthreads();
   sort_and_write(sm.buf, k, out);
+}
+
+__global__ __launch_bounds__(TK_THREADS) void topk_kernel(TopkArgs a) {
+  __shared__ TkSmem sm;
+  topk_head(sm, a, blockIdx.x / a.g.G, blockIdx.x % a.g.G);
+}
+
+// decode_step's fallback: one workgroup per unit whose flag is set takes the
+// top-k of its heads in turn and then, with un.uidx, the union of the lists
+// it wrote (union_of_lists; the workgroup's own global writes, ordered by
+// its barriers)
+__global__ __launch_bounds__(TK_THREADS) void topk_unit_kernel(TopkArgs a, UnionBufs un) {
+  __shared__ TkSmem sm;
+  const int u = blockIdx.x;
+  if (a.unit_flag[u] == 0) return;
+  const int G = a.g.G;
+  for (int h = 0; h < G; ++h) {
+    topk_head(sm, a, u, h);
+    __syncthreads();
+  }
+  if (!un.uidx) return;
+  const long long sel = (long long)G * a.k;
+  union_of_lists(a.idx + u * sel, G, a.k, a.g.n[a.g.seq_of(u)], un.uidx + u * sel,
+                 un.umask + u * sel, un.ucount + u);
 }
 
 // maximum over the wavefront: DPP inside each 16-lane row (quad_perm xor 1,
@@ -260,8 +292,8 @@ __global__ __launch_bounds__(TK_THREADS) void threshold_kernel(ThreshArgs a) {
     if (r > m) {
       tkey = 0;  // the sample is too small to cut anything: all are candidates
     } else {
-      const float* sc = a.cb.sample + uh * a.cb.sample_ld;
-      auto keyf = [&](long long i) { return order_key(sc[i]); };
+      const uint16_t* sc = a.cb.sample + uh * a.cb.sample_ld;
+      auto keyf = [&](long long i) { return (uint32_t)sc[i] << 16; };
       int t_eq, c_eq;
       tkey = radix_select(sm, 0, ngr * glen, (int)r, keyf, valid, &t_eq, &c_eq);
     }
@@ -317,21 +349,26 @@ __global__ __launch_bounds__(TH_THREADS) void threshold_reg_kernel(ThreshArgs a)
     } else {
       // sample position i = (group gi, offset j) holds token gi * SAMPLE_STRIDE * 64 + j;
       // invalid positions hold key 0, below every probe
-      const float* sc = a.cb.sample + uh * a.cb.sample_ld;
+      // (16-byte loads: thread t takes positions 8 (q * TH_THREADS + t) .. + 7;
+      // rows and len are multiples of 8; a key is its stored upper half)
+      const uint4* sc = reinterpret_cast<const uint4*>(a.cb.sample + uh * a.cb.sample_ld);
       const long long len = ngr * glen;
-      float f[NPT];
+      uint4 w8[NPT / 8];
 #pragma unroll
-      for (int q = 0; q < NPT; ++q) {
-        const long long i = (long long)q * TH_THREADS + tid;
-        f[q] = sc[i < len ? i : 0];
+      for (int q = 0; q < NPT / 8; ++q) {
+        const long long i8 = (long long)q * TH_THREADS + tid;
+        w8[q] = sc[8 * i8 < len ? i8 : 0];
       }
       uint32_t key[NPT];
       uint32_t mx = 0u;
 #pragma unroll
       for (int q = 0; q < NPT; ++q) {
-        const long long i = (long long)q * TH_THREADS + tid;
+        const long long i = 8 * ((long long)(q / 8) * TH_THREADS + tid) + q % 8;
         const long long t = (i / glen) * gtok + i % glen;
-        key[q] = (i < len && t >= 4 && t < hi) ? order_key(f[q]) : 0u;
+        const uint4 v = w8[q / 8];
+        const uint32_t w = (q % 8) / 2 == 0 ? v.x : (q % 8) / 2 == 1 ? v.y : (q % 8) / 2 == 2 ? v.z : v.w;
+        const uint32_t k16 = (q % 2) ? (w & 0xFFFF0000u) : (w << 16);
+        key[q] = (i < len && t >= 4 && t < hi) ? k16 : 0u;
         mx = key[q] > mx ? key[q] : mx;
       }
       if (tid == 0) nnear = 0;
@@ -425,32 +462,55 @@ __global__ __launch_bounds__(TH_THREADS) void threshold_reg_kernel(ThreshArgs a)
 }
 
 constexpr int CAND_MAX_PARTS = 4096;  // region parts per head the selection indexes (more: flagged)
-constexpr int CS_WAVES = 4;            // heads per workgroup, one wavefront each
+static_assert(CAND_CAP < 65536, "16-bit part prefixes");
+static_assert(8 * (int)sizeof(int) * (CAND_MAX_PARTS / 2 > FUSED_MAX_K ? CAND_MAX_PARTS / 2 : FUSED_MAX_K) <=
+                  65536,
+              "eight heads' areas fit 64 KiB of LDS");
 constexpr int CS_NPL = CAND_CAP / 64;  // candidates per lane
 constexpr int CS_WPL = FUSED_MAX_K / 64;  // winners per lane in the index sort
 static_assert(CAND_CAP % 64 == 0 && FUSED_MAX_K % 64 == 0, "whole wavefront rows");
+static_assert(FUSED_MAX_K <= 16 * 64, "the union merge takes at most 16 entries a lane");
 
 struct CandArgs {
   Geom g;
   int k;
   CandBufs cb;
   int32_t* idx;
-  int lds_ints;  // LDS ints per wavefront: the part prefix, then the winners
+  int lds_ints;    // LDS ints per wavefront: the 16-bit part prefix, then the winners and the head's list
+  UnionBufs un;    // the unit's union rows (when fuse_union)
+  int fuse_union;  // 1: the workgroup also merges its unit's lists (unflagged units)
 };
 
-// number of lanes of candidate rows r < NPL with pred(r); rows are taken in
-// groups of CS_GROUP, a group wholly at or past total skipped
+// sum over the wavefront: DPP inside each 16-lane row (quad_perm xor 1, xor
+// 2, row_half_mirror, row_mirror), then the four rows' sums read out; every
+// lane must be active
+__device__ __forceinline__ int wave_sum_dpp(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false);
+  return (__builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16)) +
+         (__builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48));
+}
+
+// number of lanes of candidate rows r < NPL with pred(r): per-lane counts in
+// two registers (no scalar chain per row), then one wavefront sum; rows are
+// taken in groups of CS_GROUP, a group wholly at or past total skipped
 constexpr int CS_GROUP = 16;
 template <int NPL, typename Pred>
 __device__ __forceinline__ int wave_count(int total, Pred pred) {
-  int c = 0;
+  int c0 = 0, c1 = 0;
 #pragma unroll
   for (int g = 0; g < NPL; g += CS_GROUP) {
-    if (g * 64 >= total) break;
-#pragma unroll
-    for (int r = g; r < g + CS_GROUP; ++r) c += __popcll(__ballot(pred(r)));
+    if (g * 64 < total) {
+  #pragma unroll
+      for (int r = g; r < g + CS_GROUP; r += 2) {
+        c0 += pred(r) ? 1 : 0;
+        c1 += pred(r + 1) ? 1 : 0;
+      }
+    }
   }
-  return c;
+  return wave_sum_dpp(c0 + c1);
 }
 
 // Sorts the wavefront's 64 * NE values ascending (lane-major: element
@@ -485,9 +545,12 @@ __device__ __forceinline__ void wave_bitonic_sort(int32_t (&x)[NE], int lane) {
   }
 }
 
-// the want winners in lds sorted ascending and written to out (NE a lane)
+// the want winners in lds sorted ascending and written to out, and as union
+// keys (token << 3 | head) to list (which may alias lds: every value is read
+// before any is written) (NE a lane)
 template <int NE>
-__device__ __forceinline__ void sort_winners(const int* lds, int want, int lane, int32_t* out) {
+__device__ __forceinline__ void sort_winners(const int* lds, int want, int lane, int32_t* out,
+                                             uint32_t* list, int h) {
   int32_t x[NE];
 #pragma unroll
   for (int r = 0; r < NE; ++r) {
@@ -498,42 +561,51 @@ __device__ __forceinline__ void sort_winners(const int* lds, int want, int lane,
 #pragma unroll
   for (int r = 0; r < NE; ++r) {
     const int e = lane * NE + r;
-    if (e < want) out[e] = x[r];
+    if (e < want) {
+      out[e] = x[r];
+      list[e] = ((uint32_t)x[r] << 3) | (uint32_t)h;
+    }
   }
 }
 
-// One wavefront per (unit, query head).  The candidates (at most CAND_CAP,
-// CS_NPL a lane in registers) are gathered through the prefix of the region
-// part counts; the key K* of the (k - 4 - W)-th largest is found bit by bit
-// from the top (the largest T with at least want keys >= T), the lowest token
-// indices among keys equal to K* likewise when not all of them are taken; the
-// winners are compacted in LDS, sorted by token index and written between
-// the first 4 and the last W tokens.
-__global__ __launch_bounds__(CS_WAVES * 64) void cand_select_kernel(CandArgs a) {
-  extern __shared__ int cs_lds[];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// One wavefront: the exact top-k of query head h of unit u from its
+// candidates (at most CAND_CAP, CS_NPL a lane in registers), gathered through
+// the prefix of the region part counts; the key K* of the (k - 4 - W)-th
+// largest is found bit by bit from the top (the largest T with at least want
+// keys >= T), the lowest token indices among keys equal to K* likewise when
+// not all of them are taken; the winners are compacted in LDS, sorted by
+// token index and written between the first 4 and the last W tokens.  The
+// head's list also goes to list[0, k) as union keys (token << 3 | h; padding
+// past n is ~0).  Returns true when the unit has to be redone unfused (its
+// flag is then set and nothing is written).
+__device__ __forceinline__ bool select_head(const CandArgs& a, int u, int h, int lane, int* lds,
+                                            uint32_t* list) {
   const int G = a.g.G;
-  const long long uh = (long long)blockIdx.x * CS_WAVES + wave;
-  if (uh >= (long long)a.g.units() * G) return;
-  const int u = (int)(uh / G);
-  int* lds = cs_lds + wave * a.lds_ints;
+  const long long uh = (long long)u * G + h;
   const int k = a.k;
   const long long n = a.g.n[a.g.seq_of(u)];
   int32_t* out = a.idx + uh * k;
   if (n <= k) {
-    for (int i = lane; i < k; i += 64) out[i] = i < n ? i : -1;
-    return;
+    for (int i = lane; i < k; i += 64) {
+      out[i] = i < n ? i : -1;
+      list[i] = i < n ? ((uint32_t)i << 3) | (uint32_t)h : 0xFFFFFFFFu;
+    }
+    return false;
   }
   const long long w = kept_tail(n);
   const long long hi = n - w;
   const int want = k - 4 - (int)w;
+  auto flag = [&]() {
+    if (lane == 0) a.cb.flag[u] = 1;
+    return true;
+  };
   if (want > 0) {
     const long long R = (n / BLK + a.cb.wg_blocks - 1) / a.cb.wg_blocks;
     const int nparts = (int)(R * CAND_PARTS);
-    if (nparts > CAND_MAX_PARTS || nparts > a.lds_ints) {
-      if (lane == 0) a.cb.flag[u] = 1;
-      return;
-    }
+    if (nparts > CAND_MAX_PARTS || nparts > 2 * a.lds_ints) return flag();
+    // the part counts, then their prefix, as 16-bit values over the wave's
+    // area (a unit is only taken when its total is at most CAND_CAP < 2^16)
+    uint16_t* pre = reinterpret_cast<uint16_t*>(lds);
     // exclusive prefix of the part counts ([region][part], in order): lane l
     // takes parts [l * cpl, (l + 1) * cpl), loads them all, then writes
     // their prefix after a scan of the lane sums
@@ -548,7 +620,7 @@ __global__ __launch_bounds__(CS_WAVES * 64) void cand_select_kernel(CandArgs a) 
       const int x = x0 + i;
       if (x < nparts) {
         const int c = cnt[x];
-        lds[x] = c;
+        pre[x] = (uint16_t)c;
         sum += c;
         over |= c > ps;
       }
@@ -564,34 +636,43 @@ __global__ __launch_bounds__(CS_WAVES * 64) void cand_select_kernel(CandArgs a) 
     for (int i = 0; i < cpl; ++i) {
       const int x = x0 + i;
       if (x < nparts) {
-        const int c = lds[x];
-        lds[x] = run;
+        const int c = pre[x];
+        pre[x] = (uint16_t)run;
         run += c;
       }
     }
     const int total = carry;
-    if (__ballot(over) != 0ull || total < want || total > CAND_CAP) {
-      if (lane == 0) a.cb.flag[u] = 1;
-      return;
-    }
+    if (__ballot(over) != 0ull || total < want || total > CAND_CAP) return flag();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     // candidate j = r * 64 + lane: its part is the last with prefix <= j
-    int top = 1;
-    while (2 * top < nparts) top <<= 1;
+    // (prefix 0 of part 0 is <= every j), found by halving [0, nparts) the
+    // same number of times for every row (the reads of a step issued
+    // together; rows of a group wholly past total are skipped)
     int part[CS_NPL];
 #pragma unroll
     for (int r = 0; r < CS_NPL; ++r) part[r] = 0;
-    for (int s = top; s > 0; s >>= 1) {
+    for (int m = nparts; m > 1;) {
+      const int half = m >> 1;
 #pragma unroll
       for (int g = 0; g < CS_NPL; g += CS_GROUP) {
-        if (g * 64 >= total) break;
-#pragma unroll
-        for (int r = g; r < g + CS_GROUP; ++r) {
-          const int q = part[r] + s;
-          if (q < nparts && lds[q] <= r * 64 + lane) part[r] = q;
+        if (g * 64 < total) {
+  #pragma unroll
+          for (int r = g; r < g + CS_GROUP; ++r)
+            part[r] = (int)pre[part[r] + half - 1] <= r * 64 + lane ? part[r] + half : part[r];
         }
+      }
+      m -= half;
+    }
+    // part[r] parts are known to start at or below j, and part[r] itself is
+    // the one left to test: the last part with prefix <= j
+#pragma unroll
+    for (int g = 0; g < CS_NPL; g += CS_GROUP) {
+      if (g * 64 < total) {
+  #pragma unroll
+        for (int r = g; r < g + CS_GROUP; ++r)
+          part[r] = (int)pre[part[r]] <= r * 64 + lane ? part[r] : part[r] - 1;
       }
     }
     // (order key, token index); padding (past total) is (0, INT_MAX), and no
@@ -605,25 +686,29 @@ __global__ __launch_bounds__(CS_WAVES * 64) void cand_select_kernel(CandArgs a) 
       key[r] = 0u;
       id[r] = INT_MAX;
     }
+    // every load issued before any is used (invalid lanes read slot 0), the
+    // scores' bits straight into key
 #pragma unroll
     for (int g = 0; g < CS_NPL; g += CS_GROUP) {
-      if (g * 64 >= total) break;
-      // every load of the group issued before any is used (invalid lanes
-      // read slot 0)
-      float sv[CS_GROUP];
-      int32_t si[CS_GROUP];
-#pragma unroll
-      for (int r = g; r < g + CS_GROUP; ++r) {
-        const int j = r * 64 + lane;
-        const long long e = j < total ? (long long)part[r] * ps + (j - lds[part[r]]) : 0;
-        sv[r - g] = v[e];
-        si[r - g] = ix[e];
+      if (g * 64 < total) {
+  #pragma unroll
+        for (int r = g; r < g + CS_GROUP; ++r) {
+          const int j = r * 64 + lane;
+          const long long e = j < total ? (long long)part[r] * ps + (j - pre[part[r]]) : 0;
+          key[r] = __float_as_uint(v[e]);
+          id[r] = ix[e];
+        }
       }
+    }
 #pragma unroll
-      for (int r = g; r < g + CS_GROUP; ++r) {
-        const bool ok = r * 64 + lane < total;
-        key[r] = ok ? order_key(sv[r - g]) : 0u;
-        id[r] = ok ? si[r - g] : INT_MAX;
+    for (int g = 0; g < CS_NPL; g += CS_GROUP) {
+      if (g * 64 < total) {
+  #pragma unroll
+        for (int r = g; r < g + CS_GROUP; ++r) {
+          const bool ok = r * 64 + lane < total;
+          key[r] = ok ? order_key(__uint_as_float(key[r])) : 0u;
+          id[r] = ok ? id[r] : INT_MAX;
+        }
       }
     }
     // the scan's test may also pass tokens a little below the threshold: only
@@ -631,10 +716,7 @@ __global__ __launch_bounds__(CS_WAVES * 64) void cand_select_kernel(CandArgs a) 
     const uint32_t tkey = a.cb.thresh[uh];
     const int ge =
         wave_count<CS_NPL>(total, [&](int r) { return id[r] != INT_MAX && key[r] >= tkey; });
-    if (ge < want) {
-      if (lane == 0) a.cb.flag[u] = 1;
-      return;
-    }
+    if (ge < want) return flag();
     // K*: the largest T with at least want keys >= T.  tkey <= K* <= the
     // largest key, so K* has their common top bits and the probes start below
     // them (padding keys are 0 and every probed T is at least 1).
@@ -644,23 +726,91 @@ __global__ __launch_bounds__(CS_WAVES * 64) void cand_select_kernel(CandArgs a) 
     mx = wave_max_dpp(mx);
     const uint32_t low = low_mask(tkey ^ mx);
     uint32_t T = tkey & ~low;
-    for (int b = __popc(low) - 1; b >= 0; --b) {
-      const uint32_t t = T | (1u << b);
-      if (wave_count<CS_NPL>(total, [&](int r) { return key[r] >= t; }) >= want) T = t;
+    // The free bits of K*, 8 a pass from the top (the last pass the rest):
+    // keys with T's bits above the digit are counted by the digit's value in
+    // 256 LDS bins over the spent part prefix, and the digit is the largest
+    // D with (keys above) + (keys in bins >= D) >= want.  That count never
+    // drops below want at D = 0 (it is then the count of keys >= T), and the
+    // keys above stay fewer than want, so D exists and no empty bin is taken.
+    // Padding keys are 0: they can only land in bin 0 of a pass whose upper
+    // bits are all 0, and never decide D (a real key is at least 1, so is K*).
+    int above = 0, eq = 0;  // keys above T, and equal to it, after the passes
+    int* hist = lds;
+    const int nfree = __popc(low);
+    for (int nb = nfree; nb > 0;) {
+      const int d = nb < 8 ? nb : 8;
+      const int sh = nb - d;
+      const uint32_t hm = sh + d >= 32 ? 0u : ~0u << (sh + d);
+      const uint32_t tb = T & hm;
+      const uint32_t dm = (1u << d) - 1u;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) hist[4 * lane + i] = 0;
+#pragma unroll
+      for (int g = 0; g < CS_NPL; g += CS_GROUP) {
+        if (g * 64 < total) {
+  #pragma unroll
+          for (int r = g; r < g + CS_GROUP; ++r)
+            if ((key[r] & hm) == tb) atomicAdd(&hist[(key[r] >> sh) & dm], 1);
+        }
+      }
+      // suffix sums over the bins, lane l holding bins 4l .. 4l + 3
+      int hb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) hb[i] = hist[4 * lane + i];
+      const int s3 = hb[3], s2 = s3 + hb[2], s1 = s2 + hb[1], s0 = s1 + hb[0];
+      int v = s0;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_down(v, off);
+        if (lane + off < 64) v += y;
+      }
+      const int base_cnt = above + v - s0;  // keys above, and in higher lanes' bins
+      int best = -1;
+      if (base_cnt + s0 >= want) best = 4 * lane;
+      if (base_cnt + s1 >= want) best = 4 * lane + 1;
+      if (base_cnt + s2 >= want) best = 4 * lane + 2;
+      if (base_cnt + s3 >= want) best = 4 * lane + 3;
+      const int D = (int)wave_max_dpp((uint32_t)(best + 1)) - 1;
+      int gt = 0, at = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        gt += 4 * lane + i > D ? hb[i] : 0;
+        at += 4 * lane + i == D ? hb[i] : 0;
+      }
+      above += wave_sum_dpp(gt);
+      eq = wave_sum_dpp(at);
+      T = tb | ((uint32_t)D << sh);
+      nb -= d;
     }
-    // the winners, compacted into LDS over the spent part prefix: first the
-    // keys above K*, then the lowest-index keys equal to it
+    if (nfree == 0) {  // every candidate key at or above the threshold is tkey
+      above = wave_count<CS_NPL>(total, [&](int r) { return key[r] > T; });
+      eq = wave_count<CS_NPL>(total, [&](int r) { return key[r] == T; });
+    }
+    // the winners: the keys above K*, and the lowest-index keys equal to it
+    // (rem >= 1 of them)
+    const int rem = want - above;
+    int32_t imax = INT_MAX;  // ties taken: index <= imax
+    if (eq > rem) {
+      // the rem-th lowest tie index: the largest I with fewer than rem tie
+      // indices below it
+      int32_t I = 0;
+      for (int b = 30; b >= 0; --b) {
+        const int32_t t = I | (1 << b);
+        if (wave_count<CS_NPL>(total, [&](int r) { return key[r] == T && id[r] < t; }) < rem) I = t;
+      }
+      imax = I;
+    }
+    // compacted into LDS over the spent part prefix
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     int base = 0;
-    auto emit = [&](auto win) {
 #pragma unroll
-      for (int g = 0; g < CS_NPL; g += CS_GROUP) {
-        if (g * 64 >= total) break;
-#pragma unroll
+    for (int g = 0; g < CS_NPL; g += CS_GROUP) {
+      if (g * 64 < total) {
+  #pragma unroll
         for (int r = g; r < g + CS_GROUP; ++r) {
-          const bool w_ = win(r);
+          const bool w_ = key[r] > T || (key[r] == T && id[r] <= imax);
           const uint64_t m = __ballot(w_);
           const int pos = base + (int)__builtin_amdgcn_mbcnt_hi(
                                      (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
@@ -668,36 +818,75 @@ __global__ __launch_bounds__(CS_WAVES * 64) void cand_select_kernel(CandArgs a) 
           base += __popcll(m);
         }
       }
-    };
-    emit([&](int r) { return key[r] > T; });
-    const int rem = want - base;  // >= 1 keys equal to K* are taken
-    // the ties' indices (INT_MAX for every other slot)
-#pragma unroll
-    for (int r = 0; r < CS_NPL; ++r) id[r] = key[r] == T ? id[r] : INT_MAX;
-    const int eq = wave_count<CS_NPL>(total, [&](int r) { return id[r] != INT_MAX; });
-    int32_t imax = INT_MAX - 1;  // ties taken: index <= imax
-    if (eq > rem) {
-      // the rem-th lowest tie index: the largest I with fewer than rem tie
-      // indices below it
-      int32_t I = 0;
-      for (int b = 30; b >= 0; --b) {
-        const int32_t t = I | (1 << b);
-        if (wave_count<CS_NPL>(total, [&](int r) { return id[r] < t; }) < rem) I = t;
-      }
-      imax = I;
     }
-    emit([&](int r) { return id[r] <= imax; });
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     if (want <= 64 * (CS_WPL / 2))
-      sort_winners<CS_WPL / 2>(lds, want, lane, out + 4);
+      sort_winners<CS_WPL / 2>(lds, want, lane, out + 4, list + 4, h);
     else
-      sort_winners<CS_WPL>(lds, want, lane, out + 4);
+      sort_winners<CS_WPL>(lds, want, lane, out + 4, list + 4, h);
   }
   const int nk = want > 0 ? want : 0;
-  if (lane < 4 && lane < k) out[lane] = lane;
-  for (long long i = lane; 4 + nk + i < k; i += 64) out[4 + nk + i] = (int32_t)(hi + i);
+  if (lane < 4 && lane < k) {
+    out[lane] = lane;
+    list[lane] = ((uint32_t)lane << 3) | (uint32_t)h;
+  }
+  for (long long i = lane; 4 + nk + i < k; i += 64) {
+    out[4 + nk + i] = (int32_t)(hi + i);
+    list[4 + nk + i] = ((uint32_t)(hi + i) << 3) | (uint32_t)h;
+  }
+  return false;
+}
+
+// One workgroup per unit, wavefront h for query head h (select_head).  With
+// fuse_union, once no head of the unit was flagged, the workgroup merges the
+// G strictly ascending lists (position of an entry = its index in its list
+// plus the entries below it in every other list), collapses runs of one token
+// into a union row with a G-bit head mask and writes the rows, masks and
+// count as union_kernel does, and zeroes the unit's arrival counter.
+template <int G>
+__global__ __launch_bounds__(G * 64) void cand_select_kernel(CandArgs a) {
+  extern __shared__ int cs_lds[];
+  const int tid = threadIdx.x, lane = tid & 63, h = tid >> 6;
+  const int u = blockIdx.x;
+  const int k = a.k;
+  int* lds = cs_lds + h * a.lds_ints;
+  auto list_of = [&](int b) { return reinterpret_cast<uint32_t*>(cs_lds + b * a.lds_ints); };
+  const bool flagged = select_head(a, u, h, lane, lds, list_of(h));
+  if (__syncthreads_or(flagged) || !a.fuse_union) return;
+
+  constexpr int NT = G * 64;
+  const int sel = G * k;
+  const long long n = a.g.n[a.g.seq_of(u)];
+  const int nv = n < k ? (int)n : k;  // valid entries of every list
+  uint32_t* merged = reinterpret_cast<uint32_t*>(cs_lds + G * a.lds_ints);
+  uint32_t* masks = merged + sel;  // one byte per union row
+  int* wsum = reinterpret_cast<int*>(masks + (sel + 3) / 4);
+  for (int e = tid; e < (sel + 3) / 4; e += NT) masks[e] = 0u;
+  // wavefront h brings the entries of list h, lane l entries l + 64 j (at
+  // most nv / 64 <= k / 64 a lane); a thread then owns at most as many
+  // merged positions
+  auto run = [&](auto EC) {
+    constexpr int E = decltype(EC)::value;
+    uint32_t x[E];
+    bool ok[E];
+    int p[E];  // entries below x[j] in its own list: its index
+    const uint32_t* own = list_of(h);
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      const int i = lane + 64 * j;
+      ok[j] = i < nv;
+      x[j] = own[i < nv ? i : 0];
+      p[j] = i;
+    }
+    merge_by_rank<E>(list_of, [&](int) { return nv; }, G, x, ok, p, h, merged);
+    write_union<E>(merged, G * nv, masks, wsum, a.un.uidx + (long long)u * sel,
+                   a.un.umask + (long long)u * sel, a.un.ucount + u, tid, NT);
+  };
+  if (k <= 256) run(std::integral_constant<int, 4>{});
+  else if (k <= 512) run(std::integral_constant<int, 8>{});
+  else run(std::integral_constant<int, 16>{});
 }
 
 // number of units whose flag is set, into *count (one workgroup; every
@@ -730,11 +919,10 @@ hipError_t launch_topk(const Geom& g, const float* scores, int k, int32_t* idx, 
 }
 
 hipError_t launch_topk_flagged(const Geom& g, const float* scores, int k, int32_t* idx,
-                               const int32_t* flag, hipStream_t st) {
+                               const int32_t* flag, const UnionBufs* un, hipStream_t st) {
   TopkArgs a{g, scores, k, idx, flag};
-  const long long blocks = (long long)g.units() * g.G;
-  if (blocks == 0) return hipSuccess;
-  topk_kernel<<<(unsigned)blocks, TK_THREADS, 0, st>>>(a);
+  if (g.units() == 0) return hipSuccess;
+  topk_unit_kernel<<<(unsigned)g.units(), TK_THREADS, 0, st>>>(a, un ? *un : UnionBufs{});
   return hipGetLastError();
 }
 
@@ -753,17 +941,31 @@ hipError_t launch_threshold(const Geom& g, int k, const CandBufs& cb, hipStream_
 }
 
 hipError_t launch_cand_select(const Geom& g, int k, const CandBufs& cb, int32_t* idx,
-                              hipStream_t st) {
-  const long long heads = (long long)g.units() * g.G;
-  if (heads == 0) return hipSuccess;
+                              const UnionBufs* un, bool* fused, hipStream_t st) {
+  if (fused) *fused = false;
+  if (g.units() == 0) return hipSuccess;
   long long maxnb = 0;
   for (int s = 0; s < g.S; ++s) maxnb = g.n[s] / BLK > maxnb ? g.n[s] / BLK : maxnb;
   const long long parts = (maxnb + cb.wg_blocks - 1) / cb.wg_blocks * CAND_PARTS;
-  int lds_ints = (int)(parts < CAND_MAX_PARTS ? parts : CAND_MAX_PARTS);
+  // per head: the part prefix (16 bits a part) or the k <= FUSED_MAX_K
+  // winners and list (32 bits an entry); at most 8 KiB a head
+  int lds_ints = (int)((parts < CAND_MAX_PARTS ? parts : CAND_MAX_PARTS) + 1) / 2;
   lds_ints = lds_ints > FUSED_MAX_K ? lds_ints : FUSED_MAX_K;
-  CandArgs a{g, k, cb, idx, lds_ints};
-  const size_t lds = (size_t)lds_ints * sizeof(int) * CS_WAVES;
-  cand_select_kernel<<<(unsigned)((heads + CS_WAVES - 1) / CS_WAVES), CS_WAVES * 64, lds, st>>>(a);
+  const size_t sel = (size_t)g.G * k;
+  const size_t lists = (size_t)lds_ints * sizeof(int) * g.G;
+  const size_t merge = sel * sizeof(uint32_t) + (sel + 3) / 4 * sizeof(uint32_t) + g.G * sizeof(int);
+  CandArgs a{g, k, cb, idx, lds_ints, un ? *un : UnionBufs{}, 0};
+  // the merge's LDS is only taken while the workgroup stays small
+  a.fuse_union = un != nullptr && lists + merge <= CAND_FUSED_LDS;
+  if (fused) *fused = a.fuse_union != 0;
+  const size_t lds = lists + (a.fuse_union ? merge : 0);
+  switch (g.G) {
+    case 1: cand_select_kernel<1><<<g.units(), 64, lds, st>>>(a); break;
+    case 2: cand_select_kernel<2><<<g.units(), 128, lds, st>>>(a); break;
+    case 4: cand_select_kernel<4><<<g.units(), 256, lds, st>>>(a); break;
+    case 8: cand_select_kernel<8><<<g.units(), 512, lds, st>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

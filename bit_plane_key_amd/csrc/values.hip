@@ -587,7 +587,7 @@ size_t attend_v_ws_bytes(const Geom& g, int k) { return vws_layout(g, k).total; 
 hipError_t launch_attend_v(const Geom& g, int k_dtype, const void* k_rows, const uint8_t* vplanes,
                            const uint16_t* vscales, const uint16_t* q, const int32_t* idx, int k,
                            float scale, int v_budget, float* out, int32_t* union_out,
-                           uint8_t* vdepth_out, void* ws, hipStream_t st) {
+                           uint8_t* vdepth_out, void* ws, bool union_ready, hipStream_t st) {
   if (g.units() == 0) return hipSuccess;
   const VWs w = vws_layout(g, k);
   char* base = static_cast<char*>(ws);
@@ -601,7 +601,7 @@ hipError_t launch_attend_v(const Geom& g, int k_dtype, const void* k_rows, const
   float* part = reinterpret_cast<float*>(base + w.part);
   float* vsc = reinterpret_cast<float*>(base + w.scale);
   hipError_t e = launch_union_logits(g, k_dtype, k_rows, q, idx, k, scale, uidx, umask, ucount,
-                                     ev, stats, vscales, vsc, st);
+                                     ev, stats, vscales, vsc, union_ready, st);
   if (e != hipSuccess) return e;
   const long long sel = (long long)g.G * k;
   VDepthArgs da{g,       sel,      ucount,  uidx,     ev,   stats,      fac,

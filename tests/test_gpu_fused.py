@@ -73,6 +73,18 @@ def _wg_blocks(nb, units=1):
     return wb
 
 
+def _key_floor(x):
+    """The sampled threshold as the kernel keeps it: score x with the low 16
+    bits of its order key cleared (the sample stores the upper halves)."""
+    u = int(np.array([x], dtype=np.float32).view(np.uint32)[0])
+    if (u << 1) & 0xFFFFFFFF == 0:
+        u = 0
+    key = (~u & 0xFFFFFFFF) if u & 0x80000000 else (u | 0x80000000)
+    key &= 0xFFFF0000
+    bits = (key & 0x7FFFFFFF) if key & 0x80000000 else (~key & 0xFFFFFFFF)
+    return float(np.array([bits], dtype=np.uint32).view(np.float32)[0])
+
+
 def _fused_plan(scores_h, n, k, units=1):
     """The fused plan on one head's exact scores: (tokens at or above the
     sampled threshold, the largest count of them in one wavefront part, the
@@ -86,7 +98,7 @@ def _fused_plan(scores_h, n, k, units=1):
     toks = toks[(toks >= 4) & (toks < hi)]
     m, nc = len(toks), hi - 4
     r = (2 * want * m + nc - 1) // nc + 8
-    tau = -np.inf if r > m else np.sort(scores_h[toks])[::-1][r - 1]
+    tau = -np.inf if r > m else _key_floor(np.sort(scores_h[toks])[::-1][r - 1])
     passed = np.zeros(nb * 64, dtype=bool)
     passed[4:hi] = scores_h[4:hi] >= tau
     wb = _wg_blocks(nb, units)
@@ -173,6 +185,40 @@ def test_fused_too_few_candidates_falls_back(bpk):
     assert flagged == 1
     assert torch.equal(idx, idx2)
     P.check_topk_valid(sc[:, :n].astype(np.float64), idx[0, 0, 0].cpu().numpy(), n, k, "few")
+
+
+def test_fused_ties_at_threshold_take_lowest_indices(bpk):
+    """Many candidates tie at the k-th score without overflowing: channel 0
+    holds 7 on every 50th token and -8 elsewhere (every block scale 1), the
+    query reads only channel 0 (one plane), so every such token scores the
+    same top value.  The fused selection takes the lowest indices among the
+    ties, as the unfused radix select does, without redoing the unit."""
+    b, wl = bpk
+    n, k, group = 64 * 600, 300, 4
+    rng = np.random.default_rng(50)
+    k32 = rng.uniform(-0.5, 0.5, (n, 128)).astype(np.float32)
+    k32[:, 0] = -8.0
+    top = np.arange(0, n, 50)
+    k32[top, 0] = 7.0
+    kb = f32_to_bf16_bits(k32)
+    vb = f32_to_bf16_bits(rng.standard_normal((n, 128)).astype(np.float32))
+    q32 = np.zeros((group, 128), dtype=np.float32)
+    q32[:, 0] = 1.0 + 0.25 * np.arange(group)
+    cache = _unit_cache(b, kb, vb, np.ones(128, dtype=np.float32), group)
+    q = _to_dev(f32_to_bf16_bits(q32))[None, None, None]
+    scale = 1 / math.sqrt(128)
+    idx, out, flagged = _fused(b, cache, q, 1, k, scale, group)
+    scores, idx2 = _unfused(b, cache, q, 1, k, scale)
+    torch.cuda.synchronize()
+    assert flagged == 0
+    assert torch.equal(idx, idx2)
+    w = O.kept_tail(n)
+    want = k - 4 - w
+    cand = top[(top >= 4) & (top < n - w)]
+    assert len(cand) > want  # the k-th score is tied
+    expect = np.concatenate([np.arange(4), cand[:want], np.arange(n - w, n)])
+    for h in range(group):
+        assert np.array_equal(idx[0, 0, 0, h].cpu().numpy(), expect)
 
 
 def test_fused_overflow_falls_back(bpk):

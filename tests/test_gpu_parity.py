@@ -195,6 +195,41 @@ def test_calls_c2(bpk, c2, budget):
         P.check_attention(ot[0, 0, h], att, where)
 
 
+def test_sparse_attend_list_forms(bpk, c2):
+    """The union stage merges ascending lists of different lengths (-1 padding
+    at the end) by rank and sorts unordered lists (padding anywhere) whole:
+    attention matches the oracle over each head's own set, a head with no row
+    outputs zeros, and an unordered copy of the lists gives the same result
+    bit for bit."""
+    b, wl = bpk
+    cfg, cache, q, inps = c2
+    scale = wl.softmax_scale(cfg)
+    n, k = cfg.n, cfg.k
+    rng = np.random.default_rng(11)
+    G = q.shape[3]
+    lens = [k, k // 3, 1, 0, k - 1, 37, k, 2]
+    idx = np.full((1, 1, cfg.heads, G, k), -1, dtype=np.int32)
+    for h in range(cfg.heads):
+        for g in range(G):
+            m = lens[(h + g) % len(lens)]
+            idx[0, 0, h, g, :m] = np.sort(rng.choice(n, size=m, replace=False))
+    shuffled = idx.copy()
+    for h in range(cfg.heads):
+        for g in range(G):
+            shuffled[0, 0, h, g] = rng.permutation(shuffled[0, 0, h, g])
+    out = b.sparse_attend(cache, q, torch.from_numpy(idx).cuda(), 0, 1, k, scale)
+    out2 = b.sparse_attend(cache, q, torch.from_numpy(shuffled).cuda(), 0, 1, k, scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
+    ot = out.cpu().numpy()
+    for h in range(cfg.heads):
+        att = O.attend(inps[h]["q"], inps[h]["k"], inps[h]["v"], idx[0, 0, h], scale)
+        P.check_attention(ot[0, 0, h], att, f"list forms head {h}")
+        for g in range(G):
+            if lens[(h + g) % len(lens)] == 0:
+                assert not ot[0, 0, h, g].any()
+
+
 def test_decode_step_c1(bpk, c1):
     b, wl = bpk
     cfg, cache, q, inp = c1
