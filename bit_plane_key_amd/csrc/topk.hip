@@ -845,8 +845,11 @@ __device__ __forceinline__ bool select_head(const CandArgs& a, int u, int h, int
 // plus the entries below it in every other list), collapses runs of one token
 // into a union row with a G-bit head mask and writes the rows, masks and
 // count as union_kernel does, and zeroes the unit's arrival counter.
-template <int G>
-__global__ __launch_bounds__(G * 64) void cand_select_kernel(CandArgs a) {
+// (WPE: wavefronts per SIMD the registers allow; three caps them at 168,
+// which costs each wavefront some speed but fits 50 % more workgroups)
+template <int G, int WPE>
+__global__ __launch_bounds__(G * 64) __attribute__((amdgpu_waves_per_eu(WPE)))
+void cand_select_kernel(CandArgs a) {
   extern __shared__ int cs_lds[];
   const int tid = threadIdx.x, lane = tid & 63, h = tid >> 6;
   const int u = blockIdx.x;
@@ -959,11 +962,23 @@ hipError_t launch_cand_select(const Geom& g, int k, const CandBufs& cb, int32_t*
   a.fuse_union = un != nullptr && lists + merge <= CAND_FUSED_LDS;
   if (fused) *fused = a.fuse_union != 0;
   const size_t lds = lists + (a.fuse_union ? merge : 0);
+  // units beyond what two wavefronts per SIMD hold at once (G of them per
+  // workgroup, 4 SIMDs on each of 256 CUs) take the three-wavefront variant
+  const bool many = (long long)g.units() * g.G > 2LL * 4 * 256;
   switch (g.G) {
-    case 1: cand_select_kernel<1><<<g.units(), 64, lds, st>>>(a); break;
-    case 2: cand_select_kernel<2><<<g.units(), 128, lds, st>>>(a); break;
-    case 4: cand_select_kernel<4><<<g.units(), 256, lds, st>>>(a); break;
-    case 8: cand_select_kernel<8><<<g.units(), 512, lds, st>>>(a); break;
+    case 1:
+      if (many) cand_select_kernel<1, 3><<<g.units(), 64, lds, st>>>(a);
+      else cand_select_kernel<1, 2><<<g.units(), 64, lds, st>>>(a);
+      break;
+    case 2:
+      if (many) cand_select_kernel<2, 3><<<g.units(), 128, lds, st>>>(a);
+      else cand_select_kernel<2, 2><<<g.units(), 128, lds, st>>>(a);
+      break;
+    case 4:
+      if (many) cand_select_kernel<4, 3><<<g.units(), 256, lds, st>>>(a);
+      else cand_select_kernel<4, 2><<<g.units(), 256, lds, st>>>(a);
+      break;
+    case 8: cand_select_kernel<8, 2><<<g.units(), 512, lds, st>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
