@@ -269,24 +269,6 @@ def main() -> int:
     log("warmup done")
     ms_step = time_launches(step, args.steps)
     log(f"decode step (median): {ms_step * 1e3:.1f} us")
-    # the same step replayed from a HIP graph captured once (the same kernels
-    # with the same arguments, no host launches between them); the appending
-    # workload changes the cache length every step and is not captured
-    ms_graph = None
-    if not appends:
-        graph = torch.cuda.CUDAGraph()
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            step()
-        torch.cuda.current_stream().wait_stream(side)
-        with torch.cuda.graph(graph):
-            step()
-        graph.replay()
-        torch.cuda.synchronize()
-        ms_graph = time_launches(graph.replay, args.steps)
-        del graph
-        log(f"decode step replayed from a HIP graph (median): {ms_graph * 1e3:.1f} us")
     stage_ms = traced(args.steps, step)
     ms_scan = stage_ms["scan"]
     log("stages, median us: " + " ".join(f"{nm} {v * 1e3:.1f}" for nm, v in stage_ms.items()))
@@ -534,7 +516,6 @@ def main() -> int:
             "timing": "median of HIP-event stage times",
         },
         "decode_step_us": round(ms_step * 1e3, 1),
-        "decode_step_graph_us": None if ms_graph is None else round(ms_graph * 1e3, 1),
         "stage_us": {name: round(v * 1e3, 1) for name, v in stage_ms.items()},
         "units_redone_unfused": flagged,
         "attend": {"union_rows": union_rows, "bytes": attend_bytes,
