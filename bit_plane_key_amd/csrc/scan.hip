@@ -329,9 +329,14 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : (RM <= RM_SMALL ? 3 : 2)
       // the block's own largest weight is at least a quarter of the frame's
       // if the channel that sets the frame keeps a quarter of its step max
       if (4.f * half_bits_to_f32(sm.sc[b3][cs][blk]) < sm.smax[b3][cs]) {
+        // the block's largest weight, over the read channels (|q| 8 from
+        // qa8, zero past CR; 8 channels' reads in flight at a time)
         float mb = 0.f;
-        for (int c = 0; c < CR; ++c)
-          mb = fmaxf(mb, fabsf(sm.q[h][sm.chj[c]]) * 8.f * half_bits_to_f32(sm.sc[b3][c][blk]));
+        for (int c0 = 0; c0 < CR; c0 += 8) {
+#pragma unroll
+          for (int c = c0; c < c0 + 8; ++c)
+            mb = fmaxf(mb, sm.qa8[h][c] * half_bits_to_f32(sm.sc[b3][c < RM ? c : 0][blk]));
+        }
         eb = frame_exp(mb, FRAME_BITS);
         own = eb != E;
       }
