@@ -71,7 +71,7 @@ constexpr int PSTRIDE = 136;          // LDS bytes per plane row: 16 words + 8 b
 constexpr int SCS = 20;               // LDS fp16 slots per read channel: 16 blocks + 4 of padding
 constexpr int RM_SMALL = 96;          // row capacity of the three-workgroups-per-CU variant
 constexpr long long FAST_MAX_CAP = 1ll << 25;   // one unit's planes fit a 32-bit buffer offset
-constexpr int FLAGGED_SPAN = 1024;              // blocks per workgroup of a flagged-units scan
+constexpr int FLAGGED_SPAN = 4096;              // blocks per workgroup of a flagged-units scan
 constexpr uint32_t OUT_OF_RANGE = 0x80000000u;  // a buffer offset past every unit's planes
 constexpr int RSRC_WORD3 = 0x00020000;          // raw (untyped) buffer, 32-bit data format
 
@@ -785,7 +785,8 @@ hipError_t launch_fast(const ScanArgs& a0, int rows, hipStream_t st) {
   } else {
     int wb = scan_wg_blocks(a.g);
     // the decode step's fallback scan usually finds no unit flagged: larger
-    // spans mean fewer workgroups that only read a flag and leave
+    // spans mean fewer workgroups that only read a flag and leave (a flagged
+    // unit of 2^20 tokens is then rescored by 4 workgroups)
     if (MODE == SCAN_FULL && a.unit_flag && wb < FLAGGED_SPAN) wb = FLAGGED_SPAN;
     a.wg_blocks = wb;
     grid = dim3((unsigned)((maxnb + wb - 1) / wb), (unsigned)a.g.units());
