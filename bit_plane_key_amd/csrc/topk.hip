@@ -241,6 +241,18 @@ __device__ __forceinline__ uint32_t wave_max_dpp(uint32_t v) {
             mx((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48)));
 }
 
+// sum over the wavefront: DPP inside each 16-lane row (quad_perm xor 1, xor
+// 2, row_half_mirror, row_mirror), then the four rows' sums read out; every
+// lane must be active
+__device__ __forceinline__ int wave_sum_dpp(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false);
+  return (__builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16)) +
+         (__builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48));
+}
+
 // bits at and below the highest set bit of x (0 for x == 0), by smearing
 // (no leading-zero count and no select on x == 0, both of which have
 // compiled to scalar code testing the wrong condition)
@@ -393,8 +405,8 @@ __global__ __launch_bounds__(TH_THREADS) void threshold_reg_kernel(ThreshArgs a)
       };
       // the lower bound (0 when r > 64: no cut)
       uint32_t lw = 0u;
-      if (r <= 64) {
-        for (int b = 31; b >= 0; --b) {
+      if (r <= 64) {  // (keys have 16 significant bits)
+        for (int b = 31; b >= 16; --b) {
           const uint32_t t = lw | (1u << b);
           if (__popcll(__ballot(mx >= t)) >= r) lw = t;
         }
@@ -439,7 +451,7 @@ __global__ __launch_bounds__(TH_THREADS) void threshold_reg_kernel(ThreshArgs a)
         hk = wave_max_dpp(hk);
         const uint32_t low = low_mask(L ^ hk);
         T = L & ~low;
-        for (int b = __popc(low) - 1; b >= 0; --b) {
+        for (int b = __popc(low) - 1; b >= 16; --b) {
           const uint32_t t = T | (1u << b);
           int c = 0;
 #pragma unroll
@@ -447,7 +459,7 @@ __global__ __launch_bounds__(TH_THREADS) void threshold_reg_kernel(ThreshArgs a)
           if (c >= r) T = t;
         }
       } else {
-        for (int b = 31; b >= 0; --b) {
+        for (int b = 31; b >= 16; --b) {
           const uint32_t t = T | (1u << b);
           if (block_count(t) >= r) T = t;
         }
@@ -456,6 +468,129 @@ __global__ __launch_bounds__(TH_THREADS) void threshold_reg_kernel(ThreshArgs a)
     }
   }
   if (tid == 0) {
+    a.cb.thresh[uh] = tkey;
+    if (h == 0) a.cb.flag[u] = 0;
+  }
+}
+
+// The same threshold with one wavefront per (unit, head), four heads per
+// workgroup and no workgroup barrier, for samples of at most 64 * NPT keys
+// (NPT keys a lane): the lane maxima's r-th largest bounds T from below when
+// r <= 64, the keys at or above the bound are compacted into the wavefront's
+// LDS area and searched bit by bit, four a lane; otherwise every bit is
+// probed over all keys.
+template <int NPT>
+__global__ __launch_bounds__(256) void threshold_wave_kernel(ThreshArgs a) {
+  __shared__ uint32_t near[4][TH_CAP];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int G = a.g.G;
+  const long long uh = (long long)blockIdx.x * 4 + wave;
+  if (uh >= (long long)a.g.units() * G) return;  // (no barrier follows)
+  const int u = (int)(uh / G), h = (int)(uh % G);
+  const long long n = a.g.n[a.g.seq_of(u)];
+  const long long w = kept_tail(n);
+  const long long hi = n - w;
+  const long long want = (long long)a.k - 4 - w;
+  uint32_t tkey = 0xFFFFFFFFu;  // nothing is a candidate
+  if (n > a.k && want > 0) {
+    const long long nb = n / BLK;
+    const long long ngr = (nb + SAMPLE_STRIDE - 1) / SAMPLE_STRIDE;
+    const long long gtok = (long long)SAMPLE_STRIDE * BLK, glen = (long long)SAMPLE_GROUP * BLK;
+    long long m = 0;
+    for (long long gi = 0; gi < ngr; ++gi) {
+      const long long t0 = gi * gtok, t1 = t0 + glen;
+      const long long x0 = t0 > 4 ? t0 : 4, x1 = t1 < hi ? t1 : hi;
+      m += x1 > x0 ? x1 - x0 : 0;
+    }
+    const long long nc = hi - 4;
+    const long long r = (2 * want * m + nc - 1) / nc + 8;
+    if (r > m) {
+      tkey = 0;  // the sample is too small to cut anything: all are candidates
+    } else {
+      // 16-byte loads: lane l takes positions 8 (q * 64 + l) .. + 7 (rows and
+      // len are multiples of 8; a key is its stored upper half)
+      const uint4* sc = reinterpret_cast<const uint4*>(a.cb.sample + uh * a.cb.sample_ld);
+      const long long len = ngr * glen;
+      uint4 w8[NPT / 8];
+#pragma unroll
+      for (int q = 0; q < NPT / 8; ++q) {
+        const long long i8 = (long long)q * 64 + lane;
+        w8[q] = sc[8 * i8 < len ? i8 : 0];
+      }
+      uint32_t key[NPT];
+      uint32_t mx = 0u;
+#pragma unroll
+      for (int q = 0; q < NPT; ++q) {
+        const long long i = 8 * ((long long)(q / 8) * 64 + lane) + q % 8;
+        const long long t = (i / glen) * gtok + i % glen;
+        const uint4 v = w8[q / 8];
+        const uint32_t wd = (q % 8) / 2 == 0 ? v.x : (q % 8) / 2 == 1 ? v.y : (q % 8) / 2 == 2 ? v.z : v.w;
+        const uint32_t k16 = (q % 2) ? (wd & 0xFFFF0000u) : (wd << 16);
+        key[q] = (i < len && t >= 4 && t < hi) ? k16 : 0u;
+        mx = key[q] > mx ? key[q] : mx;
+      }
+      // the lower bound (0 when r > 64: no cut); keys have 16 significant bits
+      uint32_t L = 0u;
+      if (r <= 64) {
+        for (int b = 31; b >= 16; --b) {
+          const uint32_t t = L | (1u << b);
+          if (__popcll(__ballot(mx >= t)) >= r) L = t;
+        }
+      }
+      uint32_t T = 0u;
+      int nn = TH_CAP + 1;
+      if (L != 0u) {
+        // the keys at or above the bound, compacted in key order of the lanes
+        int base = 0;
+#pragma unroll
+        for (int q = 0; q < NPT; ++q) {
+          const bool nr = key[q] >= L;
+          const uint64_t mk = __ballot(nr);
+          const int pos = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mk >> 32),
+                                                                __builtin_amdgcn_mbcnt_lo((uint32_t)mk, 0u));
+          if (nr && pos < TH_CAP) near[wave][pos] = key[q];
+          base += __popcll(mk);
+        }
+        nn = base;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      if (L != 0u && nn <= TH_CAP) {
+        // four compacted keys a lane (0 past nn, below every probe); T >= L,
+        // so the bits above the highest one where L and the largest compacted
+        // key differ are L's
+        uint32_t nk[4];
+        uint32_t hk = 0u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int i = lane + 64 * j;
+          nk[j] = i < nn ? near[wave][i] : 0u;
+          hk = nk[j] > hk ? nk[j] : hk;
+        }
+        hk = wave_max_dpp(hk);
+        const uint32_t low = low_mask(L ^ hk);
+        T = L & ~low;
+        for (int b = __popc(low) - 1; b >= 16; --b) {
+          const uint32_t t = T | (1u << b);
+          int c = 0;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) c += __popcll(__ballot(nk[j] >= t));
+          if (c >= r) T = t;
+        }
+      } else {
+        for (int b = 31; b >= 16; --b) {
+          const uint32_t t = T | (1u << b);
+          int c = 0;
+#pragma unroll
+          for (int q = 0; q < NPT; ++q) c += key[q] >= t ? 1 : 0;
+          if (wave_sum_dpp(c) >= r) T = t;
+        }
+      }
+      tkey = T;
+    }
+  }
+  if (lane == 0) {
     a.cb.thresh[uh] = tkey;
     if (h == 0) a.cb.flag[u] = 0;
   }
@@ -480,18 +615,6 @@ struct CandArgs {
   UnionBufs un;    // the unit's union rows (when fuse_union)
   int fuse_union;  // 1: the workgroup also merges its unit's lists (unflagged units)
 };
-
-// sum over the wavefront: DPP inside each 16-lane row (quad_perm xor 1, xor
-// 2, row_half_mirror, row_mirror), then the four rows' sums read out; every
-// lane must be active
-__device__ __forceinline__ int wave_sum_dpp(int v) {
-  v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);
-  v += __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);
-  v += __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);
-  v += __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false);
-  return (__builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16)) +
-         (__builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48));
-}
 
 // number of lanes of candidate rows r < NPL with pred(r): per-lane counts in
 // two registers (no scalar chain per row), then one wavefront sum; rows are
@@ -934,8 +1057,8 @@ hipError_t launch_threshold(const Geom& g, int k, const CandBufs& cb, hipStream_
   const long long blocks = (long long)g.units() * g.G;
   if (blocks == 0) return hipSuccess;
   const long long len = sample_groups(g) * SAMPLE_GROUP * BLK;
-  if (len <= 16 * TH_THREADS)
-    threshold_reg_kernel<16><<<(unsigned)blocks, TH_THREADS, 0, st>>>(a);
+  if (len <= 64 * 64)
+    threshold_wave_kernel<64><<<(unsigned)((blocks + 3) / 4), 256, 0, st>>>(a);
   else if (len <= 64 * TH_THREADS)
     threshold_reg_kernel<64><<<(unsigned)blocks, TH_THREADS, 0, st>>>(a);
   else
