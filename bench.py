@@ -134,7 +134,8 @@ def cpu_baseline(cfg, budget: int, tokens: int, units, n: int, step_units: int, 
     import concurrent.futures as cf
     import multiprocessing as mp
     jobs = [(cfg.name, s, l, h, tokens, budget, k, scale) for (s, l, h) in units]
-    # a GPU machine's host share is 16 cores, whatever the machine reports
+    # at most 16 worker processes: the host share of one GPU, whatever the
+    # machine reports
     cores = min(len(jobs), os.cpu_count() or 1, 16)
     env = {"OMP_NUM_THREADS": "1", "OPENBLAS_NUM_THREADS": "1", "MKL_NUM_THREADS": "1"}
     old = {x: os.environ.get(x) for x in env}
@@ -190,8 +191,8 @@ def main() -> int:
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the path shards over sequences and (layer, KV head) units with no exchange; "
-              "see DESIGN.md)", file=sys.stderr)
+              "(the path would shard over sequences and (layer, KV head) units with no "
+              "exchange between GPUs)", file=sys.stderr)
         return 2
 
     import numpy as np

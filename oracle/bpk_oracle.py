@@ -12,7 +12,9 @@ Sources (cited by section; no sentence of them is reproduced):
   translation of arXiv 2609.17652 -- §1 (observations 1 and 2), §2 ("Top-k
   decoding", "SparQ"), §3.1 (cost model, Eq. 1), §3.2 (bit-plane K cache).
   The extraction stops inside §3.2, so the plane word layout and the
-  prefix-decode formula follow the plainest reading listed in the design doc.
+  prefix-decode formula take the plainest reading: plane p holds bit 3 - p
+  of each offset code (the top bit first), and a t-bit prefix decodes to its
+  cell midpoint (see ``prefix_values``).
 * [ReadKV] the page "AI存储论文解读:ReadKV：KV 存得更细、每步少读..." --
   §5.2 (key-channel importance summed over the query heads that share a KV
   head), §5.3 (value depth per token from the heads' squared attention
