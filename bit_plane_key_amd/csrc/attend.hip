@@ -113,7 +113,7 @@ __global__ __launch_bounds__(ATT_THREADS) void attend_kernel(AttArgs a) {
   __shared__ int masks[ATT_ROWS];
   __shared__ float p[ATT_ROWS][G];                     // logits, then weights
   __shared__ float red[ATT_THREADS / 64][G];
-  __shared__ float oacc[ATT_THREADS / 16][G][D];       // per 16-lane row group
+  __shared__ float oacc[LG ? 1 : ATT_THREADS / 16][G][D];  // per 16-lane row group (not LG)
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, rs = lane >> 4, ch = lane & 15;
   const int split = blockIdx.x, u = blockIdx.y;
@@ -134,9 +134,6 @@ __global__ __launch_bounds__(ATT_THREADS) void attend_kernel(AttArgs a) {
       mask = a.umask[(long long)u * sel + r0 + tid];
     }
     rows[tid] = row;
-    if (LG && tid < nr)  // the row's value scale, fetched with its key row
-      a.vsc[(long long)u * sel + r0 + tid] =
-          (float)__builtin_bit_cast(_Float16, a.vscales[gu * a.g.cap + row]);
     masks[tid] = mask;
   }
   // the lane's 8 channels of each query head
@@ -186,6 +183,10 @@ __global__ __launch_bounds__(ATT_THREADS) void attend_kernel(AttArgs a) {
       }
     }
   }
+  // LG: the row's value scale, its load issued after the key rows' (stored
+  // once the logits are done)
+  uint16_t vs_bits = 0;
+  if (LG && tid < nr) vs_bits = a.vscales[gu * a.g.cap + rows[tid]];
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
     const int r = RPW * wave + 4 * it + rs;
@@ -242,9 +243,11 @@ __global__ __launch_bounds__(ATT_THREADS) void attend_kernel(AttArgs a) {
     sum[h] = v;
   }
   if constexpr (LG) {
-    if (tid < nr)
+    if (tid < nr) {
 #pragma unroll
       for (int h = 0; h < G; ++h) a.e[((long long)u * G + h) * sel + r0 + tid] = p[tid][h];
+      a.vsc[(long long)u * sel + r0 + tid] = (float)__builtin_bit_cast(_Float16, vs_bits);
+    }
     if (tid < G) {
       float* st = a.stats + (((long long)u * a.nsplit + split) * G + tid) * 2;
       st[0] = mx[tid];

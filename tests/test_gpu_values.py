@@ -215,6 +215,41 @@ def test_value_depth_bit_exact(lib):
             assert d[0, 0, 0].sum() == 1
 
 
+def test_value_depth_exact_ties_bit_exact(lib):
+    """Every value row the same (equal scales) and weights from {1/4, 1/2, 1}:
+    plane values tie within a plane and across planes (1/4 at plane 0 equals
+    1 at plane 1), so most budgets cut through a run of equal values, which
+    are handed out in (row, plane) order."""
+    b, wl = lib
+    rng = np.random.default_rng(31)
+    n, ld = 6000, 8192
+    cache = b.Cache(2, 1, 1, 6016, group=4, k_dtype="bf16", values=True)
+    cache.chan_var.fill_(1.0)
+    row = rng.standard_normal(128)
+    for s, m in enumerate((n, 300)):
+        k = _bf16(rng.standard_normal((1, 1, m, 128)))
+        v = _bf16(np.broadcast_to(row, (1, 1, m, 128)))
+        b.encode_append(cache, s, k.cuda(), v.cuda())
+    torch.cuda.synchronize()
+    _, vscales = O.encode_values(_bf16(row[None, :]).float().numpy())
+    counts = [5000, 300]
+    rows = np.full((2, 1, 1, ld), -7, dtype=np.int32)
+    nrows = np.array(counts, dtype=np.int32).reshape(2, 1, 1)
+    wts = np.full((2, 1, 1, ld), np.nan, dtype=np.float32)
+    for s, c in enumerate(counts):
+        rows[s, 0, 0, :c] = np.sort(rng.choice(n if s == 0 else 300, size=c, replace=False))
+        wts[s, 0, 0, :c] = rng.choice(np.array([0.25, 0.5, 1.0], dtype=np.float32), size=c)
+    dev = lambda x: torch.from_numpy(x).cuda()
+    for budget in (1, 2, 777, 1500, 4999, 5001, 9000, 4 * 5000 - 3):
+        d = b.value_depth(cache, 0, 1, dev(rows), dev(nrows), dev(wts), budget)
+        torch.cuda.synchronize()
+        d = d.cpu().numpy()
+        for s, c in enumerate(counts):
+            ref = O.alloc_value_depth(wts[s, 0, 0, :c], np.full(c, vscales[0]), budget)
+            assert np.array_equal(d[s, 0, 0, :c], ref), (budget, s)
+            assert int(d[s, 0, 0, :c].sum()) == min(budget, 4 * c), (budget, s)
+
+
 # ---------------------------------------------------------------------------
 # attention with value depths
 # ---------------------------------------------------------------------------
