@@ -494,8 +494,13 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : 2) void scan_wide_kernel
               const int p = d.w * 256 + d.z;
               const int th = (int)(((uint32_t)kap << bp) + (uint32_t)(c == 3 ? neg3 : 0));
               const bool pass = h < G && (c == 3 ? (p ^ neg3) : p) >= th;
-              if (__ballot(pass) != 0ull && pass)
-                append(tok, h, score4(d, dc, bp, c == 3 && neg3 != 0, eb));
+              // the test's margin for the dropped low digits grows with the
+              // rows read; a passing token is kept only if its written score
+              // reaches theta (the candidates are then exactly those tokens)
+              if (__ballot(pass) != 0ull && pass) {
+                const float sc = score4(d, dc, bp, c == 3 && neg3 != 0, eb);
+                if (sc >= theta[h]) append(tok, h, sc);
+              }
             } else {
               if (h < G) store(tok, h, score4(d, dc, bp, c == 3 && neg3 != 0, eb));
             }
