@@ -83,14 +83,17 @@ def counted_valu(config: str, budget: int):
     return (None if busy is None else float(busy)), (None if per is None else float(per))
 
 
-def time_launches(fn, steps: int):
+def time_launches(fn, steps: int, before=None):
     """Median milliseconds of `steps` calls of fn, each between two HIP events
-    recorded on the current stream (the stream the library's calls run on)."""
+    recorded on the current stream (the stream the library's calls run on);
+    `before`, if given, runs ahead of each call, outside the timed region."""
     import torch
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
     torch.cuda.synchronize()
     for a, b in ev:
+        if before is not None:
+            before()
         a.record()
         fn()
         b.record()
@@ -275,6 +278,23 @@ def main() -> int:
     log("stages, median us: " + " ".join(f"{nm} {v * 1e3:.1f}" for nm, v in stage_ms.items()))
     flagged = bpk.decode_fallback_units(cache, 0, L, k, ws)
     log(f"units redone unfused in the last step: {flagged} of {cfg.units}")
+
+    # the same step with the caches evicted first: a 1 GiB write before each
+    # call, outside the timed region (c1 and c2 fit in the L2 and the
+    # Infinity Cache, so their warm figures are latencies, not HBM rates)
+    evicted = None
+    if not appends:
+        flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+
+        def flushed():
+            flush.fill_(1.0)
+
+        ms_ev = time_launches(step, args.steps, before=flushed)
+        st_ev = traced(args.steps, lambda: (flushed(), step()))
+        del flush
+        evicted = {"decode_step_us": round(ms_ev * 1e3, 1),
+                   "stage_us": {nm: round(v * 1e3, 1) for nm, v in st_ev.items()}}
+        log(f"caches evicted before each step: {evicted}")
 
     # attention: the union of the heads' selections, fetched once per unit
     idx = torch.empty((cfg.seqs, L, cfg.heads, cfg.group, k), dtype=torch.int32, device="cuda")
@@ -518,6 +538,8 @@ def main() -> int:
         },
         "decode_step_us": round(ms_step * 1e3, 1),
         "stage_us": {name: round(v * 1e3, 1) for name, v in stage_ms.items()},
+        "evicted": None if evicted is None else dict(
+            evicted, scan_gbs=round(sbytes / (evicted["stage_us"]["scan"] * 1e-6) / 1e9, 2)),
         "units_redone_unfused": flagged,
         "attend": {"union_rows": union_rows, "bytes": attend_bytes,
                    "gbs": round(attend_bytes / (stage_ms["attend"] * 1e-3) / 1e9, 1)},
