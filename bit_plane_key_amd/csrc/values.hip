@@ -12,9 +12,9 @@
 // 2. vdepth_att_kernel, one workgroup per unit: the splits' statistics merged
 //    into one factor per (split, head), so that p_hr = e_hr f_sh; importances
 //    a_r = sum_h p_hr^2, gains w_r = a_r s_r^2, and the depth search (the
-//    budget-th largest plane value w_r 4^-t, two bits a pass over the fp32
-//    bit patterns, then the planes equal to it handed out in (row, plane)
-//    order);
+//    budget-th largest plane value w_r 4^-t by a radix select over the fp32
+//    bit patterns, 8 bits a pass, then the planes equal to it handed out in
+//    (row, plane) order);
 // 3. vaccum_kernel, one workgroup per (split, unit): the rows' first t planes
 //    read, the values rebuilt and accumulated with every head's probability;
 // 4. vsum_kernel: the splits' partial outputs added in split order.
