@@ -44,6 +44,15 @@ def scan_bytes(depth_np, n: int) -> float:
     return float(t.sum()) * nb * 8.0 + float((t > 0).sum()) * nb * 2.0
 
 
+SAMPLE_STRIDE, SAMPLE_GROUP = 4096, 64  # the sampled scan: the first 64 blocks of every 4096
+
+
+def sampled_blocks(n: int) -> int:
+    """Blocks of one unit of n tokens that the decode step's sampled scan reads."""
+    nb = n // 64
+    return sum(min(SAMPLE_GROUP, nb - g) for g in range(0, nb, SAMPLE_STRIDE))
+
+
 TRAFFIC_SOURCES = ("bit_plane_key_amd/csrc/scan.hip", "bit_plane_key_amd/csrc/scan_common.h",
                    "bit_plane_key_amd/csrc/bpk_internal.h")
 
@@ -543,6 +552,13 @@ def main() -> int:
         "units_redone_unfused": flagged,
         "attend": {"union_rows": union_rows, "bytes": attend_bytes,
                    "gbs": round(attend_bytes / (stage_ms["attend"] * 1e-3) / 1e9, 1)},
+        # algorithmic bytes over stage time: the sampled scan reads the same
+        # rows as the scan over the sampled blocks only
+        "stage_gbs": {
+            "sample": round(sbytes * sampled_blocks(n) / max(n // 64, 1)
+                            / (stage_ms["sample"] * 1e-3) / 1e9, 1),
+            "scan": round(scan_gbs, 1),
+            "attend": round(attend_bytes / (stage_ms["attend"] * 1e-3) / 1e9, 1)},
         "full_scan_us": round(ms_full * 1e3, 1),
         "full_scan_gbs": round(sbytes / (ms_full * 1e-3) / 1e9, 2),
         "keys_per_s": round(keys_per_s, 0),

@@ -206,3 +206,15 @@ def test_value_entry_points_validate(lib):
                                      None, FAKE, need_d - 1, None) == -3
     assert lib.LIB.bpk_decode_step_v(c, FAKE, 0, 1, 88, 512, 0.088, -2, FAKE, None, None, None,
                                      None, FAKE, need_d, None) == -1
+
+
+def test_bench_sample_plan_matches_the_library():
+    """bench.py counts the sampled scan's bytes with the library's sample plan
+    (the first SAMPLE_GROUP blocks of every SAMPLE_STRIDE)."""
+    import bench
+    src = open(os.path.join(ROOT, "bit_plane_key_amd", "csrc", "bpk_internal.h")).read()
+    stride = int(re.search(r"SAMPLE_STRIDE\s*=\s*(\d+)", src).group(1))
+    group = int(re.search(r"SAMPLE_GROUP\s*=\s*(\d+)", src).group(1))
+    assert (bench.SAMPLE_STRIDE, bench.SAMPLE_GROUP) == (stride, group)
+    assert bench.sampled_blocks(64 * (2 * stride + 10)) == 2 * group + 10
+    assert bench.sampled_blocks(64 * 20) == 20
