@@ -194,7 +194,7 @@ def main() -> int:
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the sweep over the workload's plane budgets (profiling runs)")
     ap.add_argument("--cpu-tokens", type=int, default=1 << 18)
-    ap.add_argument("--cpu-layers", type=int, default=4)
+    ap.add_argument("--cpu-layers", type=int, default=5)
     ap.add_argument("--host-resident", action="store_true",
                     help="rows, planes and scales in pinned host memory, read over the host "
                          "link (the regime of the Fathom page's measurements)")
