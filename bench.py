@@ -353,9 +353,13 @@ def main() -> int:
         qbq = torch.empty((cfg.seqs, L, cfg.heads, cfg.group, 128), dtype=torch.float32,
                           device="cuda")
         for name, (rule, param, ch) in rules.items():
-            def bstep(rule=rule, param=param, ch=ch):
+            # each rule's bound on the rows a unit reads: 4 r, 4 c, 128 t
+            bound = 128 * param if rule == bpk.BPK_DEPTH_UNIFORM else 4 * param
+
+            def bstep(rule=rule, param=param, ch=ch, bound=bound):
                 bpk.fixed_depth(cache, q, 0, L, rule, param, channels=ch, depth=dq, q_basis=qbq)
-                bpk.decode_step_depth(cache, q, qbq, dq, 0, L, k, scale, out=out, ws=ws)
+                bpk.decode_step_depth(cache, q, qbq, dq, 0, L, k, scale, out=out, ws=ws,
+                                      max_rows=bound)
             for _ in range(2):
                 bstep()
             ms_b = time_launches(bstep, args.steps)
@@ -396,7 +400,8 @@ def main() -> int:
 
         def one_call():  # every layer at its budget in one call
             bpk.alloc_depth_layers(cache, q, 0, L, lb_t, depth=dl, q_basis=ql)
-            bpk.decode_step_depth(cache, q, ql, dl, 0, L, k, scale, out=out, ws=ws)
+            bpk.decode_step_depth(cache, q, ql, dl, 0, L, k, scale, out=out, ws=ws,
+                                  max_rows=int(lb.max()))  # a layer's units read its budget
         for _ in range(2):
             layer_loop(lb)
             layer_loop(uni)

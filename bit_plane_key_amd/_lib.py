@@ -84,7 +84,7 @@ def _load() -> ctypes.CDLL:
         "bpk_select_topk": (ctypes.c_int, [C, P, I32, I32, I32, P, P, SZ, P]),
         "bpk_sparse_attend": (ctypes.c_int, [C, P, P, I32, I32, I32, F, P, P, SZ, P]),
         "bpk_decode_step": (ctypes.c_int, [C, P, I32, I32, I32, I32, F, P, P, P, P, SZ, P]),
-        "bpk_decode_step_depth": (ctypes.c_int, [C, P, P, P, I32, I32, I32, F, P, P, P, SZ, P]),
+        "bpk_decode_step_depth": (ctypes.c_int, [C, P, P, P, I32, I32, I32, I32, F, P, P, P, SZ, P]),
         "bpk_decode_step_noalloc": (ctypes.c_int, [C, P, I32, I32, I32, I32, F, P, P, P, P]),
         "bpk_decode_fallback_units": (ctypes.c_int, [C, I32, I32, I32, P, SZ, P, P]),
         "bpk_value_depth": (ctypes.c_int, [C, I32, I32, P, P, I32, P, I32, P, P]),
@@ -392,8 +392,9 @@ def decode_step(cache: Cache, q: torch.Tensor, l0: int, l1: int, budget: int, k:
 
 def decode_step_depth(cache: Cache, q: torch.Tensor, q_basis: torch.Tensor, depth: torch.Tensor,
                       l0: int, l1: int, k: int, softmax_scale: float, out=None, idx_out=None,
-                      ws=None, stream=None):
-    """decode_step on given depths (from alloc_depth or fixed_depth)."""
+                      ws=None, stream=None, max_rows: int = 0):
+    """decode_step on given depths (from alloc_depth or fixed_depth); max_rows:
+    a bound on the plane rows (sum of depths) of every unit, 0 if not known."""
     u = (cache.S, l1 - l0, cache.H)
     _need(q, "q", torch.bfloat16, (*u, cache.G, HEAD_DIM))
     _need(q_basis, "q_basis", torch.float32, (*u, cache.G, HEAD_DIM))
@@ -407,7 +408,8 @@ def decode_step_depth(cache: Cache, q: torch.Tensor, q_basis: torch.Tensor, dept
     if ws is None:
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     _check(LIB.bpk_decode_step_depth(cache.struct(), q.data_ptr(), q_basis.data_ptr(),
-                                     depth.data_ptr(), l0, l1, int(k), float(softmax_scale),
+                                     depth.data_ptr(), int(max_rows), l0, l1, int(k),
+                                     float(softmax_scale),
                                      out.data_ptr(), _ptr(idx_out), ws.data_ptr(), ws.numel(),
                                      _stream(stream)))
     return out

@@ -426,7 +426,8 @@ int decode_step_impl(const bpk_cache_t* c, const bpk::Geom& g, const uint16_t* q
                      uint8_t* depth_out, int32_t* idx_out, char* base, bool traced,
                      hipStream_t st, const uint8_t* depth_in = nullptr,
                      const float* qb_in = nullptr, int v_budget = -1,
-                     int32_t* union_out = nullptr, uint8_t* vdepth_out = nullptr) {
+                     int32_t* union_out = nullptr, uint8_t* vdepth_out = nullptr,
+                     int rows_bound = 0) {
   const DecodeWs w = decode_ws(g, k, v_budget >= 0);
   const bool given = depth_in != nullptr;
   float* q_basis = given ? const_cast<float*>(qb_in) : reinterpret_cast<float*>(base + w.q_basis);
@@ -436,8 +437,10 @@ int decode_step_impl(const bpk_cache_t* c, const bpk::Geom& g, const uint16_t* q
   int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(base + w.idx);
   int rc = BPK_OK;
   // alloc_depth hands out exactly min(P, 4D) planes per unit; given depths:
-  // not known on the host
-  const int rows = given ? -1 : budget_planes < 4 * bpk::D ? budget_planes : 4 * bpk::D;
+  // the caller's bound when it fits the fast scan (every unit at most that
+  // many rows), else not known on the host
+  const int rows = given ? (rows_bound > 0 && rows_bound <= bpk::SCAN_FAST_ROWS ? rows_bound : -1)
+                         : budget_planes < 4 * bpk::D ? budget_planes : 4 * bpk::D;
   if (traced && g_trace.on) ++g_trace.calls;
   auto timer = [&](int stage) { return StageTimer(stage, st, traced); };
   if (!given) {
@@ -595,19 +598,20 @@ int bpk_decode_step_v(const bpk_cache_t* c, const uint16_t* q, int32_t l0, int32
 }
 
 int bpk_decode_step_depth(const bpk_cache_t* c, const uint16_t* q, const float* q_basis,
-                          const uint8_t* depth, int32_t l0, int32_t l1, int32_t k,
-                          float softmax_scale, float* out, int32_t* idx_out, void* ws,
+                          const uint8_t* depth, int32_t max_rows, int32_t l0, int32_t l1,
+                          int32_t k, float softmax_scale, float* out, int32_t* idx_out, void* ws,
                           size_t ws_bytes, void* stream) {
   bpk::Geom g;
   int rc = check_decode(c, l0, l1, q, 0, k, out, &g);
   if (rc) return rc;
   if (!q_basis || !depth) return fail(BPK_EINVAL, "q_basis and depth must be non-NULL");
+  if (max_rows < 0) return fail(BPK_EINVAL, "max_rows < 0");
   const size_t need = decode_ws(g, k).total;
   if (!ws || ws_bytes < need)
     return fail(BPK_EWORKSPACE, "workspace of %zu bytes < %zu needed", ws_bytes, need);
   return decode_step_impl(c, g, q, 0, k, softmax_scale, out, nullptr, idx_out,
                           static_cast<char*>(ws), true, static_cast<hipStream_t>(stream), depth,
-                          q_basis);
+                          q_basis, -1, nullptr, nullptr, max_rows);
 }
 
 int bpk_decode_step_noalloc(const bpk_cache_t* c, const uint16_t* q, int32_t l0, int32_t l1,

@@ -745,7 +745,7 @@ __device__ __forceinline__ bool select_head(const CandArgs& a, int u, int h, int
         const int c = cnt[x];
         pre[x] = (uint16_t)c;
         sum += c;
-        over |= c > ps;
+        over |= c > ps || c < 0;  // (a part no scan wrote, for a unit it skipped)
       }
     }
     int incl = sum;

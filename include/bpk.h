@@ -288,11 +288,19 @@ int bpk_decode_step(const bpk_cache_t* cache, const uint16_t* q, int32_t l0, int
  * [S][nl][H][G][128] fp32 and depth [S][nl][H][128] uint8 as bpk_alloc_depth
  * or bpk_fixed_depth writes them; q bf16 for the attention; the other
  * arguments, the workspace (bpk_workspace_bytes(.., BPK_OP_DECODE, ..)) and
- * the errors as bpk_decode_step.
+ * the errors as bpk_decode_step.  max_rows: 0 when not known, else a bound on
+ * the plane rows every unit reads (the sum of its depths; the rules of
+ * bpk_fixed_depth read at most 4 r, 4 c and 128 t rows, bpk_alloc_depth_layers
+ * exactly the layer's budget).  The library cannot see the depths from the
+ * host, so without a bound it launches every scan variant and most of their
+ * workgroups only read the depths and leave; with a bound of at most 128 it
+ * launches only the variant that holds that many rows.  A unit reading more
+ * rows than a given bound is not scanned: its selection and output are then
+ * undefined (the call does not fault).  BPK_EINVAL for max_rows < 0.
  */
 int bpk_decode_step_depth(const bpk_cache_t* cache, const uint16_t* q, const float* q_basis,
-                          const uint8_t* depth, int32_t l0, int32_t l1, int32_t k,
-                          float softmax_scale, float* out, int32_t* idx_out, void* ws,
+                          const uint8_t* depth, int32_t max_rows, int32_t l0, int32_t l1,
+                          int32_t k, float softmax_scale, float* out, int32_t* idx_out, void* ws,
                           size_t ws_bytes, void* stream);
 
 /*

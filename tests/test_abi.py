@@ -150,9 +150,12 @@ def test_fixed_depth_validates(lib):
                                    None) == -1
     assert lib.LIB.bpk_fixed_depth(c, None, 0, 1, lib.BPK_DEPTH_UNIFORM, 2, None, FAKE, FAKE,
                                    None) == -1
-    rc = lib.LIB.bpk_decode_step_depth(c, FAKE, None, FAKE, 0, 1, 512, 0.088, FAKE, None, FAKE,
+    rc = lib.LIB.bpk_decode_step_depth(c, FAKE, None, FAKE, 0, 0, 1, 512, 0.088, FAKE, None, FAKE,
                                        1 << 30, None)
     assert rc == -1
+    rc = lib.LIB.bpk_decode_step_depth(c, FAKE, FAKE, FAKE, -1, 0, 1, 512, 0.088, FAKE, None,
+                                       FAKE, 1 << 30, None)
+    assert rc == -1 and "max_rows" in lib.last_error()
 
 
 def test_product_has_no_cpu_path():

@@ -91,12 +91,18 @@ def test_baseline_decode_step(c2, rule, param):
     depth, qb = _depths(b, cfg, cache, q, rule, param)
     idx = torch.empty((1, 1, cfg.heads, cfg.group, k), dtype=torch.int32, device="cuda")
     out = b.decode_step_depth(cache, q, qb, depth, 0, 1, k, scale, idx_out=idx)
+    # the rule's bound on the rows a unit reads (4 r, 4 c, 128 t) gives the
+    # same result with only the scan variants that hold that many rows
+    bound = {"sparq": 4 * param, "ds": 4 * param, "uniform": 128 * param}[rule]
+    idx_b = torch.empty_like(idx)
+    out_b = b.decode_step_depth(cache, q, qb, depth, 0, 1, k, scale, idx_out=idx_b, max_rows=bound)
     scores = b.scan_scores(cache, qb, depth, 0, 1)
     idx2 = b.select_topk(cache, scores, 0, 1, k)
     out2 = b.sparse_attend(cache, q, idx2, 0, 1, k, scale)
     torch.cuda.synchronize()
     assert torch.equal(idx, idx2)
     assert torch.equal(out, out2)
+    assert torch.equal(idx_b, idx) and torch.equal(out_b, out)
     ix = idx.cpu().numpy()
     ot = out.cpu().numpy()
     for h in (1, 6):
