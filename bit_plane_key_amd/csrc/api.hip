@@ -482,9 +482,14 @@ int decode_step_impl(const bpk_cache_t* c, const bpk::Geom& g, const uint16_t* q
     if (rc) return rc;
     {
       auto t = timer(BPK_STAGE_SCAN);
-      rc = hip_status(
-          bpk::launch_scan_cand(g, q_basis, depth, c->planes, c->scales, k, cb, rows, st),
-          "decode_step/scan");
+      // with the caller's bound, a unit above it is skipped by the scan: its
+      // counts start at zero, so that it has no candidates and is redone
+      if (given && rows > 0)
+        rc = hip_status(bpk::launch_zero_counts(g, cb, st), "decode_step/counts");
+      if (!rc)
+        rc = hip_status(
+            bpk::launch_scan_cand(g, q_basis, depth, c->planes, c->scales, k, cb, rows, st),
+            "decode_step/scan");
     }
     if (rc) return rc;
     {

@@ -129,6 +129,9 @@ hipError_t launch_scan_sample(const Geom& g, const float* q_basis, const uint8_t
                               const uint64_t* planes, const uint16_t* scales, const CandBufs& cb,
                               int rows, hipStream_t st);
 hipError_t launch_threshold(const Geom& g, int k, const CandBufs& cb, hipStream_t st);
+// the candidate part counts set to zero (a scan that may skip units writes
+// none for them)
+hipError_t launch_zero_counts(const Geom& g, const CandBufs& cb, hipStream_t st);
 hipError_t launch_scan_cand(const Geom& g, const float* q_basis, const uint8_t* depth,
                             const uint64_t* planes, const uint16_t* scales, int k,
                             const CandBufs& cb, int rows, hipStream_t st);

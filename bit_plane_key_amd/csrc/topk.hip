@@ -1031,6 +1031,25 @@ __global__ __launch_bounds__(256) void count_flags_kernel(const int32_t* flag, i
 
 }  // namespace
 
+// the candidate part counts the selection reads (every workgroup of every
+// unit and head) set to zero
+__global__ __launch_bounds__(256) void zero_counts_kernel(int32_t* count, long long regions,
+                                                          int parts, long long total) {
+  for (long long e = (long long)blockIdx.x * 256 + threadIdx.x; e < total; e += (long long)gridDim.x * 256)
+    count[(e / parts) * regions * CAND_PARTS + e % parts] = 0;
+}
+
+hipError_t launch_zero_counts(const Geom& g, const CandBufs& cb, hipStream_t st) {
+  long long maxnb = 0;
+  for (int s = 0; s < g.S; ++s) maxnb = g.n[s] / BLK > maxnb ? g.n[s] / BLK : maxnb;
+  const int parts = (int)((maxnb + cb.wg_blocks - 1) / cb.wg_blocks) * CAND_PARTS;
+  const long long total = (long long)g.units() * g.G * parts;
+  if (total == 0) return hipSuccess;
+  const long long blocks = (total + 255) / 256 < 1024 ? (total + 255) / 256 : 1024;
+  zero_counts_kernel<<<(unsigned)blocks, 256, 0, st>>>(cb.count, cb.regions, parts, total);
+  return hipGetLastError();
+}
+
 hipError_t launch_count_flags(int units, const int32_t* flag, int32_t* count, hipStream_t st) {
   count_flags_kernel<<<1, 256, 0, st>>>(flag, units, count);
   return hipGetLastError();

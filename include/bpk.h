@@ -296,7 +296,9 @@ int bpk_decode_step(const bpk_cache_t* cache, const uint16_t* q, int32_t l0, int
  * workgroups only read the depths and leave; with a bound of at most 128 it
  * launches only the variant that holds that many rows.  A unit reading more
  * rows than a given bound is not scanned: its selection and output are then
- * undefined (the call does not fault).  BPK_EINVAL for max_rows < 0.
+ * undefined (it finds no candidates and is redone by the fallback, which
+ * picks among the unit's own tokens, so every row the attention reads is a
+ * token of the unit).  BPK_EINVAL for max_rows < 0.
  */
 int bpk_decode_step_depth(const bpk_cache_t* cache, const uint16_t* q, const float* q_basis,
                           const uint8_t* depth, int32_t max_rows, int32_t l0, int32_t l1,

@@ -114,3 +114,21 @@ def test_baseline_decode_step(c2, rule, param):
         P.check_selection(ix[0, 0, h], O.select_topk(full, n, k), full, l1, n, k, f"{rule} head {h}")
         P.check_attention(ot[0, 0, h], O.attend(inp["q"], inp["k"], inp["v"], ix[0, 0, h], scale),
                           f"{rule} head {h}")
+
+
+def test_decode_step_depth_bound_below_the_rows_read(c2):
+    """A bound below the rows the units read (SparQ r = 32: 128 rows, bound
+    64) leaves every unit unscanned: the call still completes, and every
+    selected index is a token of the unit (the result itself is undefined)."""
+    b, wl, cfg, cache, q, inps = c2
+    n, k = cfg.n, cfg.k
+    scale = wl.softmax_scale(cfg)
+    depth, qb = _depths(b, cfg, cache, q, "sparq", 32)
+    idx = torch.empty((1, 1, cfg.heads, cfg.group, k), dtype=torch.int32, device="cuda")
+    ws = torch.zeros(b.workspace_bytes(cache, b.BPK_OP_DECODE, 0, 1, k), dtype=torch.uint8,
+                     device="cuda")
+    out = b.decode_step_depth(cache, q, qb, depth, 0, 1, k, scale, idx_out=idx, ws=ws, max_rows=64)
+    torch.cuda.synchronize()
+    ix = idx.cpu().numpy()
+    assert ((ix >= 0) & (ix < n)).all()
+    assert torch.isfinite(out).all()
