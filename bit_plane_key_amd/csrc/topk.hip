@@ -967,7 +967,7 @@ __device__ __forceinline__ bool select_head(const CandArgs& a, int u, int h, int
 // G strictly ascending lists (position of an entry = its index in its list
 // plus the entries below it in every other list), collapses runs of one token
 // into a union row with a G-bit head mask and writes the rows, masks and
-// count as union_kernel does, and zeroes the unit's arrival counter.
+// row count as union_kernel does.
 // (WPE: wavefronts per SIMD the registers allow; three caps them at 168,
 // which costs each wavefront some speed but fits 50 % more workgroups)
 template <int G, int WPE>
