@@ -282,7 +282,12 @@ __global__ __launch_bounds__(SCAN_THREADS, G == 8 ? 1 : (RM <= RM_SMALL ? 3 : 2)
     u16x2 mv = {0, 0};
     if (step_blocks(i) == GB) {
 #pragma unroll
-      for (int x = 0; x < 4; ++x) mv = __builtin_elementwise_max(mv, __builtin_bit_cast(u16x2, sw[x]));
+      for (int x = 0; x < 4; ++x) {
+        // the word goes through a scalar first: a bit cast of the vector
+        // element itself compiled to a read of element 0 for every x
+        const uint32_t w = sw[x];
+        mv = __builtin_elementwise_max(mv, __builtin_bit_cast(u16x2, w));
+      }
     } else {
       const int nv = step_blocks(i) - 8 * sc_h;
 #pragma unroll

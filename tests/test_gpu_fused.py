@@ -288,3 +288,47 @@ def test_fused_long_unit_radix_threshold(bpk):
     planes, scales = O.encode_unit(kv[toks])      # the sampled blocks, re-encoded
     ref, l1 = O.scan_scores(qv, depth, planes, scales, len(toks))
     P.check_scores(sc[:, toks], ref, l1, "long unit sample")
+
+
+def _random_cases(count=8, seed=2026):
+    """Seeded random decode shapes: ragged n, every group size, k up to the
+    fused limit, budgets from none to the wide kernel's row counts."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(count):
+        group = int(rng.choice([1, 2, 4, 8]))
+        n = int(rng.integers(1200, 40000))
+        k = int(rng.integers(40, min(1024, n // 2)))
+        budget = int(rng.choice([0, 1, 37, 88, 128, 200, 512]))
+        cases.append((i, n, group, k, budget))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_cases(), ids=lambda c: f"n{c[1]}-G{c[2]}-k{c[3]}-P{c[4]}")
+def test_fused_random_shapes_against_oracle(bpk, case):
+    """Random shapes with heavy-tailed channel scales and one outlier
+    channel: the fused step selects what the unfused path selects, its sets
+    pass the oracle's top-k bar and its attention is within 2e-3."""
+    b, wl = bpk
+    i, n, group, k, budget = case
+    _say(f"random case {i}: n={n} G={group} k={k} P={budget}")
+    rng = np.random.default_rng(1000 + i)
+    sig = np.exp(rng.uniform(math.log(0.05), math.log(3.0), 128))
+    sig[int(rng.integers(128))] *= 12.0  # an outlier channel
+    kb = f32_to_bf16_bits((rng.standard_t(4, (n, 128)) * sig).astype(np.float32))
+    vb = f32_to_bf16_bits(rng.standard_normal((n, 128)).astype(np.float32))
+    qb = f32_to_bf16_bits(rng.standard_normal((group, 128)).astype(np.float32))
+    var = (sig ** 2).astype(np.float32)
+    cache = _unit_cache(b, kb, vb, var, group)
+    q = _to_dev(qb)[None, None, None]
+    scale = 1 / math.sqrt(128)
+    idx, out, flagged = _fused(b, cache, q, budget, k, scale, group)
+    scores, idx2 = _unfused(b, cache, q, budget, k, scale)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx2)
+    kv, vv, qv = bf16_bits_to_f32(kb), bf16_bits_to_f32(vb), bf16_bits_to_f32(qb)
+    ref = O.decode_unit(qv, var, kv, vv, n, budget, k, scale)
+    ix = idx[0, 0, 0].cpu().numpy()
+    where = f"case {i} n={n} G={group} k={k} P={budget}"
+    P.check_selection(ix, ref["idx"], ref["scores"], ref["l1"], n, k, where)
+    P.check_attention(out[0, 0, 0].cpu().numpy(), O.attend(qv, kv, vv, ix, scale), where)
